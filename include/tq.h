@@ -1,0 +1,189 @@
+/*
+ * tq.h — C ABI of the trellis / MXFP4 routed-expert library for AMD MI355X (gfx950).
+ *
+ * The library multiplies token activations by routed mixture-of-experts weights that stay
+ * compressed in device memory and are decoded on the fly:
+ *   - T16 bitshift-trellis codes, K = 2, 3 or 4 bits per weight (DeepSeek-V4.1-Flash-1017
+ *     · dsx T16 page, "How T16 works": 16-bit window, multiply by 0x3A2F, add the
+ *     product's two bytes; column-major positions in 16 x 16 tiles; per-output scales;
+ *     128-wide Hadamard rotation of the inputs);
+ *   - MXFP4 (E2M1 elements, one E8M0 scale per 32 inputs), the official expert store
+ *     (DeepSeek-V4.1-Flash-1017 · exlr8 page, "Stores").
+ * Every bit-level rule (tile order, bit order, tail-biting windows, nibble order, rounding)
+ * is the one in FORMAT.md, rules F1-F14.
+ *
+ * Conventions for every entry point:
+ *   - Pointers marked "device" are device memory owned by the caller; the library never
+ *     frees, allocates or retains them. Pointers marked "host" are read during the call.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream). Work is
+ *     enqueued asynchronously on it. The compute entry points never synchronise, never
+ *     allocate and never read routes back to the host, so they can be captured in a graph.
+ *   - All host-side argument checks run before any HIP call. Return value 0 = success;
+ *     a negative TQ_E* code otherwise, with a message from tq_last_error() (thread-local).
+ *   - Device-side data errors (an expert id outside [-1, E), a width byte not in {2,3,4},
+ *     a misaligned unit offset) do not fault: the affected output slot is set to NaN and
+ *     a sticky bit is set in the workspace status word (read with tq_device_status).
+ */
+#ifndef TQ_H
+#define TQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- return codes ------------------------------------------------------------------ */
+#define TQ_OK 0
+#define TQ_EINVAL (-1)       /* bad shape, null pointer, bad K, bad flag                */
+#define TQ_EUNSUPPORTED (-2) /* device is not gfx950                                    */
+#define TQ_EALIGN (-3)       /* a pointer is not aligned as documented                  */
+#define TQ_EWORKSPACE (-4)   /* workspace missing or smaller than tq_workspace_bytes()  */
+#define TQ_EHIP (-5)         /* a HIP runtime call failed                               */
+
+/* ---- flags of the expert GEMM calls -------------------------------------------------- */
+#define TQ_AUTO 0u     /* choose the decode-batch kernel when T*topk <= 16*E, else prefill */
+#define TQ_GEMV 1u     /* force the decode-batch kernel (grouped GEMV, tokens in 16s)      */
+#define TQ_GEMM 2u     /* force the prefill kernel (route bucketing + grouped MFMA GEMM)   */
+#define TQ_COMBINE 4u  /* write y[T][out] = sum over k = 0..topk-1 (in order) of the slots */
+
+/* ---- device status bits (tq_device_status) ------------------------------------------ */
+#define TQ_STATUS_BAD_EXPERT 1u  /* an id outside [-1, E): that slot's output is NaN    */
+#define TQ_STATUS_BAD_UNIT 2u    /* a width byte not in {2,3,4} or a misaligned offset  */
+
+/*
+ * A trellis expert layer (FORMAT F1-F7, F12). Expert e's unit holds out*in*K/8 bytes at
+ * byte offset code_off[e] of `codes`: 16 x 16 tiles in strip-major order (tile (to, ti)
+ * at index to*(in/16)+ti), each tile 8*K little-endian uint32 words, bits read most
+ * significant first, the state of position p being the 16-bit window at bit p*K read
+ * circularly within the tile. Mixed widths may share one buffer (the pages' layers group
+ * k2, k3, k4 units with ascending expert ids — DeepSeek-V4.1-Flash-1017 TrellisMX K2 Mix,
+ * "What is stored"; any layout works through the per-expert descriptor).
+ */
+typedef struct tq_trellis_layer {
+  int32_t E;                /* experts in the layer, 1 .. 65535                          */
+  int32_t out;              /* output channels per expert, multiple of 16                 */
+  int32_t in;               /* inputs per expert, multiple of 256                         */
+  int32_t reserved;         /* must be 0                                                  */
+  const uint8_t* bits;      /* device [E]: K of each expert (2, 3 or 4)                   */
+  const int64_t* code_off;  /* device [E]: byte offset of each unit in codes, 16-aligned  */
+  const uint32_t* codes;    /* device: the units                                          */
+  const uint16_t* scales;   /* device [E][out]: fp16 per-output-channel scales            */
+} tq_trellis_layer;
+
+/*
+ * An MXFP4 expert layer (FORMAT F9). E units back to back, each out*in/2 code bytes
+ * (row = output channel, element 2j in the low nibble of byte j) followed by out*in/32
+ * E8M0 scale bytes (row-major [out][in/32]).
+ */
+typedef struct tq_mxfp4_layer {
+  int32_t E;                /* experts, 1 .. 65535                                        */
+  int32_t out;              /* output channels, multiple of 16                            */
+  int32_t in;               /* inputs, multiple of 256                                    */
+  int32_t reserved;         /* must be 0                                                  */
+  const uint8_t* units;     /* device: E * (out*in/2 + out*in/32) bytes, 16-aligned       */
+} tq_mxfp4_layer;
+
+/*
+ * trellis_expert_gemm — routed activations x trellis-coded expert weights.
+ *
+ *   y[t][k][o] = g[t][k] * f32(scale_e[o]) * sum_i x[t][i] * q_e[i][o],  e = topk_ids[t][k]
+ *
+ * (DeepSeek-V4.1-Flash-1017 · dsx T16 page, "How T16 works" items 1, 2 and 4; FORMAT
+ * F5, F6, F10, F11.) q_e is decoded from the codes inside the kernels; it is never
+ * materialised in memory.
+ *   L         host: the layer description above.
+ *   x         device bf16 [T][L->in], 16-byte aligned rows. Pass the rotated inputs
+ *             (hadamard128 output) for layers encoded with rotated inputs.
+ *   T         tokens (>= 0; T == 0 is a successful no-op).
+ *   topk_ids  device int32 [T][topk]; -1 = empty slot (output zero).
+ *   topk_w    device fp32 [T][topk] gates, or NULL for gate 1.
+ *   topk      slots per token, 1 .. 64.
+ *   y         device fp32, 16-byte aligned: [T][topk][out], or [T][out] with TQ_COMBINE.
+ *   flags     TQ_AUTO / TQ_GEMV / TQ_GEMM, optionally | TQ_COMBINE.
+ *   ws        device workspace of at least tq_workspace_bytes(T, topk, E, out, in, flags)
+ *             bytes, 256-byte aligned, ZERO-FILLED BEFORE ITS FIRST USE. Every call leaves
+ *             its counters at zero again, so a workspace is initialised once and reused;
+ *             calls that share a workspace must be ordered on one stream.
+ * Determinism: results are bitwise reproducible for a given mode and do not depend on
+ * launch timing; a mixed-width layer gives the same bits as single-width layers.
+ * Precondition of the decode-batch kernel: |x| < 65520 (it feeds the matrix cores f16
+ * operands, FORMAT F10).
+ */
+int trellis_expert_gemm(const tq_trellis_layer* L, const void* x, int64_t T,
+                        const int32_t* topk_ids, const float* topk_w, int32_t topk,
+                        float* y, uint32_t flags, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * mxfp4_expert_gemm — routed activations x MXFP4 expert weights.
+ *
+ *   y[t][k][o] = g[t][k] * sum_i x[t][i] * E2M1[c_e[o][i]] * 2^(b_e[o][i/32] - 127)
+ *
+ * (DeepSeek-V4.1-Flash-1017 · exlr8 page, "Stores": FP4 E2M1 values with one E8M0 scale
+ * per 32 inputs; FORMAT F9-F11.) Arguments as trellis_expert_gemm; no per-channel scale.
+ */
+int mxfp4_expert_gemm(const tq_mxfp4_layer* L, const void* x, int64_t T,
+                      const int32_t* topk_ids, const float* topk_w, int32_t topk,
+                      float* y, uint32_t flags, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * hadamard128 — the 128-wide input rotation (FORMAT F8; DeepSeek-V4.1-Flash-1017 · dsx T16
+ * page, "How T16 works", opening paragraph; exlr8 page, "Stores": per-layer signs).
+ * Per block of 128 inputs: v = s * x; seven fp32 butterfly stages (strides 1..64,
+ * (a, b) -> (a + b, a - b)); times fp32 0x3DB504F3; round to nearest-even bf16.
+ *   x      device bf16 [rows][n], 16-byte aligned.
+ *   y      device bf16 [rows][n], 16-byte aligned; may equal x (in place).
+ *   rows   >= 0.   n  multiple of 128.
+ *   signs  device int8 [n] of +1 / -1, or NULL for all +1.
+ */
+int hadamard128(const void* x, void* y, int64_t rows, int64_t n, const int8_t* signs,
+                void* stream);
+
+/*
+ * route_bucket — stable counting sort of the (token, slot) pairs by expert id (FORMAT F11,
+ * F14). The prefill path runs the same kernels internally; this entry point exposes them.
+ *   topk_ids  device int32 [T][topk].
+ *   counts    device int32 [E]: pairs per expert.
+ *   offsets   device int32 [E+1]: exclusive prefix of counts.
+ *   pairs     device int32 [T*topk]: flat slot indices t*topk+k of valid slots ordered by
+ *             (expert, flat index); entries past offsets[E] are left unchanged.
+ *   ws        workspace as for trellis_expert_gemm with TQ_GEMM.
+ */
+int route_bucket(const int32_t* topk_ids, int64_t T, int32_t topk, int32_t E,
+                 int32_t* counts, int32_t* offsets, int32_t* pairs, void* ws,
+                 size_t ws_bytes, void* stream);
+
+/*
+ * trellis_decode — test hook: decode one trellis unit to its integer values with the
+ * same device decoders the GEMV (path 0) or GEMM (path 1) kernels use.
+ *   codes  device, out*in*K/8 bytes, 16-byte aligned.   K in {2, 3, 4}.
+ *   q      device int16 [out][in] (HF orientation: row = output channel).
+ */
+int trellis_decode(const uint32_t* codes, int32_t K, int32_t out, int32_t in, int16_t* q,
+                   int32_t path, void* stream);
+
+/*
+ * mxfp4_decode — test hook: decode one MXFP4 unit to bf16 [out][in] with the device
+ * decoder the MXFP4 kernels use.
+ */
+int mxfp4_decode(const uint8_t* unit, int32_t out, int32_t in, uint16_t* w, void* stream);
+
+/* Workspace bytes the expert GEMM calls (and route_bucket with flags TQ_GEMM) need. */
+size_t tq_workspace_bytes(int64_t T, int32_t topk, int32_t E, int32_t out, int32_t in,
+                          uint32_t flags);
+
+/* Message of the last error on this thread ("" if none). */
+const char* tq_last_error(void);
+
+/* Synchronises `stream`, copies the workspace status word to *flags_out and clears it. */
+int tq_device_status(void* ws, void* stream, uint32_t* flags_out);
+
+/* Library version, major * 10000 + minor * 100 + patch. */
+int tq_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TQ_H */

@@ -134,9 +134,9 @@ def decode_unit(words, K, out, inputs):
         raise ValueError("word count does not match the unit shape")
     # Bits, MSB first per word: write each word big-endian, then unpack bytes MSB first.
     bits = np.unpackbits(w.astype(">u4").view(np.uint8)).reshape(n_to * n_ti, 256 * K)
-    win = bits[:, _window_index(K)].astype(np.int64)          # [tiles, 256, 16]
-    weights = (1 << np.arange(15, -1, -1, dtype=np.int64))    # 2^(15-j)
-    states = win @ weights                                    # [tiles, 256]
+    win = bits[:, _window_index(K)]                           # [tiles, 256, 16], MSB first
+    two = np.packbits(win, axis=-1).astype(np.int64)          # the window as 2 bytes
+    states = two[..., 0] * 256 + two[..., 1]                  # [tiles, 256]
     qt = t16_value_array(states).reshape(n_to, n_ti, TILE, TILE)  # [to, ti, o_l, i_l]
     q = qt.transpose(0, 2, 1, 3).reshape(out, inputs)
     return q.astype(np.int16)

@@ -1,0 +1,90 @@
+"""Helpers for the GPU parity tests: upload seeded workloads, run the oracle on the same
+inputs, compare. The oracle never sees a value the GPU produced except where a test
+compares two GPU results with each other."""
+
+import numpy as np
+import pytest
+
+import oracle
+
+torch = pytest.importorskip("torch")
+
+gpu = pytest.mark.gpu
+needs_gpu = pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")
+
+
+def ops():
+    from trellis_quantized_moe_amd import ops as _ops
+    return _ops
+
+
+def dev():
+    return torch.device("cuda", 0)
+
+
+def to_dev(a, dtype=None):
+    a = np.ascontiguousarray(a)
+    if dtype is not None:
+        a = a.view(dtype)
+    return torch.from_numpy(a).to(dev())
+
+
+def rel_l2(got, ref):
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    return float(np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-300))
+
+
+def trellis_weight_fns(layer):
+    """weight_of / scale_of for the oracle contraction of a host trellis layer."""
+    cache = {}
+
+    def weight_of(e):
+        if e not in cache:
+            K = int(layer["bits"][e])
+            nwords = layer["out"] * layer["in"] * K // 32
+            start = int(layer["code_off"][e]) // 4
+            cache[e] = oracle.decode_unit(layer["codes"][start:start + nwords], K,
+                                          layer["out"], layer["in"]).astype(np.float64)
+        return cache[e]
+
+    scales = oracle.f16_bits_to_f64(layer["scales"])
+
+    def scale_of(e):
+        return scales[e]
+
+    return weight_of, scale_of
+
+
+def mxfp4_weight_fn(layer):
+    ub = oracle.mxfp4_unit_bytes(layer["out"], layer["in"])
+    units = layer["units"].reshape(layer["E"], ub)
+    return lambda e: oracle.decode_mxfp4_unit(units[e], layer["out"], layer["in"])
+
+
+def oracle_trellis(layer, x_rot_bits, ids, gates, sample=None):
+    """FP64 oracle outputs [T, topk, out]; with `sample` (flat slot indices) only those
+    slots are computed (others are zero)."""
+    ids = np.asarray(ids)
+    if sample is not None:
+        keep = np.full(ids.size, -1, dtype=np.int64)
+        keep[sample] = ids.reshape(-1)[sample]
+        ids = keep.reshape(ids.shape)
+    w, s = trellis_weight_fns(layer)
+    return oracle.expert_gemm(x_rot_bits, ids, gates, layer["E"], w, s)
+
+
+def oracle_mxfp4(layer, x_bits, ids, gates, sample=None):
+    ids = np.asarray(ids)
+    if sample is not None:
+        keep = np.full(ids.size, -1, dtype=np.int64)
+        keep[sample] = ids.reshape(-1)[sample]
+        ids = keep.reshape(ids.shape)
+    return oracle.expert_gemm(x_bits, ids, gates, layer["E"], mxfp4_weight_fn(layer), None)
+
+
+def rotate_host(wl):
+    """x~ for a workload: the oracle's fp32-order rotation (FORMAT F8) when it rotates."""
+    if not wl["rotate"]:
+        return wl["x"]
+    return oracle.hadamard128_fp32_order(wl["x"], wl["layer"]["signs"])

@@ -1,0 +1,127 @@
+"""Host-side tests of the C ABI (no GPU): the library loads, exports every function that
+include/tq.h declares, and rejects bad arguments with the documented codes before any
+HIP call (so these run on a machine without a GPU)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from conftest import ROOT
+
+tq = pytest.importorskip("trellis_quantized_moe_amd")
+from trellis_quantized_moe_amd import _lib  # noqa: E402
+
+HEADER = os.path.join(ROOT, "include", "tq.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        pytest.fail("libtq.so is not built: run __graft_entry__.build()")
+    return _lib.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*([a-z_0-9]+)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+def test_every_declared_function_is_exported(lib):
+    names = declared_functions()
+    assert {"trellis_expert_gemm", "mxfp4_expert_gemm", "hadamard128"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+        assert n in _lib.SIGNATURES, n
+
+
+def test_version(lib):
+    assert lib.tq_version() == 100
+
+
+def _layer(E=4, out=128, inp=5120, fake=0x1000):
+    return _lib.TrellisLayerC(E, out, inp, 0, fake, fake, fake, fake)
+
+
+def _call_trellis(lib, layer, T=2, topk=2, x=0x1000, ids=0x1000, y=0x1000, flags=0,
+                  ws=0x10000, ws_bytes=1 << 30):
+    return lib.trellis_expert_gemm(ctypes.byref(layer), x, T, ids, None, topk, y, flags, ws,
+                                   ws_bytes, None)
+
+
+def test_trellis_argument_errors(lib):
+    assert lib.trellis_expert_gemm(None, 0x1000, 1, 0x1000, None, 1, 0x1000, 0, 0x1000, 1 << 30,
+                                   None) == _lib.TQ_EINVAL
+    for bad in (_layer(E=0), _layer(out=24), _layer(inp=200), _layer(E=70000)):
+        assert _call_trellis(lib, bad) == _lib.TQ_EINVAL
+    lay = _layer()
+    lay.reserved = 1
+    assert _call_trellis(lib, lay) == _lib.TQ_EINVAL
+    lay = _layer()
+    lay.codes = 0x1008
+    assert _call_trellis(lib, lay) == _lib.TQ_EALIGN
+    assert _call_trellis(lib, _layer(), topk=0) == _lib.TQ_EINVAL
+    assert _call_trellis(lib, _layer(), topk=65) == _lib.TQ_EINVAL
+    assert _call_trellis(lib, _layer(), T=-1) == _lib.TQ_EINVAL
+    assert _call_trellis(lib, _layer(), T=1 << 30, topk=4) == _lib.TQ_EINVAL
+    assert _call_trellis(lib, _layer(), flags=3) == _lib.TQ_EINVAL
+    assert _call_trellis(lib, _layer(), flags=8) == _lib.TQ_EINVAL
+    assert _call_trellis(lib, _layer(), x=0x1002) == _lib.TQ_EALIGN
+    assert _call_trellis(lib, _layer(), y=0) == _lib.TQ_EINVAL
+    assert _call_trellis(lib, _layer(), ids=0) == _lib.TQ_EINVAL
+    assert _call_trellis(lib, _layer(), ws=0) == _lib.TQ_EWORKSPACE
+    assert _call_trellis(lib, _layer(), ws=0x10010) == _lib.TQ_EALIGN
+    assert _call_trellis(lib, _layer(), ws_bytes=16) == _lib.TQ_EWORKSPACE
+    assert b"workspace" in lib.tq_last_error()
+    # the prefill path is limited to E <= 4096
+    assert _call_trellis(lib, _layer(E=5000), T=100000, topk=8, flags=_lib.TQ_GEMM) == _lib.TQ_EINVAL
+
+
+def test_empty_batch_is_a_no_op(lib):
+    # T == 0 succeeds without touching the device (no workspace needed either)
+    assert _call_trellis(lib, _layer(), T=0, x=0, ids=0, y=0, ws=0, ws_bytes=0) == _lib.TQ_OK
+    assert lib.tq_last_error() == b""
+    m = _lib.Mxfp4LayerC(4, 128, 5120, 0, 0x1000)
+    assert lib.mxfp4_expert_gemm(ctypes.byref(m), 0, 0, 0, None, 8, 0, 0, 0, 0, None) == _lib.TQ_OK
+    assert lib.hadamard128(0, 0, 0, 128, None, None) == _lib.TQ_OK
+
+
+def test_mxfp4_argument_errors(lib):
+    m = _lib.Mxfp4LayerC(4, 128, 5120 + 256, 0, 0x1000)
+    assert lib.mxfp4_expert_gemm(ctypes.byref(m), 0x1000, 1, 0x1000, None, 1, 0x1000, 0, 0x1000,
+                                 1 << 30, None) == _lib.TQ_EINVAL
+    m = _lib.Mxfp4LayerC(4, 128, 5120, 0, 0x1001)
+    assert lib.mxfp4_expert_gemm(ctypes.byref(m), 0x1000, 1, 0x1000, None, 1, 0x1000, 0, 0x1000,
+                                 1 << 30, None) == _lib.TQ_EALIGN
+
+
+def test_hadamard_decode_route_argument_errors(lib):
+    assert lib.hadamard128(0x1000, 0x1000, 1, 100, None, None) == _lib.TQ_EINVAL
+    assert lib.hadamard128(0x1000, 0x1000, -1, 128, None, None) == _lib.TQ_EINVAL
+    assert lib.hadamard128(0x1001, 0x1000, 1, 128, None, None) == _lib.TQ_EALIGN
+    assert lib.hadamard128(0x1000, 0x1000, 1, 128, 0x1004, None) == _lib.TQ_EALIGN
+    assert lib.trellis_decode(0x1000, 5, 16, 64, 0x1000, 0, None) == _lib.TQ_EINVAL
+    assert lib.trellis_decode(0x1000, 2, 17, 64, 0x1000, 0, None) == _lib.TQ_EINVAL
+    assert lib.trellis_decode(0x1000, 2, 16, 48, 0x1000, 0, None) == _lib.TQ_EINVAL
+    assert lib.trellis_decode(0x1000, 2, 16, 64, 0x1000, 2, None) == _lib.TQ_EINVAL
+    assert lib.trellis_decode(0x1004, 2, 16, 64, 0x1000, 0, None) == _lib.TQ_EALIGN
+    assert lib.mxfp4_decode(0x1000, 16, 48, 0x1000, None) == _lib.TQ_EINVAL
+    assert lib.route_bucket(0x1000, 4, 2, 0, 0x1000, 0x1000, 0x1000, 0x1000, 1 << 20, None) == _lib.TQ_EINVAL
+    assert lib.route_bucket(0x1000, 4, 2, 5000, 0x1000, 0x1000, 0x1000, 0x1000, 1 << 20, None) == _lib.TQ_EINVAL
+    assert lib.route_bucket(0x1000, 4, 2, 8, 0x1000, 0x1000, 0x1000, 0x1000, 8, None) == _lib.TQ_EWORKSPACE
+    v = ctypes.c_uint32(0)
+    assert lib.tq_device_status(None, None, ctypes.byref(v)) == _lib.TQ_EINVAL
+
+
+def test_workspace_sizes(lib):
+    # decode batch: counters + slice partials; prefill: route buffers and items
+    gemv = lib.tq_workspace_bytes(128, 8, 384, 128, 5120, _lib.TQ_AUTO)
+    gemm = lib.tq_workspace_bytes(8192, 8, 384, 128, 5120, _lib.TQ_AUTO)
+    assert gemv >= 256 + 384 * 4 + 4 * 1024 * 128 * 4
+    assert gemm >= 256 + 8192 * 8 * 4 * 2 + (8192 * 8 // 128 + 384) * 16
+    comb = lib.tq_workspace_bytes(8192, 8, 384, 128, 5120, _lib.TQ_COMBINE)
+    assert comb >= gemm + 8192 * 8 * 128 * 4
+    assert lib.tq_workspace_bytes(-1, 8, 384, 128, 5120, 0) == 0

@@ -1,0 +1,251 @@
+"""Trellis expert GEMV / GEMM on the GPU vs the FP64 oracle (relative L2 <= 1e-3, the bound
+the FORMAT note fixes), plus the structural invariants: determinism, token permutation,
+mixed width == single width, empty and invalid slots, combine, graph replay."""
+
+import numpy as np
+import pytest
+
+import oracle
+from gpu_helpers import (dev, gpu, needs_gpu, ops, oracle_trellis, rel_l2, rotate_host, to_dev,
+                         torch)
+from workloads import (bf16_from_normal, mixed_layer, one_unit, prefill_chunk, rng_for,
+                       single_matrix, softmax_gates, trellis_layer, uniform_routes, zipf_routes)
+
+pytestmark = [gpu, needs_gpu]
+TOL = 1e-3
+
+
+def run(layer_h, x_bits, ids, gates=None, flags=0, rotate_signs=None):
+    o = ops()
+    L = o.TrellisLayer.from_host(layer_h)
+    x = to_dev(x_bits, np.int16)
+    if rotate_signs is not None:
+        x = o.hadamard128(x, to_dev(rotate_signs))
+    y = o.trellis_expert_gemm(L, x, to_dev(ids), None if gates is None else to_dev(gates),
+                              flags=flags)
+    torch.cuda.synchronize()
+    return y.cpu().numpy().astype(np.float64)
+
+
+def small_layer(seed, E, out, inp, widths=None):
+    w = np.asarray(widths if widths is not None else rng_for(seed, 9).integers(2, 5, size=E),
+                   dtype=np.uint8)
+    return trellis_layer(seed, w, out, inp, with_signs=True)
+
+
+def test_single_matrix_256():
+    wl = single_matrix()
+    y = run(wl["layer"], wl["x"], wl["topk_ids"])
+    ref = oracle_trellis(wl["layer"], wl["x"], wl["topk_ids"], None)
+    assert rel_l2(y, ref) <= TOL
+
+
+@pytest.mark.parametrize("K", [2, 3, 4])
+@pytest.mark.parametrize("T", [1, 4, 16])
+def test_one_unit_rotated(K, T):
+    wl = one_unit(K, T)
+    y = run(wl["layer"], wl["x"], wl["topk_ids"], rotate_signs=wl["layer"]["signs"])
+    ref = oracle_trellis(wl["layer"], rotate_host(wl), wl["topk_ids"], None)
+    assert rel_l2(y, ref) <= TOL
+    # per output as well: no slot may hide a large error behind the others
+    err = np.abs(y - ref).max() / np.abs(ref).max()
+    assert err <= 1e-3
+
+
+@pytest.mark.parametrize("flags", [1, 2])
+def test_small_mixed_layer_both_modes(flags):
+    E, T, topk = 9, 70, 4
+    layer = small_layer(400, E, 128, 1024)
+    x = bf16_from_normal(rng_for(400, 1), (T, 1024))
+    ids = uniform_routes(rng_for(400, 2), T, E, topk)
+    ids[3, 1] = -1
+    ids[10, :] = -1
+    gates = softmax_gates(rng_for(400, 3), T, topk)
+    y = run(layer, x, ids, gates, flags=flags)
+    ref = oracle_trellis(layer, x, ids, gates)
+    assert rel_l2(y, ref) <= TOL
+    assert np.all(y[3, 1] == 0) and np.all(y[10] == 0)
+
+
+def test_many_tokens_per_expert_in_gemv_mode():
+    # more than 16 tokens per expert forces several chunks in the decode-batch kernel
+    E, T, topk = 3, 50, 2
+    layer = small_layer(401, E, 256, 512, widths=[2, 3, 4])
+    x = bf16_from_normal(rng_for(401, 1), (T, 512))
+    ids = uniform_routes(rng_for(401, 2), T, E, topk)
+    y1 = run(layer, x, ids, flags=1)
+    y2 = run(layer, x, ids, flags=2)
+    ref = oracle_trellis(layer, x, ids, None)
+    assert rel_l2(y1, ref) <= TOL and rel_l2(y2, ref) <= TOL
+
+
+def test_one_hot_reproduces_decoded_columns():
+    layer = small_layer(402, 2, 32, 256, widths=[3, 2])
+    x = np.zeros((6, 256), dtype=np.uint16)
+    cols = [0, 17, 100, 128, 201, 255]
+    for t, c in enumerate(cols):
+        x[t, c] = 0x3F80
+    ids = np.array([[0], [1], [0], [1], [0], [1]], dtype=np.int32)
+    for flags in (1, 2):
+        y = run(layer, x, ids, flags=flags)
+        sc = oracle.f16_bits_to_f64(layer["scales"]).astype(np.float32)
+        for t, c in enumerate(cols):
+            e = ids[t, 0]
+            K = int(layer["bits"][e])
+            nw = 32 * 256 * K // 32
+            off = int(layer["code_off"][e]) // 4
+            q = oracle.decode_unit(layer["codes"][off:off + nw], K, 32, 256)
+            expect = (q[:, c].astype(np.float32) * sc[e]).astype(np.float64)
+            assert np.array_equal(y[t, 0], expect), (flags, t)
+
+
+def test_empty_invalid_and_status():
+    o = ops()
+    layer = small_layer(403, 4, 128, 512)
+    L = o.TrellisLayer.from_host(layer)
+    x = to_dev(bf16_from_normal(rng_for(403, 1), (5, 512)), np.int16)
+    ids_h = np.array([[0, -1], [7, 1], [2, -5], [3, 3], [-1, -1]], dtype=np.int32)
+    for flags in (1, 2):
+        ws = o.workspace(5, 2, 4, 128, 512, flags)
+        y = o.trellis_expert_gemm(L, x, to_dev(ids_h), flags=flags, ws=ws).cpu().numpy()
+        assert np.all(y[0, 1] == 0) and np.all(y[4] == 0)
+        assert np.all(np.isnan(y[1, 0])) and np.all(np.isnan(y[2, 1]))
+        assert np.all(np.isfinite(y[0, 0])) and np.all(np.isfinite(y[3]))
+        assert o.device_status(ws) == 1
+        assert o.device_status(ws) == 0
+
+
+def test_bad_unit_descriptor_gives_nan():
+    o = ops()
+    layer = small_layer(404, 3, 128, 512, widths=[2, 2, 2])
+    layer["bits"] = layer["bits"].copy()
+    layer["bits"][1] = 5
+    L = o.TrellisLayer.from_host(layer)
+    x = to_dev(bf16_from_normal(rng_for(404, 1), (4, 512)), np.int16)
+    ids = to_dev(np.array([[0], [1], [2], [1]], dtype=np.int32))
+    for flags in (1, 2):
+        ws = o.workspace(4, 1, 3, 128, 512, flags)
+        y = o.trellis_expert_gemm(L, x, ids, flags=flags, ws=ws).cpu().numpy()
+        assert np.all(np.isnan(y[1])) and np.all(np.isnan(y[3]))
+        assert np.all(np.isfinite(y[0])) and np.all(np.isfinite(y[2]))
+        assert o.device_status(ws) == 2
+
+
+def test_combine_matches_slot_sum():
+    E, T, topk = 6, 33, 3
+    layer = small_layer(405, E, 128, 512)
+    x = bf16_from_normal(rng_for(405, 1), (T, 512))
+    ids = uniform_routes(rng_for(405, 2), T, E, topk)
+    gates = softmax_gates(rng_for(405, 3), T, topk)
+    for flags in (1, 2):
+        slots = run(layer, x, ids, gates, flags=flags)
+        comb = run(layer, x, ids, gates, flags=flags | 4)
+        expect = np.zeros_like(comb)
+        for k in range(topk):   # same fp32 additions, same order
+            expect = (expect.astype(np.float32) + slots[:, k].astype(np.float32)).astype(np.float64)
+        assert np.array_equal(comb, expect)
+        ref = oracle.combine_slots(oracle_trellis(layer, x, ids, gates))
+        assert rel_l2(comb, ref) <= TOL
+
+
+def test_deterministic_and_token_permutation():
+    E, T, topk = 12, 64, 8
+    layer = small_layer(406, E, 128, 1024)
+    x = bf16_from_normal(rng_for(406, 1), (T, 1024))
+    ids = uniform_routes(rng_for(406, 2), T, E, topk)
+    for flags in (1, 2):
+        a = run(layer, x, ids, flags=flags)
+        b = run(layer, x, ids, flags=flags)
+        assert np.array_equal(a, b)
+        perm = rng_for(406, 3).permutation(T)
+        c = run(layer, x[perm], ids[perm], flags=flags)
+        assert np.array_equal(c, a[perm])
+
+
+def test_mixed_width_equals_single_width_launches():
+    E, T, topk = 10, 40, 4
+    widths = np.array([2, 3, 4, 2, 2, 3, 4, 2, 3, 2], dtype=np.uint8)
+    mixed = small_layer(407, E, 128, 512, widths=widths)
+    x = bf16_from_normal(rng_for(407, 1), (T, 512))
+    ids = uniform_routes(rng_for(407, 2), T, E, topk)
+    for flags in (1, 2):
+        y_mixed = run(mixed, x, ids, flags=flags)
+        for K in (2, 3, 4):
+            # a single-width layer: width-K experts keep their units, the others get fresh
+            # width-K units and no routes
+            single = small_layer(408 + K, E, 128, 512, widths=np.full(E, K, np.uint8))
+            codes = single["codes"].copy()
+            for e in range(E):
+                if widths[e] == K:
+                    n = 128 * 512 * K // 32
+                    src = int(mixed["code_off"][e]) // 4
+                    dst = int(single["code_off"][e]) // 4
+                    codes[dst:dst + n] = mixed["codes"][src:src + n]
+            single["codes"] = codes
+            single["scales"] = mixed["scales"]
+            ids_k = np.where(widths[ids] == K, ids, -1).astype(np.int32)
+            y_k = run(single, x, ids_k, flags=flags)
+            sel = widths[ids] == K
+            assert np.array_equal(y_k[sel], y_mixed[sel]), (flags, K)
+
+
+def test_graph_replay_with_changing_routes():
+    o = ops()
+    E, T, topk = 16, 24, 4
+    layer = small_layer(409, E, 128, 512)
+    L = o.TrellisLayer.from_host(layer)
+    x = to_dev(bf16_from_normal(rng_for(409, 1), (T, 512)), np.int16)
+    ids = to_dev(uniform_routes(rng_for(409, 2), T, E, topk))
+    for flags in (1, 2):
+        ws = o.workspace(T, topk, E, 128, 512, flags)
+        y = torch.empty((T, topk, 128), dtype=torch.float32, device=dev())
+        o.trellis_expert_gemm(L, x, ids, flags=flags, out=y, ws=ws)  # warm up
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            o.trellis_expert_gemm(L, x, ids, flags=flags, out=y, ws=ws)
+        for r in range(3):
+            new = uniform_routes(rng_for(409, 10 + r), T, E, topk)
+            ids.copy_(to_dev(new))
+            g.replay()
+            torch.cuda.synchronize()
+            got = y.cpu().numpy()
+            eager = o.trellis_expert_gemm(L, x, ids, flags=flags).cpu().numpy()
+            assert np.array_equal(got, eager), (flags, r)
+            ref = oracle_trellis(layer, x.cpu().numpy().view(np.uint16), new, None)
+            assert rel_l2(got, ref) <= TOL
+
+
+def test_mixed_layer_full_size_sampled():
+    wl = mixed_layer()
+    layer = wl["layer"]
+    y = run(layer, wl["x"], wl["topk_ids"], rotate_signs=layer["signs"])
+    xr = rotate_host(wl)
+    ids = wl["topk_ids"]
+    flat = ids.reshape(-1)
+    wide = np.nonzero(layer["bits"][flat] > 2)[0]
+    sample = np.unique(np.concatenate([wide, rng_for(410, 0).choice(flat.size, 24, replace=False)]))
+    ref = oracle_trellis(layer, xr, ids, None, sample=sample)
+    got = y.reshape(-1, 128)[sample]
+    assert rel_l2(got, ref.reshape(-1, 128)[sample]) <= TOL
+    assert np.all(np.isfinite(y))
+
+
+def test_prefill_chunk_full_size_sampled():
+    wl = prefill_chunk()
+    layer = wl["layer"]
+    y = run(layer, wl["x"], wl["topk_ids"], rotate_signs=layer["signs"])
+    assert np.all(np.isfinite(y))
+    xr = rotate_host(wl)
+    ids = wl["topk_ids"]
+    flat = ids.reshape(-1)
+    rng = rng_for(411, 0)
+    # slots of the most and least popular experts plus random ones
+    counts = np.bincount(flat, minlength=384)
+    top, low = np.argmax(counts), np.argmin(np.where(counts > 0, counts, 1 << 30))
+    sample = np.unique(np.concatenate([
+        rng.choice(np.nonzero(flat == top)[0], 8, replace=False),
+        np.nonzero(flat == low)[0][:8],
+        rng.choice(flat.size, 16, replace=False)]))
+    ref = oracle_trellis(layer, xr, ids, None, sample=sample)
+    assert rel_l2(y.reshape(-1, 128)[sample], ref.reshape(-1, 128)[sample]) <= TOL

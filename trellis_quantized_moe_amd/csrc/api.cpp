@@ -1,0 +1,486 @@
+// C ABI of the library (include/tq.h): argument checks, workspace layout and dispatch.
+// Every check runs before the first HIP call of an entry point.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "../../include/tq.h"
+#include "tq_internal.h"
+
+namespace {
+
+thread_local std::string g_error;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_error = buf;
+  return code;
+}
+
+int ok() {
+  g_error.clear();
+  return TQ_OK;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+int hip_fail(hipError_t err, const char* what) {
+  return fail(TQ_EHIP, "%s: %s", what, hipGetErrorString(err));
+}
+
+// gfx950 check, cached per device.
+int check_device() {
+  static int cache[64];  // 0 unknown, 1 ok, 2 unsupported
+  int dev = 0;
+  hipError_t err = hipGetDevice(&dev);
+  if (err != hipSuccess) return hip_fail(err, "hipGetDevice");
+  if (dev >= 0 && dev < 64 && cache[dev] == 1) return TQ_OK;
+  hipDeviceProp_t prop;
+  err = hipGetDeviceProperties(&prop, dev);
+  if (err != hipSuccess) return hip_fail(err, "hipGetDeviceProperties");
+  const bool good = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+  if (dev >= 0 && dev < 64) cache[dev] = good ? 1 : 2;
+  if (!good) return fail(TQ_EUNSUPPORTED, "device %d is %s; this library is built for gfx950",
+                         dev, prop.gcnArchName);
+  return TQ_OK;
+}
+
+bool flags_valid(uint32_t flags) {
+  return (flags & ~7u) == 0 && (flags & 3u) != 3u;
+}
+
+bool use_gemm(int64_t T, int topk, int E, uint32_t flags) {
+  const uint32_t mode = flags & 3u;
+  if (mode == TQ_GEMV) return false;
+  if (mode == TQ_GEMM) return true;
+  return T * topk > 16LL * E;
+}
+
+// Largest number of steps per workgroup (a divisor of units, at most max_steps) that still
+// leaves at least target K-slices; 1 if none does.
+int pick_steps(int units, int max_steps, int target_slices) {
+  int best = 1;
+  for (int d = 1; d <= max_steps; ++d)
+    if (units % d == 0 && units / d >= target_slices) best = d;
+  return best;
+}
+
+int check_routes(int64_t T, int topk, const void* ids) {
+  if (T < 0) return fail(TQ_EINVAL, "T = %lld is negative", (long long)T);
+  if (topk < 1 || topk > 64) return fail(TQ_EINVAL, "topk = %d is outside 1..64", topk);
+  if (T * (int64_t)topk >= (int64_t)1 << 31)
+    return fail(TQ_EINVAL, "T * topk = %lld does not fit in int32", (long long)(T * topk));
+  if (T > 0 && !ids) return fail(TQ_EINVAL, "topk_ids is NULL");
+  return TQ_OK;
+}
+
+int check_io(int64_t T, const void* x, const float* y) {
+  if (T == 0) return TQ_OK;
+  if (!x || !y) return fail(TQ_EINVAL, "x or y is NULL");
+  if (!aligned(x, 16) || !aligned(y, 16))
+    return fail(TQ_EALIGN, "x and y must be 16-byte aligned");
+  return TQ_OK;
+}
+
+int check_ws(void* ws, size_t ws_bytes, size_t need) {
+  if (!ws) return fail(TQ_EWORKSPACE, "workspace is NULL");
+  if (!aligned(ws, 256)) return fail(TQ_EALIGN, "workspace must be 256-byte aligned");
+  if (ws_bytes < need)
+    return fail(TQ_EWORKSPACE, "workspace has %zu bytes, %zu needed", ws_bytes, need);
+  return TQ_OK;
+}
+
+template <class T>
+T* at(void* ws, size_t off) {
+  return reinterpret_cast<T*>(static_cast<char*>(ws) + off);
+}
+
+}  // namespace
+
+namespace tq {
+
+WsLayout ws_layout(int64_t T, int topk, int E, int out, int in, uint32_t flags, bool mxfp4) {
+  WsLayout L;
+  const int64_t N = T * topk;
+  L.groups = (out + 127) / 128;
+  L.gemm = use_gemm(T, topk, E, flags);
+  size_t off = 256;  // status word
+  if (!L.gemm) {
+    const int64_t active = N < E ? N : E;
+    const int64_t wgs_per_slice = (active > 0 ? active : 1) * L.groups;
+    const int target = (int)((2048 + wgs_per_slice - 1) / wgs_per_slice);
+    if (mxfp4) {
+      const int units = in / 512;
+      L.gemv_steps = pick_steps(units, 2, target);
+      L.gemv_slices = units / L.gemv_steps;
+    } else {
+      const int units = in / 256;
+      L.gemv_steps = pick_steps(units, 5, target);
+      L.gemv_slices = units / L.gemv_steps;
+    }
+    L.counters = off;
+    L.counters_bytes = round_up((size_t)E * L.groups * 4, 256);
+    off += L.counters_bytes;
+    if (L.gemv_slices > 1) {
+      L.partial = off;
+      L.partial_bytes = round_up((size_t)L.gemv_slices * N * out * 4, 256);
+      off += L.partial_bytes;
+    }
+  } else {
+    L.route_blocks = (int)((N + ROUTE_CHUNK - 1) / ROUTE_CHUNK);
+    L.max_items = (int)((N + GEMM_MT - 1) / GEMM_MT) + E;
+    const size_t start = off;
+    L.counts = off;
+    off += round_up((size_t)E * 4, 256);
+    L.offsets = off;
+    off += round_up((size_t)(E + 1) * 4, 256);
+    L.hist = off;
+    off += round_up((size_t)L.route_blocks * E * 4, 256);
+    L.rank = off;
+    off += round_up((size_t)N * 4, 256);
+    L.pairs = off;
+    off += round_up((size_t)N * 4, 256);
+    L.items = off;
+    off += round_up((size_t)L.max_items * 16, 256);
+    L.n_items = off;
+    off += 256;
+    L.route_bytes = off - start;
+  }
+  if (flags & TQ_COMBINE) {
+    L.slots = off;
+    L.slots_bytes = round_up((size_t)N * out * 4, 256);
+    off += L.slots_bytes;
+  }
+  L.total = off;
+  return L;
+}
+
+}  // namespace tq
+
+extern "C" {
+
+size_t tq_workspace_bytes(int64_t T, int32_t topk, int32_t E, int32_t out, int32_t in,
+                          uint32_t flags) {
+  if (T < 0 || topk < 1 || E < 1 || out < 16 || in < 256) return 0;
+  const tq::WsLayout a = tq::ws_layout(T, topk, E, out, in, flags, false);
+  const tq::WsLayout b = tq::ws_layout(T, topk, E, out, in, flags, true);
+  return a.total > b.total ? a.total : b.total;
+}
+
+const char* tq_last_error(void) { return g_error.c_str(); }
+
+int tq_version(void) { return 100; }
+
+int tq_device_status(void* ws, void* stream, uint32_t* flags_out) {
+  if (!ws || !flags_out) return fail(TQ_EINVAL, "ws and flags_out must not be NULL");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t err = hipStreamSynchronize(s);
+  if (err != hipSuccess) return hip_fail(err, "hipStreamSynchronize");
+  uint32_t v = 0;
+  err = hipMemcpy(&v, ws, 4, hipMemcpyDeviceToHost);
+  if (err != hipSuccess) return hip_fail(err, "hipMemcpy");
+  err = hipMemset(ws, 0, 4);
+  if (err != hipSuccess) return hip_fail(err, "hipMemset");
+  *flags_out = v;
+  return ok();
+}
+
+int hadamard128(const void* x, void* y, int64_t rows, int64_t n, const int8_t* signs,
+                void* stream) {
+  if (rows < 0) return fail(TQ_EINVAL, "rows = %lld is negative", (long long)rows);
+  if (n <= 0 || n % 128) return fail(TQ_EINVAL, "n = %lld is not a positive multiple of 128",
+                                     (long long)n);
+  if (rows == 0) return ok();
+  if (!x || !y) return fail(TQ_EINVAL, "x or y is NULL");
+  if (!aligned(x, 16) || !aligned(y, 16)) return fail(TQ_EALIGN, "x and y must be 16-byte aligned");
+  if (signs && !aligned(signs, 8)) return fail(TQ_EALIGN, "signs must be 8-byte aligned");
+  int rc = check_device();
+  if (rc) return rc;
+  hipError_t err = tq::launch_hadamard(static_cast<const uint16_t*>(x), static_cast<uint16_t*>(y),
+                                       rows, n, signs, static_cast<hipStream_t>(stream));
+  if (err != hipSuccess) return hip_fail(err, "hadamard128 launch");
+  return ok();
+}
+
+int trellis_decode(const uint32_t* codes, int32_t K, int32_t out, int32_t in, int16_t* q,
+                   int32_t path, void* stream) {
+  if (K < 2 || K > 4) return fail(TQ_EINVAL, "K = %d is not 2, 3 or 4", K);
+  if (out <= 0 || out % 16) return fail(TQ_EINVAL, "out = %d is not a positive multiple of 16", out);
+  if (in <= 0 || in % 64) return fail(TQ_EINVAL, "in = %d is not a positive multiple of 64", in);
+  if (path != 0 && path != 1) return fail(TQ_EINVAL, "path = %d is not 0 or 1", path);
+  if (!codes || !q) return fail(TQ_EINVAL, "codes or q is NULL");
+  if (!aligned(codes, 16)) return fail(TQ_EALIGN, "codes must be 16-byte aligned");
+  if (!aligned(q, 4)) return fail(TQ_EALIGN, "q must be 4-byte aligned");
+  int rc = check_device();
+  if (rc) return rc;
+  hipError_t err = tq::launch_trellis_decode(codes, K, out, in, q, path,
+                                             static_cast<hipStream_t>(stream));
+  if (err != hipSuccess) return hip_fail(err, "trellis_decode launch");
+  return ok();
+}
+
+int mxfp4_decode(const uint8_t* unit, int32_t out, int32_t in, uint16_t* w, void* stream) {
+  if (out <= 0) return fail(TQ_EINVAL, "out = %d is not positive", out);
+  if (in <= 0 || in % 32) return fail(TQ_EINVAL, "in = %d is not a positive multiple of 32", in);
+  if (!unit || !w) return fail(TQ_EINVAL, "unit or w is NULL");
+  if (!aligned(unit, 16) || !aligned(w, 16)) return fail(TQ_EALIGN, "unit and w must be 16-byte aligned");
+  int rc = check_device();
+  if (rc) return rc;
+  hipError_t err = tq::launch_mxfp4_decode(unit, out, in, w, static_cast<hipStream_t>(stream));
+  if (err != hipSuccess) return hip_fail(err, "mxfp4_decode launch");
+  return ok();
+}
+
+int route_bucket(const int32_t* topk_ids, int64_t T, int32_t topk, int32_t E, int32_t* counts,
+                 int32_t* offsets, int32_t* pairs, void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_routes(T, topk, topk_ids);
+  if (rc) return rc;
+  if (E < 1 || E > 4096) return fail(TQ_EINVAL, "E = %d is outside 1..4096", E);
+  if (!counts || !offsets || (T > 0 && !pairs)) return fail(TQ_EINVAL, "an output is NULL");
+  const tq::WsLayout L = tq::ws_layout(T, topk, E, 16, 256, TQ_GEMM, false);
+  rc = check_ws(ws, ws_bytes, L.total);
+  if (rc) return rc;
+  rc = check_device();
+  if (rc) return rc;
+  tq::RouteArgs r{};
+  r.ids = topk_ids;
+  r.N = T * topk;
+  r.E = E;
+  r.out = 16;
+  r.counts = counts;
+  r.offsets = offsets;
+  r.hist = at<int32_t>(ws, L.hist);
+  r.rank = at<int32_t>(ws, L.rank);
+  r.pairs = pairs;
+  r.items = nullptr;
+  r.n_items = nullptr;
+  r.y_special = nullptr;
+  r.status = at<uint32_t>(ws, L.status);
+  r.blocks = L.route_blocks;
+  r.item_rows = tq::GEMM_MT;
+  r.max_items = 0;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t err;
+  if (r.N == 0) {
+    // no slots: counts and offsets are all zero (a fill kernel, so graphs may capture it)
+    err = tq::launch_fill_i32(counts, E, 0, s);
+    if (err == hipSuccess) err = tq::launch_fill_i32(offsets, E + 1, 0, s);
+  } else {
+    err = tq::launch_route(r, s);
+  }
+  if (err != hipSuccess) return hip_fail(err, "route_bucket launch");
+  return ok();
+}
+
+namespace {
+
+int check_trellis_layer(const tq_trellis_layer* L) {
+  if (!L) return fail(TQ_EINVAL, "layer is NULL");
+  if (L->E < 1 || L->E > 65535) return fail(TQ_EINVAL, "E = %d is outside 1..65535", L->E);
+  if (L->out <= 0 || L->out % 16) return fail(TQ_EINVAL, "out = %d is not a positive multiple of 16", L->out);
+  if (L->in <= 0 || L->in % 256) return fail(TQ_EINVAL, "in = %d is not a positive multiple of 256", L->in);
+  if (L->reserved != 0) return fail(TQ_EINVAL, "reserved field must be 0");
+  if (!L->bits || !L->code_off || !L->codes || !L->scales)
+    return fail(TQ_EINVAL, "a layer pointer is NULL");
+  if (!aligned(L->codes, 16)) return fail(TQ_EALIGN, "codes must be 16-byte aligned");
+  if (!aligned(L->code_off, 8)) return fail(TQ_EALIGN, "code_off must be 8-byte aligned");
+  if (!aligned(L->scales, 2)) return fail(TQ_EALIGN, "scales must be 2-byte aligned");
+  return TQ_OK;
+}
+
+int check_mxfp4_layer(const tq_mxfp4_layer* L) {
+  if (!L) return fail(TQ_EINVAL, "layer is NULL");
+  if (L->E < 1 || L->E > 65535) return fail(TQ_EINVAL, "E = %d is outside 1..65535", L->E);
+  if (L->out <= 0 || L->out % 16) return fail(TQ_EINVAL, "out = %d is not a positive multiple of 16", L->out);
+  if (L->in <= 0 || L->in % 512) return fail(TQ_EINVAL, "in = %d is not a positive multiple of 512", L->in);
+  if (L->reserved != 0) return fail(TQ_EINVAL, "reserved field must be 0");
+  if (!L->units) return fail(TQ_EINVAL, "units is NULL");
+  if (!aligned(L->units, 16)) return fail(TQ_EALIGN, "units must be 16-byte aligned");
+  return TQ_OK;
+}
+
+// Shared front half of the two expert GEMM calls.
+int common_checks(int E, int out, int in, const void* x, int64_t T, const int32_t* ids,
+                  int32_t topk, float* y, uint32_t flags, void* ws, size_t ws_bytes, bool mxfp4,
+                  tq::WsLayout* layout) {
+  int rc = check_routes(T, topk, ids);
+  if (rc) return rc;
+  if (!flags_valid(flags)) return fail(TQ_EINVAL, "flags = 0x%x is not valid", flags);
+  rc = check_io(T, x, y);
+  if (rc) return rc;
+  *layout = tq::ws_layout(T, topk, E, out, in, flags, mxfp4);
+  if (layout->gemm && E > 4096)
+    return fail(TQ_EINVAL, "the prefill path supports E <= 4096 (E = %d)", E);
+  if (T == 0) return TQ_OK;
+  return check_ws(ws, ws_bytes, layout->total);
+}
+
+int run_route(const tq::WsLayout& L, void* ws, const int32_t* ids, int64_t N, int E, int out,
+              float* y_slots, hipStream_t s) {
+  tq::RouteArgs r{};
+  r.ids = ids;
+  r.N = N;
+  r.E = E;
+  r.out = out;
+  r.counts = at<int32_t>(ws, L.counts);
+  r.offsets = at<int32_t>(ws, L.offsets);
+  r.hist = at<int32_t>(ws, L.hist);
+  r.rank = at<int32_t>(ws, L.rank);
+  r.pairs = at<int32_t>(ws, L.pairs);
+  r.items = at<int32_t>(ws, L.items);
+  r.n_items = at<int32_t>(ws, L.n_items);
+  r.y_special = y_slots;
+  r.status = at<uint32_t>(ws, L.status);
+  r.blocks = L.route_blocks;
+  r.item_rows = tq::GEMM_MT;
+  r.max_items = L.max_items;
+  hipError_t err = tq::launch_route(r, s);
+  if (err != hipSuccess) return hip_fail(err, "route launch");
+  return TQ_OK;
+}
+
+}  // namespace
+
+int trellis_expert_gemm(const tq_trellis_layer* L, const void* x, int64_t T,
+                        const int32_t* topk_ids, const float* topk_w, int32_t topk, float* y,
+                        uint32_t flags, void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_trellis_layer(L);
+  if (rc) return rc;
+  tq::WsLayout W;
+  rc = common_checks(L->E, L->out, L->in, x, T, topk_ids, topk, y, flags, ws, ws_bytes, false, &W);
+  if (rc) return rc;
+  if (T == 0) return ok();
+  rc = check_device();
+  if (rc) return rc;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int64_t N = T * topk;
+  float* y_slots = (flags & TQ_COMBINE) ? at<float>(ws, W.slots) : y;
+  const uint16_t* xb = static_cast<const uint16_t*>(x);
+  hipError_t err;
+  if (!W.gemm) {
+    tq::TrellisGemvArgs a{};
+    a.bits = L->bits;
+    a.code_off = L->code_off;
+    a.codes = L->codes;
+    a.scales = L->scales;
+    a.x = xb;
+    a.ids = topk_ids;
+    a.gates = topk_w;
+    a.y = y_slots;
+    a.partial = W.gemv_slices > 1 ? at<float>(ws, W.partial) : nullptr;
+    a.counters = at<int32_t>(ws, W.counters);
+    a.status = at<uint32_t>(ws, W.status);
+    a.E = L->E;
+    a.out = L->out;
+    a.in = L->in;
+    a.topk = topk;
+    a.S = W.gemv_slices;
+    a.steps = W.gemv_steps;
+    a.groups = W.groups;
+    a.N = N;
+    err = tq::launch_trellis_gemv(a, s);
+    if (err != hipSuccess) return hip_fail(err, "trellis GEMV launch");
+  } else {
+    rc = run_route(W, ws, topk_ids, N, L->E, L->out, y_slots, s);
+    if (rc) return rc;
+    tq::TrellisGemmArgs a{};
+    a.bits = L->bits;
+    a.code_off = L->code_off;
+    a.codes = L->codes;
+    a.scales = L->scales;
+    a.x = xb;
+    a.gates = topk_w;
+    a.pairs = at<int32_t>(ws, W.pairs);
+    a.items = at<int32_t>(ws, W.items);
+    a.n_items = at<int32_t>(ws, W.n_items);
+    a.y = y_slots;
+    a.status = at<uint32_t>(ws, W.status);
+    a.E = L->E;
+    a.out = L->out;
+    a.in = L->in;
+    a.topk = topk;
+    a.groups = W.groups;
+    a.max_items = W.max_items;
+    err = tq::launch_trellis_gemm(a, s);
+    if (err != hipSuccess) return hip_fail(err, "trellis GEMM launch");
+  }
+  if (flags & TQ_COMBINE) {
+    err = tq::launch_combine(y_slots, y, T, topk, L->out, s);
+    if (err != hipSuccess) return hip_fail(err, "combine launch");
+  }
+  return ok();
+}
+
+int mxfp4_expert_gemm(const tq_mxfp4_layer* L, const void* x, int64_t T,
+                      const int32_t* topk_ids, const float* topk_w, int32_t topk, float* y,
+                      uint32_t flags, void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_mxfp4_layer(L);
+  if (rc) return rc;
+  tq::WsLayout W;
+  rc = common_checks(L->E, L->out, L->in, x, T, topk_ids, topk, y, flags, ws, ws_bytes, true, &W);
+  if (rc) return rc;
+  if (T == 0) return ok();
+  rc = check_device();
+  if (rc) return rc;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int64_t N = T * topk;
+  float* y_slots = (flags & TQ_COMBINE) ? at<float>(ws, W.slots) : y;
+  const uint16_t* xb = static_cast<const uint16_t*>(x);
+  hipError_t err;
+  if (!W.gemm) {
+    tq::Mxfp4GemvArgs a{};
+    a.units = L->units;
+    a.x = xb;
+    a.ids = topk_ids;
+    a.gates = topk_w;
+    a.y = y_slots;
+    a.partial = W.gemv_slices > 1 ? at<float>(ws, W.partial) : nullptr;
+    a.counters = at<int32_t>(ws, W.counters);
+    a.status = at<uint32_t>(ws, W.status);
+    a.E = L->E;
+    a.out = L->out;
+    a.in = L->in;
+    a.topk = topk;
+    a.S = W.gemv_slices;
+    a.steps = W.gemv_steps;
+    a.groups = W.groups;
+    a.N = N;
+    err = tq::launch_mxfp4_gemv(a, s);
+    if (err != hipSuccess) return hip_fail(err, "MXFP4 GEMV launch");
+  } else {
+    rc = run_route(W, ws, topk_ids, N, L->E, L->out, y_slots, s);
+    if (rc) return rc;
+    tq::Mxfp4GemmArgs a{};
+    a.units = L->units;
+    a.x = xb;
+    a.gates = topk_w;
+    a.pairs = at<int32_t>(ws, W.pairs);
+    a.items = at<int32_t>(ws, W.items);
+    a.n_items = at<int32_t>(ws, W.n_items);
+    a.y = y_slots;
+    a.E = L->E;
+    a.out = L->out;
+    a.in = L->in;
+    a.topk = topk;
+    a.groups = W.groups;
+    a.max_items = W.max_items;
+    err = tq::launch_mxfp4_gemm(a, s);
+    if (err != hipSuccess) return hip_fail(err, "MXFP4 GEMM launch");
+  }
+  if (flags & TQ_COMBINE) {
+    err = tq::launch_combine(y_slots, y, T, topk, L->out, s);
+    if (err != hipSuccess) return hip_fail(err, "combine launch");
+  }
+  return ok();
+}
+
+}  // extern "C"

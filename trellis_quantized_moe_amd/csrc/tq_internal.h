@@ -1,0 +1,122 @@
+// Host-side internal interface between the C ABI (api.cpp) and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace tq {
+
+// ---- workspace layout -------------------------------------------------------------------
+// [status 256 B][gemv counters][gemv partials][route: counts, offsets, hist, rank, pairs,
+//  items, n_items][combine slot buffer]. Offsets are 256-byte aligned.
+struct WsLayout {
+  size_t status = 0;
+  size_t counters = 0, counters_bytes = 0;
+  size_t partial = 0, partial_bytes = 0;
+  size_t counts = 0, offsets = 0, hist = 0, rank = 0, pairs = 0, items = 0, n_items = 0;
+  size_t route_bytes = 0;
+  size_t slots = 0, slots_bytes = 0;
+  size_t total = 0;
+  int gemv_slices = 1, gemv_steps = 1, groups = 1, route_blocks = 1, max_items = 0;
+  bool gemm = false;
+};
+
+constexpr int ROUTE_CHUNK = 1024;  // ids per route-count block
+constexpr int GEMM_MT = 128;       // token rows per prefill work item
+constexpr int GEMV_MAXK = 16;      // tokens per decode-batch chunk (one MFMA row block)
+
+WsLayout ws_layout(int64_t T, int topk, int E, int out, int in, uint32_t flags,
+                   bool mxfp4);
+
+// ---- kernel launchers (return hipError_t) -------------------------------------------------
+struct TrellisGemvArgs {
+  const uint8_t* bits;
+  const int64_t* code_off;
+  const uint32_t* codes;
+  const uint16_t* scales;
+  const uint16_t* x;
+  const int32_t* ids;
+  const float* gates;
+  float* y;
+  float* partial;
+  int32_t* counters;
+  uint32_t* status;
+  int E, out, in, topk, S, steps, groups;
+  int64_t N;
+};
+hipError_t launch_trellis_gemv(const TrellisGemvArgs& a, hipStream_t s);
+
+struct TrellisGemmArgs {
+  const uint8_t* bits;
+  const int64_t* code_off;
+  const uint32_t* codes;
+  const uint16_t* scales;
+  const uint16_t* x;
+  const float* gates;
+  const int32_t* pairs;
+  const int32_t* items;
+  const int32_t* n_items;
+  float* y;
+  uint32_t* status;
+  int E, out, in, topk, groups, max_items;
+};
+hipError_t launch_trellis_gemm(const TrellisGemmArgs& a, hipStream_t s);
+
+struct Mxfp4GemvArgs {
+  const uint8_t* units;
+  const uint16_t* x;
+  const int32_t* ids;
+  const float* gates;
+  float* y;
+  float* partial;
+  int32_t* counters;
+  uint32_t* status;
+  int E, out, in, topk, S, steps, groups;
+  int64_t N;
+};
+hipError_t launch_mxfp4_gemv(const Mxfp4GemvArgs& a, hipStream_t s);
+
+struct Mxfp4GemmArgs {
+  const uint8_t* units;
+  const uint16_t* x;
+  const float* gates;
+  const int32_t* pairs;
+  const int32_t* items;
+  const int32_t* n_items;
+  float* y;
+  int E, out, in, topk, groups, max_items;
+};
+hipError_t launch_mxfp4_gemm(const Mxfp4GemmArgs& a, hipStream_t s);
+
+struct RouteArgs {
+  const int32_t* ids;
+  int64_t N;
+  int E, out;
+  int32_t* counts;    // [E]
+  int32_t* offsets;   // [E+1]
+  int32_t* hist;      // [blocks][E]
+  int32_t* rank;      // [N]
+  int32_t* pairs;     // [N]
+  int32_t* items;     // [max_items][4] or null
+  int32_t* n_items;   // [1] or null
+  float* y_special;   // per-slot output rows for empty / invalid slots, or null
+  uint32_t* status;
+  int blocks, item_rows, max_items;
+};
+hipError_t launch_route(const RouteArgs& a, hipStream_t s);
+
+hipError_t launch_fill_i32(int32_t* p, int64_t n, int32_t v, hipStream_t s);
+
+hipError_t launch_combine(const float* slots, float* y, int64_t T, int topk, int out,
+                          hipStream_t s);
+
+hipError_t launch_hadamard(const uint16_t* x, uint16_t* y, int64_t rows, int64_t n,
+                           const int8_t* signs, hipStream_t s);
+
+hipError_t launch_trellis_decode(const uint32_t* codes, int K, int out, int in, int16_t* q,
+                                 int path, hipStream_t s);
+hipError_t launch_mxfp4_decode(const uint8_t* unit, int out, int in, uint16_t* w,
+                               hipStream_t s);
+
+}  // namespace tq

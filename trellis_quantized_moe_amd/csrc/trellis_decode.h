@@ -1,0 +1,147 @@
+// Lane-level T16 trellis decoders for gfx950.
+//
+// A tile is 16 x 16 weights stored as 8*K uint32 words; its bit stream is read most
+// significant bit first and position p (input p % 16 of output channel p / 16 of the tile)
+// takes the 16-bit window starting at bit p*K, circularly within the tile. The value is
+// q = lo8(m) + hi8(m) - 255 with m = state * 0x3A2F mod 2^16 (DeepSeek-V4.1-Flash-1017
+// · dsx T16 page, "How T16 works", items 1 and 2).
+//
+// One lane decodes one tile column: the 16 consecutive positions of one output channel.
+// It gathers the column's bits into at most three registers, cuts the 16 states out
+// pairwise (two states per 32-bit register, so one packed 16-bit multiply serves both),
+// and multiplies. The result is eight "m-pairs": register r holds the product of the
+// state for input IH(r) in its high half and for input IL(r) in its low half.
+//   K = 2, 3:  IH(r) = r,      IL(r) = r + 8
+//   K = 4:     IH(r) = J(r),   IL(r) = J(r) + 4, with J(r) = r (r < 4) or r + 4 (r >= 4)
+// For K = 2 and 4, the two states of a pair sit 16 bits apart in the stream, so a single
+// funnel shift yields both; K = 3 needs two funnel shifts and a bit-field merge.
+#pragma once
+
+#include "tq_device.h"
+
+namespace tq {
+
+constexpr uint32_t T16_MULT2 = 0x3A2F3A2Fu;
+
+template <int K>
+__device__ __forceinline__ int pair_ih(int r) {
+  return K == 4 ? (r < 4 ? r : r + 4) : r;
+}
+template <int K>
+__device__ __forceinline__ int pair_il(int r) {
+  return K == 4 ? pair_ih<K>(r) + 4 : r + 8;
+}
+
+// Word offsets (within a tile) a lane loads for column n, and the funnel shift for K = 3.
+// K = 2: word n (the window of the column's last states continues into word n+1, which
+//        the lane takes from its right neighbour).
+// K = 4: words 2n, 2n+1 (word 2n+2 comes from the right neighbour).
+// K = 3: the column starts at bit 48n = word a, bit b (b = 0 or 16); the lane loads
+//        words a'..a'+2 (mod 24) with a' = a for b = 16 and a' = a - 1 for b = 0, so that
+//        one funnel shift by b aligns the column start for every lane.
+__device__ __forceinline__ void k3_column_words(int n, int* w0, int* w1, int* w2,
+                                                uint32_t* shift) {
+  int start = 48 * n;
+  int a = start >> 5;
+  int b = start & 31;
+  int ap = b ? a : a - 1;
+  *w0 = (ap + 24) % 24;
+  *w1 = (ap + 25) % 24;
+  *w2 = (ap + 26) % 24;
+  *shift = (uint32_t)b;
+}
+
+// Eight m-pairs of a K = 2 column. w = word n of the tile, wn = word n + 1 (mod 16).
+__device__ __forceinline__ void col_mpairs_k2(uint32_t w, uint32_t wn, uint32_t M[8]) {
+  uint32_t R[8];
+  R[0] = w;
+#pragma unroll
+  for (int j = 1; j < 8; ++j) R[j] = funnel(w, wn, 32 - 2 * j);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    u16x2 v = __builtin_bit_cast(u16x2, R[j]) * __builtin_bit_cast(u16x2, T16_MULT2);
+    M[j] = __builtin_bit_cast(uint32_t, v);
+  }
+}
+
+// K = 4 column: w0, w1 = words 2n, 2n+1, w2 = word 2n+2 (mod 32).
+__device__ __forceinline__ void col_mpairs_k4(uint32_t w0, uint32_t w1, uint32_t w2,
+                                              uint32_t M[8]) {
+  uint32_t R[8];
+  R[0] = w0;
+  R[4] = w1;
+#pragma unroll
+  for (int j = 1; j < 4; ++j) {
+    R[j] = funnel(w0, w1, 32 - 4 * j);
+    R[4 + j] = funnel(w1, w2, 32 - 4 * j);
+  }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    u16x2 v = __builtin_bit_cast(u16x2, R[j]) * __builtin_bit_cast(u16x2, T16_MULT2);
+    M[j] = __builtin_bit_cast(uint32_t, v);
+  }
+}
+
+// K = 3 column: q0..q2 = words a'..a'+2, shift = b (see k3_column_words).
+__device__ __forceinline__ void col_mpairs_k3(uint32_t q0, uint32_t q1, uint32_t q2,
+                                              uint32_t shift, uint32_t M[8]) {
+  uint32_t u0 = funnel(q0, q1, shift);
+  uint32_t u1 = funnel(q1, q2, shift);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    uint32_t r1 = j == 0 ? u0 : funnel(u0, u1, 32 - 3 * j);  // high half: state j
+    uint32_t r2 = funnel(u0, u1, 24 - 3 * j);                 // low half: state j + 8
+    uint32_t r = (r1 & 0xFFFF0000u) | (r2 & 0x0000FFFFu);
+    u16x2 v = __builtin_bit_cast(u16x2, r) * __builtin_bit_cast(u16x2, T16_MULT2);
+    M[j] = __builtin_bit_cast(uint32_t, v);
+  }
+}
+
+// ---- decode-batch operands: bytes as f16 ---------------------------------------------
+// The matrix cores take the two bytes of each product as separate f16 operands,
+// 1024 + byte (exact: f16 has 10 mantissa bits), both multiplied by the same activation.
+// The sum over a column is then sum x * (2048 + lo + hi) = sum x * (q + 2303); the
+// 2303 * sum(x) term is removed after accumulation.
+constexpr float GEMV_BYTE_OFFSET = 2303.0f;
+
+__device__ __forceinline__ uint32_t mpair_low_bytes_f16(uint32_t M) {
+  return (M & 0x00FF00FFu) | 0x64006400u;   // [lo: 1024 + lo8(m_IL), hi: 1024 + lo8(m_IH)]
+}
+__device__ __forceinline__ uint32_t mpair_high_bytes_f16(uint32_t M) {
+  return perm(M, 0x64646464u, 0x00070005u); // [lo: 1024 + hi8(m_IL), hi: 1024 + hi8(m_IH)]
+}
+
+// ---- prefill operands: q as bf16, natural input order ---------------------------------
+// v = lo8 + hi8 per half (packed 16-bit: m - 255 * (m >> 8)); 2^23 + v is built as an
+// fp32 bit pattern and 2^23 + 255 subtracted, giving q exactly; q has at most 8
+// significant bits, so its bf16 pattern is the fp32 pattern's upper half.
+__device__ __forceinline__ void mpair_to_f32(uint32_t M, float* q_ih, float* q_il) {
+  u16x2 m = __builtin_bit_cast(u16x2, M);
+  u16x2 h = m >> (u16x2){8, 8};
+  u16x2 v = m + h * (u16x2){0xFF01, 0xFF01};
+  uint32_t vv = __builtin_bit_cast(uint32_t, v);
+  *q_ih = __uint_as_float(perm(vv, 0x4B4B4B4Bu, 0x000C0706u)) - 8388863.0f;
+  *q_il = __uint_as_float(perm(vv, 0x4B4B4B4Bu, 0x000C0504u)) - 8388863.0f;
+}
+
+// Pack two exact fp32 integers into bf16 [lo: a, hi: b].
+__device__ __forceinline__ uint32_t pack_bf16_exact(float a, float b) {
+  return perm(__float_as_uint(b), __float_as_uint(a), 0x07060302u);
+}
+
+// Eight natural-order bf16 dwords (inputs 2t, 2t+1) from the eight m-pairs of a column.
+template <int K>
+__device__ __forceinline__ void mpairs_to_bf16_natural(const uint32_t M[8], uint32_t out[8]) {
+  float q[16];
+#pragma unroll
+  for (int r = 0; r < 8; ++r) {
+    float a, b;
+    mpair_to_f32(M[r], &a, &b);
+    q[pair_ih<K>(r)] = a;
+    q[pair_il<K>(r)] = b;
+  }
+#pragma unroll
+  for (int t = 0; t < 8; ++t) out[t] = pack_bf16_exact(q[2 * t], q[2 * t + 1]);
+}
+
+}  // namespace tq
