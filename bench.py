@@ -1,0 +1,364 @@
+"""Benchmark of the routed-expert hot path on one MI355X.
+
+A step is one pass of the whole hot path over one batch of seeded synthetic input, with
+every input already resident in device memory:
+  mixed (headline): the mixed-width trellis layer, 384 experts of 128 x 5120 (368 K=2,
+      15 K=3, 1 K=4), 128 tokens, top-8 — 128-wide rotation of the inputs, then the
+      decode-batch grouped GEMV (route scan, fetch, state rebuild, T16 hash, staging,
+      matrix-core contraction, epilogue);
+  mxfp4: the MXFP4 layer, 384 experts, 64 tokens, top-8 with gates — decode-batch GEMV;
+  prefill: 8,192 tokens, top-8 over 384 K=3 experts with Zipf(1.1) popularity — rotation,
+      route bucketing (three kernels), grouped MFMA GEMM.
+Steps are captured as HIP graphs and replayed; each step reads a different replica of the
+code buffer (replicas total >= 1 GiB) so the 256 MB Infinity Cache cannot serve repeats.
+
+value = compressed bytes of the experts a step touches / step time (GB/s), or dense-
+equivalent routed flops / step time (TFLOP/s) for prefill. The roofline object times the
+dominant kernel alone with HIP events around each launch (launches queued behind a bounded
+sleep kernel so no host gap falls inside an interval). The CPU baseline times the oracle
+(test infrastructure, single thread) on a bounded sample of the same workload.
+"""
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+MALL_BYTES = 1 << 30          # replicas of the code buffer total at least this much
+SLEEP_CYCLES = 60_000_000     # ~25 ms at 2.4 GHz: the GPU is busy while launches queue
+
+
+def log(msg):
+    print("[bench] " + msg, file=sys.stderr, flush=True)
+
+
+def active_bytes_trellis(layer, ids):
+    ids = np.unique(ids[ids >= 0])
+    K = layer["bits"][ids].astype(np.int64)
+    return int(np.sum(layer["out"] * layer["in"] * K // 8)), len(ids)
+
+
+def active_bytes_mxfp4(layer, ids):
+    ids = np.unique(ids[ids >= 0])
+    ub = layer["out"] * layer["in"] // 2 + layer["out"] * layer["in"] // 32
+    return int(len(ids) * ub), len(ids)
+
+
+def source_hash(files):
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, "trellis_quantized_moe_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def time_graph_steps(torch, graphs, steps, warmup):
+    for i in range(warmup):
+        graphs[i % len(graphs)].replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        graphs[i % len(graphs)].replay()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) / steps
+
+
+def time_kernel(torch, launch, n_replicas, iters):
+    """Average duration of one launch, from an event pair around each launch."""
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(iters)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(iters)]
+    for r in range(n_replicas):           # warm every replica's code path once
+        launch(r)
+    torch.cuda.synchronize()
+    torch.cuda._sleep(SLEEP_CYCLES)
+    for i in range(iters):
+        starts[i].record()
+        launch(i % n_replicas)
+        ends[i].record()
+    torch.cuda.synchronize()
+    ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    return float(np.mean(ms)) / 1e3, float(np.median(ms)) / 1e3
+
+
+def traffic_from_profile(name, shash, per_launch_algo):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it was taken
+    on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic_%s.json" % name)
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        d = json.load(f)
+    if d.get("source_hash") != shash:
+        return None
+    return int(d["hbm_bytes_per_launch"])
+
+
+def replicate(torch, t, total_bytes):
+    n = max(1, math.ceil(MALL_BYTES / max(1, total_bytes)))
+    return [t] + [t.clone() for _ in range(n - 1)]
+
+
+# ------------------------------------------------------------------------------------------
+# workloads
+# ------------------------------------------------------------------------------------------
+
+def bench_mixed(torch, ops, args):
+    from workloads import mixed_layer
+    wl = mixed_layer()
+    lay = wl["layer"]
+    dev = torch.device("cuda", 0)
+    L = ops.TrellisLayer.from_host(lay, dev)
+    x = torch.from_numpy(wl["x"].view(np.int16)).to(dev)
+    signs = torch.from_numpy(lay["signs"]).to(dev)
+    ids = torch.from_numpy(wl["topk_ids"]).to(dev)
+    T, topk = wl["topk_ids"].shape
+    nbytes, n_active = active_bytes_trellis(lay, wl["topk_ids"])
+    reps = replicate(torch, L.codes, L.codes.numel() * 4)
+    layers = [L.with_codes(c) for c in reps]
+    xr = torch.empty_like(x)
+    y = torch.empty((T, topk, lay["out"]), dtype=torch.float32, device=dev)
+    ws = ops.workspace(T, topk, lay["E"], lay["out"], lay["in"], ops.TQ_AUTO, dev)
+    log("mixed: %d active experts, %.1f MB compressed per step, %d replicas"
+        % (n_active, nbytes / 1e6, len(reps)))
+
+    def step(r):
+        ops.hadamard128(x, signs, out=xr)
+        ops.trellis_expert_gemm(layers[r], xr, ids, out=y, ws=ws)
+
+    for r in range(len(reps)):
+        step(r)
+    torch.cuda.synchronize()
+    graphs = []
+    for r in range(len(reps)):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step(r)
+        graphs.append(g)
+    sec = time_graph_steps(torch, graphs, args.steps, args.warmup)
+    kmean, kmed = time_kernel(
+        torch, lambda r: ops.trellis_expert_gemm(layers[r], xr, ids, out=y, ws=ws),
+        len(reps), args.kernel_iters)
+    hmean, _ = time_kernel(torch, lambda r: ops.hadamard128(x, signs, out=xr), 1, args.kernel_iters)
+    shash = source_hash(["trellis_gemv.hip", "trellis_decode.h", "gemv_common.h", "route_scan.h",
+                         "tq_device.h"])
+    traffic = traffic_from_profile("trellis_gemv_mixed", shash, nbytes)
+    return {
+        "sec_per_step": sec, "bytes": nbytes, "n_active": n_active,
+        "kernel": "trellis_gemv_kernel", "kernel_sec": kmean, "kernel_sec_median": kmed,
+        "hadamard_sec": hmean, "traffic": traffic, "source_hash": shash,
+        "replicas": len(reps), "wl": wl,
+    }
+
+
+def bench_mxfp4(torch, ops, args):
+    from workloads import mxfp4_decode_layer
+    wl = mxfp4_decode_layer()
+    lay = wl["layer"]
+    dev = torch.device("cuda", 0)
+    L = ops.Mxfp4Layer.from_host(lay, dev)
+    x = torch.from_numpy(wl["x"].view(np.int16)).to(dev)
+    ids = torch.from_numpy(wl["topk_ids"]).to(dev)
+    gates = torch.from_numpy(wl["topk_w"]).to(dev)
+    T, topk = wl["topk_ids"].shape
+    nbytes, n_active = active_bytes_mxfp4(lay, wl["topk_ids"])
+    reps = replicate(torch, L.units, L.units.numel())
+    layers = [L.with_units(u) for u in reps]
+    y = torch.empty((T, topk, lay["out"]), dtype=torch.float32, device=dev)
+    ws = ops.workspace(T, topk, lay["E"], lay["out"], lay["in"], ops.TQ_AUTO, dev)
+    log("mxfp4: %d active experts, %.1f MB per step, %d replicas" % (n_active, nbytes / 1e6, len(reps)))
+
+    def step(r):
+        ops.mxfp4_expert_gemm(layers[r], x, ids, gates, out=y, ws=ws)
+
+    for r in range(len(reps)):
+        step(r)
+    torch.cuda.synchronize()
+    graphs = []
+    for r in range(len(reps)):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step(r)
+        graphs.append(g)
+    sec = time_graph_steps(torch, graphs, args.steps, args.warmup)
+    kmean, kmed = time_kernel(torch, step, len(reps), args.kernel_iters)
+    return {"sec_per_step": sec, "bytes": nbytes, "n_active": n_active,
+            "kernel": "mxfp4_gemv_kernel", "kernel_sec": kmean, "kernel_sec_median": kmed}
+
+
+def bench_prefill(torch, ops, args):
+    from workloads import prefill_chunk
+    wl = prefill_chunk()
+    lay = wl["layer"]
+    dev = torch.device("cuda", 0)
+    L = ops.TrellisLayer.from_host(lay, dev)
+    x = torch.from_numpy(wl["x"].view(np.int16)).to(dev)
+    signs = torch.from_numpy(lay["signs"]).to(dev)
+    ids = torch.from_numpy(wl["topk_ids"]).to(dev)
+    T, topk = wl["topk_ids"].shape
+    flops = 2.0 * T * topk * lay["out"] * lay["in"]
+    reps = replicate(torch, L.codes, L.codes.numel() * 4)
+    layers = [L.with_codes(c) for c in reps]
+    xr = torch.empty_like(x)
+    y = torch.empty((T, topk, lay["out"]), dtype=torch.float32, device=dev)
+    ws = ops.workspace(T, topk, lay["E"], lay["out"], lay["in"], ops.TQ_AUTO, dev)
+    log("prefill: %.1f GFLOP per step, %d replicas" % (flops / 1e9, len(reps)))
+
+    def step(r):
+        ops.hadamard128(x, signs, out=xr)
+        ops.trellis_expert_gemm(layers[r], xr, ids, out=y, ws=ws)
+
+    for r in range(len(reps)):
+        step(r)
+    torch.cuda.synchronize()
+    graphs = []
+    for r in range(len(reps)):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step(r)
+        graphs.append(g)
+    steps = max(10, args.steps // 20)
+    sec = time_graph_steps(torch, graphs, steps, max(2, args.warmup // 10))
+    gemm_only = lambda r: ops.trellis_expert_gemm(layers[r], xr, ids, out=y, ws=ws, flags=ops.TQ_GEMM)
+    kmean, kmed = time_kernel(torch, gemm_only, len(reps), max(10, args.kernel_iters // 10))
+    return {"sec_per_step": sec, "flops": flops, "steps": steps,
+            "kernel": "route + trellis_gemm_kernel", "kernel_sec": kmean, "kernel_sec_median": kmed}
+
+
+def cpu_baseline_mixed(wl, n_experts):
+    """The oracle on a bounded sample: rotation of all tokens, then decode + FP64
+    contraction for the slots of n_experts of the active experts."""
+    import oracle
+    from threadpoolctl import threadpool_limits
+    lay = wl["layer"]
+    ids = wl["topk_ids"]
+    active = np.unique(ids)
+    pick = np.random.default_rng(7).choice(active, size=min(n_experts, active.size), replace=False)
+    keep = np.where(np.isin(ids, pick), ids, -1)
+    nbytes = int(np.sum(lay["out"] * lay["in"] * lay["bits"][pick].astype(np.int64) // 8))
+    scales = oracle.f16_bits_to_f64(lay["scales"])
+
+    def weight_of(e):
+        K = int(lay["bits"][e])
+        n = lay["out"] * lay["in"] * K // 32
+        s = int(lay["code_off"][e]) // 4
+        return oracle.decode_unit(lay["codes"][s:s + n], K, lay["out"], lay["in"]).astype(np.float64)
+
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        xr = oracle.hadamard128_fp32_order(wl["x"], lay["signs"])
+        oracle.expert_gemm(xr, keep, None, lay["E"], weight_of, lambda e: scales[e])
+        sec = time.perf_counter() - t0
+    return {
+        "value": round(nbytes / sec / 1e9, 5), "unit": "GB/s", "cores": 1, "kind": "oracle",
+        "sample": "%d of %d active experts of the mixed layer (their %d slots): oracle rotation of "
+                  "all 128 tokens + decode + FP64 contraction, %.1f MB compressed, %.1f s"
+                  % (len(pick), active.size, int(np.sum(keep >= 0)), nbytes / 1e6, sec),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=1000)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--kernel-iters", type=int, default=200)
+    ap.add_argument("--extras", default="mxfp4,prefill",
+                    help="comma list of secondary workloads (mxfp4, prefill) or 'none'")
+    ap.add_argument("--cpu-sample-experts", type=int, default=128)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(requested --gpus %d, WORLD_SIZE %d)" % (args.gpus, world), file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from trellis_quantized_moe_amd import ops
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    torch.cuda.set_device(0)
+
+    res = bench_mixed(torch, ops, args)
+    gbs = res["bytes"] / res["sec_per_step"] / 1e9
+    achieved = res["bytes"] / res["kernel_sec"] / 1e9
+    wl = res.pop("wl")
+    line = {
+        "metric": "compressed-expert GB/s (decode GEMV) + TFLOP/s (prefill) vs roofline",
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(res["sec_per_step"] * 1e3, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {
+            "workload": "mixed-width trellis layer (K2 Mix style) decode batch",
+            "experts": 384, "unit": "128x5120", "widths": "368xK2 15xK3 1xK4",
+            "tokens": 128, "topk": 8, "active_experts": res["n_active"],
+            "compressed_bytes_per_step": res["bytes"], "rotation": "hadamard128 on inputs",
+            "replicas": res["replicas"],
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": res["traffic"],
+            "kernel": res["kernel"],
+            "kernel_us": round(res["kernel_sec"] * 1e6, 3),
+            "kernel_us_median": round(res["kernel_sec_median"] * 1e6, 3),
+            "algorithmic_bytes_per_launch": res["bytes"],
+            "source_hash": res["source_hash"],
+        },
+        "hadamard_us": round(res["hadamard_sec"] * 1e6, 3),
+    }
+    extras = {}
+    todo = [] if args.extras == "none" else [e for e in args.extras.split(",") if e]
+    if "mxfp4" in todo:
+        m = bench_mxfp4(torch, ops, args)
+        extras["mxfp4_decode_layer"] = {
+            "workload": "MXFP4 layer, 384 experts, 64 tokens, top-8, gates",
+            "GB/s": round(m["bytes"] / m["sec_per_step"] / 1e9, 2),
+            "ms_per_step": round(m["sec_per_step"] * 1e3, 5),
+            "kernel": m["kernel"], "kernel_us": round(m["kernel_sec"] * 1e6, 3),
+            "kernel_GB/s": round(m["bytes"] / m["kernel_sec"] / 1e9, 2),
+            "frac_hbm": round(m["bytes"] / m["kernel_sec"] / 1e9 / HBM_PEAK_GBS, 4),
+            "active_experts": m["n_active"], "bytes_per_step": m["bytes"],
+        }
+    if "prefill" in todo:
+        p = bench_prefill(torch, ops, args)
+        extras["prefill_chunk"] = {
+            "workload": "8192 tokens, top-8, 384 K=3 experts, Zipf(1.1)",
+            "TFLOP/s": round(p["flops"] / p["sec_per_step"] / 1e12, 3),
+            "ms_per_step": round(p["sec_per_step"] * 1e3, 5), "steps": p["steps"],
+            "route_plus_gemm_us": round(p["kernel_sec"] * 1e6, 3),
+            "route_plus_gemm_TFLOP/s": round(p["flops"] / p["kernel_sec"] / 1e12, 3),
+            "frac_bf16_peak": round(p["flops"] / p["kernel_sec"] / 1e12 / BF16_PEAK_TFLOPS, 4),
+        }
+    if extras:
+        line["extras"] = extras
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline_mixed(wl, args.cpu_sample_experts)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

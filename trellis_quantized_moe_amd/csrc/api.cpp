@@ -8,6 +8,7 @@
 #include <string>
 
 #include "../../include/tq.h"
+#include "gemv_common.h"
 #include "tq_internal.h"
 
 namespace {
@@ -117,7 +118,7 @@ WsLayout ws_layout(int64_t T, int topk, int E, int out, int in, uint32_t flags, 
   if (!L.gemm) {
     const int64_t active = N < E ? N : E;
     const int64_t wgs_per_slice = (active > 0 ? active : 1) * L.groups;
-    const int target = (int)((2048 + wgs_per_slice - 1) / wgs_per_slice);
+    const int target = (int)((1024 + wgs_per_slice - 1) / wgs_per_slice);
     if (mxfp4) {
       const int units = in / 512;
       L.gemv_steps = pick_steps(units, 2, target);
@@ -127,9 +128,6 @@ WsLayout ws_layout(int64_t T, int topk, int E, int out, int in, uint32_t flags, 
       L.gemv_steps = pick_steps(units, 5, target);
       L.gemv_slices = units / L.gemv_steps;
     }
-    L.counters = off;
-    L.counters_bytes = round_up((size_t)E * L.groups * 4, 256);
-    off += L.counters_bytes;
     if (L.gemv_slices > 1) {
       L.partial = off;
       L.partial_bytes = round_up((size_t)L.gemv_slices * N * out * 4, 256);
@@ -155,7 +153,7 @@ WsLayout ws_layout(int64_t T, int topk, int E, int out, int in, uint32_t flags, 
     off += 256;
     L.route_bytes = off - start;
   }
-  if (flags & TQ_COMBINE) {
+  if ((flags & TQ_COMBINE) && (L.gemm || L.gemv_slices == 1)) {
     L.slots = off;
     L.slots_bytes = round_up((size_t)N * out * 4, 256);
     off += L.slots_bytes;
@@ -348,6 +346,29 @@ int run_route(const tq::WsLayout& L, void* ws, const int32_t* ids, int64_t N, in
   return TQ_OK;
 }
 
+// Second launch of the decode-batch path with S > 1 slices: slice sums, epilogue, empty and
+// invalid slots, and (with TQ_COMBINE) the fixed-order sum over slots, straight into y.
+int run_gemv_reduce(const tq::WsLayout& L, void* ws, const int32_t* ids, const uint16_t* scales,
+                    const float* gates, float* y, int64_t N, int E, int out, int topk,
+                    uint32_t flags, hipStream_t s) {
+  tq::GemvReduceArgs r{};
+  r.ids = ids;
+  r.partial = at<float>(ws, L.partial);
+  r.scales = scales;
+  r.gates = gates;
+  r.y = y;
+  r.status = at<uint32_t>(ws, L.status);
+  r.N = (int)N;
+  r.E = E;
+  r.out = out;
+  r.topk = topk;
+  r.S = L.gemv_slices;
+  r.combine = (flags & TQ_COMBINE) ? 1 : 0;
+  hipError_t err = tq::launch_gemv_reduce(r, s);
+  if (err != hipSuccess) return hip_fail(err, "GEMV slice reduction launch");
+  return TQ_OK;
+}
+
 }  // namespace
 
 int trellis_expert_gemm(const tq_trellis_layer* L, const void* x, int64_t T,
@@ -377,7 +398,6 @@ int trellis_expert_gemm(const tq_trellis_layer* L, const void* x, int64_t T,
     a.gates = topk_w;
     a.y = y_slots;
     a.partial = W.gemv_slices > 1 ? at<float>(ws, W.partial) : nullptr;
-    a.counters = at<int32_t>(ws, W.counters);
     a.status = at<uint32_t>(ws, W.status);
     a.E = L->E;
     a.out = L->out;
@@ -389,6 +409,11 @@ int trellis_expert_gemm(const tq_trellis_layer* L, const void* x, int64_t T,
     a.N = N;
     err = tq::launch_trellis_gemv(a, s);
     if (err != hipSuccess) return hip_fail(err, "trellis GEMV launch");
+    if (W.gemv_slices > 1) {
+      rc = run_gemv_reduce(W, ws, topk_ids, L->scales, topk_w, y, N, L->E, L->out, topk, flags, s);
+      if (rc) return rc;
+      return ok();
+    }
   } else {
     rc = run_route(W, ws, topk_ids, N, L->E, L->out, y_slots, s);
     if (rc) return rc;
@@ -444,7 +469,6 @@ int mxfp4_expert_gemm(const tq_mxfp4_layer* L, const void* x, int64_t T,
     a.gates = topk_w;
     a.y = y_slots;
     a.partial = W.gemv_slices > 1 ? at<float>(ws, W.partial) : nullptr;
-    a.counters = at<int32_t>(ws, W.counters);
     a.status = at<uint32_t>(ws, W.status);
     a.E = L->E;
     a.out = L->out;
@@ -456,6 +480,11 @@ int mxfp4_expert_gemm(const tq_mxfp4_layer* L, const void* x, int64_t T,
     a.N = N;
     err = tq::launch_mxfp4_gemv(a, s);
     if (err != hipSuccess) return hip_fail(err, "MXFP4 GEMV launch");
+    if (W.gemv_slices > 1) {
+      rc = run_gemv_reduce(W, ws, topk_ids, nullptr, topk_w, y, N, L->E, L->out, topk, flags, s);
+      if (rc) return rc;
+      return ok();
+    }
   } else {
     rc = run_route(W, ws, topk_ids, N, L->E, L->out, y_slots, s);
     if (rc) return rc;

@@ -2,11 +2,11 @@
 //
 // A GEMV workgroup owns (expert e, group of up to 8 strips = 128 output channels,
 // K-slice s). Its four waves hold 16 x 16 accumulator tiles for the same outputs over
-// different K ranges; they are added through LDS in wave order. With S > 1 slices the
-// workgroup stores its slice's sums to a partial buffer indexed by flat slot, and the
-// last workgroup of (e, group) to arrive (device-scope counter) adds the S slices in slice
-// order and applies the epilogue. The counter is reset by that workgroup, so the workspace
-// is left zeroed for the next call.
+// different K ranges; they are added through LDS in wave order. With one slice the
+// workgroup applies the epilogue and writes y. With S > 1 slices it stores its slice's
+// sums to a partial buffer indexed by flat slot, and a second launch (gemv_reduce) adds
+// the S slices in slice order. The launch boundary makes the partials visible; no
+// device-wide fence (which would write back and invalidate a whole L2) is needed.
 #pragma once
 
 #include "route_scan.h"
@@ -20,17 +20,16 @@ struct GemvCommon {
   const int32_t* ids;
   const float* gates;
   const uint16_t* scales;  // fp16 [E][out] or null (scale 1)
-  float* y;                // per-slot output [N][out]
-  float* partial;          // [S][N][out]
-  int32_t* counters;       // [E][groups]
+  float* y;                // per-slot output [N][out] (S == 1)
+  float* partial;          // [S][N][out] (S > 1)
   int N, E, out, topk, S, groups;
 };
 
-__device__ __forceinline__ float gemv_epilogue(const GemvCommon& c, int e, int o, int slot,
-                                               float v) {
+__device__ __forceinline__ float gemv_epilogue(const uint16_t* scales, const float* gates, int out,
+                                               int e, int o, int slot, float v) {
   float r = v;
-  if (c.scales) r = r * f16_bits_to_f32(c.scales[(size_t)e * c.out + o]);
-  if (c.gates) r = r * c.gates[slot];
+  if (scales) r = r * f16_bits_to_f32(scales[(size_t)e * out + o]);
+  if (gates) r = r * gates[slot];
   return r;
 }
 
@@ -58,7 +57,7 @@ __device__ inline void gemv_reduce_store(const GemvCommon& c, float* red, const 
       const int o = grp * 128 + s8 * 16 + (ln & 15);
       const int slot = ch.slots[m];
       if (c.S == 1)
-        c.y[(size_t)slot * c.out + o] = gemv_epilogue(c, e, o, slot, val);
+        c.y[(size_t)slot * c.out + o] = gemv_epilogue(c.scales, c.gates, c.out, e, o, slot, val);
       else
         c.partial[((size_t)s * c.N + slot) * c.out + o] = val;
     }
@@ -66,42 +65,10 @@ __device__ inline void gemv_reduce_store(const GemvCommon& c, float* red, const 
   __syncthreads();
 }
 
-// Called by every workgroup of (e, grp) that found slots, after its last chunk. Returns
-// after the last arriving workgroup has written the outputs.
-__device__ inline void gemv_finish(const GemvCommon& c, SlotChunk& ch, int* last_flag, int e,
-                                   int grp, int ns) {
-  __threadfence();
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const int old = atomicAdd(&c.counters[e * c.groups + grp], 1);
-    *last_flag = (old == c.S - 1);
-  }
-  __syncthreads();
-  if (!*last_flag) return;
-  __threadfence();
-  const int width = ns * 16;
-  int pos = 0;
-  while (true) {
-    collect_slots(c.ids, c.N, e, pos, ch);
-    const int cnt = ch.cnt;
-    if (cnt == 0) break;
-    pos = ch.next;
-    for (int v = threadIdx.x; v < cnt * width; v += GEMV_THREADS) {
-      const int m = v / width, o = grp * 128 + v % width;
-      const int slot = ch.slots[m];
-      float sum = 0.0f;
-      for (int s = 0; s < c.S; ++s) sum += c.partial[((size_t)s * c.N + slot) * c.out + o];
-      c.y[(size_t)slot * c.out + o] = gemv_epilogue(c, e, o, slot, sum);
-    }
-    __syncthreads();
-    if (pos >= c.N) break;
-  }
-  if (threadIdx.x == 0) c.counters[e * c.groups + grp] = 0;
-}
-
-// NaN in every output of expert e's slots for this group; status bit 2.
+// NaN in this (group, slice)'s outputs of expert e's slots; status bit. With S > 1 the NaN
+// goes to the slice's partials, so the reduced outputs are NaN too.
 __device__ inline void gemv_bad_unit(const GemvCommon& c, SlotChunk& ch, uint32_t* status,
-                                     int e, int grp, int ns) {
+                                     int e, int grp, int s, int ns) {
   int pos = 0;
   while (true) {
     collect_slots(c.ids, c.N, e, pos, ch);
@@ -109,12 +76,26 @@ __device__ inline void gemv_bad_unit(const GemvCommon& c, SlotChunk& ch, uint32_
     pos = ch.next;
     for (int v = threadIdx.x; v < ch.cnt * ns * 16; v += GEMV_THREADS) {
       const int m = v / (ns * 16), o = grp * 128 + v % (ns * 16);
-      c.y[(size_t)ch.slots[m] * c.out + o] = __builtin_nanf("");
+      float* dst = c.S == 1 ? c.y + (size_t)ch.slots[m] * c.out + o
+                            : c.partial + ((size_t)s * c.N + ch.slots[m]) * c.out + o;
+      *dst = __builtin_nanf("");
     }
     if (threadIdx.x == 0) set_status(status, STATUS_BAD_UNIT);
     __syncthreads();
     if (pos >= c.N) break;
   }
 }
+
+struct GemvReduceArgs {
+  const int32_t* ids;
+  const float* partial;    // [S][N][out]
+  const uint16_t* scales;  // or null
+  const float* gates;      // or null
+  float* y;                // [N][out], or [T][out] when combine
+  uint32_t* status;
+  int N, E, out, topk, S, combine;
+};
+
+hipError_t launch_gemv_reduce(const GemvReduceArgs& a, hipStream_t s);
 
 }  // namespace tq

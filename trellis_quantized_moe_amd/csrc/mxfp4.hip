@@ -63,7 +63,6 @@ constexpr int MX_SMEM_WORDS =
 struct MxShared {
   uint32_t buf[MX_SMEM_WORDS];
   SlotChunk ch;
-  int last;
 };
 
 __device__ int mx_run_expert(const Mxfp4GemvArgs& a, const GemvCommon& c, MxShared& sh, int e,
@@ -140,7 +139,6 @@ __global__ __launch_bounds__(GEMV_THREADS) void mxfp4_gemv_kernel(Mxfp4GemvArgs 
   c.scales = nullptr;
   c.y = a.y;
   c.partial = a.partial;
-  c.counters = a.counters;
   c.N = (int)a.N;
   c.E = a.E;
   c.out = a.out;
@@ -158,9 +156,7 @@ __global__ __launch_bounds__(GEMV_THREADS) void mxfp4_gemv_kernel(Mxfp4GemvArgs 
   const int grp = rest % a.groups;
   const int s = rest / a.groups;
   const int ns = min(8, a.out / 16 - grp * 8);
-  const int found = mx_run_expert(a, c, sh, e, grp, s, ns);
-  if (a.S == 1 || found == 0) return;
-  gemv_finish(c, sh.ch, &sh.last, e, grp, ns);
+  mx_run_expert(a, c, sh, e, grp, s, ns);
 }
 
 // ---- prefill GEMM --------------------------------------------------------------------------
@@ -227,7 +223,7 @@ hipError_t launch_mxfp4_decode(const uint8_t* unit, int out, int in, uint16_t* w
 }
 
 hipError_t launch_mxfp4_gemv(const Mxfp4GemvArgs& a, hipStream_t s) {
-  const int blocks = a.E * a.groups * a.S + 1;
+  const int blocks = a.E * a.groups * a.S + (a.S == 1 ? 1 : 0);
   hipLaunchKernelGGL(mxfp4_gemv_kernel, dim3(blocks), dim3(GEMV_THREADS), 0, s, a);
   return hipGetLastError();
 }

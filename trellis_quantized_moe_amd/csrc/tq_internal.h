@@ -8,11 +8,10 @@
 namespace tq {
 
 // ---- workspace layout -------------------------------------------------------------------
-// [status 256 B][gemv counters][gemv partials][route: counts, offsets, hist, rank, pairs,
-//  items, n_items][combine slot buffer]. Offsets are 256-byte aligned.
+// [status 256 B][gemv partials][route: counts, offsets, hist, rank, pairs, items, n_items]
+// [combine slot buffer]. Offsets are 256-byte aligned.
 struct WsLayout {
   size_t status = 0;
-  size_t counters = 0, counters_bytes = 0;
   size_t partial = 0, partial_bytes = 0;
   size_t counts = 0, offsets = 0, hist = 0, rank = 0, pairs = 0, items = 0, n_items = 0;
   size_t route_bytes = 0;
@@ -40,7 +39,6 @@ struct TrellisGemvArgs {
   const float* gates;
   float* y;
   float* partial;
-  int32_t* counters;
   uint32_t* status;
   int E, out, in, topk, S, steps, groups;
   int64_t N;
@@ -70,7 +68,6 @@ struct Mxfp4GemvArgs {
   const float* gates;
   float* y;
   float* partial;
-  int32_t* counters;
   uint32_t* status;
   int E, out, in, topk, S, steps, groups;
   int64_t N;

@@ -29,7 +29,6 @@ struct Shared {
   float colsum[16 * MAX_STEPS * 16];
   float rowsum[16];
   SlotChunk ch;
-  int last;
 };
 
 // Stage A for one chunk: task (col c, row m) converts the 16 activations of tile column
@@ -167,7 +166,6 @@ __global__ __launch_bounds__(GEMV_THREADS) void trellis_gemv_kernel(TrellisGemvA
   c.scales = a.scales;
   c.y = a.y;
   c.partial = a.partial;
-  c.counters = a.counters;
   c.N = (int)a.N;
   c.E = a.E;
   c.out = a.out;
@@ -176,7 +174,7 @@ __global__ __launch_bounds__(GEMV_THREADS) void trellis_gemv_kernel(TrellisGemvA
   c.groups = a.groups;
   const int work = a.E * a.groups * a.S;
   const int bid = blockIdx.x;
-  if (bid == work) {
+  if (bid == work) {  // only launched with S == 1; with S > 1 the reduce launch does this
     special_slots(a.ids, c.N, a.E, a.out, a.y, a.status);
     return;
   }
@@ -188,19 +186,16 @@ __global__ __launch_bounds__(GEMV_THREADS) void trellis_gemv_kernel(TrellisGemvA
   const int K = a.bits[e];
   const int64_t off = a.code_off[e];
   if ((K < 2 || K > 4) || (off & 15)) {
-    if (s == 0) gemv_bad_unit(c, sh.ch, a.status, e, grp, ns);
+    gemv_bad_unit(c, sh.ch, a.status, e, grp, s, ns);
     return;
   }
   const uint32_t* unit = a.codes + off / 4;
-  int found;
   if (K == 2)
-    found = run_expert<2>(a, c, sh, e, grp, s, ns, unit);
+    run_expert<2>(a, c, sh, e, grp, s, ns, unit);
   else if (K == 3)
-    found = run_expert<3>(a, c, sh, e, grp, s, ns, unit);
+    run_expert<3>(a, c, sh, e, grp, s, ns, unit);
   else
-    found = run_expert<4>(a, c, sh, e, grp, s, ns, unit);
-  if (a.S == 1 || found == 0) return;
-  gemv_finish(c, sh.ch, &sh.last, e, grp, ns);
+    run_expert<4>(a, c, sh, e, grp, s, ns, unit);
 }
 
 // ---- decode hook ------------------------------------------------------------------------
@@ -248,7 +243,7 @@ __global__ __launch_bounds__(256) void trellis_decode_kernel(const uint32_t* __r
 }  // namespace
 
 hipError_t launch_trellis_gemv(const TrellisGemvArgs& a, hipStream_t s) {
-  const int blocks = a.E * a.groups * a.S + 1;
+  const int blocks = a.E * a.groups * a.S + (a.S == 1 ? 1 : 0);
   hipLaunchKernelGGL(trellis_gemv_kernel, dim3(blocks), dim3(GEMV_THREADS), 0, s, a);
   return hipGetLastError();
 }
