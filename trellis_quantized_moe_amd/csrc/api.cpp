@@ -7,7 +7,7 @@
 #include <cstring>
 #include <string>
 
-#include "../../include/tq.h"
+#include "tq.h"
 #include "gemv_common.h"
 #include "tq_internal.h"
 
@@ -125,8 +125,14 @@ WsLayout ws_layout(int64_t T, int topk, int E, int out, int in, uint32_t flags, 
       L.gemv_slices = units / L.gemv_steps;
     } else {
       const int units = in / 256;
-      L.gemv_steps = pick_steps(units, 5, target);
+      L.gemv_steps = pick_steps(units, units, target);
       L.gemv_slices = units / L.gemv_steps;
+    }
+    if (!mxfp4) {
+      L.xprep = off;
+      off += round_up((size_t)T * in * 2, 256);
+      L.rowsum = off;
+      off += round_up((size_t)T * 4, 256);
     }
     if (L.gemv_slices > 1) {
       L.partial = off;
@@ -349,13 +355,17 @@ int run_route(const tq::WsLayout& L, void* ws, const int32_t* ids, int64_t N, in
 // Second launch of the decode-batch path with S > 1 slices: slice sums, epilogue, empty and
 // invalid slots, and (with TQ_COMBINE) the fixed-order sum over slots, straight into y.
 int run_gemv_reduce(const tq::WsLayout& L, void* ws, const int32_t* ids, const uint16_t* scales,
-                    const float* gates, float* y, int64_t N, int E, int out, int topk,
-                    uint32_t flags, hipStream_t s) {
+                    const float* gates, const float* rowsum, float acc_scale, float offset,
+                    float* y, int64_t N, int E, int out, int topk, uint32_t flags,
+                    hipStream_t s) {
   tq::GemvReduceArgs r{};
   r.ids = ids;
   r.partial = at<float>(ws, L.partial);
   r.scales = scales;
   r.gates = gates;
+  r.rowsum = rowsum;
+  r.acc_scale = acc_scale;
+  r.offset = offset;
   r.y = y;
   r.status = at<uint32_t>(ws, L.status);
   r.N = (int)N;
@@ -388,12 +398,15 @@ int trellis_expert_gemm(const tq_trellis_layer* L, const void* x, int64_t T,
   const uint16_t* xb = static_cast<const uint16_t*>(x);
   hipError_t err;
   if (!W.gemm) {
+    err = tq::launch_gemv_prep(xb, T, L->in, at<uint32_t>(ws, W.xprep), at<float>(ws, W.rowsum), s);
+    if (err != hipSuccess) return hip_fail(err, "activation prep launch");
     tq::TrellisGemvArgs a{};
     a.bits = L->bits;
     a.code_off = L->code_off;
     a.codes = L->codes;
     a.scales = L->scales;
-    a.x = xb;
+    a.xp = at<uint32_t>(ws, W.xprep);
+    a.rowsum = at<float>(ws, W.rowsum);
     a.ids = topk_ids;
     a.gates = topk_w;
     a.y = y_slots;
@@ -410,7 +423,8 @@ int trellis_expert_gemm(const tq_trellis_layer* L, const void* x, int64_t T,
     err = tq::launch_trellis_gemv(a, s);
     if (err != hipSuccess) return hip_fail(err, "trellis GEMV launch");
     if (W.gemv_slices > 1) {
-      rc = run_gemv_reduce(W, ws, topk_ids, L->scales, topk_w, y, N, L->E, L->out, topk, flags, s);
+      rc = run_gemv_reduce(W, ws, topk_ids, L->scales, topk_w, at<float>(ws, W.rowsum),
+                           16777216.0f, 255.0f, y, N, L->E, L->out, topk, flags, s);
       if (rc) return rc;
       return ok();
     }
@@ -481,7 +495,8 @@ int mxfp4_expert_gemm(const tq_mxfp4_layer* L, const void* x, int64_t T,
     err = tq::launch_mxfp4_gemv(a, s);
     if (err != hipSuccess) return hip_fail(err, "MXFP4 GEMV launch");
     if (W.gemv_slices > 1) {
-      rc = run_gemv_reduce(W, ws, topk_ids, nullptr, topk_w, y, N, L->E, L->out, topk, flags, s);
+      rc = run_gemv_reduce(W, ws, topk_ids, nullptr, topk_w, nullptr, 1.0f, 0.0f, y, N, L->E,
+                           L->out, topk, flags, s);
       if (rc) return rc;
       return ok();
     }

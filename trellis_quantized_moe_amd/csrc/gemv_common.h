@@ -20,8 +20,11 @@ struct GemvCommon {
   const int32_t* ids;
   const float* gates;
   const uint16_t* scales;  // fp16 [E][out] or null (scale 1)
+  const float* rowsum;     // [T]: per-token sum the epilogue removes, or null
   float* y;                // per-slot output [N][out] (S == 1)
   float* partial;          // [S][N][out] (S > 1)
+  float acc_scale;         // accumulator scale (2^24 for subnormal byte operands, else 1)
+  float offset;            // y = acc * acc_scale - offset * rowsum[token]
   int N, E, out, topk, S, groups;
 };
 
@@ -34,10 +37,10 @@ __device__ __forceinline__ float gemv_epilogue(const uint16_t* scales, const flo
 }
 
 // red: LDS float [4 waves][8 strips][4][64 lanes]. Each wave writes acc, then the sums
-// (wave order) minus offset * rowsum[m] go to y (S == 1) or to the partial buffer.
+// (wave order) go to the partial buffer (S > 1), or, scaled and corrected, through the
+// epilogue to y (S == 1).
 __device__ inline void gemv_reduce_store(const GemvCommon& c, float* red, const f32x4 acc[8],
-                                         const SlotChunk& ch, const float* rowsum, float offset,
-                                         int e, int grp, int s, int ns) {
+                                         const SlotChunk& ch, int e, int grp, int s, int ns) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
 #pragma unroll
   for (int s8 = 0; s8 < 8; ++s8)
@@ -53,13 +56,15 @@ __device__ inline void gemv_reduce_store(const GemvCommon& c, float* red, const 
     sum += red[((3 * 8 + s8) * 4 + i) * 64 + ln];
     const int m = 4 * (ln >> 4) + i;
     if (m < cnt) {
-      const float val = rowsum ? sum - offset * rowsum[m] : sum;
       const int o = grp * 128 + s8 * 16 + (ln & 15);
       const int slot = ch.slots[m];
-      if (c.S == 1)
+      if (c.S == 1) {
+        float val = sum * c.acc_scale;
+        if (c.rowsum) val = val - c.offset * c.rowsum[slot / c.topk];
         c.y[(size_t)slot * c.out + o] = gemv_epilogue(c.scales, c.gates, c.out, e, o, slot, val);
-      else
-        c.partial[((size_t)s * c.N + slot) * c.out + o] = val;
+      } else {
+        c.partial[((size_t)s * c.N + slot) * c.out + o] = sum;
+      }
     }
   }
   __syncthreads();
@@ -91,8 +96,10 @@ struct GemvReduceArgs {
   const float* partial;    // [S][N][out]
   const uint16_t* scales;  // or null
   const float* gates;      // or null
+  const float* rowsum;     // [T] or null
   float* y;                // [N][out], or [T][out] when combine
   uint32_t* status;
+  float acc_scale, offset;
   int N, E, out, topk, S, combine;
 };
 

@@ -1,5 +1,6 @@
 // Second launch of the decode-batch path when the K range is split into S slices: for each
-// output, the S slice partials are added in slice order, then the per-channel scale and the
+// output, the S slice partials are added in slice order, scaled by acc_scale, corrected by
+// offset * rowsum[token] (the trellis byte encoding), then the per-channel scale and the
 // gate are applied. Empty slots (-1) give 0; ids outside [-1, E) give NaN and set the
 // status bit. With combine, y[t][o] = sum over k = 0..topk-1 (in order) of the slot values.
 #include "gemv_common.h"
@@ -19,7 +20,9 @@ __device__ __forceinline__ float slot_value(const GemvReduceArgs& a, int slot, i
   const float* p = a.partial + (size_t)slot * a.out + o;
   float sum = p[0];
   for (int s = 1; s < a.S; ++s) sum += p[(size_t)s * stride];
-  return gemv_epilogue(a.scales, a.gates, a.out, id, o, slot, sum);
+  float val = sum * a.acc_scale;
+  if (a.rowsum) val = val - a.offset * a.rowsum[slot / a.topk];
+  return gemv_epilogue(a.scales, a.gates, a.out, id, o, slot, val);
 }
 
 __global__ __launch_bounds__(256) void gemv_reduce_kernel(GemvReduceArgs a) {

@@ -124,8 +124,7 @@ __device__ int mx_run_expert(const Mxfp4GemvArgs& a, const GemvCommon& c, MxShar
       }
     }
     __syncthreads();
-    gemv_reduce_store(c, reinterpret_cast<float*>(sh.buf), acc, sh.ch, nullptr, 0.0f, e, grp,
-                      s, ns);
+    gemv_reduce_store(c, reinterpret_cast<float*>(sh.buf), acc, sh.ch, e, grp, s, ns);
     if (pos >= c.N) break;
   }
   return found;
@@ -137,6 +136,9 @@ __global__ __launch_bounds__(GEMV_THREADS) void mxfp4_gemv_kernel(Mxfp4GemvArgs 
   c.ids = a.ids;
   c.gates = a.gates;
   c.scales = nullptr;
+  c.rowsum = nullptr;
+  c.acc_scale = 1.0f;
+  c.offset = 0.0f;
   c.y = a.y;
   c.partial = a.partial;
   c.N = (int)a.N;

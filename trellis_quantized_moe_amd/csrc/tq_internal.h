@@ -16,6 +16,7 @@ struct WsLayout {
   size_t counts = 0, offsets = 0, hist = 0, rank = 0, pairs = 0, items = 0, n_items = 0;
   size_t route_bytes = 0;
   size_t slots = 0, slots_bytes = 0;
+  size_t xprep = 0, rowsum = 0;
   size_t total = 0;
   int gemv_slices = 1, gemv_steps = 1, groups = 1, route_blocks = 1, max_items = 0;
   bool gemm = false;
@@ -34,7 +35,8 @@ struct TrellisGemvArgs {
   const int64_t* code_off;
   const uint32_t* codes;
   const uint16_t* scales;
-  const uint16_t* x;
+  const uint32_t* xp;      // prepared activations: f16 pairs [T][in/16][8]
+  const float* rowsum;     // [T]: sum of each token's f16 activations
   const int32_t* ids;
   const float* gates;
   float* y;
@@ -44,6 +46,10 @@ struct TrellisGemvArgs {
   int64_t N;
 };
 hipError_t launch_trellis_gemv(const TrellisGemvArgs& a, hipStream_t s);
+// x~ (bf16 [T][in]) -> f16 pairs [T][in/16][8] (word r = [lo: x[16c + r + 8], hi: x[16c + r]])
+// and per-token sums of the f16 values, for the decode-batch kernel.
+hipError_t launch_gemv_prep(const uint16_t* x, int64_t T, int in, uint32_t* xp, float* rowsum,
+                            hipStream_t s);
 
 struct TrellisGemmArgs {
   const uint8_t* bits;

@@ -97,18 +97,42 @@ __device__ __forceinline__ void col_mpairs_k3(uint32_t q0, uint32_t q1, uint32_t
   }
 }
 
-// ---- decode-batch operands: bytes as f16 ---------------------------------------------
-// The matrix cores take the two bytes of each product as separate f16 operands,
-// 1024 + byte (exact: f16 has 10 mantissa bits), both multiplied by the same activation.
-// The sum over a column is then sum x * (2048 + lo + hi) = sum x * (q + 2303); the
-// 2303 * sum(x) term is removed after accumulation.
-constexpr float GEMV_BYTE_OFFSET = 2303.0f;
+// ---- decode-batch operands: bytes as f16 subnormals -------------------------------------
+// The matrix cores take the two bytes of each product as separate f16 operands: a byte b
+// placed in the mantissa of an f16 with a zero exponent field is the subnormal b * 2^-24,
+// exact, and the matrix cores keep subnormal inputs. Both bytes meet the same activation,
+// so a column contributes 2^-24 * sum x * (lo + hi) = 2^-24 * sum x * (q + 255); the
+// epilogue multiplies by 2^24 (exact) and removes 255 * sum(x).
+//
+// The activations use one layout for every K: word r (r = 0..7) of a tile column holds
+// [lo: x[r + 8], hi: x[r]]. bytes_as_f16 builds the matching operands from a column's
+// m-pairs: L[r] = [lo: lo8(m[r + 8]), hi: lo8(m[r])] and H[r] the same with the high bytes,
+// each one byte permute (the two m values may sit in different m-pair registers).
+constexpr float GEMV_BYTE_OFFSET = 255.0f;
+constexpr float GEMV_BYTE_SCALE = 16777216.0f;  // 2^24
 
-__device__ __forceinline__ uint32_t mpair_low_bytes_f16(uint32_t M) {
-  return (M & 0x00FF00FFu) | 0x64006400u;   // [lo: 1024 + lo8(m_IL), hi: 1024 + lo8(m_IH)]
-}
-__device__ __forceinline__ uint32_t mpair_high_bytes_f16(uint32_t M) {
-  return perm(M, 0x64646464u, 0x00070005u); // [lo: 1024 + hi8(m_IL), hi: 1024 + hi8(m_IH)]
+template <int K>
+__device__ __forceinline__ void bytes_as_f16(const uint32_t M[8], uint32_t L[8], uint32_t H[8]) {
+  if constexpr (K == 4) {
+    // M[r] (r < 4) = [hi: m[r], lo: m[r + 4]]; M[r] (r >= 4) = [hi: m[r + 4], lo: m[r + 8]]
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {  // m[r] = M[r].hi, m[r + 8] = M[r + 4].hi
+      L[r] = perm(M[r], M[r + 4], 0x0C060C02u);
+      H[r] = perm(M[r], M[r + 4], 0x0C070C03u);
+    }
+#pragma unroll
+    for (int r = 4; r < 8; ++r) {  // m[r] = M[r - 4].lo, m[r + 8] = M[r].lo
+      L[r] = perm(M[r - 4], M[r], 0x0C040C00u);
+      H[r] = perm(M[r - 4], M[r], 0x0C050C01u);
+    }
+  } else {
+    // M[r] = [hi: m[r], lo: m[r + 8]]
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      L[r] = perm(M[r], M[r], 0x0C020C00u);
+      H[r] = perm(M[r], M[r], 0x0C030C01u);
+    }
+  }
 }
 
 // ---- prefill operands: q as bf16, natural input order ---------------------------------
