@@ -62,7 +62,7 @@ extern "C" {
  * "What is stored"; any layout works through the per-expert descriptor).
  */
 typedef struct tq_trellis_layer {
-  int32_t E;                /* experts in the layer, 1 .. 65535                          */
+  int32_t E;                /* experts in the layer, 1 .. 4096                           */
   int32_t out;              /* output channels per expert, multiple of 16                 */
   int32_t in;               /* inputs per expert, multiple of 256                         */
   int32_t reserved;         /* must be 0                                                  */
@@ -78,9 +78,9 @@ typedef struct tq_trellis_layer {
  * E8M0 scale bytes (row-major [out][in/32]).
  */
 typedef struct tq_mxfp4_layer {
-  int32_t E;                /* experts, 1 .. 65535                                        */
+  int32_t E;                /* experts, 1 .. 4096                                         */
   int32_t out;              /* output channels, multiple of 16                            */
-  int32_t in;               /* inputs, multiple of 256                                    */
+  int32_t in;               /* inputs, multiple of 512                                    */
   int32_t reserved;         /* must be 0                                                  */
   const uint8_t* units;     /* device: E * (out*in/2 + out*in/32) bytes, 16-aligned       */
 } tq_mxfp4_layer;
@@ -106,8 +106,12 @@ typedef struct tq_mxfp4_layer {
  *             bytes, 256-byte aligned, ZERO-FILLED BEFORE ITS FIRST USE. Every call leaves
  *             its counters at zero again, so a workspace is initialised once and reused;
  *             calls that share a workspace must be ordered on one stream.
- * Determinism: results are bitwise reproducible for a given mode and do not depend on
- * launch timing; a mixed-width layer gives the same bits as single-width layers.
+ * Determinism (FORMAT F14): the same inputs give the same bits, whatever the launch
+ * timing. The prefill mode also gives a slot the same bits whatever the rest of the batch
+ * (a mixed-width layer equals single-width layers). The decode-batch mode splits each
+ * routed expert's inputs among workgroups in proportion to the batch's whole routed work,
+ * so across batches that route differently a slot's fp32 sum is grouped differently and
+ * agrees to rounding (about 1e-7 relative).
  * Precondition of the decode-batch kernel: |x| < 65520 (it feeds the matrix cores f16
  * operands, FORMAT F10).
  */

@@ -76,8 +76,9 @@ def test_trellis_argument_errors(lib):
     assert _call_trellis(lib, _layer(), ws=0x10010) == _lib.TQ_EALIGN
     assert _call_trellis(lib, _layer(), ws_bytes=16) == _lib.TQ_EWORKSPACE
     assert b"workspace" in lib.tq_last_error()
-    # the prefill path is limited to E <= 4096
+    # layers are limited to E <= 4096 (both modes)
     assert _call_trellis(lib, _layer(E=5000), T=100000, topk=8, flags=_lib.TQ_GEMM) == _lib.TQ_EINVAL
+    assert _call_trellis(lib, _layer(E=5000), T=4, topk=8, flags=_lib.TQ_GEMV) == _lib.TQ_EINVAL
 
 
 def test_empty_batch_is_a_no_op(lib):

@@ -162,7 +162,7 @@ def test_deterministic_and_token_permutation():
         assert np.array_equal(c, a[perm])
 
 
-def test_mixed_width_equals_single_width_launches():
+def test_mixed_width_matches_single_width_launches():
     E, T, topk = 10, 40, 4
     widths = np.array([2, 3, 4, 2, 2, 3, 4, 2, 3, 2], dtype=np.uint8)
     mixed = small_layer(407, E, 128, 512, widths=widths)
@@ -186,7 +186,14 @@ def test_mixed_width_equals_single_width_launches():
             ids_k = np.where(widths[ids] == K, ids, -1).astype(np.int32)
             y_k = run(single, x, ids_k, flags=flags)
             sel = widths[ids] == K
-            assert np.array_equal(y_k[sel], y_mixed[sel]), (flags, K)
+            if flags == 2:
+                assert np.array_equal(y_k[sel], y_mixed[sel]), (flags, K)
+            else:
+                # the decode-batch kernel splits each expert's inputs among workgroups in
+                # proportion to the whole batch's work, so the fp32 partial sums are
+                # grouped differently in the two launches: equal up to rounding
+                err = np.abs(y_k[sel] - y_mixed[sel]).max() / np.abs(y_mixed[sel]).max()
+                assert err < 1e-5, (flags, K, err)
 
 
 def test_graph_replay_with_changing_routes():

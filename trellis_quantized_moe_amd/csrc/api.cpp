@@ -9,6 +9,7 @@
 
 #include "tq.h"
 #include "gemv_common.h"
+#include "gemv_plan.h"
 #include "tq_internal.h"
 
 namespace {
@@ -115,25 +116,37 @@ WsLayout ws_layout(int64_t T, int topk, int E, int out, int in, uint32_t flags, 
   L.groups = (out + 127) / 128;
   L.gemm = use_gemm(T, topk, E, flags);
   size_t off = 256;  // status word
-  if (!L.gemm) {
+  if (!L.gemm && !mxfp4) {
+    // planned decode batch: plan records, prepared activations, per-piece partial sums
+    const size_t Q = (size_t)in / 256;
+    L.info = off;
+    off += 256;
+    L.rec = off;
+    off += round_up((size_t)E * sizeof(tq::PlanRec), 256);
+    L.desc = off;
+    off += round_up((size_t)(tq::GEMV_MAX_G + 1) * 8, 256);
+    L.list = off;
+    off += round_up((size_t)N * 4, 256);
+    L.list_tok = off;
+    off += round_up((size_t)N * 4, 256);
+    L.slot_info = off;
+    off += round_up((size_t)N * 16, 256);
+    L.prank = off;
+    off += round_up((size_t)N * 4, 256);
+    L.xprep = off;
+    off += round_up((size_t)T * in * 2, 256);
+    L.rowsum = off;
+    off += round_up((size_t)T * 4, 256);
+    L.partial = off;
+    L.partial_bytes = round_up(Q * N * out * 4, 256);
+    off += L.partial_bytes;
+  } else if (!L.gemm) {
     const int64_t active = N < E ? N : E;
     const int64_t wgs_per_slice = (active > 0 ? active : 1) * L.groups;
     const int target = (int)((1024 + wgs_per_slice - 1) / wgs_per_slice);
-    if (mxfp4) {
-      const int units = in / 512;
-      L.gemv_steps = pick_steps(units, 2, target);
-      L.gemv_slices = units / L.gemv_steps;
-    } else {
-      const int units = in / 256;
-      L.gemv_steps = pick_steps(units, units, target);
-      L.gemv_slices = units / L.gemv_steps;
-    }
-    if (!mxfp4) {
-      L.xprep = off;
-      off += round_up((size_t)T * in * 2, 256);
-      L.rowsum = off;
-      off += round_up((size_t)T * 4, 256);
-    }
+    const int units = in / 512;
+    L.gemv_steps = pick_steps(units, 2, target);
+    L.gemv_slices = units / L.gemv_steps;
     if (L.gemv_slices > 1) {
       L.partial = off;
       L.partial_bytes = round_up((size_t)L.gemv_slices * N * out * 4, 256);
@@ -159,7 +172,7 @@ WsLayout ws_layout(int64_t T, int topk, int E, int out, int in, uint32_t flags, 
     off += 256;
     L.route_bytes = off - start;
   }
-  if ((flags & TQ_COMBINE) && (L.gemm || L.gemv_slices == 1)) {
+  if ((flags & TQ_COMBINE) && (L.gemm || (mxfp4 && L.gemv_slices == 1))) {
     L.slots = off;
     L.slots_bytes = round_up((size_t)N * out * 4, 256);
     off += L.slots_bytes;
@@ -289,7 +302,7 @@ namespace {
 
 int check_trellis_layer(const tq_trellis_layer* L) {
   if (!L) return fail(TQ_EINVAL, "layer is NULL");
-  if (L->E < 1 || L->E > 65535) return fail(TQ_EINVAL, "E = %d is outside 1..65535", L->E);
+  if (L->E < 1 || L->E > 4096) return fail(TQ_EINVAL, "E = %d is outside 1..4096", L->E);
   if (L->out <= 0 || L->out % 16) return fail(TQ_EINVAL, "out = %d is not a positive multiple of 16", L->out);
   if (L->in <= 0 || L->in % 256) return fail(TQ_EINVAL, "in = %d is not a positive multiple of 256", L->in);
   if (L->reserved != 0) return fail(TQ_EINVAL, "reserved field must be 0");
@@ -303,7 +316,7 @@ int check_trellis_layer(const tq_trellis_layer* L) {
 
 int check_mxfp4_layer(const tq_mxfp4_layer* L) {
   if (!L) return fail(TQ_EINVAL, "layer is NULL");
-  if (L->E < 1 || L->E > 65535) return fail(TQ_EINVAL, "E = %d is outside 1..65535", L->E);
+  if (L->E < 1 || L->E > 4096) return fail(TQ_EINVAL, "E = %d is outside 1..4096", L->E);
   if (L->out <= 0 || L->out % 16) return fail(TQ_EINVAL, "out = %d is not a positive multiple of 16", L->out);
   if (L->in <= 0 || L->in % 512) return fail(TQ_EINVAL, "in = %d is not a positive multiple of 512", L->in);
   if (L->reserved != 0) return fail(TQ_EINVAL, "reserved field must be 0");
@@ -322,8 +335,14 @@ int common_checks(int E, int out, int in, const void* x, int64_t T, const int32_
   rc = check_io(T, x, y);
   if (rc) return rc;
   *layout = tq::ws_layout(T, topk, E, out, in, flags, mxfp4);
-  if (layout->gemm && E > 4096)
-    return fail(TQ_EINVAL, "the prefill path supports E <= 4096 (E = %d)", E);
+  if ((layout->gemm || !mxfp4) && E > 4096)
+    return fail(TQ_EINVAL, "this path supports E <= 4096 (E = %d)", E);
+  if (!layout->gemm && !mxfp4 && (int64_t)E * layout->groups * (in / 256) * 4 >= ((int64_t)1 << 31))
+    return fail(TQ_EINVAL, "E * out * in is too large for the decode-batch plan");
+  if (!layout->gemm && !mxfp4 && T * (int64_t)in * 2 >= ((int64_t)1 << 31))
+    return fail(TQ_EINVAL, "T * in is too large for the decode-batch path");
+  if (!layout->gemm && !mxfp4 && (int64_t)out * in / 2 >= ((int64_t)1 << 31))
+    return fail(TQ_EINVAL, "out * in is too large for the decode-batch path");
   if (T == 0) return TQ_OK;
   return check_ws(ws, ws_bytes, layout->total);
 }
@@ -398,36 +417,71 @@ int trellis_expert_gemm(const tq_trellis_layer* L, const void* x, int64_t T,
   const uint16_t* xb = static_cast<const uint16_t*>(x);
   hipError_t err;
   if (!W.gemm) {
-    err = tq::launch_gemv_prep(xb, T, L->in, at<uint32_t>(ws, W.xprep), at<float>(ws, W.rowsum), s);
-    if (err != hipSuccess) return hip_fail(err, "activation prep launch");
+    const int G = tq::trellis_gemv_grid();
+    if (G <= 0) return fail(TQ_EHIP, "could not size the GEMV grid");
+    const int Q = L->in / 256;
+    tq::PlanArgs p{};
+    p.ids = topk_ids;
+    p.N = (int)N;
+    p.E = L->E;
+    p.topk = topk;
+    p.bits = L->bits;
+    p.code_off = L->code_off;
+    p.unit_bytes = 0;
+    p.U = W.groups * Q;
+    p.G = G;
+    p.info = at<int32_t>(ws, W.info);
+    p.rec = at<tq::PlanRec>(ws, W.rec);
+    p.desc = at<int2>(ws, W.desc);
+    p.list = at<int32_t>(ws, W.list);
+    p.list_tok = at<int32_t>(ws, W.list_tok);
+    p.slot_info = at<int4>(ws, W.slot_info);
+    p.rank = at<int32_t>(ws, W.prank);
+    p.status = at<uint32_t>(ws, W.status);
+    p.x = xb;
+    p.T = (int)T;
+    p.in = L->in;
+    p.xp = at<uint32_t>(ws, W.xprep);
+    p.rowsum = at<float>(ws, W.rowsum);
+    err = tq::launch_gemv_plan(p, s);
+    if (err != hipSuccess) return hip_fail(err, "decode plan launch");
     tq::TrellisGemvArgs a{};
-    a.bits = L->bits;
-    a.code_off = L->code_off;
     a.codes = L->codes;
-    a.scales = L->scales;
-    a.xp = at<uint32_t>(ws, W.xprep);
-    a.rowsum = at<float>(ws, W.rowsum);
-    a.ids = topk_ids;
-    a.gates = topk_w;
-    a.y = y_slots;
-    a.partial = W.gemv_slices > 1 ? at<float>(ws, W.partial) : nullptr;
-    a.status = at<uint32_t>(ws, W.status);
+    a.xp = p.xp;
+    a.info = p.info;
+    a.rec = p.rec;
+    a.desc = p.desc;
+    a.list = p.list;
+    a.list_tok = p.list_tok;
+    a.partial = at<float>(ws, W.partial);
+    a.x_bytes = (uint32_t)(T * L->in * 2);
+    a.N = (int)N;
     a.E = L->E;
     a.out = L->out;
     a.in = L->in;
     a.topk = topk;
-    a.S = W.gemv_slices;
-    a.steps = W.gemv_steps;
     a.groups = W.groups;
-    a.N = N;
+    a.G = G;
     err = tq::launch_trellis_gemv(a, s);
     if (err != hipSuccess) return hip_fail(err, "trellis GEMV launch");
-    if (W.gemv_slices > 1) {
-      rc = run_gemv_reduce(W, ws, topk_ids, L->scales, topk_w, at<float>(ws, W.rowsum),
-                           16777216.0f, 255.0f, y, N, L->E, L->out, topk, flags, s);
-      if (rc) return rc;
-      return ok();
-    }
+    tq::PieceReduceArgs r{};
+    r.slot_info = p.slot_info;
+    r.info = p.info;
+    r.partial = a.partial;
+    r.scales = L->scales;
+    r.gates = topk_w;
+    r.rowsum = p.rowsum;
+    r.y = y;
+    r.acc_scale = 16777216.0f;
+    r.offset = 255.0f;
+    r.N = (int)N;
+    r.out = L->out;
+    r.topk = topk;
+    r.Q = Q;
+    r.combine = (flags & TQ_COMBINE) ? 1 : 0;
+    err = tq::launch_piece_reduce(r, s);
+    if (err != hipSuccess) return hip_fail(err, "GEMV piece reduction launch");
+    return ok();
   } else {
     rc = run_route(W, ws, topk_ids, N, L->E, L->out, y_slots, s);
     if (rc) return rc;

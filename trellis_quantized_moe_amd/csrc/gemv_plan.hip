@@ -1,0 +1,315 @@
+// Decode-batch plan and activation prep, one launch (see gemv_plan.h for the scheme).
+//
+// Block 0 plans. It counts the slots of every expert with shared-memory atomics, which
+// also gives each slot its position in its expert's list. Positions within one expert
+// therefore follow arrival order, but every output is computed by arithmetic that does not
+// depend on its row position, so the results are the same bits whatever the order. A
+// block-wide scan then gives list starts, the active experts in ascending id order and the
+// cost prefix over them. Last come the slot lists, the per-slot records and the first unit
+// of every GEMV workgroup's range.
+//
+// Blocks 1..T convert token t = block - 1 of x~ (bf16) to the f16 operand layout of the
+// trellis GEMV (word r of tile column c = [lo: x[16c + r + 8], hi: x[16c + r]], rounded to
+// nearest even) and sum the token's f16 values in a fixed order.
+#include "gemv_plan.h"
+#include "tq_internal.h"
+
+namespace tq {
+
+namespace {
+
+constexpr int PLAN_R = 4;                            // slots per thread kept in registers
+constexpr int PLAN_PER = PLAN_MAX_E / PLAN_THREADS;  // experts per thread in the scan
+constexpr int PLAN_WAVES = PLAN_THREADS / 64;
+
+// Exclusive block scan of three ints over PLAN_THREADS threads, in place; tot = totals.
+__device__ void block_scan3(int& x0, int& x1, int& x2, int tot[3]) {
+  __shared__ int part[3][PLAN_WAVES];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  int i0 = x0, i1 = x1, i2 = x2;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int t0 = __shfl_up(i0, d, 64), t1 = __shfl_up(i1, d, 64), t2 = __shfl_up(i2, d, 64);
+    if (lane >= d) {
+      i0 += t0;
+      i1 += t1;
+      i2 += t2;
+    }
+  }
+  if (lane == 63) {
+    part[0][w] = i0;
+    part[1][w] = i1;
+    part[2][w] = i2;
+  }
+  lds_barrier();
+  int b0 = 0, b1 = 0, b2 = 0;
+  tot[0] = tot[1] = tot[2] = 0;
+#pragma unroll
+  for (int v = 0; v < PLAN_WAVES; ++v) {
+    const int p0 = part[0][v], p1 = part[1][v], p2 = part[2][v];
+    if (v < w) {
+      b0 += p0;
+      b1 += p1;
+      b2 += p2;
+    }
+    tot[0] += p0;
+    tot[1] += p1;
+    tot[2] += p2;
+  }
+  x0 = b0 + i0 - x0;
+  x1 = b1 + i1 - x1;
+  x2 = b2 + i2 - x2;
+}
+
+// The plan is one block of PLAN_THREADS threads; each phase gives a thread about one slot,
+// one expert and one workgroup, so that no thread runs a long chain of dependent steps.
+template <bool TRELLIS>
+__device__ void plan_block(const PlanArgs& a) {
+  __shared__ int s_start[PLAN_MAX_E];   // slot counts, then list starts
+  __shared__ int s_aidx[PLAN_MAX_E];    // active index, or SLOT_EMPTY / SLOT_BAD_UNIT
+  __shared__ int s_P[PLAN_MAX_E + 1];   // cost prefix by active index
+  __shared__ uint8_t s_ka[PLAN_MAX_E];  // unit cost by active index
+  __shared__ uint32_t s_status;
+  const int tid = threadIdx.x;
+  const int N = a.N, E = a.E, U = a.U;
+  const bool in_regs = N <= PLAN_THREADS * PLAN_R;
+
+  // all route and descriptor loads are issued before any is used (indices clamped; slots
+  // past N and experts past E are skipped where used)
+  int id[PLAN_R], rk[PLAN_R];
+  if (in_regs) {
+#pragma unroll
+    for (int j = 0; j < PLAN_R; ++j) id[j] = a.ids[min(tid + PLAN_THREADS * j, N - 1)];
+  }
+  const int e0 = tid * PLAN_PER;  // this thread's experts e0 .. e0 + PLAN_PER - 1
+  int kk[PLAN_PER];
+  int64_t off[PLAN_PER];
+  if constexpr (TRELLIS) {
+#pragma unroll
+    for (int j = 0; j < PLAN_PER; ++j) {
+      const int e = min(e0 + j, E - 1);
+      kk[j] = a.bits[e];
+      off[j] = a.code_off[e];
+    }
+#pragma unroll
+    for (int j = 0; j < PLAN_PER; ++j)
+      kk[j] = (kk[j] >= 2 && kk[j] <= 4 && (off[j] & 15) == 0) ? kk[j] : 0;
+  } else {
+#pragma unroll
+    for (int j = 0; j < PLAN_PER; ++j) {
+      kk[j] = 1;
+      off[j] = (int64_t)(e0 + j) * a.unit_bytes;
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < PLAN_PER; ++j)
+    if (e0 + j < E) s_start[e0 + j] = 0;
+  if (tid == 0) s_status = 0;
+  lds_barrier();
+
+  // counts; a slot's position in its expert's list is the count before its own increment
+  uint32_t bad = 0;
+  if (in_regs) {
+#pragma unroll
+    for (int j = 0; j < PLAN_R; ++j) {
+      rk[j] = 0;
+      if (PLAN_THREADS * j < N) {  // uniform
+        if (tid + PLAN_THREADS * j < N && id[j] >= 0 && id[j] < E)
+          rk[j] = atomicAdd(&s_start[id[j]], 1);
+      }
+    }
+  } else {
+    for (int i = tid; i < N; i += PLAN_THREADS) {
+      const int v = a.ids[i];
+      if (v >= 0 && v < E) a.rank[i] = atomicAdd(&s_start[v], 1);
+    }
+  }
+  lds_barrier();
+
+  // scan over experts: list starts, active indices, cost prefix
+  int cnt[PLAN_PER];
+  int sc = 0, sa = 0, scost = 0;
+#pragma unroll
+  for (int j = 0; j < PLAN_PER; ++j) {
+    cnt[j] = e0 + j < E ? s_start[e0 + j] : 0;
+    const bool act = cnt[j] > 0 && kk[j] > 0;
+    sc += cnt[j];
+    sa += act ? 1 : 0;
+    scost += act ? kk[j] * U : 0;
+  }
+  int tot[3];
+  block_scan3(sc, sa, scost, tot);
+#pragma unroll
+  for (int j = 0; j < PLAN_PER; ++j) {
+    const int e = e0 + j;
+    if (e < E) {
+      s_start[e] = sc;
+      if (cnt[j] > 0 && kk[j] > 0) {
+        s_aidx[e] = sa;
+        s_P[sa] = scost;
+        s_ka[sa] = (uint8_t)kk[j];
+        PlanRec r;
+        r.e = e;
+        r.start = sc;
+        r.cnt = cnt[j];
+        r.k = kk[j];
+        r.off = off[j];
+        r.p0 = scost;
+        r.pad = 0;
+        a.rec[sa] = r;
+        sa += 1;
+        scost += kk[j] * U;
+      } else {
+        s_aidx[e] = cnt[j] > 0 ? SLOT_BAD_UNIT : SLOT_EMPTY;
+      }
+      sc += cnt[j];
+    }
+  }
+  const int n_act = tot[1], C = tot[2];
+  // Workgroups that get work: at most C / (largest unit cost), so that every range holds
+  // at least one unit start and the pieces of an expert's group are consecutive workgroups
+  // (piece index < units per group).
+  const int kmax = TRELLIS ? 4 : 1;
+  int Geff = C / kmax;
+  Geff = Geff < a.G ? Geff : a.G;
+  Geff = Geff > 1 ? Geff : 1;
+  if (tid == 0) {
+    s_P[n_act] = C;
+    a.info[0] = n_act;
+    a.info[1] = C;
+    a.info[2] = Geff;
+  }
+  lds_barrier();
+
+  // slot lists and per-slot records
+  auto place = [&](int i, int v, int r) {
+    int4 inf = make_int4(SLOT_EMPTY, 0, 0, 0);
+    if (v == -1) {
+    } else if (v < -1 || v >= E) {
+      inf.x = SLOT_BAD_ID;
+      bad |= STATUS_BAD_EXPERT;
+    } else {
+      const int ai = s_aidx[v];
+      if (ai < 0) {
+        inf.x = SLOT_BAD_UNIT;
+        bad |= STATUS_BAD_UNIT;
+      } else {
+        a.list[s_start[v] + r] = i;
+        a.list_tok[s_start[v] + r] = i / a.topk;
+        inf = make_int4(v, s_P[ai], s_ka[ai], 0);
+      }
+    }
+    a.slot_info[i] = inf;
+  };
+  if (in_regs) {
+#pragma unroll
+    for (int j = 0; j < PLAN_R; ++j) {
+      const int i = tid + PLAN_THREADS * j;
+      if (i < N) place(i, id[j], rk[j]);
+    }
+  } else {
+    for (int i = tid; i < N; i += PLAN_THREADS) {
+      const int v = a.ids[i];
+      place(i, v, (v >= 0 && v < E) ? a.rank[i] : 0);
+    }
+  }
+
+  // first unit of every workgroup's range; workgroups Geff .. G get the end (empty ranges)
+  for (int w = tid; w <= a.G; w += PLAN_THREADS) {
+    int lo = n_act, u = 0;
+    if (w < Geff) {
+      const int c0 = (int)((int64_t)w * C / Geff);
+      lo = 0;
+      int hi = n_act;  // smallest active index with s_P[ai + 1] > c0, or n_act
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (s_P[mid + 1] > c0)
+          hi = mid;
+        else
+          lo = mid + 1;
+      }
+      if (lo < n_act) {
+        const int k = s_ka[lo];
+        u = (c0 - s_P[lo] + k - 1) / k;
+        if (u >= U) {
+          ++lo;
+          u = 0;
+        }
+      }
+    }
+    a.desc[w] = make_int2(lo, u);
+  }
+
+  if (bad) atomicOr(&s_status, bad);
+  lds_barrier();
+  if (tid == 0 && s_status) set_status(a.status, s_status);
+}
+
+// One token per block: thread c converts tile column c (columns c + PLAN_THREADS, ... when
+// in > 16 * PLAN_THREADS). Waves without a column leave at once.
+__device__ void prep_block(const PlanArgs& a, int t) {
+  typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+  __shared__ float s_sum[PLAN_WAVES];
+  const int tid = threadIdx.x;
+  const int n_ti = a.in / 16;
+  const int active = n_ti < PLAN_THREADS ? n_ti : PLAN_THREADS;
+  if ((tid & ~63) >= active) return;  // whole wave
+  const uint4* src = reinterpret_cast<const uint4*>(a.x + (size_t)t * a.in);
+  uint4* dst = reinterpret_cast<uint4*>(a.xp + (size_t)t * n_ti * 8);
+  float sum = 0.0f;
+  for (int c = tid; c < n_ti; c += PLAN_THREADS) {
+    const uint4 u = src[2 * c], v = src[2 * c + 1];
+    const uint32_t wv[8] = {u.x, u.y, u.z, u.w, v.x, v.y, v.z, v.w};
+    float f[16];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      f[2 * k] = bf16_lo_to_f32(wv[k]);
+      f[2 * k + 1] = bf16_hi_to_f32(wv[k]);
+    }
+    uint32_t P[8];
+    float hf[16];
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      const h2 p = (h2){(_Float16)f[r + 8], (_Float16)f[r]};
+      P[r] = __builtin_bit_cast(uint32_t, p);
+      hf[r] = (float)p.y;
+      hf[r + 8] = (float)p.x;
+    }
+    float cs = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) cs += hf[i];
+    sum += cs;
+    dst[2 * c] = make_uint4(P[0], P[1], P[2], P[3]);
+    dst[2 * c + 1] = make_uint4(P[4], P[5], P[6], P[7]);
+  }
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) sum += __shfl_xor(sum, d, 64);
+  if ((tid & 63) == 0) s_sum[tid >> 6] = sum;
+  lds_barrier();
+  if (tid == 0) {
+    float s = 0.0f;
+    for (int w = 0; w < (active + 63) / 64; ++w) s += s_sum[w];
+    a.rowsum[t] = s;
+  }
+}
+
+template <bool TRELLIS>
+__global__ __launch_bounds__(PLAN_THREADS) void gemv_plan_kernel(PlanArgs a) {
+  if (blockIdx.x == 0)
+    plan_block<TRELLIS>(a);
+  else
+    prep_block(a, blockIdx.x - 1);
+}
+
+}  // namespace
+
+hipError_t launch_gemv_plan(const PlanArgs& a, hipStream_t s) {
+  const unsigned blocks = 1 + (a.x ? (unsigned)a.T : 0u);
+  if (a.bits)
+    hipLaunchKernelGGL(gemv_plan_kernel<true>, dim3(blocks), dim3(PLAN_THREADS), 0, s, a);
+  else
+    hipLaunchKernelGGL(gemv_plan_kernel<false>, dim3(blocks), dim3(PLAN_THREADS), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace tq

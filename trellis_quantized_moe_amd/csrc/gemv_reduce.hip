@@ -50,3 +50,105 @@ hipError_t launch_gemv_reduce(const GemvReduceArgs& a, hipStream_t s) {
 }
 
 }  // namespace tq
+
+// ---- piece reduction (trellis decode batches) ---------------------------------------------
+// Third launch of the planned decode-batch path (gemv_plan.h). A slot's expert group was
+// split into pieces by the plan; their partial sums are added in piece order, scaled by
+// acc_scale, corrected by offset * rowsum[token], then scaled per channel and gated. Empty
+// slots give 0, bad ids and bad units NaN (their status bits were set by the plan). Without
+// combine, one thread per 4 outputs of a slot; with combine, one block per (token, 128
+// outputs) puts the slot values in LDS and adds them over k = 0..topk-1 in order.
+#include "gemv_plan.h"
+#include "tq_internal.h"
+
+namespace tq {
+
+namespace {
+
+__device__ __forceinline__ void add4(float4& s, const float4& v) {
+  s.x += v.x;
+  s.y += v.y;
+  s.z += v.z;
+  s.w += v.w;
+}
+
+__device__ __forceinline__ float4 piece_slot(const PieceReduceArgs& a, int slot, int o, int64_t C,
+                                             int G) {
+  const int4 inf = a.slot_info[slot];
+  const float corr = a.rowsum ? a.offset * a.rowsum[slot / a.topk] : 0.0f;
+  const float gate = a.gates ? a.gates[slot] : 1.0f;
+  if (inf.x == SLOT_EMPTY) return make_float4(0.f, 0.f, 0.f, 0.f);
+  if (inf.x < 0) {
+    const float nan = __builtin_nanf("");
+    return make_float4(nan, nan, nan, nan);
+  }
+  const int e = inf.x, grp = o / 128;
+  const int64_t cs = (int64_t)inf.y + (int64_t)grp * a.Q * inf.z;
+  const int np = plan_owner(cs + (int64_t)(a.Q - 1) * inf.z, C, G) - plan_owner(cs, C, G) + 1;
+  const size_t stride = (size_t)a.N * a.out;
+  const float* p = a.partial + (size_t)slot * a.out + o;
+  const uint2 sc = *reinterpret_cast<const uint2*>(a.scales + (size_t)e * a.out + o);
+  // the first four pieces are requested together (clamped indices, unused ones dropped)
+  float4 v[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) v[q] = *reinterpret_cast<const float4*>(p + (size_t)min(q, np - 1) * stride);
+  float4 s = v[0];
+#pragma unroll
+  for (int q = 1; q < 4; ++q)
+    if (q < np) add4(s, v[q]);
+  for (int q = 4; q < np; ++q) add4(s, *reinterpret_cast<const float4*>(p + (size_t)q * stride));
+  const uint32_t sw[2] = {sc.x, sc.y};
+  float r[4] = {s.x, s.y, s.z, s.w};
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    r[j] = r[j] * a.acc_scale - corr;
+    r[j] = r[j] * f16_bits_to_f32(sw[j >> 1] >> (16 * (j & 1)));
+    if (a.gates) r[j] = r[j] * gate;
+  }
+  return make_float4(r[0], r[1], r[2], r[3]);
+}
+
+__global__ __launch_bounds__(256) void piece_reduce_kernel(PieceReduceArgs a) {
+  const int64_t C = a.info[1];
+  const int G = a.info[2];
+  const int per_row = a.out / 4;
+  if (!a.combine) {
+    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (idx >= (int64_t)a.N * per_row) return;
+    const int r = (int)(idx / per_row), o = (int)(idx % per_row) * 4;
+    *reinterpret_cast<float4*>(a.y + (size_t)r * a.out + o) = piece_slot(a, r, o, C, G);
+    return;
+  }
+  // block = (token t, outputs o0 .. o0 + 127); LDS holds the topk slot values
+  __shared__ float4 vals[PIECE_MAX_TOPK * 32];
+  const int chunks = (a.out + 127) / 128;
+  const int t = blockIdx.x / chunks, o0 = (blockIdx.x % chunks) * 128;
+  const int w4 = min(128, a.out - o0) / 4;  // float4 columns in this chunk
+  for (int v = threadIdx.x; v < a.topk * 32; v += 256) {
+    const int k = v / 32, c = v % 32;
+    if (c < w4) vals[v] = piece_slot(a, t * a.topk + k, o0 + 4 * c, C, G);
+  }
+  lds_barrier();
+  if ((int)threadIdx.x < w4) {
+    float4 acc = vals[threadIdx.x];
+    for (int k = 1; k < a.topk; ++k) add4(acc, vals[k * 32 + threadIdx.x]);
+    *reinterpret_cast<float4*>(a.y + (size_t)t * a.out + o0 + 4 * threadIdx.x) = acc;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_piece_reduce(const PieceReduceArgs& a, hipStream_t s) {
+  unsigned blocks;
+  if (a.combine) {
+    blocks = (unsigned)((int64_t)(a.N / a.topk) * ((a.out + 127) / 128));
+  } else {
+    const int64_t total = (int64_t)a.N * (a.out / 4);
+    blocks = (unsigned)((total + 255) / 256);
+  }
+  if (blocks == 0) return hipSuccess;
+  hipLaunchKernelGGL(piece_reduce_kernel, dim3(blocks), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace tq

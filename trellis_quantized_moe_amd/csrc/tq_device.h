@@ -60,6 +60,16 @@ __device__ __forceinline__ float f16_bits_to_f32(uint32_t h) {
   return (float)__builtin_bit_cast(_Float16, (unsigned short)(h & 0xFFFFu));
 }
 
+// Workgroup barrier that orders LDS only. __syncthreads() is also a fence for global
+// memory, so each wave first waits for all of its outstanding global loads and stores; a
+// kernel that keeps streaming loads in flight, or has just issued result stores, across a
+// barrier would stall on them. These fences cover the LDS address space only.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // Workspace status word: sticky error bits (relaxed device-scope OR).
 constexpr uint32_t STATUS_BAD_EXPERT = 1u;  // an id outside [-1, E)
 constexpr uint32_t STATUS_BAD_UNIT = 2u;    // width byte not in {2,3,4} or misaligned unit

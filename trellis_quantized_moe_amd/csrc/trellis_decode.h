@@ -97,41 +97,42 @@ __device__ __forceinline__ void col_mpairs_k3(uint32_t q0, uint32_t q1, uint32_t
   }
 }
 
-// ---- decode-batch operands: bytes as f16 subnormals -------------------------------------
-// The matrix cores take the two bytes of each product as separate f16 operands: a byte b
-// placed in the mantissa of an f16 with a zero exponent field is the subnormal b * 2^-24,
-// exact, and the matrix cores keep subnormal inputs. Both bytes meet the same activation,
-// so a column contributes 2^-24 * sum x * (lo + hi) = 2^-24 * sum x * (q + 255); the
-// epilogue multiplies by 2^24 (exact) and removes 255 * sum(x).
+// ---- decode-batch operands: byte sums as f16 subnormals ---------------------------------
+// The matrix cores take v = lo8(m) + hi8(m) = q + 255 (0..510) as the bits of an f16 with a
+// zero exponent field, i.e. the subnormal v * 2^-24, exact (the matrix cores keep subnormal
+// inputs). A 16-bit lane computes v = m - 255 * (m >> 8) with one packed shift and one
+// packed multiply-add. The accumulator then holds 2^-24 * sum x * (q + 255); the epilogue
+// multiplies by 2^24 (exact) and removes 255 * sum(x).
 //
 // The activations use one layout for every K: word r (r = 0..7) of a tile column holds
-// [lo: x[r + 8], hi: x[r]]. bytes_as_f16 builds the matching operands from a column's
-// m-pairs: L[r] = [lo: lo8(m[r + 8]), hi: lo8(m[r])] and H[r] the same with the high bytes,
-// each one byte permute (the two m values may sit in different m-pair registers).
+// [lo: x[r + 8], hi: x[r]], and byte_sums returns the weights in the same layout:
+// V[r] = [lo: v[r + 8], hi: v[r]].
 constexpr float GEMV_BYTE_OFFSET = 255.0f;
 constexpr float GEMV_BYTE_SCALE = 16777216.0f;  // 2^24
 
+__device__ __forceinline__ uint32_t byte_sum_pair(uint32_t M) {
+  u16x2 m = __builtin_bit_cast(u16x2, M);
+  u16x2 h = m >> (u16x2){8, 8};
+  u16x2 v = m + h * (u16x2){0xFF01, 0xFF01};  // m - 255 * h (mod 2^16)
+  return __builtin_bit_cast(uint32_t, v);
+}
+
 template <int K>
-__device__ __forceinline__ void bytes_as_f16(const uint32_t M[8], uint32_t L[8], uint32_t H[8]) {
+__device__ __forceinline__ void byte_sums(const uint32_t M[8], uint32_t V[8]) {
   if constexpr (K == 4) {
     // M[r] (r < 4) = [hi: m[r], lo: m[r + 4]]; M[r] (r >= 4) = [hi: m[r + 4], lo: m[r + 8]]
+    uint32_t W[8];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {  // m[r] = M[r].hi, m[r + 8] = M[r + 4].hi
-      L[r] = perm(M[r], M[r + 4], 0x0C060C02u);
-      H[r] = perm(M[r], M[r + 4], 0x0C070C03u);
-    }
+    for (int r = 0; r < 8; ++r) W[r] = byte_sum_pair(M[r]);
 #pragma unroll
-    for (int r = 4; r < 8; ++r) {  // m[r] = M[r - 4].lo, m[r + 8] = M[r].lo
-      L[r] = perm(M[r - 4], M[r], 0x0C040C00u);
-      H[r] = perm(M[r - 4], M[r], 0x0C050C01u);
+    for (int r = 0; r < 4; ++r) {
+      V[r] = perm(W[r], W[r + 4], 0x07060302u);      // [hi: v[r], lo: v[r + 8]]
+      V[r + 4] = perm(W[r], W[r + 4], 0x05040100u);  // [hi: v[r + 4], lo: v[r + 12]]
     }
   } else {
     // M[r] = [hi: m[r], lo: m[r + 8]]
 #pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      L[r] = perm(M[r], M[r], 0x0C020C00u);
-      H[r] = perm(M[r], M[r], 0x0C030C01u);
-    }
+    for (int r = 0; r < 8; ++r) V[r] = byte_sum_pair(M[r]);
   }
 }
 

@@ -1,25 +1,24 @@
 // Decode-batch grouped GEMV over trellis-coded experts (gfx950).
 //
-// One workgroup of 4 waves per (expert, group of up to 8 output strips = 128 channels,
-// K-slice); each wave owns a quarter of the slice and runs as an independent pipeline
-// until one final barrier:
-//   1. route scan: the wave reads the routes and keeps, in index order, the first 16
-//      slots routed to its expert (ballot + bit count; no barrier);
-//   2. stream: per step of 4 tile columns, every lane decodes one tile column (16
-//      weights) of each of the 8 strips and feeds the matrix cores; the activations of
-//      the 16 token rows come straight from the prepared f16 buffer (gemv_prep, once per
-//      call) into A-operand registers. Code words and activations of the next step are
-//      requested while the current step is decoded;
-//   3. the four waves' accumulators are added through LDS in wave order and either
-//      finished (one slice) or stored as the slice's partial sums.
-// Per tile column a lane issues one load; the 16 lanes of a row read consecutive words and
-// the 4 rows of a wave read 4 consecutive tiles, so each load instruction is one
-// contiguous run. Tile addresses are wave-uniform (scalar registers).
+// The grid is exactly as many workgroups as the GPU holds at once; workgroup w streams the
+// units of its range of the plan (see gemv_plan.h), expert by expert. For each piece (one
+// expert's units of one output group inside the range) the four waves of the workgroup
+// split every unit: wave v takes tile columns 4v .. 4v + 3 of each of the unit's 16, so a
+// wave's step is 4 tile columns of 8 strips, and the four waves read neighbouring tiles.
+// Per step and strip, each lane decodes one tile column (16 weights of one output channel)
+// and the wave feeds two 16 x 16 x 32 matrix-core operations, with the activations of up
+// to 16 routed token rows as the other operand (rows past the expert's count are zero).
 //
-// The matrix cores see each weight as two f16 subnormal operands, lo8(m) * 2^-24 and
-// hi8(m) * 2^-24 (see trellis_decode.h), both against the same activation; the epilogue
-// scales by 2^24 and removes 255 * sum(x) per token.
-#include "gemv_common.h"
+// Code words are requested D steps ahead (D = 4 at K = 2, 2 at K = 3 and 4), held in D
+// register sets used in turn, so that several steps of loads are in flight per wave, and
+// so are the activations (prepared once per call, f16). The load of a
+// strip's next words is issued right after its current words are decoded.
+//
+// At the end of a piece the four waves' accumulators are added through LDS in wave order
+// and the piece's sums are stored for the reduction launch, which adds the pieces in order
+// and applies the epilogue. Each weight reaches the matrix cores as the f16 subnormal
+// (q + 255) * 2^-24 (see trellis_decode.h).
+#include "gemv_plan.h"
 #include "tq_internal.h"
 #include "trellis_decode.h"
 
@@ -27,48 +26,14 @@ namespace tq {
 
 namespace {
 
+constexpr int GEMV_THREADS = 256;
+constexpr int GEMV_WAVES_PER_SIMD = 3;  // register budget: 168 per lane
+constexpr int GEMV_GRID_MULT = 1;       // workgroups per resident slot
+
 struct Shared {
   float red[4 * 8 * 4 * 64];  // [wave][strip][i][lane]
-  int slots[4][16];           // per wave: the chunk's slots (identical in every wave)
-  SlotChunk ch;               // the chunk as seen by the epilogue
+  int slots[16];              // the chunk's slots
 };
-
-// ---- wave-level route scan ---------------------------------------------------------------
-// Up to 16 slots with ids[slot] == e from position pos on, ascending, into sl[0..cnt).
-// Returns cnt; *next = where the following chunk resumes (N when the routes are done).
-// 1024 ids are requested at once, so a decode batch takes one round trip.
-__device__ __forceinline__ int wave_collect(const int32_t* __restrict__ ids, int N, int e, int pos,
-                                   int* sl, int* next) {
-  const int lane = threadIdx.x & 63;
-  int have = 0;
-  *next = N;
-  for (int base = pos; base < N; base += 1024) {
-    int id[16];
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const int i = base + 64 * j + lane;
-      id[j] = i < N ? ids[i] : -1;
-    }
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const uint64_t m = __ballot(id[j] == e);
-      const int r = have + (int)__builtin_amdgcn_mbcnt_hi(
-                               (uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
-      if (id[j] == e && r < 16) sl[r] = base + 64 * j + lane;
-      const int total = have + (int)__popcll(m);
-      if (total >= 16 && have < 16) {
-        // the (16 - have)-th match of this ballot ends the chunk: resume after it
-        uint64_t mm = m;
-        for (int t = 1; t < 16 - have; ++t) mm &= mm - 1;
-        *next = base + 64 * j + (int)__builtin_ctzll(mm) + 1;
-      }
-      have = total;
-    }
-    if (have >= 16) break;
-  }
-  __builtin_amdgcn_wave_barrier();
-  return have < 16 ? have : 16;
-}
 
 // ---- code words --------------------------------------------------------------------------
 // Words of one tile column a lane holds (see trellis_decode.h): K = 2 one word, K = 4 two,
@@ -127,169 +92,197 @@ __device__ __forceinline__ void decode_col(const ColWords<K>& cw, uint32_t sh3, 
     col_mpairs_k3(cw.w[0], cw.w[1], cw.w[2], sh3, M);
 }
 
-// ---- one chunk: stream this wave's quarter of the slice --------------------------------
-// The wave's `steps` steps of 4 tile columns. One register set holds the current step's
-// code words and activations; as soon as a strip's words are decoded, the same registers
-// are reloaded with that strip's words of the next step, and the next step's activations
-// are requested as soon as the current ones are in the A operands. Each load thus has about
-// one step of work to arrive, at the register cost of a single step. (The last step
-// reloads its own addresses, which hit in cache, so every load is unconditional.)
+// ---- buffer loads ------------------------------------------------------------------------
+// The streaming loads address memory as a scalar buffer resource + one per-lane byte offset
+// (fixed for the whole piece) + a scalar offset for the step and strip, so a load costs no
+// vector address arithmetic and no 64-bit address registers.
+typedef __amdgpu_buffer_rsrc_t Rsrc;
+__device__ __forceinline__ Rsrc make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+
+template <int K>
+__device__ __forceinline__ void load_col_buf(Rsrc r, const uint32_t vo[3], uint32_t so,
+                                             ColWords<K>& cw) {
+  if constexpr (K == 2) {
+    cw.w[0] = __builtin_amdgcn_raw_buffer_load_b32(r, vo[0], so, 0);
+  } else if constexpr (K == 4) {
+    const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, vo[0], so, 0);
+    cw.w[0] = v.x;
+    cw.w[1] = v.y;
+  } else {
+    cw.w[0] = __builtin_amdgcn_raw_buffer_load_b32(r, vo[0], so, 0);
+    cw.w[1] = __builtin_amdgcn_raw_buffer_load_b32(r, vo[1], so, 0);
+    cw.w[2] = __builtin_amdgcn_raw_buffer_load_b32(r, vo[2], so, 0);
+  }
+}
+
+__device__ __forceinline__ void load_x(Rsrc r, uint32_t vo, uint32_t so, u32x4& xa, u32x4& xb) {
+  xa = __builtin_amdgcn_raw_buffer_load_b128(r, vo, so, 0);
+  xb = __builtin_amdgcn_raw_buffer_load_b128(r, vo + 16, so, 0);
+}
+
+// Plan records are read through the scalar cache (constant address space): their waits
+// then count on the scalar counter and never on the vector-memory counter that the
+// streaming loads keep busy.
+typedef const __attribute__((address_space(4))) PlanRec* ConstRec;
+__device__ __forceinline__ PlanRec load_rec(const PlanRec* rec, int i) {
+  const ConstRec p = (ConstRec)rec + i;
+  PlanRec r;
+  r.e = p->e;
+  r.start = p->start;
+  r.cnt = p->cnt;
+  r.k = p->k;
+  r.off = p->off;
+  r.p0 = p->p0;
+  r.pad = 0;
+  return r;
+}
+
+// ---- one step: 4 tile columns of 8 strips ---------------------------------------------
+// cw: this step's code words and xa, xb: its activations; with RELOAD they are reloaded
+// with those D steps later (scalar offsets cso + strip offset, and xso).
+template <int K, bool RELOAD>
+__device__ __forceinline__ void step_body(ColWords<K> (&cw)[8], u32x4& xa, u32x4& xb, Rsrc rc,
+                                          const uint32_t cvo[3], uint32_t cso,
+                                          const uint32_t sso[8], uint32_t sh3, Rsrc rx,
+                                          uint32_t xvo, uint32_t xso, f32x4 acc[8]) {
+  // Every reload goes into the registers of the value it replaces, after that value's last
+  // use (the scheduling barriers keep the compiler from hoisting it), so the loop carries
+  // its registers without copies, and a copy would wait for the load in flight.
+#pragma unroll
+  for (int s8 = 0; s8 < 8; ++s8) {
+    uint32_t M[8], V[8];
+    decode_col<K>(cw[s8], sh3, M);
+    __builtin_amdgcn_sched_barrier(0);
+    if (RELOAD) load_col_buf<K>(rc, cvo, cso + sso[s8], cw[s8]);
+    byte_sums<K>(M, V);
+    acc[s8] = mfma_f16(xa, (u32x4){V[0], V[1], V[2], V[3]}, acc[s8]);  // pairs 0..3
+    acc[s8] = mfma_f16(xb, (u32x4){V[4], V[5], V[6], V[7]}, acc[s8]);  // pairs 4..7
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  if (RELOAD) load_x(rx, xvo, xso, xa, xb);
+}
+
+// Units qa .. qb - 1 of output group grp for this wave: tile columns 16 q + 4 v + g (g =
+// lane / 16) of strips grp * 8 + s8. tok = this lane's token row, or -1 (zero row: its
+// activation offset lies past the end of the buffer, where buffer loads return 0).
 template <int K>
 __device__ __forceinline__ void stream(const TrellisGemvArgs& a, const uint32_t* __restrict__ unit,
-                                       int tok, int grp, int ns, int kcol0, f32x4 acc[8]) {
-  constexpr int TW = 8 * K;
+                                       int tok, int grp, int ns, int qa, int qb, int wv,
+                                       f32x4 acc[8]) {
+  constexpr int TW = 8 * K;  // words per tile
+  constexpr int D = K == 2 ? 4 : 2;
   const int lane = threadIdx.x & 63, g = lane >> 4, n = lane & 15;
-  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int steps = a.steps;
   const int n_ti = a.in / 16;
-  const int wcol0 = kcol0 + w * 4 * steps;  // first tile column of this wave
+  const int steps = qb - qa, last = steps - 1;
   const LaneOffsets<K> lo(g, n);
-  const uint32_t* run = unit + ((size_t)grp * 8 * n_ti + wcol0) * TW;
-  int sidx[8];
+  const Rsrc rc = make_rsrc(unit, (uint32_t)((size_t)a.out * a.in * K / 8));
+  const uint32_t cvo[3] = {4u * lo.o[0], 4u * lo.o[1], 4u * lo.o[2]};
+  const uint32_t c0 = 4u * (uint32_t)(((size_t)grp * 8 * n_ti + 16 * qa + 4 * wv) * TW);
+  constexpr uint32_t cstep = 4u * 16 * TW;  // bytes per step (16 tile columns)
+  uint32_t sso[8];
 #pragma unroll
-  for (int s8 = 0; s8 < 8; ++s8) sidx[s8] = (s8 < ns ? s8 : ns - 1) * n_ti * TW;
-  // A operand row n = this lane's token; tile column wcol0 + g of the step
-  const uint4* xrow = reinterpret_cast<const uint4*>(a.xp + ((size_t)tok * n_ti + wcol0 + g) * 8);
+  for (int s8 = 0; s8 < 8; ++s8) sso[s8] = 4u * (uint32_t)((s8 < ns ? s8 : ns - 1) * n_ti * TW);
+  const Rsrc rx = make_rsrc(a.xp, a.x_bytes);
+  const uint32_t xvo = tok >= 0 ? 32u * (uint32_t)(tok * n_ti + g) : 0x80000000u;
+  const uint32_t x0 = 32u * (uint32_t)(16 * qa + 4 * wv);
+  // scalar offsets of step st, clamped to the last step (whose words are read again)
+  auto cso = [&](int st) { return c0 + (uint32_t)(st < last ? st : last) * cstep; };
+  auto xso = [&](int st) { return x0 + (uint32_t)(st < last ? st : last) * 512u; };
 
-  ColWords<K> cw[8];
+  // Activations use a ring of the same depth, and the prologue issues the loads in the
+  // loop's order (a step's code words, then its activations): loads complete in issue
+  // order, so a wait for one step's data never waits for a later step's.
+  ColWords<K> cw[D][8];
+  u32x4 xa[D], xb[D];
 #pragma unroll
-  for (int s8 = 0; s8 < 8; ++s8) load_col<K>(run + sidx[s8], lo, cw[s8]);
-  uint4 xa = xrow[0], xb = xrow[1];
+  for (int d = 0; d < D; ++d) {
+#pragma unroll
+    for (int s8 = 0; s8 < 8; ++s8) load_col_buf<K>(rc, cvo, cso(d) + sso[s8], cw[d][s8]);
+    load_x(rx, xvo, xso(d), xa[d], xb[d]);
+  }
 #pragma unroll
   for (int s8 = 0; s8 < 8; ++s8) acc[s8] = (f32x4){0.f, 0.f, 0.f, 0.f};
-  for (int st = 0; st < steps; ++st) {
-    const bool more = st + 1 < steps;
-    const uint32_t* nrun = more ? run + 4 * TW : run;
-    const uint4* nxrow = more ? xrow + 8 : xrow;  // 4 tile columns of 32 bytes further
-    const u32x4 A0 = {xa.x, xa.y, xa.z, xa.w};   // pairs 0..3
-    const u32x4 A1 = {xb.x, xb.y, xb.z, xb.w};   // pairs 4..7
-    xa = nxrow[0];
-    xb = nxrow[1];
+  int st = 0;
+  for (; st + D <= steps; st += D) {
 #pragma unroll
-    for (int s8 = 0; s8 < 8; ++s8) {
-      uint32_t M[8], L[8], H[8];
-      decode_col<K>(cw[s8], lo.sh3, M);
-      load_col<K>(nrun + sidx[s8], lo, cw[s8]);
-      bytes_as_f16<K>(M, L, H);
-      acc[s8] = mfma_f16(A0, (u32x4){L[0], L[1], L[2], L[3]}, acc[s8]);
-      acc[s8] = mfma_f16(A0, (u32x4){H[0], H[1], H[2], H[3]}, acc[s8]);
-      acc[s8] = mfma_f16(A1, (u32x4){L[4], L[5], L[6], L[7]}, acc[s8]);
-      acc[s8] = mfma_f16(A1, (u32x4){H[4], H[5], H[6], H[7]}, acc[s8]);
-    }
-    run = nrun;
-    xrow = nxrow;
+    for (int d = 0; d < D; ++d)
+      step_body<K, true>(cw[d], xa[d], xb[d], rc, cvo, cso(st + d + D), sso, lo.sh3, rx, xvo,
+                         xso(st + d + D), acc);
   }
+  const int rem = steps - st;
+#pragma unroll
+  for (int d = 0; d < D - 1; ++d)
+    if (d < rem)
+      step_body<K, false>(cw[d], xa[d], xb[d], rc, cvo, 0, sso, lo.sh3, rx, xvo, 0, acc);
 }
 
-// All chunks of expert e for this (group, slice).
+// One piece: expert record r, units qa .. qb - 1 of group grp; sums to partial[piece].
 template <int K>
-__device__ __forceinline__ void run_expert(const TrellisGemvArgs& a, const GemvCommon& c, Shared& sh, int e,
-                           int grp, int s, int ns, const uint32_t* __restrict__ unit) {
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int kcol0 = s * 16 * a.steps;
-  int pos = 0;
-  while (true) {
-    int next;
-    const int cnt = wave_collect(a.ids, c.N, e, pos, sh.slots[w], &next);
-    if (cnt == 0) break;  // identical in all waves: the whole workgroup leaves together
-    pos = next;
-    f32x4 acc[8];
-    // rows past the chunk multiply token 0's activations; those rows are never stored
-    const int n = lane & 15;
-    const int tok = n < cnt ? sh.slots[w][n] / a.topk : 0;
-    stream<K>(a, unit, tok, grp, ns, kcol0, acc);
-    if (tid == 0) {
-      sh.ch.cnt = cnt;
-      sh.ch.next = next;
-    }
-    if (tid < 16) sh.ch.slots[tid] = sh.slots[0][tid];
-    gemv_reduce_store(c, sh.red, acc, sh.ch, e, grp, s, ns);
-    if (pos >= c.N) break;
-  }
-}
-
-__global__ __launch_bounds__(GEMV_THREADS, 4) void trellis_gemv_kernel(TrellisGemvArgs a) {
-  __shared__ Shared sh;
-  GemvCommon c;
-  c.ids = a.ids;
-  c.gates = a.gates;
-  c.scales = a.scales;
-  c.rowsum = a.rowsum;
-  c.acc_scale = GEMV_BYTE_SCALE;
-  c.offset = GEMV_BYTE_OFFSET;
-  c.y = a.y;
-  c.partial = a.partial;
-  c.N = (int)a.N;
-  c.E = a.E;
-  c.out = a.out;
-  c.topk = a.topk;
-  c.S = a.S;
-  c.groups = a.groups;
-  const int work = a.E * a.groups * a.S;
-  const int bid = blockIdx.x;
-  if (bid == work) {  // only launched with S == 1; with S > 1 the reduce launch does this
-    special_slots(a.ids, c.N, a.E, a.out, a.y, a.status);
-    return;
-  }
-  const int e = bid % a.E;
-  const int rest = bid / a.E;
-  const int grp = rest % a.groups;
-  const int s = rest / a.groups;
+__device__ __forceinline__ void run_piece(const TrellisGemvArgs& a, Shared& sh, const PlanRec& r,
+                                          int grp, int qa, int qb, int piece) {
+  const int tid = threadIdx.x, lane = tid & 63, n = lane & 15;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int ns = min(8, a.out / 16 - grp * 8);
-  const int K = a.bits[e];
-  const int64_t off = a.code_off[e];
-  if ((K < 2 || K > 4) || (off & 15)) {
-    gemv_bad_unit(c, sh.ch, a.status, e, grp, s, ns);
-    return;
+  const uint32_t* unit = a.codes + r.off / 4;
+  for (int c0 = 0; c0 < r.cnt; c0 += 16) {
+    const int rows = min(16, r.cnt - c0);
+    const int slot = n < rows ? a.list[r.start + c0 + n] : -1;
+    if (tid < 16) sh.slots[tid] = slot;
+    f32x4 acc[8];
+    stream<K>(a, unit, slot >= 0 ? slot / a.topk : -1, grp, ns, qa, qb, wv, acc);
+#pragma unroll
+    for (int s8 = 0; s8 < 8; ++s8)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sh.red[((wv * 8 + s8) * 4 + i) * 64 + lane] = acc[s8][i];
+    lds_barrier();
+    float* dst = a.partial + (size_t)piece * a.N * a.out;
+    for (int v = tid; v < ns * 256; v += GEMV_THREADS) {
+      const int s8 = v >> 8, i = (v >> 6) & 3, ln = v & 63;
+      const int m = 4 * (ln >> 4) + i;  // token row of accumulator element i of lane ln
+      if (m < rows) {
+        float sum = sh.red[((0 * 8 + s8) * 4 + i) * 64 + ln];
+        sum += sh.red[((1 * 8 + s8) * 4 + i) * 64 + ln];
+        sum += sh.red[((2 * 8 + s8) * 4 + i) * 64 + ln];
+        sum += sh.red[((3 * 8 + s8) * 4 + i) * 64 + ln];
+        const int o = grp * 128 + s8 * 16 + (ln & 15);
+        dst[(size_t)sh.slots[m] * a.out + o] = sum;
+      }
+    }
+    lds_barrier();
   }
-  const uint32_t* unit = a.codes + off / 4;
-  if (K == 2)
-    run_expert<2>(a, c, sh, e, grp, s, ns, unit);
-  else if (K == 3)
-    run_expert<3>(a, c, sh, e, grp, s, ns, unit);
-  else
-    run_expert<4>(a, c, sh, e, grp, s, ns, unit);
 }
 
-// ---- activation prep -----------------------------------------------------------------------
-// One wave per token: each lane converts tile columns lane, lane + 64, ... (16 bf16 -> f16,
-// round to nearest even) into the pair layout and sums the f16 values in a fixed order;
-// the lane sums are combined by a fixed butterfly.
-__global__ __launch_bounds__(64) void gemv_prep_kernel(const uint16_t* __restrict__ x, int in,
-                                                      uint32_t* __restrict__ xp,
-                                                      float* __restrict__ rowsum) {
-  typedef _Float16 h2 __attribute__((ext_vector_type(2)));
-  const int t = blockIdx.x, lane = threadIdx.x;
-  const int n_ti = in / 16;
-  float sum = 0.0f;
-  for (int c = lane; c < n_ti; c += 64) {
-    const uint4* src = reinterpret_cast<const uint4*>(x + (size_t)t * in + (size_t)c * 16);
-    const uint4 u = src[0], v = src[1];
-    const uint32_t wv[8] = {u.x, u.y, u.z, u.w, v.x, v.y, v.z, v.w};
-    float f[16];
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      f[2 * k] = bf16_lo_to_f32(wv[k]);
-      f[2 * k + 1] = bf16_hi_to_f32(wv[k]);
+__global__ __launch_bounds__(GEMV_THREADS, GEMV_WAVES_PER_SIMD) void trellis_gemv_kernel(TrellisGemvArgs a) {
+  __shared__ Shared sh;
+  const int w = blockIdx.x;
+  const int2 d0 = a.desc[w], d1 = a.desc[w + 1];
+  const int64_t C = a.info[1];
+  const int Geff = a.info[2];  // workgroups with work (see gemv_plan.h)
+  const int Q = a.in / 256, U = a.groups * Q;
+  int ai = d0.x, u = d0.y;
+  PlanRec rn = load_rec(a.rec, min(ai, a.E - 1));
+  while (ai < d1.x || (ai == d1.x && u < d1.y)) {
+    const PlanRec r = rn;
+    rn = load_rec(a.rec, min(ai + 1, a.E - 1));  // the next expert's record, requested early
+    const int u_end = ai < d1.x ? U : d1.y;
+    while (u < u_end) {
+      const int grp = u / Q, qa = u % Q;
+      const int qb = min(Q, qa + (u_end - u));
+      const int piece = w - plan_owner((int64_t)r.p0 + (int64_t)grp * Q * r.k, C, Geff);
+      if (r.k == 2)
+        run_piece<2>(a, sh, r, grp, qa, qb, piece);
+      else if (r.k == 3)
+        run_piece<3>(a, sh, r, grp, qa, qb, piece);
+      else
+        run_piece<4>(a, sh, r, grp, qa, qb, piece);
+      u += qb - qa;
     }
-    uint32_t P[8];
-    float hf[16];
-#pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      const h2 p = (h2){(_Float16)f[r + 8], (_Float16)f[r]};
-      P[r] = __builtin_bit_cast(uint32_t, p);
-      hf[r] = (float)p.y;
-      hf[r + 8] = (float)p.x;
-    }
-#pragma unroll
-    for (int i = 0; i < 16; ++i) sum += hf[i];
-    uint4* dst = reinterpret_cast<uint4*>(xp + ((size_t)t * n_ti + c) * 8);
-    dst[0] = make_uint4(P[0], P[1], P[2], P[3]);
-    dst[1] = make_uint4(P[4], P[5], P[6], P[7]);
+    ++ai;
+    u = 0;
   }
-#pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) sum += __shfl_xor(sum, d, 64);
-  if (lane == 0) rowsum[t] = sum;
 }
 
 // ---- decode hook ------------------------------------------------------------------------
@@ -315,18 +308,14 @@ __global__ __launch_bounds__(256) void trellis_decode_kernel(const uint32_t* __r
   decode_col<K>(cw, lo.sh3, M);
   int16_t* row = q + (size_t)(strip * 16 + n) * in + (ti0 + g) * 16;
   if (path == 0) {
-    // the operands the matrix cores receive: L[r], H[r] hold inputs r (high half) and
-    // r + 8 (low half) as f16 subnormals
-    uint32_t L[8], H[8];
-    bytes_as_f16<K>(M, L, H);
+    // the operands the matrix cores receive: V[r] holds inputs r (high half) and r + 8
+    // (low half) as the f16 subnormals (q + 255) * 2^-24
+    uint32_t V[8];
+    byte_sums<K>(M, V);
 #pragma unroll
     for (int r = 0; r < 8; ++r) {
-      const float qh = (f16_bits_to_f32(L[r] >> 16) + f16_bits_to_f32(H[r] >> 16)) * GEMV_BYTE_SCALE -
-                       GEMV_BYTE_OFFSET;
-      const float ql = (f16_bits_to_f32(L[r]) + f16_bits_to_f32(H[r])) * GEMV_BYTE_SCALE -
-                       GEMV_BYTE_OFFSET;
-      row[r] = (int16_t)qh;
-      row[r + 8] = (int16_t)ql;
+      row[r] = (int16_t)(f16_bits_to_f32(V[r] >> 16) * GEMV_BYTE_SCALE - GEMV_BYTE_OFFSET);
+      row[r + 8] = (int16_t)(f16_bits_to_f32(V[r]) * GEMV_BYTE_SCALE - GEMV_BYTE_OFFSET);
     }
   } else {
     uint32_t nat[8];
@@ -341,16 +330,25 @@ __global__ __launch_bounds__(256) void trellis_decode_kernel(const uint32_t* __r
 
 }  // namespace
 
-hipError_t launch_trellis_gemv(const TrellisGemvArgs& a, hipStream_t s) {
-  const int blocks = a.E * a.groups * a.S + (a.S == 1 ? 1 : 0);
-  hipLaunchKernelGGL(trellis_gemv_kernel, dim3(blocks), dim3(GEMV_THREADS), 0, s, a);
-  return hipGetLastError();
+int trellis_gemv_grid() {
+  static int cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (dev >= 0 && dev < 64 && cache[dev]) return cache[dev];
+  int per_cu = 0, cus = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, trellis_gemv_kernel, GEMV_THREADS, 0) !=
+      hipSuccess)
+    return 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  int g = per_cu * cus * GEMV_GRID_MULT;
+  if (g > GEMV_MAX_G) g = GEMV_MAX_G;
+  if (g < 1) g = 1;
+  if (dev >= 0 && dev < 64) cache[dev] = g;
+  return g;
 }
 
-hipError_t launch_gemv_prep(const uint16_t* x, int64_t T, int in, uint32_t* xp, float* rowsum,
-                            hipStream_t s) {
-  if (T == 0) return hipSuccess;
-  hipLaunchKernelGGL(gemv_prep_kernel, dim3((unsigned)T), dim3(64), 0, s, x, in, xp, rowsum);
+hipError_t launch_trellis_gemv(const TrellisGemvArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(trellis_gemv_kernel, dim3(a.G), dim3(GEMV_THREADS), 0, s, a);
   return hipGetLastError();
 }
 
