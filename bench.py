@@ -14,9 +14,13 @@ code buffer (replicas total >= 1 GiB) so the 256 MB Infinity Cache cannot serve 
 
 value = compressed bytes of the experts a step touches / step time (GB/s), or dense-
 equivalent routed flops / step time (TFLOP/s) for prefill. The roofline object times the
-dominant kernel alone with HIP events around each launch (launches queued behind a bounded
-sleep kernel so no host gap falls inside an interval). The CPU baseline times the oracle
-(test infrastructure, single thread) on a bounded sample of the same workload.
+dominant kernel (the grouped GEMV) alone: HIP events recorded on its own stream right
+before and after it (tq_time_kernel), over --kernel-iters direct calls of the step's GEMM
+queued behind a bounded sleep kernel, so no host gap falls inside an interval. Its HBM
+traffic comes from rocprofv3 FETCH_SIZE / WRITE_SIZE runs (bench.py --drive mixed),
+calibrated against a plain elementwise copy of known size in the same runs and stored by
+bench.py --write-traffic. The CPU baseline times the oracle (test infrastructure, single
+thread) on the same workload.
 """
 
 import argparse
@@ -90,6 +94,41 @@ def time_kernel(torch, launch, n_replicas, iters):
     return float(np.mean(ms)) / 1e3, float(np.median(ms)) / 1e3
 
 
+GEMV_SOURCES = ["trellis_gemv.hip", "trellis_decode.h", "gemv_plan.h", "tq_device.h",
+                "tq_internal.h"]
+
+
+def kernel_events(torch, n):
+    """n event pairs for tq_time_kernel; each is recorded once so that it exists."""
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+    stops = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+    for e in starts + stops:
+        e.record()
+    torch.cuda.synchronize()
+    return starts, stops
+
+
+def time_main_kernel(torch, ops, call, n_replicas, iters):
+    """Mean (and median) duration of the main kernel of `call(r)`: direct launches queued
+    behind a bounded sleep kernel, each with tq_time_kernel's event pair around that kernel
+    on its own stream."""
+    starts, stops = kernel_events(torch, iters)
+    for r in range(n_replicas):
+        call(r)
+    torch.cuda.synchronize()
+    torch.cuda._sleep(SLEEP_CYCLES)
+    for i in range(iters):
+        ops.time_kernel(starts[i], stops[i])
+        call(i % n_replicas)
+    torch.cuda.synchronize()
+    return event_means(starts, stops)
+
+
+def event_means(starts, stops):
+    ms = [s.elapsed_time(e) for s, e in zip(starts, stops)]
+    return float(np.mean(ms)) / 1e3, float(np.median(ms)) / 1e3
+
+
 def traffic_from_profile(name, shash, per_launch_algo):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if it was taken
     on the current kernel sources; else None."""
@@ -145,12 +184,11 @@ def bench_mixed(torch, ops, args):
             step(r)
         graphs.append(g)
     sec = time_graph_steps(torch, graphs, args.steps, args.warmup)
-    kmean, kmed = time_kernel(
-        torch, lambda r: ops.trellis_expert_gemm(layers[r], xr, ids, out=y, ws=ws),
+    kmean, kmed = time_main_kernel(
+        torch, ops, lambda r: ops.trellis_expert_gemm(layers[r], xr, ids, out=y, ws=ws),
         len(reps), args.kernel_iters)
     hmean, _ = time_kernel(torch, lambda r: ops.hadamard128(x, signs, out=xr), 1, args.kernel_iters)
-    shash = source_hash(["trellis_gemv.hip", "trellis_decode.h", "gemv_common.h", "route_scan.h",
-                         "tq_device.h"])
+    shash = source_hash(GEMV_SOURCES)
     traffic = traffic_from_profile("trellis_gemv_mixed", shash, nbytes)
     return {
         "sec_per_step": sec, "bytes": nbytes, "n_active": n_active,
@@ -190,7 +228,7 @@ def bench_mxfp4(torch, ops, args):
             step(r)
         graphs.append(g)
     sec = time_graph_steps(torch, graphs, args.steps, args.warmup)
-    kmean, kmed = time_kernel(torch, step, len(reps), args.kernel_iters)
+    kmean, kmed = time_main_kernel(torch, ops, step, len(reps), args.kernel_iters)
     return {"sec_per_step": sec, "bytes": nbytes, "n_active": n_active,
             "kernel": "mxfp4_gemv_kernel", "kernel_sec": kmean, "kernel_sec_median": kmed}
 
@@ -228,10 +266,11 @@ def bench_prefill(torch, ops, args):
         graphs.append(g)
     steps = max(10, args.steps // 20)
     sec = time_graph_steps(torch, graphs, steps, max(2, args.warmup // 10))
-    gemm_only = lambda r: ops.trellis_expert_gemm(layers[r], xr, ids, out=y, ws=ws, flags=ops.TQ_GEMM)
-    kmean, kmed = time_kernel(torch, gemm_only, len(reps), max(10, args.kernel_iters // 10))
+    kmean, kmed = time_main_kernel(
+        torch, ops, lambda r: ops.trellis_expert_gemm(layers[r], xr, ids, out=y, ws=ws),
+        len(reps), max(10, args.kernel_iters // 10))
     return {"sec_per_step": sec, "flops": flops, "steps": steps,
-            "kernel": "route + trellis_gemm_kernel", "kernel_sec": kmean, "kernel_sec_median": kmed}
+            "kernel": "trellis_gemm_kernel", "kernel_sec": kmean, "kernel_sec_median": kmed}
 
 
 def cpu_baseline_mixed(wl, n_experts):
@@ -242,7 +281,8 @@ def cpu_baseline_mixed(wl, n_experts):
     lay = wl["layer"]
     ids = wl["topk_ids"]
     active = np.unique(ids)
-    pick = np.random.default_rng(7).choice(active, size=min(n_experts, active.size), replace=False)
+    n = active.size if n_experts <= 0 else min(n_experts, active.size)
+    pick = np.random.default_rng(7).choice(active, size=n, replace=False)
     keep = np.where(np.isin(ids, pick), ids, -1)
     nbytes = int(np.sum(lay["out"] * lay["in"] * lay["bits"][pick].astype(np.int64) // 8))
     scales = oracle.f16_bits_to_f64(lay["scales"])
@@ -266,6 +306,95 @@ def cpu_baseline_mixed(wl, n_experts):
     }
 
 
+# ------------------------------------------------------------------------------------------
+# profiler support: a plain workload driver, and the traffic summary of its counter runs
+# ------------------------------------------------------------------------------------------
+
+COPY_BYTES = 1 << 30  # the calibration copy reads and writes this many bytes (4x the MALL)
+
+
+def drive(torch, ops, which, iters):
+    """Runs `iters` steps of one workload (no timing), for rocprofv3. The mixed workload
+    ends with a calibration copy: torch.bitwise_xor over COPY_BYTES of int32, which reads
+    and writes each byte once."""
+    from workloads import mixed_layer, mxfp4_decode_layer, prefill_chunk
+    dev = torch.device("cuda", 0)
+    if which in ("mixed", "prefill"):
+        wl = mixed_layer() if which == "mixed" else prefill_chunk()
+        lay = wl["layer"]
+        L = ops.TrellisLayer.from_host(lay, dev)
+        x = torch.from_numpy(wl["x"].view(np.int16)).to(dev)
+        signs = torch.from_numpy(lay["signs"]).to(dev)
+        ids = torch.from_numpy(wl["topk_ids"]).to(dev)
+        T, topk = wl["topk_ids"].shape
+        reps = replicate(torch, L.codes, L.codes.numel() * 4)
+        layers = [L.with_codes(c) for c in reps]
+        xr = torch.empty_like(x)
+        y = torch.empty((T, topk, lay["out"]), dtype=torch.float32, device=dev)
+        ws = ops.workspace(T, topk, lay["E"], lay["out"], lay["in"], ops.TQ_AUTO, dev)
+        for i in range(iters):
+            ops.hadamard128(x, signs, out=xr)
+            ops.trellis_expert_gemm(layers[i % len(layers)], xr, ids, out=y, ws=ws)
+    else:
+        wl = mxfp4_decode_layer()
+        lay = wl["layer"]
+        L = ops.Mxfp4Layer.from_host(lay, dev)
+        x = torch.from_numpy(wl["x"].view(np.int16)).to(dev)
+        ids = torch.from_numpy(wl["topk_ids"]).to(dev)
+        gates = torch.from_numpy(wl["topk_w"]).to(dev)
+        reps = replicate(torch, L.units, L.units.numel())
+        layers = [L.with_units(u) for u in reps]
+        for i in range(iters):
+            ops.mxfp4_expert_gemm(layers[i % len(layers)], x, ids, gates)
+    if which == "mixed":
+        src = torch.arange(COPY_BYTES // 4, dtype=torch.int32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.bitwise_xor(src, 0x5A5A5A5A, out=dst)
+    torch.cuda.synchronize()
+    log("drove %s for %d steps" % (which, iters))
+
+
+def counter_means(run_dir, counter):
+    """Mean value of `counter` per dispatch, by kernel name, from a rocprofv3 csv output."""
+    import csv
+    import glob
+    files = glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit("no counter_collection.csv under " + run_dir)
+    acc = {}
+    for r in csv.DictReader(open(files[0])):
+        if r["Counter_Name"] != counter:
+            continue
+        acc.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+    return {k: float(np.mean(v)) for k, v in acc.items()}
+
+
+def write_traffic(fetch_dir, write_dir, command):
+    """HBM bytes per launch of the trellis GEMV from FETCH_SIZE and WRITE_SIZE runs (KiB per
+    dispatch), each divided by what the same counter reads per byte of the calibration copy."""
+    fetch = counter_means(fetch_dir, "FETCH_SIZE")
+    write = counter_means(write_dir, "WRITE_SIZE")
+    pick = lambda d, key: [v for k, v in d.items() if key in k]
+    gf, gw = pick(fetch, "trellis_gemv_kernel"), pick(write, "trellis_gemv_kernel")
+    cf, cw = pick(fetch, "BitwiseXor"), pick(write, "BitwiseXor")
+    if not (gf and gw and cf and cw):
+        raise SystemExit("GEMV or calibration-copy dispatches missing in the counter runs")
+    f_fac = cf[0] * 1024 / COPY_BYTES
+    w_fac = cw[0] * 1024 / COPY_BYTES
+    fb, wb = gf[0] * 1024 / f_fac, gw[0] * 1024 / w_fac
+    d = {"kernel": "trellis_gemv_kernel", "workload": "mixed",
+         "source_hash": source_hash(GEMV_SOURCES),
+         "hbm_bytes_per_launch": int(round(fb + wb)), "fetch_bytes": int(round(fb)),
+         "write_bytes": int(round(wb)), "copy_fetch_factor": round(f_fac, 4),
+         "copy_write_factor": round(w_fac, 4), "command": command}
+    path = os.path.join(ROOT, "profiles", "traffic_trellis_gemv_mixed.json")
+    with open(path, "w") as f:
+        json.dump(d, f, indent=1)
+        f.write("\n")
+    print(json.dumps(d))
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -274,9 +403,19 @@ def main():
     ap.add_argument("--kernel-iters", type=int, default=200)
     ap.add_argument("--extras", default="mxfp4,prefill",
                     help="comma list of secondary workloads (mxfp4, prefill) or 'none'")
-    ap.add_argument("--cpu-sample-experts", type=int, default=128)
+    ap.add_argument("--cpu-sample-experts", type=int, default=0,
+                    help="active experts in the CPU baseline sample (0 = all)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--drive", choices=["mixed", "mxfp4", "prefill"],
+                    help="only run --steps steps of one workload (for rocprofv3)")
+    ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="summarise rocprofv3 FETCH_SIZE / WRITE_SIZE runs of --drive mixed")
+    ap.add_argument("--traffic-command", default="",
+                    help="the profiler commands that made the --write-traffic runs")
     args = ap.parse_args()
+    if args.write_traffic:
+        write_traffic(args.write_traffic[0], args.write_traffic[1], args.traffic_command)
+        return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -290,6 +429,9 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
     torch.cuda.set_device(0)
+    if args.drive:
+        drive(torch, ops, args.drive, args.steps)
+        return
 
     res = bench_mixed(torch, ops, args)
     gbs = res["bytes"] / res["sec_per_step"] / 1e9
@@ -349,8 +491,8 @@ def main():
             "workload": "8192 tokens, top-8, 384 K=3 experts, Zipf(1.1)",
             "TFLOP/s": round(p["flops"] / p["sec_per_step"] / 1e12, 3),
             "ms_per_step": round(p["sec_per_step"] * 1e3, 5), "steps": p["steps"],
-            "route_plus_gemm_us": round(p["kernel_sec"] * 1e6, 3),
-            "route_plus_gemm_TFLOP/s": round(p["flops"] / p["kernel_sec"] / 1e12, 3),
+            "kernel": p["kernel"], "kernel_us": round(p["kernel_sec"] * 1e6, 3),
+            "kernel_TFLOP/s": round(p["flops"] / p["kernel_sec"] / 1e12, 3),
             "frac_bf16_peak": round(p["flops"] / p["kernel_sec"] / 1e12 / BF16_PEAK_TFLOPS, 4),
         }
     if extras:

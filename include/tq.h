@@ -183,6 +183,16 @@ const char* tq_last_error(void);
 /* Synchronises `stream`, copies the workspace status word to *flags_out and clears it. */
 int tq_device_status(void* ws, void* stream, uint32_t* flags_out);
 
+/*
+ * Measurement hook, for benchmarks and profilers (not part of the computation). After this
+ * call, the calling thread's next trellis_expert_gemm or mxfp4_expert_gemm records `start`
+ * on its stream immediately before its main kernel (the grouped GEMV in the decode-batch
+ * mode, the grouped GEMM in the prefill mode) and `stop` immediately after it; the hook is
+ * then cleared. start and stop are hipEvent_t passed as void*, created by the caller; under
+ * stream capture they become event-record nodes of the graph. NULL, NULL clears the hook.
+ */
+int tq_time_kernel(void* start, void* stop);
+
 /* Library version, major * 10000 + minor * 100 + patch. */
 int tq_version(void);
 

@@ -68,6 +68,7 @@ SIGNATURES = {
     "tq_last_error": (ctypes.c_char_p, []),
     "tq_device_status": (ctypes.c_int, [_P, _P, ctypes.POINTER(_U32)]),
     "tq_version": (ctypes.c_int, []),
+    "tq_time_kernel": (ctypes.c_int, [_P, _P]),
 }
 
 _lib = None

@@ -15,6 +15,17 @@
 namespace {
 
 thread_local std::string g_error;
+thread_local hipEvent_t g_time_start = nullptr, g_time_stop = nullptr;
+
+// Measurement hook (tq_time_kernel): events around the next main kernel launch.
+hipError_t time_begin(hipStream_t s) {
+  return g_time_start ? hipEventRecord(g_time_start, s) : hipSuccess;
+}
+hipError_t time_end(hipStream_t s) {
+  hipError_t err = g_time_stop ? hipEventRecord(g_time_stop, s) : hipSuccess;
+  g_time_start = g_time_stop = nullptr;
+  return err;
+}
 
 int fail(int code, const char* fmt, ...) {
   char buf[512];
@@ -194,6 +205,14 @@ size_t tq_workspace_bytes(int64_t T, int32_t topk, int32_t E, int32_t out, int32
 }
 
 const char* tq_last_error(void) { return g_error.c_str(); }
+
+int tq_time_kernel(void* start, void* stop) {
+  if ((start == nullptr) != (stop == nullptr))
+    return fail(TQ_EINVAL, "tq_time_kernel needs both events or neither");
+  g_time_start = static_cast<hipEvent_t>(start);
+  g_time_stop = static_cast<hipEvent_t>(stop);
+  return ok();
+}
 
 int tq_version(void) { return 100; }
 
@@ -462,7 +481,10 @@ int trellis_expert_gemm(const tq_trellis_layer* L, const void* x, int64_t T,
     a.topk = topk;
     a.groups = W.groups;
     a.G = G;
+    err = time_begin(s);
+    if (err != hipSuccess) return hip_fail(err, "hipEventRecord");
     err = tq::launch_trellis_gemv(a, s);
+    if (err == hipSuccess) err = time_end(s);
     if (err != hipSuccess) return hip_fail(err, "trellis GEMV launch");
     tq::PieceReduceArgs r{};
     r.slot_info = p.slot_info;
@@ -503,7 +525,10 @@ int trellis_expert_gemm(const tq_trellis_layer* L, const void* x, int64_t T,
     a.topk = topk;
     a.groups = W.groups;
     a.max_items = W.max_items;
+    err = time_begin(s);
+    if (err != hipSuccess) return hip_fail(err, "hipEventRecord");
     err = tq::launch_trellis_gemm(a, s);
+    if (err == hipSuccess) err = time_end(s);
     if (err != hipSuccess) return hip_fail(err, "trellis GEMM launch");
   }
   if (flags & TQ_COMBINE) {
@@ -546,7 +571,10 @@ int mxfp4_expert_gemm(const tq_mxfp4_layer* L, const void* x, int64_t T,
     a.steps = W.gemv_steps;
     a.groups = W.groups;
     a.N = N;
+    err = time_begin(s);
+    if (err != hipSuccess) return hip_fail(err, "hipEventRecord");
     err = tq::launch_mxfp4_gemv(a, s);
+    if (err == hipSuccess) err = time_end(s);
     if (err != hipSuccess) return hip_fail(err, "MXFP4 GEMV launch");
     if (W.gemv_slices > 1) {
       rc = run_gemv_reduce(W, ws, topk_ids, nullptr, topk_w, nullptr, 1.0f, 0.0f, y, N, L->E,
@@ -571,7 +599,10 @@ int mxfp4_expert_gemm(const tq_mxfp4_layer* L, const void* x, int64_t T,
     a.topk = topk;
     a.groups = W.groups;
     a.max_items = W.max_items;
+    err = time_begin(s);
+    if (err != hipSuccess) return hip_fail(err, "hipEventRecord");
     err = tq::launch_mxfp4_gemm(a, s);
+    if (err == hipSuccess) err = time_end(s);
     if (err != hipSuccess) return hip_fail(err, "MXFP4 GEMM launch");
   }
   if (flags & TQ_COMBINE) {

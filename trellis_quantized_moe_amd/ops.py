@@ -165,3 +165,13 @@ def device_status(ws):
 
 def version():
     return int(_lib.load().tq_version())
+
+
+def time_kernel(start, stop):
+    """Measurement hook: the next expert GEMM call on this thread records the torch.cuda.Event
+    pair (start, stop) around its main kernel, on its stream (tq_time_kernel)."""
+    if start is None:
+        check(_lib.load().tq_time_kernel(None, None))
+        return
+    check(_lib.load().tq_time_kernel(ctypes.c_void_p(start.cuda_event),
+                                      ctypes.c_void_p(stop.cuda_event)))
