@@ -358,8 +358,10 @@ int common_checks(int E, int out, int in, const void* x, int64_t T, const int32_
     return fail(TQ_EINVAL, "this path supports E <= 4096 (E = %d)", E);
   if (!layout->gemm && !mxfp4 && (int64_t)E * layout->groups * (in / 256) * 4 >= ((int64_t)1 << 31))
     return fail(TQ_EINVAL, "E * out * in is too large for the decode-batch plan");
-  if (!layout->gemm && !mxfp4 && T * (int64_t)in * 2 >= ((int64_t)1 << 31))
-    return fail(TQ_EINVAL, "T * in is too large for the decode-batch path");
+  if ((layout->gemm || !mxfp4) && T * (int64_t)in * 2 >= ((int64_t)1 << 31))
+    return fail(TQ_EINVAL, "T * in * 2 bytes of activations must stay below 2^31");
+  if (layout->gemm && (int64_t)out * in / 2 + (int64_t)out * in / 32 >= ((int64_t)1 << 31))
+    return fail(TQ_EINVAL, "out * in is too large for the prefill path");
   if (!layout->gemm && !mxfp4 && (int64_t)out * in / 2 >= ((int64_t)1 << 31))
     return fail(TQ_EINVAL, "out * in is too large for the decode-batch path");
   if (T == 0) return TQ_OK;
@@ -513,6 +515,7 @@ int trellis_expert_gemm(const tq_trellis_layer* L, const void* x, int64_t T,
     a.codes = L->codes;
     a.scales = L->scales;
     a.x = xb;
+    a.x_bytes = (uint32_t)(T * L->in * 2);
     a.gates = topk_w;
     a.pairs = at<int32_t>(ws, W.pairs);
     a.items = at<int32_t>(ws, W.items);
@@ -588,6 +591,7 @@ int mxfp4_expert_gemm(const tq_mxfp4_layer* L, const void* x, int64_t T,
     tq::Mxfp4GemmArgs a{};
     a.units = L->units;
     a.x = xb;
+    a.x_bytes = (uint32_t)(T * L->in * 2);
     a.gates = topk_w;
     a.pairs = at<int32_t>(ws, W.pairs);
     a.items = at<int32_t>(ws, W.items);

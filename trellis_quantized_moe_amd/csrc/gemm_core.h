@@ -5,10 +5,11 @@
 // steps of 32 inputs:
 //   - a B producer (format-specific) decodes the step's 32 x 128 weights into bf16, each
 //     thread one run of 16 inputs of one output channel, stored in natural input order;
-//   - each thread gathers 16 activations of one routed row into the A tile;
+//   - each thread copies 16 activations of one routed row into the A tile;
 //   - each wave runs its 4 x 4 block of 16x16x32 bf16 matrix-core operations.
-// Two LDS buffers alternate, so the next step is produced while this one multiplies. Each
-// output is written once by the workgroup owning its row.
+// Two LDS buffers alternate: while the waves multiply step kk, they decode and stage step
+// kk + 1 into the other buffer, from registers loaded GEMM_RING steps earlier. Each output
+// is written once by the workgroup owning its row.
 #pragma once
 
 #include "tq_device.h"
@@ -20,14 +21,17 @@ constexpr int GEMM_THREADS = 256;
 constexpr int GEMM_KS = 32;          // inputs per step
 constexpr int GEMM_LDS_STRIDE = 40;  // bf16 per LDS row (32 + 8 padding against bank conflicts)
 
+// 16-byte alignment lets every operand access be one ds_read_b128 / ds_write_b128 (with
+// 2-byte alignment the compiler splits them into 32-bit accesses).
 struct GemmShared {
-  uint16_t a[2][GEMM_MT * GEMM_LDS_STRIDE];
-  uint16_t b[2][128 * GEMM_LDS_STRIDE];
+  alignas(16) uint16_t a[2][GEMM_MT * GEMM_LDS_STRIDE];
+  alignas(16) uint16_t b[2][128 * GEMM_LDS_STRIDE];
   int slot[GEMM_MT];
 };
 
 struct GemmItem {
   const uint16_t* x;
+  uint32_t x_bytes;        // size of x in bytes (< 2^31)
   const float* gates;
   const uint16_t* scales;  // fp16 per output channel of this expert, or null
   float* y;
@@ -39,36 +43,61 @@ __device__ inline void gemm_load_slots(GemmShared& sh, const int32_t* pairs, int
                                        int nrows) {
   for (int m = threadIdx.x; m < GEMM_MT; m += GEMM_THREADS)
     sh.slot[m] = m < nrows ? pairs[row0 + m] : 0;
-  __syncthreads();
+  lds_barrier();
 }
 
-// Producer interface: void operator()(int kk, int* o, int* h, uint32_t nat[8]) gives the
-// thread's B run for step kk: output channel o (0..127, within the group), inputs
-// 32 kk + 16 h .. + 15, as 8 dwords of bf16 pairs in natural order (zeros if unused).
+// ---- buffer loads ------------------------------------------------------------------------
+typedef __amdgpu_buffer_rsrc_t GemmRsrc;
+__device__ __forceinline__ GemmRsrc gemm_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+
+// Producer interface (format-specific B operand):
+//   typename Raw                  this thread's undecoded data of one step (registers)
+//   void load(int kk, Raw& r)     issues the loads of step kk (any kk < steps)
+//   void decode(const Raw& r, uint32_t nat[8])
+//                                 bf16 pairs of the thread's run, natural input order
+//   int o, h                      the run: output channel o (0..127 within the group),
+//                                 inputs 32 kk + 16 h .. + 15
+//
+// The loads of step kk + GEMM_RING are issued as soon as step kk's raw data has been
+// consumed, into the same registers, so GEMM_RING steps of loads are in flight while the
+// matrix cores work; every load is unconditional (indices clamped to valid steps), so each
+// path through the loop leaves the same loads in flight.
+constexpr int GEMM_RING = 4;
+
 template <class Producer>
-__device__ void gemm_item(const GemmItem& it, GemmShared& sh, Producer& produce_b) {
+__device__ void gemm_item(const GemmItem& it, GemmShared& sh, Producer& prod) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, n = lane & 15;
   const int wm = w >> 1, wn = w & 1;
-  const int nsteps = it.in / GEMM_KS;
+  const int nsteps = it.in / GEMM_KS;  // a multiple of 8 (in is a multiple of 256)
+  // A staging: thread (a_m, a_h) copies inputs 16 a_h .. + 15 of the step for routed row
+  // a_m (rows past the item's count copy token 0's row; they are never stored)
   const int a_m = tid >> 1, a_h = tid & 1;
-  const bool a_valid = a_m < it.nrows;
-  const uint16_t* a_src =
-      it.x + (size_t)(a_valid ? sh.slot[a_m] / it.topk : 0) * it.in + 16 * a_h;
+  const int a_tok = a_m < it.nrows ? sh.slot[a_m] / it.topk : 0;
+  const GemmRsrc ra = gemm_rsrc(it.x, it.x_bytes);
+  const uint32_t a_vo = 2u * (uint32_t)((size_t)a_tok * it.in + 16 * a_h);
 
-  auto produce = [&](int kk, int buf) {
-    uint4 v0 = make_uint4(0, 0, 0, 0), v1 = v0;
-    if (a_valid) {
-      const uint4* src = reinterpret_cast<const uint4*>(a_src + kk * GEMM_KS);
-      v0 = src[0];
-      v1 = src[1];
-    }
-    uint4* da = reinterpret_cast<uint4*>(&sh.a[buf][a_m * GEMM_LDS_STRIDE + 16 * a_h]);
-    da[0] = v0;
-    da[1] = v1;
-    int o, h;
+  typename Producer::Raw raw[GEMM_RING];
+  u32x4 xa0[GEMM_RING], xa1[GEMM_RING];
+  auto load_step = [&](int slot, int kk) {
+    const int k = kk < nsteps ? kk : nsteps - 1;
+    prod.load(k, raw[slot]);
+    xa0[slot] = __builtin_amdgcn_raw_buffer_load_b128(ra, a_vo, 64u * k, 0);
+    xa1[slot] = __builtin_amdgcn_raw_buffer_load_b128(ra, a_vo + 16, 64u * k, 0);
+  };
+  // decodes the slot into LDS buffer buf, then reuses its registers for step kk_next
+  auto stage = [&](int slot, int buf, int kk_next) {
     uint32_t nat[8];
-    produce_b(kk, &o, &h, nat);
-    uint4* db = reinterpret_cast<uint4*>(&sh.b[buf][o * GEMM_LDS_STRIDE + 16 * h]);
+    prod.decode(raw[slot], nat);
+    const u32x4 v0 = xa0[slot], v1 = xa1[slot];
+    __builtin_amdgcn_sched_barrier(0);
+    load_step(slot, kk_next);
+    uint4* da = reinterpret_cast<uint4*>(&sh.a[buf][a_m * GEMM_LDS_STRIDE + 16 * a_h]);
+    da[0] = make_uint4(v0.x, v0.y, v0.z, v0.w);
+    da[1] = make_uint4(v1.x, v1.y, v1.z, v1.w);
+    uint4* db = reinterpret_cast<uint4*>(&sh.b[buf][prod.o * GEMM_LDS_STRIDE + 16 * prod.h]);
     db[0] = make_uint4(nat[0], nat[1], nat[2], nat[3]);
     db[1] = make_uint4(nat[4], nat[5], nat[6], nat[7]);
   };
@@ -84,27 +113,34 @@ __device__ void gemm_item(const GemmItem& it, GemmShared& sh, Producer& produce_
   int nblocks = it.ns - 4 * wn;
   nblocks = nblocks < 0 ? 0 : (nblocks > 4 ? 4 : nblocks);
 
-  produce(0, 0);
-  __syncthreads();
-  for (int kk = 0; kk < nsteps; ++kk) {
-    const int buf = kk & 1;
-    if (kk + 1 < nsteps) produce(kk + 1, buf ^ 1);
-    u32x4 bop[4];
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb)
-      bop[nb] = *reinterpret_cast<const u32x4*>(
-          &sh.b[buf][(64 * wn + 16 * nb + n) * GEMM_LDS_STRIDE + 8 * g]);
+  for (int d = 0; d < GEMM_RING; ++d) load_step(d, d);
+  stage(0, 0, GEMM_RING);
+  lds_barrier();
+  for (int kk = 0; kk < nsteps; kk += GEMM_RING) {
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb) {
-      if (mb < mblocks) {
-        const u32x4 aop = *reinterpret_cast<const u32x4*>(
-            &sh.a[buf][(64 * wm + 16 * mb + n) * GEMM_LDS_STRIDE + 8 * g]);
+    for (int d = 0; d < GEMM_RING; ++d) {
+      const int step = kk + d;
+      const int buf = d & 1;  // = step & 1 (GEMM_RING is even)
+      // the next step goes into the other buffer (after the last step: harmless, unread)
+      stage((d + 1) % GEMM_RING, buf ^ 1, step + 1 + GEMM_RING);
+      u32x4 bop[4];
 #pragma unroll
-        for (int nb = 0; nb < 4; ++nb)
-          if (nb < nblocks) acc[mb][nb] = mfma_bf16(aop, bop[nb], acc[mb][nb]);
+      for (int nb = 0; nb < 4; ++nb)
+        bop[nb] = *reinterpret_cast<const u32x4*>(
+            &sh.b[buf][(64 * wn + 16 * nb + n) * GEMM_LDS_STRIDE + 8 * g]);
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb) {
+        if (mb < mblocks) {
+          const u32x4 aop = *reinterpret_cast<const u32x4*>(
+              &sh.a[buf][(64 * wm + 16 * mb + n) * GEMM_LDS_STRIDE + 8 * g]);
+#pragma unroll
+          for (int nb = 0; nb < 4; ++nb)
+            if (nb < nblocks) acc[mb][nb] = mfma_bf16(aop, bop[nb], acc[mb][nb]);
+        }
       }
+      lds_barrier();
     }
-    __syncthreads();
   }
 
 #pragma unroll

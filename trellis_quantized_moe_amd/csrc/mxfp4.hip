@@ -164,33 +164,41 @@ __global__ __launch_bounds__(GEMV_THREADS) void mxfp4_gemv_kernel(Mxfp4GemvArgs 
 // ---- prefill GEMM --------------------------------------------------------------------------
 // B producer: thread (o = tid / 2, h = tid % 2) decodes 16 codes of output o, inputs
 // 32 kk + 16 h .. +15, with the scale of block kk.
+// Thread t decodes, each step, inputs 16 h .. + 15 (h = t % 2) of the step for output
+// channel o = t / 2: 8 code bytes and the channel's scale byte of the step's 32-block.
 struct Mxfp4Producer {
-  const uint8_t* codes;
-  const uint8_t* scales;
-  int in, grp, ns, o, h;
+  struct Raw {
+    uint32_t c0, c1, sb;
+  };
+  GemmRsrc rc;
+  uint32_t vo_c, vo_s;
+  int o, h;
 
-  __device__ Mxfp4Producer(const uint8_t* unit, int out, int in_, int grp_, int ns_)
-      : codes(unit), scales(unit + (size_t)out * in_ / 2), in(in_), grp(grp_), ns(ns_) {
+  __device__ Mxfp4Producer(const uint8_t* unit, int out, int in, int grp, int ns) {
     o = threadIdx.x >> 1;
     h = threadIdx.x & 1;
+    rc = gemm_rsrc(unit, (uint32_t)((size_t)out * in / 2 + (size_t)out * in / 32));
+    // channels past the group read its last channel (their rows of the B tile are unused)
+    const int og = grp * 128 + (o < 16 * ns ? o : 16 * ns - 1);
+    vo_c = (uint32_t)((size_t)og * (in / 2) + 8 * h);
+    vo_s = (uint32_t)((size_t)out * in / 2 + (size_t)og * (in / 32));
   }
 
-  __device__ __forceinline__ void operator()(int kk, int* po, int* ph, uint32_t nat[8]) {
-    *po = o;
-    *ph = h;
-#pragma unroll
-    for (int t = 0; t < 8; ++t) nat[t] = 0u;
-    if (o < 16 * ns) {
-      const int og = grp * 128 + o;
-      const uint2 cw = *reinterpret_cast<const uint2*>(codes + (size_t)og * (in / 2) + 16 * kk + 8 * h);
-      const float sc = e8m0_to_f32(scales[(size_t)og * (in / 32) + kk]);
-      fp4x8_to_bf16(cw.x, sc, nat);
-      fp4x8_to_bf16(cw.y, sc, nat + 4);
-    }
+  __device__ __forceinline__ void load(int kk, Raw& r) const {
+    const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(rc, vo_c, 16u * kk, 0);
+    r.c0 = v.x;
+    r.c1 = v.y;
+    r.sb = __builtin_amdgcn_raw_buffer_load_b8(rc, vo_s, (uint32_t)kk, 0);
+  }
+
+  __device__ __forceinline__ void decode(const Raw& r, uint32_t nat[8]) const {
+    const float sc = e8m0_to_f32(r.sb);
+    fp4x8_to_bf16(r.c0, sc, nat);
+    fp4x8_to_bf16(r.c1, sc, nat + 4);
   }
 };
 
-__global__ __launch_bounds__(GEMM_THREADS) void mxfp4_gemm_kernel(Mxfp4GemmArgs a) {
+__global__ __launch_bounds__(GEMM_THREADS, 2) void mxfp4_gemm_kernel(Mxfp4GemmArgs a) {
   __shared__ GemmShared sh;
   const int item = blockIdx.x / a.groups;
   const int grp = blockIdx.x % a.groups;
@@ -200,6 +208,7 @@ __global__ __launch_bounds__(GEMM_THREADS) void mxfp4_gemm_kernel(Mxfp4GemmArgs 
   gemm_load_slots(sh, a.pairs, itd.y, itd.z);
   GemmItem it;
   it.x = a.x;
+  it.x_bytes = a.x_bytes;
   it.gates = a.gates;
   it.scales = nullptr;
   it.y = a.y;

@@ -92,6 +92,7 @@ struct TrellisGemmArgs {
   const uint32_t* codes;
   const uint16_t* scales;
   const uint16_t* x;
+  uint32_t x_bytes;  // size of x in bytes (< 2^31)
   const float* gates;
   const int32_t* pairs;
   const int32_t* items;
@@ -118,6 +119,7 @@ hipError_t launch_mxfp4_gemv(const Mxfp4GemvArgs& a, hipStream_t s);
 struct Mxfp4GemmArgs {
   const uint8_t* units;
   const uint16_t* x;
+  uint32_t x_bytes;  // size of x in bytes (< 2^31)
   const float* gates;
   const int32_t* pairs;
   const int32_t* items;

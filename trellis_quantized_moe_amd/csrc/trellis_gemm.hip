@@ -9,56 +9,91 @@ namespace tq {
 
 namespace {
 
+// Thread t decodes, each step, tile column 2 kk + c of strip s8 (s8 = t / 32, c = t / 16 % 2)
+// for output channel n = t % 16: 16 weights of channel 16 s8 + n. The 16 lanes of a tile
+// read its words once; the neighbour word comes from the next lane (row rotation).
 template <int K>
 struct TrellisProducer {
-  const uint32_t* unit;
-  int n_ti, grp, ns;
-  int s8, c, n, o0, o1, o2;
+  struct Raw {
+    uint32_t w[K == 2 ? 1 : (K == 4 ? 2 : 3)];
+  };
+  GemmRsrc rc;
+  uint32_t vo[3];
   uint32_t sh3;
+  int o, h;
 
-  __device__ TrellisProducer(const uint32_t* u, int in, int grp_, int ns_)
-      : unit(u), n_ti(in / 16), grp(grp_), ns(ns_) {
+  __device__ TrellisProducer(const uint32_t* unit, int out, int in, int grp, int ns) {
+    constexpr int TW = 8 * K;
     const int tid = threadIdx.x;
-    s8 = tid >> 5;
-    c = (tid >> 4) & 1;
-    n = tid & 15;
-    o0 = o1 = o2 = 0;
+    const int s8 = tid >> 5, c = (tid >> 4) & 1, n = tid & 15;
+    const int n_ti = in / 16;
+    o = 16 * s8 + n;
+    h = c;
+    rc = gemm_rsrc(unit, (uint32_t)((size_t)out * in * K / 8));
+    // strips past the group read its last strip (their rows of the B tile are never used)
+    const int strip = grp * 8 + (s8 < ns ? s8 : ns - 1);
+    const uint32_t base = (uint32_t)((strip * n_ti + c) * TW);
     sh3 = 0;
-    if constexpr (K == 3) k3_column_words(n, &o0, &o1, &o2, &sh3);
+    vo[0] = vo[1] = vo[2] = 0;
+    if constexpr (K == 2) {
+      vo[0] = 4u * (base + n);
+    } else if constexpr (K == 4) {
+      vo[0] = 4u * (base + 2 * n);
+    } else {
+      int a, b, d;
+      k3_column_words(n, &a, &b, &d, &sh3);
+      vo[0] = 4u * (base + a);
+      vo[1] = 4u * (base + b);
+      vo[2] = 4u * (base + d);
+    }
   }
 
-  __device__ __forceinline__ void operator()(int kk, int* o, int* h, uint32_t nat[8]) {
-    *o = 16 * s8 + n;
-    *h = c;
-#pragma unroll
-    for (int t = 0; t < 8; ++t) nat[t] = 0u;
-    if (s8 < ns) {
-      const uint32_t* tile = unit + (size_t)((grp * 8 + s8) * n_ti + 2 * kk + c) * (8 * K);
-      uint32_t M[8];
-      if constexpr (K == 2) {
-        const uint32_t w = tile[n];
-        col_mpairs_k2(w, row_next(w), M);
-      } else if constexpr (K == 4) {
-        const uint2 ww = *reinterpret_cast<const uint2*>(tile + 2 * n);
-        col_mpairs_k4(ww.x, ww.y, row_next(ww.x), M);
-      } else {
-        col_mpairs_k3(tile[o0], tile[o1], tile[o2], sh3, M);
-      }
-      mpairs_to_bf16_natural<K>(M, nat);
+  __device__ __forceinline__ void load(int kk, Raw& r) const {
+    constexpr int TW = 8 * K;
+    const uint32_t so = 4u * (uint32_t)(2 * kk * TW);  // two tile columns per step
+    if constexpr (K == 2) {
+      r.w[0] = __builtin_amdgcn_raw_buffer_load_b32(rc, vo[0], so, 0);
+    } else if constexpr (K == 4) {
+      const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(rc, vo[0], so, 0);
+      r.w[0] = v.x;
+      r.w[1] = v.y;
+    } else {
+      r.w[0] = __builtin_amdgcn_raw_buffer_load_b32(rc, vo[0], so, 0);
+      r.w[1] = __builtin_amdgcn_raw_buffer_load_b32(rc, vo[1], so, 0);
+      r.w[2] = __builtin_amdgcn_raw_buffer_load_b32(rc, vo[2], so, 0);
     }
+  }
+
+  __device__ __forceinline__ void decode(const Raw& r, uint32_t nat[8]) const {
+    uint32_t M[8];
+    if constexpr (K == 2)
+      col_mpairs_k2(r.w[0], row_next(r.w[0]), M);
+    else if constexpr (K == 4)
+      col_mpairs_k4(r.w[0], r.w[1], row_next(r.w[0]), M);
+    else
+      col_mpairs_k3(r.w[0], r.w[1], r.w[2], sh3, M);
+    mpairs_to_bf16_natural<K>(M, nat);
   }
 };
 
-__global__ __launch_bounds__(GEMM_THREADS) void trellis_gemm_kernel(TrellisGemmArgs a) {
+// One launch per width KW (each needs its own register budget): workgroups whose item has
+// another width leave at once; the KW = 2 launch also handles bad unit descriptors.
+template <int KW>
+__global__ __launch_bounds__(GEMM_THREADS, 2) void trellis_gemm_kernel(TrellisGemmArgs a) {
   __shared__ GemmShared sh;
   const int item = blockIdx.x / a.groups;
   const int grp = blockIdx.x % a.groups;
   if (item >= *a.n_items) return;
   const int4 itd = reinterpret_cast<const int4*>(a.items)[item];
   const int e = itd.x;
+  const int K = a.bits[e];
+  const int64_t off = a.code_off[e];
+  const bool bad = (K < 2 || K > 4) || (off & 15);
+  if (bad ? KW != 2 : K != KW) return;
   gemm_load_slots(sh, a.pairs, itd.y, itd.z);
   GemmItem it;
   it.x = a.x;
+  it.x_bytes = a.x_bytes;
   it.gates = a.gates;
   it.scales = a.scales + (size_t)e * a.out;
   it.y = a.y;
@@ -68,24 +103,13 @@ __global__ __launch_bounds__(GEMM_THREADS) void trellis_gemm_kernel(TrellisGemmA
   it.grp = grp;
   it.nrows = itd.z;
   it.ns = min(8, a.out / 16 - grp * 8);
-  const int K = a.bits[e];
-  const int64_t off = a.code_off[e];
-  if ((K < 2 || K > 4) || (off & 15)) {
+  if (bad) {
     gemm_item_nan(it, sh);
     if (threadIdx.x == 0) set_status(a.status, STATUS_BAD_UNIT);
     return;
   }
-  const uint32_t* unit = a.codes + off / 4;
-  if (K == 2) {
-    TrellisProducer<2> p(unit, a.in, grp, it.ns);
-    gemm_item(it, sh, p);
-  } else if (K == 3) {
-    TrellisProducer<3> p(unit, a.in, grp, it.ns);
-    gemm_item(it, sh, p);
-  } else {
-    TrellisProducer<4> p(unit, a.in, grp, it.ns);
-    gemm_item(it, sh, p);
-  }
+  TrellisProducer<KW> p(a.codes + off / 4, a.out, a.in, grp, it.ns);
+  gemm_item(it, sh, p);
 }
 
 }  // namespace
@@ -93,7 +117,9 @@ __global__ __launch_bounds__(GEMM_THREADS) void trellis_gemm_kernel(TrellisGemmA
 hipError_t launch_trellis_gemm(const TrellisGemmArgs& a, hipStream_t s) {
   const int blocks = a.max_items * a.groups;
   if (blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL(trellis_gemm_kernel, dim3(blocks), dim3(GEMM_THREADS), 0, s, a);
+  hipLaunchKernelGGL(trellis_gemm_kernel<2>, dim3(blocks), dim3(GEMM_THREADS), 0, s, a);
+  hipLaunchKernelGGL(trellis_gemm_kernel<3>, dim3(blocks), dim3(GEMM_THREADS), 0, s, a);
+  hipLaunchKernelGGL(trellis_gemm_kernel<4>, dim3(blocks), dim3(GEMM_THREADS), 0, s, a);
   return hipGetLastError();
 }
 
