@@ -3,12 +3,14 @@
 A step is one pass of the whole hot path over one batch of seeded synthetic input, with
 every input already resident in device memory:
   mixed (headline): the mixed-width trellis layer, 384 experts of 128 x 5120 (368 K=2,
-      15 K=3, 1 K=4), 128 tokens, top-8 — 128-wide rotation of the inputs, then the
-      decode-batch grouped GEMV (route scan, fetch, state rebuild, T16 hash, staging,
-      matrix-core contraction, epilogue);
+      15 K=3, 1 K=4), 128 tokens, top-8 — the plan + activation prep kernel (route scan,
+      128-wide signed rotation of the inputs, f16 staging), the decode-batch grouped GEMV
+      (fetch, state rebuild, T16 hash, matrix-core contraction) and the piece reduction
+      (epilogue);
   mxfp4: the MXFP4 layer, 384 experts, 64 tokens, top-8 with gates — decode-batch GEMV;
-  prefill: 8,192 tokens, top-8 over 384 K=3 experts with Zipf(1.1) popularity — rotation,
-      route bucketing (three kernels), grouped MFMA GEMM.
+  prefill: 8,192 tokens, top-8 over 384 K=3 experts with Zipf(1.1) popularity — the
+      activation prep with the fused rotation, route bucketing (three kernels), grouped
+      MFMA GEMM.
 Steps are captured as HIP graphs and replayed; each step reads a different replica of the
 code buffer (replicas total >= 1 GiB) so the 256 MB Infinity Cache cannot serve repeats.
 
@@ -37,7 +39,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
-BF16_PEAK_TFLOPS = 2500.0
+F16_PEAK_TFLOPS = 2500.0
 MALL_BYTES = 1 << 30          # replicas of the code buffer total at least this much
 SLEEP_CYCLES = 60_000_000     # ~25 ms at 2.4 GHz: the GPU is busy while launches queue
 
@@ -75,23 +77,6 @@ def time_graph_steps(torch, graphs, steps, warmup):
         graphs[i % len(graphs)].replay()
     torch.cuda.synchronize()
     return (time.perf_counter() - t0) / steps
-
-
-def time_kernel(torch, launch, n_replicas, iters):
-    """Average duration of one launch, from an event pair around each launch."""
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(iters)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(iters)]
-    for r in range(n_replicas):           # warm every replica's code path once
-        launch(r)
-    torch.cuda.synchronize()
-    torch.cuda._sleep(SLEEP_CYCLES)
-    for i in range(iters):
-        starts[i].record()
-        launch(i % n_replicas)
-        ends[i].record()
-    torch.cuda.synchronize()
-    ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
-    return float(np.mean(ms)) / 1e3, float(np.median(ms)) / 1e3
 
 
 GEMV_SOURCES = ["trellis_gemv.hip", "trellis_decode.h", "gemv_plan.h", "tq_device.h",
@@ -158,21 +143,18 @@ def bench_mixed(torch, ops, args):
     dev = torch.device("cuda", 0)
     L = ops.TrellisLayer.from_host(lay, dev)
     x = torch.from_numpy(wl["x"].view(np.int16)).to(dev)
-    signs = torch.from_numpy(lay["signs"]).to(dev)
     ids = torch.from_numpy(wl["topk_ids"]).to(dev)
     T, topk = wl["topk_ids"].shape
     nbytes, n_active = active_bytes_trellis(lay, wl["topk_ids"])
     reps = replicate(torch, L.codes, L.codes.numel() * 4)
     layers = [L.with_codes(c) for c in reps]
-    xr = torch.empty_like(x)
     y = torch.empty((T, topk, lay["out"]), dtype=torch.float32, device=dev)
     ws = ops.workspace(T, topk, lay["E"], lay["out"], lay["in"], ops.TQ_AUTO, dev)
     log("mixed: %d active experts, %.1f MB compressed per step, %d replicas"
         % (n_active, nbytes / 1e6, len(reps)))
 
     def step(r):
-        ops.hadamard128(x, signs, out=xr)
-        ops.trellis_expert_gemm(layers[r], xr, ids, out=y, ws=ws)
+        ops.trellis_expert_gemm(layers[r], x, ids, flags=ops.TQ_ROTATE, out=y, ws=ws)
 
     for r in range(len(reps)):
         step(r)
@@ -184,16 +166,13 @@ def bench_mixed(torch, ops, args):
             step(r)
         graphs.append(g)
     sec = time_graph_steps(torch, graphs, args.steps, args.warmup)
-    kmean, kmed = time_main_kernel(
-        torch, ops, lambda r: ops.trellis_expert_gemm(layers[r], xr, ids, out=y, ws=ws),
-        len(reps), args.kernel_iters)
-    hmean, _ = time_kernel(torch, lambda r: ops.hadamard128(x, signs, out=xr), 1, args.kernel_iters)
+    kmean, kmed = time_main_kernel(torch, ops, step, len(reps), args.kernel_iters)
     shash = source_hash(GEMV_SOURCES)
     traffic = traffic_from_profile("trellis_gemv_mixed", shash, nbytes)
     return {
         "sec_per_step": sec, "bytes": nbytes, "n_active": n_active,
         "kernel": "trellis_gemv_kernel", "kernel_sec": kmean, "kernel_sec_median": kmed,
-        "hadamard_sec": hmean, "traffic": traffic, "source_hash": shash,
+        "traffic": traffic, "source_hash": shash,
         "replicas": len(reps), "wl": wl,
     }
 
@@ -240,20 +219,17 @@ def bench_prefill(torch, ops, args):
     dev = torch.device("cuda", 0)
     L = ops.TrellisLayer.from_host(lay, dev)
     x = torch.from_numpy(wl["x"].view(np.int16)).to(dev)
-    signs = torch.from_numpy(lay["signs"]).to(dev)
     ids = torch.from_numpy(wl["topk_ids"]).to(dev)
     T, topk = wl["topk_ids"].shape
     flops = 2.0 * T * topk * lay["out"] * lay["in"]
     reps = replicate(torch, L.codes, L.codes.numel() * 4)
     layers = [L.with_codes(c) for c in reps]
-    xr = torch.empty_like(x)
     y = torch.empty((T, topk, lay["out"]), dtype=torch.float32, device=dev)
     ws = ops.workspace(T, topk, lay["E"], lay["out"], lay["in"], ops.TQ_AUTO, dev)
     log("prefill: %.1f GFLOP per step, %d replicas" % (flops / 1e9, len(reps)))
 
     def step(r):
-        ops.hadamard128(x, signs, out=xr)
-        ops.trellis_expert_gemm(layers[r], xr, ids, out=y, ws=ws)
+        ops.trellis_expert_gemm(layers[r], x, ids, flags=ops.TQ_ROTATE, out=y, ws=ws)
 
     for r in range(len(reps)):
         step(r)
@@ -266,9 +242,7 @@ def bench_prefill(torch, ops, args):
         graphs.append(g)
     steps = max(10, args.steps // 20)
     sec = time_graph_steps(torch, graphs, steps, max(2, args.warmup // 10))
-    kmean, kmed = time_main_kernel(
-        torch, ops, lambda r: ops.trellis_expert_gemm(layers[r], xr, ids, out=y, ws=ws),
-        len(reps), max(10, args.kernel_iters // 10))
+    kmean, kmed = time_main_kernel(torch, ops, step, len(reps), max(10, args.kernel_iters // 10))
     return {"sec_per_step": sec, "flops": flops, "steps": steps,
             "kernel": "trellis_gemm_kernel", "kernel_sec": kmean, "kernel_sec_median": kmed}
 
@@ -324,17 +298,15 @@ def drive(torch, ops, which, iters):
         lay = wl["layer"]
         L = ops.TrellisLayer.from_host(lay, dev)
         x = torch.from_numpy(wl["x"].view(np.int16)).to(dev)
-        signs = torch.from_numpy(lay["signs"]).to(dev)
         ids = torch.from_numpy(wl["topk_ids"]).to(dev)
         T, topk = wl["topk_ids"].shape
         reps = replicate(torch, L.codes, L.codes.numel() * 4)
         layers = [L.with_codes(c) for c in reps]
-        xr = torch.empty_like(x)
         y = torch.empty((T, topk, lay["out"]), dtype=torch.float32, device=dev)
         ws = ops.workspace(T, topk, lay["E"], lay["out"], lay["in"], ops.TQ_AUTO, dev)
         for i in range(iters):
-            ops.hadamard128(x, signs, out=xr)
-            ops.trellis_expert_gemm(layers[i % len(layers)], xr, ids, out=y, ws=ws)
+            ops.trellis_expert_gemm(layers[i % len(layers)], x, ids, flags=ops.TQ_ROTATE,
+                                    out=y, ws=ws)
     else:
         wl = mxfp4_decode_layer()
         lay = wl["layer"]
@@ -454,7 +426,7 @@ def main():
             "workload": "mixed-width trellis layer (K2 Mix style) decode batch",
             "experts": 384, "unit": "128x5120", "widths": "368xK2 15xK3 1xK4",
             "tokens": 128, "topk": 8, "active_experts": res["n_active"],
-            "compressed_bytes_per_step": res["bytes"], "rotation": "hadamard128 on inputs",
+            "compressed_bytes_per_step": res["bytes"], "rotation": "128-wide signed Hadamard fused into the activation prep",
             "replicas": res["replicas"],
         },
         "roofline": {
@@ -470,7 +442,6 @@ def main():
             "algorithmic_bytes_per_launch": res["bytes"],
             "source_hash": res["source_hash"],
         },
-        "hadamard_us": round(res["hadamard_sec"] * 1e6, 3),
     }
     extras = {}
     todo = [] if args.extras == "none" else [e for e in args.extras.split(",") if e]
@@ -493,7 +464,7 @@ def main():
             "ms_per_step": round(p["sec_per_step"] * 1e3, 5), "steps": p["steps"],
             "kernel": p["kernel"], "kernel_us": round(p["kernel_sec"] * 1e6, 3),
             "kernel_TFLOP/s": round(p["flops"] / p["kernel_sec"] / 1e12, 3),
-            "frac_bf16_peak": round(p["flops"] / p["kernel_sec"] / 1e12 / BF16_PEAK_TFLOPS, 4),
+            "frac_f16_peak": round(p["flops"] / p["kernel_sec"] / 1e12 / F16_PEAK_TFLOPS, 4),
         }
     if extras:
         line["extras"] = extras

@@ -47,6 +47,8 @@ extern "C" {
 #define TQ_GEMV 1u     /* force the decode-batch kernel (grouped GEMV, tokens in 16s)      */
 #define TQ_GEMM 2u     /* force the prefill kernel (route bucketing + grouped MFMA GEMM)   */
 #define TQ_COMBINE 4u  /* write y[T][out] = sum over k = 0..topk-1 (in order) of the slots */
+#define TQ_ROTATE 8u   /* trellis only: x is not rotated; the call applies hadamard128 with */
+                       /* the layer's signs first (same bits as calling hadamard128)        */
 
 /* ---- device status bits (tq_device_status) ------------------------------------------ */
 #define TQ_STATUS_BAD_EXPERT 1u  /* an id outside [-1, E): that slot's output is NaN    */
@@ -70,6 +72,7 @@ typedef struct tq_trellis_layer {
   const int64_t* code_off;  /* device [E]: byte offset of each unit in codes, 16-aligned  */
   const uint32_t* codes;    /* device: the units                                          */
   const uint16_t* scales;   /* device [E][out]: fp16 per-output-channel scales            */
+  const int8_t* signs;      /* device [in]: +-1 rotation signs for TQ_ROTATE, or NULL     */
 } tq_trellis_layer;
 
 /*
@@ -95,13 +98,17 @@ typedef struct tq_mxfp4_layer {
  * materialised in memory.
  *   L         host: the layer description above.
  *   x         device bf16 [T][L->in], 16-byte aligned rows. Pass the rotated inputs
- *             (hadamard128 output) for layers encoded with rotated inputs.
+ *             (hadamard128 output) for layers encoded with rotated inputs, or the
+ *             unrotated ones with TQ_ROTATE.
  *   T         tokens (>= 0; T == 0 is a successful no-op).
  *   topk_ids  device int32 [T][topk]; -1 = empty slot (output zero).
  *   topk_w    device fp32 [T][topk] gates, or NULL for gate 1.
  *   topk      slots per token, 1 .. 64.
  *   y         device fp32, 16-byte aligned: [T][topk][out], or [T][out] with TQ_COMBINE.
- *   flags     TQ_AUTO / TQ_GEMV / TQ_GEMM, optionally | TQ_COMBINE.
+ *   flags     TQ_AUTO / TQ_GEMV / TQ_GEMM, optionally | TQ_COMBINE and | TQ_ROTATE
+ *             (then x is the unrotated input; the rotation of hadamard128 with L->signs,
+ *             or without signs when it is NULL, is applied while the activations are
+ *             prepared, bit for bit as a separate hadamard128 call would).
  *   ws        device workspace of at least tq_workspace_bytes(T, topk, E, out, in, flags)
  *             bytes, 256-byte aligned, ZERO-FILLED BEFORE ITS FIRST USE. Every call leaves
  *             its counters at zero again, so a workspace is initialised once and reused;
@@ -112,8 +119,7 @@ typedef struct tq_mxfp4_layer {
  * routed expert's inputs among workgroups in proportion to the batch's whole routed work,
  * so across batches that route differently a slot's fp32 sum is grouped differently and
  * agrees to rounding (about 1e-7 relative).
- * Precondition of the decode-batch kernel: |x| < 65520 (it feeds the matrix cores f16
- * operands, FORMAT F10).
+ * Precondition: |x| < 65520 (the kernels feed the matrix cores f16 operands, FORMAT F10).
  */
 int trellis_expert_gemm(const tq_trellis_layer* L, const void* x, int64_t T,
                         const int32_t* topk_ids, const float* topk_w, int32_t topk,
@@ -160,7 +166,9 @@ int route_bucket(const int32_t* topk_ids, int64_t T, int32_t topk, int32_t E,
 
 /*
  * trellis_decode — test hook: decode one trellis unit to its integer values with the
- * same device decoders the GEMV (path 0) or GEMM (path 1) kernels use.
+ * device decoders. Path 0 reads back the operands the matrix-core kernels (decode-batch
+ * GEMV and prefill GEMM) receive: the byte sums q + 255 as f16 subnormals. Path 1 goes
+ * through an exact bf16 conversion of q instead (a second, independent readout).
  *   codes  device, out*in*K/8 bytes, 16-byte aligned.   K in {2, 3, 4}.
  *   q      device int16 [out][in] (HF orientation: row = output channel).
  */

@@ -42,8 +42,8 @@ def test_version(lib):
     assert lib.tq_version() == 100
 
 
-def _layer(E=4, out=128, inp=5120, fake=0x1000):
-    return _lib.TrellisLayerC(E, out, inp, 0, fake, fake, fake, fake)
+def _layer(E=4, out=128, inp=5120, fake=0x1000, signs=None):
+    return _lib.TrellisLayerC(E, out, inp, 0, fake, fake, fake, fake, signs)
 
 
 def _call_trellis(lib, layer, T=2, topk=2, x=0x1000, ids=0x1000, y=0x1000, flags=0,
@@ -68,7 +68,9 @@ def test_trellis_argument_errors(lib):
     assert _call_trellis(lib, _layer(), T=-1) == _lib.TQ_EINVAL
     assert _call_trellis(lib, _layer(), T=1 << 30, topk=4) == _lib.TQ_EINVAL
     assert _call_trellis(lib, _layer(), flags=3) == _lib.TQ_EINVAL
-    assert _call_trellis(lib, _layer(), flags=8) == _lib.TQ_EINVAL
+    assert _call_trellis(lib, _layer(), flags=16) == _lib.TQ_EINVAL
+    # TQ_ROTATE reads 16 signs per tile column: the signs must be 16-byte aligned
+    assert _call_trellis(lib, _layer(signs=0x1008), flags=_lib.TQ_ROTATE) == _lib.TQ_EALIGN
     assert _call_trellis(lib, _layer(), x=0x1002) == _lib.TQ_EALIGN
     assert _call_trellis(lib, _layer(), y=0) == _lib.TQ_EINVAL
     assert _call_trellis(lib, _layer(), ids=0) == _lib.TQ_EINVAL
@@ -97,6 +99,10 @@ def test_mxfp4_argument_errors(lib):
     m = _lib.Mxfp4LayerC(4, 128, 5120, 0, 0x1001)
     assert lib.mxfp4_expert_gemm(ctypes.byref(m), 0x1000, 1, 0x1000, None, 1, 0x1000, 0, 0x1000,
                                  1 << 30, None) == _lib.TQ_EALIGN
+    # the input rotation is a trellis-layer option
+    m = _lib.Mxfp4LayerC(4, 128, 5120, 0, 0x1000)
+    assert lib.mxfp4_expert_gemm(ctypes.byref(m), 0x1000, 1, 0x1000, None, 1, 0x1000,
+                                 _lib.TQ_ROTATE, 0x1000, 1 << 30, None) == _lib.TQ_EINVAL
 
 
 def test_hadamard_decode_route_argument_errors(lib):

@@ -256,3 +256,31 @@ def test_prefill_chunk_full_size_sampled():
         rng.choice(flat.size, 16, replace=False)]))
     ref = oracle_trellis(layer, xr, ids, None, sample=sample)
     assert rel_l2(y.reshape(-1, 128)[sample], ref.reshape(-1, 128)[sample]) <= TOL
+
+
+@pytest.mark.parametrize("flags", [1, 2])
+def test_fused_rotation_equals_separate_hadamard(flags):
+    """TQ_ROTATE applies the layer's signed 128-wide rotation inside the activation prep:
+    the result is bit-identical to rotating first with hadamard128 (same fp32 butterfly,
+    same bf16 rounding) and calling without the flag."""
+    o = ops()
+    E, T, topk, inp = 12, 37, 4, 768
+    layer = small_layer(412, E, 256, inp)
+    L = o.TrellisLayer.from_host(layer)
+    x = to_dev(bf16_from_normal(rng_for(412, 1), (T, inp)), np.int16)
+    ids = to_dev(uniform_routes(rng_for(412, 2), T, E, topk))
+    gates = to_dev(softmax_gates(rng_for(412, 3), T, topk))
+    fused = o.trellis_expert_gemm(L, x, ids, gates, flags=flags | o.TQ_ROTATE)
+    xr = o.hadamard128(x, L.signs)
+    sep = o.trellis_expert_gemm(L, xr, ids, gates, flags=flags)
+    torch.cuda.synchronize()
+    assert torch.equal(fused, sep)
+    # without signs the rotation is the plain normalised Walsh-Hadamard transform
+    L0 = o.TrellisLayer(L.E, L.out, L.in_, L.bits, L.code_off, L.codes, L.scales, None)
+    fused0 = o.trellis_expert_gemm(L0, x, ids, flags=flags | o.TQ_ROTATE)
+    sep0 = o.trellis_expert_gemm(L0, o.hadamard128(x), ids, flags=flags)
+    torch.cuda.synchronize()
+    assert torch.equal(fused0, sep0)
+    ref = oracle_trellis(layer, xr.cpu().numpy().view(np.uint16), ids.cpu().numpy(),
+                         gates.cpu().numpy())
+    assert rel_l2(fused.cpu().numpy(), ref) <= TOL

@@ -21,6 +21,7 @@ TQ_AUTO = 0
 TQ_GEMV = 1
 TQ_GEMM = 2
 TQ_COMBINE = 4
+TQ_ROTATE = 8
 
 TQ_STATUS_BAD_EXPERT = 1
 TQ_STATUS_BAD_UNIT = 2
@@ -36,6 +37,7 @@ class TrellisLayerC(ctypes.Structure):
         ("code_off", ctypes.c_void_p),
         ("codes", ctypes.c_void_p),
         ("scales", ctypes.c_void_p),
+        ("signs", ctypes.c_void_p),
     ]
 
 

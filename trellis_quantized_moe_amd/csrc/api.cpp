@@ -68,7 +68,7 @@ int check_device() {
 }
 
 bool flags_valid(uint32_t flags) {
-  return (flags & ~7u) == 0 && (flags & 3u) != 3u;
+  return (flags & ~15u) == 0 && (flags & 3u) != 3u;
 }
 
 bool use_gemm(int64_t T, int topk, int E, uint32_t flags) {
@@ -182,6 +182,12 @@ WsLayout ws_layout(int64_t T, int topk, int E, int out, int in, uint32_t flags, 
     L.n_items = off;
     off += 256;
     L.route_bytes = off - start;
+    if (!mxfp4) {  // the trellis GEMM reads prepared f16 activations
+      L.xprep = off;
+      off += round_up((size_t)T * in * 2, 256);
+      L.rowsum = off;
+      off += round_up((size_t)T * 4, 256);
+    }
   }
   if ((flags & TQ_COMBINE) && (L.gemm || (mxfp4 && L.gemv_slices == 1))) {
     L.slots = off;
@@ -426,6 +432,8 @@ int trellis_expert_gemm(const tq_trellis_layer* L, const void* x, int64_t T,
                         uint32_t flags, void* ws, size_t ws_bytes, void* stream) {
   int rc = check_trellis_layer(L);
   if (rc) return rc;
+  if ((flags & TQ_ROTATE) && L->signs && !aligned(L->signs, 16))
+    return fail(TQ_EALIGN, "signs must be 16-byte aligned");
   tq::WsLayout W;
   rc = common_checks(L->E, L->out, L->in, x, T, topk_ids, topk, y, flags, ws, ws_bytes, false, &W);
   if (rc) return rc;
@@ -460,6 +468,8 @@ int trellis_expert_gemm(const tq_trellis_layer* L, const void* x, int64_t T,
     p.rank = at<int32_t>(ws, W.prank);
     p.status = at<uint32_t>(ws, W.status);
     p.x = xb;
+    p.rotate = (flags & TQ_ROTATE) != 0;
+    p.signs = L->signs;
     p.T = (int)T;
     p.in = L->in;
     p.xp = at<uint32_t>(ws, W.xprep);
@@ -507,6 +517,10 @@ int trellis_expert_gemm(const tq_trellis_layer* L, const void* x, int64_t T,
     if (err != hipSuccess) return hip_fail(err, "GEMV piece reduction launch");
     return ok();
   } else {
+    err = tq::launch_activation_prep(xb, T, L->in, at<uint32_t>(ws, W.xprep),
+                                     at<float>(ws, W.rowsum), (flags & TQ_ROTATE) != 0,
+                                     L->signs, s);
+    if (err != hipSuccess) return hip_fail(err, "activation prep launch");
     rc = run_route(W, ws, topk_ids, N, L->E, L->out, y_slots, s);
     if (rc) return rc;
     tq::TrellisGemmArgs a{};
@@ -514,7 +528,8 @@ int trellis_expert_gemm(const tq_trellis_layer* L, const void* x, int64_t T,
     a.code_off = L->code_off;
     a.codes = L->codes;
     a.scales = L->scales;
-    a.x = xb;
+    a.xp = at<uint32_t>(ws, W.xprep);
+    a.rowsum = at<float>(ws, W.rowsum);
     a.x_bytes = (uint32_t)(T * L->in * 2);
     a.gates = topk_w;
     a.pairs = at<int32_t>(ws, W.pairs);
@@ -546,6 +561,7 @@ int mxfp4_expert_gemm(const tq_mxfp4_layer* L, const void* x, int64_t T,
                       uint32_t flags, void* ws, size_t ws_bytes, void* stream) {
   int rc = check_mxfp4_layer(L);
   if (rc) return rc;
+  if (flags & TQ_ROTATE) return fail(TQ_EINVAL, "TQ_ROTATE applies to trellis layers only");
   tq::WsLayout W;
   rc = common_checks(L->E, L->out, L->in, x, T, topk_ids, topk, y, flags, ws, ws_bytes, true, &W);
   if (rc) return rc;

@@ -3,10 +3,11 @@
 // One workgroup (4 waves, 2 x 2 over a 128 x 128 output tile) multiplies up to 128 routed
 // rows of one expert by one group of up to 128 output channels over the whole K range, in
 // steps of 32 inputs:
-//   - a B producer (format-specific) decodes the step's 32 x 128 weights into bf16, each
-//     thread one run of 16 inputs of one output channel, stored in natural input order;
+//   - a B producer (format-specific) decodes the step's 32 x 128 weights into operand
+//     pairs, each thread one run of 16 inputs of one output channel;
 //   - each thread copies 16 activations of one routed row into the A tile;
-//   - each wave runs its 4 x 4 block of 16x16x32 bf16 matrix-core operations.
+//   - each wave runs its 4 x 4 block of 16x16x32 matrix-core operations (f16 for trellis
+//     weights, whose byte sums are exact f16 subnormals; bf16 for MXFP4).
 // Two LDS buffers alternate: while the waves multiply step kk, they decode and stage step
 // kk + 1 into the other buffer, from registers loaded GEMM_RING steps earlier. Each output
 // is written once by the workgroup owning its row.
@@ -30,8 +31,9 @@ struct GemmShared {
 };
 
 struct GemmItem {
-  const uint16_t* x;
+  const void* x;           // bf16 x [T][in], or f16 pairs [T][in/16][8] (producer kF16)
   uint32_t x_bytes;        // size of x in bytes (< 2^31)
+  const float* rowsum;     // kF16: per-token sums of the f16 activations
   const float* gates;
   const uint16_t* scales;  // fp16 per output channel of this expert, or null
   float* y;
@@ -54,10 +56,14 @@ __device__ __forceinline__ GemmRsrc gemm_rsrc(const void* base, uint32_t bytes) 
 }
 
 // Producer interface (format-specific B operand):
+//   static constexpr bool kF16    true: f16 operands (the B values are the trellis byte
+//                                 sums (q + 255) as f16 subnormals, A is the f16 pair layout,
+//                                 and the epilogue scales by 2^24 and removes 255 * sum x);
+//                                 false: bf16 operands in natural input order
 //   typename Raw                  this thread's undecoded data of one step (registers)
 //   void load(int kk, Raw& r)     issues the loads of step kk (any kk < steps)
 //   void decode(const Raw& r, uint32_t nat[8])
-//                                 bf16 pairs of the thread's run, natural input order
+//                                 the thread's run as 8 dwords of operand pairs
 //   int o, h                      the run: output channel o (0..127 within the group),
 //                                 inputs 32 kk + 16 h .. + 15
 //
@@ -73,7 +79,8 @@ __device__ void gemm_item(const GemmItem& it, GemmShared& sh, Producer& prod) {
   const int wm = w >> 1, wn = w & 1;
   const int nsteps = it.in / GEMM_KS;  // a multiple of 8 (in is a multiple of 256)
   // A staging: thread (a_m, a_h) copies inputs 16 a_h .. + 15 of the step for routed row
-  // a_m (rows past the item's count copy token 0's row; they are never stored)
+  // a_m (rows past the item's count copy token 0's row; they are never stored). Both
+  // activation layouts keep these 16 inputs in 32 contiguous bytes at the same offset.
   const int a_m = tid >> 1, a_h = tid & 1;
   const int a_tok = a_m < it.nrows ? sh.slot[a_m] / it.topk : 0;
   const GemmRsrc ra = gemm_rsrc(it.x, it.x_bytes);
@@ -136,7 +143,12 @@ __device__ void gemm_item(const GemmItem& it, GemmShared& sh, Producer& prod) {
               &sh.a[buf][(64 * wm + 16 * mb + n) * GEMM_LDS_STRIDE + 8 * g]);
 #pragma unroll
           for (int nb = 0; nb < 4; ++nb)
-            if (nb < nblocks) acc[mb][nb] = mfma_bf16(aop, bop[nb], acc[mb][nb]);
+            if (nb < nblocks) {
+              if constexpr (Producer::kF16)
+                acc[mb][nb] = mfma_f16(aop, bop[nb], acc[mb][nb]);
+              else
+                acc[mb][nb] = mfma_bf16(aop, bop[nb], acc[mb][nb]);
+            }
         }
       }
       lds_barrier();
@@ -155,7 +167,10 @@ __device__ void gemm_item(const GemmItem& it, GemmShared& sh, Producer& prod) {
           const int row = 64 * wm + 16 * mb + 4 * g + i;
           if (row < it.nrows) {
             const int slot = sh.slot[row];
-            float v = acc[mb][nb][i] * sc;
+            float v = acc[mb][nb][i];
+            if constexpr (Producer::kF16)
+              v = v * 16777216.0f - 255.0f * it.rowsum[slot / it.topk];
+            v = v * sc;
             if (it.gates) v = v * it.gates[slot];
             it.y[(size_t)slot * it.out + o] = v;
           }

@@ -245,8 +245,49 @@ __device__ void plan_block(const PlanArgs& a) {
   if (tid == 0 && s_status) set_status(a.status, s_status);
 }
 
+// Optional input rotation, the 128-wide Hadamard of FORMAT F8 on the 16 values of tile
+// column c held by this lane: signs, then fp32 butterflies (a, b) -> (a + b, a - b) with
+// strides 1, 2, 4, 8 inside the lane and 16, 32, 64 across lanes c ^ 1, 2, 4 (the 8 lanes
+// of one 128-block), then x 0x3DB504F3 and bf16 round-to-nearest-even. Every stage is the
+// same fp32 operation on the same values as in hadamard128, so the bits are the same.
+__device__ __forceinline__ void rotate_column(float f[16], const int8_t* signs, int c) {
+  if (signs) {
+    const uint4 sg = *reinterpret_cast<const uint4*>(signs + 16 * c);
+    const uint32_t s4[4] = {sg.x, sg.y, sg.z, sg.w};
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int8_t sj = (int8_t)((s4[j >> 2] >> (8 * (j & 3))) & 0xFF);
+      if (sj < 0) f[j] = -f[j];
+    }
+  }
+#pragma unroll
+  for (int h = 1; h < 16; h <<= 1) {
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      if ((j & h) == 0) {
+        const float x0 = f[j], x1 = f[j + h];
+        f[j] = x0 + x1;
+        f[j + h] = x0 - x1;
+      }
+    }
+  }
+#pragma unroll
+  for (int d = 1; d < 8; d <<= 1) {
+    const bool upper = (c & d) != 0;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const float other = __shfl_xor(f[j], d, 64);
+      f[j] = upper ? other - f[j] : f[j] + other;
+    }
+  }
+  const float scale = __uint_as_float(0x3DB504F3u);
+#pragma unroll
+  for (int j = 0; j < 16; ++j) f[j] = __uint_as_float(f32_to_bf16_rne(f[j] * scale) << 16);
+}
+
 // One token per block: thread c converts tile column c (columns c + PLAN_THREADS, ... when
-// in > 16 * PLAN_THREADS). Waves without a column leave at once.
+// in > 16 * PLAN_THREADS), rotating it first when asked. Waves without a column leave at
+// once (a 128-block's 8 columns are always in one wave and all present or all absent).
 __device__ void prep_block(const PlanArgs& a, int t) {
   typedef _Float16 h2 __attribute__((ext_vector_type(2)));
   __shared__ float s_sum[PLAN_WAVES];
@@ -266,6 +307,7 @@ __device__ void prep_block(const PlanArgs& a, int t) {
       f[2 * k] = bf16_lo_to_f32(wv[k]);
       f[2 * k + 1] = bf16_hi_to_f32(wv[k]);
     }
+    if (a.rotate) rotate_column(f, a.signs, c);
     uint32_t P[8];
     float hf[16];
 #pragma unroll
@@ -301,6 +343,10 @@ __global__ __launch_bounds__(PLAN_THREADS) void gemv_plan_kernel(PlanArgs a) {
     prep_block(a, blockIdx.x - 1);
 }
 
+__global__ __launch_bounds__(PLAN_THREADS) void activation_prep_kernel(PlanArgs a) {
+  prep_block(a, blockIdx.x);
+}
+
 }  // namespace
 
 hipError_t launch_gemv_plan(const PlanArgs& a, hipStream_t s) {
@@ -309,6 +355,22 @@ hipError_t launch_gemv_plan(const PlanArgs& a, hipStream_t s) {
     hipLaunchKernelGGL(gemv_plan_kernel<true>, dim3(blocks), dim3(PLAN_THREADS), 0, s, a);
   else
     hipLaunchKernelGGL(gemv_plan_kernel<false>, dim3(blocks), dim3(PLAN_THREADS), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_activation_prep(const uint16_t* x, int64_t T, int in, uint32_t* xp,
+                                  float* rowsum, bool rotate, const int8_t* signs,
+                                  hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  PlanArgs a{};
+  a.x = x;
+  a.rotate = rotate;
+  a.signs = signs;
+  a.T = (int)T;
+  a.in = in;
+  a.xp = xp;
+  a.rowsum = rowsum;
+  hipLaunchKernelGGL(activation_prep_kernel, dim3((unsigned)T), dim3(PLAN_THREADS), 0, s, a);
   return hipGetLastError();
 }
 

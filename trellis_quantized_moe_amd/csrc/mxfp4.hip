@@ -167,6 +167,7 @@ __global__ __launch_bounds__(GEMV_THREADS) void mxfp4_gemv_kernel(Mxfp4GemvArgs 
 // Thread t decodes, each step, inputs 16 h .. + 15 (h = t % 2) of the step for output
 // channel o = t / 2: 8 code bytes and the channel's scale byte of the step's 32-block.
 struct Mxfp4Producer {
+  static constexpr bool kF16 = false;
   struct Raw {
     uint32_t c0, c1, sb;
   };
@@ -209,6 +210,7 @@ __global__ __launch_bounds__(GEMM_THREADS, 2) void mxfp4_gemm_kernel(Mxfp4GemmAr
   GemmItem it;
   it.x = a.x;
   it.x_bytes = a.x_bytes;
+  it.rowsum = nullptr;
   it.gates = a.gates;
   it.scales = nullptr;
   it.y = a.y;

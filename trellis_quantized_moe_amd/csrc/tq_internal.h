@@ -50,11 +50,19 @@ struct PlanArgs {
   uint32_t* status;
   // activation prep (trellis): x null = none
   const uint16_t* x;
+  bool rotate;              // apply the 128-wide Hadamard (FORMAT F8) first
+  const int8_t* signs;      // its signs, or null
   int T, in;
   uint32_t* xp;             // f16 pairs [T][in/16][8]
   float* rowsum;            // [T]
 };
 hipError_t launch_gemv_plan(const PlanArgs& a, hipStream_t s);
+// x~ (bf16 [T][in]) -> f16 pairs [T][in/16][8] (word r of tile column c = [lo: x[16c + r + 8],
+// hi: x[16c + r]]) and per-token sums of the f16 values: the activations of the trellis
+// kernels. With rotate, x is first rotated as hadamard128 would (FORMAT F8).
+hipError_t launch_activation_prep(const uint16_t* x, int64_t T, int in, uint32_t* xp,
+                                  float* rowsum, bool rotate, const int8_t* signs,
+                                  hipStream_t s);
 
 struct TrellisGemvArgs {
   const uint32_t* codes;
@@ -91,8 +99,9 @@ struct TrellisGemmArgs {
   const int64_t* code_off;
   const uint32_t* codes;
   const uint16_t* scales;
-  const uint16_t* x;
-  uint32_t x_bytes;  // size of x in bytes (< 2^31)
+  const uint32_t* xp;     // prepared activations: f16 pairs [T][in/16][8]
+  const float* rowsum;    // [T]: sum of each token's f16 activations
+  uint32_t x_bytes;       // size of xp in bytes (< 2^31)
   const float* gates;
   const int32_t* pairs;
   const int32_t* items;

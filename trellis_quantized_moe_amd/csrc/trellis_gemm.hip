@@ -1,7 +1,9 @@
 // Prefill grouped GEMM over trellis-coded experts (gfx950): the work-item core of
 // gemm_core.h with a T16 B producer. Each thread decodes one tile column (16 weights of
 // one output channel) per step; the step's 32 inputs are two tile columns of each of the
-// group's 8 strips (256 columns, one per thread). The decoded q are exact in bf16.
+// group's 8 strips (256 columns, one per thread). Each weight enters the matrix cores as
+// the f16 subnormal (q + 255) * 2^-24 (trellis_decode.h), against the prepared f16
+// activations; the epilogue scales by 2^24 and removes 255 * sum(x) per token.
 #include "gemm_core.h"
 #include "trellis_decode.h"
 
@@ -14,6 +16,7 @@ namespace {
 // read its words once; the neighbour word comes from the next lane (row rotation).
 template <int K>
 struct TrellisProducer {
+  static constexpr bool kF16 = true;
   struct Raw {
     uint32_t w[K == 2 ? 1 : (K == 4 ? 2 : 3)];
   };
@@ -72,7 +75,7 @@ struct TrellisProducer {
       col_mpairs_k4(r.w[0], r.w[1], row_next(r.w[0]), M);
     else
       col_mpairs_k3(r.w[0], r.w[1], r.w[2], sh3, M);
-    mpairs_to_bf16_natural<K>(M, nat);
+    byte_sums<K>(M, nat);  // [lo: v[r + 8], hi: v[r]], the layout of the prepared activations
   }
 };
 
@@ -92,8 +95,9 @@ __global__ __launch_bounds__(GEMM_THREADS, 2) void trellis_gemm_kernel(TrellisGe
   if (bad ? KW != 2 : K != KW) return;
   gemm_load_slots(sh, a.pairs, itd.y, itd.z);
   GemmItem it;
-  it.x = a.x;
+  it.x = a.xp;
   it.x_bytes = a.x_bytes;
+  it.rowsum = a.rowsum;
   it.gates = a.gates;
   it.scales = a.scales + (size_t)e * a.out;
   it.y = a.y;

@@ -11,7 +11,7 @@ import numpy as np
 import torch
 
 from . import _lib
-from ._lib import TQ_AUTO, TQ_COMBINE, TQ_GEMM, TQ_GEMV, check  # noqa: F401
+from ._lib import TQ_AUTO, TQ_COMBINE, TQ_GEMM, TQ_GEMV, TQ_ROTATE, check  # noqa: F401
 
 
 def _ptr(t):
@@ -38,25 +38,31 @@ class TrellisLayer:
     code_off: torch.Tensor   # int64 [E], byte offsets
     codes: torch.Tensor      # int32 [words] (uint32 bit patterns)
     scales: torch.Tensor     # int16 [E, out] (fp16 bit patterns)
+    signs: torch.Tensor = None  # int8 [in] rotation signs (TQ_ROTATE), or None
 
     @classmethod
     def from_host(cls, layer, device="cuda"):
+        signs = layer.get("signs")
         return cls(
             E=int(layer["E"]), out=int(layer["out"]), in_=int(layer["in"]),
             bits=torch.from_numpy(np.ascontiguousarray(layer["bits"], dtype=np.uint8)).to(device),
             code_off=torch.from_numpy(np.ascontiguousarray(layer["code_off"], dtype=np.int64)).to(device),
             codes=torch.from_numpy(np.ascontiguousarray(layer["codes"]).view(np.int32)).to(device),
             scales=torch.from_numpy(np.ascontiguousarray(layer["scales"]).view(np.int16)).to(device),
+            signs=None if signs is None else
+            torch.from_numpy(np.ascontiguousarray(signs, dtype=np.int8)).to(device),
         )
 
     def with_codes(self, codes):
         """The same layer reading its units from another copy of the code buffer."""
-        return TrellisLayer(self.E, self.out, self.in_, self.bits, self.code_off, codes, self.scales)
+        return TrellisLayer(self.E, self.out, self.in_, self.bits, self.code_off, codes,
+                            self.scales, self.signs)
 
     def c_struct(self):
         return _lib.TrellisLayerC(self.E, self.out, self.in_, 0, self.bits.data_ptr(),
                                   self.code_off.data_ptr(), self.codes.data_ptr(),
-                                  self.scales.data_ptr())
+                                  self.scales.data_ptr(),
+                                  None if self.signs is None else self.signs.data_ptr())
 
 
 @dataclass
