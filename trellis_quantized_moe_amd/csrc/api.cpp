@@ -2,6 +2,7 @@
 // Every check runs before the first HIP call of an entry point.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -126,6 +127,8 @@ WsLayout ws_layout(int64_t T, int topk, int E, int out, int in, uint32_t flags, 
   const int64_t N = T * topk;
   L.groups = (out + 127) / 128;
   L.gemm = use_gemm(T, topk, E, flags);
+  // a decode batch gives every active expert group at least one wave of its own
+  if (!mxfp4 && (flags & 3u) == TQ_AUTO && (int64_t)E * L.groups > tq::GEMV_MAX_G) L.gemm = true;
   size_t off = 256;  // status word
   if (!L.gemm && !mxfp4) {
     // planned decode batch: plan records, prepared activations, per-piece partial sums
@@ -135,10 +138,8 @@ WsLayout ws_layout(int64_t T, int topk, int E, int out, int in, uint32_t flags, 
     L.rec = off;
     off += round_up((size_t)E * sizeof(tq::PlanRec), 256);
     L.desc = off;
-    off += round_up((size_t)(tq::GEMV_MAX_G + 1) * 8, 256);
+    off += round_up((size_t)tq::GEMV_MAX_G * 16, 256);
     L.list = off;
-    off += round_up((size_t)N * 4, 256);
-    L.list_tok = off;
     off += round_up((size_t)N * 4, 256);
     L.slot_info = off;
     off += round_up((size_t)N * 16, 256);
@@ -362,8 +363,9 @@ int common_checks(int E, int out, int in, const void* x, int64_t T, const int32_
   *layout = tq::ws_layout(T, topk, E, out, in, flags, mxfp4);
   if ((layout->gemm || !mxfp4) && E > 4096)
     return fail(TQ_EINVAL, "this path supports E <= 4096 (E = %d)", E);
-  if (!layout->gemm && !mxfp4 && (int64_t)E * layout->groups * (in / 256) * 4 >= ((int64_t)1 << 31))
-    return fail(TQ_EINVAL, "E * out * in is too large for the decode-batch plan");
+  if (!layout->gemm && !mxfp4 && (int64_t)E * layout->groups > tq::GEMV_MAX_G)
+    return fail(TQ_EINVAL, "decode batches take at most %d expert groups (E * out / 128)",
+                tq::GEMV_MAX_G);
   if ((layout->gemm || !mxfp4) && T * (int64_t)in * 2 >= ((int64_t)1 << 31))
     return fail(TQ_EINVAL, "T * in * 2 bytes of activations must stay below 2^31");
   if (layout->gemm && (int64_t)out * in / 2 + (int64_t)out * in / 32 >= ((int64_t)1 << 31))
@@ -448,7 +450,8 @@ int trellis_expert_gemm(const tq_trellis_layer* L, const void* x, int64_t T,
   if (!W.gemm) {
     const int G = tq::trellis_gemv_grid();
     if (G <= 0) return fail(TQ_EHIP, "could not size the GEMV grid");
-    const int Q = L->in / 256;
+    // launched waves: the resident ones, or one per expert group when that is more
+    const int Gl = (int)std::max<int64_t>(G, (int64_t)L->E * W.groups);
     tq::PlanArgs p{};
     p.ids = topk_ids;
     p.N = (int)N;
@@ -457,13 +460,14 @@ int trellis_expert_gemm(const tq_trellis_layer* L, const void* x, int64_t T,
     p.bits = L->bits;
     p.code_off = L->code_off;
     p.unit_bytes = 0;
-    p.U = W.groups * Q;
+    p.groups = W.groups;
+    p.S = L->in / 64;
     p.G = G;
+    p.Gl = Gl;
     p.info = at<int32_t>(ws, W.info);
     p.rec = at<tq::PlanRec>(ws, W.rec);
-    p.desc = at<int2>(ws, W.desc);
+    p.desc = at<int4>(ws, W.desc);
     p.list = at<int32_t>(ws, W.list);
-    p.list_tok = at<int32_t>(ws, W.list_tok);
     p.slot_info = at<int4>(ws, W.slot_info);
     p.rank = at<int32_t>(ws, W.prank);
     p.status = at<uint32_t>(ws, W.status);
@@ -479,20 +483,16 @@ int trellis_expert_gemm(const tq_trellis_layer* L, const void* x, int64_t T,
     tq::TrellisGemvArgs a{};
     a.codes = L->codes;
     a.xp = p.xp;
-    a.info = p.info;
     a.rec = p.rec;
     a.desc = p.desc;
     a.list = p.list;
-    a.list_tok = p.list_tok;
     a.partial = at<float>(ws, W.partial);
     a.x_bytes = (uint32_t)(T * L->in * 2);
     a.N = (int)N;
-    a.E = L->E;
     a.out = L->out;
     a.in = L->in;
     a.topk = topk;
-    a.groups = W.groups;
-    a.G = G;
+    a.G = Gl;
     err = time_begin(s);
     if (err != hipSuccess) return hip_fail(err, "hipEventRecord");
     err = tq::launch_trellis_gemv(a, s);
@@ -500,7 +500,6 @@ int trellis_expert_gemm(const tq_trellis_layer* L, const void* x, int64_t T,
     if (err != hipSuccess) return hip_fail(err, "trellis GEMV launch");
     tq::PieceReduceArgs r{};
     r.slot_info = p.slot_info;
-    r.info = p.info;
     r.partial = a.partial;
     r.scales = L->scales;
     r.gates = topk_w;
@@ -511,7 +510,6 @@ int trellis_expert_gemm(const tq_trellis_layer* L, const void* x, int64_t T,
     r.N = (int)N;
     r.out = L->out;
     r.topk = topk;
-    r.Q = Q;
     r.combine = (flags & TQ_COMBINE) ? 1 : 0;
     err = tq::launch_piece_reduce(r, s);
     if (err != hipSuccess) return hip_fail(err, "GEMV piece reduction launch");

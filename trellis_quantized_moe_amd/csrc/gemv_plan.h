@@ -1,23 +1,25 @@
-// Decode-batch plan: which workgroup streams which part of which routed expert.
+// Decode-batch plan: which wave streams which part of which routed expert.
 //
 // The decode-batch path runs three launches:
 //   1. plan + prep (gemv_plan.hip): one block buckets the routes by expert (slot lists,
-//      the active experts in ascending id order, a cost prefix over them, per-slot records,
-//      and the start of every workgroup's range); the other blocks prepare activations;
-//   2. the grouped GEMV: exactly as many workgroups as the GPU holds at once (G), each
-//      streaming a contiguous, equal share of the active experts' cost;
-//   3. the piece reduction (gemv_reduce.hip): per slot, the partial sums of the pieces an
+//      the active experts in ascending id order, per-slot records) and splits the work
+//      among the GEMV's waves; the other blocks prepare activations;
+//   2. the grouped GEMV: single-wave workgroups, each streaming one piece;
+//   3. the piece reduction (gemv_reduce.hip): per slot, the partial sums of the pieces its
 //      expert was split into, added in piece order, then the epilogue (and the combine).
 //
-// Work is counted in units: one unit is 128 output channels (a group of 8 strips) by 256
-// inputs. An expert has U = groups * Q units (Q = in / 256), group-major. A unit of a
-// trellis expert costs K (its bytes are proportional to K); an MXFP4 unit costs 1. With
-// C = the total cost of the active experts, the first G' = min(G, C / largest unit cost)
-// workgroups get work (so each owns at least one unit), workgroup w < G' owns the cost range
-// [c0(w), c0(w + 1)), c0(w) = floor(w * C / G'), and every unit whose first cost lies in it.
-// A workgroup's share of one expert's group is a "piece"; piece p of (expert, group) is the
-// share of workgroup owner(group start) + p. Pieces are summed in that order, so results
-// are independent of timing.
+// Work is counted in steps: one step is 64 inputs of one group of 128 output channels, so
+// a group has S = in / 64 steps. A step of a trellis expert of width K costs K (its bytes
+// are proportional to K); an MXFP4 step costs 1. Every active expert's group is split into
+// W(k) pieces of consecutive steps (W depends only on the expert's cost k), piece j taking
+// steps floor(j S / W) .. floor((j + 1) S / W) - 1, and every piece is one wave's whole
+// work: no wave crosses from one expert or group into another, so a wave's load stream
+// never restarts, and the pieces of a group differ by at most one step. W(k) =
+// ceil(S / floor(T / k)) for the smallest per-wave cost bound T >= 4 * kmax (kmax the
+// largest active cost) whose total number of waves fits the GPU's resident waves (or the
+// number of active groups, when that is larger); T >= 4 kmax keeps W(k) <= S / 4 = in / 256.
+// Pieces are summed in piece order, so results are independent of timing, and the split
+// depends only on which experts are active, never on the order of the tokens.
 #pragma once
 
 #include "tq_device.h"
@@ -29,29 +31,22 @@ struct alignas(16) PlanRec {
   int32_t e;      // expert id
   int32_t start;  // first entry of its slots in the slot list
   int32_t cnt;    // number of slots routed to it
-  int32_t k;      // cost of one unit
+  int32_t k;      // cost of one step
   int64_t off;    // byte offset of its unit
-  int32_t p0;     // cost prefix: the expert's first cost
-  int32_t pad;
+  int32_t wave0;  // first wave of its pieces
+  int32_t np;     // pieces per group, W(k)
 };
 
-// Per-slot record for the reduction: {expert id, p0, k, 0}, or code in .x:
+// desc[w], the piece of wave w (int4): {active expert index, or -1 for no work; group;
+// piece index; its steps s0 .. s1 - 1 packed as s0 | s1 << 16}.
+
+// Per-slot record for the reduction: {expert id, pieces per group, k, 0}, or code in .x:
 constexpr int SLOT_EMPTY = -1;     // id -1: output 0
 constexpr int SLOT_BAD_ID = -2;    // id outside [-1, E): NaN
 constexpr int SLOT_BAD_UNIT = -3;  // expert with a bad width byte or offset: NaN
 
 constexpr int PLAN_MAX_E = 4096;
 constexpr int PLAN_THREADS = 1024;
-constexpr int GEMV_MAX_G = 4096;   // bound on the GEMV grid (desc buffer size)
-
-// First cost owned by workgroup w.
-__device__ __forceinline__ int64_t plan_c0(int w, int64_t C, int G) {
-  return (int64_t)w * C / G;
-}
-// The workgroup whose range holds cost c (0 <= c < C): the largest w with c0(w) <= c.
-__device__ __forceinline__ int plan_owner(int64_t c, int64_t C, int G) {
-  const int64_t w = ((c + 1) * G - 1) / C;
-  return (int)(w < G - 1 ? w : G - 1);
-}
+constexpr int GEMV_MAX_G = 16384;  // bound on the GEMV grid (desc buffer size)
 
 }  // namespace tq

@@ -4,9 +4,11 @@
 // also gives each slot its position in its expert's list. Positions within one expert
 // therefore follow arrival order, but every output is computed by arithmetic that does not
 // depend on its row position, so the results are the same bits whatever the order. A
-// block-wide scan then gives list starts, the active experts in ascending id order and the
-// cost prefix over them. Last come the slot lists, the per-slot records and the first unit
-// of every GEMV workgroup's range.
+// block-wide scan then gives list starts, the active experts in ascending id order and,
+// per cost class, how many active experts precede each one. The split (pieces per group
+// for each cost class) is the smallest feasible per-wave cost bound, found by testing all
+// candidates at once. Last come the slot lists, the per-slot records and every wave's
+// piece (each active expert's thread writes its own waves').
 //
 // Blocks 1..T convert token t = block - 1 of x~ (bf16) to the f16 operand layout of the
 // trellis GEMV (word r of tile column c = [lo: x[16c + r + 8], hi: x[16c + r]], rounded to
@@ -22,57 +24,67 @@ constexpr int PLAN_R = 4;                            // slots per thread kept in
 constexpr int PLAN_PER = PLAN_MAX_E / PLAN_THREADS;  // experts per thread in the scan
 constexpr int PLAN_WAVES = PLAN_THREADS / 64;
 
-// Exclusive block scan of three ints over PLAN_THREADS threads, in place; tot = totals.
-__device__ void block_scan3(int& x0, int& x1, int& x2, int tot[3]) {
-  __shared__ int part[3][PLAN_WAVES];
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  int i0 = x0, i1 = x1, i2 = x2;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const int t0 = __shfl_up(i0, d, 64), t1 = __shfl_up(i1, d, 64), t2 = __shfl_up(i2, d, 64);
-    if (lane >= d) {
-      i0 += t0;
-      i1 += t1;
-      i2 += t2;
-    }
-  }
-  if (lane == 63) {
-    part[0][w] = i0;
-    part[1][w] = i1;
-    part[2][w] = i2;
-  }
-  lds_barrier();
-  int b0 = 0, b1 = 0, b2 = 0;
-  tot[0] = tot[1] = tot[2] = 0;
-#pragma unroll
-  for (int v = 0; v < PLAN_WAVES; ++v) {
-    const int p0 = part[0][v], p1 = part[1][v], p2 = part[2][v];
-    if (v < w) {
-      b0 += p0;
-      b1 += p1;
-      b2 += p2;
-    }
-    tot[0] += p0;
-    tot[1] += p1;
-    tot[2] += p2;
-  }
-  x0 = b0 + i0 - x0;
-  x1 = b1 + i1 - x1;
-  x2 = b2 + i2 - x2;
+// Inclusive scan of v over the 64 lanes of a wave: row shifts 1, 2, 4, 8 and the row
+// broadcasts 15 and 31 (DPP, no LDS round trip).
+__device__ __forceinline__ int wave_scan(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, true);  // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, true);  // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, true);  // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, true);  // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false);  // row_bcast:15
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false);  // row_bcast:31
+  return v;
 }
 
-// The plan is one block of PLAN_THREADS threads; each phase gives a thread about one slot,
-// one expert and one workgroup, so that no thread runs a long chain of dependent steps.
+// Exclusive block scan of NV ints over PLAN_THREADS threads, in place; tot = totals.
+template <int NV>
+__device__ void block_scan(int (&x)[NV], int (&tot)[NV]) {
+  __shared__ int part[NV][PLAN_WAVES];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  int in[NV];
+#pragma unroll
+  for (int v = 0; v < NV; ++v) in[v] = wave_scan(x[v]);
+  if (lane == 63) {
+#pragma unroll
+    for (int v = 0; v < NV; ++v) part[v][w] = in[v];
+  }
+  lds_barrier();
+#pragma unroll
+  for (int v = 0; v < NV; ++v) {
+    int b = 0, t = 0;
+#pragma unroll
+    for (int u = 0; u < PLAN_WAVES; ++u) {
+      const int p = part[v][u];
+      if (u < w) b += p;
+      t += p;
+    }
+    tot[v] = t;
+    x[v] = b + in[v] - x[v];
+  }
+}
+
+// Pieces per group for a step cost k under the per-wave cost bound T (T >= k): the steps
+// S split into pieces of at most floor(T / k) steps. The quotient is taken in fp32, exact
+// here (S <= 2^15, and a non-integer S / per is at least 1 / S away from an integer).
+__device__ __forceinline__ int pieces_for(int S, int T, int k) {
+  const int per = T / k;
+  return (int)__builtin_ceilf((float)S / (float)per);
+}
+
+// The plan is one block of PLAN_THREADS threads; each phase gives a thread about one slot
+// or one expert (ceil(E / PLAN_THREADS) of them), so that no thread runs a long chain of
+// dependent steps.
 template <bool TRELLIS>
 __device__ void plan_block(const PlanArgs& a) {
   __shared__ int s_start[PLAN_MAX_E];   // slot counts, then list starts
   __shared__ int s_aidx[PLAN_MAX_E];    // active index, or SLOT_EMPTY / SLOT_BAD_UNIT
-  __shared__ int s_P[PLAN_MAX_E + 1];   // cost prefix by active index
-  __shared__ uint8_t s_ka[PLAN_MAX_E];  // unit cost by active index
+  __shared__ uint8_t s_ka[PLAN_MAX_E];  // step cost by active index
+  __shared__ int s_T;
   __shared__ uint32_t s_status;
   const int tid = threadIdx.x;
-  const int N = a.N, E = a.E, U = a.U;
+  const int N = a.N, E = a.E, S = a.S, groups = a.groups;
   const bool in_regs = N <= PLAN_THREADS * PLAN_R;
+  const int per = (E + PLAN_THREADS - 1) / PLAN_THREADS;  // experts per thread, <= PLAN_PER
 
   // all route and descriptor loads are issued before any is used (indices clamped; slots
   // past N and experts past E are skipped where used)
@@ -81,7 +93,7 @@ __device__ void plan_block(const PlanArgs& a) {
 #pragma unroll
     for (int j = 0; j < PLAN_R; ++j) id[j] = a.ids[min(tid + PLAN_THREADS * j, N - 1)];
   }
-  const int e0 = tid * PLAN_PER;  // this thread's experts e0 .. e0 + PLAN_PER - 1
+  const int e0 = tid * per;  // this thread's experts e0 .. e0 + per - 1
   int kk[PLAN_PER];
   int64_t off[PLAN_PER];
   if constexpr (TRELLIS) {
@@ -101,10 +113,14 @@ __device__ void plan_block(const PlanArgs& a) {
       off[j] = (int64_t)(e0 + j) * a.unit_bytes;
     }
   }
+  auto mine = [&](int j) { return j < per && e0 + j < E; };
 #pragma unroll
   for (int j = 0; j < PLAN_PER; ++j)
-    if (e0 + j < E) s_start[e0 + j] = 0;
-  if (tid == 0) s_status = 0;
+    if (mine(j)) s_start[e0 + j] = 0;
+  if (tid == 0) {
+    s_status = 0;
+    s_T = 0x7FFFFFFF;
+  }
   lds_barrier();
 
   // counts; a slot's position in its expert's list is the count before its own increment
@@ -126,27 +142,60 @@ __device__ void plan_block(const PlanArgs& a) {
   }
   lds_barrier();
 
-  // scan over experts: list starts, active indices, cost prefix
+  // scan over experts: list starts and, per step cost 1..4, the active experts before each
+  // (counts of cost 1 and 2 share one int, 3 and 4 another: 16 bits each, as E <= 4096)
   int cnt[PLAN_PER];
-  int sc = 0, sa = 0, scost = 0;
+  int sv[3] = {0, 0, 0};  // slots; active of cost 1 | 2 << 16; active of cost 3 | 4 << 16
 #pragma unroll
   for (int j = 0; j < PLAN_PER; ++j) {
-    cnt[j] = e0 + j < E ? s_start[e0 + j] : 0;
-    const bool act = cnt[j] > 0 && kk[j] > 0;
-    sc += cnt[j];
-    sa += act ? 1 : 0;
-    scost += act ? kk[j] * U : 0;
+    cnt[j] = mine(j) ? s_start[e0 + j] : 0;
+    sv[0] += cnt[j];
+    if (cnt[j] > 0 && kk[j] > 0) sv[kk[j] >= 3 ? 2 : 1] += (kk[j] & 1) ? 1 : 0x10000;
   }
-  int tot[3];
-  block_scan3(sc, sa, scost, tot);
+  int tot3[3];
+  block_scan<3>(sv, tot3);
+  const int tot[5] = {0, tot3[1] & 0xFFFF, tot3[1] >> 16, tot3[2] & 0xFFFF, tot3[2] >> 16};
+  const int n_act = tot[1] + tot[2] + tot[3] + tot[4];
+  const int kmax = tot[4] ? 4 : tot[3] ? 3 : tot[2] ? 2 : 1;
+
+  // the split: the smallest cost bound T in [4 kmax, S kmax] whose waves fit the target;
+  // T = S kmax (one piece per group) always does
+  const int64_t target = max((int64_t)a.G, (int64_t)groups * n_act);
+  for (int T0 = 4 * kmax; T0 <= S * kmax; T0 += PLAN_THREADS) {  // uniform
+    const int T = T0 + tid;
+    int best = 0x7FFFFFFF;
+    if (T <= S * kmax) {
+      int64_t waves = 0;
+#pragma unroll
+      for (int k = 1; k <= 4; ++k)
+        if (tot[k]) waves += (int64_t)tot[k] * pieces_for(S, T, k);
+      if (waves * groups <= target) best = T;
+    }
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) best = min(best, __shfl_xor(best, d, 64));
+    if ((tid & 63) == 0 && best != 0x7FFFFFFF) atomicMin(&s_T, best);
+  }
+  lds_barrier();
+  const int Tb = s_T < S * kmax ? s_T : S * kmax;
+  int Wk[5];
+  Wk[0] = 0;
+#pragma unroll
+  for (int k = 1; k <= 4; ++k) Wk[k] = k <= Tb ? pieces_for(S, Tb, k) : 1;
+  const int waves = groups * (tot[1] * Wk[1] + tot[2] * Wk[2] + tot[3] * Wk[3] + tot[4] * Wk[4]);
+
+  // active experts: records, and their waves' pieces, group-major, piece p of a group
+  // taking steps floor(p S / W) .. floor((p + 1) S / W) - 1 (advanced without division)
+  const int pre[5] = {0, sv[1] & 0xFFFF, sv[1] >> 16, sv[2] & 0xFFFF, sv[2] >> 16};
+  int sc = sv[0], sa = pre[1] + pre[2] + pre[3] + pre[4];
+  int wb = groups * (pre[1] * Wk[1] + pre[2] * Wk[2] + pre[3] * Wk[3] + pre[4] * Wk[4]);
 #pragma unroll
   for (int j = 0; j < PLAN_PER; ++j) {
-    const int e = e0 + j;
-    if (e < E) {
+    if (mine(j)) {
+      const int e = e0 + j;
       s_start[e] = sc;
       if (cnt[j] > 0 && kk[j] > 0) {
+        const int W = Wk[kk[j]];
         s_aidx[e] = sa;
-        s_P[sa] = scost;
         s_ka[sa] = (uint8_t)kk[j];
         PlanRec r;
         r.e = e;
@@ -154,30 +203,32 @@ __device__ void plan_block(const PlanArgs& a) {
         r.cnt = cnt[j];
         r.k = kk[j];
         r.off = off[j];
-        r.p0 = scost;
-        r.pad = 0;
+        r.wave0 = wb;
+        r.np = W;
         a.rec[sa] = r;
+        const int base = S / W, rem = S - base * W;
+        for (int grp = 0, q = wb; grp < groups; ++grp) {
+          int s0 = 0, acc = 0;
+          for (int p = 0; p < W; ++p, ++q) {
+            acc += rem;
+            const int s1 = s0 + base + (acc >= W ? 1 : 0);
+            acc -= acc >= W ? W : 0;
+            a.desc[q] = make_int4(sa, grp, p, s0 | (s1 << 16));
+            s0 = s1;
+          }
+        }
         sa += 1;
-        scost += kk[j] * U;
+        wb += groups * W;
       } else {
         s_aidx[e] = cnt[j] > 0 ? SLOT_BAD_UNIT : SLOT_EMPTY;
       }
       sc += cnt[j];
     }
   }
-  const int n_act = tot[1], C = tot[2];
-  // Workgroups that get work: at most C / (largest unit cost), so that every range holds
-  // at least one unit start and the pieces of an expert's group are consecutive workgroups
-  // (piece index < units per group).
-  const int kmax = TRELLIS ? 4 : 1;
-  int Geff = C / kmax;
-  Geff = Geff < a.G ? Geff : a.G;
-  Geff = Geff > 1 ? Geff : 1;
   if (tid == 0) {
-    s_P[n_act] = C;
     a.info[0] = n_act;
-    a.info[1] = C;
-    a.info[2] = Geff;
+    a.info[1] = waves;
+    a.info[2] = Tb;
   }
   lds_barrier();
 
@@ -195,8 +246,8 @@ __device__ void plan_block(const PlanArgs& a) {
         bad |= STATUS_BAD_UNIT;
       } else {
         a.list[s_start[v] + r] = i;
-        a.list_tok[s_start[v] + r] = i / a.topk;
-        inf = make_int4(v, s_P[ai], s_ka[ai], 0);
+        const int k = s_ka[ai];
+        inf = make_int4(v, Wk[k], k, 0);
       }
     }
     a.slot_info[i] = inf;
@@ -214,31 +265,8 @@ __device__ void plan_block(const PlanArgs& a) {
     }
   }
 
-  // first unit of every workgroup's range; workgroups Geff .. G get the end (empty ranges)
-  for (int w = tid; w <= a.G; w += PLAN_THREADS) {
-    int lo = n_act, u = 0;
-    if (w < Geff) {
-      const int c0 = (int)((int64_t)w * C / Geff);
-      lo = 0;
-      int hi = n_act;  // smallest active index with s_P[ai + 1] > c0, or n_act
-      while (lo < hi) {
-        const int mid = (lo + hi) >> 1;
-        if (s_P[mid + 1] > c0)
-          hi = mid;
-        else
-          lo = mid + 1;
-      }
-      if (lo < n_act) {
-        const int k = s_ka[lo];
-        u = (c0 - s_P[lo] + k - 1) / k;
-        if (u >= U) {
-          ++lo;
-          u = 0;
-        }
-      }
-    }
-    a.desc[w] = make_int2(lo, u);
-  }
+  // launched waves past the split get no piece
+  for (int w = waves + tid; w < a.Gl; w += PLAN_THREADS) a.desc[w] = make_int4(-1, 0, 0, 0);
 
   if (bad) atomicOr(&s_status, bad);
   lds_barrier();

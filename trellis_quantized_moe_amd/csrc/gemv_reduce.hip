@@ -72,8 +72,7 @@ __device__ __forceinline__ void add4(float4& s, const float4& v) {
   s.w += v.w;
 }
 
-__device__ __forceinline__ float4 piece_slot(const PieceReduceArgs& a, int slot, int o, int64_t C,
-                                             int G) {
+__device__ __forceinline__ float4 piece_slot(const PieceReduceArgs& a, int slot, int o) {
   const int4 inf = a.slot_info[slot];
   const float corr = a.rowsum ? a.offset * a.rowsum[slot / a.topk] : 0.0f;
   const float gate = a.gates ? a.gates[slot] : 1.0f;
@@ -82,21 +81,23 @@ __device__ __forceinline__ float4 piece_slot(const PieceReduceArgs& a, int slot,
     const float nan = __builtin_nanf("");
     return make_float4(nan, nan, nan, nan);
   }
-  const int e = inf.x, grp = o / 128;
-  const int64_t cs = (int64_t)inf.y + (int64_t)grp * a.Q * inf.z;
-  const int np = plan_owner(cs + (int64_t)(a.Q - 1) * inf.z, C, G) - plan_owner(cs, C, G) + 1;
+  const int e = inf.x, np = inf.y;
   const size_t stride = (size_t)a.N * a.out;
   const float* p = a.partial + (size_t)slot * a.out + o;
   const uint2 sc = *reinterpret_cast<const uint2*>(a.scales + (size_t)e * a.out + o);
-  // the first four pieces are requested together (clamped indices, unused ones dropped)
-  float4 v[4];
+  // pieces are requested eight at a time (clamped indices, unused ones dropped) and added
+  // in piece order
+  float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int q0 = 0; q0 < np; q0 += 8) {
+    float4 v[8];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) v[q] = *reinterpret_cast<const float4*>(p + (size_t)min(q, np - 1) * stride);
-  float4 s = v[0];
+    for (int q = 0; q < 8; ++q)
+      v[q] = *reinterpret_cast<const float4*>(p + (size_t)min(q0 + q, np - 1) * stride);
+    if (q0 == 0) s = v[0];
 #pragma unroll
-  for (int q = 1; q < 4; ++q)
-    if (q < np) add4(s, v[q]);
-  for (int q = 4; q < np; ++q) add4(s, *reinterpret_cast<const float4*>(p + (size_t)q * stride));
+    for (int q = 0; q < 8; ++q)
+      if ((q0 > 0 || q > 0) && q0 + q < np) add4(s, v[q]);
+  }
   const uint32_t sw[2] = {sc.x, sc.y};
   float r[4] = {s.x, s.y, s.z, s.w};
 #pragma unroll
@@ -109,14 +110,12 @@ __device__ __forceinline__ float4 piece_slot(const PieceReduceArgs& a, int slot,
 }
 
 __global__ __launch_bounds__(256) void piece_reduce_kernel(PieceReduceArgs a) {
-  const int64_t C = a.info[1];
-  const int G = a.info[2];
   const int per_row = a.out / 4;
   if (!a.combine) {
     const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (idx >= (int64_t)a.N * per_row) return;
     const int r = (int)(idx / per_row), o = (int)(idx % per_row) * 4;
-    *reinterpret_cast<float4*>(a.y + (size_t)r * a.out + o) = piece_slot(a, r, o, C, G);
+    *reinterpret_cast<float4*>(a.y + (size_t)r * a.out + o) = piece_slot(a, r, o);
     return;
   }
   // block = (token t, outputs o0 .. o0 + 127); LDS holds the topk slot values
@@ -126,7 +125,7 @@ __global__ __launch_bounds__(256) void piece_reduce_kernel(PieceReduceArgs a) {
   const int w4 = min(128, a.out - o0) / 4;  // float4 columns in this chunk
   for (int v = threadIdx.x; v < a.topk * 32; v += 256) {
     const int k = v / 32, c = v % 32;
-    if (c < w4) vals[v] = piece_slot(a, t * a.topk + k, o0 + 4 * c, C, G);
+    if (c < w4) vals[v] = piece_slot(a, t * a.topk + k, o0 + 4 * c);
   }
   lds_barrier();
   if ((int)threadIdx.x < w4) {

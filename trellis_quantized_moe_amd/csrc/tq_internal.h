@@ -17,7 +17,7 @@ struct WsLayout {
   size_t route_bytes = 0;
   size_t slots = 0, slots_bytes = 0;
   size_t xprep = 0, rowsum = 0;
-  size_t info = 0, rec = 0, desc = 0, list = 0, list_tok = 0, slot_info = 0, prank = 0;
+  size_t info = 0, rec = 0, desc = 0, list = 0, slot_info = 0, prank = 0;
   size_t total = 0;
   int gemv_slices = 1, gemv_steps = 1, groups = 1, route_blocks = 1, max_items = 0;
   bool gemm = false;
@@ -36,15 +36,16 @@ struct PlanRec;
 struct PlanArgs {
   const int32_t* ids;
   int N, E, topk;
-  const uint8_t* bits;      // trellis widths, or null: every unit costs 1 (MXFP4)
+  const uint8_t* bits;      // trellis widths, or null: every step costs 1 (MXFP4)
   const int64_t* code_off;  // trellis unit offsets (with bits)
   int64_t unit_bytes;       // MXFP4: expert e's unit is at e * unit_bytes
-  int U, G;                 // units per expert, GEMV workgroups
-  int32_t* info;            // [0] active experts, [1] total cost, [2] workgroups with work
+  int groups, S;            // output groups per expert, steps per group (in / 64)
+  int G;                    // resident GEMV waves (the split's target)
+  int Gl;                   // launched GEMV waves (desc entries written)
+  int32_t* info;            // [0] active experts, [1] waves with work, [2] cost bound T
   PlanRec* rec;             // [E]
-  int2* desc;               // [G + 1]
+  int4* desc;               // [Gl]
   int32_t* list;            // [N]
-  int32_t* list_tok;        // [N]: token (slot / topk) of each list entry
   int4* slot_info;          // [N]
   int32_t* rank;            // [N] (used when N exceeds what the plan keeps in registers)
   uint32_t* status;
@@ -67,29 +68,26 @@ hipError_t launch_activation_prep(const uint16_t* x, int64_t T, int in, uint32_t
 struct TrellisGemvArgs {
   const uint32_t* codes;
   const uint32_t* xp;
-  const int32_t* info;
   const PlanRec* rec;
-  const int2* desc;
+  const int4* desc;     // [G]
   const int32_t* list;
-  const int32_t* list_tok;  // token of each list entry
-  float* partial;  // [Q][N][out]
-  uint32_t x_bytes;  // size of xp in bytes (< 2^31)
-  int N, E, out, in, topk, groups, G;
+  float* partial;       // [in / 256][N][out]: the pieces of each slot
+  uint32_t x_bytes;     // size of xp in bytes (< 2^31)
+  int N, out, in, topk, G;
 };
-// Workgroups of the trellis GEMV grid (all resident at once); 0 on a HIP error.
+// Waves of the trellis GEMV that the GPU holds at once; 0 on a HIP error.
 int trellis_gemv_grid();
 hipError_t launch_trellis_gemv(const TrellisGemvArgs& a, hipStream_t s);
 
 struct PieceReduceArgs {
-  const int4* slot_info;
-  const int32_t* info;
+  const int4* slot_info;  // {expert, pieces, k, 0} or a SLOT_ code
   const float* partial;
   const uint16_t* scales;
   const float* gates;   // or null
   const float* rowsum;  // or null
   float* y;
   float acc_scale, offset;
-  int N, out, topk, Q, combine;
+  int N, out, topk, combine;
 };
 constexpr int PIECE_MAX_TOPK = 64;  // largest topk (checked by the C ABI)
 hipError_t launch_piece_reduce(const PieceReduceArgs& a, hipStream_t s);

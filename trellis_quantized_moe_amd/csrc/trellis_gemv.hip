@@ -1,23 +1,22 @@
 // Decode-batch grouped GEMV over trellis-coded experts (gfx950).
 //
-// The grid is exactly as many workgroups as the GPU holds at once; workgroup w streams the
-// units of its range of the plan (see gemv_plan.h), expert by expert. For each piece (one
-// expert's units of one output group inside the range) the four waves of the workgroup
-// split every unit: wave v takes tile columns 4v .. 4v + 3 of each of the unit's 16, so a
-// wave's step is 4 tile columns of 8 strips, and the four waves read neighbouring tiles.
-// Per step and strip, each lane decodes one tile column (16 weights of one output channel)
-// and the wave feeds two 16 x 16 x 32 matrix-core operations, with the activations of up
-// to 16 routed token rows as the other operand (rows past the expert's count are zero).
+// One wave is one worker of the plan (see gemv_plan.h): the grid is single-wave workgroups,
+// and wave w streams the one piece the plan gave it, steps s0 .. s1 - 1 of one group of one
+// expert, on its own: no LDS and no barrier, so a wave that waits for memory never holds
+// up another, and its load stream never restarts. A step is 4 tile columns (64 inputs) of
+// the group's 8 strips (128 output channels). Per step and strip, each lane decodes one
+// tile column (16 weights of one output channel) and the wave feeds two 16 x 16 x 32
+// matrix-core operations, with the activations of up to 16 routed token rows as the other
+// operand (rows past the expert's count are zero).
 //
 // Code words are requested D steps ahead (D = 4 at K = 2, 2 at K = 3 and 4), held in D
 // register sets used in turn, so that several steps of loads are in flight per wave, and
-// so are the activations (prepared once per call, f16). The load of a
-// strip's next words is issued right after its current words are decoded.
+// so are the activations (prepared once per call, f16). The load of a strip's next words
+// is issued right after its current words are decoded.
 //
-// At the end of a piece the four waves' accumulators are added through LDS in wave order
-// and the piece's sums are stored for the reduction launch, which adds the pieces in order
-// and applies the epilogue. Each weight reaches the matrix cores as the f16 subnormal
-// (q + 255) * 2^-24 (see trellis_decode.h).
+// At the end the wave stores its accumulators as the piece's partial sums; the reduction
+// launch adds the pieces in order and applies the epilogue. Each weight reaches the matrix
+// cores as the f16 subnormal (q + 255) * 2^-24 (see trellis_decode.h).
 #include "gemv_plan.h"
 #include "tq_internal.h"
 #include "trellis_decode.h"
@@ -26,14 +25,8 @@ namespace tq {
 
 namespace {
 
-constexpr int GEMV_THREADS = 256;
+constexpr int GEMV_THREADS = 64;         // one wave per workgroup
 constexpr int GEMV_WAVES_PER_SIMD = 3;  // register budget: 168 per lane
-constexpr int GEMV_GRID_MULT = 1;       // workgroups per resident slot
-
-struct Shared {
-  float red[4 * 8 * 4 * 64];  // [wave][strip][i][lane]
-  int slots[16];              // the chunk's slots
-};
 
 // ---- code words --------------------------------------------------------------------------
 // Words of one tile column a lane holds (see trellis_decode.h): K = 2 one word, K = 4 two,
@@ -135,8 +128,8 @@ __device__ __forceinline__ PlanRec load_rec(const PlanRec* rec, int i) {
   r.cnt = p->cnt;
   r.k = p->k;
   r.off = p->off;
-  r.p0 = p->p0;
-  r.pad = 0;
+  r.wave0 = 0;
+  r.np = 0;
   return r;
 }
 
@@ -165,44 +158,45 @@ __device__ __forceinline__ void step_body(ColWords<K> (&cw)[8], u32x4& xa, u32x4
   if (RELOAD) load_x(rx, xvo, xso, xa, xb);
 }
 
-// Units qa .. qb - 1 of output group grp for this wave: tile columns 16 q + 4 v + g (g =
-// lane / 16) of strips grp * 8 + s8. tok = this lane's token row, or -1 (zero row: its
-// activation offset lies past the end of the buffer, where buffer loads return 0).
+// Steps s0 .. s1 - 1 of output group grp: step st covers tile columns 4 st .. 4 st + 3 (lane
+// group g = lane / 16 takes column 4 st + g) of each of the group's strips. tok = this
+// lane's token row, or -1 (zero row: its activation offset lies past the end of the
+// buffer, where buffer loads return 0).
 template <int K>
 __device__ __forceinline__ void stream(const TrellisGemvArgs& a, const uint32_t* __restrict__ unit,
-                                       int tok, int grp, int ns, int qa, int qb, int wv,
-                                       f32x4 acc[8]) {
+                                       int tok, int grp, int ns, int s0, int s1, f32x4 acc[8]) {
   constexpr int TW = 8 * K;  // words per tile
   constexpr int D = K == 2 ? 4 : 2;
   const int lane = threadIdx.x & 63, g = lane >> 4, n = lane & 15;
   const int n_ti = a.in / 16;
-  const int steps = qb - qa, last = steps - 1;
+  const int steps = s1 - s0, last = steps - 1;
   const LaneOffsets<K> lo(g, n);
   const Rsrc rc = make_rsrc(unit, (uint32_t)((size_t)a.out * a.in * K / 8));
   const uint32_t cvo[3] = {4u * lo.o[0], 4u * lo.o[1], 4u * lo.o[2]};
-  const uint32_t c0 = 4u * (uint32_t)(((size_t)grp * 8 * n_ti + 16 * qa + 4 * wv) * TW);
-  constexpr uint32_t cstep = 4u * 16 * TW;  // bytes per step (16 tile columns)
+  const uint32_t c0 = 4u * (uint32_t)(((size_t)grp * 8 * n_ti + 4 * s0) * TW);
+  constexpr uint32_t cstep = 4u * 4 * TW;  // bytes per step and strip (4 tile columns)
   uint32_t sso[8];
 #pragma unroll
   for (int s8 = 0; s8 < 8; ++s8) sso[s8] = 4u * (uint32_t)((s8 < ns ? s8 : ns - 1) * n_ti * TW);
   const Rsrc rx = make_rsrc(a.xp, a.x_bytes);
   const uint32_t xvo = tok >= 0 ? 32u * (uint32_t)(tok * n_ti + g) : 0x80000000u;
-  const uint32_t x0 = 32u * (uint32_t)(16 * qa + 4 * wv);
+  const uint32_t x0 = 128u * (uint32_t)s0;
   // scalar offsets of step st, clamped to the last step (whose words are read again)
   auto cso = [&](int st) { return c0 + (uint32_t)(st < last ? st : last) * cstep; };
-  auto xso = [&](int st) { return x0 + (uint32_t)(st < last ? st : last) * 512u; };
+  auto xso = [&](int st) { return x0 + (uint32_t)(st < last ? st : last) * 128u; };
 
-  // Activations use a ring of the same depth, and the prologue issues the loads in the
-  // loop's order (a step's code words, then its activations): loads complete in issue
-  // order, so a wait for one step's data never waits for a later step's.
+  // The prologue issues every code word load first (they need only the plan), then the
+  // activations (which wait for this lane's token), so the token lookup delays no code
+  // load. In the loop, a step's reloads follow its use, so loads complete in the order
+  // they are needed.
   ColWords<K> cw[D][8];
   u32x4 xa[D], xb[D];
 #pragma unroll
-  for (int d = 0; d < D; ++d) {
+  for (int d = 0; d < D; ++d)
 #pragma unroll
     for (int s8 = 0; s8 < 8; ++s8) load_col_buf<K>(rc, cvo, cso(d) + sso[s8], cw[d][s8]);
-    load_x(rx, xvo, xso(d), xa[d], xb[d]);
-  }
+#pragma unroll
+  for (int d = 0; d < D; ++d) load_x(rx, xvo, xso(d), xa[d], xb[d]);
 #pragma unroll
   for (int s8 = 0; s8 < 8; ++s8) acc[s8] = (f32x4){0.f, 0.f, 0.f, 0.f};
   int st = 0;
@@ -219,70 +213,51 @@ __device__ __forceinline__ void stream(const TrellisGemvArgs& a, const uint32_t*
       step_body<K, false>(cw[d], xa[d], xb[d], rc, cvo, 0, sso, lo.sh3, rx, xvo, 0, acc);
 }
 
-// One piece: expert record r, units qa .. qb - 1 of group grp; sums to partial[piece].
+// One piece: expert record r, steps s0 .. s1 - 1 of group grp; sums to partial[piece].
 template <int K>
-__device__ __forceinline__ void run_piece(const TrellisGemvArgs& a, Shared& sh, const PlanRec& r,
-                                          int grp, int qa, int qb, int piece) {
-  const int tid = threadIdx.x, lane = tid & 63, n = lane & 15;
-  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+__device__ __forceinline__ void run_piece(const TrellisGemvArgs& a, const PlanRec& r, int grp,
+                                          int s0, int s1, int piece) {
+  const int lane = threadIdx.x & 63, n = lane & 15, g = lane >> 4;
   const int ns = min(8, a.out / 16 - grp * 8);
   const uint32_t* unit = a.codes + r.off / 4;
+  float* dst = a.partial + (size_t)piece * a.N * a.out + grp * 128 + n;
   for (int c0 = 0; c0 < r.cnt; c0 += 16) {
     const int rows = min(16, r.cnt - c0);
+    // lane n (and n + 16, n + 32, n + 48) holds the slot of token row n
     const int slot = n < rows ? a.list[r.start + c0 + n] : -1;
-    if (tid < 16) sh.slots[tid] = slot;
     f32x4 acc[8];
-    stream<K>(a, unit, slot >= 0 ? slot / a.topk : -1, grp, ns, qa, qb, wv, acc);
+    stream<K>(a, unit, slot >= 0 ? slot / a.topk : -1, grp, ns, s0, s1, acc);
+    // accumulator element i of this lane is token row 4 g + i, output channel n of its strip
 #pragma unroll
-    for (int s8 = 0; s8 < 8; ++s8)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) sh.red[((wv * 8 + s8) * 4 + i) * 64 + lane] = acc[s8][i];
-    lds_barrier();
-    float* dst = a.partial + (size_t)piece * a.N * a.out;
-    for (int v = tid; v < ns * 256; v += GEMV_THREADS) {
-      const int s8 = v >> 8, i = (v >> 6) & 3, ln = v & 63;
-      const int m = 4 * (ln >> 4) + i;  // token row of accumulator element i of lane ln
+    for (int i = 0; i < 4; ++i) {
+      const int m = 4 * g + i;
+      const int sm = __shfl(slot, m);
       if (m < rows) {
-        float sum = sh.red[((0 * 8 + s8) * 4 + i) * 64 + ln];
-        sum += sh.red[((1 * 8 + s8) * 4 + i) * 64 + ln];
-        sum += sh.red[((2 * 8 + s8) * 4 + i) * 64 + ln];
-        sum += sh.red[((3 * 8 + s8) * 4 + i) * 64 + ln];
-        const int o = grp * 128 + s8 * 16 + (ln & 15);
-        dst[(size_t)sh.slots[m] * a.out + o] = sum;
+        float* row = dst + (size_t)sm * a.out;
+#pragma unroll
+        for (int s8 = 0; s8 < 8; ++s8)
+          if (s8 < ns) row[s8 * 16] = acc[s8][i];
       }
     }
-    lds_barrier();
   }
 }
 
+// Pieces are read through the scalar cache, like the plan records.
+typedef const __attribute__((address_space(4))) int4* ConstDesc;
+
 __global__ __launch_bounds__(GEMV_THREADS, GEMV_WAVES_PER_SIMD) void trellis_gemv_kernel(TrellisGemvArgs a) {
-  __shared__ Shared sh;
-  const int w = blockIdx.x;
-  const int2 d0 = a.desc[w], d1 = a.desc[w + 1];
-  const int64_t C = a.info[1];
-  const int Geff = a.info[2];  // workgroups with work (see gemv_plan.h)
-  const int Q = a.in / 256, U = a.groups * Q;
-  int ai = d0.x, u = d0.y;
-  PlanRec rn = load_rec(a.rec, min(ai, a.E - 1));
-  while (ai < d1.x || (ai == d1.x && u < d1.y)) {
-    const PlanRec r = rn;
-    rn = load_rec(a.rec, min(ai + 1, a.E - 1));  // the next expert's record, requested early
-    const int u_end = ai < d1.x ? U : d1.y;
-    while (u < u_end) {
-      const int grp = u / Q, qa = u % Q;
-      const int qb = min(Q, qa + (u_end - u));
-      const int piece = w - plan_owner((int64_t)r.p0 + (int64_t)grp * Q * r.k, C, Geff);
-      if (r.k == 2)
-        run_piece<2>(a, sh, r, grp, qa, qb, piece);
-      else if (r.k == 3)
-        run_piece<3>(a, sh, r, grp, qa, qb, piece);
-      else
-        run_piece<4>(a, sh, r, grp, qa, qb, piece);
-      u += qb - qa;
-    }
-    ++ai;
-    u = 0;
-  }
+  const ConstDesc dp = (ConstDesc)a.desc + blockIdx.x;
+  const int ai = dp->x;
+  if (ai < 0) return;
+  const int grp = dp->y, piece = dp->z, span = dp->w;
+  const int s0 = span & 0xFFFF, s1 = span >> 16;
+  const PlanRec r = load_rec(a.rec, ai);
+  if (r.k == 2)
+    run_piece<2>(a, r, grp, s0, s1, piece);
+  else if (r.k == 3)
+    run_piece<3>(a, r, grp, s0, s1, piece);
+  else
+    run_piece<4>(a, r, grp, s0, s1, piece);
 }
 
 // ---- decode hook ------------------------------------------------------------------------
@@ -340,7 +315,7 @@ int trellis_gemv_grid() {
       hipSuccess)
     return 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-  int g = per_cu * cus * GEMV_GRID_MULT;
+  int g = per_cu * cus;
   if (g > GEMV_MAX_G) g = GEMV_MAX_G;
   if (g < 1) g = 1;
   if (dev >= 0 && dev < 64) cache[dev] = g;
