@@ -420,13 +420,15 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f16",
+        "dtype": "i8",
         "data": "synthetic",
         "config": {
             "workload": "mixed-width trellis layer (K2 Mix style) decode batch",
             "experts": 384, "unit": "128x5120", "widths": "368xK2 15xK3 1xK4",
             "tokens": 128, "topk": 8, "active_experts": res["n_active"],
             "compressed_bytes_per_step": res["bytes"], "rotation": "128-wide signed Hadamard fused into the activation prep",
+            "operands": "int8 matrix-core products with int32 sums: the weights' signed bytes, "
+                        "activations as 16-bit per-token fixed point in two int8 halves",
             "replicas": res["replicas"],
         },
         "roofline": {

@@ -44,7 +44,7 @@ extern "C" {
 
 /* ---- flags of the expert GEMM calls -------------------------------------------------- */
 #define TQ_AUTO 0u     /* choose the decode-batch kernel when T*topk <= 16*E, else prefill */
-#define TQ_GEMV 1u     /* force the decode-batch kernel (grouped GEMV, tokens in 16s)      */
+#define TQ_GEMV 1u     /* force the decode-batch kernel (grouped GEMV, tokens in 8s)       */
 #define TQ_GEMM 2u     /* force the prefill kernel (route bucketing + grouped MFMA GEMM)   */
 #define TQ_COMBINE 4u  /* write y[T][out] = sum over k = 0..topk-1 (in order) of the slots */
 #define TQ_ROTATE 8u   /* trellis only: x is not rotated; the call applies hadamard128 with */
@@ -116,10 +116,14 @@ typedef struct tq_mxfp4_layer {
  * Determinism (FORMAT F14): the same inputs give the same bits, whatever the launch
  * timing. The prefill mode also gives a slot the same bits whatever the rest of the batch
  * (a mixed-width layer equals single-width layers). The decode-batch mode splits each
- * routed expert's inputs among workgroups in proportion to the batch's whole routed work,
- * so across batches that route differently a slot's fp32 sum is grouped differently and
+ * routed expert's inputs among waves in proportion to the batch's whole routed work, so
+ * across batches that route differently a slot's fp32 sum is grouped differently and
  * agrees to rounding (about 1e-7 relative).
- * Precondition: |x| < 65520 (the kernels feed the matrix cores f16 operands, FORMAT F10).
+ * Operands (FORMAT F10): the prefill mode feeds the matrix cores f16 activations; the
+ * decode-batch mode feeds each token's activations as 16-bit integers on a per-token
+ * power-of-two scale (two int8 halves), whose rounding of elements far below the token's
+ * largest one is covered by the parity bound.
+ * Precondition: |x| < 65520 (f16 range of the prefill operands).
  */
 int trellis_expert_gemm(const tq_trellis_layer* L, const void* x, int64_t T,
                         const int32_t* topk_ids, const float* topk_w, int32_t topk,
@@ -166,9 +170,9 @@ int route_bucket(const int32_t* topk_ids, int64_t T, int32_t topk, int32_t E,
 
 /*
  * trellis_decode — test hook: decode one trellis unit to its integer values with the
- * device decoders. Path 0 reads back the operands the matrix-core kernels (decode-batch
- * GEMV and prefill GEMM) receive: the byte sums q + 255 as f16 subnormals. Path 1 goes
- * through an exact bf16 conversion of q instead (a second, independent readout).
+ * device decoders, read back from the operands the matrix cores receive. Path 0: the
+ * decode-batch GEMV's signed bytes lo8(m) - 128 and hi8(m) - 128 (q = their sum + 1).
+ * Path 1: the prefill GEMM's byte sums q + 255 as f16 subnormals.
  *   codes  device, out*in*K/8 bytes, 16-byte aligned.   K in {2, 3, 4}.
  *   q      device int16 [out][in] (HF orientation: row = output channel).
  */

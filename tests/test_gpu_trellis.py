@@ -284,3 +284,60 @@ def test_fused_rotation_equals_separate_hadamard(flags):
     ref = oracle_trellis(layer, xr.cpu().numpy().view(np.uint16), ids.cpu().numpy(),
                          gates.cpu().numpy())
     assert rel_l2(fused.cpu().numpy(), ref) <= TOL
+
+
+def _bf16_bits(v):
+    """Round-to-nearest-even bf16 patterns of float values (test input construction)."""
+    f = np.asarray(v, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    r = (f + 0x7FFF + ((f >> 16) & 1)) >> 16
+    return r.astype(np.uint16)
+
+
+def test_decode_batch_exact_on_the_token_grid():
+    """FORMAT F10: every element within a factor 2^7 of its token's largest magnitude is
+    exact on the decode GEMV's 16-bit grid, so only the fp32 summation separates the GPU
+    from the exact FP64 result."""
+    E, T, topk = 10, 24, 4
+    layer = small_layer(413, E, 128, 512)
+    rng = rng_for(413, 1)
+    # magnitudes 2^-6 .. 2^0 with 8 significant bits: all within 2^7 of the maximum
+    mant = rng.integers(128, 256, size=(T, 512)) / 128.0
+    expo = rng.integers(-6, 0, size=(T, 512))
+    x = _bf16_bits(np.where(rng.random((T, 512)) < 0.5, -1.0, 1.0) * mant * 2.0 ** expo)
+    ids = uniform_routes(rng_for(413, 2), T, E, topk)
+    y = run(layer, x, ids, flags=1)
+    ref = oracle_trellis(layer, x, ids, None)
+    assert rel_l2(y, ref) <= 1e-6
+
+
+def test_decode_batch_outlier_tokens():
+    """Tokens whose largest element is 30 and 1000 times their RMS: the decode GEMV rounds
+    their small elements to a coarser grid (FORMAT F10); the error stays within the bound
+    and grows with the ratio."""
+    E, T, topk = 12, 32, 4
+    layer = small_layer(414, E, 128, 1024)
+    xf = rng_for(414, 1).standard_normal((T, 1024))
+    xf[: T // 2, 7] = 30.0
+    xf[T // 2:, 700] = -1000.0
+    x = _bf16_bits(xf)
+    ids = uniform_routes(rng_for(414, 2), T, E, topk)
+    y = run(layer, x, ids, flags=1)
+    ref = oracle_trellis(layer, x, ids, None)
+    e30 = rel_l2(y[: T // 2], ref[: T // 2])
+    e1000 = rel_l2(y[T // 2:], ref[T // 2:])
+    assert e30 <= 2e-4
+    assert e1000 <= TOL
+
+
+def test_decode_batch_nonfinite_token():
+    """A token with an infinite element gives NaN in its slots; the others are unaffected."""
+    E, T, topk = 8, 16, 4
+    layer = small_layer(415, E, 128, 512)
+    x = bf16_from_normal(rng_for(415, 1), (T, 512)).copy()
+    x[5, 100] = 0x7F80  # +inf
+    ids = uniform_routes(rng_for(415, 2), T, E, topk)
+    y = run(layer, x, ids, flags=1)
+    assert np.all(np.isnan(y[5]))
+    keep = np.arange(T) != 5
+    ref = oracle_trellis(layer, x[keep], ids[keep], None)
+    assert rel_l2(y[keep], ref) <= TOL

@@ -145,9 +145,11 @@ WsLayout ws_layout(int64_t T, int topk, int E, int out, int in, uint32_t flags, 
     off += round_up((size_t)N * 16, 256);
     L.prank = off;
     off += round_up((size_t)N * 4, 256);
-    L.xprep = off;
-    off += round_up((size_t)T * in * 2, 256);
-    L.rowsum = off;
+    L.xq = off;
+    off += round_up((size_t)T * in * 4, 256);
+    L.xscale = off;
+    off += round_up((size_t)T * 4, 256);
+    L.xsum = off;
     off += round_up((size_t)T * 4, 256);
     L.partial = off;
     L.partial_bytes = round_up(Q * N * out * 4, 256);
@@ -366,8 +368,9 @@ int common_checks(int E, int out, int in, const void* x, int64_t T, const int32_
   if (!layout->gemm && !mxfp4 && (int64_t)E * layout->groups > tq::GEMV_MAX_G)
     return fail(TQ_EINVAL, "decode batches take at most %d expert groups (E * out / 128)",
                 tq::GEMV_MAX_G);
-  if ((layout->gemm || !mxfp4) && T * (int64_t)in * 2 >= ((int64_t)1 << 31))
-    return fail(TQ_EINVAL, "T * in * 2 bytes of activations must stay below 2^31");
+  if ((layout->gemm || !mxfp4) && T * (int64_t)in * (layout->gemm ? 2 : 4) >= ((int64_t)1 << 31))
+    return fail(TQ_EINVAL, "the prepared activations (T * in * %d bytes) must stay below 2^31",
+                layout->gemm ? 2 : 4);
   if (layout->gemm && (int64_t)out * in / 2 + (int64_t)out * in / 32 >= ((int64_t)1 << 31))
     return fail(TQ_EINVAL, "out * in is too large for the prefill path");
   if (!layout->gemm && !mxfp4 && (int64_t)out * in / 2 >= ((int64_t)1 << 31))
@@ -476,18 +479,19 @@ int trellis_expert_gemm(const tq_trellis_layer* L, const void* x, int64_t T,
     p.signs = L->signs;
     p.T = (int)T;
     p.in = L->in;
-    p.xp = at<uint32_t>(ws, W.xprep);
-    p.rowsum = at<float>(ws, W.rowsum);
+    p.xq = at<uint32_t>(ws, W.xq);
+    p.xscale = at<float>(ws, W.xscale);
+    p.xsum = at<int32_t>(ws, W.xsum);
     err = tq::launch_gemv_plan(p, s);
     if (err != hipSuccess) return hip_fail(err, "decode plan launch");
     tq::TrellisGemvArgs a{};
     a.codes = L->codes;
-    a.xp = p.xp;
+    a.xq = p.xq;
     a.rec = p.rec;
     a.desc = p.desc;
     a.list = p.list;
     a.partial = at<float>(ws, W.partial);
-    a.x_bytes = (uint32_t)(T * L->in * 2);
+    a.x_bytes = (uint32_t)(T * L->in * 4);
     a.N = (int)N;
     a.out = L->out;
     a.in = L->in;
@@ -503,10 +507,9 @@ int trellis_expert_gemm(const tq_trellis_layer* L, const void* x, int64_t T,
     r.partial = a.partial;
     r.scales = L->scales;
     r.gates = topk_w;
-    r.rowsum = p.rowsum;
+    r.xsum = p.xsum;
+    r.xscale = p.xscale;
     r.y = y;
-    r.acc_scale = 16777216.0f;
-    r.offset = 255.0f;
     r.N = (int)N;
     r.out = L->out;
     r.topk = topk;

@@ -10,9 +10,9 @@
 // candidates at once. Last come the slot lists, the per-slot records and every wave's
 // piece (each active expert's thread writes its own waves').
 //
-// Blocks 1..T convert token t = block - 1 of x~ (bf16) to the f16 operand layout of the
-// trellis GEMV (word r of tile column c = [lo: x[16c + r + 8], hi: x[16c + r]], rounded to
-// nearest even) and sum the token's f16 values in a fixed order.
+// Blocks 1..T convert token t = block - 1 of x~ (bf16, rotated first when asked) to the
+// int8 operands of the decode GEMV (see prep_block). The prefill GEMM's f16 operands come
+// from the same conversion code, launched on its own (launch_activation_prep).
 #include "gemv_plan.h"
 #include "tq_internal.h"
 
@@ -313,53 +313,145 @@ __device__ __forceinline__ void rotate_column(float f[16], const int8_t* signs, 
   for (int j = 0; j < 16; ++j) f[j] = __uint_as_float(f32_to_bf16_rne(f[j] * scale) << 16);
 }
 
+// x~ of tile column c of token t as 16 floats (bf16 values), rotated when asked.
+__device__ __forceinline__ void load_column(const PlanArgs& a, int t, int c, float f[16]) {
+  const uint4* src = reinterpret_cast<const uint4*>(a.x + (size_t)t * a.in);
+  const uint4 u = src[2 * c], v = src[2 * c + 1];
+  const uint32_t wv[8] = {u.x, u.y, u.z, u.w, v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    f[2 * k] = bf16_lo_to_f32(wv[k]);
+    f[2 * k + 1] = bf16_hi_to_f32(wv[k]);
+  }
+  if (a.rotate) rotate_column(f, a.signs, c);
+}
+
+// Block-wide reductions over the waves that hold columns (nw of them).
+__device__ __forceinline__ float block_max(float v, float* red, int nw) {
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) v = fmaxf(v, __shfl_xor(v, d, 64));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  lds_barrier();
+  float m = red[0];
+  for (int w = 1; w < nw; ++w) m = fmaxf(m, red[w]);
+  return m;
+}
+
 // One token per block: thread c converts tile column c (columns c + PLAN_THREADS, ... when
 // in > 16 * PLAN_THREADS), rotating it first when asked. Waves without a column leave at
 // once (a 128-block's 8 columns are always in one wave and all present or all absent).
+//
+// F16 (prefill GEMM operands): f16 pairs, and the token's sum of its f16 values in a fixed
+// order.
+// I8 (decode GEMV operands): the token's scale 2^e is the largest power of two with
+// max |x~| * 2^e <= 32639; every element becomes the integer x = rint(x~ * 2^e) (ties to
+// even; exact for elements within 2^7 of the maximum), split as x = 256 hi + lo with hi, lo
+// in [-128, 127]. Operand register r of a tile column holds bytes [v[r + 8], v[r + 8], v[r],
+// v[r]] of one half (v = hi, then v = lo: two 32-byte rows per column), matching the
+// weights' signed bytes (trellis_decode.h). The token's sum of the integers x and 2^-e are
+// kept for the epilogue; a token with a non-finite element gets the scale NaN.
+template <bool I8>
 __device__ void prep_block(const PlanArgs& a, int t) {
   typedef _Float16 h2 __attribute__((ext_vector_type(2)));
-  __shared__ float s_sum[PLAN_WAVES];
+  __shared__ float s_red[PLAN_WAVES];
+  __shared__ int s_ired[PLAN_WAVES];
   const int tid = threadIdx.x;
   const int n_ti = a.in / 16;
   const int active = n_ti < PLAN_THREADS ? n_ti : PLAN_THREADS;
+  const int nw = (active + 63) / 64;
   if ((tid & ~63) >= active) return;  // whole wave
-  const uint4* src = reinterpret_cast<const uint4*>(a.x + (size_t)t * a.in);
-  uint4* dst = reinterpret_cast<uint4*>(a.xp + (size_t)t * n_ti * 8);
-  float sum = 0.0f;
-  for (int c = tid; c < n_ti; c += PLAN_THREADS) {
-    const uint4 u = src[2 * c], v = src[2 * c + 1];
-    const uint32_t wv[8] = {u.x, u.y, u.z, u.w, v.x, v.y, v.z, v.w};
-    float f[16];
+  if constexpr (!I8) {
+    uint4* dst = reinterpret_cast<uint4*>(a.xp + (size_t)t * n_ti * 8);
+    float sum = 0.0f;
+    for (int c = tid; c < n_ti; c += PLAN_THREADS) {
+      float f[16];
+      load_column(a, t, c, f);
+      uint32_t P[8];
+      float hf[16];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      f[2 * k] = bf16_lo_to_f32(wv[k]);
-      f[2 * k + 1] = bf16_hi_to_f32(wv[k]);
+      for (int r = 0; r < 8; ++r) {
+        const h2 p = (h2){(_Float16)f[r + 8], (_Float16)f[r]};
+        P[r] = __builtin_bit_cast(uint32_t, p);
+        hf[r] = (float)p.y;
+        hf[r + 8] = (float)p.x;
+      }
+      float cs = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) cs += hf[i];
+      sum += cs;
+      dst[2 * c] = make_uint4(P[0], P[1], P[2], P[3]);
+      dst[2 * c + 1] = make_uint4(P[4], P[5], P[6], P[7]);
     }
-    if (a.rotate) rotate_column(f, a.signs, c);
-    uint32_t P[8];
-    float hf[16];
 #pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      const h2 p = (h2){(_Float16)f[r + 8], (_Float16)f[r]};
-      P[r] = __builtin_bit_cast(uint32_t, p);
-      hf[r] = (float)p.y;
-      hf[r + 8] = (float)p.x;
+    for (int d = 32; d >= 1; d >>= 1) sum += __shfl_xor(sum, d, 64);
+    if ((tid & 63) == 0) s_red[tid >> 6] = sum;
+    lds_barrier();
+    if (tid == 0) {
+      float s = 0.0f;
+      for (int w = 0; w < nw; ++w) s += s_red[w];
+      a.rowsum[t] = s;
     }
-    float cs = 0.0f;
+  } else {
+    // pass 1: the largest magnitude (non-finite elements flagged as +inf)
+    float amax = 0.0f;
+    for (int c = tid; c < n_ti; c += PLAN_THREADS) {
+      float f[16];
+      load_column(a, t, c, f);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) cs += hf[i];
-    sum += cs;
-    dst[2 * c] = make_uint4(P[0], P[1], P[2], P[3]);
-    dst[2 * c + 1] = make_uint4(P[4], P[5], P[6], P[7]);
-  }
+      for (int j = 0; j < 16; ++j) {
+        const float m = fabsf(f[j]);
+        amax = fmaxf(amax, m <= 3.4e38f ? m : __builtin_inff());
+      }
+    }
+    amax = block_max(amax, s_red, nw);
+    int e = 0;
+    bool finite = amax <= 3.4e38f;
+    if (finite && amax > 0.0f) {
+      int ex;
+      (void)frexpf(amax, &ex);  // amax = f * 2^ex, f in [0.5, 1)
+      e = 15 - ex;
+      if (ldexpf(amax, e) > 32639.0f) e -= 1;
+    }
+    // pass 2: integers, halves, operand layout
+    int isum = 0;
+    for (int c = tid; c < n_ti; c += PLAN_THREADS) {
+      float f[16];
+      load_column(a, t, c, f);
+      int hi[16], lo[16];
 #pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) sum += __shfl_xor(sum, d, 64);
-  if ((tid & 63) == 0) s_sum[tid >> 6] = sum;
-  lds_barrier();
-  if (tid == 0) {
-    float s = 0.0f;
-    for (int w = 0; w < (active + 63) / 64; ++w) s += s_sum[w];
-    a.rowsum[t] = s;
+      for (int j = 0; j < 16; ++j) {
+        float v = finite ? rintf(ldexpf(f[j], e)) : 0.0f;
+        v = fminf(fmaxf(v, -32639.0f), 32639.0f);
+        const int xi = (int)v;
+        isum += xi;
+        hi[j] = (xi + 128) >> 8;
+        lo[j] = xi - (hi[j] << 8);
+      }
+      uint32_t H[8], L[8];
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        const uint32_t h8 = (uint32_t)hi[r + 8] & 0xFFu, h0 = (uint32_t)hi[r] & 0xFFu;
+        const uint32_t l8 = (uint32_t)lo[r + 8] & 0xFFu, l0 = (uint32_t)lo[r] & 0xFFu;
+        H[r] = h8 | (h8 << 8) | (h0 << 16) | (h0 << 24);
+        L[r] = l8 | (l8 << 8) | (l0 << 16) | (l0 << 24);
+      }
+      uint4* dh = reinterpret_cast<uint4*>(a.xq + ((size_t)(2 * t) * n_ti + c) * 8);
+      uint4* dl = reinterpret_cast<uint4*>(a.xq + ((size_t)(2 * t + 1) * n_ti + c) * 8);
+      dh[0] = make_uint4(H[0], H[1], H[2], H[3]);
+      dh[1] = make_uint4(H[4], H[5], H[6], H[7]);
+      dl[0] = make_uint4(L[0], L[1], L[2], L[3]);
+      dl[1] = make_uint4(L[4], L[5], L[6], L[7]);
+    }
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) isum += __shfl_xor(isum, d, 64);
+    if ((tid & 63) == 0) s_ired[tid >> 6] = isum;
+    lds_barrier();
+    if (tid == 0) {
+      int s = 0;
+      for (int w = 0; w < nw; ++w) s += s_ired[w];
+      a.xsum[t] = s;
+      a.xscale[t] = finite ? ldexpf(1.0f, -e) : __builtin_nanf("");
+    }
   }
 }
 
@@ -368,11 +460,11 @@ __global__ __launch_bounds__(PLAN_THREADS) void gemv_plan_kernel(PlanArgs a) {
   if (blockIdx.x == 0)
     plan_block<TRELLIS>(a);
   else
-    prep_block(a, blockIdx.x - 1);
+    prep_block<true>(a, blockIdx.x - 1);
 }
 
 __global__ __launch_bounds__(PLAN_THREADS) void activation_prep_kernel(PlanArgs a) {
-  prep_block(a, blockIdx.x);
+  prep_block<false>(a, blockIdx.x);
 }
 
 }  // namespace

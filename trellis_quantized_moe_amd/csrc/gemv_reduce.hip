@@ -53,8 +53,9 @@ hipError_t launch_gemv_reduce(const GemvReduceArgs& a, hipStream_t s) {
 
 // ---- piece reduction (trellis decode batches) ---------------------------------------------
 // Third launch of the planned decode-batch path (gemv_plan.h). A slot's expert group was
-// split into pieces by the plan; their partial sums are added in piece order, scaled by
-// acc_scale, corrected by offset * rowsum[token], then scaled per channel and gated. Empty
+// split into pieces by the plan; their partial sums (of x * (q - 1), x the token's 16-bit
+// integers) are added in piece order, the token's sum of x is added back and the token's
+// 2^-e applied, then the per-channel scale and the gate. Empty
 // slots give 0, bad ids and bad units NaN (their status bits were set by the plan). Without
 // combine, one thread per 4 outputs of a slot; with combine, one block per (token, 128
 // outputs) puts the slot values in LDS and adds them over k = 0..topk-1 in order.
@@ -74,7 +75,8 @@ __device__ __forceinline__ void add4(float4& s, const float4& v) {
 
 __device__ __forceinline__ float4 piece_slot(const PieceReduceArgs& a, int slot, int o) {
   const int4 inf = a.slot_info[slot];
-  const float corr = a.rowsum ? a.offset * a.rowsum[slot / a.topk] : 0.0f;
+  const int t = slot / a.topk;
+  const float add = (float)a.xsum[t], mul = a.xscale[t];
   const float gate = a.gates ? a.gates[slot] : 1.0f;
   if (inf.x == SLOT_EMPTY) return make_float4(0.f, 0.f, 0.f, 0.f);
   if (inf.x < 0) {
@@ -102,7 +104,7 @@ __device__ __forceinline__ float4 piece_slot(const PieceReduceArgs& a, int slot,
   float r[4] = {s.x, s.y, s.z, s.w};
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    r[j] = r[j] * a.acc_scale - corr;
+    r[j] = (r[j] + add) * mul;
     r[j] = r[j] * f16_bits_to_f32(sw[j >> 1] >> (16 * (j & 1)));
     if (a.gates) r[j] = r[j] * gate;
   }

@@ -16,7 +16,7 @@ struct WsLayout {
   size_t counts = 0, offsets = 0, hist = 0, rank = 0, pairs = 0, items = 0, n_items = 0;
   size_t route_bytes = 0;
   size_t slots = 0, slots_bytes = 0;
-  size_t xprep = 0, rowsum = 0;
+  size_t xprep = 0, rowsum = 0, xq = 0, xscale = 0, xsum = 0;
   size_t info = 0, rec = 0, desc = 0, list = 0, slot_info = 0, prank = 0;
   size_t total = 0;
   int gemv_slices = 1, gemv_steps = 1, groups = 1, route_blocks = 1, max_items = 0;
@@ -49,30 +49,33 @@ struct PlanArgs {
   int4* slot_info;          // [N]
   int32_t* rank;            // [N] (used when N exceeds what the plan keeps in registers)
   uint32_t* status;
-  // activation prep (trellis): x null = none
+  // activation prep: x null = none
   const uint16_t* x;
   bool rotate;              // apply the 128-wide Hadamard (FORMAT F8) first
   const int8_t* signs;      // its signs, or null
   int T, in;
-  uint32_t* xp;             // f16 pairs [T][in/16][8]
+  uint32_t* xp;             // f16 pairs [T][in/16][8] (prefill GEMM operands)
   float* rowsum;            // [T]
+  uint32_t* xq;             // or int8 halves [T][2][in/16][8] (decode GEMV operands)
+  float* xscale;            // [T]: 2^-e of each token
+  int32_t* xsum;            // [T]: sum of each token's 16-bit integers
 };
 hipError_t launch_gemv_plan(const PlanArgs& a, hipStream_t s);
 // x~ (bf16 [T][in]) -> f16 pairs [T][in/16][8] (word r of tile column c = [lo: x[16c + r + 8],
 // hi: x[16c + r]]) and per-token sums of the f16 values: the activations of the trellis
-// kernels. With rotate, x is first rotated as hadamard128 would (FORMAT F8).
+// prefill GEMM. With rotate, x is first rotated as hadamard128 would (FORMAT F8).
 hipError_t launch_activation_prep(const uint16_t* x, int64_t T, int in, uint32_t* xp,
                                   float* rowsum, bool rotate, const int8_t* signs,
                                   hipStream_t s);
 
 struct TrellisGemvArgs {
   const uint32_t* codes;
-  const uint32_t* xp;
+  const uint32_t* xq;   // int8 halves [T][2][in/16][8] (the plan's prep)
   const PlanRec* rec;
   const int4* desc;     // [G]
   const int32_t* list;
   float* partial;       // [in / 256][N][out]: the pieces of each slot
-  uint32_t x_bytes;     // size of xp in bytes (< 2^31)
+  uint32_t x_bytes;     // size of xq in bytes (< 2^31)
   int N, out, in, topk, G;
 };
 // Waves of the trellis GEMV that the GPU holds at once; 0 on a HIP error.
@@ -84,9 +87,9 @@ struct PieceReduceArgs {
   const float* partial;
   const uint16_t* scales;
   const float* gates;   // or null
-  const float* rowsum;  // or null
+  const int32_t* xsum;  // [T]: added to each slot's sum (the signed-byte correction)
+  const float* xscale;  // [T]: then multiplied
   float* y;
-  float acc_scale, offset;
   int N, out, topk, combine;
 };
 constexpr int PIECE_MAX_TOPK = 64;  // largest topk (checked by the C ABI)

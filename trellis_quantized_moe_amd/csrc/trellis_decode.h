@@ -97,7 +97,7 @@ __device__ __forceinline__ void col_mpairs_k3(uint32_t q0, uint32_t q1, uint32_t
   }
 }
 
-// ---- decode-batch operands: byte sums as f16 subnormals ---------------------------------
+// ---- prefill operands: byte sums as f16 subnormals ----------------------------------------
 // The matrix cores take v = lo8(m) + hi8(m) = q + 255 (0..510) as the bits of an f16 with a
 // zero exponent field, i.e. the subnormal v * 2^-24, exact (the matrix cores keep subnormal
 // inputs). A 16-bit lane computes v = m - 255 * (m >> 8) with one packed shift and one
@@ -107,8 +107,8 @@ __device__ __forceinline__ void col_mpairs_k3(uint32_t q0, uint32_t q1, uint32_t
 // The activations use one layout for every K: word r (r = 0..7) of a tile column holds
 // [lo: x[r + 8], hi: x[r]], and byte_sums returns the weights in the same layout:
 // V[r] = [lo: v[r + 8], hi: v[r]].
-constexpr float GEMV_BYTE_OFFSET = 255.0f;
-constexpr float GEMV_BYTE_SCALE = 16777216.0f;  // 2^24
+constexpr float BYTE_SUM_OFFSET = 255.0f;
+constexpr float BYTE_SUM_SCALE = 16777216.0f;  // 2^24
 
 __device__ __forceinline__ uint32_t byte_sum_pair(uint32_t M) {
   u16x2 m = __builtin_bit_cast(u16x2, M);
@@ -136,37 +136,32 @@ __device__ __forceinline__ void byte_sums(const uint32_t M[8], uint32_t V[8]) {
   }
 }
 
-// ---- prefill operands: q as bf16, natural input order ---------------------------------
-// v = lo8 + hi8 per half (packed 16-bit: m - 255 * (m >> 8)); 2^23 + v is built as an
-// fp32 bit pattern and 2^23 + 255 subtracted, giving q exactly; q has at most 8
-// significant bits, so its bf16 pattern is the fp32 pattern's upper half.
-__device__ __forceinline__ void mpair_to_f32(uint32_t M, float* q_ih, float* q_il) {
-  u16x2 m = __builtin_bit_cast(u16x2, M);
-  u16x2 h = m >> (u16x2){8, 8};
-  u16x2 v = m + h * (u16x2){0xFF01, 0xFF01};
-  uint32_t vv = __builtin_bit_cast(uint32_t, v);
-  *q_ih = __uint_as_float(perm(vv, 0x4B4B4B4Bu, 0x000C0706u)) - 8388863.0f;
-  *q_il = __uint_as_float(perm(vv, 0x4B4B4B4Bu, 0x000C0504u)) - 8388863.0f;
-}
+// ---- decode-batch operands: signed bytes ----------------------------------------------
+// The int8 matrix-core operation takes the two bytes of m as two separate k positions,
+// each against the same activation, so the sum over a weight's two positions is
+// x * (lo8(m) + hi8(m)). One xor with 0x80 per byte makes the bytes signed: (lo8 - 128) +
+// (hi8 - 128) = q - 1, and the epilogue adds sum(x) back. A register of m-pairs becomes one
+// operand register with a single xor.
+//
+// The activations use one layout for every K: bytes 0..3 of operand register r of a tile
+// column hold [x[r + 8], x[r + 8], x[r], x[r]], and i8_operands returns the weights in the
+// matching layout: register r = [lo8, hi8 of m[r + 8] | lo8, hi8 of m[r]], each byte - 128.
+__device__ __forceinline__ uint32_t signed_bytes(uint32_t M) { return M ^ 0x80808080u; }
 
-// Pack two exact fp32 integers into bf16 [lo: a, hi: b].
-__device__ __forceinline__ uint32_t pack_bf16_exact(float a, float b) {
-  return perm(__float_as_uint(b), __float_as_uint(a), 0x07060302u);
-}
-
-// Eight natural-order bf16 dwords (inputs 2t, 2t+1) from the eight m-pairs of a column.
 template <int K>
-__device__ __forceinline__ void mpairs_to_bf16_natural(const uint32_t M[8], uint32_t out[8]) {
-  float q[16];
+__device__ __forceinline__ void i8_operands(const uint32_t M[8], uint32_t B[8]) {
+  if constexpr (K == 4) {
+    // M[r] (r < 4) = [hi: m[r], lo: m[r + 4]]; M[r] (r >= 4) = [hi: m[r + 4], lo: m[r + 8]]
 #pragma unroll
-  for (int r = 0; r < 8; ++r) {
-    float a, b;
-    mpair_to_f32(M[r], &a, &b);
-    q[pair_ih<K>(r)] = a;
-    q[pair_il<K>(r)] = b;
+    for (int r = 0; r < 4; ++r) {
+      B[r] = signed_bytes(perm(M[r], M[r + 4], 0x07060302u));      // [hi: m[r], lo: m[r + 8]]
+      B[r + 4] = signed_bytes(perm(M[r], M[r + 4], 0x05040100u));  // [hi: m[r + 4], lo: m[r + 12]]
+    }
+  } else {
+    // M[r] = [hi: m[r], lo: m[r + 8]]
+#pragma unroll
+    for (int r = 0; r < 8; ++r) B[r] = signed_bytes(M[r]);
   }
-#pragma unroll
-  for (int t = 0; t < 8; ++t) out[t] = pack_bf16_exact(q[2 * t], q[2 * t + 1]);
 }
 
 }  // namespace tq

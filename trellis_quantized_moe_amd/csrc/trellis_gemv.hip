@@ -5,18 +5,19 @@
 // expert, on its own: no LDS and no barrier, so a wave that waits for memory never holds
 // up another, and its load stream never restarts. A step is 4 tile columns (64 inputs) of
 // the group's 8 strips (128 output channels). Per step and strip, each lane decodes one
-// tile column (16 weights of one output channel) and the wave feeds two 16 x 16 x 32
-// matrix-core operations, with the activations of up to 16 routed token rows as the other
-// operand (rows past the expert's count are zero).
+// tile column (16 weights of one output channel) and the wave feeds two 16 x 16 x 64 int8
+// matrix-core operations: the weights as signed bytes (two k positions per weight, see
+// trellis_decode.h), the activations as the high and the low int8 halves of each token's
+// 16-bit integers (rows 0..7: high halves of up to 8 routed tokens, rows 8..15: their low
+// halves; rows past the expert's count are zero). The accumulators are exact int32.
 //
-// Code words are requested D steps ahead (D = 4 at K = 2, 2 at K = 3 and 4), held in D
-// register sets used in turn, so that several steps of loads are in flight per wave, and
-// so are the activations (prepared once per call, f16). The load of a strip's next words
-// is issued right after its current words are decoded.
+// Code words are requested D = 2 steps ahead, held in D register sets used in turn, so
+// that several steps of loads are in flight per wave, and so are the activations (prepared
+// once per call). The load of a strip's next words is issued right after its current words
+// are decoded.
 //
-// At the end the wave stores its accumulators as the piece's partial sums; the reduction
-// launch adds the pieces in order and applies the epilogue. Each weight reaches the matrix
-// cores as the f16 subnormal (q + 255) * 2^-24 (see trellis_decode.h).
+// At the end the wave joins each token's two halves (256 hi + lo) and stores the piece's
+// partial sums; the reduction launch adds the pieces in order and applies the epilogue.
 #include "gemv_plan.h"
 #include "tq_internal.h"
 #include "trellis_decode.h"
@@ -29,8 +30,10 @@ constexpr int GEMV_THREADS = 64;         // one wave per workgroup
 constexpr int GEMV_WAVES_PER_SIMD = 3;  // register budget: 168 per lane
 
 // ---- code words --------------------------------------------------------------------------
-// Words of one tile column a lane holds (see trellis_decode.h): K = 2 one word, K = 4 two,
-// K = 3 three.
+// Words of one tile column a lane loads (see trellis_decode.h): K = 2 word n, K = 4 words
+// 2n and 2n + 1, K = 3 the three words of k3_column_words. The word after them (which the
+// last states' windows reach) is the next lane's first word, taken by a row rotation: a
+// second load would cost more than the two instructions of the rotation.
 template <int K>
 struct ColWords {
   uint32_t w[K == 2 ? 1 : (K == 4 ? 2 : 3)];
@@ -140,19 +143,19 @@ template <int K, bool RELOAD>
 __device__ __forceinline__ void step_body(ColWords<K> (&cw)[8], u32x4& xa, u32x4& xb, Rsrc rc,
                                           const uint32_t cvo[3], uint32_t cso,
                                           const uint32_t sso[8], uint32_t sh3, Rsrc rx,
-                                          uint32_t xvo, uint32_t xso, f32x4 acc[8]) {
+                                          uint32_t xvo, uint32_t xso, i32x4 acc[8]) {
   // Every reload goes into the registers of the value it replaces, after that value's last
   // use (the scheduling barriers keep the compiler from hoisting it), so the loop carries
   // its registers without copies, and a copy would wait for the load in flight.
 #pragma unroll
   for (int s8 = 0; s8 < 8; ++s8) {
-    uint32_t M[8], V[8];
+    uint32_t M[8], B[8];
     decode_col<K>(cw[s8], sh3, M);
     __builtin_amdgcn_sched_barrier(0);
     if (RELOAD) load_col_buf<K>(rc, cvo, cso + sso[s8], cw[s8]);
-    byte_sums<K>(M, V);
-    acc[s8] = mfma_f16(xa, (u32x4){V[0], V[1], V[2], V[3]}, acc[s8]);  // pairs 0..3
-    acc[s8] = mfma_f16(xb, (u32x4){V[4], V[5], V[6], V[7]}, acc[s8]);  // pairs 4..7
+    i8_operands<K>(M, B);
+    acc[s8] = mfma_i8(xa, (u32x4){B[0], B[1], B[2], B[3]}, acc[s8]);  // pairs 0..3
+    acc[s8] = mfma_i8(xb, (u32x4){B[4], B[5], B[6], B[7]}, acc[s8]);  // pairs 4..7
   }
   __builtin_amdgcn_sched_barrier(0);
   if (RELOAD) load_x(rx, xvo, xso, xa, xb);
@@ -160,13 +163,14 @@ __device__ __forceinline__ void step_body(ColWords<K> (&cw)[8], u32x4& xa, u32x4
 
 // Steps s0 .. s1 - 1 of output group grp: step st covers tile columns 4 st .. 4 st + 3 (lane
 // group g = lane / 16 takes column 4 st + g) of each of the group's strips. tok = this
-// lane's token row, or -1 (zero row: its activation offset lies past the end of the
-// buffer, where buffer loads return 0).
+// lane's token, or -1 (zero row: its activation offset lies past the end of the buffer,
+// where buffer loads return 0); half = 0 (high int8 halves) or 1 (low).
 template <int K>
 __device__ __forceinline__ void stream(const TrellisGemvArgs& a, const uint32_t* __restrict__ unit,
-                                       int tok, int grp, int ns, int s0, int s1, f32x4 acc[8]) {
+                                       int tok, int half, int grp, int ns, int s0, int s1,
+                                       i32x4 acc[8]) {
   constexpr int TW = 8 * K;  // words per tile
-  constexpr int D = K == 2 ? 4 : 2;
+  constexpr int D = 2;
   const int lane = threadIdx.x & 63, g = lane >> 4, n = lane & 15;
   const int n_ti = a.in / 16;
   const int steps = s1 - s0, last = steps - 1;
@@ -178,8 +182,8 @@ __device__ __forceinline__ void stream(const TrellisGemvArgs& a, const uint32_t*
   uint32_t sso[8];
 #pragma unroll
   for (int s8 = 0; s8 < 8; ++s8) sso[s8] = 4u * (uint32_t)((s8 < ns ? s8 : ns - 1) * n_ti * TW);
-  const Rsrc rx = make_rsrc(a.xp, a.x_bytes);
-  const uint32_t xvo = tok >= 0 ? 32u * (uint32_t)(tok * n_ti + g) : 0x80000000u;
+  const Rsrc rx = make_rsrc(a.xq, a.x_bytes);
+  const uint32_t xvo = tok >= 0 ? 32u * (uint32_t)((2 * tok + half) * n_ti + g) : 0x80000000u;
   const uint32_t x0 = 128u * (uint32_t)s0;
   // scalar offsets of step st, clamped to the last step (whose words are read again)
   auto cso = [&](int st) { return c0 + (uint32_t)(st < last ? st : last) * cstep; };
@@ -198,7 +202,7 @@ __device__ __forceinline__ void stream(const TrellisGemvArgs& a, const uint32_t*
 #pragma unroll
   for (int d = 0; d < D; ++d) load_x(rx, xvo, xso(d), xa[d], xb[d]);
 #pragma unroll
-  for (int s8 = 0; s8 < 8; ++s8) acc[s8] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  for (int s8 = 0; s8 < 8; ++s8) acc[s8] = (i32x4){0, 0, 0, 0};
   int st = 0;
   for (; st + D <= steps; st += D) {
 #pragma unroll
@@ -213,30 +217,37 @@ __device__ __forceinline__ void stream(const TrellisGemvArgs& a, const uint32_t*
       step_body<K, false>(cw[d], xa[d], xb[d], rc, cvo, 0, sso, lo.sh3, rx, xvo, 0, acc);
 }
 
-// One piece: expert record r, steps s0 .. s1 - 1 of group grp; sums to partial[piece].
+// One piece: expert record r, steps s0 .. s1 - 1 of group grp; sums to partial[piece], in
+// chunks of up to 8 routed tokens.
 template <int K>
 __device__ __forceinline__ void run_piece(const TrellisGemvArgs& a, const PlanRec& r, int grp,
                                           int s0, int s1, int piece) {
   const int lane = threadIdx.x & 63, n = lane & 15, g = lane >> 4;
+  const int j = n & 7, half = n >> 3;  // this lane's A row: token j of the chunk, its half
   const int ns = min(8, a.out / 16 - grp * 8);
   const uint32_t* unit = a.codes + r.off / 4;
   float* dst = a.partial + (size_t)piece * a.N * a.out + grp * 128 + n;
-  for (int c0 = 0; c0 < r.cnt; c0 += 16) {
-    const int rows = min(16, r.cnt - c0);
-    // lane n (and n + 16, n + 32, n + 48) holds the slot of token row n
-    const int slot = n < rows ? a.list[r.start + c0 + n] : -1;
-    f32x4 acc[8];
-    stream<K>(a, unit, slot >= 0 ? slot / a.topk : -1, grp, ns, s0, s1, acc);
-    // accumulator element i of this lane is token row 4 g + i, output channel n of its strip
+  for (int c0 = 0; c0 < r.cnt; c0 += 8) {
+    const int rows = min(8, r.cnt - c0);
+    // lanes with j = m hold the slot of token m of the chunk
+    const int slot = j < rows ? a.list[r.start + c0 + j] : -1;
+    i32x4 acc[8];
+    stream<K>(a, unit, slot >= 0 ? slot / a.topk : -1, half, grp, ns, s0, s1, acc);
+    // accumulator element i of lane (g, n) is row 4 g + i: for g < 2 the high half of token
+    // 4 g + i, whose low half is in lane + 32
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int m = 4 * g + i;
-      const int sm = __shfl(slot, m);
-      if (m < rows) {
+      const int sm = __shfl(slot, m & 7);
+      float v[8];
+#pragma unroll
+      for (int s8 = 0; s8 < 8; ++s8)
+        v[s8] = 256.0f * (float)acc[s8][i] + (float)__shfl_xor(acc[s8][i], 32, 64);
+      if (g < 2 && m < rows) {
         float* row = dst + (size_t)sm * a.out;
 #pragma unroll
         for (int s8 = 0; s8 < 8; ++s8)
-          if (s8 < ns) row[s8 * 16] = acc[s8][i];
+          if (s8 < ns) row[s8 * 16] = v[s8];
       }
     }
   }
@@ -262,8 +273,9 @@ __global__ __launch_bounds__(GEMV_THREADS, GEMV_WAVES_PER_SIMD) void trellis_gem
 
 // ---- decode hook ------------------------------------------------------------------------
 // One wave per (strip, 4 tile columns); lane (g, n) decodes column n of tile column
-// 4 * blk + g with the GEMV (path 0) or prefill (path 1) operand conversion, and writes
-// q[out][in] as int16.
+// 4 * blk + g with the decode-batch GEMV's (path 0: signed bytes) or the prefill GEMM's
+// (path 1: byte sums as f16 subnormals) operand conversion, and writes q[out][in] as int16
+// recovered from those operands.
 template <int K>
 __global__ __launch_bounds__(256) void trellis_decode_kernel(const uint32_t* __restrict__ codes,
                                                              int out, int in,
@@ -283,22 +295,26 @@ __global__ __launch_bounds__(256) void trellis_decode_kernel(const uint32_t* __r
   decode_col<K>(cw, lo.sh3, M);
   int16_t* row = q + (size_t)(strip * 16 + n) * in + (ti0 + g) * 16;
   if (path == 0) {
-    // the operands the matrix cores receive: V[r] holds inputs r (high half) and r + 8
-    // (low half) as the f16 subnormals (q + 255) * 2^-24
+    // operand register r: bytes [lo8 - 128, hi8 - 128] of input r + 8, then of input r;
+    // q = (lo8 - 128) + (hi8 - 128) + 1
+    uint32_t B[8];
+    i8_operands<K>(M, B);
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      const int8_t b0 = (int8_t)(B[r] & 0xFF), b1 = (int8_t)((B[r] >> 8) & 0xFF);
+      const int8_t b2 = (int8_t)((B[r] >> 16) & 0xFF), b3 = (int8_t)(B[r] >> 24);
+      row[r] = (int16_t)(b2 + b3 + 1);
+      row[r + 8] = (int16_t)(b0 + b1 + 1);
+    }
+  } else {
+    // V[r] holds inputs r (high half) and r + 8 (low half) as the f16 subnormals
+    // (q + 255) * 2^-24
     uint32_t V[8];
     byte_sums<K>(M, V);
 #pragma unroll
     for (int r = 0; r < 8; ++r) {
-      row[r] = (int16_t)(f16_bits_to_f32(V[r] >> 16) * GEMV_BYTE_SCALE - GEMV_BYTE_OFFSET);
-      row[r + 8] = (int16_t)(f16_bits_to_f32(V[r]) * GEMV_BYTE_SCALE - GEMV_BYTE_OFFSET);
-    }
-  } else {
-    uint32_t nat[8];
-    mpairs_to_bf16_natural<K>(M, nat);
-#pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      row[2 * t] = (int16_t)bf16_lo_to_f32(nat[t]);
-      row[2 * t + 1] = (int16_t)bf16_hi_to_f32(nat[t]);
+      row[r] = (int16_t)(f16_bits_to_f32(V[r] >> 16) * BYTE_SUM_SCALE - BYTE_SUM_OFFSET);
+      row[r + 8] = (int16_t)(f16_bits_to_f32(V[r]) * BYTE_SUM_SCALE - BYTE_SUM_OFFSET);
     }
   }
 }
