@@ -392,15 +392,28 @@ __device__ void prep_block(const PlanArgs& a, int t) {
       a.rowsum[t] = s;
     }
   } else {
-    // pass 1: the largest magnitude (non-finite elements flagged as +inf)
+    // pass 1: the largest magnitude (non-finite elements flagged as +inf); with at most
+    // one column per thread the rotated column stays in registers for pass 2
+    const bool one = n_ti <= PLAN_THREADS;
+    float f0[16];
     float amax = 0.0f;
-    for (int c = tid; c < n_ti; c += PLAN_THREADS) {
-      float f[16];
-      load_column(a, t, c, f);
+    auto fold_max = [&](const float f[16]) {
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
         const float m = fabsf(f[j]);
         amax = fmaxf(amax, m <= 3.4e38f ? m : __builtin_inff());
+      }
+    };
+    if (one) {
+      if (tid < n_ti) {
+        load_column(a, t, tid, f0);
+        fold_max(f0);
+      }
+    } else {
+      for (int c = tid; c < n_ti; c += PLAN_THREADS) {
+        float f[16];
+        load_column(a, t, c, f);
+        fold_max(f);
       }
     }
     amax = block_max(amax, s_red, nw);
@@ -414,9 +427,7 @@ __device__ void prep_block(const PlanArgs& a, int t) {
     }
     // pass 2: integers, halves, operand layout
     int isum = 0;
-    for (int c = tid; c < n_ti; c += PLAN_THREADS) {
-      float f[16];
-      load_column(a, t, c, f);
+    auto quantize = [&](const float f[16], int c) {
       int hi[16], lo[16];
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
@@ -441,6 +452,15 @@ __device__ void prep_block(const PlanArgs& a, int t) {
       dh[1] = make_uint4(H[4], H[5], H[6], H[7]);
       dl[0] = make_uint4(L[0], L[1], L[2], L[3]);
       dl[1] = make_uint4(L[4], L[5], L[6], L[7]);
+    };
+    if (one) {
+      if (tid < n_ti) quantize(f0, tid);
+    } else {
+      for (int c = tid; c < n_ti; c += PLAN_THREADS) {
+        float f[16];
+        load_column(a, t, c, f);
+        quantize(f, c);
+      }
     }
 #pragma unroll
     for (int d = 32; d >= 1; d >>= 1) isum += __shfl_xor(isum, d, 64);
