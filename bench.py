@@ -79,7 +79,7 @@ def time_graph_steps(torch, graphs, steps, warmup):
     return (time.perf_counter() - t0) / steps
 
 
-GEMV_SOURCES = ["trellis_gemv.hip", "trellis_decode.h", "gemv_plan.h", "tq_device.h",
+GEMV_SOURCES = ["trellis_gemv.hip", "trellis_decode.h", "gemv_plan.h", "gemv_wave.h", "tq_device.h",
                 "tq_internal.h"]
 
 

@@ -9,7 +9,6 @@
 #include <string>
 
 #include "tq.h"
-#include "gemv_common.h"
 #include "gemv_plan.h"
 #include "tq_internal.h"
 
@@ -79,15 +78,6 @@ bool use_gemm(int64_t T, int topk, int E, uint32_t flags) {
   return T * topk > 16LL * E;
 }
 
-// Largest number of steps per workgroup (a divisor of units, at most max_steps) that still
-// leaves at least target K-slices; 1 if none does.
-int pick_steps(int units, int max_steps, int target_slices) {
-  int best = 1;
-  for (int d = 1; d <= max_steps; ++d)
-    if (units % d == 0 && units / d >= target_slices) best = d;
-  return best;
-}
-
 int check_routes(int64_t T, int topk, const void* ids) {
   if (T < 0) return fail(TQ_EINVAL, "T = %lld is negative", (long long)T);
   if (topk < 1 || topk > 64) return fail(TQ_EINVAL, "topk = %d is outside 1..64", topk);
@@ -128,11 +118,13 @@ WsLayout ws_layout(int64_t T, int topk, int E, int out, int in, uint32_t flags, 
   L.groups = (out + 127) / 128;
   L.gemm = use_gemm(T, topk, E, flags);
   // a decode batch gives every active expert group at least one wave of its own
-  if (!mxfp4 && (flags & 3u) == TQ_AUTO && (int64_t)E * L.groups > tq::GEMV_MAX_G) L.gemm = true;
+  if ((flags & 3u) == TQ_AUTO && (int64_t)E * L.groups > tq::GEMV_MAX_G) L.gemm = true;
   size_t off = 256;  // status word
-  if (!L.gemm && !mxfp4) {
-    // planned decode batch: plan records, prepared activations, per-piece partial sums
-    const size_t Q = (size_t)in / 256;
+  if (!L.gemm) {
+    // planned decode batch: plan records, prepared activations (trellis), per-piece partial
+    // sums (at most in / 256 pieces per slot for trellis steps of 64 inputs, in / 512 for
+    // MXFP4 steps of 128)
+    const size_t Q = (size_t)in / (mxfp4 ? 512 : 256);
     L.info = off;
     off += 256;
     L.rec = off;
@@ -145,27 +137,17 @@ WsLayout ws_layout(int64_t T, int topk, int E, int out, int in, uint32_t flags, 
     off += round_up((size_t)N * 16, 256);
     L.prank = off;
     off += round_up((size_t)N * 4, 256);
-    L.xq = off;
-    off += round_up((size_t)T * in * 4, 256);
-    L.xscale = off;
-    off += round_up((size_t)T * 4, 256);
-    L.xsum = off;
-    off += round_up((size_t)T * 4, 256);
+    if (!mxfp4) {
+      L.xq = off;
+      off += round_up((size_t)T * in * 4, 256);
+      L.xscale = off;
+      off += round_up((size_t)T * 4, 256);
+      L.xsum = off;
+      off += round_up((size_t)T * 4, 256);
+    }
     L.partial = off;
     L.partial_bytes = round_up(Q * N * out * 4, 256);
     off += L.partial_bytes;
-  } else if (!L.gemm) {
-    const int64_t active = N < E ? N : E;
-    const int64_t wgs_per_slice = (active > 0 ? active : 1) * L.groups;
-    const int target = (int)((1024 + wgs_per_slice - 1) / wgs_per_slice);
-    const int units = in / 512;
-    L.gemv_steps = pick_steps(units, 2, target);
-    L.gemv_slices = units / L.gemv_steps;
-    if (L.gemv_slices > 1) {
-      L.partial = off;
-      L.partial_bytes = round_up((size_t)L.gemv_slices * N * out * 4, 256);
-      off += L.partial_bytes;
-    }
   } else {
     L.route_blocks = (int)((N + ROUTE_CHUNK - 1) / ROUTE_CHUNK);
     L.max_items = (int)((N + GEMM_MT - 1) / GEMM_MT) + E;
@@ -192,7 +174,7 @@ WsLayout ws_layout(int64_t T, int topk, int E, int out, int in, uint32_t flags, 
       off += round_up((size_t)T * 4, 256);
     }
   }
-  if ((flags & TQ_COMBINE) && (L.gemm || (mxfp4 && L.gemv_slices == 1))) {
+  if ((flags & TQ_COMBINE) && L.gemm) {
     L.slots = off;
     L.slots_bytes = round_up((size_t)N * out * 4, 256);
     off += L.slots_bytes;
@@ -365,7 +347,7 @@ int common_checks(int E, int out, int in, const void* x, int64_t T, const int32_
   *layout = tq::ws_layout(T, topk, E, out, in, flags, mxfp4);
   if ((layout->gemm || !mxfp4) && E > 4096)
     return fail(TQ_EINVAL, "this path supports E <= 4096 (E = %d)", E);
-  if (!layout->gemm && !mxfp4 && (int64_t)E * layout->groups > tq::GEMV_MAX_G)
+  if (!layout->gemm && (int64_t)E * layout->groups > tq::GEMV_MAX_G)
     return fail(TQ_EINVAL, "decode batches take at most %d expert groups (E * out / 128)",
                 tq::GEMV_MAX_G);
   if ((layout->gemm || !mxfp4) && T * (int64_t)in * (layout->gemm ? 2 : 4) >= ((int64_t)1 << 31))
@@ -403,32 +385,6 @@ int run_route(const tq::WsLayout& L, void* ws, const int32_t* ids, int64_t N, in
   return TQ_OK;
 }
 
-// Second launch of the decode-batch path with S > 1 slices: slice sums, epilogue, empty and
-// invalid slots, and (with TQ_COMBINE) the fixed-order sum over slots, straight into y.
-int run_gemv_reduce(const tq::WsLayout& L, void* ws, const int32_t* ids, const uint16_t* scales,
-                    const float* gates, const float* rowsum, float acc_scale, float offset,
-                    float* y, int64_t N, int E, int out, int topk, uint32_t flags,
-                    hipStream_t s) {
-  tq::GemvReduceArgs r{};
-  r.ids = ids;
-  r.partial = at<float>(ws, L.partial);
-  r.scales = scales;
-  r.gates = gates;
-  r.rowsum = rowsum;
-  r.acc_scale = acc_scale;
-  r.offset = offset;
-  r.y = y;
-  r.status = at<uint32_t>(ws, L.status);
-  r.N = (int)N;
-  r.E = E;
-  r.out = out;
-  r.topk = topk;
-  r.S = L.gemv_slices;
-  r.combine = (flags & TQ_COMBINE) ? 1 : 0;
-  hipError_t err = tq::launch_gemv_reduce(r, s);
-  if (err != hipSuccess) return hip_fail(err, "GEMV slice reduction launch");
-  return TQ_OK;
-}
 
 }  // namespace
 
@@ -575,33 +531,63 @@ int mxfp4_expert_gemm(const tq_mxfp4_layer* L, const void* x, int64_t T,
   const uint16_t* xb = static_cast<const uint16_t*>(x);
   hipError_t err;
   if (!W.gemm) {
+    const int G = tq::mxfp4_gemv_grid();
+    if (G <= 0) return fail(TQ_EHIP, "could not size the GEMV grid");
+    const int Gl = (int)std::max<int64_t>(G, (int64_t)L->E * W.groups);
+    tq::PlanArgs p{};
+    p.ids = topk_ids;
+    p.N = (int)N;
+    p.E = L->E;
+    p.topk = topk;
+    p.bits = nullptr;  // every step costs 1
+    p.unit_bytes = (int64_t)L->out * L->in / 2 + (int64_t)L->out * L->in / 32;
+    p.groups = W.groups;
+    p.S = L->in / 128;
+    p.G = G;
+    p.Gl = Gl;
+    p.info = at<int32_t>(ws, W.info);
+    p.rec = at<tq::PlanRec>(ws, W.rec);
+    p.desc = at<int4>(ws, W.desc);
+    p.list = at<int32_t>(ws, W.list);
+    p.slot_info = at<int4>(ws, W.slot_info);
+    p.rank = at<int32_t>(ws, W.prank);
+    p.status = at<uint32_t>(ws, W.status);
+    p.x = nullptr;  // no activation prep: the GEMV reads bf16 x
+    err = tq::launch_gemv_plan(p, s);
+    if (err != hipSuccess) return hip_fail(err, "decode plan launch");
     tq::Mxfp4GemvArgs a{};
     a.units = L->units;
     a.x = xb;
-    a.ids = topk_ids;
-    a.gates = topk_w;
-    a.y = y_slots;
-    a.partial = W.gemv_slices > 1 ? at<float>(ws, W.partial) : nullptr;
-    a.status = at<uint32_t>(ws, W.status);
-    a.E = L->E;
+    a.x_bytes = (uint32_t)(T * L->in * 2);
+    a.rec = p.rec;
+    a.desc = p.desc;
+    a.list = p.list;
+    a.partial = at<float>(ws, W.partial);
+    a.N = (int)N;
     a.out = L->out;
     a.in = L->in;
     a.topk = topk;
-    a.S = W.gemv_slices;
-    a.steps = W.gemv_steps;
-    a.groups = W.groups;
-    a.N = N;
+    a.G = Gl;
     err = time_begin(s);
     if (err != hipSuccess) return hip_fail(err, "hipEventRecord");
     err = tq::launch_mxfp4_gemv(a, s);
     if (err == hipSuccess) err = time_end(s);
     if (err != hipSuccess) return hip_fail(err, "MXFP4 GEMV launch");
-    if (W.gemv_slices > 1) {
-      rc = run_gemv_reduce(W, ws, topk_ids, nullptr, topk_w, nullptr, 1.0f, 0.0f, y, N, L->E,
-                           L->out, topk, flags, s);
-      if (rc) return rc;
-      return ok();
-    }
+    tq::PieceReduceArgs r{};
+    r.slot_info = p.slot_info;
+    r.partial = a.partial;
+    r.scales = nullptr;
+    r.gates = topk_w;
+    r.xsum = nullptr;
+    r.xscale = nullptr;
+    r.y = y;
+    r.N = (int)N;
+    r.out = L->out;
+    r.topk = topk;
+    r.combine = (flags & TQ_COMBINE) ? 1 : 0;
+    err = tq::launch_piece_reduce(r, s);
+    if (err != hipSuccess) return hip_fail(err, "GEMV piece reduction launch");
+    return ok();
   } else {
     rc = run_route(W, ws, topk_ids, N, L->E, L->out, y_slots, s);
     if (rc) return rc;

@@ -1,61 +1,8 @@
-// Second launch of the decode-batch path when the K range is split into S slices: for each
-// output, the S slice partials are added in slice order, scaled by acc_scale, corrected by
-// offset * rowsum[token] (the trellis byte encoding), then the per-channel scale and the
-// gate are applied. Empty slots (-1) give 0; ids outside [-1, E) give NaN and set the
-// status bit. With combine, y[t][o] = sum over k = 0..topk-1 (in order) of the slot values.
-#include "gemv_common.h"
-
-namespace tq {
-
-namespace {
-
-__device__ __forceinline__ float slot_value(const GemvReduceArgs& a, int slot, int o) {
-  const int id = a.ids[slot];
-  if (id == -1) return 0.0f;
-  if (id < -1 || id >= a.E) {
-    set_status(a.status, STATUS_BAD_EXPERT);
-    return __builtin_nanf("");
-  }
-  const size_t stride = (size_t)a.N * a.out;
-  const float* p = a.partial + (size_t)slot * a.out + o;
-  float sum = p[0];
-  for (int s = 1; s < a.S; ++s) sum += p[(size_t)s * stride];
-  float val = sum * a.acc_scale;
-  if (a.rowsum) val = val - a.offset * a.rowsum[slot / a.topk];
-  return gemv_epilogue(a.scales, a.gates, a.out, id, o, slot, val);
-}
-
-__global__ __launch_bounds__(256) void gemv_reduce_kernel(GemvReduceArgs a) {
-  const int rows = a.combine ? a.N / a.topk : a.N;
-  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (idx >= (int64_t)rows * a.out) return;
-  const int r = (int)(idx / a.out), o = (int)(idx % a.out);
-  if (!a.combine) {
-    a.y[idx] = slot_value(a, r, o);
-    return;
-  }
-  float acc = 0.0f;
-  for (int k = 0; k < a.topk; ++k) acc += slot_value(a, r * a.topk + k, o);
-  a.y[idx] = acc;
-}
-
-}  // namespace
-
-hipError_t launch_gemv_reduce(const GemvReduceArgs& a, hipStream_t s) {
-  const int rows = a.combine ? a.N / a.topk : a.N;
-  const int64_t total = (int64_t)rows * a.out;
-  if (total == 0) return hipSuccess;
-  hipLaunchKernelGGL(gemv_reduce_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, a);
-  return hipGetLastError();
-}
-
-}  // namespace tq
-
-// ---- piece reduction (trellis decode batches) ---------------------------------------------
-// Third launch of the planned decode-batch path (gemv_plan.h). A slot's expert group was
-// split into pieces by the plan; their partial sums (of x * (q - 1), x the token's 16-bit
-// integers) are added in piece order, the token's sum of x is added back and the token's
-// 2^-e applied, then the per-channel scale and the gate. Empty
+// Piece reduction: the third launch of the planned decode batches (gemv_plan.h), trellis and
+// MXFP4. A slot's expert group was split into pieces by the plan; their partial sums are
+// added in piece order. For trellis layers those sums are of x * (q - 1) with x the
+// token's 16-bit integers: the token's sum of x is added back and the token's 2^-e
+// applied, then the per-channel fp16 scale; MXFP4 sums are final. Then the gate. Empty
 // slots give 0, bad ids and bad units NaN (their status bits were set by the plan). Without
 // combine, one thread per 4 outputs of a slot; with combine, one block per (token, 128
 // outputs) puts the slot values in LDS and adds them over k = 0..topk-1 in order.
@@ -76,7 +23,8 @@ __device__ __forceinline__ void add4(float4& s, const float4& v) {
 __device__ __forceinline__ float4 piece_slot(const PieceReduceArgs& a, int slot, int o) {
   const int4 inf = a.slot_info[slot];
   const int t = slot / a.topk;
-  const float add = (float)a.xsum[t], mul = a.xscale[t];
+  const float add = a.xsum ? (float)a.xsum[t] : 0.0f;
+  const float mul = a.xscale ? a.xscale[t] : 1.0f;
   const float gate = a.gates ? a.gates[slot] : 1.0f;
   if (inf.x == SLOT_EMPTY) return make_float4(0.f, 0.f, 0.f, 0.f);
   if (inf.x < 0) {
@@ -86,7 +34,8 @@ __device__ __forceinline__ float4 piece_slot(const PieceReduceArgs& a, int slot,
   const int e = inf.x, np = inf.y;
   const size_t stride = (size_t)a.N * a.out;
   const float* p = a.partial + (size_t)slot * a.out + o;
-  const uint2 sc = *reinterpret_cast<const uint2*>(a.scales + (size_t)e * a.out + o);
+  const uint2 sc = a.scales ? *reinterpret_cast<const uint2*>(a.scales + (size_t)e * a.out + o)
+                           : make_uint2(0x3C003C00u, 0x3C003C00u);  // fp16 1.0
   // pieces are requested eight at a time (clamped indices, unused ones dropped) and added
   // in piece order
   float4 s = make_float4(0.f, 0.f, 0.f, 0.f);

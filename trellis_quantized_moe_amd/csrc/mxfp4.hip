@@ -6,7 +6,7 @@
 // dword of 8 codes becomes 4 bf16 pairs in 4 instructions; E2M1 * 2^e is exact in bf16
 // for every finite E8M0 scale, so decoding is bit-exact.
 #include "gemm_core.h"
-#include "gemv_common.h"
+#include "gemv_wave.h"
 #include "tq_internal.h"
 
 namespace tq {
@@ -47,118 +47,149 @@ __global__ __launch_bounds__(256) void mxfp4_decode_kernel(const uint8_t* __rest
 }
 
 // ---- decode-batch GEMV -------------------------------------------------------------------
-// One workgroup (4 waves) per (expert, group of 8 strips, K-slice). The slice's activations
-// of the chunk's tokens sit in LDS as bf16 rows. Per step a wave covers 128 inputs: lane
-// (g, n) loads 32 codes (16 bytes) of output n, inputs 32g .. 32g+31 of the step, plus the
-// dword of scales of the step's 4 blocks, and feeds 4 matrix-core operations; operation c
-// takes inputs 32g + 8c .. +7 of every lane group, and the A operand is read to match.
-constexpr int MX_MAX_STEPS = 4;                            // 128-input steps per wave
-constexpr int MX_SLICE_MAX = 4 * 128 * MX_MAX_STEPS;       // inputs per workgroup
-constexpr int MX_ROW = MX_SLICE_MAX + 8;                   // bf16 per LDS row (+16 B pad)
-constexpr int MX_SMEM_A_WORDS = 16 * MX_ROW / 2;
-constexpr int MX_SMEM_RED_WORDS = 4 * 8 * 4 * 64;
-constexpr int MX_SMEM_WORDS =
-    MX_SMEM_A_WORDS > MX_SMEM_RED_WORDS ? MX_SMEM_A_WORDS : MX_SMEM_RED_WORDS;
+// One wave is one worker of the plan (gemv_plan.h, every step costing 1): wave w streams its
+// piece, 128-input steps s0 .. s1 - 1 of one group of 8 strips (128 output channels) of one
+// expert, on its own. Per step and strip, lane (g, n) loads 32 codes (16 bytes) of output
+// n, inputs 32 g .. 32 g + 31 of the step, takes that block's scale, and feeds 4 bf16
+// 16 x 16 x 32 matrix-core operations: operation c takes inputs 32 g + 8 c .. + 7 of every
+// lane group, against the same inputs of up to 16 routed token rows (bf16 x as given; rows
+// past the expert's count are zero). Codes and activations are requested D steps ahead,
+// into register sets used in turn. The scales come in blocks of 4 steps: two 16-byte loads
+// per lane bring the 128 rows' 16 scale bytes of the next block into registers, which go to
+// a double-buffered LDS stage (2 KB per block) at the block boundary; each lane then reads
+// its byte per strip and step from LDS, so a step issues no scale load of its own. At the
+// end the wave stores its accumulators as the piece's partial sums.
+constexpr int MX_THREADS = 64;
+constexpr int MX_WAVES_PER_SIMD = 3;
+constexpr int MX_D = 1;
 
-struct MxShared {
-  uint32_t buf[MX_SMEM_WORDS];
-  SlotChunk ch;
+struct MxStep {
+  u32x4 code[8];
+  u32x4 x[4];
 };
 
-__device__ int mx_run_expert(const Mxfp4GemvArgs& a, const GemvCommon& c, MxShared& sh, int e,
-                             int grp, int s, int ns) {
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, n = lane & 15;
-  const int slice = 512 * a.steps;
-  const int kbase = s * slice;
-  const int row_stride = slice + 8;  // bf16
-  const size_t unit_bytes = (size_t)a.out * a.in / 2 + (size_t)a.out * a.in / 32;
-  const uint8_t* unit = a.units + (size_t)e * unit_bytes;
-  const uint8_t* scales = unit + (size_t)a.out * a.in / 2;
-  uint16_t* A = reinterpret_cast<uint16_t*>(sh.buf);
-  int pos = 0, found = 0;
-  while (true) {
-    collect_slots(a.ids, c.N, e, pos, sh.ch);
-    const int cnt = sh.ch.cnt;
-    if (cnt == 0) break;
-    found += cnt;
-    pos = sh.ch.next;
-    // stage A: 16 rows x slice bf16, 16 bytes per task
-    const int chunks = slice / 8;
-    for (int task = tid; task < 16 * chunks; task += GEMV_THREADS) {
-      const int m = task / chunks, q = task % chunks;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (m < cnt) {
-        const int tok = sh.ch.slots[m] / a.topk;
-        v = *reinterpret_cast<const uint4*>(a.x + (size_t)tok * a.in + kbase + 8 * q);
-      }
-      *reinterpret_cast<uint4*>(A + (size_t)m * row_stride + 8 * q) = v;
-    }
-    __syncthreads();
-    f32x4 acc[8];
+struct MxShared {
+  alignas(16) uint8_t sc[2][128 * 16];  // [buffer][row][step of the block][block of the step]
+};
+
+template <bool RELOAD>
+__device__ __forceinline__ void mx_step(MxStep& cur, const uint8_t* sc, Rsrc ru, uint32_t cvo,
+                                        const uint32_t cso[8], uint32_t cst, Rsrc rx,
+                                        uint32_t xvo, uint32_t xst, f32x4 acc[8]) {
+  // sc: this lane's scale byte of strip 0 for this step (strip s8 at + 256 s8)
+  // each reload replaces the registers of the value it follows, after that value's last use
 #pragma unroll
-    for (int s8 = 0; s8 < 8; ++s8) acc[s8] = (f32x4){0.f, 0.f, 0.f, 0.f};
-    for (int st = 0; st < a.steps; ++st) {
-      const int k0 = w * 128 * a.steps + 128 * st;  // within the slice
-      u32x4 Aop[4];
+  for (int s8 = 0; s8 < 8; ++s8) {
+    const float scale = e8m0_to_f32(sc[256 * s8]);
+    uint32_t b[4][4];
 #pragma unroll
-      for (int cc = 0; cc < 4; ++cc)
-        Aop[cc] = *reinterpret_cast<const u32x4*>(A + (size_t)n * row_stride + k0 + 32 * g + 8 * cc);
-      const int kg = kbase + k0;  // global input of the step
+    for (int c = 0; c < 4; ++c) fp4x8_to_bf16(cur.code[s8][c], scale, b[c]);
+    __builtin_amdgcn_sched_barrier(0);
+    if (RELOAD) cur.code[s8] = __builtin_amdgcn_raw_buffer_load_b128(ru, cvo, cso[s8] + cst, 0);
 #pragma unroll
-      for (int s8 = 0; s8 < 8; ++s8) {
-        if (s8 < ns) {
-          const int o = grp * 128 + 16 * s8 + n;
-          const uint4 cw = *reinterpret_cast<const uint4*>(unit + (size_t)o * (a.in / 2) +
-                                                           (kg + 32 * g) / 2);
-          const uint32_t sw = *reinterpret_cast<const uint32_t*>(scales + (size_t)o * (a.in / 32) +
-                                                                 kg / 32);
-          const float sc = e8m0_to_f32((sw >> (8 * g)) & 0xFFu);
-          const uint32_t cws[4] = {cw.x, cw.y, cw.z, cw.w};
-#pragma unroll
-          for (int cc = 0; cc < 4; ++cc) {
-            uint32_t b[4];
-            fp4x8_to_bf16(cws[cc], sc, b);
-            acc[s8] = mfma_bf16(Aop[cc], (u32x4){b[0], b[1], b[2], b[3]}, acc[s8]);
-          }
-        }
-      }
-    }
-    __syncthreads();
-    gemv_reduce_store(c, reinterpret_cast<float*>(sh.buf), acc, sh.ch, e, grp, s, ns);
-    if (pos >= c.N) break;
+    for (int c = 0; c < 4; ++c)
+      acc[s8] = mfma_bf16(cur.x[c], (u32x4){b[c][0], b[c][1], b[c][2], b[c][3]}, acc[s8]);
   }
-  return found;
+  __builtin_amdgcn_sched_barrier(0);
+  if (RELOAD) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) cur.x[c] = __builtin_amdgcn_raw_buffer_load_b128(rx, xvo, xst + 16u * c, 0);
+  }
 }
 
-__global__ __launch_bounds__(GEMV_THREADS) void mxfp4_gemv_kernel(Mxfp4GemvArgs a) {
-  __shared__ MxShared sh;
-  GemvCommon c;
-  c.ids = a.ids;
-  c.gates = a.gates;
-  c.scales = nullptr;
-  c.rowsum = nullptr;
-  c.acc_scale = 1.0f;
-  c.offset = 0.0f;
-  c.y = a.y;
-  c.partial = a.partial;
-  c.N = (int)a.N;
-  c.E = a.E;
-  c.out = a.out;
-  c.topk = a.topk;
-  c.S = a.S;
-  c.groups = a.groups;
-  const int work = a.E * a.groups * a.S;
-  const int bid = blockIdx.x;
-  if (bid == work) {
-    special_slots(a.ids, c.N, a.E, a.out, a.y, a.status);
-    return;
+__device__ __forceinline__ void mx_stream(const Mxfp4GemvArgs& a, MxShared& sh, Rsrc ru, int tok,
+                                          int grp, int ns, int s0, int s1, f32x4 acc[8]) {
+  const int lane = threadIdx.x & 63, g = lane >> 4, n = lane & 15;
+  const uint32_t row = (uint32_t)a.in / 2, srow = (uint32_t)a.in / 32;
+  const uint32_t cvo = n * row + 16u * g;  // code byte of output n, block g
+  uint32_t cso[8];
+#pragma unroll
+  for (int s8 = 0; s8 < 8; ++s8)
+    cso[s8] = (uint32_t)(grp * 128 + 16 * (s8 < ns ? s8 : ns - 1)) * row;
+  // scale blocks: lane L brings rows L and L + 64 (16 bytes each: 4 steps x 4 blocks)
+  const uint32_t svo0 = (uint32_t)a.out * row + (uint32_t)(grp * 128 + lane) * srow;
+  const uint32_t svo1 = svo0 + 64u * srow;
+  const Rsrc rx = make_rsrc(a.x, a.x_bytes);
+  const uint32_t xvo = tok >= 0 ? (uint32_t)tok * (uint32_t)a.in * 2u + 64u * g : 0x80000000u;
+  const int steps = s1 - s0, last = steps - 1;
+  // scalar offsets of step st (clamped to the last step, whose data is read again)
+  auto cst = [&](int st) { return 64u * (uint32_t)(s0 + (st < last ? st : last)); };
+  auto xst = [&](int st) { return 256u * (uint32_t)(s0 + (st < last ? st : last)); };
+  auto bso = [&](int blk) { return 16u * (uint32_t)blk + 4u * (uint32_t)s0; };  // 4-step block
+  MxStep ring[MX_D];
+#pragma unroll
+  for (int d = 0; d < MX_D; ++d)
+#pragma unroll
+    for (int s8 = 0; s8 < 8; ++s8)
+      ring[d].code[s8] = __builtin_amdgcn_raw_buffer_load_b128(ru, cvo, cso[s8] + cst(d), 0);
+  u32x4 sa = __builtin_amdgcn_raw_buffer_load_b128(ru, svo0, bso(0), 0);
+  u32x4 sb = __builtin_amdgcn_raw_buffer_load_b128(ru, svo1, bso(0), 0);
+#pragma unroll
+  for (int d = 0; d < MX_D; ++d)
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      ring[d].x[c] = __builtin_amdgcn_raw_buffer_load_b128(rx, xvo, xst(d) + 16u * c, 0);
+#pragma unroll
+  for (int s8 = 0; s8 < 8; ++s8) acc[s8] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  // this lane's scale byte: row n of strip 0, step k of the block, block g of the step
+  const int sbase = 16 * n + g;
+  int st = 0;
+  for (int blk = 0; blk < steps; blk += 4) {
+    const int buf = (blk >> 2) & 1;
+    *reinterpret_cast<u32x4*>(&sh.sc[buf][16 * lane]) = sa;
+    *reinterpret_cast<u32x4*>(&sh.sc[buf][16 * (lane + 64)]) = sb;
+    if (blk + 4 < steps) {  // the next block's scales, in flight during this block
+      sa = __builtin_amdgcn_raw_buffer_load_b128(ru, svo0, bso(blk + 4), 0);
+      sb = __builtin_amdgcn_raw_buffer_load_b128(ru, svo1, bso(blk + 4), 0);
+    }
+#pragma unroll
+    for (int k = 0; k < 4; k += MX_D) {
+      if (st + MX_D <= steps) {
+#pragma unroll
+        for (int d = 0; d < MX_D; ++d)
+          mx_step<true>(ring[d], &sh.sc[buf][sbase + 4 * (k + d)], ru, cvo, cso, cst(st + d + MX_D),
+                        rx, xvo, xst(st + d + MX_D), acc);
+        st += MX_D;
+      } else {
+#pragma unroll
+        for (int d = 0; d < MX_D; ++d)
+          if (st + d < steps)
+            mx_step<false>(ring[d], &sh.sc[buf][sbase + 4 * (k + d)], ru, cvo, cso, 0, rx, xvo,
+                           0, acc);
+        st = steps;
+      }
+    }
   }
-  const int e = bid % a.E;
-  const int rest = bid / a.E;
-  const int grp = rest % a.groups;
-  const int s = rest / a.groups;
-  const int ns = min(8, a.out / 16 - grp * 8);
-  mx_run_expert(a, c, sh, e, grp, s, ns);
+}
+
+__global__ __launch_bounds__(MX_THREADS, MX_WAVES_PER_SIMD) void mxfp4_gemv_kernel(Mxfp4GemvArgs a) {
+  __shared__ MxShared sh;
+  Piece pc;
+  if (!load_piece(a.desc, blockIdx.x, pc)) return;
+  const PlanRec r = load_rec(a.rec, pc.ai);
+  const int lane = threadIdx.x & 63, n = lane & 15, g = lane >> 4;
+  const int ns = min(8, a.out / 16 - pc.grp * 8);
+  const uint32_t unit_bytes = (uint32_t)((size_t)a.out * a.in / 2 + (size_t)a.out * a.in / 32);
+  const Rsrc ru = make_rsrc(a.units + r.off, unit_bytes);
+  float* dst = a.partial + (size_t)pc.idx * a.N * a.out + pc.grp * 128 + n;
+  for (int c0 = 0; c0 < r.cnt; c0 += 16) {
+    const int rows = min(16, r.cnt - c0);
+    const int slot = n < rows ? a.list[r.start + c0 + n] : -1;
+    f32x4 acc[8];
+    mx_stream(a, sh, ru, slot >= 0 ? slot / a.topk : -1, pc.grp, ns, pc.s0, pc.s1, acc);
+    // accumulator element i of lane (g, n) is token row 4 g + i, output channel n of its strip
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int m = 4 * g + i;
+      const int sm = __shfl(slot, m);
+      if (m < rows) {
+        float* rowp = dst + (size_t)sm * a.out;
+#pragma unroll
+        for (int s8 = 0; s8 < 8; ++s8)
+          if (s8 < ns) rowp[s8 * 16] = acc[s8][i];
+      }
+    }
+  }
 }
 
 // ---- prefill GEMM --------------------------------------------------------------------------
@@ -235,9 +266,25 @@ hipError_t launch_mxfp4_decode(const uint8_t* unit, int out, int in, uint16_t* w
   return hipGetLastError();
 }
 
+int mxfp4_gemv_grid() {
+  static int cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (dev >= 0 && dev < 64 && cache[dev]) return cache[dev];
+  int per_cu = 0, cus = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, mxfp4_gemv_kernel, MX_THREADS, 0) !=
+      hipSuccess)
+    return 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  int g = per_cu * cus;
+  if (g > GEMV_MAX_G) g = GEMV_MAX_G;
+  if (g < 1) g = 1;
+  if (dev >= 0 && dev < 64) cache[dev] = g;
+  return g;
+}
+
 hipError_t launch_mxfp4_gemv(const Mxfp4GemvArgs& a, hipStream_t s) {
-  const int blocks = a.E * a.groups * a.S + (a.S == 1 ? 1 : 0);
-  hipLaunchKernelGGL(mxfp4_gemv_kernel, dim3(blocks), dim3(GEMV_THREADS), 0, s, a);
+  hipLaunchKernelGGL(mxfp4_gemv_kernel, dim3(a.G), dim3(MX_THREADS), 0, s, a);
   return hipGetLastError();
 }
 

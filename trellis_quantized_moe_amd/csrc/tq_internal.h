@@ -19,7 +19,7 @@ struct WsLayout {
   size_t xprep = 0, rowsum = 0, xq = 0, xscale = 0, xsum = 0;
   size_t info = 0, rec = 0, desc = 0, list = 0, slot_info = 0, prank = 0;
   size_t total = 0;
-  int gemv_slices = 1, gemv_steps = 1, groups = 1, route_blocks = 1, max_items = 0;
+  int groups = 1, route_blocks = 1, max_items = 0;
   bool gemm = false;
 };
 
@@ -85,10 +85,10 @@ hipError_t launch_trellis_gemv(const TrellisGemvArgs& a, hipStream_t s);
 struct PieceReduceArgs {
   const int4* slot_info;  // {expert, pieces, k, 0} or a SLOT_ code
   const float* partial;
-  const uint16_t* scales;
+  const uint16_t* scales;  // fp16 per output channel, or null
   const float* gates;   // or null
-  const int32_t* xsum;  // [T]: added to each slot's sum (the signed-byte correction)
-  const float* xscale;  // [T]: then multiplied
+  const int32_t* xsum;  // [T]: added to each slot's sum (the signed-byte correction), or null
+  const float* xscale;  // [T]: then multiplied, or null
   float* y;
   int N, out, topk, combine;
 };
@@ -115,15 +115,16 @@ hipError_t launch_trellis_gemm(const TrellisGemmArgs& a, hipStream_t s);
 
 struct Mxfp4GemvArgs {
   const uint8_t* units;
-  const uint16_t* x;
-  const int32_t* ids;
-  const float* gates;
-  float* y;
-  float* partial;
-  uint32_t* status;
-  int E, out, in, topk, S, steps, groups;
-  int64_t N;
+  const uint16_t* x;     // bf16 [T][in]
+  uint32_t x_bytes;      // size of x in bytes (< 2^31)
+  const PlanRec* rec;
+  const int4* desc;      // [G]
+  const int32_t* list;
+  float* partial;        // [in / 512][N][out]: the pieces of each slot
+  int N, out, in, topk, G;
 };
+// Waves of the MXFP4 GEMV that the GPU holds at once; 0 on a HIP error.
+int mxfp4_gemv_grid();
 hipError_t launch_mxfp4_gemv(const Mxfp4GemvArgs& a, hipStream_t s);
 
 struct Mxfp4GemmArgs {

@@ -18,7 +18,7 @@
 //
 // At the end the wave joins each token's two halves (256 hi + lo) and stores the piece's
 // partial sums; the reduction launch adds the pieces in order and applies the epilogue.
-#include "gemv_plan.h"
+#include "gemv_wave.h"
 #include "tq_internal.h"
 #include "trellis_decode.h"
 
@@ -89,15 +89,6 @@ __device__ __forceinline__ void decode_col(const ColWords<K>& cw, uint32_t sh3, 
 }
 
 // ---- buffer loads ------------------------------------------------------------------------
-// The streaming loads address memory as a scalar buffer resource + one per-lane byte offset
-// (fixed for the whole piece) + a scalar offset for the step and strip, so a load costs no
-// vector address arithmetic and no 64-bit address registers.
-typedef __amdgpu_buffer_rsrc_t Rsrc;
-__device__ __forceinline__ Rsrc make_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
-                                           0x00020000);
-}
-
 template <int K>
 __device__ __forceinline__ void load_col_buf(Rsrc r, const uint32_t vo[3], uint32_t so,
                                              ColWords<K>& cw) {
@@ -117,23 +108,6 @@ __device__ __forceinline__ void load_col_buf(Rsrc r, const uint32_t vo[3], uint3
 __device__ __forceinline__ void load_x(Rsrc r, uint32_t vo, uint32_t so, u32x4& xa, u32x4& xb) {
   xa = __builtin_amdgcn_raw_buffer_load_b128(r, vo, so, 0);
   xb = __builtin_amdgcn_raw_buffer_load_b128(r, vo + 16, so, 0);
-}
-
-// Plan records are read through the scalar cache (constant address space): their waits
-// then count on the scalar counter and never on the vector-memory counter that the
-// streaming loads keep busy.
-typedef const __attribute__((address_space(4))) PlanRec* ConstRec;
-__device__ __forceinline__ PlanRec load_rec(const PlanRec* rec, int i) {
-  const ConstRec p = (ConstRec)rec + i;
-  PlanRec r;
-  r.e = p->e;
-  r.start = p->start;
-  r.cnt = p->cnt;
-  r.k = p->k;
-  r.off = p->off;
-  r.wave0 = 0;
-  r.np = 0;
-  return r;
 }
 
 // ---- one step: 4 tile columns of 8 strips ---------------------------------------------
@@ -253,22 +227,16 @@ __device__ __forceinline__ void run_piece(const TrellisGemvArgs& a, const PlanRe
   }
 }
 
-// Pieces are read through the scalar cache, like the plan records.
-typedef const __attribute__((address_space(4))) int4* ConstDesc;
-
 __global__ __launch_bounds__(GEMV_THREADS, GEMV_WAVES_PER_SIMD) void trellis_gemv_kernel(TrellisGemvArgs a) {
-  const ConstDesc dp = (ConstDesc)a.desc + blockIdx.x;
-  const int ai = dp->x;
-  if (ai < 0) return;
-  const int grp = dp->y, piece = dp->z, span = dp->w;
-  const int s0 = span & 0xFFFF, s1 = span >> 16;
-  const PlanRec r = load_rec(a.rec, ai);
+  Piece pc;
+  if (!load_piece(a.desc, blockIdx.x, pc)) return;
+  const PlanRec r = load_rec(a.rec, pc.ai);
   if (r.k == 2)
-    run_piece<2>(a, r, grp, s0, s1, piece);
+    run_piece<2>(a, r, pc.grp, pc.s0, pc.s1, pc.idx);
   else if (r.k == 3)
-    run_piece<3>(a, r, grp, s0, s1, piece);
+    run_piece<3>(a, r, pc.grp, pc.s0, pc.s1, pc.idx);
   else
-    run_piece<4>(a, r, grp, s0, s1, piece);
+    run_piece<4>(a, r, pc.grp, pc.s0, pc.s1, pc.idx);
 }
 
 // ---- decode hook ------------------------------------------------------------------------
