@@ -40,6 +40,22 @@ struct GemmItem {
   int in, out, topk, grp, nrows, ns;
 };
 
+// The work unit of this workgroup. Consecutive workgroups land on the 8 XCDs in turn
+// (workgroup b on XCD b % 8), so the grid is read as 8 interleaved streams and stream x
+// takes a contiguous range of the n_items * groups units: the units of one expert, which
+// read the same weight unit, then share one L2. The grid has gemm_grid() workgroups.
+__device__ inline bool gemm_unit(const int32_t* n_items, int groups, int* item, int* grp) {
+  const int units = *n_items * groups;
+  const int per = (units + 7) >> 3;
+  const int j = blockIdx.x >> 3;
+  const int u = (blockIdx.x & 7) * per + j;
+  if (j >= per || u >= units) return false;
+  *item = u / groups;
+  *grp = u % groups;
+  return true;
+}
+inline int gemm_grid(int max_items, int groups) { return (max_items * groups + 7) & ~7; }
+
 // Load slot indices of the item's rows into LDS (all threads; ends with a barrier).
 __device__ inline void gemm_load_slots(GemmShared& sh, const int32_t* pairs, int row0,
                                        int nrows) {
@@ -74,17 +90,20 @@ __device__ __forceinline__ GemmRsrc gemm_rsrc(const void* base, uint32_t bytes) 
 constexpr int GEMM_RING = 4;
 
 template <class Producer>
-__device__ void gemm_item(const GemmItem& it, GemmShared& sh, Producer& prod) {
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, n = lane & 15;
+__device__ __forceinline__ void gemm_item(const GemmItem& it, GemmShared& sh, Producer& prod) {
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, n = lane & 15;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar branches
   const int wm = w >> 1, wn = w & 1;
   const int nsteps = it.in / GEMM_KS;  // a multiple of 8 (in is a multiple of 256)
   // A staging: thread (a_m, a_h) copies inputs 16 a_h .. + 15 of the step for routed row
-  // a_m (rows past the item's count copy token 0's row; they are never stored). Both
-  // activation layouts keep these 16 inputs in 32 contiguous bytes at the same offset.
+  // a_m. Both activation layouts keep these 16 inputs in 32 contiguous bytes at the same
+  // offset. Rows past the item's count load from beyond the buffer's end (x_bytes < 2^31):
+  // the hardware returns zeros without a memory access, and those rows are never stored.
   const int a_m = tid >> 1, a_h = tid & 1;
-  const int a_tok = a_m < it.nrows ? sh.slot[a_m] / it.topk : 0;
   const GemmRsrc ra = gemm_rsrc(it.x, it.x_bytes);
-  const uint32_t a_vo = 2u * (uint32_t)((size_t)a_tok * it.in + 16 * a_h);
+  const uint32_t a_vo =
+      a_m < it.nrows ? 2u * (uint32_t)((size_t)(sh.slot[a_m] / it.topk) * it.in + 16 * a_h)
+                     : 0x80000000u;
 
   typename Producer::Raw raw[GEMM_RING];
   u32x4 xa0[GEMM_RING], xa1[GEMM_RING];
@@ -94,19 +113,22 @@ __device__ void gemm_item(const GemmItem& it, GemmShared& sh, Producer& prod) {
     xa0[slot] = __builtin_amdgcn_raw_buffer_load_b128(ra, a_vo, 64u * k, 0);
     xa1[slot] = __builtin_amdgcn_raw_buffer_load_b128(ra, a_vo + 16, 64u * k, 0);
   };
-  // decodes the slot into LDS buffer buf, then reuses its registers for step kk_next
+  // decodes the slot into LDS buffer buf, then reuses its registers for step kk_next. The
+  // stores come first: the new loads then write the very registers just read, and every
+  // ring slot stays in the same registers from one loop iteration to the next (a slot
+  // moved between registers would have to wait for all loads in flight).
   auto stage = [&](int slot, int buf, int kk_next) {
     uint32_t nat[8];
     prod.decode(raw[slot], nat);
     const u32x4 v0 = xa0[slot], v1 = xa1[slot];
-    __builtin_amdgcn_sched_barrier(0);
-    load_step(slot, kk_next);
     uint4* da = reinterpret_cast<uint4*>(&sh.a[buf][a_m * GEMM_LDS_STRIDE + 16 * a_h]);
     da[0] = make_uint4(v0.x, v0.y, v0.z, v0.w);
     da[1] = make_uint4(v1.x, v1.y, v1.z, v1.w);
     uint4* db = reinterpret_cast<uint4*>(&sh.b[buf][prod.o * GEMM_LDS_STRIDE + 16 * prod.h]);
     db[0] = make_uint4(nat[0], nat[1], nat[2], nat[3]);
     db[1] = make_uint4(nat[4], nat[5], nat[6], nat[7]);
+    __builtin_amdgcn_sched_barrier(0);
+    load_step(slot, kk_next);
   };
 
   f32x4 acc[4][4];
@@ -136,19 +158,21 @@ __device__ void gemm_item(const GemmItem& it, GemmShared& sh, Producer& prod) {
       for (int nb = 0; nb < 4; ++nb)
         bop[nb] = *reinterpret_cast<const u32x4*>(
             &sh.b[buf][(64 * wn + 16 * nb + n) * GEMM_LDS_STRIDE + 8 * g]);
+      // Row blocks past the item's rows are skipped (a wave-uniform branch). Column blocks
+      // past the group's strips are multiplied anyway: their B rows hold a copy of the last
+      // strip and their results are never stored.
 #pragma unroll
       for (int mb = 0; mb < 4; ++mb) {
         if (mb < mblocks) {
           const u32x4 aop = *reinterpret_cast<const u32x4*>(
               &sh.a[buf][(64 * wm + 16 * mb + n) * GEMM_LDS_STRIDE + 8 * g]);
 #pragma unroll
-          for (int nb = 0; nb < 4; ++nb)
-            if (nb < nblocks) {
-              if constexpr (Producer::kF16)
-                acc[mb][nb] = mfma_f16(aop, bop[nb], acc[mb][nb]);
-              else
-                acc[mb][nb] = mfma_bf16(aop, bop[nb], acc[mb][nb]);
-            }
+          for (int nb = 0; nb < 4; ++nb) {
+            if constexpr (Producer::kF16)
+              acc[mb][nb] = mfma_f16(aop, bop[nb], acc[mb][nb]);
+            else
+              acc[mb][nb] = mfma_bf16(aop, bop[nb], acc[mb][nb]);
+          }
         }
       }
       lds_barrier();

@@ -232,9 +232,8 @@ struct Mxfp4Producer {
 
 __global__ __launch_bounds__(GEMM_THREADS, 2) void mxfp4_gemm_kernel(Mxfp4GemmArgs a) {
   __shared__ GemmShared sh;
-  const int item = blockIdx.x / a.groups;
-  const int grp = blockIdx.x % a.groups;
-  if (item >= *a.n_items) return;
+  int item, grp;
+  if (!gemm_unit(a.n_items, a.groups, &item, &grp)) return;
   const int4 itd = reinterpret_cast<const int4*>(a.items)[item];
   const int e = itd.x;
   gemm_load_slots(sh, a.pairs, itd.y, itd.z);
@@ -289,7 +288,7 @@ hipError_t launch_mxfp4_gemv(const Mxfp4GemvArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_mxfp4_gemm(const Mxfp4GemmArgs& a, hipStream_t s) {
-  const int blocks = a.max_items * a.groups;
+  const int blocks = gemm_grid(a.max_items, a.groups);
   if (blocks == 0) return hipSuccess;
   hipLaunchKernelGGL(mxfp4_gemm_kernel, dim3(blocks), dim3(GEMM_THREADS), 0, s, a);
   return hipGetLastError();
