@@ -277,17 +277,54 @@ __device__ void plan_block(const PlanArgs& a) {
 // column c held by this lane: signs, then fp32 butterflies (a, b) -> (a + b, a - b) with
 // strides 1, 2, 4, 8 inside the lane and 16, 32, 64 across lanes c ^ 1, 2, 4 (the 8 lanes
 // of one 128-block), then x 0x3DB504F3 and bf16 round-to-nearest-even. Every stage is the
-// same fp32 operation on the same values as in hadamard128, so the bits are the same.
-__device__ __forceinline__ void rotate_column(float f[16], const int8_t* signs, int c) {
-  if (signs) {
-    const uint4 sg = *reinterpret_cast<const uint4*>(signs + 16 * c);
-    const uint32_t s4[4] = {sg.x, sg.y, sg.z, sg.w};
+// same fp32 operation on the same values as in hadamard128, so the bits are the same: a
+// sign is applied by flipping the sign bit, and the upper lane of a cross-lane pair forms
+// a - b as (-b) + a.
+
+// Sign-bit masks of the 16 signs of column c (0 or 0x80000000), or zeros without signs.
+__device__ __forceinline__ void sign_masks(const int8_t* signs, int c, uint32_t m[16]) {
+  if (!signs) {
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const int8_t sj = (int8_t)((s4[j >> 2] >> (8 * (j & 3))) & 0xFF);
-      if (sj < 0) f[j] = -f[j];
-    }
+    for (int j = 0; j < 16; ++j) m[j] = 0;
+    return;
   }
+  const uint4 sg = *reinterpret_cast<const uint4*>(signs + 16 * c);
+  const uint32_t s4[4] = {sg.x, sg.y, sg.z, sg.w};
+#pragma unroll
+  for (int j = 0; j < 16; ++j) m[j] = (s4[j >> 2] << (24 - 8 * (j & 3))) & 0x80000000u;
+}
+
+// The value of lane l ^ D (D = 1, 2, 4; all lanes of the 8-lane group active), by DPP:
+// quad permutations for 1 and 2, a quad reversal then a half-row mirror for 4.
+template <int D>
+__device__ __forceinline__ float lane_xor(float v) {
+  int x = __float_as_int(v);
+  if constexpr (D == 1) {
+    x = __builtin_amdgcn_mov_dpp(x, 0xB1, 0xF, 0xF, true);  // quad_perm [1, 0, 3, 2]
+  } else if constexpr (D == 2) {
+    x = __builtin_amdgcn_mov_dpp(x, 0x4E, 0xF, 0xF, true);  // quad_perm [2, 3, 0, 1]
+  } else {
+    static_assert(D == 4, "lane_xor: D is 1, 2 or 4");
+    x = __builtin_amdgcn_mov_dpp(x, 0x1B, 0xF, 0xF, true);   // quad_perm [3, 2, 1, 0]
+    x = __builtin_amdgcn_mov_dpp(x, 0x141, 0xF, 0xF, true);  // row_half_mirror
+  }
+  return __int_as_float(x);
+}
+
+template <int D>
+__device__ __forceinline__ void cross_stage(float f[16], int c) {
+  const uint32_t up = (c & D) ? 0x80000000u : 0u;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const float other = lane_xor<D>(f[j]);
+    f[j] = __uint_as_float(__float_as_uint(f[j]) ^ up) + other;
+  }
+}
+
+// Signs and butterflies, then the scale; the caller rounds to bf16.
+__device__ __forceinline__ void rotate_column_f32(float f[16], const uint32_t m[16], int c) {
+#pragma unroll
+  for (int j = 0; j < 16; ++j) f[j] = __uint_as_float(__float_as_uint(f[j]) ^ m[j]);
 #pragma unroll
   for (int h = 1; h < 16; h <<= 1) {
 #pragma unroll
@@ -299,18 +336,18 @@ __device__ __forceinline__ void rotate_column(float f[16], const int8_t* signs, 
       }
     }
   }
-#pragma unroll
-  for (int d = 1; d < 8; d <<= 1) {
-    const bool upper = (c & d) != 0;
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const float other = __shfl_xor(f[j], d, 64);
-      f[j] = upper ? other - f[j] : f[j] + other;
-    }
-  }
+  cross_stage<1>(f, c);
+  cross_stage<2>(f, c);
+  cross_stage<4>(f, c);
   const float scale = __uint_as_float(0x3DB504F3u);
 #pragma unroll
-  for (int j = 0; j < 16; ++j) f[j] = __uint_as_float(f32_to_bf16_rne(f[j] * scale) << 16);
+  for (int j = 0; j < 16; ++j) f[j] = f[j] * scale;
+}
+
+__device__ __forceinline__ void rotate_column(float f[16], const uint32_t m[16], int c) {
+  rotate_column_f32(f, m, c);
+#pragma unroll
+  for (int j = 0; j < 16; ++j) f[j] = __uint_as_float(f32_to_bf16_rne(f[j]) << 16);
 }
 
 // x~ of tile column c of token t as 16 floats (bf16 values), rotated when asked.
@@ -323,7 +360,11 @@ __device__ __forceinline__ void load_column(const PlanArgs& a, int t, int c, flo
     f[2 * k] = bf16_lo_to_f32(wv[k]);
     f[2 * k + 1] = bf16_hi_to_f32(wv[k]);
   }
-  if (a.rotate) rotate_column(f, a.signs, c);
+  if (a.rotate) {
+    uint32_t m[16];
+    sign_masks(a.signs, c, m);
+    rotate_column(f, m, c);
+  }
 }
 
 // Block-wide reductions over the waves that hold columns (nw of them).
@@ -337,22 +378,17 @@ __device__ __forceinline__ float block_max(float v, float* red, int nw) {
   return m;
 }
 
-// One token per block: thread c converts tile column c (columns c + PLAN_THREADS, ... when
-// in > 16 * PLAN_THREADS), rotating it first when asked. Waves without a column leave at
-// once (a 128-block's 8 columns are always in one wave and all present or all absent).
-//
-// F16 (prefill GEMM operands): f16 pairs, and the token's sum of its f16 values in a fixed
-// order.
-// I8 (decode GEMV operands): the token's scale 2^e is the largest power of two with
+// Decode-GEMV operands of token t, one token per block: thread c converts tile column c
+// (columns c + PLAN_THREADS, ... when in > 16 * PLAN_THREADS), rotating it first when asked.
+// Waves without a column leave at once (a 128-block's 8 columns are always in one wave and
+// all present or all absent). The token's scale 2^e is the largest power of two with
 // max |x~| * 2^e <= 32639; every element becomes the integer x = rint(x~ * 2^e) (ties to
 // even; exact for elements within 2^7 of the maximum), split as x = 256 hi + lo with hi, lo
 // in [-128, 127]. Operand register r of a tile column holds bytes [v[r + 8], v[r + 8], v[r],
 // v[r]] of one half (v = hi, then v = lo: two 32-byte rows per column), matching the
 // weights' signed bytes (trellis_decode.h). The token's sum of the integers x and 2^-e are
 // kept for the epilogue; a token with a non-finite element gets the scale NaN.
-template <bool I8>
 __device__ void prep_block(const PlanArgs& a, int t) {
-  typedef _Float16 h2 __attribute__((ext_vector_type(2)));
   __shared__ float s_red[PLAN_WAVES];
   __shared__ int s_ired[PLAN_WAVES];
   const int tid = threadIdx.x;
@@ -360,118 +396,85 @@ __device__ void prep_block(const PlanArgs& a, int t) {
   const int active = n_ti < PLAN_THREADS ? n_ti : PLAN_THREADS;
   const int nw = (active + 63) / 64;
   if ((tid & ~63) >= active) return;  // whole wave
-  if constexpr (!I8) {
-    uint4* dst = reinterpret_cast<uint4*>(a.xp + (size_t)t * n_ti * 8);
-    float sum = 0.0f;
+  // pass 1: the largest magnitude (non-finite elements flagged as +inf); with at most
+  // one column per thread the rotated column stays in registers for pass 2
+  const bool one = n_ti <= PLAN_THREADS;
+  float f0[16];
+  float amax = 0.0f;
+  auto fold_max = [&](const float f[16]) {
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const float m = fabsf(f[j]);
+      amax = fmaxf(amax, m <= 3.4e38f ? m : __builtin_inff());
+    }
+  };
+  if (one) {
+    if (tid < n_ti) {
+      load_column(a, t, tid, f0);
+      fold_max(f0);
+    }
+  } else {
     for (int c = tid; c < n_ti; c += PLAN_THREADS) {
       float f[16];
       load_column(a, t, c, f);
-      uint32_t P[8];
-      float hf[16];
-#pragma unroll
-      for (int r = 0; r < 8; ++r) {
-        const h2 p = (h2){(_Float16)f[r + 8], (_Float16)f[r]};
-        P[r] = __builtin_bit_cast(uint32_t, p);
-        hf[r] = (float)p.y;
-        hf[r + 8] = (float)p.x;
-      }
-      float cs = 0.0f;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) cs += hf[i];
-      sum += cs;
-      dst[2 * c] = make_uint4(P[0], P[1], P[2], P[3]);
-      dst[2 * c + 1] = make_uint4(P[4], P[5], P[6], P[7]);
+      fold_max(f);
     }
+  }
+  amax = block_max(amax, s_red, nw);
+  int e = 0;
+  bool finite = amax <= 3.4e38f;
+  if (finite && amax > 0.0f) {
+    int ex;
+    (void)frexpf(amax, &ex);  // amax = f * 2^ex, f in [0.5, 1)
+    e = 15 - ex;
+    if (ldexpf(amax, e) > 32639.0f) e -= 1;
+  }
+  // pass 2: integers, halves, operand layout
+  int isum = 0;
+  auto quantize = [&](const float f[16], int c) {
+    int hi[16], lo[16];
 #pragma unroll
-    for (int d = 32; d >= 1; d >>= 1) sum += __shfl_xor(sum, d, 64);
-    if ((tid & 63) == 0) s_red[tid >> 6] = sum;
-    lds_barrier();
-    if (tid == 0) {
-      float s = 0.0f;
-      for (int w = 0; w < nw; ++w) s += s_red[w];
-      a.rowsum[t] = s;
+    for (int j = 0; j < 16; ++j) {
+      float v = finite ? rintf(ldexpf(f[j], e)) : 0.0f;
+      v = fminf(fmaxf(v, -32639.0f), 32639.0f);
+      const int xi = (int)v;
+      isum += xi;
+      hi[j] = (xi + 128) >> 8;
+      lo[j] = xi - (hi[j] << 8);
     }
+    uint32_t H[8], L[8];
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      const uint32_t h8 = (uint32_t)hi[r + 8] & 0xFFu, h0 = (uint32_t)hi[r] & 0xFFu;
+      const uint32_t l8 = (uint32_t)lo[r + 8] & 0xFFu, l0 = (uint32_t)lo[r] & 0xFFu;
+      H[r] = h8 | (h8 << 8) | (h0 << 16) | (h0 << 24);
+      L[r] = l8 | (l8 << 8) | (l0 << 16) | (l0 << 24);
+    }
+    uint4* dh = reinterpret_cast<uint4*>(a.xq + ((size_t)(2 * t) * n_ti + c) * 8);
+    uint4* dl = reinterpret_cast<uint4*>(a.xq + ((size_t)(2 * t + 1) * n_ti + c) * 8);
+    dh[0] = make_uint4(H[0], H[1], H[2], H[3]);
+    dh[1] = make_uint4(H[4], H[5], H[6], H[7]);
+    dl[0] = make_uint4(L[0], L[1], L[2], L[3]);
+    dl[1] = make_uint4(L[4], L[5], L[6], L[7]);
+  };
+  if (one) {
+    if (tid < n_ti) quantize(f0, tid);
   } else {
-    // pass 1: the largest magnitude (non-finite elements flagged as +inf); with at most
-    // one column per thread the rotated column stays in registers for pass 2
-    const bool one = n_ti <= PLAN_THREADS;
-    float f0[16];
-    float amax = 0.0f;
-    auto fold_max = [&](const float f[16]) {
-#pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const float m = fabsf(f[j]);
-        amax = fmaxf(amax, m <= 3.4e38f ? m : __builtin_inff());
-      }
-    };
-    if (one) {
-      if (tid < n_ti) {
-        load_column(a, t, tid, f0);
-        fold_max(f0);
-      }
-    } else {
-      for (int c = tid; c < n_ti; c += PLAN_THREADS) {
-        float f[16];
-        load_column(a, t, c, f);
-        fold_max(f);
-      }
+    for (int c = tid; c < n_ti; c += PLAN_THREADS) {
+      float f[16];
+      load_column(a, t, c, f);
+      quantize(f, c);
     }
-    amax = block_max(amax, s_red, nw);
-    int e = 0;
-    bool finite = amax <= 3.4e38f;
-    if (finite && amax > 0.0f) {
-      int ex;
-      (void)frexpf(amax, &ex);  // amax = f * 2^ex, f in [0.5, 1)
-      e = 15 - ex;
-      if (ldexpf(amax, e) > 32639.0f) e -= 1;
-    }
-    // pass 2: integers, halves, operand layout
-    int isum = 0;
-    auto quantize = [&](const float f[16], int c) {
-      int hi[16], lo[16];
+  }
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        float v = finite ? rintf(ldexpf(f[j], e)) : 0.0f;
-        v = fminf(fmaxf(v, -32639.0f), 32639.0f);
-        const int xi = (int)v;
-        isum += xi;
-        hi[j] = (xi + 128) >> 8;
-        lo[j] = xi - (hi[j] << 8);
-      }
-      uint32_t H[8], L[8];
-#pragma unroll
-      for (int r = 0; r < 8; ++r) {
-        const uint32_t h8 = (uint32_t)hi[r + 8] & 0xFFu, h0 = (uint32_t)hi[r] & 0xFFu;
-        const uint32_t l8 = (uint32_t)lo[r + 8] & 0xFFu, l0 = (uint32_t)lo[r] & 0xFFu;
-        H[r] = h8 | (h8 << 8) | (h0 << 16) | (h0 << 24);
-        L[r] = l8 | (l8 << 8) | (l0 << 16) | (l0 << 24);
-      }
-      uint4* dh = reinterpret_cast<uint4*>(a.xq + ((size_t)(2 * t) * n_ti + c) * 8);
-      uint4* dl = reinterpret_cast<uint4*>(a.xq + ((size_t)(2 * t + 1) * n_ti + c) * 8);
-      dh[0] = make_uint4(H[0], H[1], H[2], H[3]);
-      dh[1] = make_uint4(H[4], H[5], H[6], H[7]);
-      dl[0] = make_uint4(L[0], L[1], L[2], L[3]);
-      dl[1] = make_uint4(L[4], L[5], L[6], L[7]);
-    };
-    if (one) {
-      if (tid < n_ti) quantize(f0, tid);
-    } else {
-      for (int c = tid; c < n_ti; c += PLAN_THREADS) {
-        float f[16];
-        load_column(a, t, c, f);
-        quantize(f, c);
-      }
-    }
-#pragma unroll
-    for (int d = 32; d >= 1; d >>= 1) isum += __shfl_xor(isum, d, 64);
-    if ((tid & 63) == 0) s_ired[tid >> 6] = isum;
-    lds_barrier();
-    if (tid == 0) {
-      int s = 0;
-      for (int w = 0; w < nw; ++w) s += s_ired[w];
-      a.xsum[t] = s;
-      a.xscale[t] = finite ? ldexpf(1.0f, -e) : __builtin_nanf("");
-    }
+  for (int d = 32; d >= 1; d >>= 1) isum += __shfl_xor(isum, d, 64);
+  if ((tid & 63) == 0) s_ired[tid >> 6] = isum;
+  lds_barrier();
+  if (tid == 0) {
+    int s = 0;
+    for (int w = 0; w < nw; ++w) s += s_ired[w];
+    a.xsum[t] = s;
+    a.xscale[t] = finite ? ldexpf(1.0f, -e) : __builtin_nanf("");
   }
 }
 
@@ -480,11 +483,91 @@ __global__ __launch_bounds__(PLAN_THREADS) void gemv_plan_kernel(PlanArgs a) {
   if (blockIdx.x == 0)
     plan_block<TRELLIS>(a);
   else
-    prep_block<true>(a, blockIdx.x - 1);
+    prep_block(a, blockIdx.x - 1);
 }
 
-__global__ __launch_bounds__(PLAN_THREADS) void activation_prep_kernel(PlanArgs a) {
-  prep_block<false>(a, blockIdx.x);
+// Prefill-GEMM operands: PREP_TPB tokens per block, thread c converts tile column c of each
+// (columns c + blockDim, ... when in > 16 * blockDim), rotating it first when asked, into f16
+// pairs [lo: x[r + 8], hi: x[r]], and each token's sum of its f16 values in a fixed order
+// (16 values of a column in order, a thread's columns in order, the waves' butterfly, the
+// waves in order). The loads of all the block's tokens are issued before any is converted.
+constexpr int PREP_TPB = 1;
+
+// At most 64 registers (8 waves per SIMD): the kernel waits on memory, so occupancy counts.
+__global__ __launch_bounds__(PLAN_THREADS) __attribute__((amdgpu_waves_per_eu(8, 8)))
+void activation_prep_kernel(PlanArgs a) {
+  typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+  __shared__ float s_red[PREP_TPB][PLAN_WAVES];
+  const int tid = threadIdx.x, stride = blockDim.x;
+  const int n_ti = a.in / 16;
+  const int t0 = blockIdx.x * PREP_TPB;
+  float sum[PREP_TPB];
+#pragma unroll
+  for (int k = 0; k < PREP_TPB; ++k) sum[k] = 0.0f;
+  for (int c = tid; c < n_ti; c += stride) {
+    uint32_t m[16];
+    if (a.rotate) sign_masks(a.signs, c, m);
+    uint4 raw[PREP_TPB][2];
+#pragma unroll
+    for (int k = 0; k < PREP_TPB; ++k) {
+      if (t0 + k < a.T) {  // uniform
+        const uint4* src = reinterpret_cast<const uint4*>(a.x + (size_t)(t0 + k) * a.in);
+        raw[k][0] = src[2 * c];
+        raw[k][1] = src[2 * c + 1];
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < PREP_TPB; ++k) {
+      if (t0 + k < a.T) {
+        const uint32_t wv[8] = {raw[k][0].x, raw[k][0].y, raw[k][0].z, raw[k][0].w,
+                                raw[k][1].x, raw[k][1].y, raw[k][1].z, raw[k][1].w};
+        float f[16];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          f[2 * q] = bf16_lo_to_f32(wv[q]);
+          f[2 * q + 1] = bf16_hi_to_f32(wv[q]);
+        }
+        if (a.rotate) {
+          // the hardware conversion rounds to nearest even like f32_to_bf16_rne; the two
+          // could differ only on bf16 subnormals, which the f16 conversion below makes 0
+          rotate_column_f32(f, m, c);
+#pragma unroll
+          for (int q = 0; q < 16; ++q)
+            f[q] = __uint_as_float((uint32_t)__builtin_bit_cast(unsigned short, (__bf16)f[q]) << 16);
+        }
+        uint32_t P[8];
+        float hf[16];
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+          const h2 p = (h2){(_Float16)f[r + 8], (_Float16)f[r]};
+          P[r] = __builtin_bit_cast(uint32_t, p);
+          hf[r] = (float)p.y;
+          hf[r + 8] = (float)p.x;
+        }
+        float cs = 0.0f;
+#pragma unroll
+        for (int q = 0; q < 16; ++q) cs += hf[q];
+        sum[k] += cs;
+        uint4* dst = reinterpret_cast<uint4*>(a.xp + (size_t)(t0 + k) * n_ti * 8);
+        dst[2 * c] = make_uint4(P[0], P[1], P[2], P[3]);
+        dst[2 * c + 1] = make_uint4(P[4], P[5], P[6], P[7]);
+      }
+    }
+  }
+  const int nw = stride / 64;
+#pragma unroll
+  for (int k = 0; k < PREP_TPB; ++k) {
+    float v = sum[k];
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) v += __shfl_xor(v, d, 64);
+    if ((tid & 63) == 0) s_red[k][tid >> 6] = v;
+  }
+  lds_barrier();
+  if (tid < PREP_TPB && t0 + tid < a.T) {
+    float v = 0.0f;
+    for (int w = 0; w < nw; ++w) v += s_red[tid][w];
+    a.rowsum[t0 + tid] = v;
+  }
 }
 
 }  // namespace
@@ -510,7 +593,11 @@ hipError_t launch_activation_prep(const uint16_t* x, int64_t T, int in, uint32_t
   a.in = in;
   a.xp = xp;
   a.rowsum = rowsum;
-  hipLaunchKernelGGL(activation_prep_kernel, dim3((unsigned)T), dim3(PLAN_THREADS), 0, s, a);
+  // one thread per tile column (up to PLAN_THREADS): no wave without a column is launched
+  const int n_ti = in / 16;
+  const int threads = n_ti >= PLAN_THREADS ? PLAN_THREADS : (n_ti + 63) / 64 * 64;
+  const unsigned blocks = (unsigned)((T + PREP_TPB - 1) / PREP_TPB);
+  hipLaunchKernelGGL(activation_prep_kernel, dim3(blocks), dim3(threads), 0, s, a);
   return hipGetLastError();
 }
 

@@ -53,9 +53,10 @@ __device__ __forceinline__ float bf16_hi_to_f32(uint32_t w) { return __uint_as_f
 
 // bf16 round-to-nearest-even of an fp32 value (NaN kept quiet with its sign).
 __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return ((u >> 16) & 0x8000u) | 0x7FC0u;
-  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+  const uint32_t u = __float_as_uint(f);
+  const uint32_t rounded = (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+  const uint32_t qnan = ((u >> 16) & 0x8000u) | 0x7FC0u;
+  return (u & 0x7FFFFFFFu) > 0x7F800000u ? qnan : rounded;  // a select, not a branch
 }
 
 // f16 bits of an fp32 value, round to nearest even (v_cvt_f16_f32 in the default mode).

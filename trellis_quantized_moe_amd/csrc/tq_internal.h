@@ -23,7 +23,7 @@ struct WsLayout {
   bool gemm = false;
 };
 
-constexpr int ROUTE_CHUNK = 1024;  // ids per route-count block
+constexpr int ROUTE_CHUNK = 2048;  // ids per route-count block
 constexpr int GEMM_MT = 128;       // token rows per prefill work item
 constexpr int GEMV_MAXK = 16;      // tokens per decode-batch chunk (one MFMA row block)
 
