@@ -14,7 +14,7 @@
 //   K = 2, 3:  IH(r) = r,      IL(r) = r + 8
 //   K = 4:     IH(r) = J(r),   IL(r) = J(r) + 4, with J(r) = r (r < 4) or r + 4 (r >= 4)
 // For K = 2 and 4, the two states of a pair sit 16 bits apart in the stream, so a single
-// funnel shift yields both; K = 3 needs two funnel shifts and a bit-field merge.
+// funnel shift yields both; K = 3 needs two funnel shifts and a bit-field merge per pair.
 #pragma once
 
 #include "tq_device.h"
@@ -32,23 +32,20 @@ __device__ __forceinline__ int pair_il(int r) {
   return K == 4 ? pair_ih<K>(r) + 4 : r + 8;
 }
 
-// Word offsets (within a tile) a lane loads for column n, and the funnel shift for K = 3.
+// Word offsets (within a tile) a lane loads for column n.
 // K = 2: word n (the window of the column's last states continues into word n+1, which
 //        the lane takes from its right neighbour).
 // K = 4: words 2n, 2n+1 (word 2n+2 comes from the right neighbour).
-// K = 3: the column starts at bit 48n = word a, bit b (b = 0 or 16); the lane loads
-//        words a'..a'+2 (mod 24) with a' = a for b = 16 and a' = a - 1 for b = 0, so that
-//        one funnel shift by b aligns the column start for every lane.
-__device__ __forceinline__ void k3_column_words(int n, int* w0, int* w1, int* w2,
-                                                uint32_t* shift) {
-  int start = 48 * n;
-  int a = start >> 5;
-  int b = start & 31;
-  int ap = b ? a : a - 1;
-  *w0 = (ap + 24) % 24;
-  *w1 = (ap + 25) % 24;
-  *w2 = (ap + 26) % 24;
-  *shift = (uint32_t)b;
+// K = 3: the column starts at bit 48n: word p = floor(3n / 2), at bit 0 (n even) or bit 16
+//        (n odd). The lane loads words p and p+1; the 61 bits of an odd lane's column run
+//        into word p+2, which is the first word of the right neighbour (column n+1 starts
+//        at word p+2), taken from it. A byte selector aligns the column start: u0 = the
+//        column's bits 0..31, u1 = bits 32..63, one byte permutation each.
+__device__ __forceinline__ void k3_column_words(int n, int* w0, int* w1, uint32_t* sel) {
+  const int p = (3 * n) >> 1;
+  *w0 = p % 24;
+  *w1 = (p + 1) % 24;
+  *sel = (n & 1) ? 0x05040302u : 0x07060504u;  // {lo16(a), hi16(b)} or a
 }
 
 // Eight m-pairs of a K = 2 column. w = word n of the tile, wn = word n + 1 (mod 16).
@@ -82,16 +79,45 @@ __device__ __forceinline__ void col_mpairs_k4(uint32_t w0, uint32_t w1, uint32_t
   }
 }
 
-// K = 3 column: q0..q2 = words a'..a'+2, shift = b (see k3_column_words).
-__device__ __forceinline__ void col_mpairs_k3(uint32_t q0, uint32_t q1, uint32_t q2,
-                                              uint32_t shift, uint32_t M[8]) {
-  uint32_t u0 = funnel(q0, q1, shift);
-  uint32_t u1 = funnel(q1, q2, shift);
+// K = 3 column: x0, x1 = words p, p+1 and x2 = the right neighbour's x0 (see
+// k3_column_words).
+__device__ __forceinline__ void col_mpairs_k3(uint32_t x0, uint32_t x1, uint32_t x2,
+                                              uint32_t sel, uint32_t M[8]) {
+  const uint32_t u0 = perm(x0, x1, sel);
+  const uint32_t u1 = perm(x1, x2, sel);
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     uint32_t r1 = j == 0 ? u0 : funnel(u0, u1, 32 - 3 * j);  // high half: state j
     uint32_t r2 = funnel(u0, u1, 24 - 3 * j);                 // low half: state j + 8
     uint32_t r = (r1 & 0xFFFF0000u) | (r2 & 0x0000FFFFu);
+    u16x2 v = __builtin_bit_cast(u16x2, r) * __builtin_bit_cast(u16x2, T16_MULT2);
+    M[j] = __builtin_bit_cast(uint32_t, v);
+  }
+}
+
+// Half h (pairs 4 h .. 4 h + 3) of the eight m-pairs of a K = 2 column: the pairs of the
+// column's first (h = 0) or second (h = 1) matrix-core product.
+__device__ __forceinline__ void half_mpairs_k2(uint32_t w, uint32_t wn, int h, uint32_t M[4]) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int jj = 4 * h + j;
+    const uint32_t r = jj == 0 ? w : funnel(w, wn, 32 - 2 * jj);
+    u16x2 v = __builtin_bit_cast(u16x2, r) * __builtin_bit_cast(u16x2, T16_MULT2);
+    M[j] = __builtin_bit_cast(uint32_t, v);
+  }
+}
+
+// Half h of the eight m-pairs of a K = 3 column (x0..x2, sel as for col_mpairs_k3).
+__device__ __forceinline__ void half_mpairs_k3(uint32_t x0, uint32_t x1, uint32_t x2,
+                                               uint32_t sel, int h, uint32_t M[4]) {
+  const uint32_t u0 = perm(x0, x1, sel);
+  const uint32_t u1 = perm(x1, x2, sel);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int jj = 4 * h + j;
+    const uint32_t r1 = jj == 0 ? u0 : funnel(u0, u1, 32 - 3 * jj);
+    const uint32_t r2 = funnel(u0, u1, 24 - 3 * jj);
+    const uint32_t r = (r1 & 0xFFFF0000u) | (r2 & 0x0000FFFFu);
     u16x2 v = __builtin_bit_cast(u16x2, r) * __builtin_bit_cast(u16x2, T16_MULT2);
     M[j] = __builtin_bit_cast(uint32_t, v);
   }

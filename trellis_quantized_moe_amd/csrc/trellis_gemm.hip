@@ -25,6 +25,8 @@
 #include "gemm_core.h"
 #include "trellis_decode.h"
 
+#include <type_traits>
+
 namespace tq {
 
 namespace {
@@ -64,13 +66,13 @@ __device__ __forceinline__ void bare_barrier() {
 
 template <int K>
 struct ColWords {
-  uint32_t w[K == 2 ? 1 : (K == 4 ? 2 : 3)];
+  uint32_t w[K == 2 ? 1 : 2];
 };
 
 // Vector-memory instructions per step and wave: 8 activation loads and the code loads.
 template <int K>
 constexpr int step_loads() {
-  return 8 + 4 * (K == 3 ? 3 : 1);
+  return 8 + 4 * (K == 3 ? 2 : 1);
 }
 
 template <int K>
@@ -106,18 +108,17 @@ __device__ __forceinline__ void tg_item(const TrellisGemmArgs& a, TgShared& sh,
   // code loads: strip 8 grp + 4 w + nb (strips past the group read its last strip; their
   // outputs are never stored), tile column 4 kk + g, channel n of the strip
   const GemmRsrc rc = gemm_rsrc(unit, (uint32_t)((size_t)a.out * a.in * K / 8));
-  uint32_t cvo[3] = {0, 0, 0};
-  uint32_t sh3 = 0;
+  uint32_t cvo[2] = {0, 0};
+  uint32_t sel3 = 0;
   if constexpr (K == 2) {
     cvo[0] = 4u * (g * TW + n);
   } else if constexpr (K == 4) {
     cvo[0] = 4u * (g * TW + 2 * n);
   } else {
-    int w0, w1, w2;
-    k3_column_words(n, &w0, &w1, &w2, &sh3);
+    int w0, w1;
+    k3_column_words(n, &w0, &w1, &sel3);
     cvo[0] = 4u * (g * TW + w0);
     cvo[1] = 4u * (g * TW + w1);
-    cvo[2] = 4u * (g * TW + w2);
   }
   uint32_t strip_off[4];
 #pragma unroll
@@ -140,7 +141,6 @@ __device__ __forceinline__ void tg_item(const TrellisGemmArgs& a, TgShared& sh,
       } else {
         code[slot][nb].w[0] = __builtin_amdgcn_raw_buffer_load_b32(rc, cvo[0], o, 0);
         code[slot][nb].w[1] = __builtin_amdgcn_raw_buffer_load_b32(rc, cvo[1], o, 0);
-        code[slot][nb].w[2] = __builtin_amdgcn_raw_buffer_load_b32(rc, cvo[2], o, 0);
       }
     }
   };
@@ -155,54 +155,102 @@ __device__ __forceinline__ void tg_item(const TrellisGemmArgs& a, TgShared& sh,
   const uint32_t rd0 = 128u * n + 16u * ((2 * g) ^ (n >> 1));
   const uint32_t rd1 = 128u * n + 16u * ((2 * g + 1) ^ (n >> 1));
 
+  // B0 / B1: operand registers of the step's first / second product for each strip (pairs
+  // 0..3 / 4..7 of the lane's tile column). For K = 2, 3 the halves are decoded apart, so
+  // that each half is decoded while the matrix cores run the other half's products.
+  uint32_t B0[4][4], B1[4][4];
+  auto dec_half = [&](int slot, int h, uint32_t Bh[4][4]) {
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) {
+      const ColWords<K>& c = code[slot][nb];
+      uint32_t M[4];
+      if constexpr (K == 2)
+        half_mpairs_k2(c.w[0], row_next(c.w[0]), h, M);
+      else if constexpr (K == 3)
+        half_mpairs_k3(c.w[0], c.w[1], row_next(c.w[0]), sel3, h, M);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) Bh[nb][r] = byte_sum_pair(M[r]);
+    }
+  };
+  auto dec_full = [&](int slot) {
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) {
+      const ColWords<K>& c = code[slot][nb];
+      uint32_t M[8], V[8];
+      if constexpr (K == 2)
+        col_mpairs_k2(c.w[0], row_next(c.w[0]), M);
+      else if constexpr (K == 4)
+        col_mpairs_k4(c.w[0], c.w[1], row_next(c.w[0]), M);
+      else
+        col_mpairs_k3(c.w[0], c.w[1], row_next(c.w[0]), sel3, M);
+      byte_sums<K>(M, V);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        B0[nb][r] = V[r];
+        B1[nb][r] = V[4 + r];
+      }
+    }
+  };
+  auto products = [&](const uint8_t* st, uint32_t rd, const uint32_t Bh[4][4], auto full_tag) {
+    constexpr bool FULL = decltype(full_tag)::value;
+#pragma unroll
+    for (int mb = 0; mb < 8; ++mb) {
+      if (FULL || mb < mblocks) {
+        const u32x4 av = *reinterpret_cast<const u32x4*>(st + 2048 * mb + rd);
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb)
+          acc[mb][nb] = mfma_f16(av, (u32x4){Bh[nb][0], Bh[nb][1], Bh[nb][2], Bh[nb][3]},
+                                 acc[mb][nb]);
+      }
+    }
+  };
+
   // prologue: steps 0 and 1 (every step issues its loads in the order activations, codes)
   load_a(0);
   load_codes(0, 0);
   load_a(1);
   load_codes(1, 1);
+  if constexpr (K == 4)
+    dec_full(0);
+  else
+    dec_half(0, 0, B0);
 
-  for (int kk = 0; kk < nsteps; kk += 2) {
+  auto run = [&](auto full_tag) {
+    for (int kk = 0; kk < nsteps; kk += 2) {
 #pragma unroll
-    for (int d = 0; d < 2; ++d) {
-      const int step = kk + d;
-      // this wave's loads of `step` have landed (those of step + 1 may be in flight)
-      wait_vmcnt<step_loads<K>()>();
-      bare_barrier();
-      // refill the stage read two steps ago (every load is issued, clamped to the last
-      // step, so the wait counts above stay exact)
-      const int nxt = step + 2 < nsteps ? step + 2 : nsteps - 1;
-      load_a(nxt);
-      uint32_t B[4][8];
-#pragma unroll
-      for (int nb = 0; nb < 4; ++nb) {
-        uint32_t M[8];
-        const ColWords<K>& c = code[d][nb];
-        if constexpr (K == 2)
-          col_mpairs_k2(c.w[0], row_next(c.w[0]), M);
-        else if constexpr (K == 4)
-          col_mpairs_k4(c.w[0], c.w[1], row_next(c.w[0]), M);
-        else
-          col_mpairs_k3(c.w[0], c.w[1], c.w[2], sh3, M);
-        byte_sums<K>(M, B[nb]);
-      }
-      load_codes(d, nxt);
-      const uint8_t* st = sh.a[step % TG_STAGES];
-#pragma unroll
-      for (int mb = 0; mb < 8; ++mb) {
-        if (mb < mblocks) {
-          const u32x4 a0 = *reinterpret_cast<const u32x4*>(st + 2048 * mb + rd0);
-          const u32x4 a1 = *reinterpret_cast<const u32x4*>(st + 2048 * mb + rd1);
-#pragma unroll
-          for (int nb = 0; nb < 4; ++nb) {
-            acc[mb][nb] = mfma_f16(a0, (u32x4){B[nb][0], B[nb][1], B[nb][2], B[nb][3]},
-                                   acc[mb][nb]);
-            acc[mb][nb] = mfma_f16(a1, (u32x4){B[nb][4], B[nb][5], B[nb][6], B[nb][7]},
-                                   acc[mb][nb]);
-          }
+      for (int d = 0; d < 2; ++d) {
+        const int step = kk + d;
+        // this wave's loads of `step` have landed (those of step + 1 may be in flight)
+        wait_vmcnt<step_loads<K>()>();
+        bare_barrier();
+        // refill the stage read two steps ago (every load is issued, clamped to the last
+        // step, so the wait counts above stay exact)
+        const int nxt = step + 2 < nsteps ? step + 2 : nsteps - 1;
+        load_a(nxt);
+        const uint8_t* st = sh.a[step % TG_STAGES];
+        if constexpr (K == 4) {
+          products(st, rd0, B0, full_tag);
+          products(st, rd1, B1, full_tag);
+          load_codes(d, nxt);
+          dec_full(d ^ 1);  // the next step (past the last: unused)
+        } else {
+          // each half's products overlap the decoding of the other half; the scheduling
+          // barrier keeps the next step's first half from being decoded while this step's
+          // first-half products still read B0
+          dec_half(d, 1, B1);
+          products(st, rd0, B0, full_tag);
+          load_codes(d, nxt);
+          __builtin_amdgcn_sched_barrier(0);
+          dec_half(d ^ 1, 0, B0);  // the next step's first half (past the last: unused)
+          products(st, rd1, B1, full_tag);
         }
       }
     }
-  }
+  };
+  if (mblocks == 8)
+    run(std::integral_constant<bool, true>());
+  else
+    run(std::integral_constant<bool, false>());
   // no load may still be writing this workgroup's LDS when it ends
   wait_vmcnt<0>();
 

@@ -31,33 +31,32 @@ constexpr int GEMV_WAVES_PER_SIMD = 3;  // register budget: 168 per lane
 
 // ---- code words --------------------------------------------------------------------------
 // Words of one tile column a lane loads (see trellis_decode.h): K = 2 word n, K = 4 words
-// 2n and 2n + 1, K = 3 the three words of k3_column_words. The word after them (which the
+// 2n and 2n + 1, K = 3 the two words of k3_column_words. The word after them (which the
 // last states' windows reach) is the next lane's first word, taken by a row rotation: a
-// second load would cost more than the two instructions of the rotation.
+// further load would cost more than the two instructions of the rotation.
 template <int K>
 struct ColWords {
-  uint32_t w[K == 2 ? 1 : (K == 4 ? 2 : 3)];
+  uint32_t w[K == 2 ? 1 : 2];
 };
 
 // Per-lane word offsets inside the wave's run of 4 consecutive tiles.
 template <int K>
 struct LaneOffsets {
-  int o[3];
-  uint32_t sh3;
+  int o[2];
+  uint32_t sel3;
   __device__ LaneOffsets(int g, int n) {
     constexpr int TW = 8 * K;
-    o[0] = o[1] = o[2] = 0;
-    sh3 = 0;
+    o[0] = o[1] = 0;
+    sel3 = 0;
     if constexpr (K == 2) {
       o[0] = g * TW + n;
     } else if constexpr (K == 4) {
       o[0] = g * TW + 2 * n;
     } else {
-      int a, b, c;
-      k3_column_words(n, &a, &b, &c, &sh3);
+      int a, b;
+      k3_column_words(n, &a, &b, &sel3);
       o[0] = g * TW + a;
       o[1] = g * TW + b;
-      o[2] = g * TW + c;
     }
   }
 };
@@ -74,23 +73,22 @@ __device__ __forceinline__ void load_col(const uint32_t* __restrict__ run,
   } else {
     cw.w[0] = run[lo.o[0]];
     cw.w[1] = run[lo.o[1]];
-    cw.w[2] = run[lo.o[2]];
   }
 }
 
 template <int K>
-__device__ __forceinline__ void decode_col(const ColWords<K>& cw, uint32_t sh3, uint32_t M[8]) {
+__device__ __forceinline__ void decode_col(const ColWords<K>& cw, uint32_t sel3, uint32_t M[8]) {
   if constexpr (K == 2)
     col_mpairs_k2(cw.w[0], row_next(cw.w[0]), M);
   else if constexpr (K == 4)
     col_mpairs_k4(cw.w[0], cw.w[1], row_next(cw.w[0]), M);
   else
-    col_mpairs_k3(cw.w[0], cw.w[1], cw.w[2], sh3, M);
+    col_mpairs_k3(cw.w[0], cw.w[1], row_next(cw.w[0]), sel3, M);
 }
 
 // ---- buffer loads ------------------------------------------------------------------------
 template <int K>
-__device__ __forceinline__ void load_col_buf(Rsrc r, const uint32_t vo[3], uint32_t so,
+__device__ __forceinline__ void load_col_buf(Rsrc r, const uint32_t vo[2], uint32_t so,
                                              ColWords<K>& cw) {
   if constexpr (K == 2) {
     cw.w[0] = __builtin_amdgcn_raw_buffer_load_b32(r, vo[0], so, 0);
@@ -101,7 +99,6 @@ __device__ __forceinline__ void load_col_buf(Rsrc r, const uint32_t vo[3], uint3
   } else {
     cw.w[0] = __builtin_amdgcn_raw_buffer_load_b32(r, vo[0], so, 0);
     cw.w[1] = __builtin_amdgcn_raw_buffer_load_b32(r, vo[1], so, 0);
-    cw.w[2] = __builtin_amdgcn_raw_buffer_load_b32(r, vo[2], so, 0);
   }
 }
 
@@ -115,8 +112,8 @@ __device__ __forceinline__ void load_x(Rsrc r, uint32_t vo, uint32_t so, u32x4& 
 // with those D steps later (scalar offsets cso + strip offset, and xso).
 template <int K, bool RELOAD>
 __device__ __forceinline__ void step_body(ColWords<K> (&cw)[8], u32x4& xa, u32x4& xb, Rsrc rc,
-                                          const uint32_t cvo[3], uint32_t cso,
-                                          const uint32_t sso[8], uint32_t sh3, Rsrc rx,
+                                          const uint32_t cvo[2], uint32_t cso,
+                                          const uint32_t sso[8], uint32_t sel3, Rsrc rx,
                                           uint32_t xvo, uint32_t xso, i32x4 acc[8]) {
   // Every reload goes into the registers of the value it replaces, after that value's last
   // use (the scheduling barriers keep the compiler from hoisting it), so the loop carries
@@ -124,7 +121,7 @@ __device__ __forceinline__ void step_body(ColWords<K> (&cw)[8], u32x4& xa, u32x4
 #pragma unroll
   for (int s8 = 0; s8 < 8; ++s8) {
     uint32_t M[8], B[8];
-    decode_col<K>(cw[s8], sh3, M);
+    decode_col<K>(cw[s8], sel3, M);
     __builtin_amdgcn_sched_barrier(0);
     if (RELOAD) load_col_buf<K>(rc, cvo, cso + sso[s8], cw[s8]);
     i8_operands<K>(M, B);
@@ -150,7 +147,7 @@ __device__ __forceinline__ void stream(const TrellisGemvArgs& a, const uint32_t*
   const int steps = s1 - s0, last = steps - 1;
   const LaneOffsets<K> lo(g, n);
   const Rsrc rc = make_rsrc(unit, (uint32_t)((size_t)a.out * a.in * K / 8));
-  const uint32_t cvo[3] = {4u * lo.o[0], 4u * lo.o[1], 4u * lo.o[2]};
+  const uint32_t cvo[2] = {4u * lo.o[0], 4u * lo.o[1]};
   const uint32_t c0 = 4u * (uint32_t)(((size_t)grp * 8 * n_ti + 4 * s0) * TW);
   constexpr uint32_t cstep = 4u * 4 * TW;  // bytes per step and strip (4 tile columns)
   uint32_t sso[8];
@@ -181,14 +178,14 @@ __device__ __forceinline__ void stream(const TrellisGemvArgs& a, const uint32_t*
   for (; st + D <= steps; st += D) {
 #pragma unroll
     for (int d = 0; d < D; ++d)
-      step_body<K, true>(cw[d], xa[d], xb[d], rc, cvo, cso(st + d + D), sso, lo.sh3, rx, xvo,
+      step_body<K, true>(cw[d], xa[d], xb[d], rc, cvo, cso(st + d + D), sso, lo.sel3, rx, xvo,
                          xso(st + d + D), acc);
   }
   const int rem = steps - st;
 #pragma unroll
   for (int d = 0; d < D - 1; ++d)
     if (d < rem)
-      step_body<K, false>(cw[d], xa[d], xb[d], rc, cvo, 0, sso, lo.sh3, rx, xvo, 0, acc);
+      step_body<K, false>(cw[d], xa[d], xb[d], rc, cvo, 0, sso, lo.sel3, rx, xvo, 0, acc);
 }
 
 // One piece: expert record r, steps s0 .. s1 - 1 of group grp; sums to partial[piece], in
@@ -260,7 +257,7 @@ __global__ __launch_bounds__(256) void trellis_decode_kernel(const uint32_t* __r
   ColWords<K> cw;
   load_col<K>(codes + (size_t)(strip * n_ti + ti0) * TW, lo, cw);
   uint32_t M[8];
-  decode_col<K>(cw, lo.sh3, M);
+  decode_col<K>(cw, lo.sel3, M);
   int16_t* row = q + (size_t)(strip * 16 + n) * in + (ti0 + g) * 16;
   if (path == 0) {
     // operand register r: bytes [lo8 - 128, hi8 - 128] of input r + 8, then of input r;
