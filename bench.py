@@ -212,6 +212,42 @@ def bench_mxfp4(torch, ops, args):
             "kernel": "mxfp4_gemv_kernel", "kernel_sec": kmean, "kernel_sec_median": kmed}
 
 
+def bench_nvfp4(torch, ops, args):
+    """MXFP4 -> NVFP4 transcode of the 384-unit MXFP4 layer: bytes read (units) + written
+    (nibbles, E4M3 scales, fp32 second-level scales, flags) per call."""
+    from workloads import mxfp4_decode_layer
+    lay = mxfp4_decode_layer()["layer"]
+    dev = torch.device("cuda", 0)
+    L = ops.Mxfp4Layer.from_host(lay, dev)
+    E, out_ch, in_ = lay["E"], lay["out"], lay["in"]
+    reps = replicate(torch, L.units, L.units.numel())
+    layers = [L.with_units(u) for u in reps]
+    outs = []
+    for _ in range(2):  # two output sets alternate: together more than the Infinity Cache
+        outs.append((torch.empty((E, out_ch * in_ // 2), dtype=torch.uint8, device=dev),
+                     torch.empty((E, out_ch, in_ // 16), dtype=torch.uint8, device=dev),
+                     torch.empty(E, dtype=torch.float32, device=dev),
+                     torch.empty(E, dtype=torch.uint8, device=dev)))
+    nbytes = L.units.numel() + sum(t.numel() * t.element_size() for t in outs[0])
+    log("nvfp4: %.1f MB per call, %d replicas" % (nbytes / 1e6, len(reps)))
+
+    def step(r):
+        ops.mxfp4_to_nvfp4(layers[r], *outs[r % 2])
+
+    for r in range(len(reps)):
+        step(r)
+    torch.cuda.synchronize()
+    graphs = []
+    for r in range(len(reps)):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step(r)
+        graphs.append(g)
+    steps = max(20, args.steps // 10)
+    sec = time_graph_steps(torch, graphs, steps, max(4, args.warmup // 10))
+    return {"sec_per_step": sec, "bytes": nbytes, "steps": steps, "kernel": "nvfp4_transcode_kernel"}
+
+
 def bench_prefill(torch, ops, args):
     from workloads import prefill_chunk
     wl = prefill_chunk()
@@ -307,6 +343,14 @@ def drive(torch, ops, which, iters):
         for i in range(iters):
             ops.trellis_expert_gemm(layers[i % len(layers)], x, ids, flags=ops.TQ_ROTATE,
                                     out=y, ws=ws)
+    elif which == "nvfp4":
+        lay = mxfp4_decode_layer()["layer"]
+        L = ops.Mxfp4Layer.from_host(lay, dev)
+        reps = replicate(torch, L.units, L.units.numel())
+        layers = [L.with_units(u) for u in reps]
+        outs = [ops.mxfp4_to_nvfp4(L) for _ in range(2)]
+        for i in range(iters):
+            ops.mxfp4_to_nvfp4(layers[i % len(layers)], *outs[i % 2])
     else:
         wl = mxfp4_decode_layer()
         lay = wl["layer"]
@@ -373,12 +417,12 @@ def main():
     ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--kernel-iters", type=int, default=200)
-    ap.add_argument("--extras", default="mxfp4,prefill",
-                    help="comma list of secondary workloads (mxfp4, prefill) or 'none'")
+    ap.add_argument("--extras", default="mxfp4,prefill,nvfp4",
+                    help="comma list of secondary workloads (mxfp4, prefill, nvfp4) or 'none'")
     ap.add_argument("--cpu-sample-experts", type=int, default=0,
                     help="active experts in the CPU baseline sample (0 = all)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--drive", choices=["mixed", "mxfp4", "prefill"],
+    ap.add_argument("--drive", choices=["mixed", "mxfp4", "prefill", "nvfp4"],
                     help="only run --steps steps of one workload (for rocprofv3)")
     ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="summarise rocprofv3 FETCH_SIZE / WRITE_SIZE runs of --drive mixed")
@@ -467,6 +511,15 @@ def main():
             "kernel": p["kernel"], "kernel_us": round(p["kernel_sec"] * 1e6, 3),
             "kernel_TFLOP/s": round(p["flops"] / p["kernel_sec"] / 1e12, 3),
             "frac_f16_peak": round(p["flops"] / p["kernel_sec"] / 1e12 / F16_PEAK_TFLOPS, 4),
+        }
+    if "nvfp4" in todo:
+        v = bench_nvfp4(torch, ops, args)
+        extras["nvfp4_transcode"] = {
+            "workload": "MXFP4 -> NVFP4 transcode of 384 units of 128 x 5120",
+            "GB/s": round(v["bytes"] / v["sec_per_step"] / 1e9, 2),
+            "us_per_call": round(v["sec_per_step"] * 1e6, 3), "steps": v["steps"],
+            "kernel": v["kernel"], "bytes_per_call": v["bytes"],
+            "frac_hbm": round(v["bytes"] / v["sec_per_step"] / 1e9 / HBM_PEAK_GBS, 4),
         }
     if extras:
         line["extras"] = extras

@@ -185,6 +185,26 @@ int trellis_decode(const uint32_t* codes, int32_t K, int32_t out, int32_t in, in
  */
 int mxfp4_decode(const uint8_t* unit, int32_t out, int32_t in, uint16_t* w, void* stream);
 
+/*
+ * mxfp4_to_nvfp4 — transcode an MXFP4 layer to NVFP4 (FORMAT F13; DeepSeek-V4.1-Flash-1017
+ * NVFP4 page, "Model": 16-element blocks with E4M3 scales under one fp32 scale per tensor).
+ * Per unit e (one expert's out x in weights), with bmax its largest E8M0 scale byte:
+ *   codes[e]    = the unit's E2M1 nibbles, unchanged (out*in/2 bytes);
+ *   scales[e]   = E4M3 [out][in/16]: both 16-blocks of the 32-block with byte b get
+ *                 2^(b - bmax + 8), or 0 when bmax - b > 17 (below E4M3's smallest power of
+ *                 two: the block's values flush to zero), or 0x7F (NaN) when b = 255;
+ *   scale2[e]   = fp32 2^(bmax - 135), so that scale * scale2 = 2^(b - 127);
+ *   status[e]   = 1 if the transcode is exact (bmax - b <= 17 for every block), 0 if some
+ *                 block flushed, 2 if the unit holds a NaN scale byte.
+ *   L        host: the MXFP4 layer (E up to 65535).
+ *   codes    device, E * out*in/2 bytes, 16-byte aligned.
+ *   scales   device, E * out*in/16 bytes, 16-byte aligned.
+ *   scale2   device fp32 [E].   status  device uint8 [E].
+ * The outputs must not overlap the layer. Asynchronous on `stream`.
+ */
+int mxfp4_to_nvfp4(const tq_mxfp4_layer* L, uint8_t* codes, uint8_t* scales, float* scale2,
+                   uint8_t* status, void* stream);
+
 /* Workspace bytes the expert GEMM calls (and route_bucket with flags TQ_GEMM) need. */
 size_t tq_workspace_bytes(int64_t T, int32_t topk, int32_t E, int32_t out, int32_t in,
                           uint32_t flags);

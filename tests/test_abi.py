@@ -116,6 +116,14 @@ def test_hadamard_decode_route_argument_errors(lib):
     assert lib.trellis_decode(0x1000, 2, 16, 64, 0x1000, 2, None) == _lib.TQ_EINVAL
     assert lib.trellis_decode(0x1004, 2, 16, 64, 0x1000, 0, None) == _lib.TQ_EALIGN
     assert lib.mxfp4_decode(0x1000, 16, 48, 0x1000, None) == _lib.TQ_EINVAL
+    m = _lib.Mxfp4LayerC(4, 128, 5120, 0, 0x1000)
+    assert lib.mxfp4_to_nvfp4(None, 0x1000, 0x1000, 0x1000, 0x1000, None) == _lib.TQ_EINVAL
+    for bad in (_lib.Mxfp4LayerC(0, 128, 5120, 0, 0x1000), _lib.Mxfp4LayerC(4, 24, 5120, 0, 0x1000),
+                _lib.Mxfp4LayerC(4, 128, 1000, 0, 0x1000), _lib.Mxfp4LayerC(4, 128, 5120, 1, 0x1000)):
+        assert lib.mxfp4_to_nvfp4(ctypes.byref(bad), 0x1000, 0x1000, 0x1000, 0x1000, None) == _lib.TQ_EINVAL
+    assert lib.mxfp4_to_nvfp4(ctypes.byref(m), None, 0x1000, 0x1000, 0x1000, None) == _lib.TQ_EINVAL
+    assert lib.mxfp4_to_nvfp4(ctypes.byref(m), 0x1008, 0x1000, 0x1000, 0x1000, None) == _lib.TQ_EALIGN
+    assert lib.mxfp4_to_nvfp4(ctypes.byref(m), 0x1000, 0x1000, 0x1002, 0x1000, None) == _lib.TQ_EALIGN
     assert lib.route_bucket(0x1000, 4, 2, 0, 0x1000, 0x1000, 0x1000, 0x1000, 1 << 20, None) == _lib.TQ_EINVAL
     assert lib.route_bucket(0x1000, 4, 2, 5000, 0x1000, 0x1000, 0x1000, 0x1000, 1 << 20, None) == _lib.TQ_EINVAL
     assert lib.route_bucket(0x1000, 4, 2, 8, 0x1000, 0x1000, 0x1000, 0x1000, 8, None) == _lib.TQ_EWORKSPACE

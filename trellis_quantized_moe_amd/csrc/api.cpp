@@ -267,6 +267,28 @@ int mxfp4_decode(const uint8_t* unit, int32_t out, int32_t in, uint16_t* w, void
   return ok();
 }
 
+int mxfp4_to_nvfp4(const tq_mxfp4_layer* L, uint8_t* codes, uint8_t* scales, float* scale2,
+                   uint8_t* status, void* stream) {
+  if (!L) return fail(TQ_EINVAL, "layer is NULL");
+  if (L->E < 1 || L->E > 65535) return fail(TQ_EINVAL, "E = %d is outside 1..65535", L->E);
+  if (L->out <= 0 || L->out % 16) return fail(TQ_EINVAL, "out = %d is not a positive multiple of 16", L->out);
+  if (L->in <= 0 || L->in % 512) return fail(TQ_EINVAL, "in = %d is not a positive multiple of 512", L->in);
+  if (L->reserved != 0) return fail(TQ_EINVAL, "reserved field must be 0");
+  if ((int64_t)L->out * L->in / 2 >= ((int64_t)1 << 31))
+    return fail(TQ_EINVAL, "out * in is too large");
+  if (!L->units || !codes || !scales || !scale2 || !status)
+    return fail(TQ_EINVAL, "a pointer is NULL");
+  if (!aligned(L->units, 16) || !aligned(codes, 16) || !aligned(scales, 16))
+    return fail(TQ_EALIGN, "units, codes and scales must be 16-byte aligned");
+  if (!aligned(scale2, 4)) return fail(TQ_EALIGN, "scale2 must be 4-byte aligned");
+  int rc = check_device();
+  if (rc) return rc;
+  hipError_t err = tq::launch_nvfp4_transcode(L->units, L->E, L->out, L->in, codes, scales,
+                                              scale2, status, static_cast<hipStream_t>(stream));
+  if (err != hipSuccess) return hip_fail(err, "mxfp4_to_nvfp4 launch");
+  return ok();
+}
+
 int route_bucket(const int32_t* topk_ids, int64_t T, int32_t topk, int32_t E, int32_t* counts,
                  int32_t* offsets, int32_t* pairs, void* ws, size_t ws_bytes, void* stream) {
   int rc = check_routes(T, topk, topk_ids);

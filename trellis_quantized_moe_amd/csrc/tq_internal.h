@@ -169,5 +169,8 @@ hipError_t launch_trellis_decode(const uint32_t* codes, int K, int out, int in, 
                                  int path, hipStream_t s);
 hipError_t launch_mxfp4_decode(const uint8_t* unit, int out, int in, uint16_t* w,
                                hipStream_t s);
+hipError_t launch_nvfp4_transcode(const uint8_t* units, int E, int out, int in,
+                                  uint8_t* codes, uint8_t* scales, float* scale2,
+                                  uint8_t* status, hipStream_t s);
 
 }  // namespace tq

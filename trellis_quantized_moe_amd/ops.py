@@ -162,6 +162,26 @@ def mxfp4_decode(unit, out_ch, in_):
     return w
 
 
+def mxfp4_to_nvfp4(layer, codes=None, scales=None, scale2=None, status=None):
+    """NVFP4 form of an MXFP4 layer: (codes uint8 [E, out*in/2], scales uint8 [E, out, in/16],
+    scale2 fp32 [E], status uint8 [E]) (see mxfp4_to_nvfp4 in include/tq.h)."""
+    _require_cuda(layer.units, codes, scales, scale2, status)
+    dev = layer.units.device
+    E, out_ch, in_ = layer.E, layer.out, layer.in_
+    if codes is None:
+        codes = torch.empty((E, out_ch * in_ // 2), dtype=torch.uint8, device=dev)
+    if scales is None:
+        scales = torch.empty((E, out_ch, in_ // 16), dtype=torch.uint8, device=dev)
+    if scale2 is None:
+        scale2 = torch.empty(E, dtype=torch.float32, device=dev)
+    if status is None:
+        status = torch.empty(E, dtype=torch.uint8, device=dev)
+    c = layer.c_struct()
+    check(_lib.load().mxfp4_to_nvfp4(ctypes.byref(c), _ptr(codes), _ptr(scales), _ptr(scale2),
+                                     _ptr(status), _stream(dev)))
+    return codes, scales, scale2, status
+
+
 def device_status(ws):
     """Synchronise, read and clear the workspace status bits."""
     v = ctypes.c_uint32(0)
