@@ -10,7 +10,8 @@ every input already resident in device memory:
   mxfp4: the MXFP4 layer, 384 experts, 64 tokens, top-8 with gates — decode-batch GEMV;
   prefill: 8,192 tokens, top-8 over 384 K=3 experts with Zipf(1.1) popularity — the
       activation prep with the fused rotation, route bucketing (three kernels), grouped
-      MFMA GEMM.
+      MFMA GEMM;
+  nvfp4: the MXFP4 -> NVFP4 transcode of the 384-unit MXFP4 layer (bytes read + written).
 Steps are captured as HIP graphs and replayed; each step reads a different replica of the
 code buffer (replicas total >= 1 GiB) so the 256 MB Infinity Cache cannot serve repeats.
 
