@@ -66,7 +66,7 @@ def decode_mxfp4_unit(unit, out, inputs):
 
 
 # ----------------------------------------------------------------------------------
-# NVFP4 split (a check of the closed form; not on the GPU path)
+# NVFP4 split (FORMAT F13): the closed form, and the oracle of the transcode kernel
 # ----------------------------------------------------------------------------------
 
 def e4m3_value(byte):
