@@ -11,7 +11,10 @@ every input already resident in device memory:
   prefill: 8,192 tokens, top-8 over 384 K=3 experts with Zipf(1.1) popularity — the
       activation prep with the fused rotation, route bucketing (three kernels), grouped
       MFMA GEMM;
-  nvfp4: the MXFP4 -> NVFP4 transcode of the 384-unit MXFP4 layer (bytes read + written).
+  nvfp4: the MXFP4 -> NVFP4 transcode of the 384-unit MXFP4 layer (bytes read + written);
+  ffn: the routed expert FFN (gate, up, SwiGLU, rotated down projection, combine) of 384
+      experts with 768 intermediate channels, 128 tokens, top-8 — three decode-batch
+      pipelines, the SwiGLU kernel and the combine.
 Steps are captured as HIP graphs and replayed; each step reads a different replica of the
 code buffer (replicas total >= 1 GiB) so the 256 MB Infinity Cache cannot serve repeats.
 
@@ -249,6 +252,38 @@ def bench_nvfp4(torch, ops, args):
     return {"sec_per_step": sec, "bytes": nbytes, "steps": steps, "kernel": "nvfp4_transcode_kernel"}
 
 
+def bench_ffn(torch, ops, args):
+    """Routed expert FFN decode batch: gate, up, SwiGLU, rotated down projection, combine.
+    Bytes = the compressed units (gate + up + down) of the active experts."""
+    from workloads import ffn_decode
+    wl = ffn_decode()
+    dev = torch.device("cuda", 0)
+    G, U, D = (ops.TrellisLayer.from_host(wl[k], dev) for k in ("gate", "up", "down"))
+    x = torch.from_numpy(wl["x"].view(np.int16)).to(dev)
+    ids = torch.from_numpy(wl["topk_ids"]).to(dev)
+    gates = torch.from_numpy(wl["topk_w"]).to(dev)
+    T, topk = wl["topk_ids"].shape
+    nbytes = sum(active_bytes_trellis(wl[k], wl["topk_ids"])[0] for k in ("gate", "up", "down"))
+    n_active = active_bytes_trellis(wl["gate"], wl["topk_ids"])[1]
+    E, H, I = G.E, G.in_, G.out
+    y = torch.empty((T, H), dtype=torch.float32, device=dev)
+    ws = ops.ffn_workspace(T, topk, E, H, I, ops.TQ_AUTO, dev)
+    log("ffn: %d active experts, %.1f MB compressed per step" % (n_active, nbytes / 1e6))
+
+    def step():
+        ops.trellis_expert_ffn(G, U, D, x, ids, gates, flags=ops.TQ_ROTATE, out=y, ws=ws)
+
+    step()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    steps = max(20, args.steps // 5)
+    sec = time_graph_steps(torch, [g], steps, max(4, args.warmup // 5))
+    return {"sec_per_step": sec, "bytes": nbytes, "n_active": n_active, "steps": steps,
+            "code_bytes": int(sum(wl[k]["codes"].nbytes for k in ("gate", "up", "down")))}
+
+
 def bench_prefill(torch, ops, args):
     from workloads import prefill_chunk
     wl = prefill_chunk()
@@ -418,8 +453,8 @@ def main():
     ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--kernel-iters", type=int, default=200)
-    ap.add_argument("--extras", default="mxfp4,prefill,nvfp4",
-                    help="comma list of secondary workloads (mxfp4, prefill, nvfp4) or 'none'")
+    ap.add_argument("--extras", default="mxfp4,prefill,nvfp4,ffn",
+                    help="comma list of secondary workloads (mxfp4, prefill, nvfp4, ffn) or 'none'")
     ap.add_argument("--cpu-sample-experts", type=int, default=0,
                     help="active experts in the CPU baseline sample (0 = all)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -521,6 +556,16 @@ def main():
             "us_per_call": round(v["sec_per_step"] * 1e6, 3), "steps": v["steps"],
             "kernel": v["kernel"], "bytes_per_call": v["bytes"],
             "frac_hbm": round(v["bytes"] / v["sec_per_step"] / 1e9 / HBM_PEAK_GBS, 4),
+        }
+    if "ffn" in todo:
+        f = bench_ffn(torch, ops, args)
+        extras["ffn_decode"] = {
+            "workload": "routed expert FFN, 384 experts (gate/up 768 x 5120, down 5120 x 768, "
+                        "368 K2 / 15 K3 / 1 K4), 128 tokens, top-8, gates",
+            "GB/s": round(f["bytes"] / f["sec_per_step"] / 1e9, 2),
+            "ms_per_step": round(f["sec_per_step"] * 1e3, 5), "steps": f["steps"],
+            "active_experts": f["n_active"], "compressed_bytes_per_step": f["bytes"],
+            "frac_hbm": round(f["bytes"] / f["sec_per_step"] / 1e9 / HBM_PEAK_GBS, 4),
         }
     if extras:
         line["extras"] = extras

@@ -186,6 +186,40 @@ int trellis_decode(const uint32_t* codes, int32_t K, int32_t out, int32_t in, in
 int mxfp4_decode(const uint8_t* unit, int32_t out, int32_t in, uint16_t* w, void* stream);
 
 /*
+ * trellis_expert_ffn — the routed expert FFN over trellis-coded gate, up and down projections
+ * (FORMAT F15; DeepSeek-V4.1-Flash-1017 · exlr8 page, "Layout" and "Stores": every expert
+ * projection cut into units of 128 intermediate channels; dsx T16 page, "October 25 runtime
+ * checkpoint": fused gate/up post-processing):
+ *
+ *   g = gate_e(x~), u = up_e(x~)           fp32, as trellis_expert_gemm (per-channel scales)
+ *   h = bf16_rne(silu(g) * u),  silu(a) = a / (1 + e^-a)  (fp32)
+ *   z = down_e(rot(h))                     rot: the signed 128-wide rotation of hadamard128
+ *                                          over the intermediate, with down->signs
+ *   y[t] = sum over k = 0..topk-1, in order, of g[t][k] * z[t][k]
+ *
+ *   gate, up  host: trellis layers with out = I (intermediate), in = H (hidden), same E.
+ *   down      host: trellis layer with out = H, in = I, same E (its units strip-major over
+ *             the whole intermediate, FORMAT F2).
+ *   x         device bf16 [T][H]; with TQ_ROTATE the unrotated input (gate->signs rotate
+ *             it for both gate and up), else the rotated one.
+ *   topk_ids, topk_w, topk   as trellis_expert_gemm.
+ *   y         device fp32 [T][H], 16-byte aligned.
+ *   flags     TQ_AUTO / TQ_GEMV / TQ_GEMM (applied to every projection), | TQ_ROTATE.
+ *   ws        device workspace of tq_ffn_workspace_bytes(T, topk, E, H, I, flags) bytes,
+ *             256-byte aligned, zero-filled before its first use (as for trellis_expert_gemm);
+ *             the status word of tq_device_status is its first word.
+ * H and I are multiples of 256.
+ */
+int trellis_expert_ffn(const tq_trellis_layer* gate, const tq_trellis_layer* up,
+                       const tq_trellis_layer* down, const void* x, int64_t T,
+                       const int32_t* topk_ids, const float* topk_w, int32_t topk, float* y,
+                       uint32_t flags, void* ws, size_t ws_bytes, void* stream);
+
+/* Workspace bytes trellis_expert_ffn needs (0 for invalid sizes). */
+size_t tq_ffn_workspace_bytes(int64_t T, int32_t topk, int32_t E, int32_t H, int32_t I,
+                              uint32_t flags);
+
+/*
  * mxfp4_to_nvfp4 — transcode an MXFP4 layer to NVFP4 (FORMAT F13; DeepSeek-V4.1-Flash-1017
  * NVFP4 page, "Model": 16-element blocks with E4M3 scales under one fp32 scale per tensor).
  * Per unit e (one expert's out x in weights), with bmax its largest E8M0 scale byte:

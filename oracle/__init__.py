@@ -28,5 +28,6 @@ from .fpbits import (bf16_bits_to_f64, f16_bits_to_f64, f64_to_bf16_bits_exact,
 from .hadamard import sylvester_hadamard, hadamard128_f64, hadamard128_fp32_order
 from .routing import route_bucket
 from .gemm import expert_gemm, expert_gemm_exact, combine_slots
+from .ffn import silu, silu_scalar, expert_ffn
 
 __all__ = [name for name in dir() if not name.startswith("_")]

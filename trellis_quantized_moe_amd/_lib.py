@@ -67,6 +67,10 @@ SIGNATURES = {
     "trellis_decode": (ctypes.c_int, [_P, _I32, _I32, _I32, _P, _I32, _P]),
     "mxfp4_decode": (ctypes.c_int, [_P, _I32, _I32, _P, _P]),
     "mxfp4_to_nvfp4": (ctypes.c_int, [ctypes.POINTER(Mxfp4LayerC), _P, _P, _P, _P, _P]),
+    "trellis_expert_ffn": (ctypes.c_int, [ctypes.POINTER(TrellisLayerC), ctypes.POINTER(TrellisLayerC),
+                                          ctypes.POINTER(TrellisLayerC), _P, _I64, _P, _P, _I32,
+                                          _P, _U32, _P, _SZ, _P]),
+    "tq_ffn_workspace_bytes": (_SZ, [_I64, _I32, _I32, _I32, _I32, _U32]),
     "tq_workspace_bytes": (_SZ, [_I64, _I32, _I32, _I32, _I32, _U32]),
     "tq_last_error": (ctypes.c_char_p, []),
     "tq_device_status": (ctypes.c_int, [_P, _P, ctypes.POINTER(_U32)]),

@@ -195,6 +195,42 @@ size_t tq_workspace_bytes(int64_t T, int32_t topk, int32_t E, int32_t out, int32
   return a.total > b.total ? a.total : b.total;
 }
 
+namespace {
+
+// The FFN workspace: the gate/up calls' workspace, the down call's, then g, u (fp32), h (bf16)
+// and the down projection's per-slot outputs (fp32), each 256-byte aligned.
+struct FfnWs {
+  size_t gu, down, g, u, h, yd, total;
+};
+FfnWs ffn_ws(int64_t T, int32_t topk, int32_t E, int32_t H, int32_t I, uint32_t flags) {
+  FfnWs w{};
+  const int64_t N = T * topk;
+  const uint32_t mode = flags & 3u;
+  size_t off = 0;
+  w.gu = off;
+  off += round_up(tq_workspace_bytes(T, topk, E, I, H, mode), 256);
+  w.down = off;
+  off += round_up(tq_workspace_bytes(N, 1, E, H, I, mode), 256);
+  w.g = off;
+  off += round_up((size_t)N * I * 4, 256);
+  w.u = off;
+  off += round_up((size_t)N * I * 4, 256);
+  w.h = off;
+  off += round_up((size_t)N * I * 2, 256);
+  w.yd = off;
+  off += round_up((size_t)N * H * 4, 256);
+  w.total = off;
+  return w;
+}
+
+}  // namespace
+
+size_t tq_ffn_workspace_bytes(int64_t T, int32_t topk, int32_t E, int32_t H, int32_t I,
+                              uint32_t flags) {
+  if (T < 0 || topk < 1 || E < 1 || H < 256 || I < 256 || H % 256 || I % 256) return 0;
+  return ffn_ws(T, topk, E, H, I, flags).total;
+}
+
 const char* tq_last_error(void) { return g_error.c_str(); }
 
 int tq_time_kernel(void* start, void* stop) {
@@ -264,6 +300,54 @@ int mxfp4_decode(const uint8_t* unit, int32_t out, int32_t in, uint16_t* w, void
   if (rc) return rc;
   hipError_t err = tq::launch_mxfp4_decode(unit, out, in, w, static_cast<hipStream_t>(stream));
   if (err != hipSuccess) return hip_fail(err, "mxfp4_decode launch");
+  return ok();
+}
+
+int trellis_expert_ffn(const tq_trellis_layer* gate, const tq_trellis_layer* up,
+                       const tq_trellis_layer* down, const void* x, int64_t T,
+                       const int32_t* topk_ids, const float* topk_w, int32_t topk, float* y,
+                       uint32_t flags, void* ws, size_t ws_bytes, void* stream) {
+  if (!gate || !up || !down) return fail(TQ_EINVAL, "a layer is NULL");
+  if ((flags & ~(3u | TQ_ROTATE)) != 0 || (flags & 3u) == 3u)
+    return fail(TQ_EINVAL, "flags = 0x%x is not valid for the FFN", flags);
+  const int E = gate->E, I = gate->out, H = gate->in;
+  if (up->E != E || down->E != E) return fail(TQ_EINVAL, "the three layers must have the same E");
+  if (up->out != I || up->in != H) return fail(TQ_EINVAL, "up must have the shape of gate");
+  if (down->out != H || down->in != I)
+    return fail(TQ_EINVAL, "down must be in = gate.out (%d), out = gate.in (%d)", I, H);
+  if (H % 256 || I % 256) return fail(TQ_EINVAL, "H and I must be multiples of 256");
+  int rc = check_routes(T, topk, topk_ids);
+  if (rc) return rc;
+  rc = check_io(T, x, y);
+  if (rc) return rc;
+  if (T == 0) return ok();
+  const FfnWs W = ffn_ws(T, topk, E, H, I, flags);
+  rc = check_ws(ws, ws_bytes, W.total);
+  if (rc) return rc;
+  const int64_t N = T * topk;
+  uint8_t* base = static_cast<uint8_t*>(ws);
+  float* g = reinterpret_cast<float*>(base + W.g);
+  float* u = reinterpret_cast<float*>(base + W.u);
+  uint16_t* h = reinterpret_cast<uint16_t*>(base + W.h);
+  float* yd = reinterpret_cast<float*>(base + W.yd);
+  const uint32_t mode = flags & 3u;
+  // gate and up projections of every routed slot (the same workspace, calls in order)
+  rc = trellis_expert_gemm(gate, x, T, topk_ids, nullptr, topk, g, mode | (flags & TQ_ROTATE),
+                           base + W.gu, W.down - W.gu, stream);
+  if (rc) return rc;
+  rc = trellis_expert_gemm(up, x, T, topk_ids, nullptr, topk, u, mode | (flags & TQ_ROTATE),
+                           base + W.gu, W.down - W.gu, stream);
+  if (rc) return rc;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t err = tq::launch_swiglu(g, u, h, N * I, s);
+  if (err != hipSuccess) return hip_fail(err, "swiglu launch");
+  // down projection: each slot is a row of its own (routes and gates read as [T*topk][1]),
+  // with the 128-wide rotation of the intermediate
+  rc = trellis_expert_gemm(down, h, N, topk_ids, topk_w, 1, yd, mode | TQ_ROTATE,
+                           base + W.down, W.g - W.down, stream);
+  if (rc) return rc;
+  err = tq::launch_combine(yd, y, T, topk, H, s);
+  if (err != hipSuccess) return hip_fail(err, "combine launch");
   return ok();
 }
 
@@ -492,6 +576,7 @@ int trellis_expert_gemm(const tq_trellis_layer* L, const void* x, int64_t T,
     r.out = L->out;
     r.topk = topk;
     r.combine = (flags & TQ_COMBINE) ? 1 : 0;
+    r.qmax = L->in / 256;
     err = tq::launch_piece_reduce(r, s);
     if (err != hipSuccess) return hip_fail(err, "GEMV piece reduction launch");
     return ok();
@@ -607,6 +692,7 @@ int mxfp4_expert_gemm(const tq_mxfp4_layer* L, const void* x, int64_t T,
     r.out = L->out;
     r.topk = topk;
     r.combine = (flags & TQ_COMBINE) ? 1 : 0;
+    r.qmax = L->in / 512;
     err = tq::launch_piece_reduce(r, s);
     if (err != hipSuccess) return hip_fail(err, "GEMV piece reduction launch");
     return ok();

@@ -21,33 +21,40 @@ __device__ __forceinline__ void add4(float4& s, const float4& v) {
 }
 
 __device__ __forceinline__ float4 piece_slot(const PieceReduceArgs& a, int slot, int o) {
-  const int4 inf = a.slot_info[slot];
   const int t = slot / a.topk;
+  const size_t stride = (size_t)a.N * a.out;
+  const float* p = a.partial + (size_t)slot * a.out + o;
+  // The slot's record, its token's values and gate, and its first eight pieces are all
+  // requested before any arrives: the pieces' addresses do not depend on the record
+  // (indices clamped to the buffer's qmax pieces; the ones past the slot's count are
+  // dropped). Further pieces follow eight at a time; all are added in piece order.
+  const int4 inf = a.slot_info[slot];
   const float add = a.xsum ? (float)a.xsum[t] : 0.0f;
   const float mul = a.xscale ? a.xscale[t] : 1.0f;
   const float gate = a.gates ? a.gates[slot] : 1.0f;
+  float4 v[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q)
+    v[q] = *reinterpret_cast<const float4*>(p + (size_t)min(q, a.qmax - 1) * stride);
   if (inf.x == SLOT_EMPTY) return make_float4(0.f, 0.f, 0.f, 0.f);
   if (inf.x < 0) {
     const float nan = __builtin_nanf("");
     return make_float4(nan, nan, nan, nan);
   }
   const int e = inf.x, np = inf.y;
-  const size_t stride = (size_t)a.N * a.out;
-  const float* p = a.partial + (size_t)slot * a.out + o;
   const uint2 sc = a.scales ? *reinterpret_cast<const uint2*>(a.scales + (size_t)e * a.out + o)
                            : make_uint2(0x3C003C00u, 0x3C003C00u);  // fp16 1.0
-  // pieces are requested eight at a time (clamped indices, unused ones dropped) and added
-  // in piece order
-  float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int q0 = 0; q0 < np; q0 += 8) {
-    float4 v[8];
+  float4 s = v[0];
+#pragma unroll
+  for (int q = 1; q < 8; ++q)
+    if (q < np) add4(s, v[q]);
+  for (int q0 = 8; q0 < np; q0 += 8) {
 #pragma unroll
     for (int q = 0; q < 8; ++q)
       v[q] = *reinterpret_cast<const float4*>(p + (size_t)min(q0 + q, np - 1) * stride);
-    if (q0 == 0) s = v[0];
 #pragma unroll
     for (int q = 0; q < 8; ++q)
-      if ((q0 > 0 || q > 0) && q0 + q < np) add4(s, v[q]);
+      if (q0 + q < np) add4(s, v[q]);
   }
   const uint32_t sw[2] = {sc.x, sc.y};
   float r[4] = {s.x, s.y, s.z, s.w};

@@ -91,6 +91,7 @@ struct PieceReduceArgs {
   const float* xscale;  // [T]: then multiplied, or null
   float* y;
   int N, out, topk, combine;
+  int qmax;  // pieces the partial buffer holds per slot
 };
 constexpr int PIECE_MAX_TOPK = 64;  // largest topk (checked by the C ABI)
 hipError_t launch_piece_reduce(const PieceReduceArgs& a, hipStream_t s);
@@ -169,6 +170,8 @@ hipError_t launch_trellis_decode(const uint32_t* codes, int K, int out, int in, 
                                  int path, hipStream_t s);
 hipError_t launch_mxfp4_decode(const uint8_t* unit, int out, int in, uint16_t* w,
                                hipStream_t s);
+hipError_t launch_swiglu(const float* g, const float* u, uint16_t* h, int64_t n,
+                         hipStream_t s);
 hipError_t launch_nvfp4_transcode(const uint8_t* units, int E, int out, int in,
                                   uint8_t* codes, uint8_t* scales, float* scale2,
                                   uint8_t* status, hipStream_t s);

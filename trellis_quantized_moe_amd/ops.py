@@ -162,6 +162,28 @@ def mxfp4_decode(unit, out_ch, in_):
     return w
 
 
+def ffn_workspace(T, topk, E, H, I, flags=TQ_AUTO, device="cuda"):
+    n = max(256, int(_lib.load().tq_ffn_workspace_bytes(T, topk, E, H, I, flags)))
+    return torch.zeros(n, dtype=torch.uint8, device=device)
+
+
+def trellis_expert_ffn(gate, up, down, x, topk_ids, topk_w=None, flags=TQ_AUTO, out=None,
+                       ws=None):
+    """fp32 [T, H]: the routed expert FFN over trellis gate, up and down layers."""
+    _require_cuda(x, topk_ids, topk_w, out, ws)
+    T, topk = topk_ids.shape
+    if out is None:
+        out = torch.empty((T, gate.in_), dtype=torch.float32, device=x.device)
+    if ws is None:
+        ws = ffn_workspace(T, topk, gate.E, gate.in_, gate.out, flags, device=x.device)
+    g, u, d = gate.c_struct(), up.c_struct(), down.c_struct()
+    check(_lib.load().trellis_expert_ffn(ctypes.byref(g), ctypes.byref(u), ctypes.byref(d),
+                                         _ptr(x), T, _ptr(topk_ids), _ptr(topk_w), topk,
+                                         _ptr(out), flags, _ptr(ws), ws.numel(),
+                                         _stream(x.device)))
+    return out
+
+
 def mxfp4_to_nvfp4(layer, codes=None, scales=None, scale2=None, status=None):
     """NVFP4 form of an MXFP4 layer: (codes uint8 [E, out*in/2], scales uint8 [E, out, in/16],
     scale2 fp32 [E], status uint8 [E]) (see mxfp4_to_nvfp4 in include/tq.h)."""

@@ -6,7 +6,7 @@ __all__ = [
     "rng_for", "bf16_from_normal", "fp16_scales", "random_words", "random_signs",
     "uniform_routes", "zipf_routes", "softmax_gates", "trellis_layer", "mxfp4_layer",
     "single_matrix", "one_unit", "mxfp4_decode_layer", "mixed_widths", "mixed_layer",
-    "prefill_chunk",
+    "prefill_chunk", "ffn_layers", "ffn_decode",
     "WORKLOADS",
 ]
 
@@ -32,7 +32,8 @@ def fp16_scales(rng, shape, inputs):
 
 
 def random_words(rng, n):
-    return rng.integers(0, 1 << 32, size=n, dtype=np.uint64).astype(np.uint32)
+    """n uniform uint32 words."""
+    return rng.integers(0, 1 << 32, size=int(n), dtype=np.uint32)
 
 
 def random_signs(rng, n):
@@ -156,6 +157,36 @@ def prefill_chunk(E=384, T=8192, topk=8, K=3):
     ids = zipf_routes(rng_for(5, ROUTES), T, E, topk)
     return {"name": "prefill_e%d_t%d_top%d_k%d" % (E, T, topk, K), "kind": "trellis",
             "layer": layer, "x": x, "topk_ids": ids, "topk_w": None, "rotate": True}
+
+
+def ffn_layers(workload, widths, H, I, extra=()):
+    """Gate, up (I x H) and down (H x I) trellis layers of one routed-expert FFN. Gate and up
+    share the gate's signs (one input rotation serves both); the down layer has its own
+    signs for the rotation of the intermediate. The fp16 scales are U(0.5, 1.5) /
+    (sqrt(in) * 128), so that with N(0, 1) inputs each projection's outputs are of order 1
+    (the decoded integers have a standard deviation of about 104)."""
+    gate = trellis_layer(workload, widths, I, H, with_signs=True, extra=(0,) + tuple(extra))
+    up = trellis_layer(workload, widths, I, H, with_signs=True, extra=(1,) + tuple(extra))
+    down = trellis_layer(workload, widths, H, I, with_signs=True, extra=(2,) + tuple(extra))
+    up["signs"] = gate["signs"]
+    for lay, j in ((gate, 0), (up, 1), (down, 2)):
+        v = rng_for(workload, SCALES, j, 99, *extra).uniform(0.5, 1.5, size=(lay["E"], lay["out"]))
+        lay["scales"] = (v / (np.sqrt(float(lay["in"])) * 128.0)).astype(np.float16).view(np.uint16)
+    return gate, up, down
+
+
+def ffn_decode(E=384, T=128, topk=8, H=5120, I=768):
+    """Routed-expert FFN decode batch: E experts whose gate, up and down projections are
+    6 units of 128 intermediate channels each (I = 768, the 18 units per expert of the
+    exlr8 layout), mixed widths as the mixed layer, T tokens, top-k uniform, gates."""
+    n3 = round(E * 608 / 15360)
+    n4 = max(1, round(E * 21 / 15360))
+    gate, up, down = ffn_layers(7, mixed_widths(E, n3, n4), H, I)
+    x = bf16_from_normal(rng_for(7, ACTS), (T, H))
+    ids = uniform_routes(rng_for(7, ROUTES), T, E, topk)
+    w = softmax_gates(rng_for(7, GATES), T, topk)
+    return {"name": "ffn_e%d_t%d_top%d" % (E, T, topk), "kind": "ffn", "gate": gate, "up": up,
+            "down": down, "x": x, "topk_ids": ids, "topk_w": w, "rotate": True}
 
 
 WORKLOADS = {
