@@ -44,6 +44,22 @@ def test_decode_layer_full_size():
     assert rel_l2(y2, ref) <= TOL
 
 
+def test_long_pieces_sampled():
+    # More expert groups (320 x 8) than the plan's wave target: each group is one piece of
+    # 12 steps (or, on a GPU with a larger target, two of 6), so a piece spans several of the
+    # kernel's 4-step scale blocks, starting at steps that are not multiples of 4.
+    E, T, topk, out, inputs = 320, 256, 8, 1024, 1536
+    layer = mxfp4_layer(501, E, out, inputs)
+    x = bf16_from_normal(rng_for(501, 1), (T, inputs))
+    ids = uniform_routes(rng_for(501, 2), T, E, topk)
+    gates = softmax_gates(rng_for(501, 3), T, topk)
+    y = run(layer, x, ids, gates)
+    sample = np.sort(rng_for(501, 4).choice(T * topk, 48, replace=False))
+    ref = oracle_mxfp4(layer, x, ids, gates, sample=sample)
+    got = y.reshape(-1, out)[sample]
+    assert rel_l2(got, ref.reshape(-1, out)[sample]) <= TOL
+
+
 def test_deterministic():
     wl = mxfp4_decode_layer(E=64, T=32)
     a = run(wl["layer"], wl["x"], wl["topk_ids"], wl["topk_w"])

@@ -515,7 +515,7 @@ int trellis_expert_gemm(const tq_trellis_layer* L, const void* x, int64_t T,
   if (!W.gemm) {
     const int G = tq::trellis_gemv_grid();
     if (G <= 0) return fail(TQ_EHIP, "could not size the GEMV grid");
-    // launched waves: the resident ones, or one per expert group when that is more
+    // launched waves: the plan's target, or one per expert group when that is more
     const int Gl = (int)std::max<int64_t>(G, (int64_t)L->E * W.groups);
     tq::PlanArgs p{};
     p.ids = topk_ids;

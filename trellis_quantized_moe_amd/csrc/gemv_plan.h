@@ -48,5 +48,10 @@ constexpr int SLOT_BAD_UNIT = -3;  // expert with a bad width byte or offset: Na
 constexpr int PLAN_MAX_E = 4096;
 constexpr int PLAN_THREADS = 1024;
 constexpr int GEMV_MAX_G = 16384;  // bound on the GEMV grid (desc buffer size)
+// Waves per compute unit the plan aims for (2 per SIMD). The decode-batch kernels are bound
+// by VALU issue (the decode), not by memory latency: two waves per SIMD keep the VALU busy,
+// and fewer, longer pieces spend less on each wave's setup and on the partial sums that the
+// reduction reads.
+constexpr int GEMV_TARGET_PER_CU = 8;
 
 }  // namespace tq

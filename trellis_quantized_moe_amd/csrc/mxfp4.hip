@@ -115,7 +115,8 @@ __device__ __forceinline__ void mx_stream(const Mxfp4GemvArgs& a, MxShared& sh, 
   // scalar offsets of step st (clamped to the last step, whose data is read again)
   auto cst = [&](int st) { return 64u * (uint32_t)(s0 + (st < last ? st : last)); };
   auto xst = [&](int st) { return 256u * (uint32_t)(s0 + (st < last ? st : last)); };
-  auto bso = [&](int blk) { return 16u * (uint32_t)blk + 4u * (uint32_t)s0; };  // 4-step block
+  // scale bytes of the 4-step block starting at step st (4 bytes per row and step)
+  auto bso = [&](int st) { return 4u * (uint32_t)(s0 + st); };
   MxStep ring[MX_D];
 #pragma unroll
   for (int d = 0; d < MX_D; ++d)
@@ -275,7 +276,7 @@ int mxfp4_gemv_grid() {
       hipSuccess)
     return 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-  int g = per_cu * cus;
+  int g = std::min(per_cu, GEMV_TARGET_PER_CU) * cus;
   if (g > GEMV_MAX_G) g = GEMV_MAX_G;
   if (g < 1) g = 1;
   if (dev >= 0 && dev < 64) cache[dev] = g;

@@ -296,7 +296,7 @@ int trellis_gemv_grid() {
       hipSuccess)
     return 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-  int g = per_cu * cus;
+  int g = std::min(per_cu, GEMV_TARGET_PER_CU) * cus;
   if (g > GEMV_MAX_G) g = GEMV_MAX_G;
   if (g < 1) g = 1;
   if (dev >= 0 && dev < 64) cache[dev] = g;
