@@ -29,5 +29,6 @@ from .hadamard import sylvester_hadamard, hadamard128_f64, hadamard128_fp32_orde
 from .routing import route_bucket
 from .gemm import expert_gemm, expert_gemm_exact, combine_slots
 from .ffn import silu, silu_scalar, expert_ffn
+from .fp8b32 import fp8b32_unit_bytes, decode_fp8b32_unit, decode_fp8b32_weight_scalar
 
 __all__ = [name for name in dir() if not name.startswith("_")]

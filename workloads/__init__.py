@@ -17,6 +17,8 @@ layer, top-8 routing, 8,192-token prefill chunks):
 - activations: N(0, 1) drawn in fp32, rounded to bf16 (nearest-even);
 - MXFP4: codes uniform over the 16 nibbles, E8M0 bytes uniform in 119..125
   (exponents -8..-2);
+- fp8b32: codes uniform over the 254 non-NaN E4M3 bytes, E8M0 bytes uniform in
+  113..119 (exponents -14..-8);
 - routes: top-k distinct experts per token, uniform or Zipf-skewed;
 - gates: softmax of topk N(0, 1) logits per token (fp32).
 """

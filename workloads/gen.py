@@ -6,7 +6,7 @@ __all__ = [
     "rng_for", "bf16_from_normal", "fp16_scales", "random_words", "random_signs",
     "uniform_routes", "zipf_routes", "softmax_gates", "trellis_layer", "mxfp4_layer",
     "single_matrix", "one_unit", "mxfp4_decode_layer", "mixed_widths", "mixed_layer",
-    "prefill_chunk", "ffn_layers", "ffn_decode",
+    "prefill_chunk", "ffn_layers", "ffn_decode", "fp8b32_layer", "shared_expert",
     "WORKLOADS",
 ]
 
@@ -127,6 +127,29 @@ def mxfp4_decode_layer(E=384, T=64, topk=8):
     w = softmax_gates(rng_for(3, GATES), T, topk)
     return {"name": "mxfp4_e%d_t%d_top%d" % (E, T, topk), "kind": "mxfp4", "layer": layer,
             "x": x, "topk_ids": ids, "topk_w": w, "rotate": False}
+
+
+def fp8b32_layer(workload, E, out, inputs, extra=()):
+    """E fp8b32 units (codes uint8 [out][in], then E8M0 bytes [out/32][in/32]) back to back.
+    Codes are uniform over the 254 non-NaN E4M3 bytes, scale bytes uniform in 113..119
+    (exponents -14..-8)."""
+    rng = rng_for(workload, CODES, *extra)
+    nc, ns = out * inputs, (out // 32) * (inputs // 32)
+    units = np.empty((E, nc + ns), dtype=np.uint8)
+    c = rng.integers(0, 254, size=(E, nc), dtype=np.uint8)
+    units[:, :nc] = c + (c >= 0x7F) + (c >= 0xFE)  # skip 0x7F and 0xFF (NaN)
+    units[:, nc:] = rng_for(workload, SCALES, *extra).integers(113, 120, size=(E, ns), dtype=np.uint8)
+    return {"E": E, "out": out, "in": inputs, "units": units.reshape(-1)}
+
+
+def shared_expert(T=128, out=1536, inputs=5120):
+    """The shared expert's gate and up projections (2 x 768 channels over 5120 inputs) in the
+    fp8b32 store: one expert that every token routes to."""
+    layer = fp8b32_layer(8, 1, out, inputs)
+    x = bf16_from_normal(rng_for(8, ACTS), (T, inputs))
+    ids = np.zeros((T, 1), dtype=np.int32)
+    return {"name": "shared_fp8b32_t%d_%dx%d" % (T, out, inputs), "kind": "fp8b32",
+            "layer": layer, "x": x, "topk_ids": ids, "topk_w": None, "rotate": False}
 
 
 def mixed_widths(E=384, n3=15, n4=1):
