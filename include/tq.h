@@ -89,6 +89,22 @@ typedef struct tq_mxfp4_layer {
 } tq_mxfp4_layer;
 
 /*
+ * An fp8b32 expert layer (FORMAT F16; DeepSeek-V4.1-Flash-1017 · exlr8 page, "Stores": the
+ * shared expert's store, FP8 E4M3 values with one E8M0 scale per 32 x 32 block, 656,000
+ * bytes per 128 x 5120 unit). E units back to back, each out*in code bytes (row = output
+ * channel, one E4M3 byte per weight) followed by (out/32)*(in/32) E8M0 scale bytes
+ * (row-major [out/32][in/32]). The shared expert is a layer with E = 1 that every token
+ * routes to (topk = 1, all ids 0).
+ */
+typedef struct tq_fp8b32_layer {
+  int32_t E;                /* experts, 1 .. 4096                                         */
+  int32_t out;              /* output channels, multiple of 32                            */
+  int32_t in;               /* inputs, multiple of 512                                    */
+  int32_t reserved;         /* must be 0                                                  */
+  const uint8_t* units;     /* device: E * (out*in + out*in/1024) bytes, 16-aligned       */
+} tq_fp8b32_layer;
+
+/*
  * trellis_expert_gemm — routed activations x trellis-coded expert weights.
  *
  *   y[t][k][o] = g[t][k] * f32(scale_e[o]) * sum_i x[t][i] * q_e[i][o],  e = topk_ids[t][k]
@@ -142,6 +158,21 @@ int mxfp4_expert_gemm(const tq_mxfp4_layer* L, const void* x, int64_t T,
                       float* y, uint32_t flags, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * fp8b32_expert_gemm — routed activations x fp8b32 expert weights.
+ *
+ *   y[t][k][o] = g[t][k] * sum_i x[t][i] * E4M3[c_e[o][i]] * 2^(b_e[o/32][i/32] - 127)
+ *
+ * (DeepSeek-V4.1-Flash-1017 · exlr8 page, "Stores"; FORMAT F16, F10, F11.) Arguments,
+ * workspace, modes and determinism as mxfp4_expert_gemm. The decoded weights are exact in
+ * bf16 (the matrix-core operand) for scale bytes 10 .. 246; outside that range a product
+ * below the smallest normal bf16 value or above the largest one is rounded by the
+ * hardware conversion.
+ */
+int fp8b32_expert_gemm(const tq_fp8b32_layer* L, const void* x, int64_t T,
+                       const int32_t* topk_ids, const float* topk_w, int32_t topk,
+                       float* y, uint32_t flags, void* ws, size_t ws_bytes, void* stream);
+
+/*
  * hadamard128 — the 128-wide input rotation (FORMAT F8; DeepSeek-V4.1-Flash-1017 · dsx T16
  * page, "How T16 works", opening paragraph; exlr8 page, "Stores": per-layer signs).
  * Per block of 128 inputs: v = s * x; seven fp32 butterfly stages (strides 1..64,
@@ -184,6 +215,12 @@ int trellis_decode(const uint32_t* codes, int32_t K, int32_t out, int32_t in, in
  * decoder the MXFP4 kernels use.
  */
 int mxfp4_decode(const uint8_t* unit, int32_t out, int32_t in, uint16_t* w, void* stream);
+
+/*
+ * fp8b32_decode — test hook: decode one fp8b32 unit to bf16 [out][in] with the device
+ * decoder the fp8b32 kernels use. out multiple of 32, in multiple of 32, out*in < 2^31.
+ */
+int fp8b32_decode(const uint8_t* unit, int32_t out, int32_t in, uint16_t* w, void* stream);
 
 /*
  * trellis_expert_ffn — the routed expert FFN over trellis-coded gate, up and down projections

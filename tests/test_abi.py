@@ -105,6 +105,29 @@ def test_mxfp4_argument_errors(lib):
                                  _lib.TQ_ROTATE, 0x1000, 1 << 30, None) == _lib.TQ_EINVAL
 
 
+def test_fp8b32_argument_errors(lib):
+    ok = _lib.Mxfp4LayerC(1, 1536, 5120, 0, 0x1000)
+    assert lib.fp8b32_expert_gemm(ctypes.byref(ok), 0, 0, 0, None, 1, 0, 0, 0, 0, None) == _lib.TQ_OK
+    for bad in (_lib.Mxfp4LayerC(0, 128, 5120, 0, 0x1000), _lib.Mxfp4LayerC(1, 48, 5120, 0, 0x1000),
+                _lib.Mxfp4LayerC(1, 128, 5120 + 128, 0, 0x1000), _lib.Mxfp4LayerC(1, 128, 5120, 1, 0x1000)):
+        assert lib.fp8b32_expert_gemm(ctypes.byref(bad), 0x1000, 1, 0x1000, None, 1, 0x1000, 0,
+                                      0x1000, 1 << 30, None) == _lib.TQ_EINVAL
+    mis = _lib.Mxfp4LayerC(1, 128, 5120, 0, 0x1008)
+    assert lib.fp8b32_expert_gemm(ctypes.byref(mis), 0x1000, 1, 0x1000, None, 1, 0x1000, 0, 0x1000,
+                                  1 << 30, None) == _lib.TQ_EALIGN
+    assert lib.fp8b32_expert_gemm(ctypes.byref(ok), 0x1000, 1, 0x1000, None, 1, 0x1000,
+                                  _lib.TQ_ROTATE, 0x1000, 1 << 30, None) == _lib.TQ_EINVAL
+    assert lib.fp8b32_decode(0x1000, 48, 64, 0x1000, None) == _lib.TQ_EINVAL
+    assert lib.fp8b32_decode(0x1000, 32, 48, 0x1000, None) == _lib.TQ_EINVAL
+    assert lib.fp8b32_decode(0x1008, 32, 64, 0x1000, None) == _lib.TQ_EALIGN
+
+
+def test_internal_helpers_are_not_exported(lib):
+    for name in ("common_checks", "check_trellis_layer", "check_mxfp4_layer", "run_route",
+                 "ffn_ws", "mx_unit_bytes"):
+        assert not hasattr(lib, name), name
+
+
 def test_hadamard_decode_route_argument_errors(lib):
     assert lib.hadamard128(0x1000, 0x1000, 1, 100, None, None) == _lib.TQ_EINVAL
     assert lib.hadamard128(0x1000, 0x1000, -1, 128, None, None) == _lib.TQ_EINVAL

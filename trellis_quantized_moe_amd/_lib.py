@@ -42,6 +42,7 @@ class TrellisLayerC(ctypes.Structure):
 
 
 class Mxfp4LayerC(ctypes.Structure):
+    # also the layout of tq_fp8b32_layer (same fields)
     _fields_ = [
         ("E", ctypes.c_int32),
         ("out", ctypes.c_int32),
@@ -66,6 +67,9 @@ SIGNATURES = {
     "route_bucket": (ctypes.c_int, [_P, _I64, _I32, _I32, _P, _P, _P, _P, _SZ, _P]),
     "trellis_decode": (ctypes.c_int, [_P, _I32, _I32, _I32, _P, _I32, _P]),
     "mxfp4_decode": (ctypes.c_int, [_P, _I32, _I32, _P, _P]),
+    "fp8b32_expert_gemm": (ctypes.c_int, [ctypes.POINTER(Mxfp4LayerC), _P, _I64, _P, _P, _I32,
+                                          _P, _U32, _P, _SZ, _P]),
+    "fp8b32_decode": (ctypes.c_int, [_P, _I32, _I32, _P, _P]),
     "mxfp4_to_nvfp4": (ctypes.c_int, [ctypes.POINTER(Mxfp4LayerC), _P, _P, _P, _P, _P]),
     "trellis_expert_ffn": (ctypes.c_int, [ctypes.POINTER(TrellisLayerC), ctypes.POINTER(TrellisLayerC),
                                           ctypes.POINTER(TrellisLayerC), _P, _I64, _P, _P, _I32,

@@ -202,7 +202,7 @@ namespace {
 struct FfnWs {
   size_t gu, down, g, u, h, yd, total;
 };
-FfnWs ffn_ws(int64_t T, int32_t topk, int32_t E, int32_t H, int32_t I, uint32_t flags) {
+static FfnWs ffn_ws(int64_t T, int32_t topk, int32_t E, int32_t H, int32_t I, uint32_t flags) {
   FfnWs w{};
   const int64_t N = T * topk;
   const uint32_t mode = flags & 3u;
@@ -300,6 +300,19 @@ int mxfp4_decode(const uint8_t* unit, int32_t out, int32_t in, uint16_t* w, void
   if (rc) return rc;
   hipError_t err = tq::launch_mxfp4_decode(unit, out, in, w, static_cast<hipStream_t>(stream));
   if (err != hipSuccess) return hip_fail(err, "mxfp4_decode launch");
+  return ok();
+}
+
+int fp8b32_decode(const uint8_t* unit, int32_t out, int32_t in, uint16_t* w, void* stream) {
+  if (out <= 0 || out % 32) return fail(TQ_EINVAL, "out = %d is not a positive multiple of 32", out);
+  if (in <= 0 || in % 32) return fail(TQ_EINVAL, "in = %d is not a positive multiple of 32", in);
+  if ((int64_t)out * in >= ((int64_t)1 << 31)) return fail(TQ_EINVAL, "out * in must stay below 2^31");
+  if (!unit || !w) return fail(TQ_EINVAL, "unit or w is NULL");
+  if (!aligned(unit, 16) || !aligned(w, 16)) return fail(TQ_EALIGN, "unit and w must be 16-byte aligned");
+  int rc = check_device();
+  if (rc) return rc;
+  hipError_t err = tq::launch_fp8b32_decode(unit, out, in, w, static_cast<hipStream_t>(stream));
+  if (err != hipSuccess) return hip_fail(err, "fp8b32_decode launch");
   return ok();
 }
 
@@ -416,7 +429,7 @@ int route_bucket(const int32_t* topk_ids, int64_t T, int32_t topk, int32_t E, in
 
 namespace {
 
-int check_trellis_layer(const tq_trellis_layer* L) {
+static int check_trellis_layer(const tq_trellis_layer* L) {
   if (!L) return fail(TQ_EINVAL, "layer is NULL");
   if (L->E < 1 || L->E > 4096) return fail(TQ_EINVAL, "E = %d is outside 1..4096", L->E);
   if (L->out <= 0 || L->out % 16) return fail(TQ_EINVAL, "out = %d is not a positive multiple of 16", L->out);
@@ -430,7 +443,7 @@ int check_trellis_layer(const tq_trellis_layer* L) {
   return TQ_OK;
 }
 
-int check_mxfp4_layer(const tq_mxfp4_layer* L) {
+static int check_mxfp4_layer(const tq_mxfp4_layer* L) {
   if (!L) return fail(TQ_EINVAL, "layer is NULL");
   if (L->E < 1 || L->E > 4096) return fail(TQ_EINVAL, "E = %d is outside 1..4096", L->E);
   if (L->out <= 0 || L->out % 16) return fail(TQ_EINVAL, "out = %d is not a positive multiple of 16", L->out);
@@ -441,10 +454,29 @@ int check_mxfp4_layer(const tq_mxfp4_layer* L) {
   return TQ_OK;
 }
 
-// Shared front half of the two expert GEMM calls.
-int common_checks(int E, int out, int in, const void* x, int64_t T, const int32_t* ids,
-                  int32_t topk, float* y, uint32_t flags, void* ws, size_t ws_bytes, bool mxfp4,
-                  tq::WsLayout* layout) {
+static int check_fp8b32_layer(const tq_fp8b32_layer* L) {
+  if (!L) return fail(TQ_EINVAL, "layer is NULL");
+  if (L->E < 1 || L->E > 4096) return fail(TQ_EINVAL, "E = %d is outside 1..4096", L->E);
+  if (L->out <= 0 || L->out % 32) return fail(TQ_EINVAL, "out = %d is not a positive multiple of 32", L->out);
+  if (L->in <= 0 || L->in % 512) return fail(TQ_EINVAL, "in = %d is not a positive multiple of 512", L->in);
+  if (L->reserved != 0) return fail(TQ_EINVAL, "reserved field must be 0");
+  if (!L->units) return fail(TQ_EINVAL, "units is NULL");
+  if (!aligned(L->units, 16)) return fail(TQ_EALIGN, "units must be 16-byte aligned");
+  return TQ_OK;
+}
+
+// Bytes of one unit of the E8M0-scaled stores.
+static int64_t mx_unit_bytes(int fmt, int out, int in) {
+  if (fmt == tq::MX_FP8B32) return (int64_t)out * in + (int64_t)(out / 32) * (in / 32);
+  return (int64_t)out * in / 2 + (int64_t)out * in / 32;
+}
+
+// Shared front half of the expert GEMM calls. mx_unit: bytes per unit of an E8M0-scaled
+// store, 0 for trellis layers.
+static int common_checks(int E, int out, int in, const void* x, int64_t T, const int32_t* ids,
+                  int32_t topk, float* y, uint32_t flags, void* ws, size_t ws_bytes,
+                  int64_t mx_unit, tq::WsLayout* layout) {
+  const bool mxfp4 = mx_unit != 0;
   int rc = check_routes(T, topk, ids);
   if (rc) return rc;
   if (!flags_valid(flags)) return fail(TQ_EINVAL, "flags = 0x%x is not valid", flags);
@@ -459,15 +491,15 @@ int common_checks(int E, int out, int in, const void* x, int64_t T, const int32_
   if ((layout->gemm || !mxfp4) && T * (int64_t)in * (layout->gemm ? 2 : 4) >= ((int64_t)1 << 31))
     return fail(TQ_EINVAL, "the prepared activations (T * in * %d bytes) must stay below 2^31",
                 layout->gemm ? 2 : 4);
-  if (layout->gemm && (int64_t)out * in / 2 + (int64_t)out * in / 32 >= ((int64_t)1 << 31))
-    return fail(TQ_EINVAL, "out * in is too large for the prefill path");
+  if (mxfp4 && mx_unit >= ((int64_t)1 << 31))
+    return fail(TQ_EINVAL, "a unit of out * in weights must stay below 2^31 bytes");
   if (!layout->gemm && !mxfp4 && (int64_t)out * in / 2 >= ((int64_t)1 << 31))
     return fail(TQ_EINVAL, "out * in is too large for the decode-batch path");
   if (T == 0) return TQ_OK;
   return check_ws(ws, ws_bytes, layout->total);
 }
 
-int run_route(const tq::WsLayout& L, void* ws, const int32_t* ids, int64_t N, int E, int out,
+static int run_route(const tq::WsLayout& L, void* ws, const int32_t* ids, int64_t N, int E, int out,
               float* y_slots, hipStream_t s) {
   tq::RouteArgs r{};
   r.ids = ids;
@@ -502,7 +534,7 @@ int trellis_expert_gemm(const tq_trellis_layer* L, const void* x, int64_t T,
   if ((flags & TQ_ROTATE) && L->signs && !aligned(L->signs, 16))
     return fail(TQ_EALIGN, "signs must be 16-byte aligned");
   tq::WsLayout W;
-  rc = common_checks(L->E, L->out, L->in, x, T, topk_ids, topk, y, flags, ws, ws_bytes, false, &W);
+  rc = common_checks(L->E, L->out, L->in, x, T, topk_ids, topk, y, flags, ws, ws_bytes, 0, &W);
   if (rc) return rc;
   if (T == 0) return ok();
   rc = check_device();
@@ -620,14 +652,24 @@ int trellis_expert_gemm(const tq_trellis_layer* L, const void* x, int64_t T,
   return ok();
 }
 
-int mxfp4_expert_gemm(const tq_mxfp4_layer* L, const void* x, int64_t T,
-                      const int32_t* topk_ids, const float* topk_w, int32_t topk, float* y,
-                      uint32_t flags, void* ws, size_t ws_bytes, void* stream) {
-  int rc = check_mxfp4_layer(L);
-  if (rc) return rc;
+}  // extern "C"
+
+namespace {
+
+// The expert GEMM of the E8M0-scaled stores (MXFP4, fp8b32): E units of `unit` bytes back
+// to back at `units`.
+struct MxLayer {
+  int fmt, E, out, in;
+  const uint8_t* units;
+};
+
+int mx_expert_gemm(const MxLayer* L, const void* x, int64_t T, const int32_t* topk_ids,
+                   const float* topk_w, int32_t topk, float* y, uint32_t flags, void* ws,
+                   size_t ws_bytes, void* stream) {
   if (flags & TQ_ROTATE) return fail(TQ_EINVAL, "TQ_ROTATE applies to trellis layers only");
+  const int64_t unit = mx_unit_bytes(L->fmt, L->out, L->in);
   tq::WsLayout W;
-  rc = common_checks(L->E, L->out, L->in, x, T, topk_ids, topk, y, flags, ws, ws_bytes, true, &W);
+  int rc = common_checks(L->E, L->out, L->in, x, T, topk_ids, topk, y, flags, ws, ws_bytes, unit, &W);
   if (rc) return rc;
   if (T == 0) return ok();
   rc = check_device();
@@ -638,7 +680,7 @@ int mxfp4_expert_gemm(const tq_mxfp4_layer* L, const void* x, int64_t T,
   const uint16_t* xb = static_cast<const uint16_t*>(x);
   hipError_t err;
   if (!W.gemm) {
-    const int G = tq::mxfp4_gemv_grid();
+    const int G = tq::mxfp4_gemv_grid(L->fmt);
     if (G <= 0) return fail(TQ_EHIP, "could not size the GEMV grid");
     const int Gl = (int)std::max<int64_t>(G, (int64_t)L->E * W.groups);
     tq::PlanArgs p{};
@@ -647,7 +689,7 @@ int mxfp4_expert_gemm(const tq_mxfp4_layer* L, const void* x, int64_t T,
     p.E = L->E;
     p.topk = topk;
     p.bits = nullptr;  // every step costs 1
-    p.unit_bytes = (int64_t)L->out * L->in / 2 + (int64_t)L->out * L->in / 32;
+    p.unit_bytes = unit;
     p.groups = W.groups;
     p.S = L->in / 128;
     p.G = G;
@@ -663,6 +705,7 @@ int mxfp4_expert_gemm(const tq_mxfp4_layer* L, const void* x, int64_t T,
     err = tq::launch_gemv_plan(p, s);
     if (err != hipSuccess) return hip_fail(err, "decode plan launch");
     tq::Mxfp4GemvArgs a{};
+    a.fmt = L->fmt;
     a.units = L->units;
     a.x = xb;
     a.x_bytes = (uint32_t)(T * L->in * 2);
@@ -679,7 +722,7 @@ int mxfp4_expert_gemm(const tq_mxfp4_layer* L, const void* x, int64_t T,
     if (err != hipSuccess) return hip_fail(err, "hipEventRecord");
     err = tq::launch_mxfp4_gemv(a, s);
     if (err == hipSuccess) err = time_end(s);
-    if (err != hipSuccess) return hip_fail(err, "MXFP4 GEMV launch");
+    if (err != hipSuccess) return hip_fail(err, "GEMV launch");
     tq::PieceReduceArgs r{};
     r.slot_info = p.slot_info;
     r.partial = a.partial;
@@ -700,6 +743,7 @@ int mxfp4_expert_gemm(const tq_mxfp4_layer* L, const void* x, int64_t T,
     rc = run_route(W, ws, topk_ids, N, L->E, L->out, y_slots, s);
     if (rc) return rc;
     tq::Mxfp4GemmArgs a{};
+    a.fmt = L->fmt;
     a.units = L->units;
     a.x = xb;
     a.x_bytes = (uint32_t)(T * L->in * 2);
@@ -718,13 +762,35 @@ int mxfp4_expert_gemm(const tq_mxfp4_layer* L, const void* x, int64_t T,
     if (err != hipSuccess) return hip_fail(err, "hipEventRecord");
     err = tq::launch_mxfp4_gemm(a, s);
     if (err == hipSuccess) err = time_end(s);
-    if (err != hipSuccess) return hip_fail(err, "MXFP4 GEMM launch");
+    if (err != hipSuccess) return hip_fail(err, "GEMM launch");
   }
   if (flags & TQ_COMBINE) {
     err = tq::launch_combine(y_slots, y, T, topk, L->out, s);
     if (err != hipSuccess) return hip_fail(err, "combine launch");
   }
   return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int mxfp4_expert_gemm(const tq_mxfp4_layer* L, const void* x, int64_t T,
+                      const int32_t* topk_ids, const float* topk_w, int32_t topk, float* y,
+                      uint32_t flags, void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_mxfp4_layer(L);
+  if (rc) return rc;
+  const MxLayer m{tq::MX_FP4, L->E, L->out, L->in, L->units};
+  return mx_expert_gemm(&m, x, T, topk_ids, topk_w, topk, y, flags, ws, ws_bytes, stream);
+}
+
+int fp8b32_expert_gemm(const tq_fp8b32_layer* L, const void* x, int64_t T,
+                       const int32_t* topk_ids, const float* topk_w, int32_t topk, float* y,
+                       uint32_t flags, void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_fp8b32_layer(L);
+  if (rc) return rc;
+  const MxLayer m{tq::MX_FP8B32, L->E, L->out, L->in, L->units};
+  return mx_expert_gemm(&m, x, T, topk_ids, topk_w, topk, y, flags, ws, ws_bytes, stream);
 }
 
 }  // extern "C"

@@ -1,10 +1,17 @@
-// MXFP4 routed-expert kernels (gfx950): decode hook, decode-batch GEMV, prefill GEMM.
+// Kernels of the two E8M0-scaled expert stores (gfx950): decode hooks, decode-batch GEMV,
+// prefill GEMM (DeepSeek-V4.1-Flash-1017 · exlr8 page, "Stores").
 //
-// A unit is codes [out][in/2] (element 2j in the low nibble of byte j) followed by E8M0
-// scales [out][in/32] (DeepSeek-V4.1-Flash-1017 · exlr8 page, "Stores"). gfx950 converts
-// FP4 E2M1 pairs straight to bf16 with an fp32 scale (v_cvt_scalef32_pk_bf16_fp4), so a
-// dword of 8 codes becomes 4 bf16 pairs in 4 instructions; E2M1 * 2^e is exact in bf16
-// for every finite E8M0 scale, so decoding is bit-exact.
+// MXFP4 (routed experts): codes [out][in/2] (element 2j in the low nibble of byte j)
+// followed by E8M0 scales [out][in/32]. gfx950 converts FP4 E2M1 pairs straight to bf16
+// with an fp32 scale (v_cvt_scalef32_pk_bf16_fp4), so a dword of 8 codes becomes 4 bf16
+// pairs in 4 instructions; E2M1 * 2^e is exact in bf16 for every finite E8M0 scale.
+//
+// fp8b32 (the shared expert): codes [out][in], one FP8 E4M3 byte per weight, followed by
+// E8M0 scales [out/32][in/32], one per 32 x 32 block. v_cvt_scalef32_pk_bf16_fp8 turns two
+// E4M3 bytes into a bf16 pair with the fp32 scale, so 32 codes also take 16 instructions;
+// E4M3 * 2^e is exact in bf16 while the product stays a normal bf16 value.
+//
+// Both share one GEMV and one GEMM, with the unit format as a template parameter.
 #include "gemm_core.h"
 #include "gemv_wave.h"
 #include "tq_internal.h"
@@ -30,7 +37,45 @@ __device__ __forceinline__ void fp4x8_to_bf16(uint32_t codes, float scale, uint3
   out[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 3));
 }
 
-// ---- decode hook -----------------------------------------------------------------------
+// 4 E4M3 codes (inputs 4j .. 4j+3, lowest byte first) -> 2 dwords of bf16 pairs.
+__device__ __forceinline__ void fp8x4_to_bf16(uint32_t codes, float scale, uint32_t* out) {
+  out[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes, scale, false));
+  out[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes, scale, true));
+}
+
+// Unit geometry of the two stores.
+template <int FMT>
+struct MxUnit {
+  static constexpr bool kFp8 = FMT == MX_FP8B32;
+  // code bytes of one row (output channel)
+  __device__ __host__ static uint32_t row_bytes(int in) { return kFp8 ? (uint32_t)in : (uint32_t)in / 2; }
+  __device__ __host__ static size_t code_bytes(int out, int in) { return (size_t)out * row_bytes(in); }
+  __device__ __host__ static size_t unit_bytes(int out, int in) {
+    return code_bytes(out, in) + (kFp8 ? (size_t)(out / 32) * (in / 32) : (size_t)out * (in / 32));
+  }
+  // byte offset of the scale of output o, 32-input block kb
+  __device__ __host__ static uint32_t scale_at(int out, int in, int o, int kb) {
+    return (uint32_t)(code_bytes(out, in) + (kFp8 ? (size_t)(o / 32) * (in / 32) : (size_t)o * (in / 32)) + kb);
+  }
+};
+
+// ---- decode hooks ----------------------------------------------------------------------
+__global__ __launch_bounds__(256) void fp8b32_decode_kernel(const uint8_t* __restrict__ unit,
+                                                            int out, int in,
+                                                            uint16_t* __restrict__ wout) {
+  const int per_row = in / 8;
+  const int idx = blockIdx.x * 256 + threadIdx.x;
+  if (idx >= out * per_row) return;
+  const int o = idx / per_row, j = idx % per_row;
+  const uint2 codes = *reinterpret_cast<const uint2*>(unit + (size_t)o * in + 8 * j);
+  const uint32_t sb = unit[MxUnit<MX_FP8B32>::scale_at(out, in, o, (8 * j) / 32)];
+  const float sc = e8m0_to_f32(sb);
+  uint32_t r[4];
+  fp8x4_to_bf16(codes.x, sc, r);
+  fp8x4_to_bf16(codes.y, sc, r + 2);
+  *reinterpret_cast<uint4*>(wout + (size_t)o * in + 8 * j) = make_uint4(r[0], r[1], r[2], r[3]);
+}
+
 __global__ __launch_bounds__(256) void mxfp4_decode_kernel(const uint8_t* __restrict__ unit,
                                                            int out, int in,
                                                            uint16_t* __restrict__ wout) {
@@ -49,43 +94,65 @@ __global__ __launch_bounds__(256) void mxfp4_decode_kernel(const uint8_t* __rest
 // ---- decode-batch GEMV -------------------------------------------------------------------
 // One wave is one worker of the plan (gemv_plan.h, every step costing 1): wave w streams its
 // piece, 128-input steps s0 .. s1 - 1 of one group of 8 strips (128 output channels) of one
-// expert, on its own. Per step and strip, lane (g, n) loads 32 codes (16 bytes) of output
-// n, inputs 32 g .. 32 g + 31 of the step, takes that block's scale, and feeds 4 bf16
-// 16 x 16 x 32 matrix-core operations: operation c takes inputs 32 g + 8 c .. + 7 of every
-// lane group, against the same inputs of up to 16 routed token rows (bf16 x as given; rows
-// past the expert's count are zero). Codes and activations are requested D steps ahead,
-// into register sets used in turn. The scales come in blocks of 4 steps: two 16-byte loads
-// per lane bring the 128 rows' 16 scale bytes of the next block into registers, which go to
-// a double-buffered LDS stage (2 KB per block) at the block boundary; each lane then reads
-// its byte per strip and step from LDS, so a step issues no scale load of its own. At the
-// end the wave stores its accumulators as the piece's partial sums.
+// expert, on its own. Per step and strip, lane (g, n) loads the 32 codes of output n,
+// inputs 32 g .. 32 g + 31 of the step (16 bytes of MXFP4, 32 of fp8b32), takes that
+// block's scale, and feeds 4 bf16 16 x 16 x 32 matrix-core operations: operation c takes
+// inputs 32 g + 8 c .. + 7 of every lane group, against the same inputs of up to 16 routed
+// token rows (bf16 x as given; rows past the expert's count are zero). Codes and
+// activations are requested D steps ahead, into register sets used in turn. The scales
+// come in blocks of 4 steps: 16-byte loads bring the group's scale bytes of the next block
+// into registers (MXFP4: 128 rows, two loads per lane; fp8b32: the 4 row blocks, lanes
+// 0..3), which go to a double-buffered LDS stage at the block boundary; each lane then
+// reads its byte per strip and step from LDS, so a step issues no scale load of its own.
+// At the end the wave stores its accumulators as the piece's partial sums.
 constexpr int MX_THREADS = 64;
 constexpr int MX_WAVES_PER_SIMD = 3;
 constexpr int MX_D = 1;
 
+template <int FMT>
 struct MxStep {
-  u32x4 code[8];
+  u32x4 code[8][MxUnit<FMT>::kFp8 ? 2 : 1];
   u32x4 x[4];
 };
 
 struct MxShared {
-  alignas(16) uint8_t sc[2][128 * 16];  // [buffer][row][step of the block][block of the step]
+  // MXFP4: [row][step of the block][block of the step]; fp8b32: [row block][step][block]
+  alignas(16) uint8_t sc[2][128 * 16];
 };
 
-template <bool RELOAD>
-__device__ __forceinline__ void mx_step(MxStep& cur, const uint8_t* sc, Rsrc ru, uint32_t cvo,
+// LDS offset of strip s8's scale byte relative to strip 0's
+template <int FMT>
+__device__ __forceinline__ int strip_scale_offset(int s8) {
+  return MxUnit<FMT>::kFp8 ? 16 * (s8 >> 1) : 256 * s8;
+}
+
+template <int FMT, bool RELOAD>
+__device__ __forceinline__ void mx_step(MxStep<FMT>& cur, const uint8_t* sc, Rsrc ru, uint32_t cvo,
                                         const uint32_t cso[8], uint32_t cst, Rsrc rx,
                                         uint32_t xvo, uint32_t xst, f32x4 acc[8]) {
-  // sc: this lane's scale byte of strip 0 for this step (strip s8 at + 256 s8)
+  // sc: this lane's scale byte of strip 0 for this step
   // each reload replaces the registers of the value it follows, after that value's last use
 #pragma unroll
   for (int s8 = 0; s8 < 8; ++s8) {
-    const float scale = e8m0_to_f32(sc[256 * s8]);
+    const float scale = e8m0_to_f32(sc[strip_scale_offset<FMT>(s8)]);
     uint32_t b[4][4];
+    if constexpr (MxUnit<FMT>::kFp8) {
 #pragma unroll
-    for (int c = 0; c < 4; ++c) fp4x8_to_bf16(cur.code[s8][c], scale, b[c]);
+      for (int c = 0; c < 4; ++c) {
+        // inputs 8c .. 8c + 7 of the lane's 32: dwords 2c and 2c + 1 of its codes
+        fp8x4_to_bf16(cur.code[s8][c >> 1][(2 * c) & 3], scale, b[c]);
+        fp8x4_to_bf16(cur.code[s8][c >> 1][(2 * c + 1) & 3], scale, b[c] + 2);
+      }
+    } else {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) fp4x8_to_bf16(cur.code[s8][0][c], scale, b[c]);
+    }
     __builtin_amdgcn_sched_barrier(0);
-    if (RELOAD) cur.code[s8] = __builtin_amdgcn_raw_buffer_load_b128(ru, cvo, cso[s8] + cst, 0);
+    if (RELOAD) {
+      cur.code[s8][0] = __builtin_amdgcn_raw_buffer_load_b128(ru, cvo, cso[s8] + cst, 0);
+      if constexpr (MxUnit<FMT>::kFp8)
+        cur.code[s8][1] = __builtin_amdgcn_raw_buffer_load_b128(ru, cvo + 16u, cso[s8] + cst, 0);
+    }
 #pragma unroll
     for (int c = 0; c < 4; ++c)
       acc[s8] = mfma_bf16(cur.x[c], (u32x4){b[c][0], b[c][1], b[c][2], b[c][3]}, acc[s8]);
@@ -97,34 +164,47 @@ __device__ __forceinline__ void mx_step(MxStep& cur, const uint8_t* sc, Rsrc ru,
   }
 }
 
+template <int FMT>
 __device__ __forceinline__ void mx_stream(const Mxfp4GemvArgs& a, MxShared& sh, Rsrc ru, int tok,
                                           int grp, int ns, int s0, int s1, f32x4 acc[8]) {
+  using U = MxUnit<FMT>;
   const int lane = threadIdx.x & 63, g = lane >> 4, n = lane & 15;
-  const uint32_t row = (uint32_t)a.in / 2, srow = (uint32_t)a.in / 32;
-  const uint32_t cvo = n * row + 16u * g;  // code byte of output n, block g
+  const uint32_t row = U::row_bytes(a.in);
+  const uint32_t cvo = n * row + (U::kFp8 ? 32u : 16u) * g;  // codes of output n, block g
+  const uint32_t cstep = U::kFp8 ? 128u : 64u;                 // code bytes per row and step
   uint32_t cso[8];
 #pragma unroll
   for (int s8 = 0; s8 < 8; ++s8)
     cso[s8] = (uint32_t)(grp * 128 + 16 * (s8 < ns ? s8 : ns - 1)) * row;
-  // scale blocks: lane L brings rows L and L + 64 (16 bytes each: 4 steps x 4 blocks)
-  const uint32_t svo0 = (uint32_t)a.out * row + (uint32_t)(grp * 128 + lane) * srow;
-  const uint32_t svo1 = svo0 + 64u * srow;
+  // scale rows of a 4-step block, 16 bytes each (4 steps x 4 blocks): MXFP4 lane L brings
+  // rows L and L + 64 of the group; fp8b32 lanes 0..3 bring the group's 4 row blocks
+  uint32_t svo0, svo1;
+  if constexpr (U::kFp8) {
+    svo0 = U::scale_at(a.out, a.in, 32 * (grp * 4 + (lane & 3)), 0);
+    svo1 = svo0;
+  } else {
+    svo0 = U::scale_at(a.out, a.in, grp * 128 + lane, 0);
+    svo1 = U::scale_at(a.out, a.in, grp * 128 + lane + 64, 0);
+  }
   const Rsrc rx = make_rsrc(a.x, a.x_bytes);
   const uint32_t xvo = tok >= 0 ? (uint32_t)tok * (uint32_t)a.in * 2u + 64u * g : 0x80000000u;
   const int steps = s1 - s0, last = steps - 1;
   // scalar offsets of step st (clamped to the last step, whose data is read again)
-  auto cst = [&](int st) { return 64u * (uint32_t)(s0 + (st < last ? st : last)); };
+  auto cst = [&](int st) { return cstep * (uint32_t)(s0 + (st < last ? st : last)); };
   auto xst = [&](int st) { return 256u * (uint32_t)(s0 + (st < last ? st : last)); };
   // scale bytes of the 4-step block starting at step st (4 bytes per row and step)
   auto bso = [&](int st) { return 4u * (uint32_t)(s0 + st); };
-  MxStep ring[MX_D];
+  MxStep<FMT> ring[MX_D];
 #pragma unroll
   for (int d = 0; d < MX_D; ++d)
 #pragma unroll
-    for (int s8 = 0; s8 < 8; ++s8)
-      ring[d].code[s8] = __builtin_amdgcn_raw_buffer_load_b128(ru, cvo, cso[s8] + cst(d), 0);
+    for (int s8 = 0; s8 < 8; ++s8) {
+      ring[d].code[s8][0] = __builtin_amdgcn_raw_buffer_load_b128(ru, cvo, cso[s8] + cst(d), 0);
+      if constexpr (U::kFp8)
+        ring[d].code[s8][1] = __builtin_amdgcn_raw_buffer_load_b128(ru, cvo + 16u, cso[s8] + cst(d), 0);
+    }
   u32x4 sa = __builtin_amdgcn_raw_buffer_load_b128(ru, svo0, bso(0), 0);
-  u32x4 sb = __builtin_amdgcn_raw_buffer_load_b128(ru, svo1, bso(0), 0);
+  u32x4 sb = U::kFp8 ? sa : __builtin_amdgcn_raw_buffer_load_b128(ru, svo1, bso(0), 0);
 #pragma unroll
   for (int d = 0; d < MX_D; ++d)
 #pragma unroll
@@ -132,37 +212,42 @@ __device__ __forceinline__ void mx_stream(const Mxfp4GemvArgs& a, MxShared& sh, 
       ring[d].x[c] = __builtin_amdgcn_raw_buffer_load_b128(rx, xvo, xst(d) + 16u * c, 0);
 #pragma unroll
   for (int s8 = 0; s8 < 8; ++s8) acc[s8] = (f32x4){0.f, 0.f, 0.f, 0.f};
-  // this lane's scale byte: row n of strip 0, step k of the block, block g of the step
-  const int sbase = 16 * n + g;
+  // this lane's scale byte of strip 0: step k of the block at + 4 k, block g of the step
+  const int sbase = U::kFp8 ? g : 16 * n + g;
   int st = 0;
   for (int blk = 0; blk < steps; blk += 4) {
     const int buf = (blk >> 2) & 1;
-    *reinterpret_cast<u32x4*>(&sh.sc[buf][16 * lane]) = sa;
-    *reinterpret_cast<u32x4*>(&sh.sc[buf][16 * (lane + 64)]) = sb;
+    if constexpr (U::kFp8) {
+      if (lane < 4) *reinterpret_cast<u32x4*>(&sh.sc[buf][16 * lane]) = sa;
+    } else {
+      *reinterpret_cast<u32x4*>(&sh.sc[buf][16 * lane]) = sa;
+      *reinterpret_cast<u32x4*>(&sh.sc[buf][16 * (lane + 64)]) = sb;
+    }
     if (blk + 4 < steps) {  // the next block's scales, in flight during this block
       sa = __builtin_amdgcn_raw_buffer_load_b128(ru, svo0, bso(blk + 4), 0);
-      sb = __builtin_amdgcn_raw_buffer_load_b128(ru, svo1, bso(blk + 4), 0);
+      if constexpr (!U::kFp8) sb = __builtin_amdgcn_raw_buffer_load_b128(ru, svo1, bso(blk + 4), 0);
     }
 #pragma unroll
     for (int k = 0; k < 4; k += MX_D) {
       if (st + MX_D <= steps) {
 #pragma unroll
         for (int d = 0; d < MX_D; ++d)
-          mx_step<true>(ring[d], &sh.sc[buf][sbase + 4 * (k + d)], ru, cvo, cso, cst(st + d + MX_D),
-                        rx, xvo, xst(st + d + MX_D), acc);
+          mx_step<FMT, true>(ring[d], &sh.sc[buf][sbase + 4 * (k + d)], ru, cvo, cso,
+                             cst(st + d + MX_D), rx, xvo, xst(st + d + MX_D), acc);
         st += MX_D;
       } else {
 #pragma unroll
         for (int d = 0; d < MX_D; ++d)
           if (st + d < steps)
-            mx_step<false>(ring[d], &sh.sc[buf][sbase + 4 * (k + d)], ru, cvo, cso, 0, rx, xvo,
-                           0, acc);
+            mx_step<FMT, false>(ring[d], &sh.sc[buf][sbase + 4 * (k + d)], ru, cvo, cso, 0, rx,
+                                xvo, 0, acc);
         st = steps;
       }
     }
   }
 }
 
+template <int FMT>
 __global__ __launch_bounds__(MX_THREADS, MX_WAVES_PER_SIMD) void mxfp4_gemv_kernel(Mxfp4GemvArgs a) {
   __shared__ MxShared sh;
   Piece pc;
@@ -170,14 +255,13 @@ __global__ __launch_bounds__(MX_THREADS, MX_WAVES_PER_SIMD) void mxfp4_gemv_kern
   const PlanRec r = load_rec(a.rec, pc.ai);
   const int lane = threadIdx.x & 63, n = lane & 15, g = lane >> 4;
   const int ns = min(8, a.out / 16 - pc.grp * 8);
-  const uint32_t unit_bytes = (uint32_t)((size_t)a.out * a.in / 2 + (size_t)a.out * a.in / 32);
-  const Rsrc ru = make_rsrc(a.units + r.off, unit_bytes);
+  const Rsrc ru = make_rsrc(a.units + r.off, (uint32_t)MxUnit<FMT>::unit_bytes(a.out, a.in));
   float* dst = a.partial + (size_t)pc.idx * a.N * a.out + pc.grp * 128 + n;
   for (int c0 = 0; c0 < r.cnt; c0 += 16) {
     const int rows = min(16, r.cnt - c0);
     const int slot = n < rows ? a.list[r.start + c0 + n] : -1;
     f32x4 acc[8];
-    mx_stream(a, sh, ru, slot >= 0 ? slot / a.topk : -1, pc.grp, ns, pc.s0, pc.s1, acc);
+    mx_stream<FMT>(a, sh, ru, slot >= 0 ? slot / a.topk : -1, pc.grp, ns, pc.s0, pc.s1, acc);
     // accumulator element i of lane (g, n) is token row 4 g + i, output channel n of its strip
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -231,6 +315,43 @@ struct Mxfp4Producer {
   }
 };
 
+// fp8b32 B producer: thread (o = tid / 2, h = tid % 2) decodes inputs 16 h .. + 15 of the
+// step's 32-block for output channel o: 16 code bytes and the scale byte of the channel's
+// 32 x 32 block.
+struct Fp8b32Producer {
+  static constexpr bool kF16 = false;
+  struct Raw {
+    u32x4 c;
+    uint32_t sb;
+  };
+  GemmRsrc rc;
+  uint32_t vo_c, vo_s;
+  int o, h;
+
+  __device__ Fp8b32Producer(const uint8_t* unit, int out, int in, int grp, int ns) {
+    using U = MxUnit<MX_FP8B32>;
+    o = threadIdx.x >> 1;
+    h = threadIdx.x & 1;
+    rc = gemm_rsrc(unit, (uint32_t)U::unit_bytes(out, in));
+    // channels past the group read its last channel (their rows of the B tile are unused)
+    const int og = grp * 128 + (o < 16 * ns ? o : 16 * ns - 1);
+    vo_c = (uint32_t)((size_t)og * in + 16 * h);
+    vo_s = U::scale_at(out, in, og, 0);
+  }
+
+  __device__ __forceinline__ void load(int kk, Raw& r) const {
+    r.c = __builtin_amdgcn_raw_buffer_load_b128(rc, vo_c, 32u * kk, 0);
+    r.sb = __builtin_amdgcn_raw_buffer_load_b8(rc, vo_s, (uint32_t)kk, 0);
+  }
+
+  __device__ __forceinline__ void decode(const Raw& r, uint32_t nat[8]) const {
+    const float sc = e8m0_to_f32(r.sb);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) fp8x4_to_bf16(r.c[j], sc, nat + 2 * j);
+  }
+};
+
+template <int FMT>
 __global__ __launch_bounds__(GEMM_THREADS, 2) void mxfp4_gemm_kernel(Mxfp4GemmArgs a) {
   __shared__ GemmShared sh;
   int item, grp;
@@ -251,9 +372,14 @@ __global__ __launch_bounds__(GEMM_THREADS, 2) void mxfp4_gemm_kernel(Mxfp4GemmAr
   it.grp = grp;
   it.nrows = itd.z;
   it.ns = min(8, a.out / 16 - grp * 8);
-  const size_t unit_bytes = (size_t)a.out * a.in / 2 + (size_t)a.out * a.in / 32;
-  Mxfp4Producer p(a.units + (size_t)e * unit_bytes, a.out, a.in, grp, it.ns);
-  gemm_item(it, sh, p);
+  const uint8_t* unit = a.units + (size_t)e * MxUnit<FMT>::unit_bytes(a.out, a.in);
+  if constexpr (FMT == MX_FP8B32) {
+    Fp8b32Producer p(unit, a.out, a.in, grp, it.ns);
+    gemm_item(it, sh, p);
+  } else {
+    Mxfp4Producer p(unit, a.out, a.in, grp, it.ns);
+    gemm_item(it, sh, p);
+  }
 }
 
 }  // namespace
@@ -266,32 +392,49 @@ hipError_t launch_mxfp4_decode(const uint8_t* unit, int out, int in, uint16_t* w
   return hipGetLastError();
 }
 
-int mxfp4_gemv_grid() {
-  static int cache[64];
+hipError_t launch_fp8b32_decode(const uint8_t* unit, int out, int in, uint16_t* w,
+                                hipStream_t s) {
+  const int total = out * (in / 8);
+  hipLaunchKernelGGL(fp8b32_decode_kernel, dim3((total + 255) / 256), dim3(256), 0, s, unit, out,
+                     in, w);
+  return hipGetLastError();
+}
+
+int mxfp4_gemv_grid(int fmt) {
+  static int cache[2][64];
   int dev = 0;
+  if (fmt != MX_FP4 && fmt != MX_FP8B32) return 0;
   if (hipGetDevice(&dev) != hipSuccess) return 0;
-  if (dev >= 0 && dev < 64 && cache[dev]) return cache[dev];
+  if (dev >= 0 && dev < 64 && cache[fmt][dev]) return cache[fmt][dev];
   int per_cu = 0, cus = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, mxfp4_gemv_kernel, MX_THREADS, 0) !=
-      hipSuccess)
-    return 0;
+  const hipError_t e =
+      fmt == MX_FP8B32
+          ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, mxfp4_gemv_kernel<MX_FP8B32>, MX_THREADS, 0)
+          : hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, mxfp4_gemv_kernel<MX_FP4>, MX_THREADS, 0);
+  if (e != hipSuccess) return 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
   int g = std::min(per_cu, GEMV_TARGET_PER_CU) * cus;
   if (g > GEMV_MAX_G) g = GEMV_MAX_G;
   if (g < 1) g = 1;
-  if (dev >= 0 && dev < 64) cache[dev] = g;
+  if (dev >= 0 && dev < 64) cache[fmt][dev] = g;
   return g;
 }
 
 hipError_t launch_mxfp4_gemv(const Mxfp4GemvArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(mxfp4_gemv_kernel, dim3(a.G), dim3(MX_THREADS), 0, s, a);
+  if (a.fmt == MX_FP8B32)
+    hipLaunchKernelGGL(mxfp4_gemv_kernel<MX_FP8B32>, dim3(a.G), dim3(MX_THREADS), 0, s, a);
+  else
+    hipLaunchKernelGGL(mxfp4_gemv_kernel<MX_FP4>, dim3(a.G), dim3(MX_THREADS), 0, s, a);
   return hipGetLastError();
 }
 
 hipError_t launch_mxfp4_gemm(const Mxfp4GemmArgs& a, hipStream_t s) {
   const int blocks = gemm_grid(a.max_items, a.groups);
   if (blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL(mxfp4_gemm_kernel, dim3(blocks), dim3(GEMM_THREADS), 0, s, a);
+  if (a.fmt == MX_FP8B32)
+    hipLaunchKernelGGL(mxfp4_gemm_kernel<MX_FP8B32>, dim3(blocks), dim3(GEMM_THREADS), 0, s, a);
+  else
+    hipLaunchKernelGGL(mxfp4_gemm_kernel<MX_FP4>, dim3(blocks), dim3(GEMM_THREADS), 0, s, a);
   return hipGetLastError();
 }
 

@@ -114,7 +114,12 @@ struct TrellisGemmArgs {
 };
 hipError_t launch_trellis_gemm(const TrellisGemmArgs& a, hipStream_t s);
 
+// Unit formats of the E8M0-scaled stores (mxfp4.hip).
+constexpr int MX_FP4 = 0;     // MXFP4: E2M1 codes, a scale per row and 32 inputs
+constexpr int MX_FP8B32 = 1;  // fp8b32: E4M3 codes, a scale per 32 x 32 block
+
 struct Mxfp4GemvArgs {
+  int fmt;               // MX_FP4 or MX_FP8B32
   const uint8_t* units;
   const uint16_t* x;     // bf16 [T][in]
   uint32_t x_bytes;      // size of x in bytes (< 2^31)
@@ -124,11 +129,13 @@ struct Mxfp4GemvArgs {
   float* partial;        // [in / 512][N][out]: the pieces of each slot
   int N, out, in, topk, G;
 };
-// Waves of the MXFP4 GEMV that the GPU holds at once; 0 on a HIP error.
-int mxfp4_gemv_grid();
+// The plan's wave target for the MXFP4 / fp8b32 GEMV (2 per SIMD, or fewer if the GPU
+// holds fewer); 0 on a HIP error.
+int mxfp4_gemv_grid(int fmt);
 hipError_t launch_mxfp4_gemv(const Mxfp4GemvArgs& a, hipStream_t s);
 
 struct Mxfp4GemmArgs {
+  int fmt;  // MX_FP4 or MX_FP8B32
   const uint8_t* units;
   const uint16_t* x;
   uint32_t x_bytes;  // size of x in bytes (< 2^31)
@@ -170,6 +177,8 @@ hipError_t launch_trellis_decode(const uint32_t* codes, int K, int out, int in, 
                                  int path, hipStream_t s);
 hipError_t launch_mxfp4_decode(const uint8_t* unit, int out, int in, uint16_t* w,
                                hipStream_t s);
+hipError_t launch_fp8b32_decode(const uint8_t* unit, int out, int in, uint16_t* w,
+                                hipStream_t s);
 hipError_t launch_swiglu(const float* g, const float* u, uint16_t* h, int64_t n,
                          hipStream_t s);
 hipError_t launch_nvfp4_transcode(const uint8_t* units, int E, int out, int in,

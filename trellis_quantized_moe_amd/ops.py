@@ -85,6 +85,26 @@ class Mxfp4Layer:
         return _lib.Mxfp4LayerC(self.E, self.out, self.in_, 0, self.units.data_ptr())
 
 
+@dataclass
+class Fp8b32Layer:
+    """An fp8b32 expert layer in device memory (see tq_fp8b32_layer in include/tq.h)."""
+    E: int
+    out: int
+    in_: int
+    units: torch.Tensor      # uint8 [E * unit_bytes]
+
+    @classmethod
+    def from_host(cls, layer, device="cuda"):
+        return cls(E=int(layer["E"]), out=int(layer["out"]), in_=int(layer["in"]),
+                   units=torch.from_numpy(np.ascontiguousarray(layer["units"], dtype=np.uint8)).to(device))
+
+    def with_units(self, units):
+        return Fp8b32Layer(self.E, self.out, self.in_, units)
+
+    def c_struct(self):
+        return _lib.Mxfp4LayerC(self.E, self.out, self.in_, 0, self.units.data_ptr())
+
+
 def workspace_bytes(T, topk, E, out, in_, flags=TQ_AUTO):
     return int(_lib.load().tq_workspace_bytes(T, topk, E, out, in_, flags))
 
@@ -130,6 +150,11 @@ def mxfp4_expert_gemm(layer, x, topk_ids, topk_w=None, flags=TQ_AUTO, out=None, 
                  layer.in_, x, topk_ids, topk_w, flags, out, ws, True)
 
 
+def fp8b32_expert_gemm(layer, x, topk_ids, topk_w=None, flags=TQ_AUTO, out=None, ws=None):
+    return _gemm(_lib.load().fp8b32_expert_gemm, layer.c_struct(), layer.E, layer.out,
+                 layer.in_, x, topk_ids, topk_w, flags, out, ws, True)
+
+
 def route_bucket(topk_ids, E, ws=None):
     """(counts [E], offsets [E+1], pairs [T*topk]) as int32 device tensors."""
     _require_cuda(topk_ids, ws)
@@ -159,6 +184,14 @@ def mxfp4_decode(unit, out_ch, in_):
     _require_cuda(unit)
     w = torch.empty((out_ch, in_), dtype=torch.int16, device=unit.device)
     check(_lib.load().mxfp4_decode(_ptr(unit), out_ch, in_, _ptr(w), _stream(unit.device)))
+    return w
+
+
+def fp8b32_decode(unit, out_ch, in_):
+    """bf16 bit patterns (int16) [out, in] of one fp8b32 unit."""
+    _require_cuda(unit)
+    w = torch.empty((out_ch, in_), dtype=torch.int16, device=unit.device)
+    check(_lib.load().fp8b32_decode(_ptr(unit), out_ch, in_, _ptr(w), _stream(unit.device)))
     return w
 
 
