@@ -284,6 +284,62 @@ def bench_ffn(torch, ops, args):
             "code_bytes": int(sum(wl[k]["codes"].nbytes for k in ("gate", "up", "down")))}
 
 
+def bench_shared(torch, ops, args):
+    """The shared expert's gate and up projections (1536 x 5120) in the fp8b32 store, every
+    token routed to it: a 128-token decode batch (unit bytes per step) and an 8,192-token
+    prefill chunk (flops per step)."""
+    from workloads import shared_expert
+    dev = torch.device("cuda", 0)
+    res = {}
+    for T, key in ((128, "decode"), (8192, "prefill")):
+        wl = shared_expert(T=T)
+        lay = wl["layer"]
+        L = ops.Fp8b32Layer.from_host(lay, dev)
+        x = torch.from_numpy(wl["x"].view(np.int16)).to(dev)
+        ids = torch.from_numpy(wl["topk_ids"]).to(dev)
+        y = torch.empty((T, 1, lay["out"]), dtype=torch.float32, device=dev)
+        ws = ops.workspace(T, 1, 1, lay["out"], lay["in"], ops.TQ_AUTO, dev)
+        reps = replicate(torch, L.units, L.units.numel()) if key == "decode" else [L.units]
+        layers = [L.with_units(u) for u in reps]
+
+        def step(r):
+            ops.fp8b32_expert_gemm(layers[r], x, ids, out=y, ws=ws)
+
+        for r in range(len(reps)):
+            step(r)
+        torch.cuda.synchronize()
+        # a step is short next to a graph launch on the host, so each graph holds up to 16
+        # consecutive steps (each on its own replica); every step still runs in full
+        per = min(16, len(reps))
+        graphs = []
+        for r0 in range(0, len(reps), per):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for r in range(r0, min(len(reps), r0 + per)):
+                    step(r)
+            graphs.append((g, min(len(reps), r0 + per) - r0))
+        steps = args.steps if key == "decode" else max(1, args.steps // 20)
+        n_launch = max(1, steps // per)
+        for i in range(max(1, min(args.warmup, steps) // per)):
+            graphs[i % len(graphs)][0].replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        done = 0
+        for i in range(n_launch):
+            g, k = graphs[i % len(graphs)]
+            g.replay()
+            done += k
+        torch.cuda.synchronize()
+        sec = (time.perf_counter() - t0) / done
+        steps = done
+        kmean, kmed = time_main_kernel(torch, ops, step, len(reps), min(args.kernel_iters, 50))
+        res[key] = {"sec_per_step": sec, "kernel_sec": kmean, "steps": steps, "T": T,
+                    "bytes": int(L.units.numel()), "flops": 2.0 * T * lay["out"] * lay["in"]}
+        log("shared %s: T = %d, %.1f MB of fp8b32 units, %d replicas" % (key, T, L.units.numel() / 1e6, len(reps)))
+        del graphs
+    return res
+
+
 def bench_prefill(torch, ops, args):
     from workloads import prefill_chunk
     wl = prefill_chunk()
@@ -453,8 +509,8 @@ def main():
     ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--kernel-iters", type=int, default=200)
-    ap.add_argument("--extras", default="mxfp4,prefill,nvfp4,ffn",
-                    help="comma list of secondary workloads (mxfp4, prefill, nvfp4, ffn) or 'none'")
+    ap.add_argument("--extras", default="mxfp4,prefill,nvfp4,ffn,shared",
+                    help="comma list of secondary workloads (mxfp4, prefill, nvfp4, ffn, shared) or 'none'")
     ap.add_argument("--cpu-sample-experts", type=int, default=0,
                     help="active experts in the CPU baseline sample (0 = all)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -566,6 +622,24 @@ def main():
             "ms_per_step": round(f["sec_per_step"] * 1e3, 5), "steps": f["steps"],
             "active_experts": f["n_active"], "compressed_bytes_per_step": f["bytes"],
             "frac_hbm": round(f["bytes"] / f["sec_per_step"] / 1e9 / HBM_PEAK_GBS, 4),
+        }
+    if "shared" in todo:
+        sh = bench_shared(torch, ops, args)
+        d, pf = sh["decode"], sh["prefill"]
+        extras["shared_expert_fp8b32"] = {
+            "workload": "shared expert gate+up (1536 x 5120, fp8b32: E4M3, E8M0 per 32 x 32 block), "
+                        "every token routed to it",
+            "decode_tokens": d["T"], "decode_GB/s": round(d["bytes"] / d["sec_per_step"] / 1e9, 2),
+            "decode_us_per_step": round(d["sec_per_step"] * 1e6, 3),
+            "decode_kernel": "mxfp4_gemv_kernel<fp8b32>",
+            "decode_kernel_us": round(d["kernel_sec"] * 1e6, 3),
+            "decode_frac_hbm": round(d["bytes"] / d["kernel_sec"] / 1e9 / HBM_PEAK_GBS, 4),
+            "unit_bytes": d["bytes"],
+            "prefill_tokens": pf["T"], "prefill_TFLOP/s": round(pf["flops"] / pf["sec_per_step"] / 1e12, 3),
+            "prefill_ms_per_step": round(pf["sec_per_step"] * 1e3, 5),
+            "prefill_kernel": "mxfp4_gemm_kernel<fp8b32>",
+            "prefill_kernel_us": round(pf["kernel_sec"] * 1e6, 3),
+            "prefill_frac_bf16_peak": round(pf["flops"] / pf["kernel_sec"] / 1e12 / F16_PEAK_TFLOPS, 4),
         }
     if extras:
         line["extras"] = extras

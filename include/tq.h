@@ -43,7 +43,8 @@ extern "C" {
 #define TQ_EHIP (-5)         /* a HIP runtime call failed                               */
 
 /* ---- flags of the expert GEMM calls -------------------------------------------------- */
-#define TQ_AUTO 0u     /* choose the decode-batch kernel when T*topk <= 16*E, else prefill */
+#define TQ_AUTO 0u     /* prefill when T*topk > 16*E and its items, groups*ceil(T*topk/128),
+                          number at least 256; else the decode batch (when it fits) */
 #define TQ_GEMV 1u     /* force the decode-batch kernel (grouped GEMV, tokens in 8s)       */
 #define TQ_GEMM 2u     /* force the prefill kernel (route bucketing + grouped MFMA GEMM)   */
 #define TQ_COMBINE 4u  /* write y[T][out] = sum over k = 0..topk-1 (in order) of the slots */

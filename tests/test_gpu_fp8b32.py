@@ -94,10 +94,11 @@ def test_small_layer(flags):
     assert rel_l2(y, ref) <= TOL
 
 
-@pytest.mark.parametrize("T, flags", [(128, 0), (128, 2), (1024, 0)])
+@pytest.mark.parametrize("T, flags", [(128, 0), (128, 2), (1024, 0), (1024, 2), (4096, 0)])
 def test_shared_expert(T, flags):
     # the shared expert's gate and up projections (1536 x 5120), every token routed to it:
-    # 128 tokens take the decode batch by default, 1024 the prefill GEMM
+    # up to 2048 tokens take the decode batch by default (their 12 x T/128 prefill items are
+    # fewer than the GPU's compute units), 4096 the prefill GEMM; flags 2 forces the GEMM
     wl = shared_expert(T=T)
     y = run(wl["layer"], wl["x"], wl["topk_ids"], None, flags=flags)
     ref = reference(wl["layer"], wl["x"], wl["topk_ids"], None)

@@ -71,11 +71,17 @@ bool flags_valid(uint32_t flags) {
   return (flags & ~15u) == 0 && (flags & 3u) != 3u;
 }
 
-bool use_gemm(int64_t T, int topk, int E, uint32_t flags) {
+// The prefill GEMM pays off when experts average more than 16 routed slots and its items
+// (128 routed rows of one group) are enough to give every compute unit of the GPU one;
+// otherwise the decode batch, whose waves take 8 or 16 slots each, spreads the work wider.
+constexpr int64_t GEMM_MIN_ITEMS = 256;
+
+bool use_gemm(int64_t T, int topk, int E, int groups, uint32_t flags) {
   const uint32_t mode = flags & 3u;
   if (mode == TQ_GEMV) return false;
   if (mode == TQ_GEMM) return true;
-  return T * topk > 16LL * E;
+  const int64_t N = T * topk;
+  return N > 16LL * E && (int64_t)groups * ((N + 127) / 128) >= GEMM_MIN_ITEMS;
 }
 
 int check_routes(int64_t T, int topk, const void* ids) {
@@ -112,13 +118,24 @@ T* at(void* ws, size_t off) {
 
 namespace tq {
 
+// Routed slots one decode-batch wave takes: the token rows of its matrix-core operations.
+int gemv_rows(bool mxfp4) { return mxfp4 ? 16 : 8; }
+
+// Upper bound on the decode-batch plan's (group, chunk) pairs, each of which gets at least
+// one wave: every active expert has ceil(cnt / R) <= cnt / R + 1 chunks.
+int64_t gemv_chunk_bound(int64_t N, int E, int groups, bool mxfp4) {
+  const int R = gemv_rows(mxfp4);
+  return (int64_t)groups * ((int64_t)E + (N + R - 1) / R);
+}
+
 WsLayout ws_layout(int64_t T, int topk, int E, int out, int in, uint32_t flags, bool mxfp4) {
   WsLayout L;
   const int64_t N = T * topk;
   L.groups = (out + 127) / 128;
-  L.gemm = use_gemm(T, topk, E, flags);
-  // a decode batch gives every active expert group at least one wave of its own
-  if ((flags & 3u) == TQ_AUTO && (int64_t)E * L.groups > tq::GEMV_MAX_G) L.gemm = true;
+  L.gemm = use_gemm(T, topk, E, L.groups, flags);
+  // a decode batch gives every active expert group and chunk at least one wave of its own
+  if ((flags & 3u) == TQ_AUTO && gemv_chunk_bound(N, E, L.groups, mxfp4) > tq::GEMV_MAX_G)
+    L.gemm = true;
   size_t off = 256;  // status word
   if (!L.gemm) {
     // planned decode batch: plan records, prepared activations (trellis), per-piece partial
@@ -485,9 +502,10 @@ static int common_checks(int E, int out, int in, const void* x, int64_t T, const
   *layout = tq::ws_layout(T, topk, E, out, in, flags, mxfp4);
   if ((layout->gemm || !mxfp4) && E > 4096)
     return fail(TQ_EINVAL, "this path supports E <= 4096 (E = %d)", E);
-  if (!layout->gemm && (int64_t)E * layout->groups > tq::GEMV_MAX_G)
-    return fail(TQ_EINVAL, "decode batches take at most %d expert groups (E * out / 128)",
-                tq::GEMV_MAX_G);
+  if (!layout->gemm && tq::gemv_chunk_bound(T * topk, E, layout->groups, mxfp4) > tq::GEMV_MAX_G)
+    return fail(TQ_EINVAL,
+                "decode batches take at most %d (group, chunk) pairs: (E + T*topk/%d) * out/128",
+                tq::GEMV_MAX_G, tq::gemv_rows(mxfp4));
   if ((layout->gemm || !mxfp4) && T * (int64_t)in * (layout->gemm ? 2 : 4) >= ((int64_t)1 << 31))
     return fail(TQ_EINVAL, "the prepared activations (T * in * %d bytes) must stay below 2^31",
                 layout->gemm ? 2 : 4);
@@ -548,7 +566,7 @@ int trellis_expert_gemm(const tq_trellis_layer* L, const void* x, int64_t T,
     const int G = tq::trellis_gemv_grid();
     if (G <= 0) return fail(TQ_EHIP, "could not size the GEMV grid");
     // launched waves: the plan's target, or one per expert group when that is more
-    const int Gl = (int)std::max<int64_t>(G, (int64_t)L->E * W.groups);
+    const int Gl = (int)std::max<int64_t>(G, tq::gemv_chunk_bound(N, L->E, W.groups, false));
     tq::PlanArgs p{};
     p.ids = topk_ids;
     p.N = (int)N;
@@ -559,6 +577,7 @@ int trellis_expert_gemm(const tq_trellis_layer* L, const void* x, int64_t T,
     p.unit_bytes = 0;
     p.groups = W.groups;
     p.S = L->in / 64;
+    p.R = tq::gemv_rows(false);
     p.G = G;
     p.Gl = Gl;
     p.info = at<int32_t>(ws, W.info);
@@ -682,7 +701,7 @@ int mx_expert_gemm(const MxLayer* L, const void* x, int64_t T, const int32_t* to
   if (!W.gemm) {
     const int G = tq::mxfp4_gemv_grid(L->fmt);
     if (G <= 0) return fail(TQ_EHIP, "could not size the GEMV grid");
-    const int Gl = (int)std::max<int64_t>(G, (int64_t)L->E * W.groups);
+    const int Gl = (int)std::max<int64_t>(G, tq::gemv_chunk_bound(N, L->E, W.groups, true));
     tq::PlanArgs p{};
     p.ids = topk_ids;
     p.N = (int)N;
@@ -692,6 +711,7 @@ int mx_expert_gemm(const MxLayer* L, const void* x, int64_t T, const int32_t* to
     p.unit_bytes = unit;
     p.groups = W.groups;
     p.S = L->in / 128;
+    p.R = tq::gemv_rows(true);
     p.G = G;
     p.Gl = Gl;
     p.info = at<int32_t>(ws, W.info);

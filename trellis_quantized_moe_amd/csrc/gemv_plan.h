@@ -10,14 +10,18 @@
 //
 // Work is counted in steps: one step is 64 inputs of one group of 128 output channels, so
 // a group has S = in / 64 steps. A step of a trellis expert of width K costs K (its bytes
-// are proportional to K); an MXFP4 step costs 1. Every active expert's group is split into
-// W(k) pieces of consecutive steps (W depends only on the expert's cost k), piece j taking
+// are proportional to K); an MXFP4 step costs 1. An expert's routed slots come in chunks of
+// R (the rows one wave's matrix-core operations hold: 8 tokens for trellis, 16 for the
+// E8M0-scaled stores), and each chunk of each group is its own work. Every active expert's
+// group and chunk is split into W(k) pieces of consecutive steps (W depends only on the
+// expert's cost k), piece j taking
 // steps floor(j S / W) .. floor((j + 1) S / W) - 1, and every piece is one wave's whole
 // work: no wave crosses from one expert or group into another, so a wave's load stream
 // never restarts, and the pieces of a group differ by at most one step. W(k) =
 // ceil(S / floor(T / k)) for the smallest per-wave cost bound T >= 4 * kmax (kmax the
-// largest active cost) whose total number of waves fits the GPU's resident waves (or the
-// number of active groups, when that is larger); T >= 4 kmax keeps W(k) <= S / 4 = in / 256.
+// largest active cost) whose total number of waves fits the wave target (or the number of
+// active groups and chunks, when that is larger); T >= 4 kmax keeps W(k) <= S / 4 =
+// in / 256. A slot's pieces are the W(k) pieces of its group and chunk.
 // Pieces are summed in piece order, so results are independent of timing, and the split
 // depends only on which experts are active, never on the order of the tokens.
 #pragma once
@@ -37,8 +41,9 @@ struct alignas(16) PlanRec {
   int32_t np;     // pieces per group, W(k)
 };
 
-// desc[w], the piece of wave w (int4): {active expert index, or -1 for no work; group;
-// piece index; its steps s0 .. s1 - 1 packed as s0 | s1 << 16}.
+// desc[w], the piece of wave w (int4): {active expert index, or -1 for no work; group |
+// chunk << 16 (the chunk of the expert's slot list: slots c R .. c R + R - 1); piece index;
+// its steps s0 .. s1 - 1 packed as s0 | s1 << 16}.
 
 // Per-slot record for the reduction: {expert id, pieces per group, k, 0}, or code in .x:
 constexpr int SLOT_EMPTY = -1;     // id -1: output 0
@@ -47,7 +52,13 @@ constexpr int SLOT_BAD_UNIT = -3;  // expert with a bad width byte or offset: Na
 
 constexpr int PLAN_MAX_E = 4096;
 constexpr int PLAN_THREADS = 1024;
-constexpr int GEMV_MAX_G = 16384;  // bound on the GEMV grid (desc buffer size)
+// An expert with at most PLAN_OWN_PIECES pieces has them written by its own thread of the
+// plan; larger ones (at most GEMV_MAX_G / PLAN_OWN_PIECES of them) by the whole block.
+constexpr int PLAN_OWN_PIECES = 32;
+// Bound on the GEMV grid (desc buffer size). It keeps a chunk index below 2^15 and the
+// plan's per-cost chunk counts below 2^16 (the host checks groups * (E + N / R) against it).
+constexpr int GEMV_MAX_G = 32768;
+constexpr int PLAN_MAX_BIG = GEMV_MAX_G / PLAN_OWN_PIECES;
 // Waves per compute unit the plan aims for (2 per SIMD). The decode-batch kernels are bound
 // by VALU issue (the decode), not by memory latency: two waves per SIMD keep the VALU busy,
 // and fewer, longer pieces spend less on each wave's setup and on the partial sums that the

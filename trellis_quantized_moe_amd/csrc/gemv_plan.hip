@@ -79,6 +79,8 @@ __device__ void plan_block(const PlanArgs& a) {
   __shared__ int s_start[PLAN_MAX_E];   // slot counts, then list starts
   __shared__ int s_aidx[PLAN_MAX_E];    // active index, or SLOT_EMPTY / SLOT_BAD_UNIT
   __shared__ uint8_t s_ka[PLAN_MAX_E];  // step cost by active index
+  __shared__ int4 s_big[PLAN_MAX_BIG];  // experts whose pieces the whole block writes
+  __shared__ int s_nbig;
   __shared__ int s_T;
   __shared__ uint32_t s_status;
   const int tid = threadIdx.x;
@@ -119,6 +121,7 @@ __device__ void plan_block(const PlanArgs& a) {
     if (mine(j)) s_start[e0 + j] = 0;
   if (tid == 0) {
     s_status = 0;
+    s_nbig = 0;
     s_T = 0x7FFFFFFF;
   }
   lds_barrier();
@@ -142,25 +145,32 @@ __device__ void plan_block(const PlanArgs& a) {
   }
   lds_barrier();
 
-  // scan over experts: list starts and, per step cost 1..4, the active experts before each
-  // (counts of cost 1 and 2 share one int, 3 and 4 another: 16 bits each, as E <= 4096)
+  // scan over experts: list starts, the active experts before each (its active index) and,
+  // per step cost 1..4, the chunks of R slots of the active experts before each (chunks of
+  // cost 1 and 2 share one int, 3 and 4 another: 16 bits each, as the host keeps
+  // E + N / R <= GEMV_MAX_G)
   int cnt[PLAN_PER];
-  int sv[3] = {0, 0, 0};  // slots; active of cost 1 | 2 << 16; active of cost 3 | 4 << 16
+  int sv[4] = {0, 0, 0, 0};  // slots; chunks of cost 1 | 2 << 16; of cost 3 | 4 << 16; active
 #pragma unroll
   for (int j = 0; j < PLAN_PER; ++j) {
     cnt[j] = mine(j) ? s_start[e0 + j] : 0;
     sv[0] += cnt[j];
-    if (cnt[j] > 0 && kk[j] > 0) sv[kk[j] >= 3 ? 2 : 1] += (kk[j] & 1) ? 1 : 0x10000;
+    if (cnt[j] > 0 && kk[j] > 0) {
+      const int nch = (cnt[j] + a.R - 1) / a.R;
+      sv[kk[j] >= 3 ? 2 : 1] += (kk[j] & 1) ? nch : (nch << 16);
+      sv[3] += 1;
+    }
   }
-  int tot3[3];
-  block_scan<3>(sv, tot3);
-  const int tot[5] = {0, tot3[1] & 0xFFFF, tot3[1] >> 16, tot3[2] & 0xFFFF, tot3[2] >> 16};
-  const int n_act = tot[1] + tot[2] + tot[3] + tot[4];
+  int tot4[4];
+  block_scan<4>(sv, tot4);
+  const int tot[5] = {0, tot4[1] & 0xFFFF, tot4[1] >> 16, tot4[2] & 0xFFFF, tot4[2] >> 16};
+  const int n_act = tot4[3];
+  const int n_chunks = tot[1] + tot[2] + tot[3] + tot[4];
   const int kmax = tot[4] ? 4 : tot[3] ? 3 : tot[2] ? 2 : 1;
 
   // the split: the smallest cost bound T in [4 kmax, S kmax] whose waves fit the target;
-  // T = S kmax (one piece per group) always does
-  const int64_t target = max((int64_t)a.G, (int64_t)groups * n_act);
+  // T = S kmax (one piece per group and chunk) always does
+  const int64_t target = max((int64_t)a.G, (int64_t)groups * n_chunks);
   for (int T0 = 4 * kmax; T0 <= S * kmax; T0 += PLAN_THREADS) {  // uniform
     const int T = T0 + tid;
     int best = 0x7FFFFFFF;
@@ -183,10 +193,11 @@ __device__ void plan_block(const PlanArgs& a) {
   for (int k = 1; k <= 4; ++k) Wk[k] = k <= Tb ? pieces_for(S, Tb, k) : 1;
   const int waves = groups * (tot[1] * Wk[1] + tot[2] * Wk[2] + tot[3] * Wk[3] + tot[4] * Wk[4]);
 
-  // active experts: records, and their waves' pieces, group-major, piece p of a group
-  // taking steps floor(p S / W) .. floor((p + 1) S / W) - 1 (advanced without division)
+  // active experts: records, and their waves' pieces, group-major, then chunk by chunk of
+  // the slot list, piece p of a group and chunk taking steps floor(p S / W) .. floor((p + 1)
+  // S / W) - 1 (advanced without division)
   const int pre[5] = {0, sv[1] & 0xFFFF, sv[1] >> 16, sv[2] & 0xFFFF, sv[2] >> 16};
-  int sc = sv[0], sa = pre[1] + pre[2] + pre[3] + pre[4];
+  int sc = sv[0], sa = sv[3];
   int wb = groups * (pre[1] * Wk[1] + pre[2] * Wk[2] + pre[3] * Wk[3] + pre[4] * Wk[4]);
 #pragma unroll
   for (int j = 0; j < PLAN_PER; ++j) {
@@ -207,18 +218,25 @@ __device__ void plan_block(const PlanArgs& a) {
         r.np = W;
         a.rec[sa] = r;
         const int base = S / W, rem = S - base * W;
-        for (int grp = 0, q = wb; grp < groups; ++grp) {
-          int s0 = 0, acc = 0;
-          for (int p = 0; p < W; ++p, ++q) {
-            acc += rem;
-            const int s1 = s0 + base + (acc >= W ? 1 : 0);
-            acc -= acc >= W ? W : 0;
-            a.desc[q] = make_int4(sa, grp, p, s0 | (s1 << 16));
-            s0 = s1;
+        const int nch = (cnt[j] + a.R - 1) / a.R;
+        if (groups * nch * W <= PLAN_OWN_PIECES) {
+          for (int grp = 0, q = wb; grp < groups; ++grp) {
+            for (int c = 0; c < nch; ++c) {
+              int s0 = 0, acc = 0;
+              for (int p = 0; p < W; ++p, ++q) {
+                acc += rem;
+                const int s1 = s0 + base + (acc >= W ? 1 : 0);
+                acc -= acc >= W ? W : 0;
+                a.desc[q] = make_int4(sa, grp | (c << 16), p, s0 | (s1 << 16));
+                s0 = s1;
+              }
+            }
           }
+        } else {  // many pieces (a hot expert, or many groups): the whole block writes them
+          s_big[atomicAdd(&s_nbig, 1)] = make_int4(sa, wb, W, nch);
         }
         sa += 1;
-        wb += groups * W;
+        wb += groups * W * nch;
       } else {
         s_aidx[e] = cnt[j] > 0 ? SLOT_BAD_UNIT : SLOT_EMPTY;
       }
@@ -229,8 +247,24 @@ __device__ void plan_block(const PlanArgs& a) {
     a.info[0] = n_act;
     a.info[1] = waves;
     a.info[2] = Tb;
+    a.info[3] = n_chunks;
   }
   lds_barrier();
+
+  // the pieces of the experts with many: wave v of the block takes experts v, v + 16, ...,
+  // its lanes every 64th piece: wave wb + l is group l / (nch W), chunk (l / W) % nch,
+  // piece l % W, whose steps are floor(p S / W) .. floor((p + 1) S / W) - 1 (the same as
+  // the advancing form above)
+  const int nbig = s_nbig;
+  for (int b = tid >> 6; b < nbig; b += PLAN_WAVES) {  // uniform per wave
+    const int4 bg = s_big[b];
+    const int W = bg.z, cw = bg.w * W, nd = groups * cw;
+    for (int l = tid & 63; l < nd; l += 64) {
+      const int grp = l / cw, r = l - grp * cw, c = r / W, p = r - c * W;
+      const int s0 = p * S / W, s1 = (p + 1) * S / W;
+      a.desc[bg.y + l] = make_int4(bg.x, grp | (c << 16), p, s0 | (s1 << 16));
+    }
+  }
 
   // slot lists and per-slot records
   auto place = [&](int i, int v, int r) {

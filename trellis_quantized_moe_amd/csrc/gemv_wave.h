@@ -38,13 +38,15 @@ typedef const __attribute__((address_space(4))) int4* ConstDesc;
 
 // The piece of wave w (see gemv_plan.h): false when the wave has none.
 struct Piece {
-  int ai, grp, idx, s0, s1;
+  int ai, grp, chunk, idx, s0, s1;
 };
 __device__ __forceinline__ bool load_piece(const int4* desc, int w, Piece& p) {
   const ConstDesc dp = (ConstDesc)desc + w;
   p.ai = dp->x;
   if (p.ai < 0) return false;
-  p.grp = dp->y;
+  const int gc = dp->y;
+  p.grp = gc & 0xFFFF;
+  p.chunk = gc >> 16;
   p.idx = dp->z;
   const int span = dp->w;
   p.s0 = span & 0xFFFF;

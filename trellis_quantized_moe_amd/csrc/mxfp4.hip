@@ -98,7 +98,8 @@ __global__ __launch_bounds__(256) void mxfp4_decode_kernel(const uint8_t* __rest
 // inputs 32 g .. 32 g + 31 of the step (16 bytes of MXFP4, 32 of fp8b32), takes that
 // block's scale, and feeds 4 bf16 16 x 16 x 32 matrix-core operations: operation c takes
 // inputs 32 g + 8 c .. + 7 of every lane group, against the same inputs of up to 16 routed
-// token rows (bf16 x as given; rows past the expert's count are zero). Codes and
+// token rows of one chunk of the expert's slot list (bf16 x as given; rows past the
+// expert's count are zero). Codes and
 // activations are requested D steps ahead, into register sets used in turn. The scales
 // come in blocks of 4 steps: 16-byte loads bring the group's scale bytes of the next block
 // into registers (MXFP4: 128 rows, two loads per lane; fp8b32: the 4 row blocks, lanes
@@ -257,7 +258,8 @@ __global__ __launch_bounds__(MX_THREADS, MX_WAVES_PER_SIMD) void mxfp4_gemv_kern
   const int ns = min(8, a.out / 16 - pc.grp * 8);
   const Rsrc ru = make_rsrc(a.units + r.off, (uint32_t)MxUnit<FMT>::unit_bytes(a.out, a.in));
   float* dst = a.partial + (size_t)pc.idx * a.N * a.out + pc.grp * 128 + n;
-  for (int c0 = 0; c0 < r.cnt; c0 += 16) {
+  {
+    const int c0 = 16 * pc.chunk;  // this wave's chunk of the slot list
     const int rows = min(16, r.cnt - c0);
     const int slot = n < rows ? a.list[r.start + c0 + n] : -1;
     f32x4 acc[8];

@@ -40,9 +40,11 @@ struct PlanArgs {
   const int64_t* code_off;  // trellis unit offsets (with bits)
   int64_t unit_bytes;       // MXFP4: expert e's unit is at e * unit_bytes
   int groups, S;            // output groups per expert, steps per group (in / 64)
-  int G;                    // resident GEMV waves (the split's target)
+  int R;                    // routed slots one wave takes at most (a chunk of a slot list)
+  int G;                    // the split's wave target
   int Gl;                   // launched GEMV waves (desc entries written)
-  int32_t* info;            // [0] active experts, [1] waves with work, [2] cost bound T
+  int32_t* info;            // [0] active experts, [1] waves with work, [2] cost bound T,
+                            // [3] chunks
   PlanRec* rec;             // [E]
   int4* desc;               // [Gl]
   int32_t* list;            // [N]

@@ -16,8 +16,10 @@
 // once per call). The load of a strip's next words is issued right after its current words
 // are decoded.
 //
-// At the end the wave joins each token's two halves (256 hi + lo) and stores the piece's
-// partial sums; the reduction launch adds the pieces in order and applies the epilogue.
+// A wave takes one chunk of up to 8 of its expert's routed tokens (the plan gives each
+// chunk its own waves). At the end it joins each token's two halves (256 hi + lo) and
+// stores the piece's partial sums; the reduction launch adds the pieces in order and
+// applies the epilogue.
 #include "gemv_wave.h"
 #include "tq_internal.h"
 #include "trellis_decode.h"
@@ -188,17 +190,18 @@ __device__ __forceinline__ void stream(const TrellisGemvArgs& a, const uint32_t*
       step_body<K, false>(cw[d], xa[d], xb[d], rc, cvo, 0, sso, lo.sel3, rx, xvo, 0, acc);
 }
 
-// One piece: expert record r, steps s0 .. s1 - 1 of group grp; sums to partial[piece], in
-// chunks of up to 8 routed tokens.
+// One piece: expert record r, steps s0 .. s1 - 1 of group grp for chunk `chunk` of the
+// expert's slot list (up to 8 routed tokens); sums to partial[piece].
 template <int K>
 __device__ __forceinline__ void run_piece(const TrellisGemvArgs& a, const PlanRec& r, int grp,
-                                          int s0, int s1, int piece) {
+                                          int chunk, int s0, int s1, int piece) {
   const int lane = threadIdx.x & 63, n = lane & 15, g = lane >> 4;
   const int j = n & 7, half = n >> 3;  // this lane's A row: token j of the chunk, its half
   const int ns = min(8, a.out / 16 - grp * 8);
   const uint32_t* unit = a.codes + r.off / 4;
   float* dst = a.partial + (size_t)piece * a.N * a.out + grp * 128 + n;
-  for (int c0 = 0; c0 < r.cnt; c0 += 8) {
+  {
+    const int c0 = 8 * chunk;
     const int rows = min(8, r.cnt - c0);
     // lanes with j = m hold the slot of token m of the chunk
     const int slot = j < rows ? a.list[r.start + c0 + j] : -1;
@@ -229,11 +232,11 @@ __global__ __launch_bounds__(GEMV_THREADS, GEMV_WAVES_PER_SIMD) void trellis_gem
   if (!load_piece(a.desc, blockIdx.x, pc)) return;
   const PlanRec r = load_rec(a.rec, pc.ai);
   if (r.k == 2)
-    run_piece<2>(a, r, pc.grp, pc.s0, pc.s1, pc.idx);
+    run_piece<2>(a, r, pc.grp, pc.chunk, pc.s0, pc.s1, pc.idx);
   else if (r.k == 3)
-    run_piece<3>(a, r, pc.grp, pc.s0, pc.s1, pc.idx);
+    run_piece<3>(a, r, pc.grp, pc.chunk, pc.s0, pc.s1, pc.idx);
   else
-    run_piece<4>(a, r, pc.grp, pc.s0, pc.s1, pc.idx);
+    run_piece<4>(a, r, pc.grp, pc.chunk, pc.s0, pc.s1, pc.idx);
 }
 
 // ---- decode hook ------------------------------------------------------------------------
