@@ -435,6 +435,20 @@ def drive(torch, ops, which, iters):
         for i in range(iters):
             ops.trellis_expert_gemm(layers[i % len(layers)], x, ids, flags=ops.TQ_ROTATE,
                                     out=y, ws=ws)
+    elif which == "shared":
+        from workloads import shared_expert
+        for T in (128, 8192):
+            wl = shared_expert(T=T)
+            lay = wl["layer"]
+            L = ops.Fp8b32Layer.from_host(lay, dev)
+            x = torch.from_numpy(wl["x"].view(np.int16)).to(dev)
+            ids = torch.from_numpy(wl["topk_ids"]).to(dev)
+            reps = replicate(torch, L.units, L.units.numel()) if T == 128 else [L.units]
+            layers = [L.with_units(u) for u in reps]
+            y = torch.empty((T, 1, lay["out"]), dtype=torch.float32, device=dev)
+            ws = ops.workspace(T, 1, 1, lay["out"], lay["in"], ops.TQ_AUTO, dev)
+            for i in range(iters):
+                ops.fp8b32_expert_gemm(layers[i % len(layers)], x, ids, out=y, ws=ws)
     elif which == "nvfp4":
         lay = mxfp4_decode_layer()["layer"]
         L = ops.Mxfp4Layer.from_host(lay, dev)
@@ -514,7 +528,7 @@ def main():
     ap.add_argument("--cpu-sample-experts", type=int, default=0,
                     help="active experts in the CPU baseline sample (0 = all)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--drive", choices=["mixed", "mxfp4", "prefill", "nvfp4"],
+    ap.add_argument("--drive", choices=["mixed", "mxfp4", "prefill", "nvfp4", "shared"],
                     help="only run --steps steps of one workload (for rocprofv3)")
     ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="summarise rocprofv3 FETCH_SIZE / WRITE_SIZE runs of --drive mixed")
