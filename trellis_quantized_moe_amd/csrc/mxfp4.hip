@@ -99,21 +99,20 @@ __global__ __launch_bounds__(256) void mxfp4_decode_kernel(const uint8_t* __rest
 // block's scale, and feeds 4 bf16 16 x 16 x 32 matrix-core operations: operation c takes
 // inputs 32 g + 8 c .. + 7 of every lane group, against the same inputs of up to 16 routed
 // token rows of one chunk of the expert's slot list (bf16 x as given; rows past the
-// expert's count are zero). Codes and
-// activations are requested D steps ahead, into register sets used in turn. The scales
+// expert's count are zero). Codes are requested one step ahead, strip by strip after each
+// strip's last use; activations one step ahead too, into a second register set, at the
+// start of a step, so a step's first products never wait for its last code loads. The scales
 // come in blocks of 4 steps: 16-byte loads bring the group's scale bytes of the next block
 // into registers (MXFP4: 128 rows, two loads per lane; fp8b32: the 4 row blocks, lanes
 // 0..3), which go to a double-buffered LDS stage at the block boundary; each lane then
 // reads its byte per strip and step from LDS, so a step issues no scale load of its own.
 // At the end the wave stores its accumulators as the piece's partial sums.
 constexpr int MX_THREADS = 64;
-constexpr int MX_WAVES_PER_SIMD = 3;
-constexpr int MX_D = 1;
+constexpr int MX_WAVES_PER_SIMD = 3;  // MXFP4; fp8b32 (twice the code registers) 2
 
 template <int FMT>
 struct MxStep {
   u32x4 code[8][MxUnit<FMT>::kFp8 ? 2 : 1];
-  u32x4 x[4];
 };
 
 struct MxShared {
@@ -127,15 +126,26 @@ __device__ __forceinline__ int strip_scale_offset(int s8) {
   return MxUnit<FMT>::kFp8 ? 16 * (s8 >> 1) : 256 * s8;
 }
 
+__device__ __forceinline__ void load_x4(u32x4 (&x)[4], Rsrc rx, uint32_t xvo, uint32_t xst) {
+#pragma unroll
+  for (int c = 0; c < 4; ++c) x[c] = __builtin_amdgcn_raw_buffer_load_b128(rx, xvo, xst + 16u * c, 0);
+}
+
+// One step: 8 strips of the codes in `cur` against the activations x. With RELOAD, each
+// strip's codes are replaced by those of the next step (scalar offset cst) after their
+// last use.
 template <int FMT, bool RELOAD>
 __device__ __forceinline__ void mx_step(MxStep<FMT>& cur, const uint8_t* sc, Rsrc ru, uint32_t cvo,
-                                        const uint32_t cso[8], uint32_t cst, Rsrc rx,
-                                        uint32_t xvo, uint32_t xst, f32x4 acc[8]) {
-  // sc: this lane's scale byte of strip 0 for this step
-  // each reload replaces the registers of the value it follows, after that value's last use
+                                        const uint32_t cso[8], uint32_t cst,
+                                        const u32x4 (&x)[4], f32x4 acc[8]) {
+  // sc: this lane's scale byte of strip 0 for this step; the 8 strips' bytes are read
+  // together, so one LDS wait covers them
+  uint32_t sbyte[8];
+#pragma unroll
+  for (int s8 = 0; s8 < 8; ++s8) sbyte[s8] = sc[strip_scale_offset<FMT>(s8)];
 #pragma unroll
   for (int s8 = 0; s8 < 8; ++s8) {
-    const float scale = e8m0_to_f32(sc[strip_scale_offset<FMT>(s8)]);
+    const float scale = e8m0_to_f32(sbyte[s8]);
     uint32_t b[4][4];
     if constexpr (MxUnit<FMT>::kFp8) {
 #pragma unroll
@@ -156,13 +166,9 @@ __device__ __forceinline__ void mx_step(MxStep<FMT>& cur, const uint8_t* sc, Rsr
     }
 #pragma unroll
     for (int c = 0; c < 4; ++c)
-      acc[s8] = mfma_bf16(cur.x[c], (u32x4){b[c][0], b[c][1], b[c][2], b[c][3]}, acc[s8]);
+      acc[s8] = mfma_bf16(x[c], (u32x4){b[c][0], b[c][1], b[c][2], b[c][3]}, acc[s8]);
   }
   __builtin_amdgcn_sched_barrier(0);
-  if (RELOAD) {
-#pragma unroll
-    for (int c = 0; c < 4; ++c) cur.x[c] = __builtin_amdgcn_raw_buffer_load_b128(rx, xvo, xst + 16u * c, 0);
-  }
 }
 
 template <int FMT>
@@ -189,33 +195,29 @@ __device__ __forceinline__ void mx_stream(const Mxfp4GemvArgs& a, MxShared& sh, 
   }
   const Rsrc rx = make_rsrc(a.x, a.x_bytes);
   const uint32_t xvo = tok >= 0 ? (uint32_t)tok * (uint32_t)a.in * 2u + 64u * g : 0x80000000u;
-  const int steps = s1 - s0, last = steps - 1;
-  // scalar offsets of step st (clamped to the last step, whose data is read again)
-  auto cst = [&](int st) { return cstep * (uint32_t)(s0 + (st < last ? st : last)); };
-  auto xst = [&](int st) { return 256u * (uint32_t)(s0 + (st < last ? st : last)); };
+  const int steps = s1 - s0;
+  auto cst = [&](int st) { return cstep * (uint32_t)(s0 + st); };
+  auto xst = [&](int st) { return 256u * (uint32_t)(s0 + st); };
   // scale bytes of the 4-step block starting at step st (4 bytes per row and step)
   auto bso = [&](int st) { return 4u * (uint32_t)(s0 + st); };
-  MxStep<FMT> ring[MX_D];
+  // codes one step ahead, reloaded strip by strip; activations in two register sets, the
+  // next step's requested at the start of a step (ahead of its codes), so a step's first
+  // products wait only for what they use
+  MxStep<FMT> ring;
 #pragma unroll
-  for (int d = 0; d < MX_D; ++d)
-#pragma unroll
-    for (int s8 = 0; s8 < 8; ++s8) {
-      ring[d].code[s8][0] = __builtin_amdgcn_raw_buffer_load_b128(ru, cvo, cso[s8] + cst(d), 0);
-      if constexpr (U::kFp8)
-        ring[d].code[s8][1] = __builtin_amdgcn_raw_buffer_load_b128(ru, cvo + 16u, cso[s8] + cst(d), 0);
-    }
+  for (int s8 = 0; s8 < 8; ++s8) {
+    ring.code[s8][0] = __builtin_amdgcn_raw_buffer_load_b128(ru, cvo, cso[s8] + cst(0), 0);
+    if constexpr (U::kFp8)
+      ring.code[s8][1] = __builtin_amdgcn_raw_buffer_load_b128(ru, cvo + 16u, cso[s8] + cst(0), 0);
+  }
   u32x4 sa = __builtin_amdgcn_raw_buffer_load_b128(ru, svo0, bso(0), 0);
   u32x4 sb = U::kFp8 ? sa : __builtin_amdgcn_raw_buffer_load_b128(ru, svo1, bso(0), 0);
-#pragma unroll
-  for (int d = 0; d < MX_D; ++d)
-#pragma unroll
-    for (int c = 0; c < 4; ++c)
-      ring[d].x[c] = __builtin_amdgcn_raw_buffer_load_b128(rx, xvo, xst(d) + 16u * c, 0);
+  u32x4 xr[2][4];
+  load_x4(xr[0], rx, xvo, xst(0));
 #pragma unroll
   for (int s8 = 0; s8 < 8; ++s8) acc[s8] = (f32x4){0.f, 0.f, 0.f, 0.f};
   // this lane's scale byte of strip 0: step k of the block at + 4 k, block g of the step
   const int sbase = U::kFp8 ? g : 16 * n + g;
-  int st = 0;
   for (int blk = 0; blk < steps; blk += 4) {
     const int buf = (blk >> 2) & 1;
     if constexpr (U::kFp8) {
@@ -229,27 +231,23 @@ __device__ __forceinline__ void mx_stream(const Mxfp4GemvArgs& a, MxShared& sh, 
       if constexpr (!U::kFp8) sb = __builtin_amdgcn_raw_buffer_load_b128(ru, svo1, bso(blk + 4), 0);
     }
 #pragma unroll
-    for (int k = 0; k < 4; k += MX_D) {
-      if (st + MX_D <= steps) {
-#pragma unroll
-        for (int d = 0; d < MX_D; ++d)
-          mx_step<FMT, true>(ring[d], &sh.sc[buf][sbase + 4 * (k + d)], ru, cvo, cso,
-                             cst(st + d + MX_D), rx, xvo, xst(st + d + MX_D), acc);
-        st += MX_D;
-      } else {
-#pragma unroll
-        for (int d = 0; d < MX_D; ++d)
-          if (st + d < steps)
-            mx_step<FMT, false>(ring[d], &sh.sc[buf][sbase + 4 * (k + d)], ru, cvo, cso, 0, rx,
-                                xvo, 0, acc);
-        st = steps;
+    for (int k = 0; k < 4; ++k) {
+      const int st = blk + k;  // its activations are in xr[k & 1] (blk is a multiple of 4)
+      if (st < steps) {        // uniform
+        if (st + 1 < steps) {
+          load_x4(xr[(k + 1) & 1], rx, xvo, xst(st + 1));
+          mx_step<FMT, true>(ring, &sh.sc[buf][sbase + 4 * k], ru, cvo, cso, cst(st + 1),
+                             xr[k & 1], acc);
+        } else {
+          mx_step<FMT, false>(ring, &sh.sc[buf][sbase + 4 * k], ru, cvo, cso, 0, xr[k & 1], acc);
+        }
       }
     }
   }
 }
 
 template <int FMT>
-__global__ __launch_bounds__(MX_THREADS, MX_WAVES_PER_SIMD) void mxfp4_gemv_kernel(Mxfp4GemvArgs a) {
+__global__ __launch_bounds__(MX_THREADS, MxUnit<FMT>::kFp8 ? 2 : MX_WAVES_PER_SIMD) void mxfp4_gemv_kernel(Mxfp4GemvArgs a) {
   __shared__ MxShared sh;
   Piece pc;
   if (!load_piece(a.desc, blockIdx.x, pc)) return;
