@@ -186,7 +186,7 @@ def bench_mxfp4(torch, ops, args):
     wl = mxfp4_decode_layer()
     lay = wl["layer"]
     dev = torch.device("cuda", 0)
-    L = ops.Mxfp4Layer.from_host(lay, dev)
+    L = ops.Mxfp4Layer.from_host(lay, dev).repacked()  # units in the GEMV's read order, once
     x = torch.from_numpy(wl["x"].view(np.int16)).to(dev)
     ids = torch.from_numpy(wl["topk_ids"]).to(dev)
     gates = torch.from_numpy(wl["topk_w"]).to(dev)
@@ -294,7 +294,7 @@ def bench_shared(torch, ops, args):
     for T, key in ((128, "decode"), (8192, "prefill")):
         wl = shared_expert(T=T)
         lay = wl["layer"]
-        L = ops.Fp8b32Layer.from_host(lay, dev)
+        L = ops.Fp8b32Layer.from_host(lay, dev).repacked()  # the GEMV's read order, once
         x = torch.from_numpy(wl["x"].view(np.int16)).to(dev)
         ids = torch.from_numpy(wl["topk_ids"]).to(dev)
         y = torch.empty((T, 1, lay["out"]), dtype=torch.float32, device=dev)
@@ -440,7 +440,7 @@ def drive(torch, ops, which, iters):
         for T in (128, 8192):
             wl = shared_expert(T=T)
             lay = wl["layer"]
-            L = ops.Fp8b32Layer.from_host(lay, dev)
+            L = ops.Fp8b32Layer.from_host(lay, dev).repacked()  # the GEMV's read order, once
             x = torch.from_numpy(wl["x"].view(np.int16)).to(dev)
             ids = torch.from_numpy(wl["topk_ids"]).to(dev)
             reps = replicate(torch, L.units, L.units.numel()) if T == 128 else [L.units]
@@ -460,7 +460,7 @@ def drive(torch, ops, which, iters):
     else:
         wl = mxfp4_decode_layer()
         lay = wl["layer"]
-        L = ops.Mxfp4Layer.from_host(lay, dev)
+        L = ops.Mxfp4Layer.from_host(lay, dev).repacked()
         x = torch.from_numpy(wl["x"].view(np.int16)).to(dev)
         ids = torch.from_numpy(wl["topk_ids"]).to(dev)
         gates = torch.from_numpy(wl["topk_w"]).to(dev)
@@ -601,6 +601,7 @@ def main():
         m = bench_mxfp4(torch, ops, args)
         extras["mxfp4_decode_layer"] = {
             "workload": "MXFP4 layer, 384 experts, 64 tokens, top-8, gates",
+            "layout": "units repacked once into the GEMV's read order (TQ_LAYOUT_GEMV)",
             "GB/s": round(m["bytes"] / m["sec_per_step"] / 1e9, 2),
             "ms_per_step": round(m["sec_per_step"] * 1e3, 5),
             "kernel": m["kernel"], "kernel_us": round(m["kernel_sec"] * 1e6, 3),
@@ -643,6 +644,7 @@ def main():
         extras["shared_expert_fp8b32"] = {
             "workload": "shared expert gate+up (1536 x 5120, fp8b32: E4M3, E8M0 per 32 x 32 block), "
                         "every token routed to it",
+            "layout": "unit repacked once into the GEMV's read order (TQ_LAYOUT_GEMV)",
             "decode_tokens": d["T"], "decode_GB/s": round(d["bytes"] / d["sec_per_step"] / 1e9, 2),
             "decode_us_per_step": round(d["sec_per_step"] * 1e6, 3),
             "decode_kernel": "mxfp4_gemv_kernel<fp8b32>",

@@ -77,6 +77,17 @@ typedef struct tq_trellis_layer {
 } tq_trellis_layer;
 
 /*
+ * Code layouts of the E8M0-scaled stores (MXFP4, fp8b32). TQ_LAYOUT_STORE is the pages'
+ * store order (HF orientation, rows of in/32 blocks). TQ_LAYOUT_GEMV is the same units
+ * repacked once by mxfp4_repack / fp8b32_repack so that every 128-input step of every
+ * strip of 16 output channels is one contiguous chunk (16 rows x 4 blocks): the decode
+ * GEMV then streams contiguous memory. The scales keep their store order. Both layouts give
+ * the same results bit for bit.
+ */
+#define TQ_LAYOUT_STORE 0
+#define TQ_LAYOUT_GEMV 1
+
+/*
  * An MXFP4 expert layer (FORMAT F9). E units back to back, each out*in/2 code bytes
  * (row = output channel, element 2j in the low nibble of byte j) followed by out*in/32
  * E8M0 scale bytes (row-major [out][in/32]).
@@ -85,7 +96,7 @@ typedef struct tq_mxfp4_layer {
   int32_t E;                /* experts, 1 .. 4096                                         */
   int32_t out;              /* output channels, multiple of 16                            */
   int32_t in;               /* inputs, multiple of 512                                    */
-  int32_t reserved;         /* must be 0                                                  */
+  int32_t layout;           /* TQ_LAYOUT_STORE, or TQ_LAYOUT_GEMV after mxfp4_repack      */
   const uint8_t* units;     /* device: E * (out*in/2 + out*in/32) bytes, 16-aligned       */
 } tq_mxfp4_layer;
 
@@ -101,7 +112,7 @@ typedef struct tq_fp8b32_layer {
   int32_t E;                /* experts, 1 .. 4096                                         */
   int32_t out;              /* output channels, multiple of 32                            */
   int32_t in;               /* inputs, multiple of 512                                    */
-  int32_t reserved;         /* must be 0                                                  */
+  int32_t layout;           /* TQ_LAYOUT_STORE, or TQ_LAYOUT_GEMV after fp8b32_repack     */
   const uint8_t* units;     /* device: E * (out*in + out*in/1024) bytes, 16-aligned       */
 } tq_fp8b32_layer;
 
@@ -216,6 +227,16 @@ int trellis_decode(const uint32_t* codes, int32_t K, int32_t out, int32_t in, in
  * decoder the MXFP4 kernels use.
  */
 int mxfp4_decode(const uint8_t* unit, int32_t out, int32_t in, uint16_t* w, void* stream);
+
+/*
+ * mxfp4_repack / fp8b32_repack — copy a layer's units from TQ_LAYOUT_STORE into
+ * TQ_LAYOUT_GEMV (see above): once, when a layer is loaded.
+ *   L      host: the layer, L->layout == TQ_LAYOUT_STORE.
+ *   dst    device, 16-byte aligned, as many bytes as L->units holds, not overlapping it;
+ *          use it as the units of a layer with layout TQ_LAYOUT_GEMV.
+ */
+int mxfp4_repack(const tq_mxfp4_layer* L, uint8_t* dst, void* stream);
+int fp8b32_repack(const tq_fp8b32_layer* L, uint8_t* dst, void* stream);
 
 /*
  * fp8b32_decode — test hook: decode one fp8b32 unit to bf16 [out][in] with the device

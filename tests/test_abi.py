@@ -109,7 +109,7 @@ def test_fp8b32_argument_errors(lib):
     ok = _lib.Mxfp4LayerC(1, 1536, 5120, 0, 0x1000)
     assert lib.fp8b32_expert_gemm(ctypes.byref(ok), 0, 0, 0, None, 1, 0, 0, 0, 0, None) == _lib.TQ_OK
     for bad in (_lib.Mxfp4LayerC(0, 128, 5120, 0, 0x1000), _lib.Mxfp4LayerC(1, 48, 5120, 0, 0x1000),
-                _lib.Mxfp4LayerC(1, 128, 5120 + 128, 0, 0x1000), _lib.Mxfp4LayerC(1, 128, 5120, 1, 0x1000)):
+                _lib.Mxfp4LayerC(1, 128, 5120 + 128, 0, 0x1000), _lib.Mxfp4LayerC(1, 128, 5120, 2, 0x1000)):
         assert lib.fp8b32_expert_gemm(ctypes.byref(bad), 0x1000, 1, 0x1000, None, 1, 0x1000, 0,
                                       0x1000, 1 << 30, None) == _lib.TQ_EINVAL
     mis = _lib.Mxfp4LayerC(1, 128, 5120, 0, 0x1008)
@@ -120,6 +120,20 @@ def test_fp8b32_argument_errors(lib):
     assert lib.fp8b32_decode(0x1000, 48, 64, 0x1000, None) == _lib.TQ_EINVAL
     assert lib.fp8b32_decode(0x1000, 32, 48, 0x1000, None) == _lib.TQ_EINVAL
     assert lib.fp8b32_decode(0x1008, 32, 64, 0x1000, None) == _lib.TQ_EALIGN
+
+
+def test_repack_argument_errors(lib):
+    for fn in (lib.mxfp4_repack, lib.fp8b32_repack):
+        store = _lib.Mxfp4LayerC(2, 128, 5120, _lib.TQ_LAYOUT_STORE, 0x100000)
+        packed = _lib.Mxfp4LayerC(2, 128, 5120, _lib.TQ_LAYOUT_GEMV, 0x100000)
+        assert fn(None, 0x1000, None) == _lib.TQ_EINVAL
+        assert fn(ctypes.byref(packed), 0x10000000, None) == _lib.TQ_EINVAL   # already repacked
+        assert fn(ctypes.byref(store), None, None) == _lib.TQ_EINVAL
+        assert fn(ctypes.byref(store), 0x10000008, None) == _lib.TQ_EALIGN
+        assert fn(ctypes.byref(store), 0x100010, None) == _lib.TQ_EINVAL      # overlaps the units
+    bad = _lib.Mxfp4LayerC(4, 128, 5120, 2, 0x1000)
+    assert lib.mxfp4_expert_gemm(ctypes.byref(bad), 0x1000, 1, 0x1000, None, 1, 0x1000, 0, 0x1000,
+                                 1 << 30, None) == _lib.TQ_EINVAL
 
 
 def test_internal_helpers_are_not_exported(lib):

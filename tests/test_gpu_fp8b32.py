@@ -112,3 +112,24 @@ def test_deterministic():
     a = run(wl["layer"], wl["x"], wl["topk_ids"])
     b = run(wl["layer"], wl["x"], wl["topk_ids"])
     assert np.array_equal(a, b)
+
+
+@pytest.mark.parametrize("flags", [1, 2, 1 | 4])
+def test_repacked_layout_is_bit_equal(flags):
+    # 224 output channels: one full group of 8 strips and a partial group of 6
+    E, T, topk = 5, 40, 2
+    layer = fp8b32_layer(912, E, 224, 1024)
+    x = bf16_from_normal(rng_for(912, 1), (T, 1024))
+    ids = uniform_routes(rng_for(912, 2), T, E, topk)
+    gates = softmax_gates(rng_for(912, 3), T, topk)
+    o = ops()
+    L = o.Fp8b32Layer.from_host(layer)
+    P = L.repacked()
+    outs = []
+    for lay in (L, P):
+        y = o.fp8b32_expert_gemm(lay, to_dev(x, np.int16), to_dev(ids), to_dev(gates), flags=flags)
+        torch.cuda.synchronize()
+        outs.append(y.cpu().numpy())
+    assert np.array_equal(outs[0], outs[1])
+    ref = reference(layer, x, ids, gates)
+    assert rel_l2(outs[1], ref.sum(axis=1) if flags & 4 else ref) <= TOL

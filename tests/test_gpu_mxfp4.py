@@ -65,3 +65,37 @@ def test_deterministic():
     a = run(wl["layer"], wl["x"], wl["topk_ids"], wl["topk_w"])
     b = run(wl["layer"], wl["x"], wl["topk_ids"], wl["topk_w"])
     assert np.array_equal(a, b)
+
+
+def run_layer(L, x_bits, ids, gates=None, flags=0):
+    o = ops()
+    y = o.mxfp4_expert_gemm(L, to_dev(x_bits, np.int16), to_dev(ids),
+                            None if gates is None else to_dev(gates), flags=flags)
+    torch.cuda.synchronize()
+    return y.cpu().numpy()
+
+
+@pytest.mark.parametrize("flags", [1, 2, 1 | 4, 2 | 4])
+def test_repacked_layout_is_bit_equal(flags):
+    # 208 output channels: one full group of 8 strips and a partial group of 5
+    E, T, topk = 7, 45, 3
+    layer = mxfp4_layer(502, E, 208, 1024)
+    x = bf16_from_normal(rng_for(502, 1), (T, 1024))
+    ids = uniform_routes(rng_for(502, 2), T, E, topk)
+    gates = softmax_gates(rng_for(502, 3), T, topk)
+    L = ops().Mxfp4Layer.from_host(layer)
+    P = L.repacked()
+    assert P.layout == ops().TQ_LAYOUT_GEMV
+    a = run_layer(L, x, ids, gates, flags)
+    b = run_layer(P, x, ids, gates, flags)
+    assert np.array_equal(a, b)
+    ref = oracle_mxfp4(layer, x, ids, gates)
+    assert rel_l2(b, ref.sum(axis=1) if flags & 4 else ref) <= TOL
+
+
+def test_repacked_full_size_decode():
+    wl = mxfp4_decode_layer()
+    L = ops().Mxfp4Layer.from_host(wl["layer"])
+    a = run_layer(L, wl["x"], wl["topk_ids"], wl["topk_w"])
+    b = run_layer(L.repacked(), wl["x"], wl["topk_ids"], wl["topk_w"])
+    assert np.array_equal(a, b)

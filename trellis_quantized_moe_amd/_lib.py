@@ -17,6 +17,9 @@ TQ_EALIGN = -3
 TQ_EWORKSPACE = -4
 TQ_EHIP = -5
 
+TQ_LAYOUT_STORE = 0
+TQ_LAYOUT_GEMV = 1
+
 TQ_AUTO = 0
 TQ_GEMV = 1
 TQ_GEMM = 2
@@ -47,7 +50,7 @@ class Mxfp4LayerC(ctypes.Structure):
         ("E", ctypes.c_int32),
         ("out", ctypes.c_int32),
         ("in_", ctypes.c_int32),
-        ("reserved", ctypes.c_int32),
+        ("layout", ctypes.c_int32),
         ("units", ctypes.c_void_p),
     ]
 
@@ -70,6 +73,8 @@ SIGNATURES = {
     "fp8b32_expert_gemm": (ctypes.c_int, [ctypes.POINTER(Mxfp4LayerC), _P, _I64, _P, _P, _I32,
                                           _P, _U32, _P, _SZ, _P]),
     "fp8b32_decode": (ctypes.c_int, [_P, _I32, _I32, _P, _P]),
+    "mxfp4_repack": (ctypes.c_int, [ctypes.POINTER(Mxfp4LayerC), _P, _P]),
+    "fp8b32_repack": (ctypes.c_int, [ctypes.POINTER(Mxfp4LayerC), _P, _P]),
     "mxfp4_to_nvfp4": (ctypes.c_int, [ctypes.POINTER(Mxfp4LayerC), _P, _P, _P, _P, _P]),
     "trellis_expert_ffn": (ctypes.c_int, [ctypes.POINTER(TrellisLayerC), ctypes.POINTER(TrellisLayerC),
                                           ctypes.POINTER(TrellisLayerC), _P, _I64, _P, _P, _I32,

@@ -387,7 +387,8 @@ int mxfp4_to_nvfp4(const tq_mxfp4_layer* L, uint8_t* codes, uint8_t* scales, flo
   if (L->E < 1 || L->E > 65535) return fail(TQ_EINVAL, "E = %d is outside 1..65535", L->E);
   if (L->out <= 0 || L->out % 16) return fail(TQ_EINVAL, "out = %d is not a positive multiple of 16", L->out);
   if (L->in <= 0 || L->in % 512) return fail(TQ_EINVAL, "in = %d is not a positive multiple of 512", L->in);
-  if (L->reserved != 0) return fail(TQ_EINVAL, "reserved field must be 0");
+  if (L->layout != TQ_LAYOUT_STORE)
+    return fail(TQ_EINVAL, "the transcode reads units in TQ_LAYOUT_STORE (layout = %d)", L->layout);
   if ((int64_t)L->out * L->in / 2 >= ((int64_t)1 << 31))
     return fail(TQ_EINVAL, "out * in is too large");
   if (!L->units || !codes || !scales || !scale2 || !status)
@@ -465,7 +466,8 @@ static int check_mxfp4_layer(const tq_mxfp4_layer* L) {
   if (L->E < 1 || L->E > 4096) return fail(TQ_EINVAL, "E = %d is outside 1..4096", L->E);
   if (L->out <= 0 || L->out % 16) return fail(TQ_EINVAL, "out = %d is not a positive multiple of 16", L->out);
   if (L->in <= 0 || L->in % 512) return fail(TQ_EINVAL, "in = %d is not a positive multiple of 512", L->in);
-  if (L->reserved != 0) return fail(TQ_EINVAL, "reserved field must be 0");
+  if (L->layout != TQ_LAYOUT_STORE && L->layout != TQ_LAYOUT_GEMV)
+    return fail(TQ_EINVAL, "layout = %d is not TQ_LAYOUT_STORE or TQ_LAYOUT_GEMV", L->layout);
   if (!L->units) return fail(TQ_EINVAL, "units is NULL");
   if (!aligned(L->units, 16)) return fail(TQ_EALIGN, "units must be 16-byte aligned");
   return TQ_OK;
@@ -476,7 +478,8 @@ static int check_fp8b32_layer(const tq_fp8b32_layer* L) {
   if (L->E < 1 || L->E > 4096) return fail(TQ_EINVAL, "E = %d is outside 1..4096", L->E);
   if (L->out <= 0 || L->out % 32) return fail(TQ_EINVAL, "out = %d is not a positive multiple of 32", L->out);
   if (L->in <= 0 || L->in % 512) return fail(TQ_EINVAL, "in = %d is not a positive multiple of 512", L->in);
-  if (L->reserved != 0) return fail(TQ_EINVAL, "reserved field must be 0");
+  if (L->layout != TQ_LAYOUT_STORE && L->layout != TQ_LAYOUT_GEMV)
+    return fail(TQ_EINVAL, "layout = %d is not TQ_LAYOUT_STORE or TQ_LAYOUT_GEMV", L->layout);
   if (!L->units) return fail(TQ_EINVAL, "units is NULL");
   if (!aligned(L->units, 16)) return fail(TQ_EALIGN, "units must be 16-byte aligned");
   return TQ_OK;
@@ -678,7 +681,7 @@ namespace {
 // The expert GEMM of the E8M0-scaled stores (MXFP4, fp8b32): E units of `unit` bytes back
 // to back at `units`.
 struct MxLayer {
-  int fmt, E, out, in;
+  int fmt, E, out, in, layout;
   const uint8_t* units;
 };
 
@@ -726,6 +729,7 @@ int mx_expert_gemm(const MxLayer* L, const void* x, int64_t T, const int32_t* to
     if (err != hipSuccess) return hip_fail(err, "decode plan launch");
     tq::Mxfp4GemvArgs a{};
     a.fmt = L->fmt;
+    a.layout = L->layout;
     a.units = L->units;
     a.x = xb;
     a.x_bytes = (uint32_t)(T * L->in * 2);
@@ -764,6 +768,7 @@ int mx_expert_gemm(const MxLayer* L, const void* x, int64_t T, const int32_t* to
     if (rc) return rc;
     tq::Mxfp4GemmArgs a{};
     a.fmt = L->fmt;
+    a.layout = L->layout;
     a.units = L->units;
     a.x = xb;
     a.x_bytes = (uint32_t)(T * L->in * 2);
@@ -800,8 +805,39 @@ int mxfp4_expert_gemm(const tq_mxfp4_layer* L, const void* x, int64_t T,
                       uint32_t flags, void* ws, size_t ws_bytes, void* stream) {
   int rc = check_mxfp4_layer(L);
   if (rc) return rc;
-  const MxLayer m{tq::MX_FP4, L->E, L->out, L->in, L->units};
+  const MxLayer m{tq::MX_FP4, L->E, L->out, L->in, L->layout, L->units};
   return mx_expert_gemm(&m, x, T, topk_ids, topk_w, topk, y, flags, ws, ws_bytes, stream);
+}
+
+static int mx_repack(int fmt, int E, int out, int in, int layout, const uint8_t* units,
+                     uint8_t* dst, void* stream) {
+  if (layout != TQ_LAYOUT_STORE)
+    return fail(TQ_EINVAL, "the layer to repack must be in TQ_LAYOUT_STORE (layout = %d)", layout);
+  if (!dst) return fail(TQ_EINVAL, "dst is NULL");
+  if (!aligned(dst, 16)) return fail(TQ_EALIGN, "dst must be 16-byte aligned");
+  const int64_t total = mx_unit_bytes(fmt, out, in) * E;
+  const char* a = reinterpret_cast<const char*>(units);
+  const char* b = reinterpret_cast<const char*>(dst);
+  if (a < b + total && b < a + total) return fail(TQ_EINVAL, "dst overlaps the layer's units");
+  if (mx_unit_bytes(fmt, out, in) >= ((int64_t)1 << 31))
+    return fail(TQ_EINVAL, "a unit of out * in weights must stay below 2^31 bytes");
+  int rc = check_device();
+  if (rc) return rc;
+  hipError_t err = tq::launch_mx_repack(fmt, units, dst, E, out, in, static_cast<hipStream_t>(stream));
+  if (err != hipSuccess) return hip_fail(err, "repack launch");
+  return ok();
+}
+
+int mxfp4_repack(const tq_mxfp4_layer* L, uint8_t* dst, void* stream) {
+  int rc = check_mxfp4_layer(L);
+  if (rc) return rc;
+  return mx_repack(tq::MX_FP4, L->E, L->out, L->in, L->layout, L->units, dst, stream);
+}
+
+int fp8b32_repack(const tq_fp8b32_layer* L, uint8_t* dst, void* stream) {
+  int rc = check_fp8b32_layer(L);
+  if (rc) return rc;
+  return mx_repack(tq::MX_FP8B32, L->E, L->out, L->in, L->layout, L->units, dst, stream);
 }
 
 int fp8b32_expert_gemm(const tq_fp8b32_layer* L, const void* x, int64_t T,
@@ -809,7 +845,7 @@ int fp8b32_expert_gemm(const tq_fp8b32_layer* L, const void* x, int64_t T,
                        uint32_t flags, void* ws, size_t ws_bytes, void* stream) {
   int rc = check_fp8b32_layer(L);
   if (rc) return rc;
-  const MxLayer m{tq::MX_FP8B32, L->E, L->out, L->in, L->units};
+  const MxLayer m{tq::MX_FP8B32, L->E, L->out, L->in, L->layout, L->units};
   return mx_expert_gemm(&m, x, T, topk_ids, topk_w, topk, y, flags, ws, ws_bytes, stream);
 }
 

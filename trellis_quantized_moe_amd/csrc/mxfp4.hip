@@ -57,7 +57,58 @@ struct MxUnit {
   __device__ __host__ static uint32_t scale_at(int out, int in, int o, int kb) {
     return (uint32_t)(code_bytes(out, in) + (kFp8 ? (size_t)(o / 32) * (in / 32) : (size_t)o * (in / 32)) + kb);
   }
+  // code bytes of one row and 32-input block
+  static constexpr uint32_t kCB = kFp8 ? 32u : 16u;
+  // Repacked codes (layout 1, the GEMV's read order): per group of 128 rows, per 128-input
+  // step, per strip of 16 rows, the strip's 16 rows x 4 blocks of kCB bytes (row-major)
+  // are one contiguous chunk of 64 kCB bytes; a group's steps follow each other with its
+  // ns strips each (ns = 8 but in a last, partial group). Scales keep their store order.
+  __device__ __host__ static uint32_t group_strips(int out, int grp) {
+    const int ns = out / 16 - grp * 8;
+    return (uint32_t)(ns < 8 ? ns : 8);
+  }
+  __device__ __host__ static uint32_t packed_at(int out, int in, int o, int kb) {
+    const int grp = o / 128, s8 = (o % 128) / 16, n = o % 16, st = kb / 4, g = kb % 4;
+    const size_t S = (size_t)in / 128;
+    return (uint32_t)(((size_t)grp * S * 8 + (size_t)st * group_strips(out, grp) + s8) * 64 * kCB +
+                      (size_t)n * 4 * kCB + (size_t)g * kCB);
+  }
+  // store order: byte offset of output o's codes of block kb
+  __device__ __host__ static uint32_t stored_at(int in, int o, int kb) {
+    return (uint32_t)((size_t)o * row_bytes(in) + (size_t)kb * kCB);
+  }
 };
+
+// Repack kernel: thread i copies one (row, 32-input block) chunk of kCB code bytes of unit
+// blockIdx.y from store order to the GEMV's read order; the scales are copied as they are.
+template <int FMT>
+__global__ __launch_bounds__(256) void mx_repack_kernel(const uint8_t* __restrict__ src,
+                                                        uint8_t* __restrict__ dst, int out,
+                                                        int in) {
+  using U = MxUnit<FMT>;
+  const size_t ub = U::unit_bytes(out, in);
+  const uint8_t* su = src + (size_t)blockIdx.y * ub;
+  uint8_t* du = dst + (size_t)blockIdx.y * ub;
+  const int nkb = in / 32;
+  const int64_t chunks = (int64_t)out * nkb;
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < chunks) {
+    const int o = (int)(i / nkb), kb = (int)(i % nkb);
+    const uint4* a = reinterpret_cast<const uint4*>(su + U::stored_at(in, o, kb));
+    uint4* b = reinterpret_cast<uint4*>(du + U::packed_at(out, in, o, kb));
+    b[0] = a[0];
+    if constexpr (U::kFp8) b[1] = a[1];
+  }
+  // the scales: 16-byte pieces after the codes
+  const size_t cb = U::code_bytes(out, in), sbytes = ub - cb;
+  for (size_t j = (size_t)i * 16; j < sbytes; j += (size_t)gridDim.x * 256 * 16) {
+    if (j + 16 <= sbytes) {
+      *reinterpret_cast<uint4*>(du + cb + j) = *reinterpret_cast<const uint4*>(su + cb + j);
+    } else {
+      for (size_t q = j; q < sbytes; ++q) du[cb + q] = su[cb + q];
+    }
+  }
+}
 
 // ---- decode hooks ----------------------------------------------------------------------
 __global__ __launch_bounds__(256) void fp8b32_decode_kernel(const uint8_t* __restrict__ unit,
@@ -176,13 +227,24 @@ __device__ __forceinline__ void mx_stream(const Mxfp4GemvArgs& a, MxShared& sh, 
                                           int grp, int ns, int s0, int s1, f32x4 acc[8]) {
   using U = MxUnit<FMT>;
   const int lane = threadIdx.x & 63, g = lane >> 4, n = lane & 15;
-  const uint32_t row = U::row_bytes(a.in);
-  const uint32_t cvo = n * row + (U::kFp8 ? 32u : 16u) * g;  // codes of output n, block g
-  const uint32_t cstep = U::kFp8 ? 128u : 64u;                 // code bytes per row and step
-  uint32_t cso[8];
+  // codes of output n, block g of a step: a per-lane offset, a scalar offset per strip and
+  // one per step, in either layout
+  uint32_t cvo, cstep, cso[8];
+  if (a.layout == 0) {  // store order: rows of in/32 blocks
+    const uint32_t row = U::row_bytes(a.in);
+    cvo = n * row + U::kCB * g;
+    cstep = 4 * U::kCB;
 #pragma unroll
-  for (int s8 = 0; s8 < 8; ++s8)
-    cso[s8] = (uint32_t)(grp * 128 + 16 * (s8 < ns ? s8 : ns - 1)) * row;
+    for (int s8 = 0; s8 < 8; ++s8)
+      cso[s8] = (uint32_t)(grp * 128 + 16 * (s8 < ns ? s8 : ns - 1)) * row;
+  } else {  // the GEMV's read order: a strip-step is 64 kCB contiguous bytes
+    const uint32_t chunk = 64 * U::kCB;
+    cvo = n * 4 * U::kCB + U::kCB * g;
+    cstep = (uint32_t)ns * chunk;
+    const uint32_t base = U::packed_at(a.out, a.in, grp * 128, 0);
+#pragma unroll
+    for (int s8 = 0; s8 < 8; ++s8) cso[s8] = base + (uint32_t)(s8 < ns ? s8 : ns - 1) * chunk;
+  }
   // scale rows of a 4-step block, 16 bytes each (4 steps x 4 blocks): MXFP4 lane L brings
   // rows L and L + 64 of the group; fp8b32 lanes 0..3 bring the group's 4 row blocks
   uint32_t svo0, svo1;
@@ -291,18 +353,27 @@ struct Mxfp4Producer {
   uint32_t vo_c, vo_s;
   int o, h;
 
-  __device__ Mxfp4Producer(const uint8_t* unit, int out, int in, int grp, int ns) {
+  uint32_t pstep;  // layout 1: code bytes per 128-input step of the group, else 0
+
+  __device__ Mxfp4Producer(const uint8_t* unit, int out, int in, int grp, int ns, int layout) {
+    using U = MxUnit<MX_FP4>;
     o = threadIdx.x >> 1;
     h = threadIdx.x & 1;
-    rc = gemm_rsrc(unit, (uint32_t)((size_t)out * in / 2 + (size_t)out * in / 32));
+    rc = gemm_rsrc(unit, (uint32_t)U::unit_bytes(out, in));
     // channels past the group read its last channel (their rows of the B tile are unused)
     const int og = grp * 128 + (o < 16 * ns ? o : 16 * ns - 1);
-    vo_c = (uint32_t)((size_t)og * (in / 2) + 8 * h);
-    vo_s = (uint32_t)((size_t)out * in / 2 + (size_t)og * (in / 32));
+    vo_c = (layout ? U::packed_at(out, in, og, 0) : U::stored_at(in, og, 0)) + 8 * h;
+    pstep = layout ? (uint32_t)ns * 64 * U::kCB : 0u;
+    vo_s = U::scale_at(out, in, og, 0);
+  }
+
+  // scalar offset of block kk's codes
+  __device__ __forceinline__ uint32_t koff(int kk) const {
+    return pstep ? (uint32_t)(kk >> 2) * pstep + 16u * (uint32_t)(kk & 3) : 16u * kk;
   }
 
   __device__ __forceinline__ void load(int kk, Raw& r) const {
-    const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(rc, vo_c, 16u * kk, 0);
+    const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(rc, vo_c, koff(kk), 0);
     r.c0 = v.x;
     r.c1 = v.y;
     r.sb = __builtin_amdgcn_raw_buffer_load_b8(rc, vo_s, (uint32_t)kk, 0);
@@ -328,19 +399,26 @@ struct Fp8b32Producer {
   uint32_t vo_c, vo_s;
   int o, h;
 
-  __device__ Fp8b32Producer(const uint8_t* unit, int out, int in, int grp, int ns) {
+  uint32_t pstep;  // layout 1: code bytes per 128-input step of the group, else 0
+
+  __device__ Fp8b32Producer(const uint8_t* unit, int out, int in, int grp, int ns, int layout) {
     using U = MxUnit<MX_FP8B32>;
     o = threadIdx.x >> 1;
     h = threadIdx.x & 1;
     rc = gemm_rsrc(unit, (uint32_t)U::unit_bytes(out, in));
     // channels past the group read its last channel (their rows of the B tile are unused)
     const int og = grp * 128 + (o < 16 * ns ? o : 16 * ns - 1);
-    vo_c = (uint32_t)((size_t)og * in + 16 * h);
+    vo_c = (layout ? U::packed_at(out, in, og, 0) : U::stored_at(in, og, 0)) + 16 * h;
+    pstep = layout ? (uint32_t)ns * 64 * U::kCB : 0u;
     vo_s = U::scale_at(out, in, og, 0);
   }
 
+  __device__ __forceinline__ uint32_t koff(int kk) const {
+    return pstep ? (uint32_t)(kk >> 2) * pstep + 32u * (uint32_t)(kk & 3) : 32u * kk;
+  }
+
   __device__ __forceinline__ void load(int kk, Raw& r) const {
-    r.c = __builtin_amdgcn_raw_buffer_load_b128(rc, vo_c, 32u * kk, 0);
+    r.c = __builtin_amdgcn_raw_buffer_load_b128(rc, vo_c, koff(kk), 0);
     r.sb = __builtin_amdgcn_raw_buffer_load_b8(rc, vo_s, (uint32_t)kk, 0);
   }
 
@@ -374,10 +452,10 @@ __global__ __launch_bounds__(GEMM_THREADS, 2) void mxfp4_gemm_kernel(Mxfp4GemmAr
   it.ns = min(8, a.out / 16 - grp * 8);
   const uint8_t* unit = a.units + (size_t)e * MxUnit<FMT>::unit_bytes(a.out, a.in);
   if constexpr (FMT == MX_FP8B32) {
-    Fp8b32Producer p(unit, a.out, a.in, grp, it.ns);
+    Fp8b32Producer p(unit, a.out, a.in, grp, it.ns, a.layout);
     gemm_item(it, sh, p);
   } else {
-    Mxfp4Producer p(unit, a.out, a.in, grp, it.ns);
+    Mxfp4Producer p(unit, a.out, a.in, grp, it.ns, a.layout);
     gemm_item(it, sh, p);
   }
 }
@@ -397,6 +475,17 @@ hipError_t launch_fp8b32_decode(const uint8_t* unit, int out, int in, uint16_t* 
   const int total = out * (in / 8);
   hipLaunchKernelGGL(fp8b32_decode_kernel, dim3((total + 255) / 256), dim3(256), 0, s, unit, out,
                      in, w);
+  return hipGetLastError();
+}
+
+hipError_t launch_mx_repack(int fmt, const uint8_t* src, uint8_t* dst, int E, int out, int in,
+                            hipStream_t s) {
+  const int64_t chunks = (int64_t)out * (in / 32);
+  const dim3 grid((unsigned)((chunks + 255) / 256), (unsigned)E);
+  if (fmt == MX_FP8B32)
+    hipLaunchKernelGGL(mx_repack_kernel<MX_FP8B32>, grid, dim3(256), 0, s, src, dst, out, in);
+  else
+    hipLaunchKernelGGL(mx_repack_kernel<MX_FP4>, grid, dim3(256), 0, s, src, dst, out, in);
   return hipGetLastError();
 }
 

@@ -122,6 +122,7 @@ constexpr int MX_FP8B32 = 1;  // fp8b32: E4M3 codes, a scale per 32 x 32 block
 
 struct Mxfp4GemvArgs {
   int fmt;               // MX_FP4 or MX_FP8B32
+  int layout;            // 0: codes in store order; 1: repacked (mx_repack_kernel)
   const uint8_t* units;
   const uint16_t* x;     // bf16 [T][in]
   uint32_t x_bytes;      // size of x in bytes (< 2^31)
@@ -137,7 +138,8 @@ int mxfp4_gemv_grid(int fmt);
 hipError_t launch_mxfp4_gemv(const Mxfp4GemvArgs& a, hipStream_t s);
 
 struct Mxfp4GemmArgs {
-  int fmt;  // MX_FP4 or MX_FP8B32
+  int fmt;     // MX_FP4 or MX_FP8B32
+  int layout;  // 0: codes in store order; 1: repacked
   const uint8_t* units;
   const uint16_t* x;
   uint32_t x_bytes;  // size of x in bytes (< 2^31)
@@ -179,6 +181,9 @@ hipError_t launch_trellis_decode(const uint32_t* codes, int K, int out, int in, 
                                  int path, hipStream_t s);
 hipError_t launch_mxfp4_decode(const uint8_t* unit, int out, int in, uint16_t* w,
                                hipStream_t s);
+// Copies E units of an E8M0-scaled store from store order into the GEMV's read order.
+hipError_t launch_mx_repack(int fmt, const uint8_t* src, uint8_t* dst, int E, int out, int in,
+                            hipStream_t s);
 hipError_t launch_fp8b32_decode(const uint8_t* unit, int out, int in, uint16_t* w,
                                 hipStream_t s);
 hipError_t launch_swiglu(const float* g, const float* u, uint16_t* h, int64_t n,

@@ -11,7 +11,8 @@ import numpy as np
 import torch
 
 from . import _lib
-from ._lib import TQ_AUTO, TQ_COMBINE, TQ_GEMM, TQ_GEMV, TQ_ROTATE, check  # noqa: F401
+from ._lib import (TQ_AUTO, TQ_COMBINE, TQ_GEMM, TQ_GEMV, TQ_LAYOUT_GEMV,  # noqa: F401
+                   TQ_LAYOUT_STORE, TQ_ROTATE, check)
 
 
 def _ptr(t):
@@ -72,6 +73,7 @@ class Mxfp4Layer:
     out: int
     in_: int
     units: torch.Tensor      # uint8 [E * unit_bytes]
+    layout: int = TQ_LAYOUT_STORE
 
     @classmethod
     def from_host(cls, layer, device="cuda"):
@@ -79,10 +81,19 @@ class Mxfp4Layer:
                    units=torch.from_numpy(np.ascontiguousarray(layer["units"], dtype=np.uint8)).to(device))
 
     def with_units(self, units):
-        return Mxfp4Layer(self.E, self.out, self.in_, units)
+        return Mxfp4Layer(self.E, self.out, self.in_, units, self.layout)
 
     def c_struct(self):
-        return _lib.Mxfp4LayerC(self.E, self.out, self.in_, 0, self.units.data_ptr())
+        return _lib.Mxfp4LayerC(self.E, self.out, self.in_, self.layout, self.units.data_ptr())
+
+    def repacked(self):
+        """The same layer with its units copied into TQ_LAYOUT_GEMV (see mxfp4_repack in
+        include/tq.h)."""
+        _require_cuda(self.units)
+        dst = torch.empty_like(self.units)
+        c = self.c_struct()
+        check(_lib.load().mxfp4_repack(ctypes.byref(c), _ptr(dst), _stream(self.units.device)))
+        return Mxfp4Layer(self.E, self.out, self.in_, dst, TQ_LAYOUT_GEMV)
 
 
 @dataclass
@@ -92,6 +103,7 @@ class Fp8b32Layer:
     out: int
     in_: int
     units: torch.Tensor      # uint8 [E * unit_bytes]
+    layout: int = TQ_LAYOUT_STORE
 
     @classmethod
     def from_host(cls, layer, device="cuda"):
@@ -99,10 +111,19 @@ class Fp8b32Layer:
                    units=torch.from_numpy(np.ascontiguousarray(layer["units"], dtype=np.uint8)).to(device))
 
     def with_units(self, units):
-        return Fp8b32Layer(self.E, self.out, self.in_, units)
+        return Fp8b32Layer(self.E, self.out, self.in_, units, self.layout)
 
     def c_struct(self):
-        return _lib.Mxfp4LayerC(self.E, self.out, self.in_, 0, self.units.data_ptr())
+        return _lib.Mxfp4LayerC(self.E, self.out, self.in_, self.layout, self.units.data_ptr())
+
+    def repacked(self):
+        """The same layer with its units copied into TQ_LAYOUT_GEMV (see fp8b32_repack in
+        include/tq.h)."""
+        _require_cuda(self.units)
+        dst = torch.empty_like(self.units)
+        c = self.c_struct()
+        check(_lib.load().fp8b32_repack(ctypes.byref(c), _ptr(dst), _stream(self.units.device)))
+        return Fp8b32Layer(self.E, self.out, self.in_, dst, TQ_LAYOUT_GEMV)
 
 
 def workspace_bytes(T, topk, E, out, in_, flags=TQ_AUTO):
