@@ -136,6 +136,23 @@ def test_repack_argument_errors(lib):
                                  1 << 30, None) == _lib.TQ_EINVAL
 
 
+def test_decode_batch_wave_bound(lib):
+    # 4096 experts of 1024 outputs (8 groups): 8 * (4096 + ceil(1 / 16)) (group, chunk) pairs
+    # exceed the 32768 launched waves of a decode batch: forced decode is rejected before
+    # any device work, and the automatic choice takes the prefill path (its workspace)
+    m = _lib.Mxfp4LayerC(4096, 1024, 512, 0, 0x1000)
+    assert lib.mxfp4_expert_gemm(ctypes.byref(m), 0x1000, 1, 0x1000, None, 1, 0x1000,
+                                 _lib.TQ_GEMV, 0x1000, 1 << 30, None) == _lib.TQ_EINVAL
+    assert b"32768" in lib.tq_last_error()
+    auto = lib.tq_workspace_bytes(1, 1, 4096, 1024, 512, _lib.TQ_AUTO)
+    gemm = lib.tq_workspace_bytes(1, 1, 4096, 1024, 512, _lib.TQ_GEMM)
+    assert auto == gemm
+    # one group fewer fits: 7 * 4097 <= 32768
+    m = _lib.Mxfp4LayerC(4096, 896, 512, 0, 0x1000)
+    assert lib.mxfp4_expert_gemm(ctypes.byref(m), 0x1000, 1, 0x1000, None, 1, 0x1000,
+                                 _lib.TQ_GEMV, 0x1000, 8, None) == _lib.TQ_EWORKSPACE
+
+
 def test_internal_helpers_are_not_exported(lib):
     for name in ("common_checks", "check_trellis_layer", "check_mxfp4_layer", "run_route",
                  "ffn_ws", "mx_unit_bytes"):
