@@ -341,3 +341,27 @@ def test_decode_batch_nonfinite_token():
     keep = np.arange(T) != 5
     ref = oracle_trellis(layer, x[keep], ids[keep], None)
     assert rel_l2(y[keep], ref) <= TOL
+
+
+def test_skewed_decode_batch_sampled():
+    # a 128-token decode batch routed by Zipf(1.1) popularity over 384 mixed-width experts:
+    # hot experts take dozens of tokens, i.e. several 8-token chunks with waves of their own
+    # (some experts with more than 32 pieces, written by the plan's waves); sampled slots of
+    # the hottest experts and of random ones against the oracle
+    wl = mixed_layer()
+    layer = wl["layer"]
+    ids = zipf_routes(rng_for(413, 4), 128, layer["E"], 8)
+    counts = np.bincount(ids.reshape(-1), minlength=layer["E"])
+    assert counts.max() > 32
+    y = run(layer, wl["x"], ids, flags=ops().TQ_GEMV, rotate_signs=layer["signs"])
+    xr = rotate_host(wl)
+    flat = ids.reshape(-1)
+    hot = np.argsort(counts)[-3:]
+    hot_slots = np.nonzero(np.isin(flat, hot))[0]
+    sample = np.unique(np.concatenate([
+        rng_for(413, 5).choice(hot_slots, 24, replace=False),
+        rng_for(413, 6).choice(flat.size, 24, replace=False)]))
+    ref = oracle_trellis(layer, xr, ids, None, sample=sample)
+    got = y.reshape(-1, 128)[sample]
+    assert rel_l2(got, ref.reshape(-1, 128)[sample]) <= TOL
+    assert np.all(np.isfinite(y))
