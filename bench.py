@@ -435,6 +435,18 @@ def drive(torch, ops, which, iters):
         for i in range(iters):
             ops.trellis_expert_gemm(layers[i % len(layers)], x, ids, flags=ops.TQ_ROTATE,
                                     out=y, ws=ws)
+    elif which == "ffn":
+        from workloads import ffn_decode
+        wl = ffn_decode()
+        G, U, D = (ops.TrellisLayer.from_host(wl[k], dev) for k in ("gate", "up", "down"))
+        x = torch.from_numpy(wl["x"].view(np.int16)).to(dev)
+        ids = torch.from_numpy(wl["topk_ids"]).to(dev)
+        gates = torch.from_numpy(wl["topk_w"]).to(dev)
+        T, topk = wl["topk_ids"].shape
+        y = torch.empty((T, G.in_), dtype=torch.float32, device=dev)
+        ws = ops.ffn_workspace(T, topk, G.E, G.in_, G.out, ops.TQ_AUTO, dev)
+        for i in range(iters):
+            ops.trellis_expert_ffn(G, U, D, x, ids, gates, flags=ops.TQ_ROTATE, out=y, ws=ws)
     elif which == "shared":
         from workloads import shared_expert
         for T in (128, 8192):
@@ -528,7 +540,7 @@ def main():
     ap.add_argument("--cpu-sample-experts", type=int, default=0,
                     help="active experts in the CPU baseline sample (0 = all)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--drive", choices=["mixed", "mxfp4", "prefill", "nvfp4", "shared"],
+    ap.add_argument("--drive", choices=["mixed", "mxfp4", "prefill", "nvfp4", "shared", "ffn"],
                     help="only run --steps steps of one workload (for rocprofv3)")
     ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="summarise rocprofv3 FETCH_SIZE / WRITE_SIZE runs of --drive mixed")
