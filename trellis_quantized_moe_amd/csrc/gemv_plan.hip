@@ -66,6 +66,15 @@ __device__ void block_scan(int (&x)[NV], int (&tot)[NV]) {
 // Pieces per group for a step cost k under the per-wave cost bound T (T >= k): the steps
 // S split into pieces of at most floor(T / k) steps. The quotient is taken in fp32, exact
 // here (S <= 2^15, and a non-integer S / per is at least 1 / S away from an integer).
+// n / d for 0 <= n < 2^22 and d > 0, given rd = 1 / d in fp32: the product is within one of
+// the quotient there (its relative error is a few ulp, the quotient below 2^22), and one
+// remainder test corrects it. A handful of instructions in place of the integer divide.
+__device__ __forceinline__ int small_div(int n, int d, float rd) {
+  const int q = (int)((float)n * rd);
+  const int r = n - q * d;
+  return q + (r >= d) - (r < 0);
+}
+
 __device__ __forceinline__ int pieces_for(int S, int T, int k) {
   const int per = T / k;
   return (int)__builtin_ceilf((float)S / (float)per);
@@ -259,9 +268,13 @@ __device__ void plan_block(const PlanArgs& a) {
   for (int b = tid >> 6; b < nbig; b += PLAN_WAVES) {  // uniform per wave
     const int4 bg = s_big[b];
     const int W = bg.z, cw = bg.w * W, nd = groups * cw;
+    const float rcw = 1.0f / (float)cw, rw = 1.0f / (float)W;
+    const bool fast = W * S < (1 << 22);  // l < nd <= GEMV_MAX_G always is
     for (int l = tid & 63; l < nd; l += 64) {
-      const int grp = l / cw, r = l - grp * cw, c = r / W, p = r - c * W;
-      const int s0 = p * S / W, s1 = (p + 1) * S / W;
+      const int grp = small_div(l, cw, rcw), r = l - grp * cw;
+      const int c = small_div(r, W, rw), p = r - c * W;
+      const int s0 = fast ? small_div(p * S, W, rw) : p * S / W;
+      const int s1 = fast ? small_div((p + 1) * S, W, rw) : (p + 1) * S / W;
       a.desc[bg.y + l] = make_int4(bg.x, grp | (c << 16), p, s0 | (s1 << 16));
     }
   }
