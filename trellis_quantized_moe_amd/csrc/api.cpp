@@ -123,6 +123,15 @@ int gemv_rows(bool mxfp4) { return mxfp4 ? 16 : 8; }
 
 // Upper bound on the decode-batch plan's (group, chunk) pairs, each of which gets at least
 // one wave: every active expert has ceil(cnt / R) <= cnt / R + 1 chunks.
+// Pieces the reduction loads ahead of each slot's record. When the (group, expert) pairs
+// alone can fill the GEMV grid the split is expected to give one piece per slot, and planes
+// past the first would be stale reads; else up to 8 are fetched ahead. Only speed depends on
+// it: pieces past a slot's count are never added.
+static int reduce_prefetch(int64_t N, int E, int groups, int grid, int qmax) {
+  if ((int64_t)groups * std::min<int64_t>(E, N) >= grid) return 1;
+  return std::max(1, std::min(8, qmax));
+}
+
 int64_t gemv_chunk_bound(int64_t N, int E, int groups, bool mxfp4) {
   const int R = gemv_rows(mxfp4);
   return (int64_t)groups * ((int64_t)E + (N + R - 1) / R);
@@ -631,6 +640,7 @@ int trellis_expert_gemm(const tq_trellis_layer* L, const void* x, int64_t T,
     r.topk = topk;
     r.combine = (flags & TQ_COMBINE) ? 1 : 0;
     r.qmax = L->in / 256;
+    r.pre = tq::reduce_prefetch(N, L->E, W.groups, G, r.qmax);
     err = tq::launch_piece_reduce(r, s);
     if (err != hipSuccess) return hip_fail(err, "GEMV piece reduction launch");
     return ok();
@@ -760,6 +770,7 @@ int mx_expert_gemm(const MxLayer* L, const void* x, int64_t T, const int32_t* to
     r.topk = topk;
     r.combine = (flags & TQ_COMBINE) ? 1 : 0;
     r.qmax = L->in / 512;
+    r.pre = tq::reduce_prefetch(N, L->E, W.groups, G, r.qmax);
     err = tq::launch_piece_reduce(r, s);
     if (err != hipSuccess) return hip_fail(err, "GEMV piece reduction launch");
     return ok();

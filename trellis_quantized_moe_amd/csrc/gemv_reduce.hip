@@ -24,24 +24,30 @@ __device__ __forceinline__ float4 piece_slot(const PieceReduceArgs& a, int slot,
   const int t = slot / a.topk;
   const size_t stride = (size_t)a.N * a.out;
   const float* p = a.partial + (size_t)slot * a.out + o;
-  // The slot's record, its token's values and gate, and its first eight pieces are all
-  // requested before any arrives: the pieces' addresses do not depend on the record
-  // (indices clamped to the buffer's qmax pieces; the ones past the slot's count are
-  // dropped). Further pieces follow eight at a time; all are added in piece order.
+  // The slot's record, its token's values and gate and its first a.pre pieces are
+  // requested together (indices clamped to the buffer's qmax pieces; the ones past the
+  // slot's count are dropped); pieces pre .. 7 only once the record gives the slot's count.
+  // The host takes pre = 1 when the split is expected to give one piece per slot: a plane
+  // past the count holds no partial and would be read from HBM for nothing. Further pieces
+  // follow eight at a time; all are added in piece order.
   const int4 inf = a.slot_info[slot];
   const float add = a.xsum ? (float)a.xsum[t] : 0.0f;
   const float mul = a.xscale ? a.xscale[t] : 1.0f;
   const float gate = a.gates ? a.gates[slot] : 1.0f;
   float4 v[8];
+  v[0] = *reinterpret_cast<const float4*>(p);
 #pragma unroll
-  for (int q = 0; q < 8; ++q)
-    v[q] = *reinterpret_cast<const float4*>(p + (size_t)min(q, a.qmax - 1) * stride);
+  for (int q = 1; q < 8; ++q)
+    if (q < a.pre) v[q] = *reinterpret_cast<const float4*>(p + (size_t)min(q, a.qmax - 1) * stride);
   if (inf.x == SLOT_EMPTY) return make_float4(0.f, 0.f, 0.f, 0.f);
   if (inf.x < 0) {
     const float nan = __builtin_nanf("");
     return make_float4(nan, nan, nan, nan);
   }
   const int e = inf.x, np = inf.y;
+#pragma unroll
+  for (int q = 1; q < 8; ++q)
+    if (q >= a.pre && q < np) v[q] = *reinterpret_cast<const float4*>(p + (size_t)q * stride);
   const uint2 sc = a.scales ? *reinterpret_cast<const uint2*>(a.scales + (size_t)e * a.out + o)
                            : make_uint2(0x3C003C00u, 0x3C003C00u);  // fp16 1.0
   float4 s = v[0];

@@ -94,6 +94,7 @@ struct PieceReduceArgs {
   float* y;
   int N, out, topk, combine;
   int qmax;  // pieces the partial buffer holds per slot
+  int pre;   // pieces loaded before the slot's record arrives, 1 .. min(8, qmax)
 };
 constexpr int PIECE_MAX_TOPK = 64;  // largest topk (checked by the C ABI)
 hipError_t launch_piece_reduce(const PieceReduceArgs& a, hipStream_t s);
