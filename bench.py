@@ -25,8 +25,8 @@ before and after it (tq_time_kernel), over --kernel-iters direct calls of the st
 queued behind a bounded sleep kernel, so no host gap falls inside an interval. Its HBM
 traffic comes from rocprofv3 FETCH_SIZE / WRITE_SIZE runs (bench.py --drive mixed),
 calibrated against a plain elementwise copy of known size in the same runs and stored by
-bench.py --write-traffic. The CPU baseline times the oracle (test infrastructure, single
-thread) on the same workload.
+bench.py --write-traffic. The CPU baseline times the oracle (test infrastructure) on the
+same workload, on every core this process may use.
 """
 
 import argparse
@@ -376,10 +376,12 @@ def bench_prefill(torch, ops, args):
 
 
 def cpu_baseline_mixed(wl, n_experts):
-    """The oracle on a bounded sample: rotation of all tokens, then decode + FP64
-    contraction for the slots of n_experts of the active experts."""
+    """The oracle on a bounded sample, on every core this process may use: rotation of all
+    tokens, then decode + FP64 contraction for the slots of n_experts of the active experts
+    (0 = all), the experts split among worker processes (oracle.pool), each calling the
+    oracle unchanged with one BLAS thread."""
     import oracle
-    from threadpoolctl import threadpool_limits
+    from oracle import pool
     lay = wl["layer"]
     ids = wl["topk_ids"]
     active = np.unique(ids)
@@ -387,24 +389,17 @@ def cpu_baseline_mixed(wl, n_experts):
     pick = np.random.default_rng(7).choice(active, size=n, replace=False)
     keep = np.where(np.isin(ids, pick), ids, -1)
     nbytes = int(np.sum(lay["out"] * lay["in"] * lay["bits"][pick].astype(np.int64) // 8))
-    scales = oracle.f16_bits_to_f64(lay["scales"])
-
-    def weight_of(e):
-        K = int(lay["bits"][e])
-        n = lay["out"] * lay["in"] * K // 32
-        s = int(lay["code_off"][e]) // 4
-        return oracle.decode_unit(lay["codes"][s:s + n], K, lay["out"], lay["in"]).astype(np.float64)
-
-    with threadpool_limits(limits=1):
-        t0 = time.perf_counter()
-        xr = oracle.hadamard128_fp32_order(wl["x"], lay["signs"])
-        oracle.expert_gemm(xr, keep, None, lay["E"], weight_of, lambda e: scales[e])
-        sec = time.perf_counter() - t0
+    workers = pool.default_workers()
+    t0 = time.perf_counter()
+    xr = oracle.hadamard128_fp32_order(wl["x"], lay["signs"])
+    pool.trellis_slots(lay, xr, keep, None, workers=workers)
+    sec = time.perf_counter() - t0
     return {
-        "value": round(nbytes / sec / 1e9, 5), "unit": "GB/s", "cores": 1, "kind": "oracle",
+        "value": round(nbytes / sec / 1e9, 5), "unit": "GB/s", "cores": workers, "kind": "oracle",
         "sample": "%d of %d active experts of the mixed layer (their %d slots): oracle rotation of "
-                  "all 128 tokens + decode + FP64 contraction, %.1f MB compressed, %.1f s"
-                  % (len(pick), active.size, int(np.sum(keep >= 0)), nbytes / 1e6, sec),
+                  "all 128 tokens + decode + FP64 contraction, %.1f MB compressed, %.1f s wall "
+                  "on %d worker processes (worker start-up included)"
+                  % (len(pick), active.size, int(np.sum(keep >= 0)), nbytes / 1e6, sec, workers),
     }
 
 

@@ -21,8 +21,9 @@
  *   - All host-side argument checks run before any HIP call. Return value 0 = success;
  *     a negative TQ_E* code otherwise, with a message from tq_last_error() (thread-local).
  *   - Device-side data errors (an expert id outside [-1, E), a width byte not in {2,3,4},
- *     a misaligned unit offset) do not fault: the affected output slot is set to NaN and
- *     a sticky bit is set in the workspace status word (read with tq_device_status).
+ *     a unit offset that is misaligned or puts the unit outside the code buffer) do not
+ *     fault: the affected output slot is set to NaN and a sticky bit is set in the
+ *     workspace status word (read with tq_device_status).
  */
 #ifndef TQ_H
 #define TQ_H
@@ -53,7 +54,23 @@ extern "C" {
 
 /* ---- device status bits (tq_device_status) ------------------------------------------ */
 #define TQ_STATUS_BAD_EXPERT 1u  /* an id outside [-1, E): that slot's output is NaN    */
-#define TQ_STATUS_BAD_UNIT 2u    /* a width byte not in {2,3,4} or a misaligned offset  */
+#define TQ_STATUS_BAD_UNIT 2u    /* a width byte not in {2,3,4}, or an offset that is   */
+                                 /* misaligned or puts the unit outside codes_bytes     */
+
+/*
+ * Code layouts. TQ_LAYOUT_STORE is the store order of the pages' units (trellis: FORMAT F2;
+ * MXFP4 / fp8b32: HF orientation, rows of in/32 blocks). TQ_LAYOUT_GEMV is the same units
+ * repacked once (trellis_repack, mxfp4_repack, fp8b32_repack) into the order the kernels
+ * read them, so that a wave's loads stream contiguous memory. Both layouts give the same
+ * results bit for bit.
+ *   - trellis: the runs of 4 tiles that one 64-input step takes from each strip are
+ *     step-major within each group of 8 strips (128 output channels): the 8 runs of a
+ *     step, then the next step's; groups follow each other.
+ *   - MXFP4 / fp8b32: every 128-input step of every strip of 16 output channels is one
+ *     contiguous chunk (16 rows x 4 blocks); the scales keep their store order.
+ */
+#define TQ_LAYOUT_STORE 0
+#define TQ_LAYOUT_GEMV 1
 
 /*
  * A trellis expert layer (FORMAT F1-F7, F12). Expert e's unit holds out*in*K/8 bytes at
@@ -68,24 +85,14 @@ typedef struct tq_trellis_layer {
   int32_t E;                /* experts in the layer, 1 .. 4096                           */
   int32_t out;              /* output channels per expert, multiple of 16                 */
   int32_t in;               /* inputs per expert, multiple of 256                         */
-  int32_t reserved;         /* must be 0                                                  */
+  int32_t layout;           /* TQ_LAYOUT_STORE, or TQ_LAYOUT_GEMV after trellis_repack    */
   const uint8_t* bits;      /* device [E]: K of each expert (2, 3 or 4)                   */
   const int64_t* code_off;  /* device [E]: byte offset of each unit in codes, 16-aligned  */
   const uint32_t* codes;    /* device: the units                                          */
   const uint16_t* scales;   /* device [E][out]: fp16 per-output-channel scales            */
   const int8_t* signs;      /* device [in]: +-1 rotation signs for TQ_ROTATE, or NULL     */
+  int64_t codes_bytes;      /* bytes of `codes` (> 0): a unit must lie inside them         */
 } tq_trellis_layer;
-
-/*
- * Code layouts of the E8M0-scaled stores (MXFP4, fp8b32). TQ_LAYOUT_STORE is the pages'
- * store order (HF orientation, rows of in/32 blocks). TQ_LAYOUT_GEMV is the same units
- * repacked once by mxfp4_repack / fp8b32_repack so that every 128-input step of every
- * strip of 16 output channels is one contiguous chunk (16 rows x 4 blocks): the decode
- * GEMV then streams contiguous memory. The scales keep their store order. Both layouts give
- * the same results bit for bit.
- */
-#define TQ_LAYOUT_STORE 0
-#define TQ_LAYOUT_GEMV 1
 
 /*
  * An MXFP4 expert layer (FORMAT F9). E units back to back, each out*in/2 code bytes
@@ -142,16 +149,18 @@ typedef struct tq_fp8b32_layer {
  *             its counters at zero again, so a workspace is initialised once and reused;
  *             calls that share a workspace must be ordered on one stream.
  * Determinism (FORMAT F14): the same inputs give the same bits, whatever the launch
- * timing. The prefill mode also gives a slot the same bits whatever the rest of the batch
- * (a mixed-width layer equals single-width layers). The decode-batch mode splits each
- * routed expert's inputs among waves in proportion to the batch's whole routed work, so
- * across batches that route differently a slot's fp32 sum is grouped differently and
- * agrees to rounding (about 1e-7 relative).
- * Operands (FORMAT F10): the prefill mode feeds the matrix cores f16 activations; the
- * decode-batch mode feeds each token's activations as 16-bit integers on a per-token
- * power-of-two scale (two int8 halves), whose rounding of elements far below the token's
- * largest one is covered by the parity bound.
- * Precondition: |x| < 65520 (f16 range of the prefill operands).
+ * timing, and within one mode a slot gets the same bits whatever the rest of the batch
+ * routes: a mixed-width layer equals separate single-width layers bit for bit (the
+ * mixed-width kernels of the DeepSeek-V4.1-Flash-1017 TrellisMX K2 Mix page, intro, keep
+ * each width's routes bit-identical to the single-rate kernels). The decode-batch mode
+ * splits an expert's inputs among waves by the batch's whole routed work, but its piece
+ * sums are exact integers, added exactly, so the split never shows in a result.
+ * Operands (FORMAT F10): both modes put each token on a power-of-two scale of its own.
+ * The prefill mode feeds the matrix cores f16 activations (exact for every element within
+ * 2^31 of its token's largest magnitude); the decode-batch mode feeds 16-bit integers in
+ * two int8 halves, whose rounding of elements far below the token's largest one is covered
+ * by the parity bound. Any finite bf16 input is valid; a token with an infinite or NaN
+ * element gets NaN in its slots.
  */
 int trellis_expert_gemm(const tq_trellis_layer* L, const void* x, int64_t T,
                         const int32_t* topk_ids, const float* topk_w, int32_t topk,
@@ -212,21 +221,43 @@ int route_bucket(const int32_t* topk_ids, int64_t T, int32_t topk, int32_t E,
                  size_t ws_bytes, void* stream);
 
 /*
- * trellis_decode — test hook: decode one trellis unit to its integer values with the
- * device decoders, read back from the operands the matrix cores receive. Path 0: the
- * decode-batch GEMV's signed bytes lo8(m) - 128 and hi8(m) - 128 (q = their sum + 1).
- * Path 1: the prefill GEMM's byte sums q + 255 as f16 subnormals.
+ * trellis_decode — test hook: decode one trellis unit to its integer values
+ *   q[o][i] = lo8(m) + hi8(m) - 255,  m = state * 0x3A2F mod 2^16
+ * (DeepSeek-V4.1-Flash-1017 · dsx T16 page, "How T16 works", items 1 and 2: the 16-bit
+ * window, the multiply by 0x3A2F, the byte sum, column-major positions in 16 x 16 tiles;
+ * FORMAT F1-F5) with the device decoders the kernels run, read back from the operands the
+ * matrix cores receive. Path 0: the decode-batch GEMV's column decoder and signed bytes
+ * lo8(m) - 128 and hi8(m) - 128 (q = their sum + 1). Path 1: the prefill GEMM's decoders
+ * (each half of a tile column on its own for K = 2 and 3, the whole column for K = 4) and
+ * its byte sums q + 255 as f16 subnormals.
  *   codes  device, out*in*K/8 bytes, 16-byte aligned.   K in {2, 3, 4}.
- *   q      device int16 [out][in] (HF orientation: row = output channel).
+ *   out    multiple of 16.   in  multiple of 64.
+ *   q      device int16 [out][in] (HF orientation: row = output channel), 4-byte aligned.
+ * Errors: TQ_EINVAL for a bad K, shape or path, TQ_EALIGN for misaligned pointers.
  */
 int trellis_decode(const uint32_t* codes, int32_t K, int32_t out, int32_t in, int16_t* q,
                    int32_t path, void* stream);
 
 /*
- * mxfp4_decode — test hook: decode one MXFP4 unit to bf16 [out][in] with the device
- * decoder the MXFP4 kernels use.
+ * mxfp4_decode — test hook: decode one MXFP4 unit to bf16 [out][in],
+ *   w[o][i] = E2M1[code] * 2^(b[o][i/32] - 127)
+ * (DeepSeek-V4.1-Flash-1017 · exlr8 page, "Stores": E2M1 values, one E8M0 scale per 32
+ * inputs, codes then scales; FORMAT F9) with the device decoder the MXFP4 kernels use.
+ *   unit   device, out*in/2 + out*in/32 bytes, 16-byte aligned.   in multiple of 32.
+ *   w      device bf16 [out][in], 16-byte aligned.
  */
 int mxfp4_decode(const uint8_t* unit, int32_t out, int32_t in, uint16_t* w, void* stream);
+
+/*
+ * trellis_repack — copy a trellis layer's units from TQ_LAYOUT_STORE into TQ_LAYOUT_GEMV
+ * (see above): once, when a layer is loaded. Every unit with a good descriptor (width 2, 3 or
+ * 4, 16-byte aligned, inside codes_bytes) is written at its own offset code_off[e] of dst;
+ * other bytes of dst are left as they are.
+ *   L      host: the layer, L->layout == TQ_LAYOUT_STORE.
+ *   dst    device, 16-byte aligned, L->codes_bytes bytes, not overlapping L->codes; use it
+ *          as the codes of a layer with layout TQ_LAYOUT_GEMV (same bits, code_off, scales).
+ */
+int trellis_repack(const tq_trellis_layer* L, uint32_t* dst, void* stream);
 
 /*
  * mxfp4_repack / fp8b32_repack — copy a layer's units from TQ_LAYOUT_STORE into
@@ -239,8 +270,11 @@ int mxfp4_repack(const tq_mxfp4_layer* L, uint8_t* dst, void* stream);
 int fp8b32_repack(const tq_fp8b32_layer* L, uint8_t* dst, void* stream);
 
 /*
- * fp8b32_decode — test hook: decode one fp8b32 unit to bf16 [out][in] with the device
- * decoder the fp8b32 kernels use. out multiple of 32, in multiple of 32, out*in < 2^31.
+ * fp8b32_decode — test hook: decode one fp8b32 unit to bf16 [out][in],
+ *   w[o][i] = E4M3[code] * 2^(b[o/32][i/32] - 127)
+ * (DeepSeek-V4.1-Flash-1017 · exlr8 page, "Stores": FP8 E4M3 values with one E8M0 scale per
+ * 32 x 32 block; FORMAT F16) with the device decoder the fp8b32 kernels use. out multiple
+ * of 32, in multiple of 32, out*in < 2^31; unit and w 16-byte aligned.
  */
 int fp8b32_decode(const uint8_t* unit, int32_t out, int32_t in, uint16_t* w, void* stream);
 

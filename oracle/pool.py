@@ -1,0 +1,171 @@
+"""Runs the oracle over disjoint sets of experts in spawned worker processes (CPU only).
+
+TEST INFRASTRUCTURE, like the rest of this package: used by the GPU parity tests and by the
+benchmark's CPU baseline. It holds none of the method's arithmetic: each worker calls the
+oracle's own functions unchanged.
+
+A full-size workload is hundreds of expert units; decoding them one after another takes
+minutes in a single process. The outputs of different experts never interact (each
+routed slot reads one expert), so the routes are split by expert, each worker calls the
+oracle unchanged on the routes of its experts (the other slots masked to -1), and the
+parent puts the slots back together. The workers are started with the "spawn" method:
+they import numpy and the oracle only, never torch or the GPU library, and read the layer
+arrays from shared memory.
+"""
+
+import multiprocessing as mp
+import os
+from multiprocessing import shared_memory
+
+import numpy as np
+
+from . import ffn as _ffn, fpbits as _fpbits, gemm as _gemm, t16 as _t16
+
+_ARR = {}
+_META = {}
+_SHM = []
+
+
+def _attach(specs, meta):
+    # one BLAS thread per worker: the workers already use every core between them
+    from threadpoolctl import threadpool_limits
+    _SHM.append(threadpool_limits(limits=1))
+    for key, (name, shape, dtype) in specs.items():
+        shm = shared_memory.SharedMemory(name=name)
+        _SHM.append(shm)
+        _ARR[key] = np.ndarray(shape, dtype=np.dtype(dtype), buffer=shm.buf)
+    _META.update(meta)
+
+
+def _layer(prefix):
+    d = {k: _META[prefix + "." + k] for k in ("E", "out", "in")}
+    for k in ("bits", "code_off", "codes", "scales", "signs"):
+        d[k] = _ARR.get(prefix + "." + k)
+    return d
+
+
+def _trellis_fns(lay):
+    cache = {}
+
+    def weight_of(e):
+        if e not in cache:
+            K = int(lay["bits"][e])
+            n = lay["out"] * lay["in"] * K // 32
+            s = int(lay["code_off"][e]) // 4
+            cache.clear()  # one expert at a time: bounded memory
+            cache[e] = _t16.decode_unit(lay["codes"][s:s + n], K, lay["out"],
+                                          lay["in"]).astype(np.float64)
+        return cache[e]
+
+    scales = _fpbits.f16_bits_to_f64(lay["scales"])
+    return weight_of, (lambda e: scales[e])
+
+
+def _masked(ids, experts):
+    return np.where(np.isin(ids, experts), ids, -1)
+
+
+def _gemm_task(experts):
+    lay = _layer("layer")
+    ids = _ARR["ids"]
+    gates = _ARR.get("gates")
+    keep = _masked(ids, experts)
+    flat = np.nonzero(keep.reshape(-1) >= 0)[0]
+    if flat.size == 0:
+        return flat, np.zeros((0, lay["out"]))
+    y = _gemm.expert_gemm(_ARR["x"], keep, gates, lay["E"], *_trellis_fns(lay))
+    return flat, y.reshape(-1, lay["out"])[flat]
+
+
+def _ffn_task(experts):
+    g, u, d = _layer("gate"), _layer("up"), _layer("down")
+    ids = _ARR["ids"]
+    keep = _masked(ids, experts)
+    if not np.any(keep >= 0):
+        return np.zeros((ids.shape[0], d["out"]))
+    return _ffn.expert_ffn(_ARR["x"], keep, _ARR.get("gates"), g["E"], _trellis_fns(g),
+                             _trellis_fns(u), _trellis_fns(d), d["signs"])
+
+
+def default_workers():
+    """Worker processes: the cores this process may run on, at most 16."""
+    return min(16, len(os.sched_getaffinity(0)))
+
+
+class _Pool:
+    def __init__(self, arrays, meta, workers=None):
+        n = workers or default_workers()
+        self.shms = []
+        specs = {}
+        for key, a in arrays.items():
+            if a is None:
+                continue
+            a = np.ascontiguousarray(a)
+            shm = shared_memory.SharedMemory(create=True, size=max(1, a.nbytes))
+            np.ndarray(a.shape, dtype=a.dtype, buffer=shm.buf)[...] = a
+            self.shms.append(shm)
+            specs[key] = (shm.name, a.shape, a.dtype.str)
+        ctx = mp.get_context("spawn")
+        self.pool = ctx.Pool(n, initializer=_attach, initargs=(specs, meta))
+        self.n = n
+
+    def map(self, fn, items):
+        return self.pool.map(fn, items, chunksize=1)
+
+    def close(self):
+        self.pool.close()
+        self.pool.join()
+        for shm in self.shms:
+            shm.close()
+            shm.unlink()
+
+
+def _expert_chunks(ids, n, E):
+    active = np.unique(ids[(ids >= 0) & (ids < E)])
+    k = max(1, min(len(active), 4 * n))
+    return [c for c in np.array_split(active, k) if c.size]
+
+
+def _layer_arrays(prefix, lay):
+    arrays = {prefix + "." + k: lay.get(k) for k in ("bits", "code_off", "codes", "scales", "signs")}
+    meta = {prefix + "." + k: int(lay[k]) for k in ("E", "out", "in")}
+    return arrays, meta
+
+
+def trellis_slots(layer, x_bits, ids, gates=None, workers=None):
+    """oracle.expert_gemm of a trellis layer, [T, topk, out], computed expert by expert in
+    parallel. Slots with ids outside [0, E) are left as the oracle defines them (0 for -1,
+    NaN for invalid ids)."""
+    ids = np.asarray(ids)
+    arrays, meta = _layer_arrays("layer", layer)
+    arrays.update({"x": x_bits, "ids": ids, "gates": gates})
+    pool = _Pool(arrays, meta, workers)
+    try:
+        parts = pool.map(_gemm_task, _expert_chunks(ids, pool.n, layer["E"]))
+    finally:
+        pool.close()
+    y = np.zeros((ids.size, layer["out"]))
+    for flat, rows in parts:
+        y[flat] = rows
+    bad = ((ids < -1) | (ids >= layer["E"])).reshape(-1)
+    y[bad] = np.nan
+    return y.reshape(ids.shape + (layer["out"],))
+
+
+def ffn(gate, up, down, x_rot_bits, ids, gates=None, workers=None):
+    """oracle.expert_ffn, [T, H], summed over disjoint expert sets computed in parallel."""
+    ids = np.asarray(ids)
+    arrays, meta = {}, {}
+    for p, lay in (("gate", gate), ("up", up), ("down", down)):
+        a, m = _layer_arrays(p, lay)
+        arrays.update(a)
+        meta.update(m)
+    arrays.update({"x": x_rot_bits, "ids": ids, "gates": gates})
+    pool = _Pool(arrays, meta, workers)
+    try:
+        parts = pool.map(_ffn_task, _expert_chunks(ids, pool.n, gate["E"]))
+    finally:
+        pool.close()
+    y = np.sum(parts, axis=0)
+    y[np.any((ids < -1) | (ids >= gate["E"]), axis=1)] = np.nan  # as the oracle: NaN rows
+    return y

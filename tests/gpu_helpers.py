@@ -35,6 +35,17 @@ def rel_l2(got, ref):
     return float(np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-300))
 
 
+def slot_errors(got, ref):
+    """(pooled relative L2, largest per-slot relative L2) over the last axis. A slot whose
+    reference is all zero must be all zero (its error is then 0, else inf)."""
+    got = np.asarray(got, dtype=np.float64).reshape(-1, np.shape(ref)[-1])
+    ref = np.asarray(ref, dtype=np.float64).reshape(got.shape)
+    num = np.linalg.norm(got - ref, axis=1)
+    den = np.linalg.norm(ref, axis=1)
+    per = np.where(den > 0, num / np.where(den > 0, den, 1.0), np.where(num > 0, np.inf, 0.0))
+    return rel_l2(got, ref), float(per.max())
+
+
 def trellis_weight_fns(layer):
     """weight_of / scale_of for the oracle contraction of a host trellis layer."""
     cache = {}

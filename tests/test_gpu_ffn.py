@@ -5,7 +5,8 @@ import numpy as np
 import pytest
 
 import oracle
-from gpu_helpers import gpu, needs_gpu, ops, rel_l2, to_dev, torch, trellis_weight_fns
+from oracle import pool as oracle_pool
+from gpu_helpers import gpu, needs_gpu, ops, rel_l2, slot_errors, to_dev, torch, trellis_weight_fns
 from workloads import (bf16_from_normal, ffn_decode, ffn_layers, mixed_widths, rng_for,
                        softmax_gates, uniform_routes)
 
@@ -52,3 +53,4 @@ def test_ffn_decode_shapes_sampled_experts():
     y = run(wl["gate"], wl["up"], wl["down"], wl["x"], ids, gates, 0)
     ref = reference(wl["gate"], wl["up"], wl["down"], wl["x"], ids, gates)
     assert rel_l2(y, ref) <= TOL
+

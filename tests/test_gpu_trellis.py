@@ -6,8 +6,9 @@ import numpy as np
 import pytest
 
 import oracle
-from gpu_helpers import (dev, gpu, needs_gpu, ops, oracle_trellis, rel_l2, rotate_host, to_dev,
-                         torch)
+from oracle import pool as oracle_pool
+from gpu_helpers import (dev, gpu, needs_gpu, ops, oracle_trellis, rel_l2, rotate_host,
+                         slot_errors, to_dev, torch)
 from workloads import (bf16_from_normal, mixed_layer, one_unit, prefill_chunk, rng_for,
                        single_matrix, softmax_gates, trellis_layer, uniform_routes, zipf_routes)
 
@@ -116,17 +117,24 @@ def test_empty_invalid_and_status():
 
 
 def test_bad_unit_descriptor_gives_nan():
+    # a bad width byte (expert 1), a unit reaching past the end of the code buffer (expert
+    # 3: its offset is moved up by 16 bytes), a negative offset (expert 4)
     o = ops()
-    layer = small_layer(404, 3, 128, 512, widths=[2, 2, 2])
+    layer = small_layer(404, 5, 128, 512, widths=[2, 2, 2, 2, 2])
     layer["bits"] = layer["bits"].copy()
     layer["bits"][1] = 5
+    layer["code_off"] = layer["code_off"].copy()
+    assert layer["code_off"][4] == layer["codes"].nbytes - 128 * 512 * 2 // 8
+    layer["code_off"][3] = layer["code_off"][4] + 16
+    layer["code_off"][4] = -16
     L = o.TrellisLayer.from_host(layer)
-    x = to_dev(bf16_from_normal(rng_for(404, 1), (4, 512)), np.int16)
-    ids = to_dev(np.array([[0], [1], [2], [1]], dtype=np.int32))
+    x = to_dev(bf16_from_normal(rng_for(404, 1), (6, 512)), np.int16)
+    ids = to_dev(np.array([[0], [1], [2], [1], [3], [4]], dtype=np.int32))
     for flags in (1, 2):
-        ws = o.workspace(4, 1, 3, 128, 512, flags)
+        ws = o.workspace(6, 1, 5, 128, 512, flags)
         y = o.trellis_expert_gemm(L, x, ids, flags=flags, ws=ws).cpu().numpy()
-        assert np.all(np.isnan(y[1])) and np.all(np.isnan(y[3]))
+        for t in (1, 3, 4, 5):
+            assert np.all(np.isnan(y[t])), (flags, t)
         assert np.all(np.isfinite(y[0])) and np.all(np.isfinite(y[2]))
         assert o.device_status(ws) == 2
 
@@ -186,14 +194,27 @@ def test_mixed_width_matches_single_width_launches():
             ids_k = np.where(widths[ids] == K, ids, -1).astype(np.int32)
             y_k = run(single, x, ids_k, flags=flags)
             sel = widths[ids] == K
-            if flags == 2:
-                assert np.array_equal(y_k[sel], y_mixed[sel]), (flags, K)
-            else:
-                # the decode-batch kernel splits each expert's inputs among workgroups in
-                # proportion to the whole batch's work, so the fp32 partial sums are
-                # grouped differently in the two launches: equal up to rounding
-                err = np.abs(y_k[sel] - y_mixed[sel]).max() / np.abs(y_mixed[sel]).max()
-                assert err < 1e-5, (flags, K, err)
+            # both modes: the decode batch splits an expert's inputs by the whole batch's
+            # work, but adds the pieces' exact integer sums, so the split never shows
+            assert np.array_equal(y_k[sel], y_mixed[sel]), (flags, K)
+
+
+def test_decode_batch_slot_bits_do_not_depend_on_the_batch():
+    """One token's slots alone, and the same slots inside a large batch over many experts:
+    the plan splits the experts' inputs into very different pieces in the two launches (up
+    to in / 256 pieces alone, a few inside the large batch), and the results are the
+    same bits (FORMAT F14)."""
+    E, topk, inp = 64, 8, 5120
+    layer = small_layer(416, E, 128, inp)
+    x = bf16_from_normal(rng_for(416, 1), (200, inp))
+    ids = uniform_routes(rng_for(416, 2), 200, E, topk)
+    gates = softmax_gates(rng_for(416, 3), 200, topk)
+    big = run(layer, x, ids, gates, flags=1)
+    for t in (0, 77, 199):
+        alone = run(layer, x[t:t + 1], ids[t:t + 1], gates[t:t + 1], flags=1)
+        assert np.array_equal(alone[0], big[t]), t
+    ref = oracle_trellis(layer, x, ids, gates)
+    assert rel_l2(big, ref) <= TOL
 
 
 def test_graph_replay_with_changing_routes():
@@ -223,39 +244,40 @@ def test_graph_replay_with_changing_routes():
             assert rel_l2(got, ref) <= TOL
 
 
-def test_mixed_layer_full_size_sampled():
+@pytest.mark.timeout(900)
+def test_mixed_layer_full_size_every_slot():
+    """The mixed-width decode batch at full size (384 experts of 128 x 5120, 368 K=2, 15
+    K=3, 1 K=4, 128 tokens, top-8, the rotation fused), every one of the 1,024 slots
+    against the FP64 oracle: pooled and per-slot relative L2."""
     wl = mixed_layer()
     layer = wl["layer"]
-    y = run(layer, wl["x"], wl["topk_ids"], rotate_signs=layer["signs"])
-    xr = rotate_host(wl)
-    ids = wl["topk_ids"]
-    flat = ids.reshape(-1)
-    wide = np.nonzero(layer["bits"][flat] > 2)[0]
-    sample = np.unique(np.concatenate([wide, rng_for(410, 0).choice(flat.size, 24, replace=False)]))
-    ref = oracle_trellis(layer, xr, ids, None, sample=sample)
-    got = y.reshape(-1, 128)[sample]
-    assert rel_l2(got, ref.reshape(-1, 128)[sample]) <= TOL
-    assert np.all(np.isfinite(y))
+    o = ops()
+    L = o.TrellisLayer.from_host(layer)
+    y = o.trellis_expert_gemm(L, to_dev(wl["x"], np.int16), to_dev(wl["topk_ids"]),
+                              flags=o.TQ_ROTATE)
+    y = y.cpu().numpy()
+    ref = oracle_pool.trellis_slots(layer, rotate_host(wl), wl["topk_ids"])
+    pooled, worst = slot_errors(y, ref)
+    print("mixed layer, 1024 slots: pooled %.3e, worst slot %.3e" % (pooled, worst))
+    assert pooled <= TOL and worst <= TOL
 
 
-def test_prefill_chunk_full_size_sampled():
+@pytest.mark.timeout(900)
+def test_prefill_chunk_full_size_every_slot():
+    """The prefill chunk at full size (8,192 tokens, top-8, 384 K=3 experts, Zipf(1.1)
+    popularity, the rotation fused), every one of the 65,536 slots against the FP64
+    oracle: pooled and per-slot relative L2."""
     wl = prefill_chunk()
     layer = wl["layer"]
-    y = run(layer, wl["x"], wl["topk_ids"], rotate_signs=layer["signs"])
-    assert np.all(np.isfinite(y))
-    xr = rotate_host(wl)
-    ids = wl["topk_ids"]
-    flat = ids.reshape(-1)
-    rng = rng_for(411, 0)
-    # slots of the most and least popular experts plus random ones
-    counts = np.bincount(flat, minlength=384)
-    top, low = np.argmax(counts), np.argmin(np.where(counts > 0, counts, 1 << 30))
-    sample = np.unique(np.concatenate([
-        rng.choice(np.nonzero(flat == top)[0], 8, replace=False),
-        np.nonzero(flat == low)[0][:8],
-        rng.choice(flat.size, 16, replace=False)]))
-    ref = oracle_trellis(layer, xr, ids, None, sample=sample)
-    assert rel_l2(y.reshape(-1, 128)[sample], ref.reshape(-1, 128)[sample]) <= TOL
+    o = ops()
+    L = o.TrellisLayer.from_host(layer)
+    y = o.trellis_expert_gemm(L, to_dev(wl["x"], np.int16), to_dev(wl["topk_ids"]),
+                              flags=o.TQ_ROTATE)
+    y = y.cpu().numpy()
+    ref = oracle_pool.trellis_slots(layer, rotate_host(wl), wl["topk_ids"])
+    pooled, worst = slot_errors(y, ref)
+    print("prefill chunk, 65536 slots: pooled %.3e, worst slot %.3e" % (pooled, worst))
+    assert pooled <= TOL and worst <= TOL
 
 
 @pytest.mark.parametrize("flags", [1, 2])
@@ -343,25 +365,93 @@ def test_decode_batch_nonfinite_token():
     assert rel_l2(y[keep], ref) <= TOL
 
 
-def test_skewed_decode_batch_sampled():
+@pytest.mark.timeout(900)
+def test_skewed_decode_batch_every_slot():
     # a 128-token decode batch routed by Zipf(1.1) popularity over 384 mixed-width experts:
     # hot experts take dozens of tokens, i.e. several 8-token chunks with waves of their own
-    # (some experts with more than 32 pieces, written by the plan's waves); sampled slots of
-    # the hottest experts and of random ones against the oracle
+    # (some experts with more than 32 pieces, written by the plan's waves); every slot
+    # against the oracle
     wl = mixed_layer()
     layer = wl["layer"]
     ids = zipf_routes(rng_for(413, 4), 128, layer["E"], 8)
     counts = np.bincount(ids.reshape(-1), minlength=layer["E"])
     assert counts.max() > 32
     y = run(layer, wl["x"], ids, flags=ops().TQ_GEMV, rotate_signs=layer["signs"])
-    xr = rotate_host(wl)
-    flat = ids.reshape(-1)
-    hot = np.argsort(counts)[-3:]
-    hot_slots = np.nonzero(np.isin(flat, hot))[0]
-    sample = np.unique(np.concatenate([
-        rng_for(413, 5).choice(hot_slots, 24, replace=False),
-        rng_for(413, 6).choice(flat.size, 24, replace=False)]))
-    ref = oracle_trellis(layer, xr, ids, None, sample=sample)
-    got = y.reshape(-1, 128)[sample]
-    assert rel_l2(got, ref.reshape(-1, 128)[sample]) <= TOL
-    assert np.all(np.isfinite(y))
+    ref = oracle_pool.trellis_slots(layer, rotate_host(wl), ids)
+    pooled, worst = slot_errors(y, ref)
+    assert pooled <= TOL and worst <= TOL
+
+
+def test_decode_batch_reduction_prefetch_one_with_many_pieces():
+    """The reduction loads one piece ahead of a slot's record when the (group, expert)
+    pairs alone could fill the GEMV grid (groups * min(E, N) >= grid). Routes concentrated
+    on a few of many experts still give those experts many pieces: the later pieces are
+    then loaded after the record, and every one must be added."""
+    o = ops()
+    # 2,048 experts and 2,048 slots: groups * min(E, N) = 2048, the GEMV grid of a 256-CU
+    # GPU at 8 waves per CU, so the reduction prefetches one piece; the slots go to four
+    # experts, whose chunks then get several pieces each (up to in / 256 = 8)
+    E, T, topk, inp = 2048, 1024, 2, 2048
+    layer = small_layer(417, E, 128, inp, widths=np.full(E, 2, np.uint8))
+    x = bf16_from_normal(rng_for(417, 1), (T, inp))
+    ids = ((np.arange(T * topk, dtype=np.int32) % 3) * 5).reshape(T, topk)  # experts 0, 5, 10
+    ids[0, 1] = 7
+    y = run(layer, x, ids, flags=o.TQ_GEMV)
+    ref = oracle_trellis(layer, x, ids, None)
+    pooled, worst = slot_errors(y, ref)
+    assert pooled <= TOL and worst <= TOL
+
+
+@pytest.mark.parametrize("flags", [1, 2])
+def test_token_means_and_magnitudes(flags):
+    """Tokens with a large common offset (means 3 and 30: the prefill's byte-sum correction
+    removes 255 * sum(x), of order 1e7, from the accumulator), tokens far outside the f16
+    range (1e6, 1e30) and far below it (1e-6, 1e-30), a token mixing 1e4 and 1e-4, and a
+    token with an infinite element (NaN in its slots only): both modes keep every finite
+    token within the bound (each token is put on a power-of-two scale of its own)."""
+    E, T, topk, inp = 8, 9, 4, 1024
+    layer = small_layer(418, E, 128, inp)
+    rng = rng_for(418, 1)
+    z = rng.standard_normal((T, inp))
+    xf = np.stack([z[0] + 3.0, z[1] + 30.0, z[2] * 1e6, z[3] * 1e30, z[4] * 1e-6,
+                   z[5] * 1e-30, np.where(np.arange(inp) % 2 == 0, 1e4, 1e-4) * z[6],
+                   z[7], z[8]])
+    x = _bf16_bits(xf)
+    x[8, 3] = 0x7F80  # +inf
+    ids = uniform_routes(rng_for(418, 2), T, E, topk)
+    y = run(layer, x, ids, flags=flags)
+    assert np.all(np.isnan(y[8]))
+    ref = oracle_trellis(layer, x[:8], ids[:8], None)
+    for t in range(8):
+        pooled, worst = slot_errors(y[t], ref[t])
+        assert worst <= TOL, (flags, t, worst)
+    assert np.all(np.isfinite(y[:8]))
+
+@pytest.mark.parametrize("flags", [1, 2])
+@pytest.mark.parametrize("out_ch", [128, 176, 384])
+def test_repacked_layout_gives_the_same_bits(flags, out_ch):
+    """trellis_repack copies every unit into the kernels' read order (TQ_LAYOUT_GEMV): the
+    results are bit-equal to the store order in both modes, including a last group of fewer
+    than 8 strips (out = 176) and several groups (out = 384)."""
+    o = ops()
+    E, T, topk, inp = 10, 40, 4, 768
+    widths = np.array([2, 3, 4, 2, 2, 3, 4, 2, 3, 2], dtype=np.uint8)
+    layer = small_layer(419, E, out_ch, inp, widths=widths)
+    L = o.TrellisLayer.from_host(layer)
+    R = L.repacked()
+    assert R.layout == o.TQ_LAYOUT_GEMV and not torch.equal(R.codes, L.codes)
+    x = to_dev(bf16_from_normal(rng_for(419, 1), (T, inp)), np.int16)
+    ids_h = uniform_routes(rng_for(419, 2), T, E, topk)
+    ids_h[2, 1] = -1
+    ids = to_dev(ids_h)
+    gates = to_dev(softmax_gates(rng_for(419, 3), T, topk))
+    for fl in (flags | o.TQ_ROTATE, flags | o.TQ_ROTATE | o.TQ_COMBINE):
+        a = o.trellis_expert_gemm(L, x, ids, gates, flags=fl)
+        b = o.trellis_expert_gemm(R, x, ids, gates, flags=fl)
+        torch.cuda.synchronize()
+        assert torch.equal(a, b), fl
+    y = o.trellis_expert_gemm(R, x, ids, gates, flags=flags | o.TQ_ROTATE).cpu().numpy()
+    xr = oracle.hadamard128_fp32_order(x.cpu().numpy().view(np.uint16), layer["signs"])
+    ref = oracle_trellis(layer, xr, ids_h, gates.cpu().numpy())
+    pooled, worst = slot_errors(y, ref)
+    assert pooled <= TOL and worst <= TOL

@@ -35,12 +35,13 @@ class TrellisLayerC(ctypes.Structure):
         ("E", ctypes.c_int32),
         ("out", ctypes.c_int32),
         ("in_", ctypes.c_int32),
-        ("reserved", ctypes.c_int32),
+        ("layout", ctypes.c_int32),
         ("bits", ctypes.c_void_p),
         ("code_off", ctypes.c_void_p),
         ("codes", ctypes.c_void_p),
         ("scales", ctypes.c_void_p),
         ("signs", ctypes.c_void_p),
+        ("codes_bytes", ctypes.c_int64),
     ]
 
 
@@ -73,6 +74,7 @@ SIGNATURES = {
     "fp8b32_expert_gemm": (ctypes.c_int, [ctypes.POINTER(Mxfp4LayerC), _P, _I64, _P, _P, _I32,
                                           _P, _U32, _P, _SZ, _P]),
     "fp8b32_decode": (ctypes.c_int, [_P, _I32, _I32, _P, _P]),
+    "trellis_repack": (ctypes.c_int, [ctypes.POINTER(TrellisLayerC), _P, _P]),
     "mxfp4_repack": (ctypes.c_int, [ctypes.POINTER(Mxfp4LayerC), _P, _P]),
     "fp8b32_repack": (ctypes.c_int, [ctypes.POINTER(Mxfp4LayerC), _P, _P]),
     "mxfp4_to_nvfp4": (ctypes.c_int, [ctypes.POINTER(Mxfp4LayerC), _P, _P, _P, _P, _P]),

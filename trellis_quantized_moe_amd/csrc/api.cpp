@@ -118,11 +118,11 @@ T* at(void* ws, size_t off) {
 
 namespace tq {
 
+int set_error(int code, const char* msg) { return fail(code, "%s", msg); }
+
 // Routed slots one decode-batch wave takes: the token rows of its matrix-core operations.
 int gemv_rows(bool mxfp4) { return mxfp4 ? 16 : 8; }
 
-// Upper bound on the decode-batch plan's (group, chunk) pairs, each of which gets at least
-// one wave: every active expert has ceil(cnt / R) <= cnt / R + 1 chunks.
 // Pieces the reduction loads ahead of each slot's record. When the (group, expert) pairs
 // alone can fill the GEMV grid the split is expected to give one piece per slot, and planes
 // past the first would be stale reads; else up to 8 are fetched ahead. Only speed depends on
@@ -132,6 +132,8 @@ static int reduce_prefetch(int64_t N, int E, int groups, int grid, int qmax) {
   return std::max(1, std::min(8, qmax));
 }
 
+// Upper bound on the decode-batch plan's (group, chunk) pairs, each of which gets at least
+// one wave: every active expert has ceil(cnt / R) <= cnt / R + 1 chunks.
 int64_t gemv_chunk_bound(int64_t N, int E, int groups, bool mxfp4) {
   const int R = gemv_rows(mxfp4);
   return (int64_t)groups * ((int64_t)E + (N + R - 1) / R);
@@ -172,7 +174,7 @@ WsLayout ws_layout(int64_t T, int topk, int E, int out, int in, uint32_t flags, 
       off += round_up((size_t)T * 4, 256);
     }
     L.partial = off;
-    L.partial_bytes = round_up(Q * N * out * 4, 256);
+    L.partial_bytes = round_up(Q * N * out * (mxfp4 ? 4 : 8), 256);  // int64 trellis sums
     off += L.partial_bytes;
   } else {
     L.route_blocks = (int)((N + ROUTE_CHUNK - 1) / ROUTE_CHUNK);
@@ -197,7 +199,7 @@ WsLayout ws_layout(int64_t T, int topk, int E, int out, int in, uint32_t flags, 
       L.xprep = off;
       off += round_up((size_t)T * in * 2, 256);
       L.rowsum = off;
-      off += round_up((size_t)T * 4, 256);
+      off += round_up((size_t)T * 8, 256);
     }
   }
   if ((flags & TQ_COMBINE) && L.gemm) {
@@ -461,12 +463,15 @@ static int check_trellis_layer(const tq_trellis_layer* L) {
   if (L->E < 1 || L->E > 4096) return fail(TQ_EINVAL, "E = %d is outside 1..4096", L->E);
   if (L->out <= 0 || L->out % 16) return fail(TQ_EINVAL, "out = %d is not a positive multiple of 16", L->out);
   if (L->in <= 0 || L->in % 256) return fail(TQ_EINVAL, "in = %d is not a positive multiple of 256", L->in);
-  if (L->reserved != 0) return fail(TQ_EINVAL, "reserved field must be 0");
+  if (L->layout != TQ_LAYOUT_STORE && L->layout != TQ_LAYOUT_GEMV)
+    return fail(TQ_EINVAL, "layout = %d is not TQ_LAYOUT_STORE or TQ_LAYOUT_GEMV", L->layout);
   if (!L->bits || !L->code_off || !L->codes || !L->scales)
     return fail(TQ_EINVAL, "a layer pointer is NULL");
   if (!aligned(L->codes, 16)) return fail(TQ_EALIGN, "codes must be 16-byte aligned");
   if (!aligned(L->code_off, 8)) return fail(TQ_EALIGN, "code_off must be 8-byte aligned");
   if (!aligned(L->scales, 2)) return fail(TQ_EALIGN, "scales must be 2-byte aligned");
+  if (L->codes_bytes <= 0) return fail(TQ_EINVAL, "codes_bytes = %lld is not positive",
+                                       (long long)L->codes_bytes);
   return TQ_OK;
 }
 
@@ -586,7 +591,8 @@ int trellis_expert_gemm(const tq_trellis_layer* L, const void* x, int64_t T,
     p.topk = topk;
     p.bits = L->bits;
     p.code_off = L->code_off;
-    p.unit_bytes = 0;
+    p.codes_bytes = L->codes_bytes;
+    p.unit_bytes = (int64_t)L->out * L->in / 8;
     p.groups = W.groups;
     p.S = L->in / 64;
     p.R = tq::gemv_rows(false);
@@ -610,12 +616,13 @@ int trellis_expert_gemm(const tq_trellis_layer* L, const void* x, int64_t T,
     err = tq::launch_gemv_plan(p, s);
     if (err != hipSuccess) return hip_fail(err, "decode plan launch");
     tq::TrellisGemvArgs a{};
+    a.layout = L->layout;
     a.codes = L->codes;
     a.xq = p.xq;
     a.rec = p.rec;
     a.desc = p.desc;
     a.list = p.list;
-    a.partial = at<float>(ws, W.partial);
+    a.partial = at<int64_t>(ws, W.partial);
     a.x_bytes = (uint32_t)(T * L->in * 4);
     a.N = (int)N;
     a.out = L->out;
@@ -630,6 +637,7 @@ int trellis_expert_gemm(const tq_trellis_layer* L, const void* x, int64_t T,
     tq::PieceReduceArgs r{};
     r.slot_info = p.slot_info;
     r.partial = a.partial;
+    r.exact = 1;
     r.scales = L->scales;
     r.gates = topk_w;
     r.xsum = p.xsum;
@@ -646,18 +654,20 @@ int trellis_expert_gemm(const tq_trellis_layer* L, const void* x, int64_t T,
     return ok();
   } else {
     err = tq::launch_activation_prep(xb, T, L->in, at<uint32_t>(ws, W.xprep),
-                                     at<float>(ws, W.rowsum), (flags & TQ_ROTATE) != 0,
+                                     at<float2>(ws, W.rowsum), (flags & TQ_ROTATE) != 0,
                                      L->signs, s);
     if (err != hipSuccess) return hip_fail(err, "activation prep launch");
     rc = run_route(W, ws, topk_ids, N, L->E, L->out, y_slots, s);
     if (rc) return rc;
     tq::TrellisGemmArgs a{};
+    a.layout = L->layout;
     a.bits = L->bits;
     a.code_off = L->code_off;
     a.codes = L->codes;
+    a.codes_bytes = L->codes_bytes;
     a.scales = L->scales;
     a.xp = at<uint32_t>(ws, W.xprep);
-    a.rowsum = at<float>(ws, W.rowsum);
+    a.rowsum = at<float2>(ws, W.rowsum);
     a.x_bytes = (uint32_t)(T * L->in * 2);
     a.gates = topk_w;
     a.pairs = at<int32_t>(ws, W.pairs);
@@ -760,6 +770,7 @@ int mx_expert_gemm(const MxLayer* L, const void* x, int64_t T, const int32_t* to
     tq::PieceReduceArgs r{};
     r.slot_info = p.slot_info;
     r.partial = a.partial;
+    r.exact = 0;
     r.scales = nullptr;
     r.gates = topk_w;
     r.xsum = nullptr;
@@ -836,6 +847,27 @@ static int mx_repack(int fmt, int E, int out, int in, int layout, const uint8_t*
   if (rc) return rc;
   hipError_t err = tq::launch_mx_repack(fmt, units, dst, E, out, in, static_cast<hipStream_t>(stream));
   if (err != hipSuccess) return hip_fail(err, "repack launch");
+  return ok();
+}
+
+int trellis_repack(const tq_trellis_layer* L, uint32_t* dst, void* stream) {
+  int rc = check_trellis_layer(L);
+  if (rc) return rc;
+  if (L->layout != TQ_LAYOUT_STORE)
+    return fail(TQ_EINVAL, "the layer to repack must be in TQ_LAYOUT_STORE (layout = %d)", L->layout);
+  if (!dst) return fail(TQ_EINVAL, "dst is NULL");
+  if (!aligned(dst, 16)) return fail(TQ_EALIGN, "dst must be 16-byte aligned");
+  const char* a = reinterpret_cast<const char*>(L->codes);
+  const char* b = reinterpret_cast<const char*>(dst);
+  if (a < b + L->codes_bytes && b < a + L->codes_bytes)
+    return fail(TQ_EINVAL, "dst overlaps the layer's codes");
+  if ((int64_t)L->out * L->in / 2 >= ((int64_t)1 << 31))
+    return fail(TQ_EINVAL, "out * in is too large");
+  rc = check_device();
+  if (rc) return rc;
+  hipError_t err = tq::launch_trellis_repack(L->bits, L->code_off, L->codes, L->codes_bytes, L->E,
+                                             L->out, L->in, dst, static_cast<hipStream_t>(stream));
+  if (err != hipSuccess) return hip_fail(err, "trellis_repack launch");
   return ok();
 }
 

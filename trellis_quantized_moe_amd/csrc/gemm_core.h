@@ -6,8 +6,7 @@
 //   - a B producer (format-specific) decodes the step's 32 x 128 weights into operand
 //     pairs, each thread one run of 16 inputs of one output channel;
 //   - each thread copies 16 activations of one routed row into the A tile;
-//   - each wave runs its 4 x 4 block of 16x16x32 matrix-core operations (f16 for trellis
-//     weights, whose byte sums are exact f16 subnormals; bf16 for MXFP4).
+//   - each wave runs its 4 x 4 block of 16x16x32 bf16 matrix-core operations.
 // Two LDS buffers alternate: while the waves multiply step kk, they decode and stage step
 // kk + 1 into the other buffer, from registers loaded GEMM_RING steps earlier. Each output
 // is written once by the workgroup owning its row.
@@ -31,9 +30,8 @@ struct GemmShared {
 };
 
 struct GemmItem {
-  const void* x;           // bf16 x [T][in], or f16 pairs [T][in/16][8] (producer kF16)
+  const void* x;           // bf16 x [T][in]
   uint32_t x_bytes;        // size of x in bytes (< 2^31)
-  const float* rowsum;     // kF16: per-token sums of the f16 activations
   const float* gates;
   const uint16_t* scales;  // fp16 per output channel of this expert, or null
   float* y;
@@ -71,11 +69,7 @@ __device__ __forceinline__ GemmRsrc gemm_rsrc(const void* base, uint32_t bytes) 
                                            0x00020000);
 }
 
-// Producer interface (format-specific B operand):
-//   static constexpr bool kF16    true: f16 operands (the B values are the trellis byte
-//                                 sums (q + 255) as f16 subnormals, A is the f16 pair layout,
-//                                 and the epilogue scales by 2^24 and removes 255 * sum x);
-//                                 false: bf16 operands in natural input order
+// Producer interface (format-specific B operand, bf16 in natural input order):
 //   typename Raw                  this thread's undecoded data of one step (registers)
 //   void load(int kk, Raw& r)     issues the loads of step kk (any kk < steps)
 //   void decode(const Raw& r, uint32_t nat[8])
@@ -167,12 +161,7 @@ __device__ __forceinline__ void gemm_item(const GemmItem& it, GemmShared& sh, Pr
           const u32x4 aop = *reinterpret_cast<const u32x4*>(
               &sh.a[buf][(64 * wm + 16 * mb + n) * GEMM_LDS_STRIDE + 8 * g]);
 #pragma unroll
-          for (int nb = 0; nb < 4; ++nb) {
-            if constexpr (Producer::kF16)
-              acc[mb][nb] = mfma_f16(aop, bop[nb], acc[mb][nb]);
-            else
-              acc[mb][nb] = mfma_bf16(aop, bop[nb], acc[mb][nb]);
-          }
+          for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = mfma_bf16(aop, bop[nb], acc[mb][nb]);
         }
       }
       lds_barrier();
@@ -192,8 +181,6 @@ __device__ __forceinline__ void gemm_item(const GemmItem& it, GemmShared& sh, Pr
           if (row < it.nrows) {
             const int slot = sh.slot[row];
             float v = acc[mb][nb][i];
-            if constexpr (Producer::kF16)
-              v = v * 16777216.0f - 255.0f * it.rowsum[slot / it.topk];
             v = v * sc;
             if (it.gates) v = v * it.gates[slot];
             it.y[(size_t)slot * it.out + o] = v;

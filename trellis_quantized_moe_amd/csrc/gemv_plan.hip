@@ -63,9 +63,6 @@ __device__ void block_scan(int (&x)[NV], int (&tot)[NV]) {
   }
 }
 
-// Pieces per group for a step cost k under the per-wave cost bound T (T >= k): the steps
-// S split into pieces of at most floor(T / k) steps. The quotient is taken in fp32, exact
-// here (S <= 2^15, and a non-integer S / per is at least 1 / S away from an integer).
 // n / d for 0 <= n < 2^22 and d > 0, given rd = 1 / d in fp32: the product is within one of
 // the quotient there (its relative error is a few ulp, the quotient below 2^22), and one
 // remainder test corrects it. A handful of instructions in place of the integer divide.
@@ -75,6 +72,9 @@ __device__ __forceinline__ int small_div(int n, int d, float rd) {
   return q + (r >= d) - (r < 0);
 }
 
+// Pieces per group for a step cost k under the per-wave cost bound T (T >= k): the steps
+// S split into pieces of at most floor(T / k) steps. The quotient is taken in fp32, exact
+// here (S <= 2^15, and a non-integer S / per is at least 1 / S away from an integer).
 __device__ __forceinline__ int pieces_for(int S, int T, int k) {
   const int per = T / k;
   return (int)__builtin_ceilf((float)S / (float)per);
@@ -114,9 +114,14 @@ __device__ void plan_block(const PlanArgs& a) {
       kk[j] = a.bits[e];
       off[j] = a.code_off[e];
     }
+    // a unit is good when its width is 2, 3 or 4 and it lies, 16-byte aligned, inside codes
+    const int64_t ub = a.unit_bytes;  // a unit's bytes per bit of width: out * in / 8
 #pragma unroll
-    for (int j = 0; j < PLAN_PER; ++j)
-      kk[j] = (kk[j] >= 2 && kk[j] <= 4 && (off[j] & 15) == 0) ? kk[j] : 0;
+    for (int j = 0; j < PLAN_PER; ++j) {
+      const bool good = kk[j] >= 2 && kk[j] <= 4 && (off[j] & 15) == 0 && off[j] >= 0 &&
+                        off[j] <= a.codes_bytes - ub * kk[j];
+      kk[j] = good ? kk[j] : 0;
+    }
   } else {
 #pragma unroll
     for (int j = 0; j < PLAN_PER; ++j) {
@@ -533,87 +538,105 @@ __global__ __launch_bounds__(PLAN_THREADS) void gemv_plan_kernel(PlanArgs a) {
     prep_block(a, blockIdx.x - 1);
 }
 
-// Prefill-GEMM operands: PREP_TPB tokens per block, thread c converts tile column c of each
-// (columns c + blockDim, ... when in > 16 * blockDim), rotating it first when asked, into f16
-// pairs [lo: x[r + 8], hi: x[r]], and each token's sum of its f16 values in a fixed order
-// (16 values of a column in order, a thread's columns in order, the waves' butterfly, the
-// waves in order). The loads of all the block's tokens are issued before any is converted.
-constexpr int PREP_TPB = 1;
-
+// Prefill-GEMM operands, one token per block: thread c converts tile column c (columns
+// c + blockDim, ... when in > 16 * blockDim), rotating it first when asked (bf16 rounding
+// as hadamard128 does it), into f16 pairs [lo: x[r + 8], hi: x[r]]. Each token is first
+// scaled by a power of two 2^s, the one that puts its largest magnitude in [2^14, 2^15):
+// every element within 2^31 of that largest one is then exact in f16 (bf16 has 8
+// significant bits, f16 11 above 2^-14), and no token can overflow the f16 range. The
+// token's sum of its f16 values (in a fixed order: 16 values of a column in order, a
+// thread's columns in order, the waves' butterfly, the waves in order) and 2^-s are kept
+// for the epilogue; a token with a non-finite element gets 2^-s = NaN.
 // At most 64 registers (8 waves per SIMD): the kernel waits on memory, so occupancy counts.
 __global__ __launch_bounds__(PLAN_THREADS) __attribute__((amdgpu_waves_per_eu(8, 8)))
 void activation_prep_kernel(PlanArgs a) {
   typedef _Float16 h2 __attribute__((ext_vector_type(2)));
-  __shared__ float s_red[PREP_TPB][PLAN_WAVES];
-  const int tid = threadIdx.x, stride = blockDim.x;
+  __shared__ float s_red[PLAN_WAVES];
+  __shared__ float s_sum[PLAN_WAVES];
+  const int tid = threadIdx.x, stride = blockDim.x, nw = stride / 64;
   const int n_ti = a.in / 16;
-  const int t0 = blockIdx.x * PREP_TPB;
-  float sum[PREP_TPB];
+  const int t = blockIdx.x;
+  const bool one = n_ti <= stride;  // one column per thread: kept in registers
+  const uint4* src = reinterpret_cast<const uint4*>(a.x + (size_t)t * a.in);
+  auto column = [&](int c, float f[16]) {
+    const uint4 u = src[2 * c], v = src[2 * c + 1];
+    const uint32_t wv[8] = {u.x, u.y, u.z, u.w, v.x, v.y, v.z, v.w};
 #pragma unroll
-  for (int k = 0; k < PREP_TPB; ++k) sum[k] = 0.0f;
-  for (int c = tid; c < n_ti; c += stride) {
-    uint32_t m[16];
-    if (a.rotate) sign_masks(a.signs, c, m);
-    uint4 raw[PREP_TPB][2];
-#pragma unroll
-    for (int k = 0; k < PREP_TPB; ++k) {
-      if (t0 + k < a.T) {  // uniform
-        const uint4* src = reinterpret_cast<const uint4*>(a.x + (size_t)(t0 + k) * a.in);
-        raw[k][0] = src[2 * c];
-        raw[k][1] = src[2 * c + 1];
-      }
+    for (int q = 0; q < 8; ++q) {
+      f[2 * q] = bf16_lo_to_f32(wv[q]);
+      f[2 * q + 1] = bf16_hi_to_f32(wv[q]);
     }
+    if (a.rotate) {
+      uint32_t m[16];
+      sign_masks(a.signs, c, m);
+      rotate_column(f, m, c);
+    }
+  };
+  float amax = 0.0f;
+  auto fold_max = [&](const float f[16]) {
 #pragma unroll
-    for (int k = 0; k < PREP_TPB; ++k) {
-      if (t0 + k < a.T) {
-        const uint32_t wv[8] = {raw[k][0].x, raw[k][0].y, raw[k][0].z, raw[k][0].w,
-                                raw[k][1].x, raw[k][1].y, raw[k][1].z, raw[k][1].w};
-        float f[16];
-#pragma unroll
-        for (int q = 0; q < 8; ++q) {
-          f[2 * q] = bf16_lo_to_f32(wv[q]);
-          f[2 * q + 1] = bf16_hi_to_f32(wv[q]);
-        }
-        if (a.rotate) {
-          // the hardware conversion rounds to nearest even like f32_to_bf16_rne; the two
-          // could differ only on bf16 subnormals, which the f16 conversion below makes 0
-          rotate_column_f32(f, m, c);
-#pragma unroll
-          for (int q = 0; q < 16; ++q)
-            f[q] = __uint_as_float((uint32_t)__builtin_bit_cast(unsigned short, (__bf16)f[q]) << 16);
-        }
-        uint32_t P[8];
-        float hf[16];
-#pragma unroll
-        for (int r = 0; r < 8; ++r) {
-          const h2 p = (h2){(_Float16)f[r + 8], (_Float16)f[r]};
-          P[r] = __builtin_bit_cast(uint32_t, p);
-          hf[r] = (float)p.y;
-          hf[r + 8] = (float)p.x;
-        }
-        float cs = 0.0f;
-#pragma unroll
-        for (int q = 0; q < 16; ++q) cs += hf[q];
-        sum[k] += cs;
-        uint4* dst = reinterpret_cast<uint4*>(a.xp + (size_t)(t0 + k) * n_ti * 8);
-        dst[2 * c] = make_uint4(P[0], P[1], P[2], P[3]);
-        dst[2 * c + 1] = make_uint4(P[4], P[5], P[6], P[7]);
-      }
+    for (int j = 0; j < 16; ++j) {
+      const float m = fabsf(f[j]);
+      amax = fmaxf(amax, m <= 3.4e38f ? m : __builtin_inff());
+    }
+  };
+  float f0[16];
+  if (one) {
+    if (tid < n_ti) {
+      column(tid, f0);
+      fold_max(f0);
+    }
+  } else {
+    for (int c = tid; c < n_ti; c += stride) {
+      float f[16];
+      column(c, f);
+      fold_max(f);
     }
   }
-  const int nw = stride / 64;
-#pragma unroll
-  for (int k = 0; k < PREP_TPB; ++k) {
-    float v = sum[k];
-#pragma unroll
-    for (int d = 32; d >= 1; d >>= 1) v += __shfl_xor(v, d, 64);
-    if ((tid & 63) == 0) s_red[k][tid >> 6] = v;
+  amax = block_max(amax, s_red, nw);
+  const bool finite = amax <= 3.4e38f;
+  int e = 0;
+  if (finite && amax > 0.0f) {
+    int ex;
+    (void)frexpf(amax, &ex);  // amax in [2^(ex - 1), 2^ex)
+    e = min(15 - ex, 100);
   }
+  float sum = 0.0f;
+  auto convert = [&](const float f[16], int c) {
+    uint32_t P[8];
+    float hf[16];
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      const h2 p = (h2){(_Float16)ldexpf(f[r + 8], e), (_Float16)ldexpf(f[r], e)};
+      P[r] = __builtin_bit_cast(uint32_t, p);
+      hf[r] = (float)p.y;
+      hf[r + 8] = (float)p.x;
+    }
+    float cs = 0.0f;
+#pragma unroll
+    for (int q = 0; q < 16; ++q) cs += hf[q];
+    sum += cs;
+    uint4* dst = reinterpret_cast<uint4*>(a.xp + (size_t)t * n_ti * 8);
+    dst[2 * c] = make_uint4(P[0], P[1], P[2], P[3]);
+    dst[2 * c + 1] = make_uint4(P[4], P[5], P[6], P[7]);
+  };
+  if (one) {
+    if (tid < n_ti) convert(f0, tid);
+  } else {
+    for (int c = tid; c < n_ti; c += stride) {
+      float f[16];
+      column(c, f);
+      convert(f, c);
+    }
+  }
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) sum += __shfl_xor(sum, d, 64);
+  if ((tid & 63) == 0) s_sum[tid >> 6] = sum;
   lds_barrier();
-  if (tid < PREP_TPB && t0 + tid < a.T) {
+  if (tid == 0) {
     float v = 0.0f;
-    for (int w = 0; w < nw; ++w) v += s_red[tid][w];
-    a.rowsum[t0 + tid] = v;
+    for (int w = 0; w < nw; ++w) v += s_sum[w];
+    a.rowsum[t] = make_float2(v, finite ? ldexpf(1.0f, -e) : __builtin_nanf(""));
   }
 }
 
@@ -629,7 +652,7 @@ hipError_t launch_gemv_plan(const PlanArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_activation_prep(const uint16_t* x, int64_t T, int in, uint32_t* xp,
-                                  float* rowsum, bool rotate, const int8_t* signs,
+                                  float2* rowsum, bool rotate, const int8_t* signs,
                                   hipStream_t s) {
   if (T == 0) return hipSuccess;
   PlanArgs a{};
@@ -643,7 +666,7 @@ hipError_t launch_activation_prep(const uint16_t* x, int64_t T, int in, uint32_t
   // one thread per tile column (up to PLAN_THREADS): no wave without a column is launched
   const int n_ti = in / 16;
   const int threads = n_ti >= PLAN_THREADS ? PLAN_THREADS : (n_ti + 63) / 64 * 64;
-  const unsigned blocks = (unsigned)((T + PREP_TPB - 1) / PREP_TPB);
+  const unsigned blocks = (unsigned)T;
   hipLaunchKernelGGL(activation_prep_kernel, dim3(blocks), dim3(threads), 0, s, a);
   return hipGetLastError();
 }

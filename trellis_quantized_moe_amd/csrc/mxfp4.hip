@@ -345,7 +345,6 @@ __global__ __launch_bounds__(MX_THREADS, MxUnit<FMT>::kFp8 ? 2 : MX_WAVES_PER_SI
 // Thread t decodes, each step, inputs 16 h .. + 15 (h = t % 2) of the step for output
 // channel o = t / 2: 8 code bytes and the channel's scale byte of the step's 32-block.
 struct Mxfp4Producer {
-  static constexpr bool kF16 = false;
   struct Raw {
     uint32_t c0, c1, sb;
   };
@@ -390,7 +389,6 @@ struct Mxfp4Producer {
 // step's 32-block for output channel o: 16 code bytes and the scale byte of the channel's
 // 32 x 32 block.
 struct Fp8b32Producer {
-  static constexpr bool kF16 = false;
   struct Raw {
     u32x4 c;
     uint32_t sb;
@@ -440,7 +438,6 @@ __global__ __launch_bounds__(GEMM_THREADS, 2) void mxfp4_gemm_kernel(Mxfp4GemmAr
   GemmItem it;
   it.x = a.x;
   it.x_bytes = a.x_bytes;
-  it.rowsum = nullptr;
   it.gates = a.gates;
   it.scales = nullptr;
   it.y = a.y;

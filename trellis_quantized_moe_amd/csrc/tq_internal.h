@@ -27,6 +27,9 @@ constexpr int ROUTE_CHUNK = 2048;  // ids per route-count block
 constexpr int GEMM_MT = 128;       // token rows per prefill work item
 constexpr int GEMV_MAXK = 16;      // tokens per decode-batch chunk (one MFMA row block)
 
+// Records `msg` as this thread's last error (tq_last_error) and returns `code`.
+int set_error(int code, const char* msg);
+
 WsLayout ws_layout(int64_t T, int topk, int E, int out, int in, uint32_t flags,
                    bool mxfp4);
 
@@ -38,7 +41,9 @@ struct PlanArgs {
   int N, E, topk;
   const uint8_t* bits;      // trellis widths, or null: every step costs 1 (MXFP4)
   const int64_t* code_off;  // trellis unit offsets (with bits)
-  int64_t unit_bytes;       // MXFP4: expert e's unit is at e * unit_bytes
+  int64_t codes_bytes;      // trellis: size of the code buffer (a unit must lie inside)
+  int64_t unit_bytes;       // MXFP4: expert e's unit is at e * unit_bytes; trellis: a
+                            // unit's bytes per bit of width (out * in / 8)
   int groups, S;            // output groups per expert, steps per group (in / 64)
   int R;                    // routed slots one wave takes at most (a chunk of a slot list)
   int G;                    // the split's wave target
@@ -57,26 +62,28 @@ struct PlanArgs {
   const int8_t* signs;      // its signs, or null
   int T, in;
   uint32_t* xp;             // f16 pairs [T][in/16][8] (prefill GEMM operands)
-  float* rowsum;            // [T]
+  float2* rowsum;           // [T]: sum of the token's f16 values, and 2^-s
   uint32_t* xq;             // or int8 halves [T][2][in/16][8] (decode GEMV operands)
   float* xscale;            // [T]: 2^-e of each token
   int32_t* xsum;            // [T]: sum of each token's 16-bit integers
 };
 hipError_t launch_gemv_plan(const PlanArgs& a, hipStream_t s);
-// x~ (bf16 [T][in]) -> f16 pairs [T][in/16][8] (word r of tile column c = [lo: x[16c + r + 8],
-// hi: x[16c + r]]) and per-token sums of the f16 values: the activations of the trellis
-// prefill GEMM. With rotate, x is first rotated as hadamard128 would (FORMAT F8).
+// x~ (bf16 [T][in]) times a per-token power of two 2^s -> f16 pairs [T][in/16][8] (word r of
+// tile column c = [lo: x[16c + r + 8], hi: x[16c + r]]), and per token {sum of its f16
+// values, 2^-s}: the activations of the trellis prefill GEMM. With rotate, x is first
+// rotated as hadamard128 would (FORMAT F8).
 hipError_t launch_activation_prep(const uint16_t* x, int64_t T, int in, uint32_t* xp,
-                                  float* rowsum, bool rotate, const int8_t* signs,
+                                  float2* rowsum, bool rotate, const int8_t* signs,
                                   hipStream_t s);
 
 struct TrellisGemvArgs {
+  int layout;           // 0: units in store order (FORMAT F2); 1: read order (trellis_repack)
   const uint32_t* codes;
   const uint32_t* xq;   // int8 halves [T][2][in/16][8] (the plan's prep)
   const PlanRec* rec;
   const int4* desc;     // [G]
   const int32_t* list;
-  float* partial;       // [in / 256][N][out]: the pieces of each slot
+  int64_t* partial;     // [in / 256][N][out]: the pieces' exact sums of each slot
   uint32_t x_bytes;     // size of xq in bytes (< 2^31)
   int N, out, in, topk, G;
 };
@@ -86,7 +93,8 @@ hipError_t launch_trellis_gemv(const TrellisGemvArgs& a, hipStream_t s);
 
 struct PieceReduceArgs {
   const int4* slot_info;  // {expert, pieces, k, 0} or a SLOT_ code
-  const float* partial;
+  const void* partial;     // pieces: int64 exact sums (trellis) or fp32 (E8M0 stores)
+  int exact;               // 1: int64 pieces of x * (q - 1), 0: fp32 pieces
   const uint16_t* scales;  // fp16 per output channel, or null
   const float* gates;   // or null
   const int32_t* xsum;  // [T]: added to each slot's sum (the signed-byte correction), or null
@@ -100,12 +108,14 @@ constexpr int PIECE_MAX_TOPK = 64;  // largest topk (checked by the C ABI)
 hipError_t launch_piece_reduce(const PieceReduceArgs& a, hipStream_t s);
 
 struct TrellisGemmArgs {
+  int layout;           // 0: units in store order (FORMAT F2); 1: read order (trellis_repack)
   const uint8_t* bits;
   const int64_t* code_off;
   const uint32_t* codes;
+  int64_t codes_bytes;
   const uint16_t* scales;
   const uint32_t* xp;     // prepared activations: f16 pairs [T][in/16][8]
-  const float* rowsum;    // [T]: sum of each token's f16 activations
+  const float2* rowsum;   // [T]: {sum of the token's f16 activations, 2^-s}
   uint32_t x_bytes;       // size of xp in bytes (< 2^31)
   const float* gates;
   const int32_t* pairs;
@@ -178,6 +188,11 @@ hipError_t launch_combine(const float* slots, float* y, int64_t T, int topk, int
 hipError_t launch_hadamard(const uint16_t* x, uint16_t* y, int64_t rows, int64_t n,
                            const int8_t* signs, hipStream_t s);
 
+// Copies every good unit of a trellis layer (width 2..4, inside codes_bytes, 16-byte
+// aligned) from store order into the read order, at the same offset of dst.
+hipError_t launch_trellis_repack(const uint8_t* bits, const int64_t* code_off,
+                                 const uint32_t* codes, int64_t codes_bytes, int E, int out,
+                                 int in, uint32_t* dst, hipStream_t s);
 hipError_t launch_trellis_decode(const uint32_t* codes, int K, int out, int in, int16_t* q,
                                  int path, hipStream_t s);
 hipError_t launch_mxfp4_decode(const uint8_t* unit, int out, int in, uint16_t* w,

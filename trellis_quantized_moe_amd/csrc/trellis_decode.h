@@ -23,6 +23,21 @@ namespace tq {
 
 constexpr uint32_t T16_MULT2 = 0x3A2F3A2Fu;
 
+// ---- unit layouts ---------------------------------------------------------------------------
+// A unit is out / 16 strips of in / 16 tiles; the kernels read it in runs: the 4 tiles of
+// one strip that one 64-input step covers (tile columns 4 st .. 4 st + 3, 128 K bytes). In
+// the store order (FORMAT F2, TQ_LAYOUT_STORE) a strip's runs follow each other; in the
+// read order (TQ_LAYOUT_GEMV, written once by trellis_repack) the runs of one group of
+// 8 strips (128 output channels) are step-major, so the runs a step of a group needs are
+// contiguous, and so are a group's steps. Word offset of run (strip t, step st) within the
+// unit, S = in / 64 steps, n_strips = out / 16, TW = 8 K words per tile:
+__device__ __forceinline__ uint32_t run_word(int layout, int t, int st, int S, int n_strips,
+                                             int TW) {
+  if (layout == 0) return (uint32_t)((t * S + st) * 4 * TW);
+  const int g = t >> 3, ns = min(8, n_strips - 8 * g);
+  return (uint32_t)(((g * S * 8) + st * ns + (t & 7)) * 4 * TW);
+}
+
 template <int K>
 __device__ __forceinline__ int pair_ih(int r) {
   return K == 4 ? (r < 4 ? r : r + 4) : r;
@@ -159,6 +174,43 @@ __device__ __forceinline__ void byte_sums(const uint32_t M[8], uint32_t V[8]) {
     // M[r] = [hi: m[r], lo: m[r + 8]]
 #pragma unroll
     for (int r = 0; r < 8; ++r) V[r] = byte_sum_pair(M[r]);
+  }
+}
+
+// The prefill GEMM's operands of one tile column, in the layout above (register r holds
+// [hi: v[r], lo: v[r + 8]]), split into the two halves that feed the step's two products:
+// half h is registers 4 h .. 4 h + 3. w0, w1: the column's loaded words (w1 unused at
+// K = 2), wn: the right neighbour's first word, sel3: the K = 3 byte selector.
+// K = 2, 3 decode each half on its own (only its four m-pairs).
+template <int K>
+__device__ __forceinline__ void prefill_half(uint32_t w0, uint32_t w1, uint32_t wn,
+                                             uint32_t sel3, int h, uint32_t B[4]) {
+  static_assert(K == 2 || K == 3, "prefill_half: K = 2 or 3");
+  uint32_t M[4];
+  if constexpr (K == 2)
+    half_mpairs_k2(w0, wn, h, M);
+  else
+    half_mpairs_k3(w0, w1, wn, sel3, h, M);
+#pragma unroll
+  for (int r = 0; r < 4; ++r) B[r] = byte_sum_pair(M[r]);
+}
+
+// Both halves at once (K = 4 pairs its states across the halves, so it always takes this).
+template <int K>
+__device__ __forceinline__ void prefill_full(uint32_t w0, uint32_t w1, uint32_t wn,
+                                             uint32_t sel3, uint32_t B0[4], uint32_t B1[4]) {
+  uint32_t M[8], V[8];
+  if constexpr (K == 2)
+    col_mpairs_k2(w0, wn, M);
+  else if constexpr (K == 4)
+    col_mpairs_k4(w0, w1, wn, M);
+  else
+    col_mpairs_k3(w0, w1, wn, sel3, M);
+  byte_sums<K>(M, V);
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    B0[r] = V[r];
+    B1[r] = V[4 + r];
   }
 }
 

@@ -20,8 +20,9 @@
 // Each step: wait for this wave's loads of the step, one barrier (the partner wave's half
 // of the stage has landed and both waves are done with the stage about to be refilled),
 // start the loads of step + 2, decode, then 8 x 4 x 2 products. The epilogue scales by
-// 2^24, removes 255 * sum(x) per token (the byte-sum offset), applies the channel scale and
-// the gate, and writes each output once.
+// 2^24, removes 255 * sum(x) per token (the byte-sum offset), applies the channel scale,
+// the gate and the token's 2^-s (the prep's power-of-two scale), and writes each output
+// once.
 #include "gemm_core.h"
 #include "trellis_decode.h"
 
@@ -40,8 +41,8 @@ constexpr int TG_STAGES = 3;
 struct TgShared {
   alignas(16) uint8_t a[TG_STAGES][TG_STAGE];
   int slot[GEMM_MT];
-  float rs[GEMM_MT];    // 255 * sum of the row's token activations
-  float gate[GEMM_MT];  // the slot's gate, or 1
+  float rs[GEMM_MT];    // 255 * sum of the row's token activations (scaled by 2^s)
+  float gate[GEMM_MT];  // the slot's gate (or 1) times the token's 2^-s
 };
 
 typedef __attribute__((address_space(3))) void* LdsPtr;
@@ -120,15 +121,19 @@ __device__ __forceinline__ void tg_item(const TrellisGemmArgs& a, TgShared& sh,
     cvo[0] = 4u * (g * TW + w0);
     cvo[1] = 4u * (g * TW + w1);
   }
+  // run (strip 8 grp + s, step kk) at strip_off[nb] + kk * sstep bytes (run_word)
+  const int S = n_ti / 4, nst = a.out / 16;
+  const uint32_t base = 4u * run_word(a.layout, 8 * grp, 0, S, nst, TW);
+  const uint32_t sstep = 4u * run_word(a.layout, 8 * grp, 1, S, nst, TW) - base;
   uint32_t strip_off[4];
 #pragma unroll
   for (int nb = 0; nb < 4; ++nb) {
     const int s = 4 * w + nb;
-    strip_off[nb] = 4u * (uint32_t)((8 * grp + (s < ns ? s : ns - 1)) * n_ti * TW);
+    strip_off[nb] = 4u * run_word(a.layout, 8 * grp + (s < ns ? s : ns - 1), 0, S, nst, TW);
   }
   ColWords<K> code[2][4];
   auto load_codes = [&](int slot, int kk) {
-    const uint32_t so = 4u * (uint32_t)(4 * kk * TW);
+    const uint32_t so = (uint32_t)kk * sstep;
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb) {
       const uint32_t o = strip_off[nb] + so;
@@ -160,35 +165,19 @@ __device__ __forceinline__ void tg_item(const TrellisGemmArgs& a, TgShared& sh,
   // that each half is decoded while the matrix cores run the other half's products.
   uint32_t B0[4][4], B1[4][4];
   auto dec_half = [&](int slot, int h, uint32_t Bh[4][4]) {
+    if constexpr (K != 4) {
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb) {
-      const ColWords<K>& c = code[slot][nb];
-      uint32_t M[4];
-      if constexpr (K == 2)
-        half_mpairs_k2(c.w[0], row_next(c.w[0]), h, M);
-      else if constexpr (K == 3)
-        half_mpairs_k3(c.w[0], c.w[1], row_next(c.w[0]), sel3, h, M);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) Bh[nb][r] = byte_sum_pair(M[r]);
+      for (int nb = 0; nb < 4; ++nb) {
+        const ColWords<K>& c = code[slot][nb];
+        prefill_half<K>(c.w[0], c.w[K == 2 ? 0 : 1], row_next(c.w[0]), sel3, h, Bh[nb]);
+      }
     }
   };
   auto dec_full = [&](int slot) {
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb) {
       const ColWords<K>& c = code[slot][nb];
-      uint32_t M[8], V[8];
-      if constexpr (K == 2)
-        col_mpairs_k2(c.w[0], row_next(c.w[0]), M);
-      else if constexpr (K == 4)
-        col_mpairs_k4(c.w[0], c.w[1], row_next(c.w[0]), M);
-      else
-        col_mpairs_k3(c.w[0], c.w[1], row_next(c.w[0]), sel3, M);
-      byte_sums<K>(M, V);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        B0[nb][r] = V[r];
-        B1[nb][r] = V[4 + r];
-      }
+      prefill_full<K>(c.w[0], c.w[K == 2 ? 0 : 1], row_next(c.w[0]), sel3, B0[nb], B1[nb]);
     }
   };
   auto products = [&](const uint8_t* st, uint32_t rd, const uint32_t Bh[4][4], auto full_tag) {
@@ -293,8 +282,10 @@ __global__ __launch_bounds__(TG_THREADS, 2) void trellis_gemm_kernel(TrellisGemm
     float rs = 0.0f, gt = 1.0f;
     if (m < nrows) {
       slot = a.pairs[itd.y + m];
-      rs = BYTE_SUM_OFFSET * a.rowsum[slot / a.topk];
-      if (a.gates) gt = a.gates[slot];
+      const float2 rw = a.rowsum[slot / a.topk];
+      rs = BYTE_SUM_OFFSET * rw.x;
+      gt = rw.y;  // a power of two: the product below is exact
+      if (a.gates) gt = a.gates[slot] * gt;
     }
     sh.slot[m] = slot;
     sh.rs[m] = rs;
@@ -302,11 +293,14 @@ __global__ __launch_bounds__(TG_THREADS, 2) void trellis_gemm_kernel(TrellisGemm
   }
   __syncthreads();
   const uint32_t* unit = a.codes + off / 4;
-  if (K == 2 && !(off & 15)) {
+  // the unit must be 16-byte aligned and lie inside the code buffer
+  const bool inside = !(off & 15) && off >= 0 &&
+                      off <= a.codes_bytes - (int64_t)a.out * a.in / 8 * (K >= 2 && K <= 4 ? K : 0);
+  if (K == 2 && inside) {
     tg_item<2>(a, sh, unit, e, grp, nrows, ns);
-  } else if (K == 3 && !(off & 15)) {
+  } else if (K == 3 && inside) {
     tg_item<3>(a, sh, unit, e, grp, nrows, ns);
-  } else if (K == 4 && !(off & 15)) {
+  } else if (K == 4 && inside) {
     tg_item<4>(a, sh, unit, e, grp, nrows, ns);
   } else {
     for (int v = threadIdx.x; v < nrows * ns * 16; v += TG_THREADS) {

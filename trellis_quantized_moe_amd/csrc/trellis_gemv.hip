@@ -17,9 +17,9 @@
 // are decoded.
 //
 // A wave takes one chunk of up to 8 of its expert's routed tokens (the plan gives each
-// chunk its own waves). At the end it joins each token's two halves (256 hi + lo) and
-// stores the piece's partial sums; the reduction launch adds the pieces in order and
-// applies the epilogue.
+// chunk its own waves). At the end it joins each token's two halves (256 hi + lo, exact in
+// int64) and stores the piece's exact integer sums; the reduction launch adds the pieces
+// (exactly, so the split never changes a result) and applies the epilogue.
 #include "gemv_wave.h"
 #include "tq_internal.h"
 #include "trellis_decode.h"
@@ -150,11 +150,16 @@ __device__ __forceinline__ void stream(const TrellisGemvArgs& a, const uint32_t*
   const LaneOffsets<K> lo(g, n);
   const Rsrc rc = make_rsrc(unit, (uint32_t)((size_t)a.out * a.in * K / 8));
   const uint32_t cvo[2] = {4u * lo.o[0], 4u * lo.o[1]};
-  const uint32_t c0 = 4u * (uint32_t)(((size_t)grp * 8 * n_ti + 4 * s0) * TW);
-  constexpr uint32_t cstep = 4u * 4 * TW;  // bytes per step and strip (4 tile columns)
+  // byte offsets: run (strip 8 grp + s8, step st) at c0 + st cstep + sso[s8] (run_word)
+  const int S = n_ti / 4, nst = a.out / 16;
+  const uint32_t c0 = 4u * run_word(a.layout, 8 * grp, s0, S, nst, TW);
+  const uint32_t cstep = 4u * (run_word(a.layout, 8 * grp, s0 + 1, S, nst, TW) -
+                               run_word(a.layout, 8 * grp, s0, S, nst, TW));
   uint32_t sso[8];
 #pragma unroll
-  for (int s8 = 0; s8 < 8; ++s8) sso[s8] = 4u * (uint32_t)((s8 < ns ? s8 : ns - 1) * n_ti * TW);
+  for (int s8 = 0; s8 < 8; ++s8)
+    sso[s8] = 4u * (run_word(a.layout, 8 * grp + (s8 < ns ? s8 : ns - 1), s0, S, nst, TW) -
+                    run_word(a.layout, 8 * grp, s0, S, nst, TW));
   const Rsrc rx = make_rsrc(a.xq, a.x_bytes);
   const uint32_t xvo = tok >= 0 ? 32u * (uint32_t)((2 * tok + half) * n_ti + g) : 0x80000000u;
   const uint32_t x0 = 128u * (uint32_t)s0;
@@ -191,7 +196,7 @@ __device__ __forceinline__ void stream(const TrellisGemvArgs& a, const uint32_t*
 }
 
 // One piece: expert record r, steps s0 .. s1 - 1 of group grp for chunk `chunk` of the
-// expert's slot list (up to 8 routed tokens); sums to partial[piece].
+// expert's slot list (up to 8 routed tokens); exact int64 sums to partial[piece].
 template <int K>
 __device__ __forceinline__ void run_piece(const TrellisGemvArgs& a, const PlanRec& r, int grp,
                                           int chunk, int s0, int s1, int piece) {
@@ -199,7 +204,7 @@ __device__ __forceinline__ void run_piece(const TrellisGemvArgs& a, const PlanRe
   const int j = n & 7, half = n >> 3;  // this lane's A row: token j of the chunk, its half
   const int ns = min(8, a.out / 16 - grp * 8);
   const uint32_t* unit = a.codes + r.off / 4;
-  float* dst = a.partial + (size_t)piece * a.N * a.out + grp * 128 + n;
+  int64_t* dst = a.partial + (size_t)piece * a.N * a.out + grp * 128 + n;
   {
     const int c0 = 8 * chunk;
     const int rows = min(8, r.cnt - c0);
@@ -213,12 +218,12 @@ __device__ __forceinline__ void run_piece(const TrellisGemvArgs& a, const PlanRe
     for (int i = 0; i < 4; ++i) {
       const int m = 4 * g + i;
       const int sm = __shfl(slot, m & 7);
-      float v[8];
+      int64_t v[8];
 #pragma unroll
       for (int s8 = 0; s8 < 8; ++s8)
-        v[s8] = 256.0f * (float)acc[s8][i] + (float)__shfl_xor(acc[s8][i], 32, 64);
+        v[s8] = (int64_t)acc[s8][i] * 256 + (int64_t)__shfl_xor(acc[s8][i], 32, 64);
       if (g < 2 && m < rows) {
-        float* row = dst + (size_t)sm * a.out;
+        int64_t* row = dst + (size_t)sm * a.out;
 #pragma unroll
         for (int s8 = 0; s8 < 8; ++s8)
           if (s8 < ns) row[s8 * 16] = v[s8];
@@ -259,10 +264,10 @@ __global__ __launch_bounds__(256) void trellis_decode_kernel(const uint32_t* __r
   const LaneOffsets<K> lo(g, n);
   ColWords<K> cw;
   load_col<K>(codes + (size_t)(strip * n_ti + ti0) * TW, lo, cw);
-  uint32_t M[8];
-  decode_col<K>(cw, lo.sel3, M);
   int16_t* row = q + (size_t)(strip * 16 + n) * in + (ti0 + g) * 16;
   if (path == 0) {
+    uint32_t M[8];
+    decode_col<K>(cw, lo.sel3, M);
     // operand register r: bytes [lo8 - 128, hi8 - 128] of input r + 8, then of input r;
     // q = (lo8 - 128) + (hi8 - 128) + 1
     uint32_t B[8];
@@ -275,10 +280,17 @@ __global__ __launch_bounds__(256) void trellis_decode_kernel(const uint32_t* __r
       row[r + 8] = (int16_t)(b0 + b1 + 1);
     }
   } else {
-    // V[r] holds inputs r (high half) and r + 8 (low half) as the f16 subnormals
-    // (q + 255) * 2^-24
+    // the prefill GEMM's operands (prefill_half for K = 2, 3, as its main loop decodes
+    // them; prefill_full for K = 4): V[r] holds inputs r (high half) and r + 8 (low half)
+    // as the f16 subnormals (q + 255) * 2^-24
     uint32_t V[8];
-    byte_sums<K>(M, V);
+    const uint32_t w1 = cw.w[K == 2 ? 0 : 1], wn = row_next(cw.w[0]);
+    if constexpr (K == 4) {
+      prefill_full<K>(cw.w[0], w1, wn, lo.sel3, V, V + 4);
+    } else {
+      prefill_half<K>(cw.w[0], w1, wn, lo.sel3, 0, V);
+      prefill_half<K>(cw.w[0], w1, wn, lo.sel3, 1, V + 4);
+    }
 #pragma unroll
     for (int r = 0; r < 8; ++r) {
       row[r] = (int16_t)(f16_bits_to_f32(V[r] >> 16) * BYTE_SUM_SCALE - BYTE_SUM_OFFSET);
@@ -287,7 +299,42 @@ __global__ __launch_bounds__(256) void trellis_decode_kernel(const uint32_t* __r
   }
 }
 
+// ---- repack into the read order ---------------------------------------------------------
+// Thread i of grid row e copies 16-byte chunk i of unit e from its run in store order to the
+// same run in read order (run_word). A unit is out / 16 strips x S runs of 128 K bytes; bad
+// units (width not 2..4, misaligned, not inside codes) are skipped.
+__global__ __launch_bounds__(256) void trellis_repack_kernel(const uint8_t* __restrict__ bits,
+                                                             const int64_t* __restrict__ code_off,
+                                                             const uint32_t* __restrict__ codes,
+                                                             int64_t codes_bytes, int out, int in,
+                                                             uint32_t* __restrict__ dst) {
+  const int e = blockIdx.y;
+  const int K = bits[e];
+  const int64_t off = code_off[e];
+  const int64_t ub = (int64_t)out * in / 8 * K;
+  if (K < 2 || K > 4 || (off & 15) || off < 0 || off > codes_bytes - ub) return;
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= ub / 16) return;
+  const int TW = 8 * K, S = in / 64, nst = out / 16;
+  const int per_run = 8 * K;  // 16-byte chunks per run (128 K bytes)
+  const int r = (int)(i / per_run), c = (int)(i % per_run);
+  const int t = r / S, st = r % S;
+  const uint4* from = reinterpret_cast<const uint4*>(codes + off / 4 + run_word(0, t, st, S, nst, TW));
+  uint4* to = reinterpret_cast<uint4*>(dst + off / 4 + run_word(1, t, st, S, nst, TW));
+  to[c] = from[c];
+}
+
 }  // namespace
+
+hipError_t launch_trellis_repack(const uint8_t* bits, const int64_t* code_off,
+                                 const uint32_t* codes, int64_t codes_bytes, int E, int out,
+                                 int in, uint32_t* dst, hipStream_t s) {
+  const int64_t chunks = (int64_t)out * in / 8 * 4 / 16;  // of the widest unit
+  const dim3 grid((unsigned)((chunks + 255) / 256), (unsigned)E);
+  hipLaunchKernelGGL(trellis_repack_kernel, grid, dim3(256), 0, s, bits, code_off, codes,
+                     codes_bytes, out, in, dst);
+  return hipGetLastError();
+}
 
 int trellis_gemv_grid() {
   static int cache[64];

@@ -40,6 +40,7 @@ class TrellisLayer:
     codes: torch.Tensor      # int32 [words] (uint32 bit patterns)
     scales: torch.Tensor     # int16 [E, out] (fp16 bit patterns)
     signs: torch.Tensor = None  # int8 [in] rotation signs (TQ_ROTATE), or None
+    layout: int = TQ_LAYOUT_STORE
 
     @classmethod
     def from_host(cls, layer, device="cuda"):
@@ -57,13 +58,24 @@ class TrellisLayer:
     def with_codes(self, codes):
         """The same layer reading its units from another copy of the code buffer."""
         return TrellisLayer(self.E, self.out, self.in_, self.bits, self.code_off, codes,
-                            self.scales, self.signs)
+                            self.scales, self.signs, self.layout)
+
+    def repacked(self):
+        """The same layer with its units copied into TQ_LAYOUT_GEMV (see trellis_repack in
+        include/tq.h)."""
+        _require_cuda(self.codes)
+        dst = torch.zeros_like(self.codes)
+        c = self.c_struct()
+        check(_lib.load().trellis_repack(ctypes.byref(c), _ptr(dst), _stream(self.codes.device)))
+        return TrellisLayer(self.E, self.out, self.in_, self.bits, self.code_off, dst,
+                            self.scales, self.signs, TQ_LAYOUT_GEMV)
 
     def c_struct(self):
-        return _lib.TrellisLayerC(self.E, self.out, self.in_, 0, self.bits.data_ptr(),
+        return _lib.TrellisLayerC(self.E, self.out, self.in_, self.layout, self.bits.data_ptr(),
                                   self.code_off.data_ptr(), self.codes.data_ptr(),
                                   self.scales.data_ptr(),
-                                  None if self.signs is None else self.signs.data_ptr())
+                                  None if self.signs is None else self.signs.data_ptr(),
+                                  self.codes.numel() * self.codes.element_size())
 
 
 @dataclass
