@@ -332,6 +332,27 @@ size_t tq_ffn_workspace_bytes(int64_t T, int32_t topk, int32_t E, int32_t H, int
 int mxfp4_to_nvfp4(const tq_mxfp4_layer* L, uint8_t* codes, uint8_t* scales, float* scale2,
                    uint8_t* status, void* stream);
 
+/*
+ * trellis_expert_gemm_noalloc — trellis_expert_gemm for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc). Arguments, results and errors as trellis_expert_gemm, without ws / ws_bytes:
+ * the workspace is a static device array of TQ_NOALLOC_SCRATCH_BYTES bytes that each GPU
+ * the library runs on holds until the process ends (looked up once per device, its status
+ * word zeroed by a small kernel on the first call's stream). The call allocates nothing.
+ *   - A call whose tq_workspace_bytes(T, topk, E, out, in, flags) exceeds
+ *     TQ_NOALLOC_SCRATCH_BYTES returns TQ_EWORKSPACE before any GPU work (32 MiB holds a
+ *     decode batch of 1,024 slots of 128 x 5120 units, or a prefill of about 2,500 tokens).
+ *   - Every call on one GPU shares that GPU's array, which keeps the last call's contents:
+ *     calls that overlap on one GPU (on different streams, or from different threads
+ *     without ordering) race. Order them on one stream.
+ *   - Data errors give NaN slots as in trellis_expert_gemm; the status word that records
+ *     them is not exposed.
+ */
+#define TQ_NOALLOC_SCRATCH_BYTES (32u << 20)
+int trellis_expert_gemm_noalloc(const tq_trellis_layer* L, const void* x, int64_t T,
+                                const int32_t* topk_ids, const float* topk_w, int32_t topk,
+                                float* y, uint32_t flags, void* stream);
+
 /* Workspace bytes the expert GEMM calls (and route_bucket with flags TQ_GEMM) need. */
 size_t tq_workspace_bytes(int64_t T, int32_t topk, int32_t E, int32_t out, int32_t in,
                           uint32_t flags);

@@ -26,6 +26,8 @@ TQ_GEMM = 2
 TQ_COMBINE = 4
 TQ_ROTATE = 8
 
+TQ_NOALLOC_SCRATCH_BYTES = 32 << 20
+
 TQ_STATUS_BAD_EXPERT = 1
 TQ_STATUS_BAD_UNIT = 2
 
@@ -81,6 +83,8 @@ SIGNATURES = {
     "trellis_expert_ffn": (ctypes.c_int, [ctypes.POINTER(TrellisLayerC), ctypes.POINTER(TrellisLayerC),
                                           ctypes.POINTER(TrellisLayerC), _P, _I64, _P, _P, _I32,
                                           _P, _U32, _P, _SZ, _P]),
+    "trellis_expert_gemm_noalloc": (ctypes.c_int, [ctypes.POINTER(TrellisLayerC), _P, _I64, _P,
+                                                   _P, _I32, _P, _U32, _P]),
     "tq_ffn_workspace_bytes": (_SZ, [_I64, _I32, _I32, _I32, _I32, _U32]),
     "tq_workspace_bytes": (_SZ, [_I64, _I32, _I32, _I32, _I32, _U32]),
     "tq_last_error": (ctypes.c_char_p, []),

@@ -178,6 +178,22 @@ def trellis_expert_gemm(layer, x, topk_ids, topk_w=None, flags=TQ_AUTO, out=None
                  layer.in_, x, topk_ids, topk_w, flags, out, ws, False)
 
 
+def trellis_expert_gemm_noalloc(layer, x, topk_ids, topk_w=None, flags=TQ_AUTO, out=None):
+    """trellis_expert_gemm with the library's static device scratch as its workspace (see
+    trellis_expert_gemm_noalloc in include/tq.h). `out` must be given for the call itself
+    to allocate nothing."""
+    _require_cuda(x, topk_ids, topk_w, out)
+    T, topk = topk_ids.shape
+    if out is None:
+        shape = (T, layer.out) if flags & TQ_COMBINE else (T, topk, layer.out)
+        out = torch.empty(shape, dtype=torch.float32, device=x.device)
+    layer_c = layer.c_struct()
+    check(_lib.load().trellis_expert_gemm_noalloc(ctypes.byref(layer_c), _ptr(x), T,
+                                                  _ptr(topk_ids), _ptr(topk_w), topk, _ptr(out),
+                                                  flags, _stream(x.device)))
+    return out
+
+
 def mxfp4_expert_gemm(layer, x, topk_ids, topk_w=None, flags=TQ_AUTO, out=None, ws=None):
     return _gemm(_lib.load().mxfp4_expert_gemm, layer.c_struct(), layer.E, layer.out,
                  layer.in_, x, topk_ids, topk_w, flags, out, ws, True)
