@@ -12,9 +12,8 @@ every input already resident in device memory:
       activation prep with the fused rotation, route bucketing (three kernels), grouped
       MFMA GEMM;
   nvfp4: the MXFP4 -> NVFP4 transcode of the 384-unit MXFP4 layer (bytes read + written);
-  ffn: the routed expert FFN (gate, up, SwiGLU, rotated down projection, combine) of 384
-      experts with 768 intermediate channels, 128 tokens, top-8 — three decode-batch
-      pipelines, the SwiGLU kernel and the combine.
+  ffn: the routed expert FFN (fused gate/up, SwiGLU, rotated down projection, combine) of
+      384 experts with 768 intermediate channels, 128 tokens, top-8 — five launches.
 Steps are captured as HIP graphs and replayed; each step reads a different replica of the
 code buffer (replicas total >= 1 GiB) so the 256 MB Infinity Cache cannot serve repeats.
 
@@ -145,7 +144,7 @@ def bench_mixed(torch, ops, args):
     wl = mixed_layer()
     lay = wl["layer"]
     dev = torch.device("cuda", 0)
-    L = ops.TrellisLayer.from_host(lay, dev)
+    L = ops.TrellisLayer.from_host(lay, dev).repacked()  # the kernels' read order, once
     x = torch.from_numpy(wl["x"].view(np.int16)).to(dev)
     ids = torch.from_numpy(wl["topk_ids"]).to(dev)
     T, topk = wl["topk_ids"].shape
@@ -258,20 +257,21 @@ def bench_ffn(torch, ops, args):
     from workloads import ffn_decode
     wl = ffn_decode()
     dev = torch.device("cuda", 0)
-    G, U, D = (ops.TrellisLayer.from_host(wl[k], dev) for k in ("gate", "up", "down"))
+    # both layers repacked once into the kernels' read order
+    GU, D = (ops.TrellisLayer.from_host(wl[k], dev).repacked() for k in ("gate_up", "down"))
     x = torch.from_numpy(wl["x"].view(np.int16)).to(dev)
     ids = torch.from_numpy(wl["topk_ids"]).to(dev)
     gates = torch.from_numpy(wl["topk_w"]).to(dev)
     T, topk = wl["topk_ids"].shape
-    nbytes = sum(active_bytes_trellis(wl[k], wl["topk_ids"])[0] for k in ("gate", "up", "down"))
-    n_active = active_bytes_trellis(wl["gate"], wl["topk_ids"])[1]
-    E, H, I = G.E, G.in_, G.out
+    nbytes = sum(active_bytes_trellis(wl[k], wl["topk_ids"])[0] for k in ("gate_up", "down"))
+    n_active = active_bytes_trellis(wl["gate_up"], wl["topk_ids"])[1]
+    E, H, I = GU.E, GU.in_, GU.out // 2
     y = torch.empty((T, H), dtype=torch.float32, device=dev)
     ws = ops.ffn_workspace(T, topk, E, H, I, ops.TQ_AUTO, dev)
     log("ffn: %d active experts, %.1f MB compressed per step" % (n_active, nbytes / 1e6))
 
     def step():
-        ops.trellis_expert_ffn(G, U, D, x, ids, gates, flags=ops.TQ_ROTATE, out=y, ws=ws)
+        ops.trellis_expert_ffn(GU, D, x, ids, gates, flags=ops.TQ_ROTATE, out=y, ws=ws)
 
     step()
     torch.cuda.synchronize()
@@ -281,7 +281,7 @@ def bench_ffn(torch, ops, args):
     steps = max(20, args.steps // 5)
     sec = time_graph_steps(torch, [g], steps, max(4, args.warmup // 5))
     return {"sec_per_step": sec, "bytes": nbytes, "n_active": n_active, "steps": steps,
-            "code_bytes": int(sum(wl[k]["codes"].nbytes for k in ("gate", "up", "down")))}
+            "code_bytes": int(sum(wl[k]["codes"].nbytes for k in ("gate_up", "down")))}
 
 
 def bench_shared(torch, ops, args):
@@ -345,7 +345,7 @@ def bench_prefill(torch, ops, args):
     wl = prefill_chunk()
     lay = wl["layer"]
     dev = torch.device("cuda", 0)
-    L = ops.TrellisLayer.from_host(lay, dev)
+    L = ops.TrellisLayer.from_host(lay, dev).repacked()  # the kernels' read order, once
     x = torch.from_numpy(wl["x"].view(np.int16)).to(dev)
     ids = torch.from_numpy(wl["topk_ids"]).to(dev)
     T, topk = wl["topk_ids"].shape
@@ -419,7 +419,7 @@ def drive(torch, ops, which, iters):
     if which in ("mixed", "prefill"):
         wl = mixed_layer() if which == "mixed" else prefill_chunk()
         lay = wl["layer"]
-        L = ops.TrellisLayer.from_host(lay, dev)
+        L = ops.TrellisLayer.from_host(lay, dev).repacked()
         x = torch.from_numpy(wl["x"].view(np.int16)).to(dev)
         ids = torch.from_numpy(wl["topk_ids"]).to(dev)
         T, topk = wl["topk_ids"].shape
@@ -433,15 +433,15 @@ def drive(torch, ops, which, iters):
     elif which == "ffn":
         from workloads import ffn_decode
         wl = ffn_decode()
-        G, U, D = (ops.TrellisLayer.from_host(wl[k], dev) for k in ("gate", "up", "down"))
+        GU, D = (ops.TrellisLayer.from_host(wl[k], dev).repacked() for k in ("gate_up", "down"))
         x = torch.from_numpy(wl["x"].view(np.int16)).to(dev)
         ids = torch.from_numpy(wl["topk_ids"]).to(dev)
         gates = torch.from_numpy(wl["topk_w"]).to(dev)
         T, topk = wl["topk_ids"].shape
-        y = torch.empty((T, G.in_), dtype=torch.float32, device=dev)
-        ws = ops.ffn_workspace(T, topk, G.E, G.in_, G.out, ops.TQ_AUTO, dev)
+        y = torch.empty((T, GU.in_), dtype=torch.float32, device=dev)
+        ws = ops.ffn_workspace(T, topk, GU.E, GU.in_, GU.out // 2, ops.TQ_AUTO, dev)
         for i in range(iters):
-            ops.trellis_expert_ffn(G, U, D, x, ids, gates, flags=ops.TQ_ROTATE, out=y, ws=ws)
+            ops.trellis_expert_ffn(GU, D, x, ids, gates, flags=ops.TQ_ROTATE, out=y, ws=ws)
     elif which == "shared":
         from workloads import shared_expert
         for T in (128, 8192):
@@ -587,6 +587,7 @@ def main():
             "operands": "int8 matrix-core products with int32 sums: the weights' signed bytes, "
                         "activations as 16-bit per-token fixed point in two int8 halves",
             "replicas": res["replicas"],
+            "layout": "units repacked once into the kernels' read order (TQ_LAYOUT_GEMV)",
         },
         "roofline": {
             "bound": "hbm",
@@ -619,7 +620,7 @@ def main():
     if "prefill" in todo:
         p = bench_prefill(torch, ops, args)
         extras["prefill_chunk"] = {
-            "workload": "8192 tokens, top-8, 384 K=3 experts, Zipf(1.1)",
+            "workload": "8192 tokens, top-8, 384 K=3 experts, Zipf(1.1), units repacked once",
             "TFLOP/s": round(p["flops"] / p["sec_per_step"] / 1e12, 3),
             "ms_per_step": round(p["sec_per_step"] * 1e3, 5), "steps": p["steps"],
             "kernel": p["kernel"], "kernel_us": round(p["kernel_sec"] * 1e6, 3),
@@ -638,8 +639,10 @@ def main():
     if "ffn" in todo:
         f = bench_ffn(torch, ops, args)
         extras["ffn_decode"] = {
-            "workload": "routed expert FFN, 384 experts (gate/up 768 x 5120, down 5120 x 768, "
-                        "368 K2 / 15 K3 / 1 K4), 128 tokens, top-8, gates",
+            "workload": "routed expert FFN, 384 experts (fused gate/up 1536 x 5120, down 5120 x 768 "
+                        "in 128-channel units, 368 K2 / 15 K3 / 1 K4), 128 tokens, top-8, gates; "
+                        "5 launches (plans + prep, gate/up GEMV, SwiGLU + rotation + down "
+                        "operands, down GEMV, reduction + combine), units repacked once",
             "GB/s": round(f["bytes"] / f["sec_per_step"] / 1e9, 2),
             "ms_per_step": round(f["sec_per_step"] * 1e3, 5), "steps": f["steps"],
             "active_experts": f["n_active"], "compressed_bytes_per_step": f["bytes"],

@@ -71,6 +71,10 @@ extern "C" {
  */
 #define TQ_LAYOUT_STORE 0
 #define TQ_LAYOUT_GEMV 1
+#define TQ_LAYOUT_UNIT128 2 /* trellis only: FORMAT F2b, the exlr8 page's units of 128     */
+                            /* input channels (the down projection's units, "Layout"):    */
+                            /* in/128 units of out x 128, each strip-major over its own   */
+                            /* 8 tile columns, back to back                               */
 
 /*
  * A trellis expert layer (FORMAT F1-F7, F12). Expert e's unit holds out*in*K/8 bytes at
@@ -85,13 +89,16 @@ typedef struct tq_trellis_layer {
   int32_t E;                /* experts in the layer, 1 .. 4096                           */
   int32_t out;              /* output channels per expert, multiple of 16                 */
   int32_t in;               /* inputs per expert, multiple of 256                         */
-  int32_t layout;           /* TQ_LAYOUT_STORE, or TQ_LAYOUT_GEMV after trellis_repack    */
+  int32_t layout;           /* TQ_LAYOUT_STORE, TQ_LAYOUT_UNIT128 or (after              */
+                            /* trellis_repack) TQ_LAYOUT_GEMV                             */
   const uint8_t* bits;      /* device [E]: K of each expert (2, 3 or 4)                   */
   const int64_t* code_off;  /* device [E]: byte offset of each unit in codes, 16-aligned  */
   const uint32_t* codes;    /* device: the units                                          */
   const uint16_t* scales;   /* device [E][out]: fp16 per-output-channel scales            */
   const int8_t* signs;      /* device [in]: +-1 rotation signs for TQ_ROTATE, or NULL     */
   int64_t codes_bytes;      /* bytes of `codes` (> 0): a unit must lie inside them         */
+  const int8_t* out_signs;  /* device [out]: +-1 signs of the output-side rotation, or NULL  */
+                            /* for none (FORMAT F17; out a multiple of 128 when given)     */
 } tq_trellis_layer;
 
 /*
@@ -127,6 +134,10 @@ typedef struct tq_fp8b32_layer {
  * trellis_expert_gemm — routed activations x trellis-coded expert weights.
  *
  *   y[t][k][o] = g[t][k] * f32(scale_e[o]) * sum_i x[t][i] * q_e[i][o],  e = topk_ids[t][k]
+ *
+ * then, when L->out_signs is given, the output-side rotation of every 128 outputs of a slot
+ * (or of a token with TQ_COMBINE), y <- s_out * ((H / sqrt(128)) y) (FORMAT F17;
+ * DeepSeek-V4.1-Flash-1017 · exlr8 page, "Stores": the 128 x 128 Hadamard on both sides).
  *
  * (DeepSeek-V4.1-Flash-1017 · dsx T16 page, "How T16 works" items 1, 2 and 4; FORMAT
  * F5, F6, F10, F11.) q_e is decoded from the codes inside the kernels; it is never
@@ -249,11 +260,11 @@ int trellis_decode(const uint32_t* codes, int32_t K, int32_t out, int32_t in, in
 int mxfp4_decode(const uint8_t* unit, int32_t out, int32_t in, uint16_t* w, void* stream);
 
 /*
- * trellis_repack — copy a trellis layer's units from TQ_LAYOUT_STORE into TQ_LAYOUT_GEMV
- * (see above): once, when a layer is loaded. Every unit with a good descriptor (width 2, 3 or
+ * trellis_repack — copy a trellis layer's units from TQ_LAYOUT_STORE or TQ_LAYOUT_UNIT128
+ * into TQ_LAYOUT_GEMV (see above): once, when a layer is loaded. Every unit with a good descriptor (width 2, 3 or
  * 4, 16-byte aligned, inside codes_bytes) is written at its own offset code_off[e] of dst;
  * other bytes of dst are left as they are.
- *   L      host: the layer, L->layout == TQ_LAYOUT_STORE.
+ *   L      host: the layer, L->layout == TQ_LAYOUT_STORE or TQ_LAYOUT_UNIT128.
  *   dst    device, 16-byte aligned, L->codes_bytes bytes, not overlapping L->codes; use it
  *          as the codes of a layer with layout TQ_LAYOUT_GEMV (same bits, code_off, scales).
  */
@@ -279,34 +290,42 @@ int fp8b32_repack(const tq_fp8b32_layer* L, uint8_t* dst, void* stream);
 int fp8b32_decode(const uint8_t* unit, int32_t out, int32_t in, uint16_t* w, void* stream);
 
 /*
- * trellis_expert_ffn — the routed expert FFN over trellis-coded gate, up and down projections
- * (FORMAT F15; DeepSeek-V4.1-Flash-1017 · exlr8 page, "Layout" and "Stores": every expert
- * projection cut into units of 128 intermediate channels; dsx T16 page, "October 25 runtime
- * checkpoint": fused gate/up post-processing):
+ * trellis_expert_ffn — the routed expert FFN over trellis-coded projections (FORMAT F15;
+ * DeepSeek-V4.1-Flash-1017 · exlr8 page, "Layout" and "Stores": every expert projection cut
+ * into units of 128 intermediate channels, gate and up stored together, trellis units
+ * rotated on both sides; dsx T16 page, "October 25 runtime checkpoint": fused gate/up
+ * post-processing):
  *
- *   g = gate_e(x~), u = up_e(x~)           fp32, as trellis_expert_gemm (per-channel scales)
- *   h = bf16_rne(silu(g) * u),  silu(a) = a / (1 + e^-a)  (fp32)
- *   z = down_e(rot(h))                     rot: the signed 128-wide rotation of hadamard128
- *                                          over the intermediate, with down->signs
+ *   gu = gate_up_e(x~)       fp32, as trellis_expert_gemm (per-channel scales; then the
+ *                            layer's output-side rotation when it has out_signs)
+ *   g = gu[0 .. I-1], u = gu[I .. 2I-1]
+ *   h = silu(g) * u,  silu(a) = a / (1 + e^-a)          fp32, never rounded to bf16
+ *   v = (H / sqrt(128)) (down->signs * h) per 128-block  fp32 (no bf16 rounding), then the
+ *                            mode's operand conversion (FORMAT F10)
+ *   z = down_e(v)            (then down's output-side rotation when it has out_signs)
  *   y[t] = sum over k = 0..topk-1, in order, of g[t][k] * z[t][k]
  *
- *   gate, up  host: trellis layers with out = I (intermediate), in = H (hidden), same E.
- *   down      host: trellis layer with out = H, in = I, same E (its units strip-major over
- *             the whole intermediate, FORMAT F2).
- *   x         device bf16 [T][H]; with TQ_ROTATE the unrotated input (gate->signs rotate
- *             it for both gate and up), else the rotated one.
+ *   gate_up   host: trellis layer with out = 2I (the gate's I channels, then the up's),
+ *             in = H.
+ *   down      host: trellis layer with out = H, in = I, same E; TQ_LAYOUT_UNIT128 stores it
+ *             as the page's units of 128 intermediate channels.
+ *   x         device bf16 [T][H]; with TQ_ROTATE the unrotated input (gate_up->signs rotate
+ *             it), else the rotated one.
  *   topk_ids, topk_w, topk   as trellis_expert_gemm.
  *   y         device fp32 [T][H], 16-byte aligned.
- *   flags     TQ_AUTO / TQ_GEMV / TQ_GEMM (applied to every projection), | TQ_ROTATE.
+ *   flags     TQ_AUTO / TQ_GEMV / TQ_GEMM (both projections), | TQ_ROTATE.
  *   ws        device workspace of tq_ffn_workspace_bytes(T, topk, E, H, I, flags) bytes,
  *             256-byte aligned, zero-filled before its first use (as for trellis_expert_gemm);
  *             the status word of tq_device_status is its first word.
- * H and I are multiples of 256.
+ * H and I are multiples of 256, I at most 4096. The decode-batch mode runs five launches:
+ * both plans with the gate/up activation prep, the gate/up GEMV, the middle step (the
+ * gate/up reduction, SwiGLU, the intermediate's rotation and the down operands, one
+ * workgroup per slot), the down GEMV, the down reduction with the combine.
  */
-int trellis_expert_ffn(const tq_trellis_layer* gate, const tq_trellis_layer* up,
-                       const tq_trellis_layer* down, const void* x, int64_t T,
-                       const int32_t* topk_ids, const float* topk_w, int32_t topk, float* y,
-                       uint32_t flags, void* ws, size_t ws_bytes, void* stream);
+int trellis_expert_ffn(const tq_trellis_layer* gate_up, const tq_trellis_layer* down,
+                       const void* x, int64_t T, const int32_t* topk_ids, const float* topk_w,
+                       int32_t topk, float* y, uint32_t flags, void* ws, size_t ws_bytes,
+                       void* stream);
 
 /* Workspace bytes trellis_expert_ffn needs (0 for invalid sizes). */
 size_t tq_ffn_workspace_bytes(int64_t T, int32_t topk, int32_t E, int32_t H, int32_t I,

@@ -19,15 +19,16 @@ unpinned: the pages print no worked example and no such file is available.
 
 from .t16 import (T16_MULT, t16_value, t16_value_array, tile_bits_scalar,
                   tile_states_scalar, decode_tile_scalar, decode_unit_scalar,
-                  decode_unit, unit_bytes)
+                  decode_unit, unit_bytes, decode_units128)
 from .mxfp4 import (E2M1_VALUES, e2m1_value, e8m0_value, decode_mxfp4_unit,
                     mxfp4_unit_bytes, mxfp4_to_nvfp4, decode_nvfp4,
                     e4m3_value, nvfp4_unit_bytes)
 from .fpbits import (bf16_bits_to_f64, f16_bits_to_f64, f64_to_bf16_bits_exact,
                      f32_to_bf16_bits_rne)
-from .hadamard import sylvester_hadamard, hadamard128_f64, hadamard128_fp32_order
+from .hadamard import (sylvester_hadamard, hadamard128_f64, hadamard128_fp32_order,
+                       rotate128_values, output_rotation128)
 from .routing import route_bucket
-from .gemm import expert_gemm, expert_gemm_exact, combine_slots
+from .gemm import expert_gemm, expert_gemm_values, expert_gemm_exact, combine_slots
 from .ffn import silu, silu_scalar, expert_ffn
 from .fp8b32 import fp8b32_unit_bytes, decode_fp8b32_unit, decode_fp8b32_weight_scalar
 

@@ -24,7 +24,14 @@ def expert_gemm(x_bits, topk_ids, topk_w, E, weight_of, scale_of=None):
     scale_of(e) -> float64 [out] or None (scale 1). topk_w: [T, topk] or None (gate 1).
     Empty slots (-1) give 0; ids outside [-1, E) give NaN.
     """
-    x = bf16_bits_to_f64(x_bits)
+    return expert_gemm_values(bf16_bits_to_f64(x_bits), topk_ids, topk_w, E, weight_of,
+                              scale_of)
+
+
+def expert_gemm_values(x_vals, topk_ids, topk_w, E, weight_of, scale_of=None):
+    """``expert_gemm`` of activations given as FP64 values [T, in] (an intermediate that is
+    not rounded to a storage format, FORMAT F15)."""
+    x = np.asarray(x_vals, dtype=np.float64)
     ids = np.asarray(topk_ids, dtype=np.int64)
     T, topk = ids.shape
     gates = None if topk_w is None else np.asarray(topk_w, dtype=np.float64)

@@ -5,11 +5,15 @@ paragraph: 128-wide Hadamard rotations as incoherence processing); DeepSeek-V4.1
 · exlr8 page, "Stores" (a 128 x 128 Hadamard with per-layer signs shared by all encodes of
 a layer).
 
-Two forms:
+Forms:
 - ``hadamard128_f64``: the exact orthonormal transform H/sqrt(128) applied to s * x in
   FP64, H the Sylvester matrix in natural order (no rounding at all);
 - ``hadamard128_fp32_order``: the rounding FORMAT F8 fixes for the bf16 output — seven
-  fp32 butterfly stages (strides 1..64), times fp32(1/sqrt(128)), rounded to bf16.
+  fp32 butterfly stages (strides 1..64), times fp32(1/sqrt(128)), rounded to bf16;
+- ``rotate128_values``: the exact transform of FP64 values (the rotation of the FFN's
+  intermediate, FORMAT F15, which is not rounded);
+- ``output_rotation128``: the output-side rotation of FORMAT F17, s * (H/sqrt(128)) y, the
+  transpose of the input rotation (exlr8 page, "Stores": Hadamard on both sides).
 """
 
 import numpy as np
@@ -70,3 +74,37 @@ def hadamard128_fp32_order(x_bits, signs=None):
         h *= 2
     v = (v * INV_SQRT128_F32).astype(np.float32)
     return f32_to_bf16_bits_rne(v.reshape(rows, n))
+
+
+def _signs_for(n, signs):
+    if signs is None:
+        return np.ones(n, dtype=np.float64)
+    s = np.asarray(signs, dtype=np.float64).reshape(-1)
+    if s.size != n or np.any((s != 1) & (s != -1)):
+        raise ValueError("signs must be +-1, one per channel")
+    return s
+
+
+def _blocks_times_h(v):
+    rows, n = v.shape
+    if n % BLOCK:
+        raise ValueError("the last axis must be a multiple of 128")
+    h = sylvester_hadamard(BLOCK).astype(np.float64) / np.sqrt(128.0)
+    return np.einsum("ij,rbj->rbi", h, v.reshape(rows, n // BLOCK, BLOCK)).reshape(rows, n)
+
+
+def rotate128_values(v, signs=None):
+    """Input-side rotation of FP64 values, exact: per 128-block, (H / sqrt(128)) (s * v)."""
+    v = np.asarray(v, dtype=np.float64)
+    shape = v.shape
+    v = v.reshape(-1, shape[-1])
+    return _blocks_times_h(v * _signs_for(shape[-1], signs)[None, :]).reshape(shape)
+
+
+def output_rotation128(y, signs=None):
+    """Output-side rotation (FORMAT F17), exact: per 128-block of the last axis,
+    s * ((H / sqrt(128)) y). The transpose of rotate128_values with the same signs."""
+    y = np.asarray(y, dtype=np.float64)
+    shape = y.shape
+    y = y.reshape(-1, shape[-1])
+    return (_blocks_times_h(y) * _signs_for(shape[-1], signs)[None, :]).reshape(shape)

@@ -19,7 +19,7 @@ from multiprocessing import shared_memory
 
 import numpy as np
 
-from . import ffn as _ffn, fpbits as _fpbits, gemm as _gemm, t16 as _t16
+from . import ffn as _ffn, fpbits as _fpbits, gemm as _gemm, hadamard as _had, t16 as _t16
 
 _ARR = {}
 _META = {}
@@ -38,8 +38,8 @@ def _attach(specs, meta):
 
 
 def _layer(prefix):
-    d = {k: _META[prefix + "." + k] for k in ("E", "out", "in")}
-    for k in ("bits", "code_off", "codes", "scales", "signs"):
+    d = {k: _META[prefix + "." + k] for k in ("E", "out", "in", "layout")}
+    for k in ("bits", "code_off", "codes", "scales", "signs", "out_signs"):
         d[k] = _ARR.get(prefix + "." + k)
     return d
 
@@ -53,8 +53,8 @@ def _trellis_fns(lay):
             n = lay["out"] * lay["in"] * K // 32
             s = int(lay["code_off"][e]) // 4
             cache.clear()  # one expert at a time: bounded memory
-            cache[e] = _t16.decode_unit(lay["codes"][s:s + n], K, lay["out"],
-                                          lay["in"]).astype(np.float64)
+            decode = _t16.decode_units128 if lay["layout"] == 2 else _t16.decode_unit
+            cache[e] = decode(lay["codes"][s:s + n], K, lay["out"], lay["in"]).astype(np.float64)
         return cache[e]
 
     scales = _fpbits.f16_bits_to_f64(lay["scales"])
@@ -78,13 +78,13 @@ def _gemm_task(experts):
 
 
 def _ffn_task(experts):
-    g, u, d = _layer("gate"), _layer("up"), _layer("down")
+    gu, d = _layer("gate_up"), _layer("down")
     ids = _ARR["ids"]
     keep = _masked(ids, experts)
     if not np.any(keep >= 0):
         return np.zeros((ids.shape[0], d["out"]))
-    return _ffn.expert_ffn(_ARR["x"], keep, _ARR.get("gates"), g["E"], _trellis_fns(g),
-                             _trellis_fns(u), _trellis_fns(d), d["signs"])
+    return _ffn.expert_ffn(_ARR["x"], keep, _ARR.get("gates"), gu["E"], _trellis_fns(gu),
+                           _trellis_fns(d), d["signs"], gu["out_signs"], d["out_signs"])
 
 
 def default_workers():
@@ -127,8 +127,10 @@ def _expert_chunks(ids, n, E):
 
 
 def _layer_arrays(prefix, lay):
-    arrays = {prefix + "." + k: lay.get(k) for k in ("bits", "code_off", "codes", "scales", "signs")}
+    arrays = {prefix + "." + k: lay.get(k)
+              for k in ("bits", "code_off", "codes", "scales", "signs", "out_signs")}
     meta = {prefix + "." + k: int(lay[k]) for k in ("E", "out", "in")}
+    meta[prefix + ".layout"] = int(lay.get("layout", 0))
     return arrays, meta
 
 
@@ -147,25 +149,27 @@ def trellis_slots(layer, x_bits, ids, gates=None, workers=None):
     y = np.zeros((ids.size, layer["out"]))
     for flat, rows in parts:
         y[flat] = rows
+    if layer.get("out_signs") is not None:  # the output-side rotation (FORMAT F17)
+        y = _had.output_rotation128(y, layer["out_signs"])
     bad = ((ids < -1) | (ids >= layer["E"])).reshape(-1)
     y[bad] = np.nan
     return y.reshape(ids.shape + (layer["out"],))
 
 
-def ffn(gate, up, down, x_rot_bits, ids, gates=None, workers=None):
+def ffn(gate_up, down, x_rot_bits, ids, gates=None, workers=None):
     """oracle.expert_ffn, [T, H], summed over disjoint expert sets computed in parallel."""
     ids = np.asarray(ids)
     arrays, meta = {}, {}
-    for p, lay in (("gate", gate), ("up", up), ("down", down)):
+    for p, lay in (("gate_up", gate_up), ("down", down)):
         a, m = _layer_arrays(p, lay)
         arrays.update(a)
         meta.update(m)
     arrays.update({"x": x_rot_bits, "ids": ids, "gates": gates})
     pool = _Pool(arrays, meta, workers)
     try:
-        parts = pool.map(_ffn_task, _expert_chunks(ids, pool.n, gate["E"]))
+        parts = pool.map(_ffn_task, _expert_chunks(ids, pool.n, gate_up["E"]))
     finally:
         pool.close()
     y = np.sum(parts, axis=0)
-    y[np.any((ids < -1) | (ids >= gate["E"]), axis=1)] = np.nan  # as the oracle: NaN rows
+    y[np.any((ids < -1) | (ids >= gate_up["E"]), axis=1)] = np.nan  # as the oracle: NaN rows
     return y

@@ -140,3 +140,18 @@ def decode_unit(words, K, out, inputs):
     qt = t16_value_array(states).reshape(n_to, n_ti, TILE, TILE)  # [to, ti, o_l, i_l]
     q = qt.transpose(0, 2, 1, 3).reshape(out, inputs)
     return q.astype(np.int16)
+
+
+def decode_units128(words, K, out, inputs):
+    """q [out, inputs] of a projection stored as inputs/128 units of 128 input channels
+    (FORMAT F2b; exlr8 page, "Layout": units of 128 intermediate channels, the inputs of the
+    down projection): unit j is an out x 128 strip-major unit (F2) holding inputs
+    128 j .. 128 j + 127, units back to back."""
+    if inputs % 128:
+        raise ValueError("inputs must be a multiple of 128")
+    w = np.asarray(words, dtype=np.uint32).reshape(-1)
+    per = out * 128 * K // 32
+    if w.size != per * (inputs // 128):
+        raise ValueError("word count does not match the unit shape")
+    return np.concatenate([decode_unit(w[j * per:(j + 1) * per], K, out, 128)
+                           for j in range(inputs // 128)], axis=1)

@@ -55,8 +55,9 @@ def trellis_weight_fns(layer):
             K = int(layer["bits"][e])
             nwords = layer["out"] * layer["in"] * K // 32
             start = int(layer["code_off"][e]) // 4
-            cache[e] = oracle.decode_unit(layer["codes"][start:start + nwords], K,
-                                          layer["out"], layer["in"]).astype(np.float64)
+            decode = oracle.decode_units128 if layer.get("layout", 0) == 2 else oracle.decode_unit
+            cache[e] = decode(layer["codes"][start:start + nwords], K,
+                              layer["out"], layer["in"]).astype(np.float64)
         return cache[e]
 
     scales = oracle.f16_bits_to_f64(layer["scales"])
@@ -82,7 +83,10 @@ def oracle_trellis(layer, x_rot_bits, ids, gates, sample=None):
         keep[sample] = ids.reshape(-1)[sample]
         ids = keep.reshape(ids.shape)
     w, s = trellis_weight_fns(layer)
-    return oracle.expert_gemm(x_rot_bits, ids, gates, layer["E"], w, s)
+    y = oracle.expert_gemm(x_rot_bits, ids, gates, layer["E"], w, s)
+    if layer.get("out_signs") is not None:  # the output-side rotation (FORMAT F17)
+        y = oracle.output_rotation128(y, layer["out_signs"])
+    return y
 
 
 def oracle_mxfp4(layer, x_bits, ids, gates, sample=None):

@@ -43,7 +43,7 @@ def test_version(lib):
 
 
 def _layer(E=4, out=128, inp=5120, fake=0x1000, signs=None, codes_bytes=1 << 30):
-    return _lib.TrellisLayerC(E, out, inp, 0, fake, fake, fake, fake, signs, codes_bytes)
+    return _lib.TrellisLayerC(E, out, inp, 0, fake, fake, fake, fake, signs, codes_bytes, None)
 
 
 def _call_trellis(lib, layer, T=2, topk=2, x=0x1000, ids=0x1000, y=0x1000, flags=0,
@@ -58,10 +58,17 @@ def test_trellis_argument_errors(lib):
     for bad in (_layer(E=0), _layer(out=24), _layer(inp=200), _layer(E=70000)):
         assert _call_trellis(lib, bad) == _lib.TQ_EINVAL
     lay = _layer()
-    lay.layout = 2
+    lay.layout = 3
     assert _call_trellis(lib, lay) == _lib.TQ_EINVAL
     assert _call_trellis(lib, _layer(codes_bytes=0)) == _lib.TQ_EINVAL
     assert b"codes_bytes" in lib.tq_last_error()
+    lay = _layer(out=144)
+    lay.out_signs = 0x1000
+    assert _call_trellis(lib, lay) == _lib.TQ_EINVAL  # output rotation needs out % 128 == 0
+    lay = _layer()
+    lay.layout = _lib.TQ_LAYOUT_UNIT128
+    lay.in_ = 5120 + 64 * 3  # not a multiple of 128 (but of 64)
+    assert _call_trellis(lib, lay) == _lib.TQ_EINVAL
     lay = _layer()
     lay.codes = 0x1008
     assert _call_trellis(lib, lay) == _lib.TQ_EALIGN

@@ -455,3 +455,45 @@ def test_repacked_layout_gives_the_same_bits(flags, out_ch):
     ref = oracle_trellis(layer, xr, ids_h, gates.cpu().numpy())
     pooled, worst = slot_errors(y, ref)
     assert pooled <= TOL and worst <= TOL
+
+
+@pytest.mark.parametrize("flags", [1, 2, 5, 6])
+def test_output_side_rotation(flags):
+    """A layer with out_signs rotates every 128 outputs of a slot (or of a token with
+    TQ_COMBINE) on the output side (FORMAT F17), in both modes, two groups of 128."""
+    E, T, topk, inp = 7, 30, 3, 512
+    layer = small_layer(420, E, 256, inp)
+    layer["out_signs"] = np.where(rng_for(420, 8).integers(0, 2, 256) == 1, 1, -1).astype(np.int8)
+    x = bf16_from_normal(rng_for(420, 1), (T, inp))
+    ids = uniform_routes(rng_for(420, 2), T, E, topk)
+    ids[4, 0] = -1
+    gates = softmax_gates(rng_for(420, 3), T, topk)
+    y = run(layer, x, ids, gates, flags=flags)
+    ref = oracle_trellis(layer, x, ids, gates)
+    if flags & 4:
+        ref = oracle.combine_slots(ref)
+    pooled, worst = slot_errors(y, ref)
+    assert pooled <= TOL and worst <= TOL
+
+
+@pytest.mark.parametrize("flags", [1, 2])
+def test_units128_layout(flags):
+    """A layer stored as the exlr8 page's units of 128 inputs (FORMAT F2b,
+    TQ_LAYOUT_UNIT128) against the oracle's decode of those units; repacked into the read
+    order it gives the same bits."""
+    o = ops()
+    E, T, topk, inp = 6, 20, 2, 768
+    layer = small_layer(421, E, 256, inp)
+    layer["layout"] = o.TQ_LAYOUT_UNIT128
+    x = bf16_from_normal(rng_for(421, 1), (T, inp))
+    ids = uniform_routes(rng_for(421, 2), T, E, topk)
+    y = run(layer, x, ids, flags=flags)
+    ref = oracle_trellis(layer, x, ids, None)
+    pooled, worst = slot_errors(y, ref)
+    assert pooled <= TOL and worst <= TOL
+    L = o.TrellisLayer.from_host(layer)
+    R = L.repacked()
+    a = o.trellis_expert_gemm(L, to_dev(x, np.int16), to_dev(ids), flags=flags)
+    b = o.trellis_expert_gemm(R, to_dev(x, np.int16), to_dev(ids), flags=flags)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)

@@ -36,10 +36,11 @@ def test_pool_slots_equal_one_process():
 
 def test_pool_ffn_equals_one_process():
     widths = np.array([2, 3, 4, 2], np.uint8)
-    gate, up, down = ffn_layers(931, widths, 256, 256)
+    gate_up, down = ffn_layers(931, widths, 256, 256, down_units128=False, out_rotation=True)
     x = bf16_from_normal(rng_for(931, 1), (6, 256))
     ids = uniform_routes(rng_for(931, 2), 6, 4, 2)
     gates = softmax_gates(rng_for(931, 3), 6, 2)
-    got = pool.ffn(gate, up, down, x, ids, gates, workers=2)
-    ref = oracle.expert_ffn(x, ids, gates, 4, _fns(gate), _fns(up), _fns(down), down["signs"])
+    got = pool.ffn(gate_up, down, x, ids, gates, workers=2)
+    ref = oracle.expert_ffn(x, ids, gates, 4, _fns(gate_up), _fns(down), down["signs"],
+                            gate_up["out_signs"], down["out_signs"])
     assert np.allclose(got, ref, rtol=1e-12, atol=1e-12 * np.abs(ref).max())

@@ -19,6 +19,7 @@ TQ_EHIP = -5
 
 TQ_LAYOUT_STORE = 0
 TQ_LAYOUT_GEMV = 1
+TQ_LAYOUT_UNIT128 = 2
 
 TQ_AUTO = 0
 TQ_GEMV = 1
@@ -44,6 +45,7 @@ class TrellisLayerC(ctypes.Structure):
         ("scales", ctypes.c_void_p),
         ("signs", ctypes.c_void_p),
         ("codes_bytes", ctypes.c_int64),
+        ("out_signs", ctypes.c_void_p),
     ]
 
 
@@ -81,8 +83,7 @@ SIGNATURES = {
     "fp8b32_repack": (ctypes.c_int, [ctypes.POINTER(Mxfp4LayerC), _P, _P]),
     "mxfp4_to_nvfp4": (ctypes.c_int, [ctypes.POINTER(Mxfp4LayerC), _P, _P, _P, _P, _P]),
     "trellis_expert_ffn": (ctypes.c_int, [ctypes.POINTER(TrellisLayerC), ctypes.POINTER(TrellisLayerC),
-                                          ctypes.POINTER(TrellisLayerC), _P, _I64, _P, _P, _I32,
-                                          _P, _U32, _P, _SZ, _P]),
+                                          _P, _I64, _P, _P, _I32, _P, _U32, _P, _SZ, _P]),
     "trellis_expert_gemm_noalloc": (ctypes.c_int, [ctypes.POINTER(TrellisLayerC), _P, _I64, _P,
                                                    _P, _I32, _P, _U32, _P]),
     "tq_ffn_workspace_bytes": (_SZ, [_I64, _I32, _I32, _I32, _I32, _U32]),

@@ -223,42 +223,6 @@ size_t tq_workspace_bytes(int64_t T, int32_t topk, int32_t E, int32_t out, int32
   return a.total > b.total ? a.total : b.total;
 }
 
-namespace {
-
-// The FFN workspace: the gate/up calls' workspace, the down call's, then g, u (fp32), h (bf16)
-// and the down projection's per-slot outputs (fp32), each 256-byte aligned.
-struct FfnWs {
-  size_t gu, down, g, u, h, yd, total;
-};
-static FfnWs ffn_ws(int64_t T, int32_t topk, int32_t E, int32_t H, int32_t I, uint32_t flags) {
-  FfnWs w{};
-  const int64_t N = T * topk;
-  const uint32_t mode = flags & 3u;
-  size_t off = 0;
-  w.gu = off;
-  off += round_up(tq_workspace_bytes(T, topk, E, I, H, mode), 256);
-  w.down = off;
-  off += round_up(tq_workspace_bytes(N, 1, E, H, I, mode), 256);
-  w.g = off;
-  off += round_up((size_t)N * I * 4, 256);
-  w.u = off;
-  off += round_up((size_t)N * I * 4, 256);
-  w.h = off;
-  off += round_up((size_t)N * I * 2, 256);
-  w.yd = off;
-  off += round_up((size_t)N * H * 4, 256);
-  w.total = off;
-  return w;
-}
-
-}  // namespace
-
-size_t tq_ffn_workspace_bytes(int64_t T, int32_t topk, int32_t E, int32_t H, int32_t I,
-                              uint32_t flags) {
-  if (T < 0 || topk < 1 || E < 1 || H < 256 || I < 256 || H % 256 || I % 256) return 0;
-  return ffn_ws(T, topk, E, H, I, flags).total;
-}
-
 const char* tq_last_error(void) { return g_error.c_str(); }
 
 int tq_time_kernel(void* start, void* stop) {
@@ -344,54 +308,6 @@ int fp8b32_decode(const uint8_t* unit, int32_t out, int32_t in, uint16_t* w, voi
   return ok();
 }
 
-int trellis_expert_ffn(const tq_trellis_layer* gate, const tq_trellis_layer* up,
-                       const tq_trellis_layer* down, const void* x, int64_t T,
-                       const int32_t* topk_ids, const float* topk_w, int32_t topk, float* y,
-                       uint32_t flags, void* ws, size_t ws_bytes, void* stream) {
-  if (!gate || !up || !down) return fail(TQ_EINVAL, "a layer is NULL");
-  if ((flags & ~(3u | TQ_ROTATE)) != 0 || (flags & 3u) == 3u)
-    return fail(TQ_EINVAL, "flags = 0x%x is not valid for the FFN", flags);
-  const int E = gate->E, I = gate->out, H = gate->in;
-  if (up->E != E || down->E != E) return fail(TQ_EINVAL, "the three layers must have the same E");
-  if (up->out != I || up->in != H) return fail(TQ_EINVAL, "up must have the shape of gate");
-  if (down->out != H || down->in != I)
-    return fail(TQ_EINVAL, "down must be in = gate.out (%d), out = gate.in (%d)", I, H);
-  if (H % 256 || I % 256) return fail(TQ_EINVAL, "H and I must be multiples of 256");
-  int rc = check_routes(T, topk, topk_ids);
-  if (rc) return rc;
-  rc = check_io(T, x, y);
-  if (rc) return rc;
-  if (T == 0) return ok();
-  const FfnWs W = ffn_ws(T, topk, E, H, I, flags);
-  rc = check_ws(ws, ws_bytes, W.total);
-  if (rc) return rc;
-  const int64_t N = T * topk;
-  uint8_t* base = static_cast<uint8_t*>(ws);
-  float* g = reinterpret_cast<float*>(base + W.g);
-  float* u = reinterpret_cast<float*>(base + W.u);
-  uint16_t* h = reinterpret_cast<uint16_t*>(base + W.h);
-  float* yd = reinterpret_cast<float*>(base + W.yd);
-  const uint32_t mode = flags & 3u;
-  // gate and up projections of every routed slot (the same workspace, calls in order)
-  rc = trellis_expert_gemm(gate, x, T, topk_ids, nullptr, topk, g, mode | (flags & TQ_ROTATE),
-                           base + W.gu, W.down - W.gu, stream);
-  if (rc) return rc;
-  rc = trellis_expert_gemm(up, x, T, topk_ids, nullptr, topk, u, mode | (flags & TQ_ROTATE),
-                           base + W.gu, W.down - W.gu, stream);
-  if (rc) return rc;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t err = tq::launch_swiglu(g, u, h, N * I, s);
-  if (err != hipSuccess) return hip_fail(err, "swiglu launch");
-  // down projection: each slot is a row of its own (routes and gates read as [T*topk][1]),
-  // with the 128-wide rotation of the intermediate
-  rc = trellis_expert_gemm(down, h, N, topk_ids, topk_w, 1, yd, mode | TQ_ROTATE,
-                           base + W.down, W.g - W.down, stream);
-  if (rc) return rc;
-  err = tq::launch_combine(yd, y, T, topk, H, s);
-  if (err != hipSuccess) return hip_fail(err, "combine launch");
-  return ok();
-}
-
 int mxfp4_to_nvfp4(const tq_mxfp4_layer* L, uint8_t* codes, uint8_t* scales, float* scale2,
                    uint8_t* status, void* stream) {
   if (!L) return fail(TQ_EINVAL, "layer is NULL");
@@ -463,8 +379,11 @@ static int check_trellis_layer(const tq_trellis_layer* L) {
   if (L->E < 1 || L->E > 4096) return fail(TQ_EINVAL, "E = %d is outside 1..4096", L->E);
   if (L->out <= 0 || L->out % 16) return fail(TQ_EINVAL, "out = %d is not a positive multiple of 16", L->out);
   if (L->in <= 0 || L->in % 256) return fail(TQ_EINVAL, "in = %d is not a positive multiple of 256", L->in);
-  if (L->layout != TQ_LAYOUT_STORE && L->layout != TQ_LAYOUT_GEMV)
-    return fail(TQ_EINVAL, "layout = %d is not TQ_LAYOUT_STORE or TQ_LAYOUT_GEMV", L->layout);
+  if (L->layout != TQ_LAYOUT_STORE && L->layout != TQ_LAYOUT_GEMV && L->layout != TQ_LAYOUT_UNIT128)
+    return fail(TQ_EINVAL, "layout = %d is not TQ_LAYOUT_STORE, TQ_LAYOUT_GEMV or TQ_LAYOUT_UNIT128",
+                L->layout);
+  if (L->layout == TQ_LAYOUT_UNIT128 && L->in % 128)
+    return fail(TQ_EINVAL, "TQ_LAYOUT_UNIT128 needs in to be a multiple of 128 (in = %d)", L->in);
   if (!L->bits || !L->code_off || !L->codes || !L->scales)
     return fail(TQ_EINVAL, "a layer pointer is NULL");
   if (!aligned(L->codes, 16)) return fail(TQ_EALIGN, "codes must be 16-byte aligned");
@@ -472,6 +391,11 @@ static int check_trellis_layer(const tq_trellis_layer* L) {
   if (!aligned(L->scales, 2)) return fail(TQ_EALIGN, "scales must be 2-byte aligned");
   if (L->codes_bytes <= 0) return fail(TQ_EINVAL, "codes_bytes = %lld is not positive",
                                        (long long)L->codes_bytes);
+  if (L->out_signs && L->out % 128)
+    return fail(TQ_EINVAL, "an output-side rotation needs out to be a multiple of 128 (out = %d)",
+                L->out);
+  if (L->out_signs && !aligned(L->out_signs, 4))
+    return fail(TQ_EALIGN, "out_signs must be 4-byte aligned");
   return TQ_OK;
 }
 
@@ -532,6 +456,14 @@ static int common_checks(int E, int out, int in, const void* x, int64_t T, const
     return fail(TQ_EINVAL, "out * in is too large for the decode-batch path");
   if (T == 0) return TQ_OK;
   return check_ws(ws, ws_bytes, layout->total);
+}
+
+// The output-side rotation of a layer that has one (FORMAT F17), on `rows` rows of y.
+static int rotate_outputs(const tq_trellis_layer* L, float* y, int64_t rows, hipStream_t s) {
+  if (!L->out_signs) return ok();
+  hipError_t err = tq::launch_rotate_out(y, rows, L->out, L->out_signs, s);
+  if (err != hipSuccess) return hip_fail(err, "output rotation launch");
+  return ok();
 }
 
 static int run_route(const tq::WsLayout& L, void* ws, const int32_t* ids, int64_t N, int E, int out,
@@ -647,11 +579,12 @@ int trellis_expert_gemm(const tq_trellis_layer* L, const void* x, int64_t T,
     r.out = L->out;
     r.topk = topk;
     r.combine = (flags & TQ_COMBINE) ? 1 : 0;
+    r.xdiv = topk;
     r.qmax = L->in / 256;
     r.pre = tq::reduce_prefetch(N, L->E, W.groups, G, r.qmax);
     err = tq::launch_piece_reduce(r, s);
     if (err != hipSuccess) return hip_fail(err, "GEMV piece reduction launch");
-    return ok();
+    return rotate_outputs(L, y, (flags & TQ_COMBINE) ? T : N, s);
   } else {
     err = tq::launch_activation_prep(xb, T, L->in, at<uint32_t>(ws, W.xprep),
                                      at<float2>(ws, W.rowsum), (flags & TQ_ROTATE) != 0,
@@ -691,7 +624,7 @@ int trellis_expert_gemm(const tq_trellis_layer* L, const void* x, int64_t T,
     err = tq::launch_combine(y_slots, y, T, topk, L->out, s);
     if (err != hipSuccess) return hip_fail(err, "combine launch");
   }
-  return ok();
+  return rotate_outputs(L, y, (flags & TQ_COMBINE) ? T : N, s);
 }
 
 }  // extern "C"
@@ -780,6 +713,7 @@ int mx_expert_gemm(const MxLayer* L, const void* x, int64_t T, const int32_t* to
     r.out = L->out;
     r.topk = topk;
     r.combine = (flags & TQ_COMBINE) ? 1 : 0;
+    r.xdiv = topk;
     r.qmax = L->in / 512;
     r.pre = tq::reduce_prefetch(N, L->E, W.groups, G, r.qmax);
     err = tq::launch_piece_reduce(r, s);
@@ -853,8 +787,9 @@ static int mx_repack(int fmt, int E, int out, int in, int layout, const uint8_t*
 int trellis_repack(const tq_trellis_layer* L, uint32_t* dst, void* stream) {
   int rc = check_trellis_layer(L);
   if (rc) return rc;
-  if (L->layout != TQ_LAYOUT_STORE)
-    return fail(TQ_EINVAL, "the layer to repack must be in TQ_LAYOUT_STORE (layout = %d)", L->layout);
+  if (L->layout != TQ_LAYOUT_STORE && L->layout != TQ_LAYOUT_UNIT128)
+    return fail(TQ_EINVAL, "the layer to repack must be in TQ_LAYOUT_STORE or TQ_LAYOUT_UNIT128 "
+                "(layout = %d)", L->layout);
   if (!dst) return fail(TQ_EINVAL, "dst is NULL");
   if (!aligned(dst, 16)) return fail(TQ_EALIGN, "dst must be 16-byte aligned");
   const char* a = reinterpret_cast<const char*>(L->codes);
@@ -866,7 +801,8 @@ int trellis_repack(const tq_trellis_layer* L, uint32_t* dst, void* stream) {
   rc = check_device();
   if (rc) return rc;
   hipError_t err = tq::launch_trellis_repack(L->bits, L->code_off, L->codes, L->codes_bytes, L->E,
-                                             L->out, L->in, dst, static_cast<hipStream_t>(stream));
+                                             L->out, L->in, L->layout, dst,
+                                             static_cast<hipStream_t>(stream));
   if (err != hipSuccess) return hip_fail(err, "trellis_repack launch");
   return ok();
 }
@@ -890,6 +826,285 @@ int fp8b32_expert_gemm(const tq_fp8b32_layer* L, const void* x, int64_t T,
   if (rc) return rc;
   const MxLayer m{tq::MX_FP8B32, L->E, L->out, L->in, L->layout, L->units};
   return mx_expert_gemm(&m, x, T, topk_ids, topk_w, topk, y, flags, ws, ws_bytes, stream);
+}
+
+}  // extern "C"
+
+// ---- the routed expert FFN -------------------------------------------------------------
+
+namespace {
+
+// The FFN workspace: the gate/up call's region (its status word first), the down
+// projection's region, then (prefill) the gate/up fp32 rows and the down slots' rows.
+struct FfnWs {
+  tq::WsLayout gu, dn;
+  size_t gu_off, dn_off, rows_off, slots_off, total;
+  bool gemm;
+};
+
+FfnWs ffn_ws(int64_t T, int32_t topk, int32_t E, int32_t H, int32_t I, uint32_t flags) {
+  FfnWs w{};
+  const int64_t N = T * topk;
+  w.gemm = use_gemm(T, topk, E, (2 * I + 127) / 128, flags);
+  // the decode batch needs both projections' (group, chunk) pairs within the GEMV's bound
+  if ((flags & 3u) == TQ_AUTO &&
+      (tq::gemv_chunk_bound(N, E, (2 * I + 127) / 128, false) > tq::GEMV_MAX_G ||
+       tq::gemv_chunk_bound(N, E, (H + 127) / 128, false) > tq::GEMV_MAX_G))
+    w.gemm = true;
+  const uint32_t mode = w.gemm ? TQ_GEMM : TQ_GEMV;
+  w.gu = tq::ws_layout(T, topk, E, 2 * I, H, mode, false);
+  w.dn = tq::ws_layout(N, 1, E, H, I, mode, false);
+  w.gu_off = 0;
+  w.dn_off = round_up(w.gu.total, 256);
+  size_t off = w.dn_off + round_up(w.dn.total, 256);
+  if (w.gemm) {
+    w.rows_off = off;
+    off += round_up((size_t)N * 2 * I * 4, 256);
+    w.slots_off = off;
+    off += round_up((size_t)N * H * 4, 256);
+  }
+  w.total = off;
+  return w;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t tq_ffn_workspace_bytes(int64_t T, int32_t topk, int32_t E, int32_t H, int32_t I,
+                              uint32_t flags) {
+  if (T < 0 || topk < 1 || E < 1 || H < 256 || I < 256 || H % 256 || I % 256) return 0;
+  return ffn_ws(T, topk, E, H, I, flags).total;
+}
+
+int trellis_expert_ffn(const tq_trellis_layer* gate_up, const tq_trellis_layer* down,
+                       const void* x, int64_t T, const int32_t* topk_ids, const float* topk_w,
+                       int32_t topk, float* y, uint32_t flags, void* ws, size_t ws_bytes,
+                       void* stream) {
+  int rc = check_trellis_layer(gate_up);
+  if (rc) return rc;
+  rc = check_trellis_layer(down);
+  if (rc) return rc;
+  if ((flags & ~(3u | TQ_ROTATE)) != 0 || (flags & 3u) == 3u)
+    return fail(TQ_EINVAL, "flags = 0x%x is not valid for the FFN", flags);
+  const int E = gate_up->E, H = gate_up->in, I = gate_up->out / 2;
+  if (gate_up->out % 2) return fail(TQ_EINVAL, "gate_up must have an even number of outputs");
+  if (down->E != E) return fail(TQ_EINVAL, "the two layers must have the same E");
+  if (down->out != H || down->in != I)
+    return fail(TQ_EINVAL, "down must be in = gate_up.out / 2 (%d), out = gate_up.in (%d)", I, H);
+  if (H % 256 || I % 256) return fail(TQ_EINVAL, "H and I must be multiples of 256");
+  if (I > 4096) return fail(TQ_EINVAL, "I = %d is above 4096", I);
+  if ((flags & TQ_ROTATE) && gate_up->signs && !aligned(gate_up->signs, 16))
+    return fail(TQ_EALIGN, "signs must be 16-byte aligned");
+  if (down->signs && !aligned(down->signs, 4)) return fail(TQ_EALIGN, "down signs must be 4-byte aligned");
+  rc = check_routes(T, topk, topk_ids);
+  if (rc) return rc;
+  rc = check_io(T, x, y);
+  if (rc) return rc;
+  const int64_t N = T * topk;
+  const FfnWs W = ffn_ws(T, topk, E, H, I, flags);
+  const uint32_t mode = W.gemm ? TQ_GEMM : TQ_GEMV;
+  // the gate/up and down calls' own limits
+  tq::WsLayout tmp;
+  rc = common_checks(E, 2 * I, H, x, T, topk_ids, topk, y, mode, nullptr, 0, 0, &tmp);
+  if (rc && rc != TQ_EWORKSPACE) return rc;
+  rc = common_checks(E, H, I, x, N, topk_ids, 1, y, mode, nullptr, 0, 0, &tmp);
+  if (rc && rc != TQ_EWORKSPACE) return rc;
+  if (T == 0) return ok();
+  rc = check_ws(ws, ws_bytes, W.total);
+  if (rc) return rc;
+  rc = check_device();
+  if (rc) return rc;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  uint8_t* base = static_cast<uint8_t*>(ws);
+  void* wg = base + W.gu_off;
+  void* wd = base + W.dn_off;
+  uint32_t* status = at<uint32_t>(wg, W.gu.status);
+  hipError_t err;
+  if (!W.gemm) {
+    // 1. both plans and the gate/up activation prep
+    const int G = tq::trellis_gemv_grid();
+    if (G <= 0) return fail(TQ_EHIP, "could not size the GEMV grid");
+    const int Glg = (int)std::max<int64_t>(G, tq::gemv_chunk_bound(N, E, W.gu.groups, false));
+    const int Gld = (int)std::max<int64_t>(G, tq::gemv_chunk_bound(N, E, W.dn.groups, false));
+    tq::PlanArgs pg{}, pd{};
+    pg.ids = topk_ids;
+    pg.N = (int)N;
+    pg.E = E;
+    pg.topk = topk;
+    pg.bits = gate_up->bits;
+    pg.code_off = gate_up->code_off;
+    pg.codes_bytes = gate_up->codes_bytes;
+    pg.unit_bytes = (int64_t)2 * I * H / 8;
+    pg.groups = W.gu.groups;
+    pg.S = H / 64;
+    pg.R = tq::gemv_rows(false);
+    pg.G = G;
+    pg.Gl = Glg;
+    pg.info = at<int32_t>(wg, W.gu.info);
+    pg.rec = at<tq::PlanRec>(wg, W.gu.rec);
+    pg.desc = at<int4>(wg, W.gu.desc);
+    pg.list = at<int32_t>(wg, W.gu.list);
+    pg.slot_info = at<int4>(wg, W.gu.slot_info);
+    pg.rank = at<int32_t>(wg, W.gu.prank);
+    pg.status = status;
+    pg.x = static_cast<const uint16_t*>(x);
+    pg.rotate = (flags & TQ_ROTATE) != 0;
+    pg.signs = gate_up->signs;
+    pg.T = (int)T;
+    pg.in = H;
+    pg.xq = at<uint32_t>(wg, W.gu.xq);
+    pg.xscale = at<float>(wg, W.gu.xscale);
+    pg.xsum = at<int32_t>(wg, W.gu.xsum);
+    pd = pg;
+    pd.N = (int)N;
+    pd.topk = 1;
+    pd.bits = down->bits;
+    pd.code_off = down->code_off;
+    pd.codes_bytes = down->codes_bytes;
+    pd.unit_bytes = (int64_t)H * I / 8;
+    pd.groups = W.dn.groups;
+    pd.S = I / 64;
+    pd.Gl = Gld;
+    pd.info = at<int32_t>(wd, W.dn.info);
+    pd.rec = at<tq::PlanRec>(wd, W.dn.rec);
+    pd.desc = at<int4>(wd, W.dn.desc);
+    pd.list = at<int32_t>(wd, W.dn.list);
+    pd.slot_info = at<int4>(wd, W.dn.slot_info);
+    pd.rank = at<int32_t>(wd, W.dn.prank);
+    pd.x = nullptr;
+    err = tq::launch_ffn_plan(pg, pd, s);
+    if (err != hipSuccess) return hip_fail(err, "FFN plan launch");
+    // 2. the gate/up GEMV
+    tq::TrellisGemvArgs a{};
+    a.layout = gate_up->layout;
+    a.codes = gate_up->codes;
+    a.xq = pg.xq;
+    a.rec = pg.rec;
+    a.desc = pg.desc;
+    a.list = pg.list;
+    a.partial = at<int64_t>(wg, W.gu.partial);
+    a.x_bytes = (uint32_t)(T * H * 4);
+    a.N = (int)N;
+    a.out = 2 * I;
+    a.in = H;
+    a.topk = topk;
+    a.G = Glg;
+    err = tq::launch_trellis_gemv(a, s);
+    if (err != hipSuccess) return hip_fail(err, "gate/up GEMV launch");
+    // 3. SwiGLU, the intermediate's rotation, the down projection's operands
+    tq::FfnMidArgs m{};
+    m.gu.slot_info = pg.slot_info;
+    m.gu.partial = a.partial;
+    m.gu.exact = 1;
+    m.gu.scales = gate_up->scales;
+    m.gu.gates = nullptr;
+    m.gu.xsum = pg.xsum;
+    m.gu.xscale = pg.xscale;
+    m.gu.N = (int)N;
+    m.gu.out = 2 * I;
+    m.gu.topk = topk;
+    m.gu.xdiv = topk;
+    m.gu.qmax = H / 256;
+    m.gu.pre = tq::reduce_prefetch(N, E, W.gu.groups, G, m.gu.qmax);
+    m.gu_out_signs = gate_up->out_signs;
+    m.down_signs = down->signs;
+    m.N = (int)N;
+    m.I = I;
+    m.xq = at<uint32_t>(wd, W.dn.xq);
+    m.xscale = at<float>(wd, W.dn.xscale);
+    m.xsum = at<int32_t>(wd, W.dn.xsum);
+    err = tq::launch_ffn_mid(m, true, s);
+    if (err != hipSuccess) return hip_fail(err, "FFN middle step launch");
+    // 4. the down GEMV, every slot a row of its own
+    tq::TrellisGemvArgs b = a;
+    b.layout = down->layout;
+    b.codes = down->codes;
+    b.xq = m.xq;
+    b.rec = pd.rec;
+    b.desc = pd.desc;
+    b.list = pd.list;
+    b.partial = at<int64_t>(wd, W.dn.partial);
+    b.x_bytes = (uint32_t)(N * I * 4);
+    b.out = H;
+    b.in = I;
+    b.topk = 1;
+    b.G = Gld;
+    err = time_begin(s);
+    if (err != hipSuccess) return hip_fail(err, "hipEventRecord");
+    err = tq::launch_trellis_gemv(b, s);
+    if (err == hipSuccess) err = time_end(s);
+    if (err != hipSuccess) return hip_fail(err, "down GEMV launch");
+    // 5. the down reduction with the gates and the combine over k
+    tq::PieceReduceArgs r{};
+    r.slot_info = pd.slot_info;
+    r.partial = b.partial;
+    r.exact = 1;
+    r.scales = down->scales;
+    r.gates = topk_w;
+    r.xsum = m.xsum;
+    r.xscale = m.xscale;
+    r.y = y;
+    r.N = (int)N;
+    r.out = H;
+    r.topk = topk;
+    r.combine = 1;
+    r.xdiv = 1;
+    r.qmax = I / 256;
+    r.pre = tq::reduce_prefetch(N, E, W.dn.groups, G, r.qmax);
+    err = tq::launch_piece_reduce(r, s);
+    if (err != hipSuccess) return hip_fail(err, "down reduction launch");
+    return rotate_outputs(down, y, T, s);
+  }
+  // prefill: the gate/up GEMM (its output-side rotation included), the middle step, route
+  // bucketing of the slots as rows, the down GEMM, the combine
+  float* gu_rows = reinterpret_cast<float*>(base + W.rows_off);
+  float* y_slots = reinterpret_cast<float*>(base + W.slots_off);
+  rc = trellis_expert_gemm(gate_up, x, T, topk_ids, nullptr, topk, gu_rows,
+                           TQ_GEMM | (flags & TQ_ROTATE), wg, W.gu.total, stream);
+  if (rc) return rc;
+  tq::FfnMidArgs m{};
+  m.gu_rows = gu_rows;
+  m.gu_out_signs = nullptr;  // applied by the gate/up call
+  m.down_signs = down->signs;
+  m.N = (int)N;
+  m.I = I;
+  m.xp = at<uint32_t>(wd, W.dn.xprep);
+  m.rowsum = at<float2>(wd, W.dn.rowsum);
+  err = tq::launch_ffn_mid(m, false, s);
+  if (err != hipSuccess) return hip_fail(err, "FFN middle step launch");
+  rc = run_route(W.dn, wd, topk_ids, N, E, H, y_slots, s);
+  if (rc) return rc;
+  tq::TrellisGemmArgs a{};
+  a.layout = down->layout;
+  a.bits = down->bits;
+  a.code_off = down->code_off;
+  a.codes = down->codes;
+  a.codes_bytes = down->codes_bytes;
+  a.scales = down->scales;
+  a.xp = m.xp;
+  a.rowsum = m.rowsum;
+  a.x_bytes = (uint32_t)(N * I * 2);
+  a.gates = topk_w;
+  a.pairs = at<int32_t>(wd, W.dn.pairs);
+  a.items = at<int32_t>(wd, W.dn.items);
+  a.n_items = at<int32_t>(wd, W.dn.n_items);
+  a.y = y_slots;
+  a.status = status;
+  a.E = E;
+  a.out = H;
+  a.in = I;
+  a.topk = 1;
+  a.groups = W.dn.groups;
+  a.max_items = W.dn.max_items;
+  err = time_begin(s);
+  if (err != hipSuccess) return hip_fail(err, "hipEventRecord");
+  err = tq::launch_trellis_gemm(a, s);
+  if (err == hipSuccess) err = time_end(s);
+  if (err != hipSuccess) return hip_fail(err, "down GEMM launch");
+  err = tq::launch_combine(y_slots, y, T, topk, H, s);
+  if (err != hipSuccess) return hip_fail(err, "combine launch");
+  return rotate_outputs(down, y, T, s);
 }
 
 }  // extern "C"

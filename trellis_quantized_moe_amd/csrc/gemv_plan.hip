@@ -538,6 +538,17 @@ __global__ __launch_bounds__(PLAN_THREADS) void gemv_plan_kernel(PlanArgs a) {
     prep_block(a, blockIdx.x - 1);
 }
 
+// The routed FFN: block 0 plans the gate/up projection, block 1 the down projection (every
+// slot a row of its own), the others prepare the tokens' gate/up operands.
+__global__ __launch_bounds__(PLAN_THREADS) void ffn_plan_kernel(PlanArgs gu, PlanArgs dn) {
+  if (blockIdx.x == 0)
+    plan_block<true>(gu);
+  else if (blockIdx.x == 1)
+    plan_block<true>(dn);
+  else
+    prep_block(gu, blockIdx.x - 2);
+}
+
 // Prefill-GEMM operands, one token per block: thread c converts tile column c (columns
 // c + blockDim, ... when in > 16 * blockDim), rotating it first when asked (bf16 rounding
 // as hadamard128 does it), into f16 pairs [lo: x[r + 8], hi: x[r]]. Each token is first
@@ -648,6 +659,12 @@ hipError_t launch_gemv_plan(const PlanArgs& a, hipStream_t s) {
     hipLaunchKernelGGL(gemv_plan_kernel<true>, dim3(blocks), dim3(PLAN_THREADS), 0, s, a);
   else
     hipLaunchKernelGGL(gemv_plan_kernel<false>, dim3(blocks), dim3(PLAN_THREADS), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_ffn_plan(const PlanArgs& gate_up, const PlanArgs& down, hipStream_t s) {
+  const unsigned blocks = 2 + (gate_up.x ? (unsigned)gate_up.T : 0u);
+  hipLaunchKernelGGL(ffn_plan_kernel, dim3(blocks), dim3(PLAN_THREADS), 0, s, gate_up, down);
   return hipGetLastError();
 }
 

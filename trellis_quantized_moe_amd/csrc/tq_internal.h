@@ -77,7 +77,7 @@ hipError_t launch_activation_prep(const uint16_t* x, int64_t T, int in, uint32_t
                                   hipStream_t s);
 
 struct TrellisGemvArgs {
-  int layout;           // 0: units in store order (FORMAT F2); 1: read order (trellis_repack)
+  int layout;           // 0: store order (F2); 1: read order (trellis_repack); 2: F2b units
   const uint32_t* codes;
   const uint32_t* xq;   // int8 halves [T][2][in/16][8] (the plan's prep)
   const PlanRec* rec;
@@ -101,6 +101,8 @@ struct PieceReduceArgs {
   const float* xscale;  // [T]: then multiplied, or null
   float* y;
   int N, out, topk, combine;
+  int xdiv;  // a slot's activation row (xsum, xscale) is slot / xdiv: topk, or 1 when every
+             // slot is a row of its own (the FFN's down projection)
   int qmax;  // pieces the partial buffer holds per slot
   int pre;   // pieces loaded before the slot's record arrives, 1 .. min(8, qmax)
 };
@@ -108,7 +110,7 @@ constexpr int PIECE_MAX_TOPK = 64;  // largest topk (checked by the C ABI)
 hipError_t launch_piece_reduce(const PieceReduceArgs& a, hipStream_t s);
 
 struct TrellisGemmArgs {
-  int layout;           // 0: units in store order (FORMAT F2); 1: read order (trellis_repack)
+  int layout;           // 0: store order (F2); 1: read order (trellis_repack); 2: F2b units
   const uint8_t* bits;
   const int64_t* code_off;
   const uint32_t* codes;
@@ -187,12 +189,15 @@ hipError_t launch_combine(const float* slots, float* y, int64_t T, int topk, int
 
 hipError_t launch_hadamard(const uint16_t* x, uint16_t* y, int64_t rows, int64_t n,
                            const int8_t* signs, hipStream_t s);
+// Output-side rotation (FORMAT F17) of fp32 rows [rows][out], in place; out % 128 == 0.
+hipError_t launch_rotate_out(float* y, int64_t rows, int out, const int8_t* signs,
+                             hipStream_t s);
 
 // Copies every good unit of a trellis layer (width 2..4, inside codes_bytes, 16-byte
 // aligned) from store order into the read order, at the same offset of dst.
 hipError_t launch_trellis_repack(const uint8_t* bits, const int64_t* code_off,
                                  const uint32_t* codes, int64_t codes_bytes, int E, int out,
-                                 int in, uint32_t* dst, hipStream_t s);
+                                 int in, int from, uint32_t* dst, hipStream_t s);
 hipError_t launch_trellis_decode(const uint32_t* codes, int K, int out, int in, int16_t* q,
                                  int path, hipStream_t s);
 hipError_t launch_mxfp4_decode(const uint8_t* unit, int out, int in, uint16_t* w,
@@ -202,8 +207,24 @@ hipError_t launch_mx_repack(int fmt, const uint8_t* src, uint8_t* dst, int E, in
                             hipStream_t s);
 hipError_t launch_fp8b32_decode(const uint8_t* unit, int out, int in, uint16_t* w,
                                 hipStream_t s);
-hipError_t launch_swiglu(const float* g, const float* u, uint16_t* h, int64_t n,
-                         hipStream_t s);
+// The routed FFN's middle step (ffn.hip): per slot, h = silu(g) * u from the fused gate/up
+// outputs, rotated with the down layer's signs, converted to the down projection's operands.
+struct FfnMidArgs {
+  PieceReduceArgs gu;          // decode: the gate/up GEMV's pieces (xdiv = topk, no gates)
+  const float* gu_rows;        // prefill: the gate/up GEMM's fp32 rows [N][2I]
+  const int8_t* gu_out_signs;  // the gate/up output-side rotation still to apply, or null
+  const int8_t* down_signs;    // the down projection's input signs, or null (all +1)
+  int N, I;
+  uint32_t* xq;                // decode: int8 halves [N][2][I/16][8]
+  float* xscale;               // [N]: 2^-e
+  int32_t* xsum;               // [N]: sum of the row's 16-bit integers
+  uint32_t* xp;                // prefill: f16 pairs [N][I/16][8]
+  float2* rowsum;              // [N]: {sum of the row's f16 values, 2^-e}
+};
+hipError_t launch_ffn_mid(const FfnMidArgs& a, bool decode, hipStream_t s);
+// The FFN's two decode-batch plans (gate/up over T tokens, down over the T * topk slots as
+// rows) and the gate/up activation prep, in one launch.
+hipError_t launch_ffn_plan(const PlanArgs& gate_up, const PlanArgs& down, hipStream_t s);
 hipError_t launch_nvfp4_transcode(const uint8_t* units, int E, int out, int in,
                                   uint8_t* codes, uint8_t* scales, float* scale2,
                                   uint8_t* status, hipStream_t s);

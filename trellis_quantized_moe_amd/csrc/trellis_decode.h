@@ -25,15 +25,21 @@ constexpr uint32_t T16_MULT2 = 0x3A2F3A2Fu;
 
 // ---- unit layouts ---------------------------------------------------------------------------
 // A unit is out / 16 strips of in / 16 tiles; the kernels read it in runs: the 4 tiles of
-// one strip that one 64-input step covers (tile columns 4 st .. 4 st + 3, 128 K bytes). In
-// the store order (FORMAT F2, TQ_LAYOUT_STORE) a strip's runs follow each other; in the
-// read order (TQ_LAYOUT_GEMV, written once by trellis_repack) the runs of one group of
-// 8 strips (128 output channels) are step-major, so the runs a step of a group needs are
-// contiguous, and so are a group's steps. Word offset of run (strip t, step st) within the
-// unit, S = in / 64 steps, n_strips = out / 16, TW = 8 K words per tile:
+// one strip that one 64-input step covers (tile columns 4 st .. 4 st + 3, 128 K bytes).
+//   layout 0 (FORMAT F2, TQ_LAYOUT_STORE): a strip's runs follow each other;
+//   layout 1 (TQ_LAYOUT_GEMV, written once by trellis_repack): the runs of one group of 8
+//            strips (128 output channels) are step-major, so the runs a step of a group
+//            needs are contiguous, and so are a group's steps;
+//   layout 2 (FORMAT F2b, TQ_LAYOUT_UNIT128): units of 128 inputs (2 steps), each
+//            strip-major over its own 8 tile columns.
+// Word offset of run (strip t, step st) within the unit, S = in / 64 steps, n_strips =
+// out / 16, TW = 8 K words per tile. For every layout, the offset between two strips does
+// not depend on the step.
 __device__ __forceinline__ uint32_t run_word(int layout, int t, int st, int S, int n_strips,
                                              int TW) {
   if (layout == 0) return (uint32_t)((t * S + st) * 4 * TW);
+  if (layout == 2)
+    return (uint32_t)((st >> 1) * n_strips * 8 * TW + (t * 2 + (st & 1)) * 4 * TW);
   const int g = t >> 3, ns = min(8, n_strips - 8 * g);
   return (uint32_t)(((g * S * 8) + st * ns + (t & 7)) * 4 * TW);
 }

@@ -121,10 +121,10 @@ __device__ __forceinline__ void tg_item(const TrellisGemmArgs& a, TgShared& sh,
     cvo[0] = 4u * (g * TW + w0);
     cvo[1] = 4u * (g * TW + w1);
   }
-  // run (strip 8 grp + s, step kk) at strip_off[nb] + kk * sstep bytes (run_word)
+  // run (strip 8 grp + s, step kk) at strip_off[nb] + step_off(kk) bytes (run_word)
   const int S = n_ti / 4, nst = a.out / 16;
   const uint32_t base = 4u * run_word(a.layout, 8 * grp, 0, S, nst, TW);
-  const uint32_t sstep = 4u * run_word(a.layout, 8 * grp, 1, S, nst, TW) - base;
+  auto step_off = [&](int kk) { return 4u * run_word(a.layout, 8 * grp, kk, S, nst, TW) - base; };
   uint32_t strip_off[4];
 #pragma unroll
   for (int nb = 0; nb < 4; ++nb) {
@@ -133,7 +133,7 @@ __device__ __forceinline__ void tg_item(const TrellisGemmArgs& a, TgShared& sh,
   }
   ColWords<K> code[2][4];
   auto load_codes = [&](int slot, int kk) {
-    const uint32_t so = (uint32_t)kk * sstep;
+    const uint32_t so = step_off(kk);
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb) {
       const uint32_t o = strip_off[nb] + so;

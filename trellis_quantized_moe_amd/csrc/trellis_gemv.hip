@@ -28,7 +28,11 @@ namespace tq {
 
 namespace {
 
-constexpr int GEMV_THREADS = 64;         // one wave per workgroup
+// Waves per workgroup. The waves of a workgroup are independent (no LDS, no barrier); a
+// workgroup of 4 puts one wave on each SIMD of its compute unit, so the waves are spread
+// evenly over the SIMDs, which single-wave workgroups leave to the dispatcher.
+constexpr int GEMV_WG_WAVES = 1;
+constexpr int GEMV_THREADS = 64 * GEMV_WG_WAVES;
 constexpr int GEMV_WAVES_PER_SIMD = 3;  // register budget: 168 per lane
 
 // ---- code words --------------------------------------------------------------------------
@@ -150,11 +154,8 @@ __device__ __forceinline__ void stream(const TrellisGemvArgs& a, const uint32_t*
   const LaneOffsets<K> lo(g, n);
   const Rsrc rc = make_rsrc(unit, (uint32_t)((size_t)a.out * a.in * K / 8));
   const uint32_t cvo[2] = {4u * lo.o[0], 4u * lo.o[1]};
-  // byte offsets: run (strip 8 grp + s8, step st) at c0 + st cstep + sso[s8] (run_word)
+  // byte offsets: run (strip 8 grp + s8, step s0 + st) at cso(st) + sso[s8] (run_word)
   const int S = n_ti / 4, nst = a.out / 16;
-  const uint32_t c0 = 4u * run_word(a.layout, 8 * grp, s0, S, nst, TW);
-  const uint32_t cstep = 4u * (run_word(a.layout, 8 * grp, s0 + 1, S, nst, TW) -
-                               run_word(a.layout, 8 * grp, s0, S, nst, TW));
   uint32_t sso[8];
 #pragma unroll
   for (int s8 = 0; s8 < 8; ++s8)
@@ -164,7 +165,9 @@ __device__ __forceinline__ void stream(const TrellisGemvArgs& a, const uint32_t*
   const uint32_t xvo = tok >= 0 ? 32u * (uint32_t)((2 * tok + half) * n_ti + g) : 0x80000000u;
   const uint32_t x0 = 128u * (uint32_t)s0;
   // scalar offsets of step st, clamped to the last step (whose words are read again)
-  auto cso = [&](int st) { return c0 + (uint32_t)(st < last ? st : last) * cstep; };
+  auto cso = [&](int st) {
+    return 4u * run_word(a.layout, 8 * grp, s0 + (st < last ? st : last), S, nst, TW);
+  };
   auto xso = [&](int st) { return x0 + (uint32_t)(st < last ? st : last) * 128u; };
 
   // The prologue issues every code word load first (they need only the plan), then the
@@ -234,7 +237,8 @@ __device__ __forceinline__ void run_piece(const TrellisGemvArgs& a, const PlanRe
 
 __global__ __launch_bounds__(GEMV_THREADS, GEMV_WAVES_PER_SIMD) void trellis_gemv_kernel(TrellisGemvArgs a) {
   Piece pc;
-  if (!load_piece(a.desc, blockIdx.x, pc)) return;
+  const int w = blockIdx.x * GEMV_WG_WAVES + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (w >= a.G || !load_piece(a.desc, w, pc)) return;  // whole wave
   const PlanRec r = load_rec(a.rec, pc.ai);
   if (r.k == 2)
     run_piece<2>(a, r, pc.grp, pc.chunk, pc.s0, pc.s1, pc.idx);
@@ -300,14 +304,15 @@ __global__ __launch_bounds__(256) void trellis_decode_kernel(const uint32_t* __r
 }
 
 // ---- repack into the read order ---------------------------------------------------------
-// Thread i of grid row e copies 16-byte chunk i of unit e from its run in store order to the
-// same run in read order (run_word). A unit is out / 16 strips x S runs of 128 K bytes; bad
+// Thread i of grid row e copies 16-byte chunk i of unit e from its run in the store order
+// `from` (layout 0 or 2) to the same run in read order (run_word). Chunk i belongs to run
+// r = i / (8 K), taken as strip r / S, step r % S (every run is found once). A unit is out / 16 strips x S runs of 128 K bytes; bad
 // units (width not 2..4, misaligned, not inside codes) are skipped.
 __global__ __launch_bounds__(256) void trellis_repack_kernel(const uint8_t* __restrict__ bits,
                                                              const int64_t* __restrict__ code_off,
                                                              const uint32_t* __restrict__ codes,
                                                              int64_t codes_bytes, int out, int in,
-                                                             uint32_t* __restrict__ dst) {
+                                                             int from, uint32_t* __restrict__ dst) {
   const int e = blockIdx.y;
   const int K = bits[e];
   const int64_t off = code_off[e];
@@ -319,20 +324,20 @@ __global__ __launch_bounds__(256) void trellis_repack_kernel(const uint8_t* __re
   const int per_run = 8 * K;  // 16-byte chunks per run (128 K bytes)
   const int r = (int)(i / per_run), c = (int)(i % per_run);
   const int t = r / S, st = r % S;
-  const uint4* from = reinterpret_cast<const uint4*>(codes + off / 4 + run_word(0, t, st, S, nst, TW));
+  const uint4* src = reinterpret_cast<const uint4*>(codes + off / 4 + run_word(from, t, st, S, nst, TW));
   uint4* to = reinterpret_cast<uint4*>(dst + off / 4 + run_word(1, t, st, S, nst, TW));
-  to[c] = from[c];
+  to[c] = src[c];
 }
 
 }  // namespace
 
 hipError_t launch_trellis_repack(const uint8_t* bits, const int64_t* code_off,
                                  const uint32_t* codes, int64_t codes_bytes, int E, int out,
-                                 int in, uint32_t* dst, hipStream_t s) {
+                                 int in, int from, uint32_t* dst, hipStream_t s) {
   const int64_t chunks = (int64_t)out * in / 8 * 4 / 16;  // of the widest unit
   const dim3 grid((unsigned)((chunks + 255) / 256), (unsigned)E);
   hipLaunchKernelGGL(trellis_repack_kernel, grid, dim3(256), 0, s, bits, code_off, codes,
-                     codes_bytes, out, in, dst);
+                     codes_bytes, out, in, from, dst);
   return hipGetLastError();
 }
 
@@ -345,6 +350,7 @@ int trellis_gemv_grid() {
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, trellis_gemv_kernel, GEMV_THREADS, 0) !=
       hipSuccess)
     return 0;
+  per_cu *= GEMV_WG_WAVES;  // waves
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
   int g = std::min(per_cu, GEMV_TARGET_PER_CU) * cus;
   if (g > GEMV_MAX_G) g = GEMV_MAX_G;
@@ -354,7 +360,8 @@ int trellis_gemv_grid() {
 }
 
 hipError_t launch_trellis_gemv(const TrellisGemvArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(trellis_gemv_kernel, dim3(a.G), dim3(GEMV_THREADS), 0, s, a);
+  hipLaunchKernelGGL(trellis_gemv_kernel, dim3((a.G + GEMV_WG_WAVES - 1) / GEMV_WG_WAVES),
+                     dim3(GEMV_THREADS), 0, s, a);
   return hipGetLastError();
 }
 

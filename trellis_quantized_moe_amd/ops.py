@@ -12,7 +12,7 @@ import torch
 
 from . import _lib
 from ._lib import (TQ_AUTO, TQ_COMBINE, TQ_GEMM, TQ_GEMV, TQ_LAYOUT_GEMV,  # noqa: F401
-                   TQ_LAYOUT_STORE, TQ_ROTATE, check)
+                   TQ_LAYOUT_STORE, TQ_LAYOUT_UNIT128, TQ_ROTATE, check)
 
 
 def _ptr(t):
@@ -41,10 +41,12 @@ class TrellisLayer:
     scales: torch.Tensor     # int16 [E, out] (fp16 bit patterns)
     signs: torch.Tensor = None  # int8 [in] rotation signs (TQ_ROTATE), or None
     layout: int = TQ_LAYOUT_STORE
+    out_signs: torch.Tensor = None  # int8 [out] output-side rotation signs, or None
 
     @classmethod
     def from_host(cls, layer, device="cuda"):
         signs = layer.get("signs")
+        out_signs = layer.get("out_signs")
         return cls(
             E=int(layer["E"]), out=int(layer["out"]), in_=int(layer["in"]),
             bits=torch.from_numpy(np.ascontiguousarray(layer["bits"], dtype=np.uint8)).to(device),
@@ -53,12 +55,15 @@ class TrellisLayer:
             scales=torch.from_numpy(np.ascontiguousarray(layer["scales"]).view(np.int16)).to(device),
             signs=None if signs is None else
             torch.from_numpy(np.ascontiguousarray(signs, dtype=np.int8)).to(device),
+            layout=int(layer.get("layout", TQ_LAYOUT_STORE)),
+            out_signs=None if out_signs is None else
+            torch.from_numpy(np.ascontiguousarray(out_signs, dtype=np.int8)).to(device),
         )
 
     def with_codes(self, codes):
         """The same layer reading its units from another copy of the code buffer."""
         return TrellisLayer(self.E, self.out, self.in_, self.bits, self.code_off, codes,
-                            self.scales, self.signs, self.layout)
+                            self.scales, self.signs, self.layout, self.out_signs)
 
     def repacked(self):
         """The same layer with its units copied into TQ_LAYOUT_GEMV (see trellis_repack in
@@ -68,14 +73,15 @@ class TrellisLayer:
         c = self.c_struct()
         check(_lib.load().trellis_repack(ctypes.byref(c), _ptr(dst), _stream(self.codes.device)))
         return TrellisLayer(self.E, self.out, self.in_, self.bits, self.code_off, dst,
-                            self.scales, self.signs, TQ_LAYOUT_GEMV)
+                            self.scales, self.signs, TQ_LAYOUT_GEMV, self.out_signs)
 
     def c_struct(self):
         return _lib.TrellisLayerC(self.E, self.out, self.in_, self.layout, self.bits.data_ptr(),
                                   self.code_off.data_ptr(), self.codes.data_ptr(),
                                   self.scales.data_ptr(),
                                   None if self.signs is None else self.signs.data_ptr(),
-                                  self.codes.numel() * self.codes.element_size())
+                                  self.codes.numel() * self.codes.element_size(),
+                                  None if self.out_signs is None else self.out_signs.data_ptr())
 
 
 @dataclass
@@ -249,20 +255,21 @@ def ffn_workspace(T, topk, E, H, I, flags=TQ_AUTO, device="cuda"):
     return torch.zeros(n, dtype=torch.uint8, device=device)
 
 
-def trellis_expert_ffn(gate, up, down, x, topk_ids, topk_w=None, flags=TQ_AUTO, out=None,
+def trellis_expert_ffn(gate_up, down, x, topk_ids, topk_w=None, flags=TQ_AUTO, out=None,
                        ws=None):
-    """fp32 [T, H]: the routed expert FFN over trellis gate, up and down layers."""
+    """fp32 [T, H]: the routed expert FFN over a fused trellis gate/up layer (out = 2I) and a
+    trellis down layer (see trellis_expert_ffn in include/tq.h)."""
     _require_cuda(x, topk_ids, topk_w, out, ws)
     T, topk = topk_ids.shape
     if out is None:
-        out = torch.empty((T, gate.in_), dtype=torch.float32, device=x.device)
+        out = torch.empty((T, gate_up.in_), dtype=torch.float32, device=x.device)
     if ws is None:
-        ws = ffn_workspace(T, topk, gate.E, gate.in_, gate.out, flags, device=x.device)
-    g, u, d = gate.c_struct(), up.c_struct(), down.c_struct()
-    check(_lib.load().trellis_expert_ffn(ctypes.byref(g), ctypes.byref(u), ctypes.byref(d),
-                                         _ptr(x), T, _ptr(topk_ids), _ptr(topk_w), topk,
-                                         _ptr(out), flags, _ptr(ws), ws.numel(),
-                                         _stream(x.device)))
+        ws = ffn_workspace(T, topk, gate_up.E, gate_up.in_, gate_up.out // 2, flags,
+                           device=x.device)
+    gu, d = gate_up.c_struct(), down.c_struct()
+    check(_lib.load().trellis_expert_ffn(ctypes.byref(gu), ctypes.byref(d), _ptr(x), T,
+                                         _ptr(topk_ids), _ptr(topk_w), topk, _ptr(out), flags,
+                                         _ptr(ws), ws.numel(), _stream(x.device)))
     return out
 
 

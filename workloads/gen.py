@@ -182,33 +182,40 @@ def prefill_chunk(E=384, T=8192, topk=8, K=3):
             "layer": layer, "x": x, "topk_ids": ids, "topk_w": None, "rotate": True}
 
 
-def ffn_layers(workload, widths, H, I, extra=()):
-    """Gate, up (I x H) and down (H x I) trellis layers of one routed-expert FFN. Gate and up
-    share the gate's signs (one input rotation serves both); the down layer has its own
-    signs for the rotation of the intermediate. The fp16 scales are U(0.5, 1.5) /
-    (sqrt(in) * 128), so that with N(0, 1) inputs each projection's outputs are of order 1
-    (the decoded integers have a standard deviation of about 104)."""
-    gate = trellis_layer(workload, widths, I, H, with_signs=True, extra=(0,) + tuple(extra))
-    up = trellis_layer(workload, widths, I, H, with_signs=True, extra=(1,) + tuple(extra))
+def ffn_layers(workload, widths, H, I, extra=(), down_units128=True, out_rotation=False):
+    """The fused gate/up layer (2I x H: the gate's I channels, then the up's) and the down
+    layer (H x I) of one routed-expert FFN. The gate/up signs rotate the input, the down
+    layer's signs the intermediate. The down layer is stored as units of 128 intermediate
+    channels (FORMAT F2b, "layout": 2) unless down_units128 is False (one strip-major unit,
+    "layout": 0). With out_rotation, both layers also carry output-side signs (FORMAT F17).
+    The fp16 scales are U(0.5, 1.5) / (sqrt(in) * 128), so that with N(0, 1) inputs each
+    projection's outputs are of order 1 (the decoded integers have a standard deviation of
+    about 104)."""
+    gate_up = trellis_layer(workload, widths, 2 * I, H, with_signs=True, extra=(0,) + tuple(extra))
     down = trellis_layer(workload, widths, H, I, with_signs=True, extra=(2,) + tuple(extra))
-    up["signs"] = gate["signs"]
-    for lay, j in ((gate, 0), (up, 1), (down, 2)):
+    gate_up["layout"] = 0
+    down["layout"] = 2 if down_units128 else 0
+    for lay, j in ((gate_up, 0), (down, 2)):
         v = rng_for(workload, SCALES, j, 99, *extra).uniform(0.5, 1.5, size=(lay["E"], lay["out"]))
         lay["scales"] = (v / (np.sqrt(float(lay["in"])) * 128.0)).astype(np.float16).view(np.uint16)
-    return gate, up, down
+        if out_rotation:
+            lay["out_signs"] = random_signs(rng_for(workload, SIGNS, j, 98, *extra), lay["out"])
+    return gate_up, down
 
 
 def ffn_decode(E=384, T=128, topk=8, H=5120, I=768):
     """Routed-expert FFN decode batch: E experts whose gate, up and down projections are
     6 units of 128 intermediate channels each (I = 768, the 18 units per expert of the
-    exlr8 layout), mixed widths as the mixed layer, T tokens, top-k uniform, gates."""
+    exlr8 layout; gate and up as one 2I-channel layer, down as its 6 units of 128
+    intermediate channels), mixed widths as the mixed layer, T tokens, top-k uniform,
+    gates."""
     n3 = round(E * 608 / 15360)
     n4 = max(1, round(E * 21 / 15360))
-    gate, up, down = ffn_layers(7, mixed_widths(E, n3, n4), H, I)
+    gate_up, down = ffn_layers(7, mixed_widths(E, n3, n4), H, I)
     x = bf16_from_normal(rng_for(7, ACTS), (T, H))
     ids = uniform_routes(rng_for(7, ROUTES), T, E, topk)
     w = softmax_gates(rng_for(7, GATES), T, topk)
-    return {"name": "ffn_e%d_t%d_top%d" % (E, T, topk), "kind": "ffn", "gate": gate, "up": up,
+    return {"name": "ffn_e%d_t%d_top%d" % (E, T, topk), "kind": "ffn", "gate_up": gate_up,
             "down": down, "x": x, "topk_ids": ids, "topk_w": w, "rotate": True}
 
 
