@@ -31,5 +31,7 @@ from .routing import route_bucket
 from .gemm import expert_gemm, expert_gemm_values, expert_gemm_exact, combine_slots
 from .ffn import silu, silu_scalar, expert_ffn
 from .fp8b32 import fp8b32_unit_bytes, decode_fp8b32_unit, decode_fp8b32_weight_scalar
+from .mx import (E4M3_MAX, e4m3_all_values, e4m3_round, mx_block_scale, quantize_mxfp8_rows,
+                 dequantize_mxfp8_rows)
 
 __all__ = [name for name in dir() if not name.startswith("_")]
