@@ -43,6 +43,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 F16_PEAK_TFLOPS = 2500.0
+FP8_PEAK_TFLOPS = 5000.0
 MALL_BYTES = 1 << 30          # replicas of the code buffer total at least this much
 SLEEP_CYCLES = 60_000_000     # ~25 ms at 2.4 GHz: the GPU is busy while launches queue
 
@@ -375,6 +376,48 @@ def bench_prefill(torch, ops, args):
             "kernel": "trellis_gemm_kernel", "kernel_sec": kmean, "kernel_sec_median": kmed}
 
 
+def bench_mx_prefill(torch, ops, args):
+    """MXFP4 prefill chunk (384 units of 128 x 5120, 8,192 tokens, top-8 Zipf(1.1), gates),
+    units repacked once: the bf16 matrix-core GEMM and the FP8 variant (MXFP8 activations x
+    the stored E2M1 codes on the block-scaled fp8 x fp4 matrix cores)."""
+    from workloads import mxfp4_prefill_chunk
+    wl = mxfp4_prefill_chunk()
+    lay = wl["layer"]
+    dev = torch.device("cuda", 0)
+    L = ops.Mxfp4Layer.from_host(lay, dev).repacked()
+    x = torch.from_numpy(wl["x"].view(np.int16)).to(dev)
+    ids = torch.from_numpy(wl["topk_ids"]).to(dev)
+    gates = torch.from_numpy(wl["topk_w"]).to(dev)
+    T, topk = wl["topk_ids"].shape
+    flops = 2.0 * T * topk * lay["out"] * lay["in"]
+    reps = replicate(torch, L.units, L.units.numel())
+    layers = [L.with_units(u) for u in reps]
+    y = torch.empty((T, topk, lay["out"]), dtype=torch.float32, device=dev)
+    res = {}
+    for key, flags in (("bf16", ops.TQ_GEMM), ("fp8", ops.TQ_FP8)):
+        ws = ops.workspace(T, topk, lay["E"], lay["out"], lay["in"], flags, dev)
+
+        def step(r):
+            ops.mxfp4_expert_gemm(layers[r], x, ids, gates, flags=flags, out=y, ws=ws)
+
+        for r in range(len(reps)):
+            step(r)
+        torch.cuda.synchronize()
+        graphs = []
+        for r in range(len(reps)):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                step(r)
+            graphs.append(g)
+        steps = max(10, args.steps // 20)
+        sec = time_graph_steps(torch, graphs, steps, max(2, args.warmup // 10))
+        kmean, kmed = time_main_kernel(torch, ops, step, len(reps), max(10, args.kernel_iters // 10))
+        res[key] = {"sec_per_step": sec, "kernel_sec": kmean, "steps": steps, "flops": flops}
+        del graphs
+    log("mxfp4 prefill: %.1f GFLOP per step, %d replicas" % (flops / 1e9, len(reps)))
+    return res
+
+
 def cpu_baseline_mixed(wl, n_experts):
     """The oracle on a bounded sample, on every core this process may use: rotation of all
     tokens, then decode + FP64 contraction for the slots of n_experts of the active experts
@@ -530,8 +573,9 @@ def main():
     ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--kernel-iters", type=int, default=200)
-    ap.add_argument("--extras", default="mxfp4,prefill,nvfp4,ffn,shared",
-                    help="comma list of secondary workloads (mxfp4, prefill, nvfp4, ffn, shared) or 'none'")
+    ap.add_argument("--extras", default="mxfp4,prefill,mxprefill,nvfp4,ffn,shared",
+                    help="comma list of secondary workloads (mxfp4, prefill, mxprefill, nvfp4, ffn, "
+                         "shared) or 'none'")
     ap.add_argument("--cpu-sample-experts", type=int, default=0,
                     help="active experts in the CPU baseline sample (0 = all)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -626,6 +670,22 @@ def main():
             "kernel": p["kernel"], "kernel_us": round(p["kernel_sec"] * 1e6, 3),
             "kernel_TFLOP/s": round(p["flops"] / p["kernel_sec"] / 1e12, 3),
             "frac_f16_peak": round(p["flops"] / p["kernel_sec"] / 1e12 / F16_PEAK_TFLOPS, 4),
+        }
+    if "mxprefill" in todo:
+        mp = bench_mx_prefill(torch, ops, args)
+        b, f = mp["bf16"], mp["fp8"]
+        extras["mxfp4_prefill_chunk"] = {
+            "workload": "MXFP4 layer, 384 units of 128 x 5120, 8192 tokens, top-8 Zipf(1.1), gates, "
+                        "units repacked once",
+            "bf16_TFLOP/s": round(b["flops"] / b["sec_per_step"] / 1e12, 3),
+            "bf16_kernel": "mxfp4_gemm_kernel", "bf16_kernel_us": round(b["kernel_sec"] * 1e6, 3),
+            "bf16_frac_bf16_peak": round(b["flops"] / b["kernel_sec"] / 1e12 / F16_PEAK_TFLOPS, 4),
+            "fp8_TFLOP/s": round(f["flops"] / f["sec_per_step"] / 1e12, 3),
+            "fp8_ms_per_step": round(f["sec_per_step"] * 1e3, 5),
+            "fp8_kernel": "mx8_gemm_kernel (MXFP8 x MXFP4, v_mfma_scale_f32_16x16x128_f8f6f4)",
+            "fp8_kernel_us": round(f["kernel_sec"] * 1e6, 3),
+            "fp8_kernel_TFLOP/s": round(f["flops"] / f["kernel_sec"] / 1e12, 3),
+            "fp8_frac_fp8_peak": round(f["flops"] / f["kernel_sec"] / 1e12 / FP8_PEAK_TFLOPS, 4),
         }
     if "nvfp4" in todo:
         v = bench_nvfp4(torch, ops, args)

@@ -51,6 +51,11 @@ extern "C" {
 #define TQ_COMBINE 4u  /* write y[T][out] = sum over k = 0..topk-1 (in order) of the slots */
 #define TQ_ROTATE 8u   /* trellis only: x is not rotated; the call applies hadamard128 with */
                        /* the layer's signs first (same bits as calling hadamard128)        */
+#define TQ_FP8 16u     /* MXFP4 only: FP8 matrix cores (FORMAT F18): the activations are   */
+                       /* converted to MXFP8 (E4M3, one E8M0 scale per 32 inputs, as       */
+                       /* mxfp8_quantize) and multiplied with the stored E2M1 codes and     */
+                       /* their scales by the block-scaled fp8 x fp4 matrix cores; prefill  */
+                       /* mode (TQ_AUTO takes it; TQ_GEMV with TQ_FP8 is an error)           */
 
 /* ---- device status bits (tq_device_status) ------------------------------------------ */
 #define TQ_STATUS_BAD_EXPERT 1u  /* an id outside [-1, E): that slot's output is NaN    */
@@ -188,6 +193,26 @@ int trellis_expert_gemm(const tq_trellis_layer* L, const void* x, int64_t T,
 int mxfp4_expert_gemm(const tq_mxfp4_layer* L, const void* x, int64_t T,
                       const int32_t* topk_ids, const float* topk_w, int32_t topk,
                       float* y, uint32_t flags, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * With TQ_FP8 (FORMAT F18; DeepSeek-V4.1-Flash-1017 TrellisMX K2 Mix page, "Credits": FP8
+ * E4M3 tensor-core operands), the result is the same contraction over the MXFP8 form of x:
+ *   y[t][k][o] = g[t][k] * sum_i xq[t][i] * E2M1[c_e[o][i]] * 2^(b_e[o][i/32] - 127),
+ *   xq[t][i] = E4M3[a[t][i]] * 2^(s[t][i/32] - 127)   (a, s: mxfp8_quantize of x)
+ * accumulated in fp32 by v_mfma_scale_f32_16x16x128_f8f6f4.
+ */
+
+/*
+ * mxfp8_quantize — the MXFP8 form of bf16 rows (FORMAT F18; OCP MX block scaling as in the
+ * exlr8 page's "Stores"): per block of 32 consecutive inputs of a row, the E8M0 byte b with
+ * max|x| / 2^(b - 127) in [128, 256) (127 for an all-zero block, 255 when the block holds an
+ * infinity or NaN), and each element's E4M3 code, the nearest (ties to even) to
+ * x * 2^(127 - b). The activation conversion of TQ_FP8, exposed on its own.
+ *   x       device bf16 [rows][n], 16-byte aligned; n a multiple of 32.
+ *   codes   device uint8 [rows][n], 16-byte aligned.   scales  device uint8 [rows][n / 32].
+ */
+int mxfp8_quantize(const void* x, int64_t rows, int64_t n, uint8_t* codes, uint8_t* scales,
+                   void* stream);
 
 /*
  * fp8b32_expert_gemm — routed activations x fp8b32 expert weights.

@@ -19,7 +19,7 @@ from multiprocessing import shared_memory
 
 import numpy as np
 
-from . import ffn as _ffn, fpbits as _fpbits, gemm as _gemm, hadamard as _had, t16 as _t16
+from . import ffn as _ffn, fpbits as _fpbits, gemm as _gemm, hadamard as _had, mxfp4 as _mx, t16 as _t16
 
 _ARR = {}
 _META = {}
@@ -75,6 +75,19 @@ def _gemm_task(experts):
         return flat, np.zeros((0, lay["out"]))
     y = _gemm.expert_gemm(_ARR["x"], keep, gates, lay["E"], *_trellis_fns(lay))
     return flat, y.reshape(-1, lay["out"])[flat]
+
+
+def _mxfp4_task(experts):
+    E, out, inp = _META["mx.E"], _META["mx.out"], _META["mx.in"]
+    units = _ARR["mx.units"].reshape(E, -1)
+    ids = _ARR["ids"]
+    keep = _masked(ids, experts)
+    flat = np.nonzero(keep.reshape(-1) >= 0)[0]
+    if flat.size == 0:
+        return flat, np.zeros((0, out))
+    y = _gemm.expert_gemm_values(_ARR["x"], keep, _ARR.get("gates"), E,
+                                 lambda e: _mx.decode_mxfp4_unit(units[e], out, inp))
+    return flat, y.reshape(-1, out)[flat]
 
 
 def _ffn_task(experts):
@@ -173,3 +186,22 @@ def ffn(gate_up, down, x_rot_bits, ids, gates=None, workers=None):
     y = np.sum(parts, axis=0)
     y[np.any((ids < -1) | (ids >= gate_up["E"]), axis=1)] = np.nan  # as the oracle: NaN rows
     return y
+
+
+def mxfp4_slots(layer, x_vals, ids, gates=None, workers=None):
+    """oracle.expert_gemm_values of an MXFP4 layer over FP64 activation values, [T, topk,
+    out], computed expert by expert in parallel (0 for -1 slots, NaN for invalid ids)."""
+    ids = np.asarray(ids)
+    arrays = {"mx.units": layer["units"], "x": np.asarray(x_vals, dtype=np.float64),
+              "ids": ids, "gates": gates}
+    meta = {"mx.E": int(layer["E"]), "mx.out": int(layer["out"]), "mx.in": int(layer["in"])}
+    pool = _Pool(arrays, meta, workers)
+    try:
+        parts = pool.map(_mxfp4_task, _expert_chunks(ids, pool.n, layer["E"]))
+    finally:
+        pool.close()
+    y = np.zeros((ids.size, layer["out"]))
+    for flat, rows in parts:
+        y[flat] = rows
+    y[((ids < -1) | (ids >= layer["E"])).reshape(-1)] = np.nan
+    return y.reshape(ids.shape + (layer["out"],))

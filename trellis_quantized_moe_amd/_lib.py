@@ -26,6 +26,7 @@ TQ_GEMV = 1
 TQ_GEMM = 2
 TQ_COMBINE = 4
 TQ_ROTATE = 8
+TQ_FP8 = 16
 
 TQ_NOALLOC_SCRATCH_BYTES = 32 << 20
 
@@ -72,6 +73,7 @@ SIGNATURES = {
     "mxfp4_expert_gemm": (ctypes.c_int, [ctypes.POINTER(Mxfp4LayerC), _P, _I64, _P, _P, _I32,
                                          _P, _U32, _P, _SZ, _P]),
     "hadamard128": (ctypes.c_int, [_P, _P, _I64, _I64, _P, _P]),
+    "mxfp8_quantize": (ctypes.c_int, [_P, _I64, _I64, _P, _P, _P]),
     "route_bucket": (ctypes.c_int, [_P, _I64, _I32, _I32, _P, _P, _P, _P, _SZ, _P]),
     "trellis_decode": (ctypes.c_int, [_P, _I32, _I32, _I32, _P, _I32, _P]),
     "mxfp4_decode": (ctypes.c_int, [_P, _I32, _I32, _P, _P]),

@@ -68,7 +68,7 @@ int check_device() {
 }
 
 bool flags_valid(uint32_t flags) {
-  return (flags & ~15u) == 0 && (flags & 3u) != 3u;
+  return (flags & ~31u) == 0 && (flags & 3u) != 3u;
 }
 
 // The prefill GEMM pays off when experts average more than 16 routed slots and its items
@@ -79,7 +79,7 @@ constexpr int64_t GEMM_MIN_ITEMS = 256;
 bool use_gemm(int64_t T, int topk, int E, int groups, uint32_t flags) {
   const uint32_t mode = flags & 3u;
   if (mode == TQ_GEMV) return false;
-  if (mode == TQ_GEMM) return true;
+  if (mode == TQ_GEMM || (flags & TQ_FP8)) return true;
   const int64_t N = T * topk;
   return N > 16LL * E && (int64_t)groups * ((N + 127) / 128) >= GEMM_MIN_ITEMS;
 }
@@ -200,6 +200,11 @@ WsLayout ws_layout(int64_t T, int topk, int E, int out, int in, uint32_t flags, 
       off += round_up((size_t)T * in * 2, 256);
       L.rowsum = off;
       off += round_up((size_t)T * 8, 256);
+    } else if (flags & TQ_FP8) {  // MXFP8 activations
+      L.xa = off;
+      off += round_up((size_t)T * in, 256);
+      L.xs = off;
+      off += round_up((size_t)T * in / 32, 256);
     }
   }
   if ((flags & TQ_COMBINE) && L.gemm) {
@@ -263,6 +268,24 @@ int hadamard128(const void* x, void* y, int64_t rows, int64_t n, const int8_t* s
   hipError_t err = tq::launch_hadamard(static_cast<const uint16_t*>(x), static_cast<uint16_t*>(y),
                                        rows, n, signs, static_cast<hipStream_t>(stream));
   if (err != hipSuccess) return hip_fail(err, "hadamard128 launch");
+  return ok();
+}
+
+int mxfp8_quantize(const void* x, int64_t rows, int64_t n, uint8_t* codes, uint8_t* scales,
+                   void* stream) {
+  if (rows < 0) return fail(TQ_EINVAL, "rows = %lld is negative", (long long)rows);
+  if (n <= 0 || n % 32) return fail(TQ_EINVAL, "n = %lld is not a positive multiple of 32",
+                                    (long long)n);
+  if (n >= ((int64_t)1 << 30)) return fail(TQ_EINVAL, "n = %lld is too large", (long long)n);
+  if (rows == 0) return ok();
+  if (!x || !codes || !scales) return fail(TQ_EINVAL, "x, codes or scales is NULL");
+  if (!aligned(x, 16) || !aligned(codes, 16))
+    return fail(TQ_EALIGN, "x and codes must be 16-byte aligned");
+  int rc = check_device();
+  if (rc) return rc;
+  hipError_t err = tq::launch_mxfp8_prep(static_cast<const uint16_t*>(x), rows, (int)n, codes,
+                                         scales, static_cast<hipStream_t>(stream));
+  if (err != hipSuccess) return hip_fail(err, "mxfp8_quantize launch");
   return ok();
 }
 
@@ -498,6 +521,7 @@ int trellis_expert_gemm(const tq_trellis_layer* L, const void* x, int64_t T,
                         uint32_t flags, void* ws, size_t ws_bytes, void* stream) {
   int rc = check_trellis_layer(L);
   if (rc) return rc;
+  if (flags & TQ_FP8) return fail(TQ_EINVAL, "TQ_FP8 applies to MXFP4 layers only");
   if ((flags & TQ_ROTATE) && L->signs && !aligned(L->signs, 16))
     return fail(TQ_EALIGN, "signs must be 16-byte aligned");
   tq::WsLayout W;
@@ -642,6 +666,12 @@ int mx_expert_gemm(const MxLayer* L, const void* x, int64_t T, const int32_t* to
                    const float* topk_w, int32_t topk, float* y, uint32_t flags, void* ws,
                    size_t ws_bytes, void* stream) {
   if (flags & TQ_ROTATE) return fail(TQ_EINVAL, "TQ_ROTATE applies to trellis layers only");
+  if ((flags & TQ_FP8) && L->fmt != tq::MX_FP4)
+    return fail(TQ_EINVAL, "TQ_FP8 applies to MXFP4 layers only");
+  if ((flags & TQ_FP8) && (flags & 3u) == TQ_GEMV)
+    return fail(TQ_EINVAL, "TQ_FP8 runs in the prefill mode only (not with TQ_GEMV)");
+  if ((flags & TQ_FP8) && T * (int64_t)L->in >= ((int64_t)1 << 31))
+    return fail(TQ_EINVAL, "the MXFP8 activations (T * in bytes) must stay below 2^31");
   const int64_t unit = mx_unit_bytes(L->fmt, L->out, L->in);
   tq::WsLayout W;
   int rc = common_checks(L->E, L->out, L->in, x, T, topk_ids, topk, y, flags, ws, ws_bytes, unit, &W);
@@ -719,6 +749,34 @@ int mx_expert_gemm(const MxLayer* L, const void* x, int64_t T, const int32_t* to
     err = tq::launch_piece_reduce(r, s);
     if (err != hipSuccess) return hip_fail(err, "GEMV piece reduction launch");
     return ok();
+  } else if (flags & TQ_FP8) {
+    err = tq::launch_mxfp8_prep(xb, T, L->in, at<uint8_t>(ws, W.xa), at<uint8_t>(ws, W.xs), s);
+    if (err != hipSuccess) return hip_fail(err, "MXFP8 activation launch");
+    rc = run_route(W, ws, topk_ids, N, L->E, L->out, y_slots, s);
+    if (rc) return rc;
+    tq::Mx8GemmArgs a{};
+    a.layout = L->layout;
+    a.units = L->units;
+    a.xa = at<uint8_t>(ws, W.xa);
+    a.xa_bytes = (uint32_t)(T * L->in);
+    a.xs = at<uint8_t>(ws, W.xs);
+    a.xs_bytes = (uint32_t)(T * L->in / 32);
+    a.gates = topk_w;
+    a.pairs = at<int32_t>(ws, W.pairs);
+    a.items = at<int32_t>(ws, W.items);
+    a.n_items = at<int32_t>(ws, W.n_items);
+    a.y = y_slots;
+    a.E = L->E;
+    a.out = L->out;
+    a.in = L->in;
+    a.topk = topk;
+    a.groups = W.groups;
+    a.max_items = W.max_items;
+    err = time_begin(s);
+    if (err != hipSuccess) return hip_fail(err, "hipEventRecord");
+    err = tq::launch_mx8_gemm(a, s);
+    if (err == hipSuccess) err = time_end(s);
+    if (err != hipSuccess) return hip_fail(err, "FP8 GEMM launch");
   } else {
     rc = run_route(W, ws, topk_ids, N, L->E, L->out, y_slots, s);
     if (rc) return rc;

@@ -17,6 +17,7 @@ struct WsLayout {
   size_t route_bytes = 0;
   size_t slots = 0, slots_bytes = 0;
   size_t xprep = 0, rowsum = 0, xq = 0, xscale = 0, xsum = 0;
+  size_t xa = 0, xs = 0;  // MXFP8 activation codes and block scales (TQ_FP8)
   size_t info = 0, rec = 0, desc = 0, list = 0, slot_info = 0, prank = 0;
   size_t total = 0;
   int groups = 1, route_blocks = 1, max_items = 0;
@@ -164,6 +165,27 @@ struct Mxfp4GemmArgs {
   int E, out, in, topk, groups, max_items;
 };
 hipError_t launch_mxfp4_gemm(const Mxfp4GemmArgs& a, hipStream_t s);
+
+// MXFP8 activations (FORMAT F18): bf16 [rows][n] -> E4M3 codes [rows][n] and E8M0 block scales
+// [rows][n / 32].
+hipError_t launch_mxfp8_prep(const uint16_t* x, int64_t rows, int n, uint8_t* codes,
+                             uint8_t* scales, hipStream_t s);
+// The MXFP4 prefill GEMM on the block-scaled fp8 x fp4 matrix cores (mx8.hip).
+struct Mx8GemmArgs {
+  int layout;            // 0: codes in store order; 1: repacked
+  const uint8_t* units;
+  const uint8_t* xa;     // E4M3 codes [T][in]
+  uint32_t xa_bytes;     // < 2^31
+  const uint8_t* xs;     // E8M0 scales [T][in / 32]
+  uint32_t xs_bytes;
+  const float* gates;
+  const int32_t* pairs;
+  const int32_t* items;
+  const int32_t* n_items;
+  float* y;
+  int E, out, in, topk, groups, max_items;
+};
+hipError_t launch_mx8_gemm(const Mx8GemmArgs& a, hipStream_t s);
 
 struct RouteArgs {
   const int32_t* ids;

@@ -12,7 +12,7 @@ import torch
 
 from . import _lib
 from ._lib import (TQ_AUTO, TQ_COMBINE, TQ_GEMM, TQ_GEMV, TQ_LAYOUT_GEMV,  # noqa: F401
-                   TQ_LAYOUT_STORE, TQ_LAYOUT_UNIT128, TQ_ROTATE, check)
+                   TQ_LAYOUT_STORE, TQ_LAYOUT_UNIT128, TQ_ROTATE, TQ_FP8, check)
 
 
 def _ptr(t):
@@ -163,6 +163,18 @@ def hadamard128(x, signs=None, out=None):
     check(_lib.load().hadamard128(_ptr(x), _ptr(y), x.shape[0], x.shape[1], _ptr(signs),
                                   _stream(x.device)))
     return y
+
+
+def mxfp8_quantize(x):
+    """(codes uint8 [rows, n], scales uint8 [rows, n / 32]): the MXFP8 form of bf16 rows (see
+    mxfp8_quantize in include/tq.h)."""
+    _require_cuda(x)
+    rows, n = x.shape
+    codes = torch.empty((rows, n), dtype=torch.uint8, device=x.device)
+    scales = torch.empty((rows, n // 32), dtype=torch.uint8, device=x.device)
+    check(_lib.load().mxfp8_quantize(_ptr(x), rows, n, _ptr(codes), _ptr(scales),
+                                     _stream(x.device)))
+    return codes, scales
 
 
 def _gemm(fn, layer_c, E, out_ch, in_, x, topk_ids, topk_w, flags, out, ws, mxfp4):

@@ -6,7 +6,8 @@ __all__ = [
     "rng_for", "bf16_from_normal", "fp16_scales", "random_words", "random_signs",
     "uniform_routes", "zipf_routes", "softmax_gates", "trellis_layer", "mxfp4_layer",
     "single_matrix", "one_unit", "mxfp4_decode_layer", "mixed_widths", "mixed_layer",
-    "prefill_chunk", "ffn_layers", "ffn_decode", "fp8b32_layer", "shared_expert",
+    "prefill_chunk", "mxfp4_prefill_chunk", "ffn_layers", "ffn_decode", "fp8b32_layer",
+    "shared_expert",
     "WORKLOADS",
 ]
 
@@ -127,6 +128,17 @@ def mxfp4_decode_layer(E=384, T=64, topk=8):
     w = softmax_gates(rng_for(3, GATES), T, topk)
     return {"name": "mxfp4_e%d_t%d_top%d" % (E, T, topk), "kind": "mxfp4", "layer": layer,
             "x": x, "topk_ids": ids, "topk_w": w, "rotate": False}
+
+
+def mxfp4_prefill_chunk(E=384, T=8192, topk=8):
+    """MXFP4 prefill chunk: the MXFP4 layer's shapes (384 units of 128 x 5120), T tokens
+    routed top-k by Zipf(1.1) popularity as the trellis prefill chunk, softmax gates."""
+    layer = mxfp4_layer(9, E, 128, 5120)
+    x = bf16_from_normal(rng_for(9, ACTS), (T, 5120))
+    ids = zipf_routes(rng_for(9, ROUTES), T, E, topk)
+    w = softmax_gates(rng_for(9, GATES), T, topk)
+    return {"name": "mxfp4_prefill_e%d_t%d_top%d" % (E, T, topk), "kind": "mxfp4",
+            "layer": layer, "x": x, "topk_ids": ids, "topk_w": w, "rotate": False}
 
 
 def fp8b32_layer(workload, E, out, inputs, extra=()):
