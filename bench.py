@@ -499,6 +499,23 @@ def drive(torch, ops, which, iters):
             ws = ops.workspace(T, 1, 1, lay["out"], lay["in"], ops.TQ_AUTO, dev)
             for i in range(iters):
                 ops.fp8b32_expert_gemm(layers[i % len(layers)], x, ids, out=y, ws=ws)
+    elif which == "mxprefill":
+        from workloads import mxfp4_prefill_chunk
+        wl = mxfp4_prefill_chunk()
+        lay = wl["layer"]
+        L = ops.Mxfp4Layer.from_host(lay, dev).repacked()
+        x = torch.from_numpy(wl["x"].view(np.int16)).to(dev)
+        ids = torch.from_numpy(wl["topk_ids"]).to(dev)
+        gates = torch.from_numpy(wl["topk_w"]).to(dev)
+        T, topk = wl["topk_ids"].shape
+        reps = replicate(torch, L.units, L.units.numel())
+        layers = [L.with_units(u) for u in reps]
+        y = torch.empty((T, topk, lay["out"]), dtype=torch.float32, device=dev)
+        for flags in (ops.TQ_GEMM, ops.TQ_FP8):
+            ws = ops.workspace(T, topk, lay["E"], lay["out"], lay["in"], flags, dev)
+            for i in range(iters):
+                ops.mxfp4_expert_gemm(layers[i % len(layers)], x, ids, gates, flags=flags, out=y,
+                                      ws=ws)
     elif which == "nvfp4":
         lay = mxfp4_decode_layer()["layer"]
         L = ops.Mxfp4Layer.from_host(lay, dev)
@@ -542,6 +559,34 @@ def counter_means(run_dir, counter):
     return {k: float(np.mean(v)) for k, v in acc.items()}
 
 
+def counter_summary(run_dirs):
+    """Per-kernel mean of every counter per dispatch over rocprofv3 csv runs, as a markdown
+    table (one row per kernel, one column per counter)."""
+    import csv
+    import glob
+    table, names = {}, []
+    for d in run_dirs:
+        files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+        if not files:
+            raise SystemExit("no counter_collection.csv under " + d)
+        acc = {}
+        for r in csv.DictReader(open(files[0])):
+            k = r["Kernel_Name"].replace("(anonymous namespace)::", "").replace("void ", "")
+            k = k.split("(")[0].split("<")[0].strip().split("::")[-1]
+            acc.setdefault((k, r["Counter_Name"]), []).append(float(r["Counter_Value"]))
+        for (k, c), v in acc.items():
+            if c not in names:
+                names.append(c)
+            table.setdefault(k, {})[c] = (float(np.mean(v)), len(v))
+    print("| kernel | dispatches | " + " | ".join(names) + " |")
+    print("|---|---:|" + "---:|" * len(names))
+    for k in sorted(table):
+        row = table[k]
+        n = max(v[1] for v in row.values())
+        cells = ["{:,.0f}".format(row[c][0]) if c in row else "" for c in names]
+        print("| %s | %d | %s |" % (k, n, " | ".join(cells)))
+
+
 def write_traffic(fetch_dir, write_dir, command):
     """HBM bytes per launch of the trellis GEMV from FETCH_SIZE and WRITE_SIZE runs (KiB per
     dispatch), each divided by what the same counter reads per byte of the calibration copy."""
@@ -579,13 +624,19 @@ def main():
     ap.add_argument("--cpu-sample-experts", type=int, default=0,
                     help="active experts in the CPU baseline sample (0 = all)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--drive", choices=["mixed", "mxfp4", "prefill", "nvfp4", "shared", "ffn"],
+    ap.add_argument("--drive", choices=["mixed", "mxfp4", "prefill", "mxprefill", "nvfp4", "shared",
+                                        "ffn"],
                     help="only run --steps steps of one workload (for rocprofv3)")
     ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="summarise rocprofv3 FETCH_SIZE / WRITE_SIZE runs of --drive mixed")
     ap.add_argument("--traffic-command", default="",
                     help="the profiler commands that made the --write-traffic runs")
+    ap.add_argument("--counter-summary", nargs="+", metavar="DIR",
+                    help="print per-kernel counter means of rocprofv3 csv runs as markdown")
     args = ap.parse_args()
+    if args.counter_summary:
+        counter_summary(args.counter_summary)
+        return
     if args.write_traffic:
         write_traffic(args.write_traffic[0], args.write_traffic[1], args.traffic_command)
         return

@@ -32,6 +32,6 @@ from .gemm import expert_gemm, expert_gemm_values, expert_gemm_exact, combine_sl
 from .ffn import silu, silu_scalar, expert_ffn
 from .fp8b32 import fp8b32_unit_bytes, decode_fp8b32_unit, decode_fp8b32_weight_scalar
 from .mx import (E4M3_MAX, e4m3_all_values, e4m3_round, mx_block_scale, quantize_mxfp8_rows,
-                 dequantize_mxfp8_rows)
+                 dequantize_mxfp8_rows, t16_e4m3, t16_e4m3_codes, mxfp8_values)
 
 __all__ = [name for name in dir() if not name.startswith("_")]

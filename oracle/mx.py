@@ -12,7 +12,10 @@ TEST INFRASTRUCTURE (see the package docstring). Written from the definitions:
 - MXFP8 activation blocks: each 32 consecutive inputs of a row share one E8M0 scale
   2^(b - 127), chosen so that the block's largest magnitude divided by it lies in
   [128, 256) (so no element can exceed 448); the elements are the E4M3 roundings of the
-  scaled values.
+  scaled values;
+- T16 values as E4M3 operands (FORMAT F19): the integer q of the T16 hash rounded to the
+  nearest E4M3 value, its per-channel fp16 scale applied after the contraction as for the
+  exact operands.
 """
 
 import math
@@ -94,3 +97,27 @@ def dequantize_mxfp8_rows(codes, scales, block=32):
     s = np.asarray(scales, dtype=np.int64)
     factor = np.where(s == 255, np.nan, np.ldexp(1.0, s - 127))
     return (vals.reshape(rows, n // block, block) * factor[:, :, None]).reshape(rows, n)
+
+
+def t16_e4m3(q):
+    """E4M3 operand of T16 values (FORMAT F19): each integer q in [-255, 255] rounded to the
+    nearest E4M3 value (ties to the even code). Returns the values, float64."""
+    q = np.asarray(q)
+    if np.any(np.abs(q) > 255):
+        raise ValueError("T16 values lie in [-255, 255]")
+    return e4m3_all_values()[e4m3_round(q.astype(np.float64))]
+
+
+def t16_e4m3_codes(q):
+    """E4M3 codes (uint8) of T16 values, as t16_e4m3 rounds them."""
+    q = np.asarray(q)
+    if np.any(np.abs(q) > 255):
+        raise ValueError("T16 values lie in [-255, 255]")
+    return e4m3_round(q.astype(np.float64))
+
+
+def mxfp8_values(x_vals):
+    """The values the FP8 matrix cores see for activation rows: MXFP8 quantisation (F18)
+    followed by its exact decode."""
+    codes, scales = quantize_mxfp8_rows(x_vals)
+    return dequantize_mxfp8_rows(codes, scales)

@@ -19,7 +19,7 @@ from multiprocessing import shared_memory
 
 import numpy as np
 
-from . import ffn as _ffn, fpbits as _fpbits, gemm as _gemm, hadamard as _had, mxfp4 as _mx, t16 as _t16
+from . import ffn as _ffn, fpbits as _fpbits, gemm as _gemm, hadamard as _had, mx as _mx8, mxfp4 as _mx, t16 as _t16
 
 _ARR = {}
 _META = {}
@@ -44,7 +44,7 @@ def _layer(prefix):
     return d
 
 
-def _trellis_fns(lay):
+def _trellis_fns(lay, e4m3=False):
     cache = {}
 
     def weight_of(e):
@@ -54,7 +54,8 @@ def _trellis_fns(lay):
             s = int(lay["code_off"][e]) // 4
             cache.clear()  # one expert at a time: bounded memory
             decode = _t16.decode_units128 if lay["layout"] == 2 else _t16.decode_unit
-            cache[e] = decode(lay["codes"][s:s + n], K, lay["out"], lay["in"]).astype(np.float64)
+            q = decode(lay["codes"][s:s + n], K, lay["out"], lay["in"])
+            cache[e] = _mx8.t16_e4m3(q) if e4m3 else q.astype(np.float64)
         return cache[e]
 
     scales = _fpbits.f16_bits_to_f64(lay["scales"])
@@ -73,7 +74,10 @@ def _gemm_task(experts):
     flat = np.nonzero(keep.reshape(-1) >= 0)[0]
     if flat.size == 0:
         return flat, np.zeros((0, lay["out"]))
-    y = _gemm.expert_gemm(_ARR["x"], keep, gates, lay["E"], *_trellis_fns(lay))
+    if _META.get("e4m3"):  # FP8 operands: MXFP8 activation values, E4M3 weights
+        y = _gemm.expert_gemm_values(_ARR["x"], keep, gates, lay["E"], *_trellis_fns(lay, True))
+    else:
+        y = _gemm.expert_gemm(_ARR["x"], keep, gates, lay["E"], *_trellis_fns(lay))
     return flat, y.reshape(-1, lay["out"])[flat]
 
 
@@ -147,12 +151,16 @@ def _layer_arrays(prefix, lay):
     return arrays, meta
 
 
-def trellis_slots(layer, x_bits, ids, gates=None, workers=None):
+def trellis_slots(layer, x_bits, ids, gates=None, workers=None, fp8=False):
     """oracle.expert_gemm of a trellis layer, [T, topk, out], computed expert by expert in
     parallel. Slots with ids outside [0, E) are left as the oracle defines them (0 for -1,
-    NaN for invalid ids)."""
+    NaN for invalid ids). With fp8, the FP8 operands of FORMAT F19: the activations' MXFP8
+    values (oracle.mxfp8_values of the bf16 x) and the E4M3 roundings of the weights."""
     ids = np.asarray(ids)
     arrays, meta = _layer_arrays("layer", layer)
+    if fp8:
+        x_bits = _mx8.mxfp8_values(_fpbits.bf16_bits_to_f64(np.asarray(x_bits, dtype=np.uint16)))
+        meta["e4m3"] = 1
     arrays.update({"x": x_bits, "ids": ids, "gates": gates})
     pool = _Pool(arrays, meta, workers)
     try:
