@@ -341,7 +341,9 @@ def bench_shared(torch, ops, args):
     return res
 
 
-def bench_prefill(torch, ops, args):
+def bench_prefill(torch, ops, args, fp8=False):
+    """The trellis prefill chunk; with fp8 the FP8 variant (MXFP8 activations x T16 values
+    rounded to E4M3 on the block-scaled fp8 matrix cores)."""
     from workloads import prefill_chunk
     wl = prefill_chunk()
     lay = wl["layer"]
@@ -354,11 +356,13 @@ def bench_prefill(torch, ops, args):
     reps = replicate(torch, L.codes, L.codes.numel() * 4)
     layers = [L.with_codes(c) for c in reps]
     y = torch.empty((T, topk, lay["out"]), dtype=torch.float32, device=dev)
-    ws = ops.workspace(T, topk, lay["E"], lay["out"], lay["in"], ops.TQ_AUTO, dev)
-    log("prefill: %.1f GFLOP per step, %d replicas" % (flops / 1e9, len(reps)))
+    flags = ops.TQ_ROTATE | (ops.TQ_FP8 if fp8 else 0)
+    ws = ops.workspace(T, topk, lay["E"], lay["out"], lay["in"], flags, dev)
+    log("prefill%s: %.1f GFLOP per step, %d replicas" % (" fp8" if fp8 else "", flops / 1e9,
+                                                         len(reps)))
 
     def step(r):
-        ops.trellis_expert_gemm(layers[r], x, ids, flags=ops.TQ_ROTATE, out=y, ws=ws)
+        ops.trellis_expert_gemm(layers[r], x, ids, flags=flags, out=y, ws=ws)
 
     for r in range(len(reps)):
         step(r)
@@ -373,7 +377,8 @@ def bench_prefill(torch, ops, args):
     sec = time_graph_steps(torch, graphs, steps, max(2, args.warmup // 10))
     kmean, kmed = time_main_kernel(torch, ops, step, len(reps), max(10, args.kernel_iters // 10))
     return {"sec_per_step": sec, "flops": flops, "steps": steps,
-            "kernel": "trellis_gemm_kernel", "kernel_sec": kmean, "kernel_sec_median": kmed}
+            "kernel": "tf8_gemm_kernel" if fp8 else "trellis_gemm_kernel", "kernel_sec": kmean,
+            "kernel_sec_median": kmed}
 
 
 def bench_mx_prefill(torch, ops, args):
@@ -459,7 +464,7 @@ def drive(torch, ops, which, iters):
     and writes each byte once."""
     from workloads import mixed_layer, mxfp4_decode_layer, prefill_chunk
     dev = torch.device("cuda", 0)
-    if which in ("mixed", "prefill"):
+    if which in ("mixed", "prefill", "prefill8"):
         wl = mixed_layer() if which == "mixed" else prefill_chunk()
         lay = wl["layer"]
         L = ops.TrellisLayer.from_host(lay, dev).repacked()
@@ -469,10 +474,10 @@ def drive(torch, ops, which, iters):
         reps = replicate(torch, L.codes, L.codes.numel() * 4)
         layers = [L.with_codes(c) for c in reps]
         y = torch.empty((T, topk, lay["out"]), dtype=torch.float32, device=dev)
-        ws = ops.workspace(T, topk, lay["E"], lay["out"], lay["in"], ops.TQ_AUTO, dev)
+        flags = ops.TQ_ROTATE | (ops.TQ_FP8 if which == "prefill8" else 0)
+        ws = ops.workspace(T, topk, lay["E"], lay["out"], lay["in"], flags, dev)
         for i in range(iters):
-            ops.trellis_expert_gemm(layers[i % len(layers)], x, ids, flags=ops.TQ_ROTATE,
-                                    out=y, ws=ws)
+            ops.trellis_expert_gemm(layers[i % len(layers)], x, ids, flags=flags, out=y, ws=ws)
     elif which == "ffn":
         from workloads import ffn_decode
         wl = ffn_decode()
@@ -624,8 +629,8 @@ def main():
     ap.add_argument("--cpu-sample-experts", type=int, default=0,
                     help="active experts in the CPU baseline sample (0 = all)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--drive", choices=["mixed", "mxfp4", "prefill", "mxprefill", "nvfp4", "shared",
-                                        "ffn"],
+    ap.add_argument("--drive", choices=["mixed", "mxfp4", "prefill", "prefill8", "mxprefill",
+                                        "nvfp4", "shared", "ffn"],
                     help="only run --steps steps of one workload (for rocprofv3)")
     ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="summarise rocprofv3 FETCH_SIZE / WRITE_SIZE runs of --drive mixed")
@@ -721,6 +726,17 @@ def main():
             "kernel": p["kernel"], "kernel_us": round(p["kernel_sec"] * 1e6, 3),
             "kernel_TFLOP/s": round(p["flops"] / p["kernel_sec"] / 1e12, 3),
             "frac_f16_peak": round(p["flops"] / p["kernel_sec"] / 1e12 / F16_PEAK_TFLOPS, 4),
+        }
+        f = bench_prefill(torch, ops, args, fp8=True)
+        extras["prefill_chunk_fp8"] = {
+            "workload": "the same chunk with FP8 operands: MXFP8 activations (rotation fused "
+                        "into their prep) x T16 values rounded to E4M3",
+            "TFLOP/s": round(f["flops"] / f["sec_per_step"] / 1e12, 3),
+            "ms_per_step": round(f["sec_per_step"] * 1e3, 5), "steps": f["steps"],
+            "kernel": f["kernel"] + " (v_mfma_scale_f32_16x16x128_f8f6f4, fp8 x fp8)",
+            "kernel_us": round(f["kernel_sec"] * 1e6, 3),
+            "kernel_TFLOP/s": round(f["flops"] / f["kernel_sec"] / 1e12, 3),
+            "frac_fp8_peak": round(f["flops"] / f["kernel_sec"] / 1e12 / FP8_PEAK_TFLOPS, 4),
         }
     if "mxprefill" in todo:
         mp = bench_mx_prefill(torch, ops, args)

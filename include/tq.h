@@ -51,11 +51,12 @@ extern "C" {
 #define TQ_COMBINE 4u  /* write y[T][out] = sum over k = 0..topk-1 (in order) of the slots */
 #define TQ_ROTATE 8u   /* trellis only: x is not rotated; the call applies hadamard128 with */
                        /* the layer's signs first (same bits as calling hadamard128)        */
-#define TQ_FP8 16u     /* MXFP4 only: FP8 matrix cores (FORMAT F18): the activations are   */
+#define TQ_FP8 16u     /* trellis and MXFP4: FP8 matrix cores. The activations are         */
                        /* converted to MXFP8 (E4M3, one E8M0 scale per 32 inputs, as       */
-                       /* mxfp8_quantize) and multiplied with the stored E2M1 codes and     */
-                       /* their scales by the block-scaled fp8 x fp4 matrix cores; prefill  */
-                       /* mode (TQ_AUTO takes it; TQ_GEMV with TQ_FP8 is an error)           */
+                       /* mxfp8_quantize; FORMAT F18) and multiplied on the block-scaled    */
+                       /* fp8 matrix cores with the stored E2M1 codes and their scales      */
+                       /* (MXFP4), or with the T16 values rounded to E4M3 (trellis, FORMAT  */
+                       /* F19); prefill mode (TQ_AUTO takes it; with TQ_GEMV an error)      */
 
 /* ---- device status bits (tq_device_status) ------------------------------------------ */
 #define TQ_STATUS_BAD_EXPERT 1u  /* an id outside [-1, E): that slot's output is NaN    */
@@ -177,6 +178,12 @@ typedef struct tq_fp8b32_layer {
  * two int8 halves, whose rounding of elements far below the token's largest one is covered
  * by the parity bound. Any finite bf16 input is valid; a token with an infinite or NaN
  * element gets NaN in its slots.
+ * With TQ_FP8 (FORMAT F19; DeepSeek-V4.1-Flash-1017 TrellisMX K2 Mix page, "Credits": the
+ * trellis decoded straight into FP8 E4M3 tensor-core operands) the call computes
+ *   y[t][k][o] = g[t][k] * f32(scale_e[o]) * sum_i xq[t][i] * E4M3(q_e[i][o]),
+ * E4M3(q) the nearest E4M3 value to q (ties to even) and xq the MXFP8 values of x (after
+ * the rotation with TQ_ROTATE), accumulated in fp32 by v_mfma_scale_f32_16x16x128_f8f6f4.
+ * A 32-input block of a token holding an infinity or NaN makes that token's slots NaN.
  */
 int trellis_expert_gemm(const tq_trellis_layer* L, const void* x, int64_t T,
                         const int32_t* topk_ids, const float* topk_w, int32_t topk,
@@ -265,7 +272,8 @@ int route_bucket(const int32_t* topk_ids, int64_t T, int32_t topk, int32_t E,
  * matrix cores receive. Path 0: the decode-batch GEMV's column decoder and signed bytes
  * lo8(m) - 128 and hi8(m) - 128 (q = their sum + 1). Path 1: the prefill GEMM's decoders
  * (each half of a tile column on its own for K = 2 and 3, the whole column for K = 4) and
- * its byte sums q + 255 as f16 subnormals.
+ * its byte sums q + 255 as f16 subnormals. Path 2: the FP8 prefill's decoder (TQ_FP8,
+ * FORMAT F19); q[o][i] then holds the E4M3 code byte (0..255) of the rounded value.
  *   codes  device, out*in*K/8 bytes, 16-byte aligned.   K in {2, 3, 4}.
  *   out    multiple of 16.   in  multiple of 64.
  *   q      device int16 [out][in] (HF orientation: row = output channel), 4-byte aligned.

@@ -195,7 +195,7 @@ WsLayout ws_layout(int64_t T, int topk, int E, int out, int in, uint32_t flags, 
     L.n_items = off;
     off += 256;
     L.route_bytes = off - start;
-    if (!mxfp4) {  // the trellis GEMM reads prepared f16 activations
+    if (!mxfp4 && !(flags & TQ_FP8)) {  // the trellis GEMM reads prepared f16 activations
       L.xprep = off;
       off += round_up((size_t)T * in * 2, 256);
       L.rowsum = off;
@@ -294,14 +294,16 @@ int trellis_decode(const uint32_t* codes, int32_t K, int32_t out, int32_t in, in
   if (K < 2 || K > 4) return fail(TQ_EINVAL, "K = %d is not 2, 3 or 4", K);
   if (out <= 0 || out % 16) return fail(TQ_EINVAL, "out = %d is not a positive multiple of 16", out);
   if (in <= 0 || in % 64) return fail(TQ_EINVAL, "in = %d is not a positive multiple of 64", in);
-  if (path != 0 && path != 1) return fail(TQ_EINVAL, "path = %d is not 0 or 1", path);
+  if (path < 0 || path > 2) return fail(TQ_EINVAL, "path = %d is not 0, 1 or 2", path);
   if (!codes || !q) return fail(TQ_EINVAL, "codes or q is NULL");
   if (!aligned(codes, 16)) return fail(TQ_EALIGN, "codes must be 16-byte aligned");
   if (!aligned(q, 4)) return fail(TQ_EALIGN, "q must be 4-byte aligned");
   int rc = check_device();
   if (rc) return rc;
-  hipError_t err = tq::launch_trellis_decode(codes, K, out, in, q, path,
-                                             static_cast<hipStream_t>(stream));
+  hipError_t err =
+      path == 2 ? tq::launch_tf8_decode(codes, K, out, in, q, static_cast<hipStream_t>(stream))
+                : tq::launch_trellis_decode(codes, K, out, in, q, path,
+                                            static_cast<hipStream_t>(stream));
   if (err != hipSuccess) return hip_fail(err, "trellis_decode launch");
   return ok();
 }
@@ -521,7 +523,10 @@ int trellis_expert_gemm(const tq_trellis_layer* L, const void* x, int64_t T,
                         uint32_t flags, void* ws, size_t ws_bytes, void* stream) {
   int rc = check_trellis_layer(L);
   if (rc) return rc;
-  if (flags & TQ_FP8) return fail(TQ_EINVAL, "TQ_FP8 applies to MXFP4 layers only");
+  if ((flags & TQ_FP8) && (flags & 3u) == TQ_GEMV)
+    return fail(TQ_EINVAL, "TQ_FP8 runs in the prefill mode only (not with TQ_GEMV)");
+  if ((flags & TQ_FP8) && T * (int64_t)L->in >= ((int64_t)1 << 31))
+    return fail(TQ_EINVAL, "the MXFP8 activations (T * in bytes) must stay below 2^31");
   if ((flags & TQ_ROTATE) && L->signs && !aligned(L->signs, 16))
     return fail(TQ_EALIGN, "signs must be 16-byte aligned");
   tq::WsLayout W;
@@ -609,6 +614,40 @@ int trellis_expert_gemm(const tq_trellis_layer* L, const void* x, int64_t T,
     err = tq::launch_piece_reduce(r, s);
     if (err != hipSuccess) return hip_fail(err, "GEMV piece reduction launch");
     return rotate_outputs(L, y, (flags & TQ_COMBINE) ? T : N, s);
+  } else if (flags & TQ_FP8) {
+    err = tq::launch_tf8_prep(xb, T, L->in, (flags & TQ_ROTATE) != 0, L->signs,
+                              at<uint8_t>(ws, W.xa), at<uint8_t>(ws, W.xs), s);
+    if (err != hipSuccess) return hip_fail(err, "MXFP8 activation prep launch");
+    rc = run_route(W, ws, topk_ids, N, L->E, L->out, y_slots, s);
+    if (rc) return rc;
+    tq::TrellisFp8GemmArgs a{};
+    a.layout = L->layout;
+    a.bits = L->bits;
+    a.code_off = L->code_off;
+    a.codes = L->codes;
+    a.codes_bytes = L->codes_bytes;
+    a.scales = L->scales;
+    a.xa = at<uint8_t>(ws, W.xa);
+    a.xa_bytes = (uint32_t)(T * L->in);
+    a.xs = at<uint8_t>(ws, W.xs);
+    a.xs_bytes = (uint32_t)(T * L->in / 32);
+    a.gates = topk_w;
+    a.pairs = at<int32_t>(ws, W.pairs);
+    a.items = at<int32_t>(ws, W.items);
+    a.n_items = at<int32_t>(ws, W.n_items);
+    a.y = y_slots;
+    a.status = at<uint32_t>(ws, W.status);
+    a.E = L->E;
+    a.out = L->out;
+    a.in = L->in;
+    a.topk = topk;
+    a.groups = W.groups;
+    a.max_items = W.max_items;
+    err = time_begin(s);
+    if (err != hipSuccess) return hip_fail(err, "hipEventRecord");
+    err = tq::launch_tf8_gemm(a, s);
+    if (err == hipSuccess) err = time_end(s);
+    if (err != hipSuccess) return hip_fail(err, "FP8 trellis GEMM launch");
   } else {
     err = tq::launch_activation_prep(xb, T, L->in, at<uint32_t>(ws, W.xprep),
                                      at<float2>(ws, W.rowsum), (flags & TQ_ROTATE) != 0,
@@ -667,7 +706,7 @@ int mx_expert_gemm(const MxLayer* L, const void* x, int64_t T, const int32_t* to
                    size_t ws_bytes, void* stream) {
   if (flags & TQ_ROTATE) return fail(TQ_EINVAL, "TQ_ROTATE applies to trellis layers only");
   if ((flags & TQ_FP8) && L->fmt != tq::MX_FP4)
-    return fail(TQ_EINVAL, "TQ_FP8 applies to MXFP4 layers only");
+    return fail(TQ_EINVAL, "TQ_FP8 applies to trellis and MXFP4 layers only");
   if ((flags & TQ_FP8) && (flags & 3u) == TQ_GEMV)
     return fail(TQ_EINVAL, "TQ_FP8 runs in the prefill mode only (not with TQ_GEMV)");
   if ((flags & TQ_FP8) && T * (int64_t)L->in >= ((int64_t)1 << 31))

@@ -8,6 +8,7 @@
 // (a, b) -> (a + b, a - b) with a the lower index; the result is scaled by fp32
 // 0x3DB504F3 and rounded to bf16 nearest-even. No multiply-add is fused (the file is
 // compiled with -ffp-contract=off), so the bits do not depend on scheduling.
+#include "hadamard_lane.h"
 #include "tq_device.h"
 #include "tq_internal.h"
 
@@ -48,28 +49,7 @@ __global__ __launch_bounds__(256) void hadamard128_kernel(const uint16_t* __rest
 #pragma unroll
     for (int j = 0; j < 8; ++j) v[j] = 0.0f;
   }
-  // strides 1, 2, 4 within the lane
-#pragma unroll
-  for (int h = 1; h < 8; h <<= 1) {
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      if ((j & h) == 0) {
-        const float a = v[j], b = v[j + h];
-        v[j] = a + b;
-        v[j + h] = a - b;
-      }
-    }
-  }
-  // strides 8, 16, 32, 64 across lanes l ^ 1, 2, 4, 8 (all lanes take part)
-#pragma unroll
-  for (int d = 1; d < 16; d <<= 1) {
-    const bool upper = (sub & d) != 0;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const float other = __shfl_xor(v[j], d, 64);
-      v[j] = upper ? other - v[j] : v[j] + other;
-    }
-  }
+  fwht128_lane8(v, sub);
   if (!active) return;
   const float scale = __uint_as_float(0x3DB504F3u);
   uint32_t o[4];

@@ -130,6 +130,33 @@ struct TrellisGemmArgs {
 };
 hipError_t launch_trellis_gemm(const TrellisGemmArgs& a, hipStream_t s);
 
+// FP8 trellis prefill (trellis_fp8.hip): MXFP8 activations (codes in the weight decoder's
+// chunk order) times T16 values rounded to E4M3.
+struct TrellisFp8GemmArgs {
+  int layout;             // 0: store order (F2); 1: read order (trellis_repack); 2: F2b units
+  const uint8_t* bits;
+  const int64_t* code_off;
+  const uint32_t* codes;
+  int64_t codes_bytes;
+  const uint16_t* scales;
+  const uint8_t* xa;      // E4M3 codes [T][in] (tf8_prep order)
+  uint32_t xa_bytes;      // < 2^31
+  const uint8_t* xs;      // E8M0 scales [T][in / 32]
+  uint32_t xs_bytes;
+  const float* gates;
+  const int32_t* pairs;
+  const int32_t* items;
+  const int32_t* n_items;
+  float* y;
+  uint32_t* status;
+  int E, out, in, topk, groups, max_items;
+};
+hipError_t launch_tf8_prep(const uint16_t* x, int64_t rows, int n, bool rotate,
+                           const int8_t* signs, uint8_t* codes, uint8_t* scales, hipStream_t s);
+hipError_t launch_tf8_gemm(const TrellisFp8GemmArgs& a, hipStream_t s);
+hipError_t launch_tf8_decode(const uint32_t* codes, int K, int out, int in, int16_t* q,
+                             hipStream_t s);
+
 // Unit formats of the E8M0-scaled stores (mxfp4.hip).
 constexpr int MX_FP4 = 0;     // MXFP4: E2M1 codes, a scale per row and 32 inputs
 constexpr int MX_FP8B32 = 1;  // fp8b32: E4M3 codes, a scale per 32 x 32 block

@@ -238,7 +238,8 @@ def route_bucket(topk_ids, E, ws=None):
 
 
 def trellis_decode(codes, K, out_ch, in_, path=0):
-    """int16 q [out, in] of one unit, via the GEMV (path 0) or prefill (path 1) decoder."""
+    """int16 q [out, in] of one unit, via the GEMV (path 0) or prefill (path 1) decoder; path
+    2 gives the E4M3 codes of the FP8 prefill's decoder."""
     _require_cuda(codes)
     q = torch.empty((out_ch, in_), dtype=torch.int16, device=codes.device)
     check(_lib.load().trellis_decode(_ptr(codes), K, out_ch, in_, _ptr(q), path,
