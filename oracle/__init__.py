@@ -31,6 +31,9 @@ from .routing import route_bucket
 from .gemm import expert_gemm, expert_gemm_values, expert_gemm_exact, combine_slots
 from .ffn import silu, silu_scalar, expert_ffn
 from .fp8b32 import fp8b32_unit_bytes, decode_fp8b32_unit, decode_fp8b32_weight_scalar
+from .codebooks import (MUL1_MULT, PMCGX_MULTS, mul1_value, mul1_value_array, decode_unit_mul1,
+                        decode_unit_mul1_scalar, pmcgx_half_sum, pmcgx_pair_codes,
+                        decode_unit_pmcgx, decode_unit_pmcgx_scalar, pmcgx_values, mul1_e4m3)
 from .mx import (E4M3_MAX, e4m3_all_values, e4m3_round, mx_block_scale, quantize_mxfp8_rows,
                  dequantize_mxfp8_rows, t16_e4m3, t16_e4m3_codes, mxfp8_values)
 

@@ -19,7 +19,8 @@ from multiprocessing import shared_memory
 
 import numpy as np
 
-from . import ffn as _ffn, fpbits as _fpbits, gemm as _gemm, hadamard as _had, mx as _mx8, mxfp4 as _mx, t16 as _t16
+from . import (codebooks as _cb, ffn as _ffn, fpbits as _fpbits, gemm as _gemm, hadamard as _had,
+               mx as _mx8, mxfp4 as _mx, t16 as _t16)
 
 _ARR = {}
 _META = {}
@@ -38,7 +39,7 @@ def _attach(specs, meta):
 
 
 def _layer(prefix):
-    d = {k: _META[prefix + "." + k] for k in ("E", "out", "in", "layout")}
+    d = {k: _META[prefix + "." + k] for k in ("E", "out", "in", "layout", "codebook")}
     for k in ("bits", "code_off", "codes", "scales", "signs", "out_signs"):
         d[k] = _ARR.get(prefix + "." + k)
     return d
@@ -53,9 +54,17 @@ def _trellis_fns(lay, e4m3=False):
             n = lay["out"] * lay["in"] * K // 32
             s = int(lay["code_off"][e]) // 4
             cache.clear()  # one expert at a time: bounded memory
-            decode = _t16.decode_units128 if lay["layout"] == 2 else _t16.decode_unit
-            q = decode(lay["codes"][s:s + n], K, lay["out"], lay["in"])
-            cache[e] = _mx8.t16_e4m3(q) if e4m3 else q.astype(np.float64)
+            words = lay["codes"][s:s + n]
+            cb = lay["codebook"]
+            if cb == 2:    # pmcgx: E4M3 weights by definition (F21)
+                cache[e] = _cb.pmcgx_values(_cb.decode_unit_pmcgx(words, K, lay["out"], lay["in"]))
+            elif cb == 1:  # mul1 (F20)
+                q = _cb.decode_unit_mul1(words, K, lay["out"], lay["in"])
+                cache[e] = _cb.mul1_e4m3(q) if e4m3 else q.astype(np.float64)
+            else:
+                decode = _t16.decode_units128 if lay["layout"] == 2 else _t16.decode_unit
+                q = decode(words, K, lay["out"], lay["in"])
+                cache[e] = _mx8.t16_e4m3(q) if e4m3 else q.astype(np.float64)
         return cache[e]
 
     scales = _fpbits.f16_bits_to_f64(lay["scales"])
@@ -148,6 +157,9 @@ def _layer_arrays(prefix, lay):
               for k in ("bits", "code_off", "codes", "scales", "signs", "out_signs")}
     meta = {prefix + "." + k: int(lay[k]) for k in ("E", "out", "in")}
     meta[prefix + ".layout"] = int(lay.get("layout", 0))
+    meta[prefix + ".codebook"] = int(lay.get("codebook", 0))
+    if meta[prefix + ".codebook"] and meta[prefix + ".layout"] == 2:
+        raise ValueError("the 128-input unit layout is read for T16 layers only")
     return arrays, meta
 
 
