@@ -83,6 +83,23 @@ extern "C" {
                             /* 8 tile columns, back to back                               */
 
 /*
+ * Trellis codebooks: how a state of the bit stream becomes a weight. One per layer (the
+ * exlr8 page, "Stores": all encodes of a layer share its codebook).
+ *   TQ_CODEBOOK_T16    the dsx T16 page's codebook ("How T16 works", item 1; FORMAT F5):
+ *                      16-bit window times 0x3A2F mod 2^16, byte sum minus 255. Every mode.
+ *   TQ_CODEBOOK_MUL1   exlr8's mul1 (FORMAT F20, a reading: 16-bit window times 0x83DCD12D
+ *                      mod 2^32, byte sum minus 510). With TQ_FP8 only: operand E4M3(q/2)
+ *                      with block scale 2.
+ *   TQ_CODEBOOK_PMCGX  exlr8's pmcgx V2 L20 (FORMAT F21, a reading: 20-bit pair windows,
+ *                      multipliers 0xCBAC1FED / 0xBCA14C51, masked fp16 halves summed and
+ *                      rounded to E4M3). With TQ_FP8 only: the E4M3 weights are the operand.
+ * mul1 and pmcgx layers use TQ_LAYOUT_STORE or TQ_LAYOUT_GEMV.
+ */
+#define TQ_CODEBOOK_T16 0
+#define TQ_CODEBOOK_MUL1 1
+#define TQ_CODEBOOK_PMCGX 2
+
+/*
  * A trellis expert layer (FORMAT F1-F7, F12). Expert e's unit holds out*in*K/8 bytes at
  * byte offset code_off[e] of `codes`: 16 x 16 tiles in strip-major order (tile (to, ti)
  * at index to*(in/16)+ti), each tile 8*K little-endian uint32 words, bits read most
@@ -105,6 +122,7 @@ typedef struct tq_trellis_layer {
   int64_t codes_bytes;      /* bytes of `codes` (> 0): a unit must lie inside them         */
   const int8_t* out_signs;  /* device [out]: +-1 signs of the output-side rotation, or NULL  */
                             /* for none (FORMAT F17; out a multiple of 128 when given)     */
+  int32_t codebook;         /* TQ_CODEBOOK_T16 (0), TQ_CODEBOOK_MUL1 or TQ_CODEBOOK_PMCGX  */
 } tq_trellis_layer;
 
 /*
@@ -272,8 +290,11 @@ int route_bucket(const int32_t* topk_ids, int64_t T, int32_t topk, int32_t E,
  * matrix cores receive. Path 0: the decode-batch GEMV's column decoder and signed bytes
  * lo8(m) - 128 and hi8(m) - 128 (q = their sum + 1). Path 1: the prefill GEMM's decoders
  * (each half of a tile column on its own for K = 2 and 3, the whole column for K = 4) and
- * its byte sums q + 255 as f16 subnormals. Path 2: the FP8 prefill's decoder (TQ_FP8,
- * FORMAT F19); q[o][i] then holds the E4M3 code byte (0..255) of the rounded value.
+ * its byte sums q + 255 as f16 subnormals. Paths 2, 3, 4: the FP8 prefill's decoders
+ * (TQ_FP8) of the T16 (FORMAT F19), mul1 (F20) and pmcgx (F21) codebooks; q[o][i] then
+ * holds the E4M3 code byte (0..255) of the operand: E4M3(q) for T16, E4M3(q / 2) for mul1
+ * (the exlr8 page, "Stores": mul1 0x83DCD12D, one weight per state; pmcgx V2 L20
+ * 0xCBAC1FED / 0xBCA14C51, two weights per 20-bit state), the weight itself for pmcgx.
  *   codes  device, out*in*K/8 bytes, 16-byte aligned.   K in {2, 3, 4}.
  *   out    multiple of 16.   in  multiple of 64.
  *   q      device int16 [out][in] (HF orientation: row = output channel), 4-byte aligned.

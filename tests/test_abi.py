@@ -80,6 +80,15 @@ def test_trellis_argument_errors(lib):
     assert _call_trellis(lib, _layer(), flags=32) == _lib.TQ_EINVAL
     # the FP8 variant is a prefill-mode contraction: not with the decode batch
     assert _call_trellis(lib, _layer(), flags=_lib.TQ_FP8 | 1) == _lib.TQ_EINVAL
+    # codebooks: only 0..2; mul1 and pmcgx need TQ_FP8 and a store or read-order layout
+    lay = _layer()
+    lay.codebook = 3
+    assert _call_trellis(lib, lay) == _lib.TQ_EINVAL
+    lay.codebook = _lib.TQ_CODEBOOK_PMCGX
+    assert _call_trellis(lib, lay, flags=_lib.TQ_GEMM) == _lib.TQ_EINVAL
+    assert b"TQ_FP8" in lib.tq_last_error()
+    lay.layout = 2
+    assert _call_trellis(lib, lay, flags=_lib.TQ_FP8) == _lib.TQ_EINVAL
     # TQ_ROTATE reads 16 signs per tile column: the signs must be 16-byte aligned
     assert _call_trellis(lib, _layer(signs=0x1008), flags=_lib.TQ_ROTATE) == _lib.TQ_EALIGN
     assert _call_trellis(lib, _layer(), x=0x1002) == _lib.TQ_EALIGN
@@ -178,7 +187,7 @@ def test_hadamard_decode_route_argument_errors(lib):
     assert lib.trellis_decode(0x1000, 5, 16, 64, 0x1000, 0, None) == _lib.TQ_EINVAL
     assert lib.trellis_decode(0x1000, 2, 17, 64, 0x1000, 0, None) == _lib.TQ_EINVAL
     assert lib.trellis_decode(0x1000, 2, 16, 48, 0x1000, 0, None) == _lib.TQ_EINVAL
-    assert lib.trellis_decode(0x1000, 2, 16, 64, 0x1000, 3, None) == _lib.TQ_EINVAL
+    assert lib.trellis_decode(0x1000, 2, 16, 64, 0x1000, 5, None) == _lib.TQ_EINVAL
     assert lib.trellis_decode(0x1004, 2, 16, 64, 0x1000, 0, None) == _lib.TQ_EALIGN
     assert lib.mxfp4_decode(0x1000, 16, 48, 0x1000, None) == _lib.TQ_EINVAL
     m = _lib.Mxfp4LayerC(4, 128, 5120, 0, 0x1000)

@@ -27,6 +27,7 @@ TQ_GEMM = 2
 TQ_COMBINE = 4
 TQ_ROTATE = 8
 TQ_FP8 = 16
+TQ_CODEBOOK_T16, TQ_CODEBOOK_MUL1, TQ_CODEBOOK_PMCGX = 0, 1, 2
 
 TQ_NOALLOC_SCRATCH_BYTES = 32 << 20
 
@@ -47,6 +48,7 @@ class TrellisLayerC(ctypes.Structure):
         ("signs", ctypes.c_void_p),
         ("codes_bytes", ctypes.c_int64),
         ("out_signs", ctypes.c_void_p),
+        ("codebook", ctypes.c_int32),
     ]
 
 

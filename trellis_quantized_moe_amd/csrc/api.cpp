@@ -294,14 +294,15 @@ int trellis_decode(const uint32_t* codes, int32_t K, int32_t out, int32_t in, in
   if (K < 2 || K > 4) return fail(TQ_EINVAL, "K = %d is not 2, 3 or 4", K);
   if (out <= 0 || out % 16) return fail(TQ_EINVAL, "out = %d is not a positive multiple of 16", out);
   if (in <= 0 || in % 64) return fail(TQ_EINVAL, "in = %d is not a positive multiple of 64", in);
-  if (path < 0 || path > 2) return fail(TQ_EINVAL, "path = %d is not 0, 1 or 2", path);
+  if (path < 0 || path > 4) return fail(TQ_EINVAL, "path = %d is not 0 .. 4", path);
   if (!codes || !q) return fail(TQ_EINVAL, "codes or q is NULL");
   if (!aligned(codes, 16)) return fail(TQ_EALIGN, "codes must be 16-byte aligned");
   if (!aligned(q, 4)) return fail(TQ_EALIGN, "q must be 4-byte aligned");
   int rc = check_device();
   if (rc) return rc;
   hipError_t err =
-      path == 2 ? tq::launch_tf8_decode(codes, K, out, in, q, static_cast<hipStream_t>(stream))
+      path >= 2 ? tq::launch_tf8_decode(codes, K, out, in, q, path - 2,
+                                        static_cast<hipStream_t>(stream))
                 : tq::launch_trellis_decode(codes, K, out, in, q, path,
                                             static_cast<hipStream_t>(stream));
   if (err != hipSuccess) return hip_fail(err, "trellis_decode launch");
@@ -421,6 +422,10 @@ static int check_trellis_layer(const tq_trellis_layer* L) {
                 L->out);
   if (L->out_signs && !aligned(L->out_signs, 4))
     return fail(TQ_EALIGN, "out_signs must be 4-byte aligned");
+  if (L->codebook < TQ_CODEBOOK_T16 || L->codebook > TQ_CODEBOOK_PMCGX)
+    return fail(TQ_EINVAL, "codebook = %d is not TQ_CODEBOOK_T16, _MUL1 or _PMCGX", L->codebook);
+  if (L->codebook != TQ_CODEBOOK_T16 && L->layout == TQ_LAYOUT_UNIT128)
+    return fail(TQ_EINVAL, "TQ_LAYOUT_UNIT128 is read for T16 layers only");
   return TQ_OK;
 }
 
@@ -527,6 +532,8 @@ int trellis_expert_gemm(const tq_trellis_layer* L, const void* x, int64_t T,
     return fail(TQ_EINVAL, "TQ_FP8 runs in the prefill mode only (not with TQ_GEMV)");
   if ((flags & TQ_FP8) && T * (int64_t)L->in >= ((int64_t)1 << 31))
     return fail(TQ_EINVAL, "the MXFP8 activations (T * in bytes) must stay below 2^31");
+  if (L->codebook != TQ_CODEBOOK_T16 && !(flags & TQ_FP8))
+    return fail(TQ_EINVAL, "mul1 and pmcgx layers run on the FP8 matrix cores only (TQ_FP8)");
   if ((flags & TQ_ROTATE) && L->signs && !aligned(L->signs, 16))
     return fail(TQ_EALIGN, "signs must be 16-byte aligned");
   tq::WsLayout W;
@@ -621,6 +628,7 @@ int trellis_expert_gemm(const tq_trellis_layer* L, const void* x, int64_t T,
     rc = run_route(W, ws, topk_ids, N, L->E, L->out, y_slots, s);
     if (rc) return rc;
     tq::TrellisFp8GemmArgs a{};
+    a.codebook = L->codebook;
     a.layout = L->layout;
     a.bits = L->bits;
     a.code_off = L->code_off;
@@ -984,6 +992,8 @@ int trellis_expert_ffn(const tq_trellis_layer* gate_up, const tq_trellis_layer* 
   if (rc) return rc;
   if ((flags & ~(3u | TQ_ROTATE)) != 0 || (flags & 3u) == 3u)
     return fail(TQ_EINVAL, "flags = 0x%x is not valid for the FFN", flags);
+  if (gate_up->codebook != TQ_CODEBOOK_T16 || down->codebook != TQ_CODEBOOK_T16)
+    return fail(TQ_EINVAL, "the FFN runs T16 layers only");
   const int E = gate_up->E, H = gate_up->in, I = gate_up->out / 2;
   if (gate_up->out % 2) return fail(TQ_EINVAL, "gate_up must have an even number of outputs");
   if (down->E != E) return fail(TQ_EINVAL, "the two layers must have the same E");

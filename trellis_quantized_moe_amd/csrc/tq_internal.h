@@ -149,13 +149,14 @@ struct TrellisFp8GemmArgs {
   const int32_t* n_items;
   float* y;
   uint32_t* status;
+  int codebook;           // 0 T16 (F19), 1 mul1 (F20), 2 pmcgx (F21)
   int E, out, in, topk, groups, max_items;
 };
 hipError_t launch_tf8_prep(const uint16_t* x, int64_t rows, int n, bool rotate,
                            const int8_t* signs, uint8_t* codes, uint8_t* scales, hipStream_t s);
 hipError_t launch_tf8_gemm(const TrellisFp8GemmArgs& a, hipStream_t s);
 hipError_t launch_tf8_decode(const uint32_t* codes, int K, int out, int in, int16_t* q,
-                             hipStream_t s);
+                             int codebook, hipStream_t s);
 
 // Unit formats of the E8M0-scaled stores (mxfp4.hip).
 constexpr int MX_FP4 = 0;     // MXFP4: E2M1 codes, a scale per row and 32 inputs

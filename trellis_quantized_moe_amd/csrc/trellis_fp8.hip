@@ -26,10 +26,14 @@
 //        c ^ (r % 8)), with each row's 4 block scales.
 //    Per step and wave: 8 x 2 products (weight block scales 2^0), fp32 accumulation. The
 //    epilogue applies the channel's fp16 scale and the gate and writes each output once.
-// 3. tf8_decode_kernel: the decode hook's path 2, the E4M3 codes of a unit through the same
-//    decoder, in natural order.
+//    Layers with the exlr8 codebooks (F20 mul1, F21 pmcgx; codebook_decode.h) run the same
+//    kernel with their decoder in place of T16's; mul1's operand is E4M3(q / 2) with the
+//    weight block scale 2^1.
+// 3. tf8_decode_kernel: the decode hook's paths 2 (T16), 3 (mul1) and 4 (pmcgx), the E4M3
+//    codes of a unit through the same decoders, in natural order.
 #include "gemm_core.h"
 #include "hadamard_lane.h"
+#include "codebook_decode.h"
 #include "trellis_cols.h"
 
 namespace tq {
@@ -182,9 +186,25 @@ constexpr int tf_step_loads() {
   return 4 + (SCALES ? 1 : 0) + 4 * (K == 3 ? 2 : 1);
 }
 
-template <int K>
+// The 16 E4M3 operand codes of one tile column (in the activations' chunk order) with
+// codebook CB.
+template <int K, int CB>
+__device__ __forceinline__ void fp8_col(const ColWords<K>& cw, uint32_t sel3, uint32_t D[4]) {
+  if constexpr (CB == CB_MUL1) {
+    mul1_col<K>(cw, sel3, D);
+  } else if constexpr (CB == CB_PMCGX) {
+    pmcgx_col<K>(cw, sel3, D);
+  } else {
+    uint32_t M[8];
+    decode_col<K>(cw, sel3, M);
+    e4m3_col<K>(M, D);
+  }
+}
+
+template <int K, int CB>
 __device__ void tf_item(const TrellisFp8GemmArgs& a, TfShared& sh, const uint32_t* unit, int e,
                         int grp, int nrows, int ns) {
+  constexpr int BSCALE = CB == CB_MUL1 ? 128 : 127;  // E8M0 of the weight operand
   constexpr int TW = 8 * K;
   const int tid = threadIdx.x, lane = tid & 63, q = lane >> 4, n = lane & 15;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -264,11 +284,7 @@ __device__ void tf_item(const TrellisFp8GemmArgs& a, TfShared& sh, const uint32_
 #pragma unroll
     for (int s = 0; s < 2; ++s)
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        uint32_t M[8];
-        decode_col<K>(cw[d][s][h], lo.sel3, M);
-        e4m3_col<K>(M, B[s] + 4 * h);
-      }
+      for (int h = 0; h < 2; ++h) fp8_col<K, CB>(cw[d][s][h], lo.sel3, B[s] + 4 * h);
     load_b(d, nxt);  // the registers just decoded, for step kk + 2
     const uint8_t* st = sh.a[kk % TF_STAGES];
     const uint32_t* ss = sh.s[kk % TF_STAGES];
@@ -286,7 +302,7 @@ __device__ void tf_item(const TrellisFp8GemmArgs& a, TfShared& sh, const uint32_
           const i32x8 bv = (i32x8){(int)B[s][0], (int)B[s][1], (int)B[s][2], (int)B[s][3],
                                    (int)B[s][4], (int)B[s][5], (int)B[s][6], (int)B[s][7]};
           acc[mb][s] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, acc[mb][s], 0, 0,
-                                                                        0, sa, 0, 127);
+                                                                        0, sa, 0, BSCALE);
         }
       }
     }
@@ -316,6 +332,7 @@ __device__ void tf_item(const TrellisFp8GemmArgs& a, TfShared& sh, const uint32_
   }
 }
 
+template <int CB>
 __global__ __launch_bounds__(TF_THREADS, 2) void tf8_gemm_kernel(TrellisFp8GemmArgs a) {
   __shared__ TfShared sh;
   int item, grp;
@@ -336,11 +353,11 @@ __global__ __launch_bounds__(TF_THREADS, 2) void tf8_gemm_kernel(TrellisFp8GemmA
   const bool inside = !(off & 15) && off >= 0 &&
                       off <= a.codes_bytes - (int64_t)a.out * a.in / 8 * (K >= 2 && K <= 4 ? K : 0);
   if (K == 2 && inside) {
-    tf_item<2>(a, sh, unit, e, grp, nrows, ns);
+    tf_item<2, CB>(a, sh, unit, e, grp, nrows, ns);
   } else if (K == 3 && inside) {
-    tf_item<3>(a, sh, unit, e, grp, nrows, ns);
+    tf_item<3, CB>(a, sh, unit, e, grp, nrows, ns);
   } else if (K == 4 && inside) {
-    tf_item<4>(a, sh, unit, e, grp, nrows, ns);
+    tf_item<4, CB>(a, sh, unit, e, grp, nrows, ns);
   } else {
     for (int v = threadIdx.x; v < nrows * ns * 16; v += TF_THREADS) {
       const int m = v / (ns * 16), o = grp * 128 + v % (ns * 16);
@@ -353,7 +370,7 @@ __global__ __launch_bounds__(TF_THREADS, 2) void tf8_gemm_kernel(TrellisFp8GemmA
 // ---- decode hook ------------------------------------------------------------------------------
 // One wave per (strip, run of 4 tile columns): lane (g, n) decodes column n of tile g with
 // the GEMM's decoder and writes the 16 E4M3 codes in input order as int16.
-template <int K>
+template <int K, int CB>
 __global__ __launch_bounds__(256) void tf8_decode_kernel(const uint32_t* __restrict__ codes,
                                                          int out, int in, int16_t* __restrict__ q) {
   constexpr int TW = 8 * K;
@@ -366,9 +383,8 @@ __global__ __launch_bounds__(256) void tf8_decode_kernel(const uint32_t* __restr
   const LaneOffsets<K> lo(g, n);
   ColWords<K> cw;
   load_col<K>(codes + (size_t)(strip * n_ti + ti0) * TW, lo, cw);
-  uint32_t M[8], D[4];
-  decode_col<K>(cw, lo.sel3, M);
-  e4m3_col<K>(M, D);
+  uint32_t D[4];
+  fp8_col<K, CB>(cw, lo.sel3, D);
   int16_t* row = q + (size_t)(strip * 16 + n) * in + (ti0 + g) * 16;
 #pragma unroll
   for (int d = 0; d < 4; ++d) {  // D[d] = [c(2d + 8), c(2d), c(2d + 9), c(2d + 1)]
@@ -394,20 +410,36 @@ hipError_t launch_tf8_prep(const uint16_t* x, int64_t rows, int n, bool rotate,
 hipError_t launch_tf8_gemm(const TrellisFp8GemmArgs& a, hipStream_t s) {
   const int blocks = gemm_grid(a.max_items, a.groups);
   if (blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL(tf8_gemm_kernel, dim3(blocks), dim3(TF_THREADS), 0, s, a);
+  if (a.codebook == CB_MUL1)
+    hipLaunchKernelGGL(tf8_gemm_kernel<CB_MUL1>, dim3(blocks), dim3(TF_THREADS), 0, s, a);
+  else if (a.codebook == CB_PMCGX)
+    hipLaunchKernelGGL(tf8_gemm_kernel<CB_PMCGX>, dim3(blocks), dim3(TF_THREADS), 0, s, a);
+  else
+    hipLaunchKernelGGL(tf8_gemm_kernel<CB_T16>, dim3(blocks), dim3(TF_THREADS), 0, s, a);
   return hipGetLastError();
 }
 
+template <int CB>
+static void tf8_decode_launch(const uint32_t* codes, int K, int out, int in, int16_t* q,
+                              int blocks, hipStream_t s) {
+  if (K == 2)
+    hipLaunchKernelGGL((tf8_decode_kernel<2, CB>), dim3(blocks), dim3(256), 0, s, codes, out, in, q);
+  else if (K == 3)
+    hipLaunchKernelGGL((tf8_decode_kernel<3, CB>), dim3(blocks), dim3(256), 0, s, codes, out, in, q);
+  else
+    hipLaunchKernelGGL((tf8_decode_kernel<4, CB>), dim3(blocks), dim3(256), 0, s, codes, out, in, q);
+}
+
 hipError_t launch_tf8_decode(const uint32_t* codes, int K, int out, int in, int16_t* q,
-                             hipStream_t s) {
+                             int codebook, hipStream_t s) {
   const int waves = (out / 16) * (in / 64);
   const int blocks = (waves + 3) / 4;
-  if (K == 2)
-    hipLaunchKernelGGL(tf8_decode_kernel<2>, dim3(blocks), dim3(256), 0, s, codes, out, in, q);
-  else if (K == 3)
-    hipLaunchKernelGGL(tf8_decode_kernel<3>, dim3(blocks), dim3(256), 0, s, codes, out, in, q);
+  if (codebook == CB_MUL1)
+    tf8_decode_launch<CB_MUL1>(codes, K, out, in, q, blocks, s);
+  else if (codebook == CB_PMCGX)
+    tf8_decode_launch<CB_PMCGX>(codes, K, out, in, q, blocks, s);
   else
-    hipLaunchKernelGGL(tf8_decode_kernel<4>, dim3(blocks), dim3(256), 0, s, codes, out, in, q);
+    tf8_decode_launch<CB_T16>(codes, K, out, in, q, blocks, s);
   return hipGetLastError();
 }
 

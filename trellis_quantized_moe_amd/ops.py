@@ -12,7 +12,8 @@ import torch
 
 from . import _lib
 from ._lib import (TQ_AUTO, TQ_COMBINE, TQ_GEMM, TQ_GEMV, TQ_LAYOUT_GEMV,  # noqa: F401
-                   TQ_LAYOUT_STORE, TQ_LAYOUT_UNIT128, TQ_ROTATE, TQ_FP8, check)
+                   TQ_LAYOUT_STORE, TQ_LAYOUT_UNIT128, TQ_ROTATE, TQ_FP8, TQ_CODEBOOK_T16,
+                   TQ_CODEBOOK_MUL1, TQ_CODEBOOK_PMCGX, check)
 
 
 def _ptr(t):
@@ -42,6 +43,7 @@ class TrellisLayer:
     signs: torch.Tensor = None  # int8 [in] rotation signs (TQ_ROTATE), or None
     layout: int = TQ_LAYOUT_STORE
     out_signs: torch.Tensor = None  # int8 [out] output-side rotation signs, or None
+    codebook: int = 0               # TQ_CODEBOOK_T16, _MUL1 or _PMCGX
 
     @classmethod
     def from_host(cls, layer, device="cuda"):
@@ -58,12 +60,13 @@ class TrellisLayer:
             layout=int(layer.get("layout", TQ_LAYOUT_STORE)),
             out_signs=None if out_signs is None else
             torch.from_numpy(np.ascontiguousarray(out_signs, dtype=np.int8)).to(device),
+            codebook=int(layer.get("codebook", 0)),
         )
 
     def with_codes(self, codes):
         """The same layer reading its units from another copy of the code buffer."""
         return TrellisLayer(self.E, self.out, self.in_, self.bits, self.code_off, codes,
-                            self.scales, self.signs, self.layout, self.out_signs)
+                            self.scales, self.signs, self.layout, self.out_signs, self.codebook)
 
     def repacked(self):
         """The same layer with its units copied into TQ_LAYOUT_GEMV (see trellis_repack in
@@ -73,7 +76,8 @@ class TrellisLayer:
         c = self.c_struct()
         check(_lib.load().trellis_repack(ctypes.byref(c), _ptr(dst), _stream(self.codes.device)))
         return TrellisLayer(self.E, self.out, self.in_, self.bits, self.code_off, dst,
-                            self.scales, self.signs, TQ_LAYOUT_GEMV, self.out_signs)
+                            self.scales, self.signs, TQ_LAYOUT_GEMV, self.out_signs,
+                            self.codebook)
 
     def c_struct(self):
         return _lib.TrellisLayerC(self.E, self.out, self.in_, self.layout, self.bits.data_ptr(),
@@ -81,7 +85,8 @@ class TrellisLayer:
                                   self.scales.data_ptr(),
                                   None if self.signs is None else self.signs.data_ptr(),
                                   self.codes.numel() * self.codes.element_size(),
-                                  None if self.out_signs is None else self.out_signs.data_ptr())
+                                  None if self.out_signs is None else self.out_signs.data_ptr(),
+                                  self.codebook)
 
 
 @dataclass
