@@ -83,8 +83,8 @@ def time_graph_steps(torch, graphs, steps, warmup):
     return (time.perf_counter() - t0) / steps
 
 
-GEMV_SOURCES = ["trellis_gemv.hip", "trellis_decode.h", "gemv_plan.h", "gemv_wave.h", "tq_device.h",
-                "tq_internal.h"]
+GEMV_SOURCES = ["trellis_gemv.hip", "trellis_cols.h", "trellis_decode.h", "gemv_plan.h", "gemv_wave.h",
+                "tq_device.h", "tq_internal.h"]
 
 
 def kernel_events(torch, n):
@@ -576,8 +576,7 @@ def counter_summary(run_dirs):
             raise SystemExit("no counter_collection.csv under " + d)
         acc = {}
         for r in csv.DictReader(open(files[0])):
-            k = r["Kernel_Name"].replace("(anonymous namespace)::", "").replace("void ", "")
-            k = k.split("(")[0].split("<")[0].strip().split("::")[-1]
+            k = _short_kernel_name(r["Kernel_Name"])
             acc.setdefault((k, r["Counter_Name"]), []).append(float(r["Counter_Value"]))
         for (k, c), v in acc.items():
             if c not in names:
@@ -590,6 +589,30 @@ def counter_summary(run_dirs):
         n = max(v[1] for v in row.values())
         cells = ["{:,.0f}".format(row[c][0]) if c in row else "" for c in names]
         print("| %s | %d | %s |" % (k, n, " | ".join(cells)))
+
+
+def _short_kernel_name(name):
+    k = name.replace("(anonymous namespace)::", "").replace("void ", "")
+    return k.split("(")[0].split("<")[0].strip().split("::")[-1]
+
+
+def trace_summary(run_dirs):
+    """The library's kernels in rocprofv3 --kernel-trace --stats runs (csv output), as a
+    markdown table: calls and mean / min / max duration per dispatch."""
+    import csv
+    import glob
+    print("| kernel | calls | mean us | min us | max us |")
+    print("|---|---:|---:|---:|---:|")
+    for d in run_dirs:
+        files = glob.glob(os.path.join(d, "**", "*kernel_stats.csv"), recursive=True)
+        if not files:
+            raise SystemExit("no kernel_stats.csv under " + d)
+        for r in csv.DictReader(open(files[0])):
+            if not r["Name"].startswith(("tq::", "void tq::")):
+                continue
+            print("| %s | %s | %.2f | %.2f | %.2f |" % (
+                _short_kernel_name(r["Name"]), r["Calls"], float(r["AverageNs"]) / 1e3,
+                float(r["MinNs"]) / 1e3, float(r["MaxNs"]) / 1e3))
 
 
 def write_traffic(fetch_dir, write_dir, command):
@@ -638,9 +661,14 @@ def main():
                     help="the profiler commands that made the --write-traffic runs")
     ap.add_argument("--counter-summary", nargs="+", metavar="DIR",
                     help="print per-kernel counter means of rocprofv3 csv runs as markdown")
+    ap.add_argument("--trace-summary", nargs="+", metavar="DIR",
+                    help="print the library's kernel durations of rocprofv3 csv runs as markdown")
     args = ap.parse_args()
     if args.counter_summary:
         counter_summary(args.counter_summary)
+        return
+    if args.trace_summary:
+        trace_summary(args.trace_summary)
         return
     if args.write_traffic:
         write_traffic(args.write_traffic[0], args.write_traffic[1], args.traffic_command)
