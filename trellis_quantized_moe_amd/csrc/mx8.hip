@@ -8,13 +8,16 @@
 //    times 2^(127 - b) (exact) are rounded to E4M3 by the hardware conversion (nearest,
 //    ties to even; no value can reach 448). Codes [rows][n], scales [rows][n / 32].
 // 2. mx8_gemm_kernel: a work item is up to 128 routed rows of one expert times one group of
-//    128 output channels over the whole input range, in steps of 128 inputs, on four waves
-//    (2 x 2 over 64 rows x 64 channels). Per step and wave: 4 x 4 products
+//    128 output channels over the whole input range, in steps of 128 inputs, on four waves,
+//    wave w owning channels 32 w .. 32 w + 31 for all rows (so no weight is loaded twice).
+//    Per step and wave: 8 x 2 products
 //    v_mfma_scale_f32_16x16x128_f8f6f4 (A: E4M3 activations with their block scales, B: E2M1
 //    weights with theirs, fp32 accumulation).
 //      - weights: lane (n, q) of a 16-channel block supplies the 32 codes of inputs
 //        32 q .. 32 q + 31 of its channel (16 contiguous bytes, one 16-byte load straight
-//        from the unit) and that block's scale byte, so nothing is decoded;
+//        from the unit) and that block's scale byte, so nothing is decoded; the scale bytes
+//        come 16 at a time (4 steps of the channel's row) every fourth step, since a load's
+//        cost is set by its lanes, not by its bytes;
 //      - activations: the item's gathered rows are loaded into a 4-stage LDS ring two steps
 //        ahead by buffer loads that write LDS (16-byte chunk c of row r at position
 //        c ^ (r % 8)), with each row's 4 block scales; lane (r, q) reads the chunks of
@@ -104,10 +107,12 @@ __device__ __forceinline__ void bare_barrier() {
 }
 
 // Vector-memory instructions a wave issues per step: A chunks (4), the scale rows (waves 0
-// and 1: one each), the weight codes (4) and weight scale bytes (4).
+// and 1: one each) and the weight codes (2); every fourth step (the first of a window of
+// four steps) also the weight scales of the next window (2).
+constexpr int M8_NB = 2;  // 16-channel blocks per wave
 template <bool SCALES>
 constexpr int m8_step_loads() {
-  return 4 + (SCALES ? 1 : 0) + 8;
+  return 4 + (SCALES ? 1 : 0) + M8_NB;
 }
 
 template <int LAYOUT>
@@ -116,7 +121,6 @@ __device__ void m8_item(const Mx8GemmArgs& a, M8Shared& sh, const uint8_t* unit,
   using U = MxUnit<MX_FP4>;
   const int tid = threadIdx.x, lane = tid & 63, q = lane >> 4, n = lane & 15;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = w >> 1, wn = w & 1;
   const int nsteps = a.in / 128;  // a multiple of 4
   const bool scale_loader = w < 2;
 
@@ -147,96 +151,122 @@ __device__ void m8_item(const Mx8GemmArgs& a, M8Shared& sh, const uint8_t* unit,
                                                (uint32_t)(4 * kk), 0, 0);
   };
 
-  // weights: lane (n, q) of block nb: channel o = 128 grp + 64 wn + 16 nb + n (channels past
+  // weights: lane (n, q) of block nb: channel o = 128 grp + 32 w + 16 nb + n (channels past
   // the group read its last one; their outputs are not stored), codes of 32-block 4 kk + q
   const GemmRsrc rb = gemm_rsrc(unit, (uint32_t)U::unit_bytes(a.out, a.in));
-  uint32_t bvo[4], bso[4];
+  uint32_t bvo[M8_NB], bso[M8_NB];
 #pragma unroll
-  for (int nb = 0; nb < 4; ++nb) {
-    const int oc = 64 * wn + 16 * nb + n;
+  for (int nb = 0; nb < M8_NB; ++nb) {
+    const int oc = 32 * w + 16 * nb + n;
     const int o = grp * 128 + (oc < 16 * ns ? oc : 16 * ns - 1);
     bvo[nb] = LAYOUT ? U::packed_at(a.out, a.in, o, q) : U::stored_at(a.in, o, q);
-    bso[nb] = U::scale_at(a.out, a.in, o, q);
+    bso[nb] = U::scale_at(a.out, a.in, o, 0);  // the channel's scale row (16-byte aligned)
   }
   // scalar step offsets of the codes (kb = 4 kk + q: store order 64 kk bytes; read order one
   // chunk per step of the group)
   const uint32_t bstep = LAYOUT ? (uint32_t)(U::packed_at(a.out, a.in, grp * 128, 4) -
                                              U::packed_at(a.out, a.in, grp * 128, 0))
                                 : 64u;
-  u32x4 bc[2][4];
-  uint32_t bs[2][4];
+  u32x4 bc[2][M8_NB];
   auto load_b = [&](int slot, int kk) {
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb) {
+    for (int nb = 0; nb < M8_NB; ++nb)
       bc[slot][nb] = __builtin_amdgcn_raw_buffer_load_b128(rb, bvo[nb], (uint32_t)kk * bstep, 0);
-      bs[slot][nb] = __builtin_amdgcn_raw_buffer_load_b8(rb, bso[nb], (uint32_t)(4 * kk), 0);
-    }
+  };
+  // weight scales by windows of 4 steps: 16 bytes of the channel's scale row (blocks
+  // 16 wi .. 16 wi + 15), one load per block of channels instead of one per step; byte
+  // 4 t + q is the scale of step 4 wi + t for this lane. Two windows alternate.
+  const int nwin = nsteps / 4;
+  u32x4 sw[2][M8_NB];
+  auto load_s = [&](int slot, int wi) {
+    const uint32_t off = 16u * (uint32_t)(wi < nwin ? wi : nwin - 1);
+#pragma unroll
+    for (int nb = 0; nb < M8_NB; ++nb)
+      sw[slot][nb] = __builtin_amdgcn_raw_buffer_load_b128(rb, bso[nb], off, 0);
   };
 
-  f32x4 acc[4][4];
+  f32x4 acc[8][M8_NB];
 #pragma unroll
-  for (int mb = 0; mb < 4; ++mb)
+  for (int mb = 0; mb < 8; ++mb)
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = (f32x4){0.f, 0.f, 0.f, 0.f};
-  int mblocks = (nrows - 64 * wm + 15) / 16;
-  mblocks = mblocks < 0 ? 0 : (mblocks > 4 ? 4 : mblocks);
+    for (int nb = 0; nb < M8_NB; ++nb) acc[mb][nb] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  int mblocks = (nrows + 15) / 16;
+  mblocks = mblocks > 8 ? 8 : mblocks;
 
-  // prologue: steps 0 and 1
+  // prologue: the first scale window, steps 0 and 1
+  load_s(0, 0);
   load_a(0, 0);
   load_b(0, 0);
   load_a(1, 1);
   load_b(1, 1);
 
-  auto step = [&](int kk, int d) {
-    // this wave's loads of step kk have landed (those of kk + 1 may be in flight)
-    if (scale_loader)
-      wait_vmcnt<m8_step_loads<true>()>();
-    else
-      wait_vmcnt<m8_step_loads<false>()>();
+  // step kk, position t = kk % 4 in scale window slot ws; d = code slot
+  auto step = [&](int kk, int d, int t, int ws) {
+    // this wave's loads of step kk have landed (those of kk + 1 may be in flight; the second
+    // step of a window also lets the next window's scales, issued by the first, be in flight)
+    if (t == 1) {
+      if (scale_loader)
+        wait_vmcnt<m8_step_loads<true>() + M8_NB>();
+      else
+        wait_vmcnt<m8_step_loads<false>() + M8_NB>();
+    } else {
+      if (scale_loader)
+        wait_vmcnt<m8_step_loads<true>()>();
+      else
+        wait_vmcnt<m8_step_loads<false>()>();
+    }
     bare_barrier();
+    if (t == 0) load_s(ws ^ 1, kk / 4 + 1);
     const int nxt = kk + 2 < nsteps ? kk + 2 : nsteps - 1;
     load_a((kk + 2) % M8_STAGES, nxt);
     const uint8_t* st = sh.a[kk % M8_STAGES];
     const uint32_t* ss = sh.s[kk % M8_STAGES];
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb) {
+    for (int mb = 0; mb < 8; ++mb) {
       if (mb < mblocks) {
-        const int r = 64 * wm + 16 * mb + n;
+        const int r = 16 * mb + n;
         const u32x4 a0 = *reinterpret_cast<const u32x4*>(st + r * M8_ROW + 16 * (q ^ (r & 7)));
         const u32x4 a1 = *reinterpret_cast<const u32x4*>(st + r * M8_ROW + 16 * ((4 + q) ^ (r & 7)));
         const int sa = (int)((ss[r] >> (8 * q)) & 0xFFu);
         const i32x8 av = (i32x8){(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w,
                                  (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
 #pragma unroll
-        for (int nb = 0; nb < 4; ++nb) {
+        for (int nb = 0; nb < M8_NB; ++nb) {
           const u32x4 b = bc[d][nb];
           const i32x8 bv = (i32x8){(int)b.x, (int)b.y, (int)b.z, (int)b.w, 0, 0, 0, 0};
+          const int sb = (int)((sw[ws][nb][t] >> (8 * q)) & 0xFFu);
           acc[mb][nb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-              av, bv, acc[mb][nb], 0, 4, 0, sa, 0, (int)bs[d][nb]);
+              av, bv, acc[mb][nb], 0, 4, 0, sa, 0, sb);
         }
       }
     }
     load_b(d, nxt);  // the slot just used, for step kk + 2
   };
-  for (int kk = 0; kk < nsteps; kk += 4) {
-    step(kk, 0);
-    step(kk + 1, 1);
-    step(kk + 2, 0);
-    step(kk + 3, 1);
+  for (int kk = 0; kk < nsteps; kk += 8) {
+    step(kk, 0, 0, 0);
+    step(kk + 1, 1, 1, 0);
+    step(kk + 2, 0, 2, 0);
+    step(kk + 3, 1, 3, 0);
+    if (kk + 4 < nsteps) {
+      step(kk + 4, 0, 0, 1);
+      step(kk + 5, 1, 1, 1);
+      step(kk + 6, 0, 2, 1);
+      step(kk + 7, 1, 3, 1);
+    }
   }
   // no load may still be writing this workgroup's LDS when it ends
   wait_vmcnt<0>();
 
 #pragma unroll
-  for (int nb = 0; nb < 4; ++nb) {
-    const int oc = 64 * wn + 16 * nb + n;
+  for (int nb = 0; nb < M8_NB; ++nb) {
+    const int oc = 32 * w + 16 * nb + n;
     if (oc < 16 * ns) {
       const int o = grp * 128 + oc;
 #pragma unroll
-      for (int mb = 0; mb < 4; ++mb) {
+      for (int mb = 0; mb < 8; ++mb) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int row = 64 * wm + 16 * mb + 4 * q + i;
+          const int row = 16 * mb + 4 * q + i;
           if (row < nrows) a.y[(size_t)sh.slot[row] * a.out + o] = acc[mb][nb][i] * sh.gate[row];
         }
       }
