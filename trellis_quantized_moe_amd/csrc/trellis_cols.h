@@ -76,8 +76,11 @@ __device__ __forceinline__ void load_col_buf(Rsrc r, const uint32_t vo[2], uint3
     cw.w[0] = v.x;
     cw.w[1] = v.y;
   } else {
-    cw.w[0] = __builtin_amdgcn_raw_buffer_load_b32(r, vo[0], so, 0);
-    cw.w[1] = __builtin_amdgcn_raw_buffer_load_b32(r, vo[1], so, 0);
+    // words p and p + 1 (k3_column_words: p <= 22, so they are adjacent): one 8-byte load
+    // (4-byte aligned; a load's cost is set by its lanes, not its bytes)
+    const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, vo[0], so, 0);
+    cw.w[0] = v.x;
+    cw.w[1] = v.y;
   }
 }
 

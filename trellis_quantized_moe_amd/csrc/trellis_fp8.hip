@@ -180,10 +180,10 @@ __device__ __forceinline__ void tf_barrier() {
 }
 
 // Vector-memory instructions a wave issues per step: 4 activation chunks, the scale row
-// (waves 0 and 1), the code words (2 strips x 2 runs, two words each at K = 3).
+// (waves 0 and 1), the code words (2 strips x 2 runs, one load each).
 template <int K, bool SCALES>
 constexpr int tf_step_loads() {
-  return 4 + (SCALES ? 1 : 0) + 4 * (K == 3 ? 2 : 1);
+  return 4 + (SCALES ? 1 : 0) + 4;
 }
 
 // The 16 E4M3 operand codes of one tile column (in the activations' chunk order) with

@@ -70,10 +70,10 @@ struct ColWords {
   uint32_t w[K == 2 ? 1 : 2];
 };
 
-// Vector-memory instructions per step and wave: 8 activation loads and the code loads.
+// Vector-memory instructions per step and wave: 8 activation loads and 4 code loads.
 template <int K>
 constexpr int step_loads() {
-  return 8 + 4 * (K == 3 ? 2 : 1);
+  return 8 + 4;
 }
 
 template <int K>
@@ -143,9 +143,10 @@ __device__ __forceinline__ void tg_item(const TrellisGemmArgs& a, TgShared& sh,
         const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(rc, cvo[0], o, 0);
         code[slot][nb].w[0] = v.x;
         code[slot][nb].w[1] = v.y;
-      } else {
-        code[slot][nb].w[0] = __builtin_amdgcn_raw_buffer_load_b32(rc, cvo[0], o, 0);
-        code[slot][nb].w[1] = __builtin_amdgcn_raw_buffer_load_b32(rc, cvo[1], o, 0);
+      } else {  // words p and p + 1 of k3_column_words, adjacent: one 8-byte load
+        const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(rc, cvo[0], o, 0);
+        code[slot][nb].w[0] = v.x;
+        code[slot][nb].w[1] = v.y;
       }
     }
   };
