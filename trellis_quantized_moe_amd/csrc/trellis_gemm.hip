@@ -2,24 +2,29 @@
 //
 // A work item is up to 128 routed rows of one expert times one group of up to 128 output
 // channels, over the whole input range, in steps of 64 inputs (four 16-input tile columns).
-// One workgroup of two waves runs an item; wave w owns output channels 64 w .. 64 w + 63
-// (tile strips 4 w .. 4 w + 3) for all 128 rows, so no weight is decoded twice and no
-// weight passes through LDS:
+// One workgroup of four waves runs an item; wave w owns output channels 32 w .. 32 w + 31
+// (tile strips 2 w, 2 w + 1) for all 128 rows, so no weight is decoded twice and no weight
+// passes through LDS:
 //   - weights: lane (g, n) of a wave (g = lane / 16, n = lane % 16) decodes, for each of
-//     its four strips, the whole tile column g of the step for channel n: 16 weights as
+//     its two strips, the whole tile column g of the step for channel n: 16 weights as
 //     eight f16 byte-sum pairs (trellis_decode.h). Pairs 0..3 are its operand of the
 //     step's first 16x16x32 matrix-core product, pairs 4..7 of the second; the activation
 //     operand is laid out to match, so the k order inside a product is a permutation of
 //     the inputs and the sum is the same.
 //   - activations: the prepared f16 rows (the same pair layout) are gathered straight
 //     from global memory into LDS by buffer loads that write LDS (no registers), into a
-//     ring of three 16 KB stages, two steps ahead. A stage holds 128 rows x 128 bytes in
-//     16-byte chunks, chunk c of row r stored at position c ^ ((r / 2) % 8) of the row,
-//     so the operand reads of one 16-lane group hit 16 different chunk columns.
-//   - codes are loaded two steps ahead into registers.
-// Each step: wait for this wave's loads of the step, one barrier (the partner wave's half
-// of the stage has landed and both waves are done with the stage about to be refilled),
-// start the loads of step + 2, decode, then 8 x 4 x 2 products. The epilogue scales by
+//     ring of three 16 KB stages, two steps ahead; each wave loads 32 of the 128 rows. A
+//     stage holds 128 rows x 128 bytes in 16-byte chunks, chunk c of row r stored at
+//     position c ^ ((r / 2) % 8) of the row, so the operand reads of one 16-lane group hit
+//     16 different chunk columns.
+//   - codes are loaded two steps ahead into registers (one load per strip and step).
+// Three items fit on a compute unit (50 KB of LDS each, 142 registers per lane), so every
+// item of a prefill chunk is resident at once and each SIMD runs three waves, whose decode
+// and matrix-core work overlap. The loads a step needs are few: the cost of a load is set by
+// its lanes, not its bytes.
+// Each step: wait for this wave's loads of the step, one barrier (the other waves' parts
+// of the stage have landed and every wave is done with the stage about to be refilled),
+// start the loads of step + 2, decode, then 8 x 2 x 2 products. The epilogue scales by
 // 2^24, removes 255 * sum(x) per token (the byte-sum offset), applies the channel scale,
 // the gate and the token's 2^-s (the prep's power-of-two scale), and writes each output
 // once.
@@ -32,7 +37,10 @@ namespace tq {
 
 namespace {
 
-constexpr int TG_THREADS = 128;
+constexpr int TG_WAVES = 4;                    // waves per item
+constexpr int TG_THREADS = 64 * TG_WAVES;
+constexpr int TG_NS = 8 / TG_WAVES;            // 16-channel strips per wave
+constexpr int TG_AROWS = GEMM_MT / TG_WAVES;   // activation rows each wave loads per step
 constexpr int TG_STEP = 64;                       // inputs per step
 constexpr int TG_ROW_BYTES = TG_STEP * 2;         // one row of a stage: 128 bytes
 constexpr int TG_STAGE = GEMM_MT * TG_ROW_BYTES;  // 16 KB
@@ -70,10 +78,11 @@ struct ColWords {
   uint32_t w[K == 2 ? 1 : 2];
 };
 
-// Vector-memory instructions per step and wave: 8 activation loads and 4 code loads.
+// Vector-memory instructions per step and wave: the activation loads (rows / 8 of them)
+// and one code load per strip.
 template <int K>
 constexpr int step_loads() {
-  return 8 + 4;
+  return TG_AROWS / 8 + TG_NS;
 }
 
 template <int K>
@@ -86,27 +95,27 @@ __device__ __forceinline__ void tg_item(const TrellisGemmArgs& a, TgShared& sh,
   const int nsteps = a.in / TG_STEP;  // a multiple of 4
   const int n_ti = a.in / 16;
 
-  // activation loads: instruction j of wave w fills rows 64 w + 8 j .. + 7 of a stage; lane l
-  // writes LDS chunk l of the instruction's 1 KB, i.e. row 64 w + 8 j + l / 8, position l % 8,
-  // which holds chunk (l % 8) ^ ((row / 2) % 8) of the row's 128 bytes. Rows past the item
-  // load from beyond the buffer's end (x_bytes < 2^31) and read zeros.
+  // activation loads: instruction j of wave w fills rows TG_AROWS w + 8 j .. + 7 of a stage;
+  // lane l writes LDS chunk l of the instruction's 1 KB, i.e. row TG_AROWS w + 8 j + l / 8,
+  // position l % 8, which holds chunk (l % 8) ^ ((row / 2) % 8) of the row's 128 bytes. Rows
+  // past the item load from beyond the buffer's end (x_bytes < 2^31) and read zeros.
   const GemmRsrc ra = gemm_rsrc(a.xp, a.x_bytes);
-  uint32_t dvo[8];
+  uint32_t dvo[TG_AROWS / 8];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int r = 64 * w + 8 * j + (lane >> 3);
+  for (int j = 0; j < TG_AROWS / 8; ++j) {
+    const int r = TG_AROWS * w + 8 * j + (lane >> 3);
     const int c = (lane & 7) ^ ((r >> 1) & 7);
     dvo[j] = r < nrows ? 2u * (uint32_t)((sh.slot[r] / a.topk) * a.in) + 16u * c : 0x80000000u;
   }
   auto load_a = [&](int kk) {
-    uint8_t* st = sh.a[kk % TG_STAGES] + 64 * w * TG_ROW_BYTES;
+    uint8_t* st = sh.a[kk % TG_STAGES] + TG_AROWS * w * TG_ROW_BYTES;
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
+    for (int j = 0; j < TG_AROWS / 8; ++j)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (LdsPtr)(st + 8 * j * TG_ROW_BYTES), 16,
                                                dvo[j], (uint32_t)(TG_ROW_BYTES * kk), 0, 0);
   };
 
-  // code loads: strip 8 grp + 4 w + nb (strips past the group read its last strip; their
+  // code loads: strip 8 grp + TG_NS w + nb (strips past the group read its last strip; their
   // outputs are never stored), tile column 4 kk + g, channel n of the strip
   const GemmRsrc rc = gemm_rsrc(unit, (uint32_t)((size_t)a.out * a.in * K / 8));
   uint32_t cvo[2] = {0, 0};
@@ -125,17 +134,17 @@ __device__ __forceinline__ void tg_item(const TrellisGemmArgs& a, TgShared& sh,
   const int S = n_ti / 4, nst = a.out / 16;
   const uint32_t base = 4u * run_word(a.layout, 8 * grp, 0, S, nst, TW);
   auto step_off = [&](int kk) { return 4u * run_word(a.layout, 8 * grp, kk, S, nst, TW) - base; };
-  uint32_t strip_off[4];
+  uint32_t strip_off[TG_NS];
 #pragma unroll
-  for (int nb = 0; nb < 4; ++nb) {
-    const int s = 4 * w + nb;
+  for (int nb = 0; nb < TG_NS; ++nb) {
+    const int s = TG_NS * w + nb;
     strip_off[nb] = 4u * run_word(a.layout, 8 * grp + (s < ns ? s : ns - 1), 0, S, nst, TW);
   }
-  ColWords<K> code[2][4];
+  ColWords<K> code[2][TG_NS];
   auto load_codes = [&](int slot, int kk) {
     const uint32_t so = step_off(kk);
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb) {
+    for (int nb = 0; nb < TG_NS; ++nb) {
       const uint32_t o = strip_off[nb] + so;
       if constexpr (K == 2) {
         code[slot][nb].w[0] = __builtin_amdgcn_raw_buffer_load_b32(rc, cvo[0], o, 0);
@@ -151,11 +160,11 @@ __device__ __forceinline__ void tg_item(const TrellisGemmArgs& a, TgShared& sh,
     }
   };
 
-  f32x4 acc[8][4];
+  f32x4 acc[8][TG_NS];
 #pragma unroll
   for (int mb = 0; mb < 8; ++mb)
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    for (int nb = 0; nb < TG_NS; ++nb) acc[mb][nb] = (f32x4){0.f, 0.f, 0.f, 0.f};
   const int mblocks = (nrows + 15) >> 4;
   // operand reads of lane (g, n): row 16 mb + n, chunks 2 g and 2 g + 1 of the step
   const uint32_t rd0 = 128u * n + 16u * ((2 * g) ^ (n >> 1));
@@ -164,11 +173,11 @@ __device__ __forceinline__ void tg_item(const TrellisGemmArgs& a, TgShared& sh,
   // B0 / B1: operand registers of the step's first / second product for each strip (pairs
   // 0..3 / 4..7 of the lane's tile column). For K = 2, 3 the halves are decoded apart, so
   // that each half is decoded while the matrix cores run the other half's products.
-  uint32_t B0[4][4], B1[4][4];
-  auto dec_half = [&](int slot, int h, uint32_t Bh[4][4]) {
+  uint32_t B0[TG_NS][4], B1[TG_NS][4];
+  auto dec_half = [&](int slot, int h, uint32_t Bh[TG_NS][4]) {
     if constexpr (K != 4) {
 #pragma unroll
-      for (int nb = 0; nb < 4; ++nb) {
+      for (int nb = 0; nb < TG_NS; ++nb) {
         const ColWords<K>& c = code[slot][nb];
         prefill_half<K>(c.w[0], c.w[K == 2 ? 0 : 1], row_next(c.w[0]), sel3, h, Bh[nb]);
       }
@@ -176,19 +185,19 @@ __device__ __forceinline__ void tg_item(const TrellisGemmArgs& a, TgShared& sh,
   };
   auto dec_full = [&](int slot) {
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb) {
+    for (int nb = 0; nb < TG_NS; ++nb) {
       const ColWords<K>& c = code[slot][nb];
       prefill_full<K>(c.w[0], c.w[K == 2 ? 0 : 1], row_next(c.w[0]), sel3, B0[nb], B1[nb]);
     }
   };
-  auto products = [&](const uint8_t* st, uint32_t rd, const uint32_t Bh[4][4], auto full_tag) {
+  auto products = [&](const uint8_t* st, uint32_t rd, const uint32_t Bh[TG_NS][4], auto full_tag) {
     constexpr bool FULL = decltype(full_tag)::value;
 #pragma unroll
     for (int mb = 0; mb < 8; ++mb) {
       if (FULL || mb < mblocks) {
         const u32x4 av = *reinterpret_cast<const u32x4*>(st + 2048 * mb + rd);
 #pragma unroll
-        for (int nb = 0; nb < 4; ++nb)
+        for (int nb = 0; nb < TG_NS; ++nb)
           acc[mb][nb] = mfma_f16(av, (u32x4){Bh[nb][0], Bh[nb][1], Bh[nb][2], Bh[nb][3]},
                                  acc[mb][nb]);
       }
@@ -245,9 +254,9 @@ __device__ __forceinline__ void tg_item(const TrellisGemmArgs& a, TgShared& sh,
   wait_vmcnt<0>();
 
 #pragma unroll
-  for (int nb = 0; nb < 4; ++nb) {
-    if (4 * w + nb < ns) {
-      const int o = grp * 128 + 64 * w + 16 * nb + n;
+  for (int nb = 0; nb < TG_NS; ++nb) {
+    if (TG_NS * w + nb < ns) {
+      const int o = grp * 128 + 16 * (TG_NS * w + nb) + n;
       const float sc = f16_bits_to_f32(a.scales[(size_t)e * a.out + o]);
 #pragma unroll
       for (int mb = 0; mb < 8; ++mb) {
@@ -268,7 +277,7 @@ __device__ __forceinline__ void tg_item(const TrellisGemmArgs& a, TgShared& sh,
 
 // One kernel for every width: the decoder is chosen per item from the expert's width byte
 // (the register budget is that of the widest decoder).
-__global__ __launch_bounds__(TG_THREADS, 2) void trellis_gemm_kernel(TrellisGemmArgs a) {
+__global__ __launch_bounds__(TG_THREADS, 3) void trellis_gemm_kernel(TrellisGemmArgs a) {
   __shared__ TgShared sh;
   int item, grp;
   if (!gemm_unit(a.n_items, a.groups, &item, &grp)) return;
