@@ -174,9 +174,14 @@ __device__ __forceinline__ void tf_wait_vmcnt() {
 }
 
 __device__ __forceinline__ void tf_barrier() {
+  // this wave's LDS reads have completed and no instruction moves across: no wave can still
+  // be reading a stage when another wave starts refilling it after the barrier
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt unlimited
+  __builtin_amdgcn_sched_barrier(0);
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
 }
 
 // Vector-memory instructions a wave issues per step: 4 activation chunks, the scale row

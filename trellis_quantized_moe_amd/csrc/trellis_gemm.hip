@@ -68,9 +68,14 @@ __device__ __forceinline__ void wait_vmcnt() {
 // stay in flight; the waits are explicit instead (wait_vmcnt before the barrier). The empty
 // asm statements keep the compiler from moving memory accesses across the barrier.
 __device__ __forceinline__ void bare_barrier() {
+  // this wave's LDS reads have completed and no instruction moves across: no wave can still
+  // be reading a stage when another wave starts refilling it after the barrier
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt unlimited
+  __builtin_amdgcn_sched_barrier(0);
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
 }
 
 template <int K>
