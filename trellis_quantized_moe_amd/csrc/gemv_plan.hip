@@ -398,8 +398,7 @@ __device__ __forceinline__ void rotate_column_f32(float f[16], const uint32_t m[
 
 __device__ __forceinline__ void rotate_column(float f[16], const uint32_t m[16], int c) {
   rotate_column_f32(f, m, c);
-#pragma unroll
-  for (int j = 0; j < 16; ++j) f[j] = __uint_as_float(f32_to_bf16_rne(f[j]) << 16);
+  round_bf16_pairs<16>(f);
 }
 
 // x~ of tile column c of token t as 16 floats (bf16 values), rotated when asked.
@@ -555,8 +554,8 @@ __global__ __launch_bounds__(PLAN_THREADS) void ffn_plan_kernel(PlanArgs gu, Pla
 // scaled by a power of two 2^s, the one that puts its largest magnitude in [2^14, 2^15):
 // every element within 2^31 of that largest one is then exact in f16 (bf16 has 8
 // significant bits, f16 11 above 2^-14), and no token can overflow the f16 range. The
-// token's sum of its f16 values (in a fixed order: 16 values of a column in order, a
-// thread's columns in order, the waves' butterfly, the waves in order) and 2^-s are kept
+// token's sum of its f16 values (in a fixed order: a column's 8 pairs in order, a thread's
+// columns in order, the waves' butterfly, the waves in order) and 2^-s are kept
 // for the epilogue; a token with a non-finite element gets 2^-s = NaN.
 // At most 64 registers (8 waves per SIMD): the kernel waits on memory, so occupancy counts.
 __global__ __launch_bounds__(PLAN_THREADS) __attribute__((amdgpu_waves_per_eu(8, 8)))
@@ -614,18 +613,15 @@ void activation_prep_kernel(PlanArgs a) {
   }
   float sum = 0.0f;
   auto convert = [&](const float f[16], int c) {
+    typedef float f2 __attribute__((ext_vector_type(2)));
     uint32_t P[8];
-    float hf[16];
-#pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      const h2 p = (h2){(_Float16)ldexpf(f[r + 8], e), (_Float16)ldexpf(f[r], e)};
-      P[r] = __builtin_bit_cast(uint32_t, p);
-      hf[r] = (float)p.y;
-      hf[r + 8] = (float)p.x;
-    }
     float cs = 0.0f;
 #pragma unroll
-    for (int q = 0; q < 16; ++q) cs += hf[q];
+    for (int r = 0; r < 8; ++r) {  // one packed conversion and one dot product per pair
+      const h2 p = __builtin_convertvector((f2){ldexpf(f[r + 8], e), ldexpf(f[r], e)}, h2);
+      P[r] = __builtin_bit_cast(uint32_t, p);
+      cs = __builtin_amdgcn_fdot2(p, (h2){(_Float16)1.0f, (_Float16)1.0f}, cs, false);
+    }
     sum += cs;
     uint4* dst = reinterpret_cast<uint4*>(a.xp + (size_t)t * n_ti * 8);
     dst[2 * c] = make_uint4(P[0], P[1], P[2], P[3]);

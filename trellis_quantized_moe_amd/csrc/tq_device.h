@@ -59,6 +59,22 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
   return (u & 0x7FFFFFFFu) > 0x7F800000u ? qnan : rounded;  // a select, not a branch
 }
 
+// Rounds N fp32 values (N even) to bf16, nearest-even, and returns them as fp32 values: one
+// v_cvt_pk_bf16_f32 per pair (finite values round as f32_to_bf16_rne does; a NaN stays a
+// NaN, its payload and sign are not kept).
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+template <int N>
+__device__ __forceinline__ void round_bf16_pairs(float f[N]) {
+#pragma unroll
+  for (int j = 0; j < N; j += 2) {
+    const bf16x2 h = __builtin_convertvector((f32x2){f[j], f[j + 1]}, bf16x2);
+    const uint32_t u = __builtin_bit_cast(uint32_t, h);
+    f[j] = __uint_as_float(u << 16);
+    f[j + 1] = __uint_as_float(u & 0xFFFF0000u);
+  }
+}
+
 // f16 bits of an fp32 value, round to nearest even (v_cvt_f16_f32 in the default mode).
 __device__ __forceinline__ uint32_t f32_to_f16_bits(float f) {
   _Float16 h = (_Float16)f;

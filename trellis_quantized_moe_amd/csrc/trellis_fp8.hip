@@ -78,7 +78,8 @@ __global__ __launch_bounds__(256) void tf8_prep_kernel(const uint16_t* __restric
     fwht128_lane8(v, sub);
     const float scale = __uint_as_float(0x3DB504F3u);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) v[j] = bf16_lo_to_f32(f32_to_bf16_rne(v[j] * scale));
+    for (int j = 0; j < 8; ++j) v[j] = v[j] * scale;
+    round_bf16_pairs<8>(v);
   }
   // the 32-block's largest magnitude (an infinity or NaN makes it +inf): lanes 4c .. 4c + 3
   float amax = 0.0f;
