@@ -144,8 +144,16 @@ WsLayout ws_layout(int64_t T, int topk, int E, int out, int in, uint32_t flags, 
   const int64_t N = T * topk;
   L.groups = (out + 127) / 128;
   L.gemm = use_gemm(T, topk, E, L.groups, flags);
+  // decode-batch GEMV groups: trellis waves take 4 strips (64 channels) when the plan's
+  // wave bound allows it, else 8, as MXFP4 waves do
+  L.vstrips = 8;
+  L.vgroups = L.groups;
+  if (!mxfp4 && gemv_chunk_bound(N, E, (out + 63) / 64, false) <= tq::GEMV_MAX_G) {
+    L.vstrips = 4;
+    L.vgroups = (out + 63) / 64;
+  }
   // a decode batch gives every active expert group and chunk at least one wave of its own
-  if ((flags & 3u) == TQ_AUTO && gemv_chunk_bound(N, E, L.groups, mxfp4) > tq::GEMV_MAX_G)
+  if ((flags & 3u) == TQ_AUTO && gemv_chunk_bound(N, E, L.vgroups, mxfp4) > tq::GEMV_MAX_G)
     L.gemm = true;
   size_t off = 256;  // status word
   if (!L.gemm) {
@@ -473,7 +481,7 @@ static int common_checks(int E, int out, int in, const void* x, int64_t T, const
   *layout = tq::ws_layout(T, topk, E, out, in, flags, mxfp4);
   if ((layout->gemm || !mxfp4) && E > 4096)
     return fail(TQ_EINVAL, "this path supports E <= 4096 (E = %d)", E);
-  if (!layout->gemm && tq::gemv_chunk_bound(T * topk, E, layout->groups, mxfp4) > tq::GEMV_MAX_G)
+  if (!layout->gemm && tq::gemv_chunk_bound(T * topk, E, layout->vgroups, mxfp4) > tq::GEMV_MAX_G)
     return fail(TQ_EINVAL,
                 "decode batches take at most %d (group, chunk) pairs: (E + T*topk/%d) * out/128",
                 tq::GEMV_MAX_G, tq::gemv_rows(mxfp4));
@@ -548,10 +556,10 @@ int trellis_expert_gemm(const tq_trellis_layer* L, const void* x, int64_t T,
   const uint16_t* xb = static_cast<const uint16_t*>(x);
   hipError_t err;
   if (!W.gemm) {
-    const int G = tq::trellis_gemv_grid();
+    const int G = tq::trellis_gemv_grid(W.vstrips);
     if (G <= 0) return fail(TQ_EHIP, "could not size the GEMV grid");
     // launched waves: the plan's target, or one per expert group when that is more
-    const int Gl = (int)std::max<int64_t>(G, tq::gemv_chunk_bound(N, L->E, W.groups, false));
+    const int Gl = (int)std::max<int64_t>(G, tq::gemv_chunk_bound(N, L->E, W.vgroups, false));
     tq::PlanArgs p{};
     p.ids = topk_ids;
     p.N = (int)N;
@@ -561,7 +569,7 @@ int trellis_expert_gemm(const tq_trellis_layer* L, const void* x, int64_t T,
     p.code_off = L->code_off;
     p.codes_bytes = L->codes_bytes;
     p.unit_bytes = (int64_t)L->out * L->in / 8;
-    p.groups = W.groups;
+    p.groups = W.vgroups;
     p.S = L->in / 64;
     p.R = tq::gemv_rows(false);
     p.G = G;
@@ -597,6 +605,7 @@ int trellis_expert_gemm(const tq_trellis_layer* L, const void* x, int64_t T,
     a.in = L->in;
     a.topk = topk;
     a.G = Gl;
+    a.strips = W.vstrips;
     err = time_begin(s);
     if (err != hipSuccess) return hip_fail(err, "hipEventRecord");
     err = tq::launch_trellis_gemv(a, s);
@@ -617,7 +626,7 @@ int trellis_expert_gemm(const tq_trellis_layer* L, const void* x, int64_t T,
     r.combine = (flags & TQ_COMBINE) ? 1 : 0;
     r.xdiv = topk;
     r.qmax = L->in / 256;
-    r.pre = tq::reduce_prefetch(N, L->E, W.groups, G, r.qmax);
+    r.pre = tq::reduce_prefetch(N, L->E, W.vgroups, G, r.qmax);
     err = tq::launch_piece_reduce(r, s);
     if (err != hipSuccess) return hip_fail(err, "GEMV piece reduction launch");
     return rotate_outputs(L, y, (flags & TQ_COMBINE) ? T : N, s);
@@ -1029,8 +1038,9 @@ int trellis_expert_ffn(const tq_trellis_layer* gate_up, const tq_trellis_layer* 
   uint32_t* status = at<uint32_t>(wg, W.gu.status);
   hipError_t err;
   if (!W.gemm) {
-    // 1. both plans and the gate/up activation prep
-    const int G = tq::trellis_gemv_grid();
+    // 1. both plans and the gate/up activation prep (GEMV waves of 8 strips: the down
+    // projection's slots each take their own waves, which 4-strip groups would double)
+    const int G = tq::trellis_gemv_grid(8);
     if (G <= 0) return fail(TQ_EHIP, "could not size the GEMV grid");
     const int Glg = (int)std::max<int64_t>(G, tq::gemv_chunk_bound(N, E, W.gu.groups, false));
     const int Gld = (int)std::max<int64_t>(G, tq::gemv_chunk_bound(N, E, W.dn.groups, false));
@@ -1097,6 +1107,7 @@ int trellis_expert_ffn(const tq_trellis_layer* gate_up, const tq_trellis_layer* 
     a.in = H;
     a.topk = topk;
     a.G = Glg;
+    a.strips = 8;
     err = tq::launch_trellis_gemv(a, s);
     if (err != hipSuccess) return hip_fail(err, "gate/up GEMV launch");
     // 3. SwiGLU, the intermediate's rotation, the down projection's operands

@@ -21,6 +21,9 @@ struct WsLayout {
   size_t info = 0, rec = 0, desc = 0, list = 0, slot_info = 0, prank = 0;
   size_t total = 0;
   int groups = 1, route_blocks = 1, max_items = 0;
+  // decode-batch GEMV: strips per wave (trellis 4 when the plan's wave bound allows, else
+  // 8; MXFP4 8) and the plan's groups of 16 * vstrips output channels
+  int vstrips = 8, vgroups = 1;
   bool gemm = false;
 };
 
@@ -87,9 +90,11 @@ struct TrellisGemvArgs {
   int64_t* partial;     // [in / 256][N][out]: the pieces' exact sums of each slot
   uint32_t x_bytes;     // size of xq in bytes (< 2^31)
   int N, out, in, topk, G;
+  int strips;           // 16-channel strips per wave and plan group: 4 or 8
 };
-// Waves of the trellis GEMV that the GPU holds at once; 0 on a HIP error.
-int trellis_gemv_grid();
+// The trellis GEMV's wave target for waves of `strips` strips (4 or 8): the waves the GPU
+// holds at once, up to 4 (strips = 4) or 2 (strips = 8) per SIMD; 0 on a HIP error.
+int trellis_gemv_grid(int strips);
 hipError_t launch_trellis_gemv(const TrellisGemvArgs& a, hipStream_t s);
 
 struct PieceReduceArgs {

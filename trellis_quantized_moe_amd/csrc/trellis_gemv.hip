@@ -3,8 +3,12 @@
 // One wave is one worker of the plan (see gemv_plan.h): the grid is single-wave workgroups,
 // and wave w streams the one piece the plan gave it, steps s0 .. s1 - 1 of one group of one
 // expert, on its own: no LDS and no barrier, so a wave that waits for memory never holds
-// up another, and its load stream never restarts. A step is 4 tile columns (64 inputs) of
-// the group's 8 strips (128 output channels). Per step and strip, each lane decodes one
+// up another, and its load stream never restarts. A group is NS = 4 or 8 strips (64 or 128
+// output channels); a step is 4 tile columns (64 inputs) of the group's strips. Routed
+// decode batches take NS = 4: the decode is bound by instruction issue, and a SIMD issues
+// VALU and matrix-core instructions faster with four waves to choose from than with two,
+// so the pieces' strips are split over twice the waves (the same pieces, so the same
+// partial sums). Per step and strip, each lane decodes one
 // tile column (16 weights of one output channel) and the wave feeds two 16 x 16 x 64 int8
 // matrix-core operations: the weights as signed bytes (two k positions per weight, see
 // trellis_decode.h), the activations as the high and the low int8 halves of each token's
@@ -34,26 +38,26 @@ namespace {
 // evenly over the SIMDs, which single-wave workgroups leave to the dispatcher.
 constexpr int GEMV_WG_WAVES = 1;
 constexpr int GEMV_THREADS = 64 * GEMV_WG_WAVES;
-constexpr int GEMV_WAVES_PER_SIMD = 3;  // register budget: 168 per lane
+constexpr int GEMV_WAVES_PER_SIMD = 4;  // register budget: 128 per lane
 
 __device__ __forceinline__ void load_x(Rsrc r, uint32_t vo, uint32_t so, u32x4& xa, u32x4& xb) {
   xa = __builtin_amdgcn_raw_buffer_load_b128(r, vo, so, 0);
   xb = __builtin_amdgcn_raw_buffer_load_b128(r, vo + 16, so, 0);
 }
 
-// ---- one step: 4 tile columns of 8 strips ---------------------------------------------
+// ---- one step: 4 tile columns of NS strips ----------------------------------------------
 // cw: this step's code words and xa, xb: its activations; with RELOAD they are reloaded
 // with those D steps later (scalar offsets cso + strip offset, and xso).
-template <int K, bool RELOAD>
-__device__ __forceinline__ void step_body(ColWords<K> (&cw)[8], u32x4& xa, u32x4& xb, Rsrc rc,
+template <int K, int NS, bool RELOAD>
+__device__ __forceinline__ void step_body(ColWords<K> (&cw)[NS], u32x4& xa, u32x4& xb, Rsrc rc,
                                           const uint32_t cvo[2], uint32_t cso,
-                                          const uint32_t sso[8], uint32_t sel3, Rsrc rx,
-                                          uint32_t xvo, uint32_t xso, i32x4 acc[8]) {
+                                          const uint32_t sso[NS], uint32_t sel3, Rsrc rx,
+                                          uint32_t xvo, uint32_t xso, i32x4 acc[NS]) {
   // Every reload goes into the registers of the value it replaces, after that value's last
   // use (the scheduling barriers keep the compiler from hoisting it), so the loop carries
   // its registers without copies, and a copy would wait for the load in flight.
 #pragma unroll
-  for (int s8 = 0; s8 < 8; ++s8) {
+  for (int s8 = 0; s8 < NS; ++s8) {
     uint32_t M[8], B[8];
     decode_col<K>(cw[s8], sel3, M);
     __builtin_amdgcn_sched_barrier(0);
@@ -66,14 +70,15 @@ __device__ __forceinline__ void step_body(ColWords<K> (&cw)[8], u32x4& xa, u32x4
   if (RELOAD) load_x(rx, xvo, xso, xa, xb);
 }
 
-// Steps s0 .. s1 - 1 of output group grp: step st covers tile columns 4 st .. 4 st + 3 (lane
-// group g = lane / 16 takes column 4 st + g) of each of the group's strips. tok = this
-// lane's token, or -1 (zero row: its activation offset lies past the end of the buffer,
-// where buffer loads return 0); half = 0 (high int8 halves) or 1 (low).
-template <int K>
+// Steps s0 .. s1 - 1 of output group grp (strips NS grp .. NS grp + ns - 1): step st covers
+// tile columns 4 st .. 4 st + 3 (lane group g = lane / 16 takes column 4 st + g) of each of
+// the group's strips. tok = this lane's token, or -1 (zero row: its activation offset lies
+// past the end of the buffer, where buffer loads return 0); half = 0 (high int8 halves) or
+// 1 (low).
+template <int K, int NS>
 __device__ __forceinline__ void stream(const TrellisGemvArgs& a, const uint32_t* __restrict__ unit,
                                        int tok, int half, int grp, int ns, int s0, int s1,
-                                       i32x4 acc[8]) {
+                                       i32x4 acc[NS]) {
   constexpr int TW = 8 * K;  // words per tile
   constexpr int D = 2;
   const int lane = threadIdx.x & 63, g = lane >> 4, n = lane & 15;
@@ -82,19 +87,19 @@ __device__ __forceinline__ void stream(const TrellisGemvArgs& a, const uint32_t*
   const LaneOffsets<K> lo(g, n);
   const Rsrc rc = make_rsrc(unit, (uint32_t)((size_t)a.out * a.in * K / 8));
   const uint32_t cvo[2] = {4u * lo.o[0], 4u * lo.o[1]};
-  // byte offsets: run (strip 8 grp + s8, step s0 + st) at cso(st) + sso[s8] (run_word)
+  // byte offsets: run (strip NS grp + s8, step s0 + st) at cso(st) + sso[s8] (run_word)
   const int S = n_ti / 4, nst = a.out / 16;
-  uint32_t sso[8];
+  uint32_t sso[NS];
 #pragma unroll
-  for (int s8 = 0; s8 < 8; ++s8)
-    sso[s8] = 4u * (run_word(a.layout, 8 * grp + (s8 < ns ? s8 : ns - 1), s0, S, nst, TW) -
-                    run_word(a.layout, 8 * grp, s0, S, nst, TW));
+  for (int s8 = 0; s8 < NS; ++s8)
+    sso[s8] = 4u * (run_word(a.layout, NS * grp + (s8 < ns ? s8 : ns - 1), s0, S, nst, TW) -
+                    run_word(a.layout, NS * grp, s0, S, nst, TW));
   const Rsrc rx = make_rsrc(a.xq, a.x_bytes);
   const uint32_t xvo = tok >= 0 ? 32u * (uint32_t)((2 * tok + half) * n_ti + g) : 0x80000000u;
   const uint32_t x0 = 128u * (uint32_t)s0;
   // scalar offsets of step st, clamped to the last step (whose words are read again)
   auto cso = [&](int st) {
-    return 4u * run_word(a.layout, 8 * grp, s0 + (st < last ? st : last), S, nst, TW);
+    return 4u * run_word(a.layout, NS * grp, s0 + (st < last ? st : last), S, nst, TW);
   };
   auto xso = [&](int st) { return x0 + (uint32_t)(st < last ? st : last) * 128u; };
 
@@ -102,78 +107,79 @@ __device__ __forceinline__ void stream(const TrellisGemvArgs& a, const uint32_t*
   // activations (which wait for this lane's token), so the token lookup delays no code
   // load. In the loop, a step's reloads follow its use, so loads complete in the order
   // they are needed.
-  ColWords<K> cw[D][8];
+  ColWords<K> cw[D][NS];
   u32x4 xa[D], xb[D];
 #pragma unroll
   for (int d = 0; d < D; ++d)
 #pragma unroll
-    for (int s8 = 0; s8 < 8; ++s8) load_col_buf<K>(rc, cvo, cso(d) + sso[s8], cw[d][s8]);
+    for (int s8 = 0; s8 < NS; ++s8) load_col_buf<K>(rc, cvo, cso(d) + sso[s8], cw[d][s8]);
 #pragma unroll
   for (int d = 0; d < D; ++d) load_x(rx, xvo, xso(d), xa[d], xb[d]);
 #pragma unroll
-  for (int s8 = 0; s8 < 8; ++s8) acc[s8] = (i32x4){0, 0, 0, 0};
+  for (int s8 = 0; s8 < NS; ++s8) acc[s8] = (i32x4){0, 0, 0, 0};
   int st = 0;
   for (; st + D <= steps; st += D) {
 #pragma unroll
     for (int d = 0; d < D; ++d)
-      step_body<K, true>(cw[d], xa[d], xb[d], rc, cvo, cso(st + d + D), sso, lo.sel3, rx, xvo,
-                         xso(st + d + D), acc);
+      step_body<K, NS, true>(cw[d], xa[d], xb[d], rc, cvo, cso(st + d + D), sso, lo.sel3, rx,
+                             xvo, xso(st + d + D), acc);
   }
   const int rem = steps - st;
 #pragma unroll
   for (int d = 0; d < D - 1; ++d)
     if (d < rem)
-      step_body<K, false>(cw[d], xa[d], xb[d], rc, cvo, 0, sso, lo.sel3, rx, xvo, 0, acc);
+      step_body<K, NS, false>(cw[d], xa[d], xb[d], rc, cvo, 0, sso, lo.sel3, rx, xvo, 0, acc);
 }
 
 // One piece: expert record r, steps s0 .. s1 - 1 of group grp for chunk `chunk` of the
 // expert's slot list (up to 8 routed tokens); exact int64 sums to partial[piece].
-template <int K>
+template <int K, int NS>
 __device__ __forceinline__ void run_piece(const TrellisGemvArgs& a, const PlanRec& r, int grp,
                                           int chunk, int s0, int s1, int piece) {
   const int lane = threadIdx.x & 63, n = lane & 15, g = lane >> 4;
   const int j = n & 7, half = n >> 3;  // this lane's A row: token j of the chunk, its half
-  const int ns = min(8, a.out / 16 - grp * 8);
+  const int ns = min(NS, a.out / 16 - grp * NS);
   const uint32_t* unit = a.codes + r.off / 4;
-  int64_t* dst = a.partial + (size_t)piece * a.N * a.out + grp * 128 + n;
+  int64_t* dst = a.partial + (size_t)piece * a.N * a.out + grp * 16 * NS + n;
   {
     const int c0 = 8 * chunk;
     const int rows = min(8, r.cnt - c0);
     // lanes with j = m hold the slot of token m of the chunk
     const int slot = j < rows ? a.list[r.start + c0 + j] : -1;
-    i32x4 acc[8];
-    stream<K>(a, unit, slot >= 0 ? slot / a.topk : -1, half, grp, ns, s0, s1, acc);
+    i32x4 acc[NS];
+    stream<K, NS>(a, unit, slot >= 0 ? slot / a.topk : -1, half, grp, ns, s0, s1, acc);
     // accumulator element i of lane (g, n) is row 4 g + i: for g < 2 the high half of token
     // 4 g + i, whose low half is in lane + 32
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int m = 4 * g + i;
       const int sm = __shfl(slot, m & 7);
-      int64_t v[8];
+      int64_t v[NS];
 #pragma unroll
-      for (int s8 = 0; s8 < 8; ++s8)
+      for (int s8 = 0; s8 < NS; ++s8)
         v[s8] = (int64_t)acc[s8][i] * 256 + (int64_t)__shfl_xor(acc[s8][i], 32, 64);
       if (g < 2 && m < rows) {
         int64_t* row = dst + (size_t)sm * a.out;
 #pragma unroll
-        for (int s8 = 0; s8 < 8; ++s8)
+        for (int s8 = 0; s8 < NS; ++s8)
           if (s8 < ns) row[s8 * 16] = v[s8];
       }
     }
   }
 }
 
+template <int NS>
 __global__ __launch_bounds__(GEMV_THREADS, GEMV_WAVES_PER_SIMD) void trellis_gemv_kernel(TrellisGemvArgs a) {
   Piece pc;
   const int w = blockIdx.x * GEMV_WG_WAVES + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if (w >= a.G || !load_piece(a.desc, w, pc)) return;  // whole wave
   const PlanRec r = load_rec(a.rec, pc.ai);
   if (r.k == 2)
-    run_piece<2>(a, r, pc.grp, pc.chunk, pc.s0, pc.s1, pc.idx);
+    run_piece<2, NS>(a, r, pc.grp, pc.chunk, pc.s0, pc.s1, pc.idx);
   else if (r.k == 3)
-    run_piece<3>(a, r, pc.grp, pc.chunk, pc.s0, pc.s1, pc.idx);
+    run_piece<3, NS>(a, r, pc.grp, pc.chunk, pc.s0, pc.s1, pc.idx);
   else
-    run_piece<4>(a, r, pc.grp, pc.chunk, pc.s0, pc.s1, pc.idx);
+    run_piece<4, NS>(a, r, pc.grp, pc.chunk, pc.s0, pc.s1, pc.idx);
 }
 
 // ---- decode hook ------------------------------------------------------------------------
@@ -269,27 +275,36 @@ hipError_t launch_trellis_repack(const uint8_t* bits, const int64_t* code_off,
   return hipGetLastError();
 }
 
-int trellis_gemv_grid() {
-  static int cache[64];
+int trellis_gemv_grid(int strips) {
+  static int cache[64][2];
+  const int c = strips == 4 ? 0 : 1;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 0;
-  if (dev >= 0 && dev < 64 && cache[dev]) return cache[dev];
+  if (dev >= 0 && dev < 64 && cache[dev][c]) return cache[dev][c];
   int per_cu = 0, cus = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, trellis_gemv_kernel, GEMV_THREADS, 0) !=
-      hipSuccess)
-    return 0;
+  const hipError_t e =
+      c == 0 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, trellis_gemv_kernel<4>,
+                                                             GEMV_THREADS, 0)
+             : hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, trellis_gemv_kernel<8>,
+                                                             GEMV_THREADS, 0);
+  if (e != hipSuccess) return 0;
   per_cu *= GEMV_WG_WAVES;  // waves
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-  int g = std::min(per_cu, GEMV_TARGET_PER_CU) * cus;
+  int g = std::min(per_cu, c == 0 ? 2 * GEMV_TARGET_PER_CU : GEMV_TARGET_PER_CU) * cus;
   if (g > GEMV_MAX_G) g = GEMV_MAX_G;
   if (g < 1) g = 1;
-  if (dev >= 0 && dev < 64) cache[dev] = g;
+  if (dev >= 0 && dev < 64) cache[dev][c] = g;
   return g;
 }
 
 hipError_t launch_trellis_gemv(const TrellisGemvArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(trellis_gemv_kernel, dim3((a.G + GEMV_WG_WAVES - 1) / GEMV_WG_WAVES),
-                     dim3(GEMV_THREADS), 0, s, a);
+  const dim3 grid((a.G + GEMV_WG_WAVES - 1) / GEMV_WG_WAVES), block(GEMV_THREADS);
+  if (a.strips == 4)
+    hipLaunchKernelGGL(trellis_gemv_kernel<4>, grid, block, 0, s, a);
+  else if (a.strips == 8)
+    hipLaunchKernelGGL(trellis_gemv_kernel<8>, grid, block, 0, s, a);
+  else
+    return hipErrorInvalidValue;
   return hipGetLastError();
 }
 
