@@ -117,8 +117,17 @@ __device__ __forceinline__ void stream(const TrellisGemvArgs& a, const uint32_t*
   for (int d = 0; d < D; ++d) load_x(rx, xvo, xso(d), xa[d], xb[d]);
 #pragma unroll
   for (int s8 = 0; s8 < NS; ++s8) acc[s8] = (i32x4){0, 0, 0, 0};
+  // A SIMD issues for its oldest wave first, so the waves that share it would finish one by
+  // one, the last ones alone and bound by their load latency. The wave's priority drops by
+  // one level per quarter of its piece, so the waves behind get the issue slots and all of
+  // them stream together to the end.
+  const int q1 = steps >> 2, q2 = steps >> 1, q3 = (3 * steps) >> 2;
+  __builtin_amdgcn_s_setprio(3);
   int st = 0;
   for (; st + D <= steps; st += D) {
+    if (st >= q1 && st < q1 + D) __builtin_amdgcn_s_setprio(2);
+    if (st >= q2 && st < q2 + D) __builtin_amdgcn_s_setprio(1);
+    if (st >= q3 && st < q3 + D) __builtin_amdgcn_s_setprio(0);
 #pragma unroll
     for (int d = 0; d < D; ++d)
       step_body<K, NS, true>(cw[d], xa[d], xb[d], rc, cvo, cso(st + d + D), sso, lo.sel3, rx,
