@@ -1038,12 +1038,13 @@ int trellis_expert_ffn(const tq_trellis_layer* gate_up, const tq_trellis_layer* 
   uint32_t* status = at<uint32_t>(wg, W.gu.status);
   hipError_t err;
   if (!W.gemm) {
-    // 1. both plans and the gate/up activation prep (GEMV waves of 8 strips: the down
-    // projection's slots each take their own waves, which 4-strip groups would double)
-    const int G = tq::trellis_gemv_grid(8);
-    if (G <= 0) return fail(TQ_EHIP, "could not size the GEMV grid");
-    const int Glg = (int)std::max<int64_t>(G, tq::gemv_chunk_bound(N, E, W.gu.groups, false));
-    const int Gld = (int)std::max<int64_t>(G, tq::gemv_chunk_bound(N, E, W.dn.groups, false));
+    // 1. both plans and the gate/up activation prep (each projection's GEMV waves take 4
+    // strips when its plan's wave bound allows, else 8: the down projection's slots each
+    // take waves of their own)
+    const int Gg = tq::trellis_gemv_grid(W.gu.vstrips), Gd = tq::trellis_gemv_grid(W.dn.vstrips);
+    if (Gg <= 0 || Gd <= 0) return fail(TQ_EHIP, "could not size the GEMV grid");
+    const int Glg = (int)std::max<int64_t>(Gg, tq::gemv_chunk_bound(N, E, W.gu.vgroups, false));
+    const int Gld = (int)std::max<int64_t>(Gd, tq::gemv_chunk_bound(N, E, W.dn.vgroups, false));
     tq::PlanArgs pg{}, pd{};
     pg.ids = topk_ids;
     pg.N = (int)N;
@@ -1053,10 +1054,10 @@ int trellis_expert_ffn(const tq_trellis_layer* gate_up, const tq_trellis_layer* 
     pg.code_off = gate_up->code_off;
     pg.codes_bytes = gate_up->codes_bytes;
     pg.unit_bytes = (int64_t)2 * I * H / 8;
-    pg.groups = W.gu.groups;
+    pg.groups = W.gu.vgroups;
     pg.S = H / 64;
     pg.R = tq::gemv_rows(false);
-    pg.G = G;
+    pg.G = Gg;
     pg.Gl = Glg;
     pg.info = at<int32_t>(wg, W.gu.info);
     pg.rec = at<tq::PlanRec>(wg, W.gu.rec);
@@ -1080,8 +1081,9 @@ int trellis_expert_ffn(const tq_trellis_layer* gate_up, const tq_trellis_layer* 
     pd.code_off = down->code_off;
     pd.codes_bytes = down->codes_bytes;
     pd.unit_bytes = (int64_t)H * I / 8;
-    pd.groups = W.dn.groups;
+    pd.groups = W.dn.vgroups;
     pd.S = I / 64;
+    pd.G = Gd;
     pd.Gl = Gld;
     pd.info = at<int32_t>(wd, W.dn.info);
     pd.rec = at<tq::PlanRec>(wd, W.dn.rec);
@@ -1107,7 +1109,7 @@ int trellis_expert_ffn(const tq_trellis_layer* gate_up, const tq_trellis_layer* 
     a.in = H;
     a.topk = topk;
     a.G = Glg;
-    a.strips = 8;
+    a.strips = W.gu.vstrips;
     err = tq::launch_trellis_gemv(a, s);
     if (err != hipSuccess) return hip_fail(err, "gate/up GEMV launch");
     // 3. SwiGLU, the intermediate's rotation, the down projection's operands
@@ -1124,7 +1126,7 @@ int trellis_expert_ffn(const tq_trellis_layer* gate_up, const tq_trellis_layer* 
     m.gu.topk = topk;
     m.gu.xdiv = topk;
     m.gu.qmax = H / 256;
-    m.gu.pre = tq::reduce_prefetch(N, E, W.gu.groups, G, m.gu.qmax);
+    m.gu.pre = tq::reduce_prefetch(N, E, W.gu.vgroups, Gg, m.gu.qmax);
     m.gu_out_signs = gate_up->out_signs;
     m.down_signs = down->signs;
     m.N = (int)N;
@@ -1148,6 +1150,7 @@ int trellis_expert_ffn(const tq_trellis_layer* gate_up, const tq_trellis_layer* 
     b.in = I;
     b.topk = 1;
     b.G = Gld;
+    b.strips = W.dn.vstrips;
     err = time_begin(s);
     if (err != hipSuccess) return hip_fail(err, "hipEventRecord");
     err = tq::launch_trellis_gemv(b, s);
@@ -1169,7 +1172,7 @@ int trellis_expert_ffn(const tq_trellis_layer* gate_up, const tq_trellis_layer* 
     r.combine = 1;
     r.xdiv = 1;
     r.qmax = I / 256;
-    r.pre = tq::reduce_prefetch(N, E, W.dn.groups, G, r.qmax);
+    r.pre = tq::reduce_prefetch(N, E, W.dn.vgroups, Gd, r.qmax);
     err = tq::launch_piece_reduce(r, s);
     if (err != hipSuccess) return hip_fail(err, "down reduction launch");
     return rotate_outputs(down, y, T, s);

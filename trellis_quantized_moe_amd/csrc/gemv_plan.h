@@ -59,10 +59,11 @@ constexpr int PLAN_OWN_PIECES = 32;
 // plan's per-cost chunk counts below 2^16 (the host checks groups * (E + N / R) against it).
 constexpr int GEMV_MAX_G = 32768;
 constexpr int PLAN_MAX_BIG = GEMV_MAX_G / PLAN_OWN_PIECES;
-// Waves per compute unit the plan aims for (2 per SIMD). The decode-batch kernels are bound
-// by VALU issue (the decode), not by memory latency: two waves per SIMD keep the VALU busy,
-// and fewer, longer pieces spend less on each wave's setup and on the partial sums that the
-// reduction reads.
+// Waves per compute unit the plan aims for, for waves of 8 strips (2 per SIMD). The trellis
+// decode is bound by instruction issue: fewer, longer pieces spend less on each wave's setup
+// and on the partial sums that the reduction reads, and the routed trellis GEMV doubles the
+// waves by splitting each piece's strips over two of them (4 per SIMD). The MXFP4 GEMV,
+// which waits on memory more than it issues, aims for 3 per SIMD.
 constexpr int GEMV_TARGET_PER_CU = 8;
 
 }  // namespace tq

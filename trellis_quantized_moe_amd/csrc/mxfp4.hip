@@ -102,6 +102,7 @@ __global__ __launch_bounds__(256) void mxfp4_decode_kernel(const uint8_t* __rest
 // At the end the wave stores its accumulators as the piece's partial sums.
 constexpr int MX_THREADS = 64;
 constexpr int MX_WAVES_PER_SIMD = 3;  // MXFP4; fp8b32 (twice the code registers) 2
+constexpr int MX_GEMV_TARGET_PER_CU = 12;
 
 template <int FMT>
 struct MxStep {
@@ -222,7 +223,14 @@ __device__ __forceinline__ void mx_stream(const Mxfp4GemvArgs& a, MxShared& sh, 
   for (int s8 = 0; s8 < 8; ++s8) acc[s8] = (f32x4){0.f, 0.f, 0.f, 0.f};
   // this lane's scale byte of strip 0: step k of the block at + 4 k, block g of the step
   const int sbase = U::kFp8 ? g : 16 * n + g;
+  // the wave's issue priority drops by quarters of its piece, so that the waves sharing a
+  // SIMD stream together to the end (the SIMD otherwise issues for its oldest wave first)
+  const int q1 = steps >> 2, q2 = steps >> 1, q3 = (3 * steps) >> 2;
+  __builtin_amdgcn_s_setprio(3);
   for (int blk = 0; blk < steps; blk += 4) {
+    if (blk >= q1 && blk < q1 + 4) __builtin_amdgcn_s_setprio(2);
+    if (blk >= q2 && blk < q2 + 4) __builtin_amdgcn_s_setprio(1);
+    if (blk >= q3 && blk < q3 + 4) __builtin_amdgcn_s_setprio(0);
     const int buf = (blk >> 2) & 1;
     if constexpr (U::kFp8) {
       if (lane < 4) *reinterpret_cast<u32x4*>(&sh.sc[buf][16 * lane]) = sa;
@@ -441,7 +449,9 @@ int mxfp4_gemv_grid(int fmt) {
           : hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, mxfp4_gemv_kernel<MX_FP4>, MX_THREADS, 0);
   if (e != hipSuccess) return 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-  int g = std::min(per_cu, GEMV_TARGET_PER_CU) * cus;
+  // the MXFP4 GEMV waits on memory more than it issues: as many waves as its registers
+  // allow (3 per SIMD; fp8b32 2), up to 3 per SIMD
+  int g = std::min(per_cu, MX_GEMV_TARGET_PER_CU) * cus;
   if (g > GEMV_MAX_G) g = GEMV_MAX_G;
   if (g < 1) g = 1;
   if (dev >= 0 && dev < 64) cache[fmt][dev] = g;
