@@ -73,11 +73,23 @@ __device__ __forceinline__ int small_div(int n, int d, float rd) {
 }
 
 // Pieces per group for a step cost k under the per-wave cost bound T (T >= k): the steps
-// S split into pieces of at most floor(T / k) steps. The quotient is taken in fp32, exact
-// here (S <= 2^15, and a non-integer S / per is at least 1 / S away from an integer).
+// S split into pieces of at most per = floor(T / k) steps, ceil(S / per) =
+// floor((S + per - 1) / per), by small_div with the hardware reciprocal (its error is an
+// ulp or two, and S + per - 1 < 2^22 here: S <= 2^15).
 __device__ __forceinline__ int pieces_for(int S, int T, int k) {
   const int per = T / k;
-  return (int)__builtin_ceilf((float)S / (float)per);
+  return small_div(S + per - 1, per, __builtin_amdgcn_rcpf((float)per));
+}
+
+// The smallest v over the wave's 64 lanes (all active): DPP within each row of 16 lanes,
+// then the four rows' results read out.
+__device__ __forceinline__ int wave_min(int v) {
+  v = min(v, __builtin_amdgcn_mov_dpp(v, 0xB1, 0xF, 0xF, true));   // quad_perm [1, 0, 3, 2]
+  v = min(v, __builtin_amdgcn_mov_dpp(v, 0x4E, 0xF, 0xF, true));   // quad_perm [2, 3, 0, 1]
+  v = min(v, __builtin_amdgcn_mov_dpp(v, 0x141, 0xF, 0xF, true));  // row_half_mirror
+  v = min(v, __builtin_amdgcn_mov_dpp(v, 0x140, 0xF, 0xF, true));  // row_mirror
+  return min(min(__builtin_amdgcn_readlane(v, 0), __builtin_amdgcn_readlane(v, 16)),
+             min(__builtin_amdgcn_readlane(v, 32), __builtin_amdgcn_readlane(v, 48)));
 }
 
 // The plan is one block of PLAN_THREADS threads; each phase gives a thread about one slot
@@ -95,6 +107,7 @@ __device__ void plan_block(const PlanArgs& a) {
   const int tid = threadIdx.x;
   const int N = a.N, E = a.E, S = a.S, groups = a.groups;
   const bool in_regs = N <= PLAN_THREADS * PLAN_R;
+  const int rsh = 31 - __builtin_clz(a.R);  // R is a power of two: chunks by a shift
   const int per = (E + PLAN_THREADS - 1) / PLAN_THREADS;  // experts per thread, <= PLAN_PER
 
   // all route and descriptor loads are issued before any is used (indices clamped; slots
@@ -170,7 +183,7 @@ __device__ void plan_block(const PlanArgs& a) {
     cnt[j] = mine(j) ? s_start[e0 + j] : 0;
     sv[0] += cnt[j];
     if (cnt[j] > 0 && kk[j] > 0) {
-      const int nch = (cnt[j] + a.R - 1) / a.R;
+      const int nch = (cnt[j] + a.R - 1) >> rsh;
       sv[kk[j] >= 3 ? 2 : 1] += (kk[j] & 1) ? nch : (nch << 16);
       sv[3] += 1;
     }
@@ -195,8 +208,7 @@ __device__ void plan_block(const PlanArgs& a) {
         if (tot[k]) waves += (int64_t)tot[k] * pieces_for(S, T, k);
       if (waves * groups <= target) best = T;
     }
-#pragma unroll
-    for (int d = 32; d >= 1; d >>= 1) best = min(best, __shfl_xor(best, d, 64));
+    best = wave_min(best);
     if ((tid & 63) == 0 && best != 0x7FFFFFFF) atomicMin(&s_T, best);
   }
   lds_barrier();
@@ -232,7 +244,7 @@ __device__ void plan_block(const PlanArgs& a) {
         r.np = W;
         a.rec[sa] = r;
         const int base = S / W, rem = S - base * W;
-        const int nch = (cnt[j] + a.R - 1) / a.R;
+        const int nch = (cnt[j] + a.R - 1) >> rsh;
         if (groups * nch * W <= PLAN_OWN_PIECES) {
           for (int grp = 0, q = wb; grp < groups; ++grp) {
             for (int c = 0; c < nch; ++c) {

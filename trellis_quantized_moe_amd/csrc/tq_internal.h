@@ -49,7 +49,8 @@ struct PlanArgs {
   int64_t unit_bytes;       // MXFP4: expert e's unit is at e * unit_bytes; trellis: a
                             // unit's bytes per bit of width (out * in / 8)
   int groups, S;            // output groups per expert, steps per group (in / 64)
-  int R;                    // routed slots one wave takes at most (a chunk of a slot list)
+  int R;                    // routed slots one wave takes at most (a chunk of a slot
+                            // list): a power of two
   int G;                    // the split's wave target
   int Gl;                   // launched GEMV waves (desc entries written)
   int32_t* info;            // [0] active experts, [1] waves with work, [2] cost bound T,
