@@ -144,16 +144,9 @@ WsLayout ws_layout(int64_t T, int topk, int E, int out, int in, uint32_t flags, 
   const int64_t N = T * topk;
   L.groups = (out + 127) / 128;
   L.gemm = use_gemm(T, topk, E, L.groups, flags);
-  // decode-batch GEMV groups: trellis waves take 4 strips (64 channels) when the plan's
-  // wave bound allows it, else 8, as MXFP4 waves do
-  L.vstrips = 8;
-  L.vgroups = L.groups;
-  if (!mxfp4 && gemv_chunk_bound(N, E, (out + 63) / 64, false) <= tq::GEMV_MAX_G) {
-    L.vstrips = 4;
-    L.vgroups = (out + 63) / 64;
-  }
-  // a decode batch gives every active expert group and chunk at least one wave of its own
-  if ((flags & 3u) == TQ_AUTO && gemv_chunk_bound(N, E, L.vgroups, mxfp4) > tq::GEMV_MAX_G)
+  L.vstrips = mxfp4 ? 8 : 4;  // trellis decode GEMV: two 4-strip waves per piece
+  // a decode batch gives every active expert group and chunk at least one piece of its own
+  if ((flags & 3u) == TQ_AUTO && gemv_chunk_bound(N, E, L.groups, mxfp4) > tq::GEMV_MAX_G)
     L.gemm = true;
   size_t off = 256;  // status word
   if (!L.gemm) {
@@ -481,7 +474,7 @@ static int common_checks(int E, int out, int in, const void* x, int64_t T, const
   *layout = tq::ws_layout(T, topk, E, out, in, flags, mxfp4);
   if ((layout->gemm || !mxfp4) && E > 4096)
     return fail(TQ_EINVAL, "this path supports E <= 4096 (E = %d)", E);
-  if (!layout->gemm && tq::gemv_chunk_bound(T * topk, E, layout->vgroups, mxfp4) > tq::GEMV_MAX_G)
+  if (!layout->gemm && tq::gemv_chunk_bound(T * topk, E, layout->groups, mxfp4) > tq::GEMV_MAX_G)
     return fail(TQ_EINVAL,
                 "decode batches take at most %d (group, chunk) pairs: (E + T*topk/%d) * out/128",
                 tq::GEMV_MAX_G, tq::gemv_rows(mxfp4));
@@ -559,7 +552,7 @@ int trellis_expert_gemm(const tq_trellis_layer* L, const void* x, int64_t T,
     const int G = tq::trellis_gemv_grid(W.vstrips);
     if (G <= 0) return fail(TQ_EHIP, "could not size the GEMV grid");
     // launched waves: the plan's target, or one per expert group when that is more
-    const int Gl = (int)std::max<int64_t>(G, tq::gemv_chunk_bound(N, L->E, W.vgroups, false));
+    const int Gl = (int)std::max<int64_t>(G, tq::gemv_chunk_bound(N, L->E, W.groups, false));
     tq::PlanArgs p{};
     p.ids = topk_ids;
     p.N = (int)N;
@@ -569,7 +562,7 @@ int trellis_expert_gemm(const tq_trellis_layer* L, const void* x, int64_t T,
     p.code_off = L->code_off;
     p.codes_bytes = L->codes_bytes;
     p.unit_bytes = (int64_t)L->out * L->in / 8;
-    p.groups = W.vgroups;
+    p.groups = W.groups;
     p.S = L->in / 64;
     p.R = tq::gemv_rows(false);
     p.G = G;
@@ -626,7 +619,7 @@ int trellis_expert_gemm(const tq_trellis_layer* L, const void* x, int64_t T,
     r.combine = (flags & TQ_COMBINE) ? 1 : 0;
     r.xdiv = topk;
     r.qmax = L->in / 256;
-    r.pre = tq::reduce_prefetch(N, L->E, W.vgroups, G, r.qmax);
+    r.pre = tq::reduce_prefetch(N, L->E, W.groups, G, r.qmax);
     err = tq::launch_piece_reduce(r, s);
     if (err != hipSuccess) return hip_fail(err, "GEMV piece reduction launch");
     return rotate_outputs(L, y, (flags & TQ_COMBINE) ? T : N, s);
@@ -1038,13 +1031,11 @@ int trellis_expert_ffn(const tq_trellis_layer* gate_up, const tq_trellis_layer* 
   uint32_t* status = at<uint32_t>(wg, W.gu.status);
   hipError_t err;
   if (!W.gemm) {
-    // 1. both plans and the gate/up activation prep (each projection's GEMV waves take 4
-    // strips when its plan's wave bound allows, else 8: the down projection's slots each
-    // take waves of their own)
+    // 1. both plans and the gate/up activation prep
     const int Gg = tq::trellis_gemv_grid(W.gu.vstrips), Gd = tq::trellis_gemv_grid(W.dn.vstrips);
     if (Gg <= 0 || Gd <= 0) return fail(TQ_EHIP, "could not size the GEMV grid");
-    const int Glg = (int)std::max<int64_t>(Gg, tq::gemv_chunk_bound(N, E, W.gu.vgroups, false));
-    const int Gld = (int)std::max<int64_t>(Gd, tq::gemv_chunk_bound(N, E, W.dn.vgroups, false));
+    const int Glg = (int)std::max<int64_t>(Gg, tq::gemv_chunk_bound(N, E, W.gu.groups, false));
+    const int Gld = (int)std::max<int64_t>(Gd, tq::gemv_chunk_bound(N, E, W.dn.groups, false));
     tq::PlanArgs pg{}, pd{};
     pg.ids = topk_ids;
     pg.N = (int)N;
@@ -1054,7 +1045,7 @@ int trellis_expert_ffn(const tq_trellis_layer* gate_up, const tq_trellis_layer* 
     pg.code_off = gate_up->code_off;
     pg.codes_bytes = gate_up->codes_bytes;
     pg.unit_bytes = (int64_t)2 * I * H / 8;
-    pg.groups = W.gu.vgroups;
+    pg.groups = W.gu.groups;
     pg.S = H / 64;
     pg.R = tq::gemv_rows(false);
     pg.G = Gg;
@@ -1081,7 +1072,7 @@ int trellis_expert_ffn(const tq_trellis_layer* gate_up, const tq_trellis_layer* 
     pd.code_off = down->code_off;
     pd.codes_bytes = down->codes_bytes;
     pd.unit_bytes = (int64_t)H * I / 8;
-    pd.groups = W.dn.vgroups;
+    pd.groups = W.dn.groups;
     pd.S = I / 64;
     pd.G = Gd;
     pd.Gl = Gld;
@@ -1126,7 +1117,7 @@ int trellis_expert_ffn(const tq_trellis_layer* gate_up, const tq_trellis_layer* 
     m.gu.topk = topk;
     m.gu.xdiv = topk;
     m.gu.qmax = H / 256;
-    m.gu.pre = tq::reduce_prefetch(N, E, W.gu.vgroups, Gg, m.gu.qmax);
+    m.gu.pre = tq::reduce_prefetch(N, E, W.gu.groups, Gg, m.gu.qmax);
     m.gu_out_signs = gate_up->out_signs;
     m.down_signs = down->signs;
     m.N = (int)N;
@@ -1172,7 +1163,7 @@ int trellis_expert_ffn(const tq_trellis_layer* gate_up, const tq_trellis_layer* 
     r.combine = 1;
     r.xdiv = 1;
     r.qmax = I / 256;
-    r.pre = tq::reduce_prefetch(N, E, W.dn.vgroups, Gd, r.qmax);
+    r.pre = tq::reduce_prefetch(N, E, W.dn.groups, Gd, r.qmax);
     err = tq::launch_piece_reduce(r, s);
     if (err != hipSuccess) return hip_fail(err, "down reduction launch");
     return rotate_outputs(down, y, T, s);

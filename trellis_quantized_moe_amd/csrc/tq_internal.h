@@ -21,9 +21,7 @@ struct WsLayout {
   size_t info = 0, rec = 0, desc = 0, list = 0, slot_info = 0, prank = 0;
   size_t total = 0;
   int groups = 1, route_blocks = 1, max_items = 0;
-  // decode-batch GEMV: strips per wave (trellis 4 when the plan's wave bound allows, else
-  // 8; MXFP4 8) and the plan's groups of 16 * vstrips output channels
-  int vstrips = 8, vgroups = 1;
+  int vstrips = 8;  // decode-batch GEMV strips per wave: trellis 4, MXFP4 8
   bool gemm = false;
 };
 
@@ -90,11 +88,13 @@ struct TrellisGemvArgs {
   const int32_t* list;
   int64_t* partial;     // [in / 256][N][out]: the pieces' exact sums of each slot
   uint32_t x_bytes;     // size of xq in bytes (< 2^31)
-  int N, out, in, topk, G;
-  int strips;           // 16-channel strips per wave and plan group: 4 or 8
+  int N, out, in, topk;
+  int G;                // pieces (desc entries) launched
+  int strips;           // 16-channel strips per wave: 4 (two waves per piece) or 8
 };
-// The trellis GEMV's wave target for waves of `strips` strips (4 or 8): the waves the GPU
-// holds at once, up to 4 (strips = 4) or 2 (strips = 8) per SIMD; 0 on a HIP error.
+// The trellis GEMV's piece target (the plan's G) for waves of `strips` strips (4 or 8): the
+// waves the GPU holds at once, up to 4 (strips = 4) or 2 (strips = 8) per SIMD, over the
+// waves per piece; 0 on a HIP error.
 int trellis_gemv_grid(int strips);
 hipError_t launch_trellis_gemv(const TrellisGemvArgs& a, hipStream_t s);
 

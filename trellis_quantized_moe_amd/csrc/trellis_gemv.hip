@@ -3,12 +3,12 @@
 // One wave is one worker of the plan (see gemv_plan.h): the grid is single-wave workgroups,
 // and wave w streams the one piece the plan gave it, steps s0 .. s1 - 1 of one group of one
 // expert, on its own: no LDS and no barrier, so a wave that waits for memory never holds
-// up another, and its load stream never restarts. A group is NS = 4 or 8 strips (64 or 128
-// output channels); a step is 4 tile columns (64 inputs) of the group's strips. Routed
-// decode batches take NS = 4: the decode is bound by instruction issue, and a SIMD issues
-// VALU and matrix-core instructions faster with four waves to choose from than with two,
-// so the pieces' strips are split over twice the waves (the same pieces, so the same
-// partial sums). Per step and strip, each lane decodes one
+// up another, and its load stream never restarts. A plan group is 8 strips (128 output
+// channels), and a wave takes NS = 4 or 8 of them: with NS = 4 two waves (wave 2 q + h
+// takes strips 4 h .. 4 h + 3) share piece q, the same pieces and so the same partial sums
+// over twice the waves. The decode is bound by instruction issue, and a SIMD issues VALU
+// and matrix-core instructions faster with four waves to choose from than with two. A step
+// is 4 tile columns (64 inputs) of the wave's strips. Per step and strip, each lane decodes one
 // tile column (16 weights of one output channel) and the wave feeds two 16 x 16 x 64 int8
 // matrix-core operations: the weights as signed bytes (two k positions per weight, see
 // trellis_decode.h), the activations as the high and the low int8 halves of each token's
@@ -70,14 +70,13 @@ __device__ __forceinline__ void step_body(ColWords<K> (&cw)[NS], u32x4& xa, u32x
   if (RELOAD) load_x(rx, xvo, xso, xa, xb);
 }
 
-// Steps s0 .. s1 - 1 of output group grp (strips NS grp .. NS grp + ns - 1): step st covers
-// tile columns 4 st .. 4 st + 3 (lane group g = lane / 16 takes column 4 st + g) of each of
-// the group's strips. tok = this lane's token, or -1 (zero row: its activation offset lies
+// Steps s0 .. s1 - 1 of strips t0 .. t0 + ns - 1: step st covers tile columns 4 st .. 4 st + 3
+// (lane group g = lane / 16 takes column 4 st + g) of each strip. tok = this lane's token, or -1 (zero row: its activation offset lies
 // past the end of the buffer, where buffer loads return 0); half = 0 (high int8 halves) or
 // 1 (low).
 template <int K, int NS>
 __device__ __forceinline__ void stream(const TrellisGemvArgs& a, const uint32_t* __restrict__ unit,
-                                       int tok, int half, int grp, int ns, int s0, int s1,
+                                       int tok, int half, int t0, int ns, int s0, int s1,
                                        i32x4 acc[NS]) {
   constexpr int TW = 8 * K;  // words per tile
   constexpr int D = 2;
@@ -87,19 +86,19 @@ __device__ __forceinline__ void stream(const TrellisGemvArgs& a, const uint32_t*
   const LaneOffsets<K> lo(g, n);
   const Rsrc rc = make_rsrc(unit, (uint32_t)((size_t)a.out * a.in * K / 8));
   const uint32_t cvo[2] = {4u * lo.o[0], 4u * lo.o[1]};
-  // byte offsets: run (strip NS grp + s8, step s0 + st) at cso(st) + sso[s8] (run_word)
+  // byte offsets: run (strip t0 + s8, step s0 + st) at cso(st) + sso[s8] (run_word)
   const int S = n_ti / 4, nst = a.out / 16;
   uint32_t sso[NS];
 #pragma unroll
   for (int s8 = 0; s8 < NS; ++s8)
-    sso[s8] = 4u * (run_word(a.layout, NS * grp + (s8 < ns ? s8 : ns - 1), s0, S, nst, TW) -
-                    run_word(a.layout, NS * grp, s0, S, nst, TW));
+    sso[s8] = 4u * (run_word(a.layout, t0 + (s8 < ns ? s8 : ns - 1), s0, S, nst, TW) -
+                    run_word(a.layout, t0, s0, S, nst, TW));
   const Rsrc rx = make_rsrc(a.xq, a.x_bytes);
   const uint32_t xvo = tok >= 0 ? 32u * (uint32_t)((2 * tok + half) * n_ti + g) : 0x80000000u;
   const uint32_t x0 = 128u * (uint32_t)s0;
   // scalar offsets of step st, clamped to the last step (whose words are read again)
   auto cso = [&](int st) {
-    return 4u * run_word(a.layout, NS * grp, s0 + (st < last ? st : last), S, nst, TW);
+    return 4u * run_word(a.layout, t0, s0 + (st < last ? st : last), S, nst, TW);
   };
   auto xso = [&](int st) { return x0 + (uint32_t)(st < last ? st : last) * 128u; };
 
@@ -140,23 +139,23 @@ __device__ __forceinline__ void stream(const TrellisGemvArgs& a, const uint32_t*
       step_body<K, NS, false>(cw[d], xa[d], xb[d], rc, cvo, 0, sso, lo.sel3, rx, xvo, 0, acc);
 }
 
-// One piece: expert record r, steps s0 .. s1 - 1 of group grp for chunk `chunk` of the
-// expert's slot list (up to 8 routed tokens); exact int64 sums to partial[piece].
+// One piece: expert record r, steps s0 .. s1 - 1 of strips t0 .. t0 + ns - 1 (ns >= 1) for
+// chunk `chunk` of the expert's slot list (up to 8 routed tokens); exact int64 sums to
+// partial[piece].
 template <int K, int NS>
-__device__ __forceinline__ void run_piece(const TrellisGemvArgs& a, const PlanRec& r, int grp,
-                                          int chunk, int s0, int s1, int piece) {
+__device__ __forceinline__ void run_piece(const TrellisGemvArgs& a, const PlanRec& r, int t0,
+                                          int ns, int chunk, int s0, int s1, int piece) {
   const int lane = threadIdx.x & 63, n = lane & 15, g = lane >> 4;
   const int j = n & 7, half = n >> 3;  // this lane's A row: token j of the chunk, its half
-  const int ns = min(NS, a.out / 16 - grp * NS);
   const uint32_t* unit = a.codes + r.off / 4;
-  int64_t* dst = a.partial + (size_t)piece * a.N * a.out + grp * 16 * NS + n;
+  int64_t* dst = a.partial + (size_t)piece * a.N * a.out + t0 * 16 + n;
   {
     const int c0 = 8 * chunk;
     const int rows = min(8, r.cnt - c0);
     // lanes with j = m hold the slot of token m of the chunk
     const int slot = j < rows ? a.list[r.start + c0 + j] : -1;
     i32x4 acc[NS];
-    stream<K, NS>(a, unit, slot >= 0 ? slot / a.topk : -1, half, grp, ns, s0, s1, acc);
+    stream<K, NS>(a, unit, slot >= 0 ? slot / a.topk : -1, half, t0, ns, s0, s1, acc);
     // accumulator element i of lane (g, n) is row 4 g + i: for g < 2 the high half of token
     // 4 g + i, whose low half is in lane + 32
 #pragma unroll
@@ -179,16 +178,21 @@ __device__ __forceinline__ void run_piece(const TrellisGemvArgs& a, const PlanRe
 
 template <int NS>
 __global__ __launch_bounds__(GEMV_THREADS, GEMV_WAVES_PER_SIMD) void trellis_gemv_kernel(TrellisGemvArgs a) {
+  constexpr int SUB = 8 / NS;  // waves per piece
   Piece pc;
   const int w = blockIdx.x * GEMV_WG_WAVES + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  if (w >= a.G || !load_piece(a.desc, w, pc)) return;  // whole wave
+  const int q = w / SUB;
+  if (q >= a.G || !load_piece(a.desc, q, pc)) return;  // whole wave
+  const int t0 = 8 * pc.grp + NS * (w % SUB);              // first strip
+  const int ns = min(NS, a.out / 16 - t0);
+  if (ns <= 0) return;  // whole wave: past the last strip of a short group
   const PlanRec r = load_rec(a.rec, pc.ai);
   if (r.k == 2)
-    run_piece<2, NS>(a, r, pc.grp, pc.chunk, pc.s0, pc.s1, pc.idx);
+    run_piece<2, NS>(a, r, t0, ns, pc.chunk, pc.s0, pc.s1, pc.idx);
   else if (r.k == 3)
-    run_piece<3, NS>(a, r, pc.grp, pc.chunk, pc.s0, pc.s1, pc.idx);
+    run_piece<3, NS>(a, r, t0, ns, pc.chunk, pc.s0, pc.s1, pc.idx);
   else
-    run_piece<4, NS>(a, r, pc.grp, pc.chunk, pc.s0, pc.s1, pc.idx);
+    run_piece<4, NS>(a, r, t0, ns, pc.chunk, pc.s0, pc.s1, pc.idx);
 }
 
 // ---- decode hook ------------------------------------------------------------------------
@@ -299,7 +303,9 @@ int trellis_gemv_grid(int strips) {
   if (e != hipSuccess) return 0;
   per_cu *= GEMV_WG_WAVES;  // waves
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-  int g = std::min(per_cu, c == 0 ? 2 * GEMV_TARGET_PER_CU : GEMV_TARGET_PER_CU) * cus;
+  // pieces: waves of 4 strips take a piece two at a time, up to 4 per SIMD
+  int g = c == 0 ? std::min(per_cu, 2 * GEMV_TARGET_PER_CU) * cus / 2
+                 : std::min(per_cu, GEMV_TARGET_PER_CU) * cus;
   if (g > GEMV_MAX_G) g = GEMV_MAX_G;
   if (g < 1) g = 1;
   if (dev >= 0 && dev < 64) cache[dev][c] = g;
@@ -307,7 +313,8 @@ int trellis_gemv_grid(int strips) {
 }
 
 hipError_t launch_trellis_gemv(const TrellisGemvArgs& a, hipStream_t s) {
-  const dim3 grid((a.G + GEMV_WG_WAVES - 1) / GEMV_WG_WAVES), block(GEMV_THREADS);
+  const int waves = a.G * (a.strips == 4 ? 2 : 1);
+  const dim3 grid((waves + GEMV_WG_WAVES - 1) / GEMV_WG_WAVES), block(GEMV_THREADS);
   if (a.strips == 4)
     hipLaunchKernelGGL(trellis_gemv_kernel<4>, grid, block, 0, s, a);
   else if (a.strips == 8)
