@@ -144,7 +144,6 @@ WsLayout ws_layout(int64_t T, int topk, int E, int out, int in, uint32_t flags, 
   const int64_t N = T * topk;
   L.groups = (out + 127) / 128;
   L.gemm = use_gemm(T, topk, E, L.groups, flags);
-  L.vstrips = mxfp4 ? 8 : 4;  // trellis decode GEMV: two 4-strip waves per piece
   // a decode batch gives every active expert group and chunk at least one piece of its own
   if ((flags & 3u) == TQ_AUTO && gemv_chunk_bound(N, E, L.groups, mxfp4) > tq::GEMV_MAX_G)
     L.gemm = true;
@@ -549,7 +548,7 @@ int trellis_expert_gemm(const tq_trellis_layer* L, const void* x, int64_t T,
   const uint16_t* xb = static_cast<const uint16_t*>(x);
   hipError_t err;
   if (!W.gemm) {
-    const int G = tq::trellis_gemv_grid(W.vstrips);
+    const int G = tq::trellis_gemv_grid();
     if (G <= 0) return fail(TQ_EHIP, "could not size the GEMV grid");
     // launched waves: the plan's target, or one per expert group when that is more
     const int Gl = (int)std::max<int64_t>(G, tq::gemv_chunk_bound(N, L->E, W.groups, false));
@@ -598,7 +597,6 @@ int trellis_expert_gemm(const tq_trellis_layer* L, const void* x, int64_t T,
     a.in = L->in;
     a.topk = topk;
     a.G = Gl;
-    a.strips = W.vstrips;
     err = time_begin(s);
     if (err != hipSuccess) return hip_fail(err, "hipEventRecord");
     err = tq::launch_trellis_gemv(a, s);
@@ -1032,8 +1030,8 @@ int trellis_expert_ffn(const tq_trellis_layer* gate_up, const tq_trellis_layer* 
   hipError_t err;
   if (!W.gemm) {
     // 1. both plans and the gate/up activation prep
-    const int Gg = tq::trellis_gemv_grid(W.gu.vstrips), Gd = tq::trellis_gemv_grid(W.dn.vstrips);
-    if (Gg <= 0 || Gd <= 0) return fail(TQ_EHIP, "could not size the GEMV grid");
+    const int Gg = tq::trellis_gemv_grid(), Gd = Gg;
+    if (Gg <= 0) return fail(TQ_EHIP, "could not size the GEMV grid");
     const int Glg = (int)std::max<int64_t>(Gg, tq::gemv_chunk_bound(N, E, W.gu.groups, false));
     const int Gld = (int)std::max<int64_t>(Gd, tq::gemv_chunk_bound(N, E, W.dn.groups, false));
     tq::PlanArgs pg{}, pd{};
@@ -1100,7 +1098,6 @@ int trellis_expert_ffn(const tq_trellis_layer* gate_up, const tq_trellis_layer* 
     a.in = H;
     a.topk = topk;
     a.G = Glg;
-    a.strips = W.gu.vstrips;
     err = tq::launch_trellis_gemv(a, s);
     if (err != hipSuccess) return hip_fail(err, "gate/up GEMV launch");
     // 3. SwiGLU, the intermediate's rotation, the down projection's operands
@@ -1141,7 +1138,6 @@ int trellis_expert_ffn(const tq_trellis_layer* gate_up, const tq_trellis_layer* 
     b.in = I;
     b.topk = 1;
     b.G = Gld;
-    b.strips = W.dn.vstrips;
     err = time_begin(s);
     if (err != hipSuccess) return hip_fail(err, "hipEventRecord");
     err = tq::launch_trellis_gemv(b, s);

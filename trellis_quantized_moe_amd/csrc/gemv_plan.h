@@ -61,9 +61,9 @@ constexpr int GEMV_MAX_G = 32768;
 constexpr int PLAN_MAX_BIG = GEMV_MAX_G / PLAN_OWN_PIECES;
 // Waves per compute unit the plan aims for, for waves of 8 strips (2 per SIMD). The trellis
 // decode is bound by instruction issue: fewer, longer pieces spend less on each wave's setup
-// and on the partial sums that the reduction reads, and the routed trellis GEMV doubles the
-// waves by splitting each piece's strips over two of them (4 per SIMD). The MXFP4 GEMV,
-// which waits on memory more than it issues, aims for 3 per SIMD.
+// and on the partial sums that the reduction reads, and the trellis GEMV doubles the waves
+// by splitting each piece's strips over two of them (4 per SIMD). The MXFP4 GEMV, which
+// waits on memory more than it issues, aims for 3 per SIMD.
 constexpr int GEMV_TARGET_PER_CU = 8;
 
 }  // namespace tq

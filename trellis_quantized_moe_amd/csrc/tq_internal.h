@@ -21,7 +21,6 @@ struct WsLayout {
   size_t info = 0, rec = 0, desc = 0, list = 0, slot_info = 0, prank = 0;
   size_t total = 0;
   int groups = 1, route_blocks = 1, max_items = 0;
-  int vstrips = 8;  // decode-batch GEMV strips per wave: trellis 4, MXFP4 8
   bool gemm = false;
 };
 
@@ -89,13 +88,11 @@ struct TrellisGemvArgs {
   int64_t* partial;     // [in / 256][N][out]: the pieces' exact sums of each slot
   uint32_t x_bytes;     // size of xq in bytes (< 2^31)
   int N, out, in, topk;
-  int G;                // pieces (desc entries) launched
-  int strips;           // 16-channel strips per wave: 4 (two waves per piece) or 8
+  int G;                // pieces (desc entries) launched; two waves each
 };
-// The trellis GEMV's piece target (the plan's G) for waves of `strips` strips (4 or 8): the
-// waves the GPU holds at once, up to 4 (strips = 4) or 2 (strips = 8) per SIMD, over the
-// waves per piece; 0 on a HIP error.
-int trellis_gemv_grid(int strips);
+// The trellis GEMV's piece target (the plan's G): half the waves the GPU holds at once, up
+// to 4 per SIMD; 0 on a HIP error.
+int trellis_gemv_grid();
 hipError_t launch_trellis_gemv(const TrellisGemvArgs& a, hipStream_t s);
 
 struct PieceReduceArgs {

@@ -4,10 +4,10 @@
 // and wave w streams the one piece the plan gave it, steps s0 .. s1 - 1 of one group of one
 // expert, on its own: no LDS and no barrier, so a wave that waits for memory never holds
 // up another, and its load stream never restarts. A plan group is 8 strips (128 output
-// channels), and a wave takes NS = 4 or 8 of them: with NS = 4 two waves (wave 2 q + h
-// takes strips 4 h .. 4 h + 3) share piece q, the same pieces and so the same partial sums
-// over twice the waves. The decode is bound by instruction issue, and a SIMD issues VALU
-// and matrix-core instructions faster with four waves to choose from than with two. A step
+// channels), and a wave takes NS = 4 of them: wave 2 q + h takes strips 4 h .. 4 h + 3 of
+// piece q. The decode is bound by instruction issue, and a SIMD issues VALU and
+// matrix-core instructions faster with four waves to choose from than with two, so the
+// pieces are shared by twice the waves (the same pieces, so the same partial sums). A step
 // is 4 tile columns (64 inputs) of the wave's strips. Per step and strip, each lane decodes one
 // tile column (16 weights of one output channel) and the wave feeds two 16 x 16 x 64 int8
 // matrix-core operations: the weights as signed bytes (two k positions per weight, see
@@ -39,6 +39,7 @@ namespace {
 constexpr int GEMV_WG_WAVES = 1;
 constexpr int GEMV_THREADS = 64 * GEMV_WG_WAVES;
 constexpr int GEMV_WAVES_PER_SIMD = 4;  // register budget: 128 per lane
+constexpr int GEMV_NS = 4;              // strips per wave (two waves per piece)
 
 __device__ __forceinline__ void load_x(Rsrc r, uint32_t vo, uint32_t so, u32x4& xa, u32x4& xb) {
   xa = __builtin_amdgcn_raw_buffer_load_b128(r, vo, so, 0);
@@ -176,9 +177,8 @@ __device__ __forceinline__ void run_piece(const TrellisGemvArgs& a, const PlanRe
   }
 }
 
-template <int NS>
 __global__ __launch_bounds__(GEMV_THREADS, GEMV_WAVES_PER_SIMD) void trellis_gemv_kernel(TrellisGemvArgs a) {
-  constexpr int SUB = 8 / NS;  // waves per piece
+  constexpr int NS = GEMV_NS, SUB = 8 / NS;  // waves per piece
   Piece pc;
   const int w = blockIdx.x * GEMV_WG_WAVES + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int q = w / SUB;
@@ -288,39 +288,29 @@ hipError_t launch_trellis_repack(const uint8_t* bits, const int64_t* code_off,
   return hipGetLastError();
 }
 
-int trellis_gemv_grid(int strips) {
-  static int cache[64][2];
-  const int c = strips == 4 ? 0 : 1;
+int trellis_gemv_grid() {
+  static int cache[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 0;
-  if (dev >= 0 && dev < 64 && cache[dev][c]) return cache[dev][c];
+  if (dev >= 0 && dev < 64 && cache[dev]) return cache[dev];
   int per_cu = 0, cus = 0;
-  const hipError_t e =
-      c == 0 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, trellis_gemv_kernel<4>,
-                                                             GEMV_THREADS, 0)
-             : hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, trellis_gemv_kernel<8>,
-                                                             GEMV_THREADS, 0);
-  if (e != hipSuccess) return 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, trellis_gemv_kernel, GEMV_THREADS, 0) !=
+      hipSuccess)
+    return 0;
   per_cu *= GEMV_WG_WAVES;  // waves
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-  // pieces: waves of 4 strips take a piece two at a time, up to 4 per SIMD
-  int g = c == 0 ? std::min(per_cu, 2 * GEMV_TARGET_PER_CU) * cus / 2
-                 : std::min(per_cu, GEMV_TARGET_PER_CU) * cus;
+  // pieces: two waves each, up to 4 waves per SIMD
+  int g = std::min(per_cu, 2 * GEMV_TARGET_PER_CU) * cus / (8 / GEMV_NS);
   if (g > GEMV_MAX_G) g = GEMV_MAX_G;
   if (g < 1) g = 1;
-  if (dev >= 0 && dev < 64) cache[dev][c] = g;
+  if (dev >= 0 && dev < 64) cache[dev] = g;
   return g;
 }
 
 hipError_t launch_trellis_gemv(const TrellisGemvArgs& a, hipStream_t s) {
-  const int waves = a.G * (a.strips == 4 ? 2 : 1);
-  const dim3 grid((waves + GEMV_WG_WAVES - 1) / GEMV_WG_WAVES), block(GEMV_THREADS);
-  if (a.strips == 4)
-    hipLaunchKernelGGL(trellis_gemv_kernel<4>, grid, block, 0, s, a);
-  else if (a.strips == 8)
-    hipLaunchKernelGGL(trellis_gemv_kernel<8>, grid, block, 0, s, a);
-  else
-    return hipErrorInvalidValue;
+  const int waves = a.G * (8 / GEMV_NS);
+  hipLaunchKernelGGL(trellis_gemv_kernel, dim3((waves + GEMV_WG_WAVES - 1) / GEMV_WG_WAVES),
+                     dim3(GEMV_THREADS), 0, s, a);
   return hipGetLastError();
 }
 
