@@ -19,9 +19,10 @@ code buffer (replicas total >= 1 GiB) so the 256 MB Infinity Cache cannot serve 
 
 value = compressed bytes of the experts a step touches / step time (GB/s), or dense-
 equivalent routed flops / step time (TFLOP/s) for prefill. The roofline object times the
-dominant kernel (the grouped GEMV) alone: HIP events recorded on its own stream right
-before and after it (tq_time_kernel), over --kernel-iters direct calls of the step's GEMM
-queued behind a bounded sleep kernel, so no host gap falls inside an interval. Its HBM
+dominant kernel (the grouped GEMV) alone: a HIP event pair that its launch
+(hipExtLaunchKernel, through tq_time_kernel) sets to the kernel's own start and end on its
+stream, over --kernel-iters direct calls of the step's GEMM queued behind a bounded sleep
+kernel. Its HBM
 traffic comes from rocprofv3 FETCH_SIZE / WRITE_SIZE runs (bench.py --drive mixed),
 calibrated against a plain elementwise copy of known size in the same runs and stored by
 bench.py --write-traffic. The CPU baseline times the oracle (test infrastructure) on the
@@ -99,8 +100,8 @@ def kernel_events(torch, n):
 
 def time_main_kernel(torch, ops, call, n_replicas, iters):
     """Mean (and median) duration of the main kernel of `call(r)`: direct launches queued
-    behind a bounded sleep kernel, each with tq_time_kernel's event pair around that kernel
-    on its own stream."""
+    behind a bounded sleep kernel, each with tq_time_kernel's event pair set to that
+    kernel's start and end."""
     starts, stops = kernel_events(torch, iters)
     for r in range(n_replicas):
         call(r)

@@ -438,11 +438,14 @@ int tq_device_status(void* ws, void* stream, uint32_t* flags_out);
 
 /*
  * Measurement hook, for benchmarks and profilers (not part of the computation). After this
- * call, the calling thread's next trellis_expert_gemm or mxfp4_expert_gemm records `start`
- * on its stream immediately before its main kernel (the grouped GEMV in the decode-batch
- * mode, the grouped GEMM in the prefill mode) and `stop` immediately after it; the hook is
- * then cleared. start and stop are hipEvent_t passed as void*, created by the caller; under
- * stream capture they become event-record nodes of the graph. NULL, NULL clears the hook.
+ * call, the calling thread's next trellis_expert_gemm, mxfp4_expert_gemm or
+ * trellis_expert_ffn times its main kernel (the grouped GEMV in the decode-batch mode, the
+ * down projection's GEMV in the FFN, the grouped GEMM in the prefill mode): the kernel is
+ * launched with hipExtLaunchKernel, which sets `start` and `stop` to the dispatch's own
+ * start and end; under stream capture they are recorded on the stream right before and
+ * after the launch instead (event-record nodes of the graph). The hook is then cleared.
+ * start and stop are hipEvent_t passed as void*, created by the caller with timing
+ * enabled. NULL, NULL clears the hook.
  */
 int tq_time_kernel(void* start, void* stop);
 

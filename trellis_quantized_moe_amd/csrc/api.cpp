@@ -16,16 +16,51 @@ namespace {
 
 thread_local std::string g_error;
 thread_local hipEvent_t g_time_start = nullptr, g_time_stop = nullptr;
+thread_local bool g_time_armed = false;     // the next launch_timed takes the events
+thread_local bool g_time_recorded = false;  // stream capture: events recorded around it
 
-// Measurement hook (tq_time_kernel): events around the next main kernel launch.
+// Measurement hook (tq_time_kernel), around the next main kernel launch. Outside stream
+// capture the launch itself records the kernel's start and end into the events
+// (launch_timed); under capture the events are recorded on the stream before and after it.
 hipError_t time_begin(hipStream_t s) {
-  return g_time_start ? hipEventRecord(g_time_start, s) : hipSuccess;
+  if (!g_time_start) return hipSuccess;
+  hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
+  hipError_t err = hipStreamIsCapturing(s, &st);
+  if (err != hipSuccess) return err;
+  if (st == hipStreamCaptureStatusNone) {
+    g_time_armed = true;
+    return hipSuccess;
+  }
+  g_time_recorded = true;
+  return hipEventRecord(g_time_start, s);
 }
 hipError_t time_end(hipStream_t s) {
-  hipError_t err = g_time_stop ? hipEventRecord(g_time_stop, s) : hipSuccess;
+  hipError_t err = hipSuccess;
+  if (g_time_recorded) {
+    err = hipEventRecord(g_time_stop, s);
+  } else if (g_time_armed) {  // no kernel was launched (an empty launch): zero duration
+    err = hipEventRecord(g_time_start, s);
+    if (err == hipSuccess) err = hipEventRecord(g_time_stop, s);
+  }
   g_time_start = g_time_stop = nullptr;
+  g_time_armed = g_time_recorded = false;
   return err;
 }
+
+}  // namespace
+
+void tq::take_kernel_events(hipEvent_t* start, hipEvent_t* stop) {
+  if (g_time_armed) {
+    *start = g_time_start;
+    *stop = g_time_stop;
+    g_time_armed = false;
+    g_time_start = g_time_stop = nullptr;
+  } else {
+    *start = *stop = nullptr;
+  }
+}
+
+namespace {
 
 int fail(int code, const char* fmt, ...) {
   char buf[512];

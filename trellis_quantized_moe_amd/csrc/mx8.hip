@@ -313,8 +313,7 @@ hipError_t launch_mxfp8_prep(const uint16_t* x, int64_t rows, int n, uint8_t* co
 hipError_t launch_mx8_gemm(const Mx8GemmArgs& a, hipStream_t s) {
   const int blocks = gemm_grid(a.max_items, a.groups);
   if (blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL(mx8_gemm_kernel, dim3(blocks), dim3(M8_THREADS), 0, s, a);
-  return hipGetLastError();
+  return launch_timed(mx8_gemm_kernel, dim3(blocks), dim3(M8_THREADS), s, a);
 }
 
 }  // namespace tq

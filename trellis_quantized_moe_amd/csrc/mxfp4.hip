@@ -460,20 +460,16 @@ int mxfp4_gemv_grid(int fmt) {
 
 hipError_t launch_mxfp4_gemv(const Mxfp4GemvArgs& a, hipStream_t s) {
   if (a.fmt == MX_FP8B32)
-    hipLaunchKernelGGL(mxfp4_gemv_kernel<MX_FP8B32>, dim3(a.G), dim3(MX_THREADS), 0, s, a);
-  else
-    hipLaunchKernelGGL(mxfp4_gemv_kernel<MX_FP4>, dim3(a.G), dim3(MX_THREADS), 0, s, a);
-  return hipGetLastError();
+    return launch_timed(mxfp4_gemv_kernel<MX_FP8B32>, dim3(a.G), dim3(MX_THREADS), s, a);
+  return launch_timed(mxfp4_gemv_kernel<MX_FP4>, dim3(a.G), dim3(MX_THREADS), s, a);
 }
 
 hipError_t launch_mxfp4_gemm(const Mxfp4GemmArgs& a, hipStream_t s) {
   const int blocks = gemm_grid(a.max_items, a.groups);
   if (blocks == 0) return hipSuccess;
   if (a.fmt == MX_FP8B32)
-    hipLaunchKernelGGL(mxfp4_gemm_kernel<MX_FP8B32>, dim3(blocks), dim3(GEMM_THREADS), 0, s, a);
-  else
-    hipLaunchKernelGGL(mxfp4_gemm_kernel<MX_FP4>, dim3(blocks), dim3(GEMM_THREADS), 0, s, a);
-  return hipGetLastError();
+    return launch_timed(mxfp4_gemm_kernel<MX_FP8B32>, dim3(blocks), dim3(GEMM_THREADS), s, a);
+  return launch_timed(mxfp4_gemm_kernel<MX_FP4>, dim3(blocks), dim3(GEMM_THREADS), s, a);
 }
 
 }  // namespace tq

@@ -1,6 +1,7 @@
 // Host-side internal interface between the C ABI (api.cpp) and the kernel files.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -27,6 +28,25 @@ struct WsLayout {
 constexpr int ROUTE_CHUNK = 2048;  // ids per route-count block
 constexpr int GEMM_MT = 128;       // token rows per prefill work item
 constexpr int GEMV_MAXK = 16;      // tokens per decode-batch chunk (one MFMA row block)
+
+// ---- measurement hook (tq_time_kernel) -------------------------------------------------
+// The hook's events for the main kernel about to be launched: both null unless the hook is
+// armed (outside stream capture); taking them disarms it.
+void take_kernel_events(hipEvent_t* start, hipEvent_t* stop);
+
+// A main kernel's launch: with the hook armed, through hipExtLaunchKernelGGL, whose events
+// take the dispatch's own start and end times (the kernel's duration, as a profiler reports
+// it); else a plain launch.
+template <typename F, typename... Args>
+hipError_t launch_timed(F kernel, dim3 grid, dim3 block, hipStream_t s, Args... args) {
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  take_kernel_events(&e0, &e1);
+  if (e0)
+    hipExtLaunchKernelGGL(kernel, grid, block, 0, s, e0, e1, 0, args...);
+  else
+    hipLaunchKernelGGL(kernel, grid, block, 0, s, args...);
+  return hipGetLastError();
+}
 
 // Records `msg` as this thread's last error (tq_last_error) and returns `code`.
 int set_error(int code, const char* msg);

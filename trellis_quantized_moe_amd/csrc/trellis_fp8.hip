@@ -417,12 +417,10 @@ hipError_t launch_tf8_gemm(const TrellisFp8GemmArgs& a, hipStream_t s) {
   const int blocks = gemm_grid(a.max_items, a.groups);
   if (blocks == 0) return hipSuccess;
   if (a.codebook == CB_MUL1)
-    hipLaunchKernelGGL(tf8_gemm_kernel<CB_MUL1>, dim3(blocks), dim3(TF_THREADS), 0, s, a);
-  else if (a.codebook == CB_PMCGX)
-    hipLaunchKernelGGL(tf8_gemm_kernel<CB_PMCGX>, dim3(blocks), dim3(TF_THREADS), 0, s, a);
-  else
-    hipLaunchKernelGGL(tf8_gemm_kernel<CB_T16>, dim3(blocks), dim3(TF_THREADS), 0, s, a);
-  return hipGetLastError();
+    return launch_timed(tf8_gemm_kernel<CB_MUL1>, dim3(blocks), dim3(TF_THREADS), s, a);
+  if (a.codebook == CB_PMCGX)
+    return launch_timed(tf8_gemm_kernel<CB_PMCGX>, dim3(blocks), dim3(TF_THREADS), s, a);
+  return launch_timed(tf8_gemm_kernel<CB_T16>, dim3(blocks), dim3(TF_THREADS), s, a);
 }
 
 template <int CB>

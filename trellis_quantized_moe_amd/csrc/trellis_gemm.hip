@@ -331,8 +331,7 @@ __global__ __launch_bounds__(TG_THREADS, 3) void trellis_gemm_kernel(TrellisGemm
 hipError_t launch_trellis_gemm(const TrellisGemmArgs& a, hipStream_t s) {
   const int blocks = gemm_grid(a.max_items, a.groups);
   if (blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL(trellis_gemm_kernel, dim3(blocks), dim3(TG_THREADS), 0, s, a);
-  return hipGetLastError();
+  return launch_timed(trellis_gemm_kernel, dim3(blocks), dim3(TG_THREADS), s, a);
 }
 
 }  // namespace tq

@@ -309,9 +309,8 @@ int trellis_gemv_grid() {
 
 hipError_t launch_trellis_gemv(const TrellisGemvArgs& a, hipStream_t s) {
   const int waves = a.G * (8 / GEMV_NS);
-  hipLaunchKernelGGL(trellis_gemv_kernel, dim3((waves + GEMV_WG_WAVES - 1) / GEMV_WG_WAVES),
-                     dim3(GEMV_THREADS), 0, s, a);
-  return hipGetLastError();
+  return launch_timed(trellis_gemv_kernel, dim3((waves + GEMV_WG_WAVES - 1) / GEMV_WG_WAVES),
+                      dim3(GEMV_THREADS), s, a);
 }
 
 hipError_t launch_trellis_decode(const uint32_t* codes, int K, int out, int in, int16_t* q,

@@ -323,8 +323,9 @@ def version():
 
 
 def time_kernel(start, stop):
-    """Measurement hook: the next expert GEMM call on this thread records the torch.cuda.Event
-    pair (start, stop) around its main kernel, on its stream (tq_time_kernel)."""
+    """Measurement hook: the next expert GEMM or FFN call on this thread sets the
+    torch.cuda.Event pair (start, stop) to its main kernel's own start and end
+    (tq_time_kernel)."""
     if start is None:
         check(_lib.load().tq_time_kernel(None, None))
         return
