@@ -3,9 +3,9 @@
 import numpy as np
 import pytest
 
-from gpu_helpers import gpu, needs_gpu, ops, oracle_mxfp4, rel_l2, to_dev, torch
-from workloads import (bf16_from_normal, mxfp4_decode_layer, mxfp4_layer, rng_for, softmax_gates,
-                       uniform_routes)
+from gpu_helpers import gpu, needs_gpu, ops, oracle_mxfp4, rel_l2, slot_errors, to_dev, torch
+from workloads import (bf16_from_normal, mxfp4_decode_layer, mxfp4_layer, mxfp4_prefill_chunk,
+                       rng_for, softmax_gates, uniform_routes)
 
 pytestmark = [gpu, needs_gpu]
 TOL = 1e-3
@@ -99,3 +99,19 @@ def test_repacked_full_size_decode():
     a = run_layer(L, wl["x"], wl["topk_ids"], wl["topk_w"])
     b = run_layer(L.repacked(), wl["x"], wl["topk_ids"], wl["topk_w"])
     assert np.array_equal(a, b)
+
+
+@pytest.mark.timeout(900)
+def test_prefill_chunk_full_size_every_slot():
+    """The MXFP4 prefill chunk (384 units of 128 x 5120, 8,192 tokens, top-8 Zipf(1.1),
+    gates) on the bf16 matrix cores, units repacked: every one of the 65,536 slots against
+    the FP64 oracle."""
+    o = ops()
+    wl = mxfp4_prefill_chunk()
+    L = o.Mxfp4Layer.from_host(wl["layer"]).repacked()
+    y = o.mxfp4_expert_gemm(L, to_dev(wl["x"], np.int16), to_dev(wl["topk_ids"]),
+                            to_dev(wl["topk_w"]), flags=o.TQ_GEMM).cpu().numpy()
+    ref = oracle_mxfp4(wl["layer"], wl["x"], wl["topk_ids"], wl["topk_w"])
+    pooled, worst = slot_errors(y, ref)
+    print("MXFP4 bf16 prefill, 65536 slots: pooled %.3e, worst slot %.3e" % (pooled, worst))
+    assert pooled <= TOL and worst <= TOL

@@ -62,6 +62,31 @@ __device__ inline void gemm_load_slots(GemmShared& sh, const int32_t* pairs, int
   lds_barrier();
 }
 
+// ---- LDS rings filled by loads that write LDS ----------------------------------------------
+typedef __attribute__((address_space(3))) void* LdsPtr;
+
+// s_waitcnt with only the vector-memory count limited (gfx9 encoding: vmcnt in bits 3:0
+// and 15:14; expcnt and lgkmcnt left at their maxima).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Workgroup barrier with no memory fence. The loads that write LDS count on the vector
+// memory counter, so an LDS fence would wait for all of them, including the ones meant to
+// stay in flight; the waits are explicit instead (wait_vmcnt before the barrier). The wave's
+// own LDS reads are waited for (lgkmcnt(0)) and no instruction moves across the barrier, so
+// no wave can still be reading a stage when another starts refilling it after the barrier.
+__device__ __forceinline__ void bare_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt unlimited
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
 // ---- buffer loads ------------------------------------------------------------------------
 typedef __amdgpu_buffer_rsrc_t GemmRsrc;
 __device__ __forceinline__ GemmRsrc gemm_rsrc(const void* base, uint32_t bytes) {

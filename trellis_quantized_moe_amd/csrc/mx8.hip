@@ -92,25 +92,6 @@ struct M8Shared {
   float gate[GEMM_MT];
 };
 
-typedef __attribute__((address_space(3))) void* LdsPtr;
-
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-
-__device__ __forceinline__ void bare_barrier() {
-  // this wave's LDS reads have completed and no instruction moves across: no wave can still
-  // be reading a stage when another wave starts refilling it after the barrier
-  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt unlimited
-  __builtin_amdgcn_sched_barrier(0);
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_sched_barrier(0);
-}
-
 // Vector-memory instructions a wave issues per step: A chunks (4), the scale rows (waves 0
 // and 1: one each) and the weight codes (2); every fourth step (the first of a window of
 // four steps) also the weight scales of the next window (2).

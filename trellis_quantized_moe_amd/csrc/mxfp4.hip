@@ -289,52 +289,7 @@ __global__ __launch_bounds__(MX_THREADS, MxUnit<FMT>::kFp8 ? 2 : MX_WAVES_PER_SI
   }
 }
 
-// ---- prefill GEMM --------------------------------------------------------------------------
-// B producer: thread (o = tid / 2, h = tid % 2) decodes 16 codes of output o, inputs
-// 32 kk + 16 h .. +15, with the scale of block kk.
-// Thread t decodes, each step, inputs 16 h .. + 15 (h = t % 2) of the step for output
-// channel o = t / 2: 8 code bytes and the channel's scale byte of the step's 32-block.
-struct Mxfp4Producer {
-  struct Raw {
-    uint32_t c0, c1, sb;
-  };
-  GemmRsrc rc;
-  uint32_t vo_c, vo_s;
-  int o, h;
-
-  uint32_t pstep;  // layout 1: code bytes per 128-input step of the group, else 0
-
-  __device__ Mxfp4Producer(const uint8_t* unit, int out, int in, int grp, int ns, int layout) {
-    using U = MxUnit<MX_FP4>;
-    o = threadIdx.x >> 1;
-    h = threadIdx.x & 1;
-    rc = gemm_rsrc(unit, (uint32_t)U::unit_bytes(out, in));
-    // channels past the group read its last channel (their rows of the B tile are unused)
-    const int og = grp * 128 + (o < 16 * ns ? o : 16 * ns - 1);
-    vo_c = (layout ? U::packed_at(out, in, og, 0) : U::stored_at(in, og, 0)) + 8 * h;
-    pstep = layout ? (uint32_t)ns * 64 * U::kCB : 0u;
-    vo_s = U::scale_at(out, in, og, 0);
-  }
-
-  // scalar offset of block kk's codes
-  __device__ __forceinline__ uint32_t koff(int kk) const {
-    return pstep ? (uint32_t)(kk >> 2) * pstep + 16u * (uint32_t)(kk & 3) : 16u * kk;
-  }
-
-  __device__ __forceinline__ void load(int kk, Raw& r) const {
-    const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(rc, vo_c, koff(kk), 0);
-    r.c0 = v.x;
-    r.c1 = v.y;
-    r.sb = __builtin_amdgcn_raw_buffer_load_b8(rc, vo_s, (uint32_t)kk, 0);
-  }
-
-  __device__ __forceinline__ void decode(const Raw& r, uint32_t nat[8]) const {
-    const float sc = e8m0_to_f32(r.sb);
-    fp4x8_to_bf16(r.c0, sc, nat);
-    fp4x8_to_bf16(r.c1, sc, nat + 4);
-  }
-};
-
+// ---- prefill GEMM (fp8b32; MXFP4 in mxfp4_prefill.hip) ---------------------------------------
 // fp8b32 B producer: thread (o = tid / 2, h = tid % 2) decodes inputs 16 h .. + 15 of the
 // step's 32-block for output channel o: 16 code bytes and the scale byte of the channel's
 // 32 x 32 block.
@@ -377,8 +332,7 @@ struct Fp8b32Producer {
   }
 };
 
-template <int FMT>
-__global__ __launch_bounds__(GEMM_THREADS, 2) void mxfp4_gemm_kernel(Mxfp4GemmArgs a) {
+__global__ __launch_bounds__(GEMM_THREADS, 2) void fp8b32_gemm_kernel(Mxfp4GemmArgs a) {
   __shared__ GemmShared sh;
   int item, grp;
   if (!gemm_unit(a.n_items, a.groups, &item, &grp)) return;
@@ -397,14 +351,9 @@ __global__ __launch_bounds__(GEMM_THREADS, 2) void mxfp4_gemm_kernel(Mxfp4GemmAr
   it.grp = grp;
   it.nrows = itd.z;
   it.ns = min(8, a.out / 16 - grp * 8);
-  const uint8_t* unit = a.units + (size_t)e * MxUnit<FMT>::unit_bytes(a.out, a.in);
-  if constexpr (FMT == MX_FP8B32) {
-    Fp8b32Producer p(unit, a.out, a.in, grp, it.ns, a.layout);
-    gemm_item(it, sh, p);
-  } else {
-    Mxfp4Producer p(unit, a.out, a.in, grp, it.ns, a.layout);
-    gemm_item(it, sh, p);
-  }
+  const uint8_t* unit = a.units + (size_t)e * MxUnit<MX_FP8B32>::unit_bytes(a.out, a.in);
+  Fp8b32Producer p(unit, a.out, a.in, grp, it.ns, a.layout);
+  gemm_item(it, sh, p);
 }
 
 }  // namespace
@@ -468,8 +417,8 @@ hipError_t launch_mxfp4_gemm(const Mxfp4GemmArgs& a, hipStream_t s) {
   const int blocks = gemm_grid(a.max_items, a.groups);
   if (blocks == 0) return hipSuccess;
   if (a.fmt == MX_FP8B32)
-    return launch_timed(mxfp4_gemm_kernel<MX_FP8B32>, dim3(blocks), dim3(GEMM_THREADS), s, a);
-  return launch_timed(mxfp4_gemm_kernel<MX_FP4>, dim3(blocks), dim3(GEMM_THREADS), s, a);
+    return launch_timed(fp8b32_gemm_kernel, dim3(blocks), dim3(GEMM_THREADS), s, a);
+  return launch_mxfp4_prefill(a, s);
 }
 
 }  // namespace tq

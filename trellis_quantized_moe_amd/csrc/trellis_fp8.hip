@@ -166,25 +166,6 @@ struct TfShared {
   float gate[GEMM_MT];
 };
 
-typedef __attribute__((address_space(3))) void* LdsPtr;
-
-template <int N>
-__device__ __forceinline__ void tf_wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-
-__device__ __forceinline__ void tf_barrier() {
-  // this wave's LDS reads have completed and no instruction moves across: no wave can still
-  // be reading a stage when another wave starts refilling it after the barrier
-  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt unlimited
-  __builtin_amdgcn_sched_barrier(0);
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_sched_barrier(0);
-}
-
 // Vector-memory instructions a wave issues per step: 4 activation chunks, the scale row
 // (waves 0 and 1), the code words (2 strips x 2 runs, one load each).
 template <int K, bool SCALES>
@@ -280,10 +261,10 @@ __device__ void tf_item(const TrellisFp8GemmArgs& a, TfShared& sh, const uint32_
     // this wave's loads of step kk have landed (those of kk + 1 may be in flight); after the
     // barrier every wave's have, and every wave is done with the stage refilled below
     if (scale_loader)
-      tf_wait_vmcnt<tf_step_loads<K, true>()>();
+      wait_vmcnt<tf_step_loads<K, true>()>();
     else
-      tf_wait_vmcnt<tf_step_loads<K, false>()>();
-    tf_barrier();
+      wait_vmcnt<tf_step_loads<K, false>()>();
+    bare_barrier();
     const int nxt = kk + 2 < nsteps ? kk + 2 : nsteps - 1;
     load_a((kk + 2) % TF_STAGES, nxt);
     uint32_t B[2][8];
@@ -318,7 +299,7 @@ __device__ void tf_item(const TrellisFp8GemmArgs& a, TfShared& sh, const uint32_
     step(kk + 1, 1);
   }
   // no load may still be writing this workgroup's LDS when it ends
-  tf_wait_vmcnt<0>();
+  wait_vmcnt<0>();
 
 #pragma unroll
   for (int s = 0; s < 2; ++s) {

@@ -53,31 +53,6 @@ struct TgShared {
   float gate[GEMM_MT];  // the slot's gate (or 1) times the token's 2^-s
 };
 
-typedef __attribute__((address_space(3))) void* LdsPtr;
-
-// s_waitcnt with only the vector-memory count limited (gfx9 encoding: vmcnt in bits 3:0
-// and 15:14; expcnt and lgkmcnt left at their maxima).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-
-// Workgroup barrier with no memory fence. The loads that write LDS count on the vector
-// memory counter, so an LDS fence would wait for all of them, including the ones meant to
-// stay in flight; the waits are explicit instead (wait_vmcnt before the barrier). The empty
-// asm statements keep the compiler from moving memory accesses across the barrier.
-__device__ __forceinline__ void bare_barrier() {
-  // this wave's LDS reads have completed and no instruction moves across: no wave can still
-  // be reading a stage when another wave starts refilling it after the barrier
-  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt unlimited
-  __builtin_amdgcn_sched_barrier(0);
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_sched_barrier(0);
-}
-
 template <int K>
 struct ColWords {
   uint32_t w[K == 2 ? 1 : 2];
