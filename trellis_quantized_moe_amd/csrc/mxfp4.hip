@@ -289,73 +289,6 @@ __global__ __launch_bounds__(MX_THREADS, MxUnit<FMT>::kFp8 ? 2 : MX_WAVES_PER_SI
   }
 }
 
-// ---- prefill GEMM (fp8b32; MXFP4 in mxfp4_prefill.hip) ---------------------------------------
-// fp8b32 B producer: thread (o = tid / 2, h = tid % 2) decodes inputs 16 h .. + 15 of the
-// step's 32-block for output channel o: 16 code bytes and the scale byte of the channel's
-// 32 x 32 block.
-struct Fp8b32Producer {
-  struct Raw {
-    u32x4 c;
-    uint32_t sb;
-  };
-  GemmRsrc rc;
-  uint32_t vo_c, vo_s;
-  int o, h;
-
-  uint32_t pstep;  // layout 1: code bytes per 128-input step of the group, else 0
-
-  __device__ Fp8b32Producer(const uint8_t* unit, int out, int in, int grp, int ns, int layout) {
-    using U = MxUnit<MX_FP8B32>;
-    o = threadIdx.x >> 1;
-    h = threadIdx.x & 1;
-    rc = gemm_rsrc(unit, (uint32_t)U::unit_bytes(out, in));
-    // channels past the group read its last channel (their rows of the B tile are unused)
-    const int og = grp * 128 + (o < 16 * ns ? o : 16 * ns - 1);
-    vo_c = (layout ? U::packed_at(out, in, og, 0) : U::stored_at(in, og, 0)) + 16 * h;
-    pstep = layout ? (uint32_t)ns * 64 * U::kCB : 0u;
-    vo_s = U::scale_at(out, in, og, 0);
-  }
-
-  __device__ __forceinline__ uint32_t koff(int kk) const {
-    return pstep ? (uint32_t)(kk >> 2) * pstep + 32u * (uint32_t)(kk & 3) : 32u * kk;
-  }
-
-  __device__ __forceinline__ void load(int kk, Raw& r) const {
-    r.c = __builtin_amdgcn_raw_buffer_load_b128(rc, vo_c, koff(kk), 0);
-    r.sb = __builtin_amdgcn_raw_buffer_load_b8(rc, vo_s, (uint32_t)kk, 0);
-  }
-
-  __device__ __forceinline__ void decode(const Raw& r, uint32_t nat[8]) const {
-    const float sc = e8m0_to_f32(r.sb);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) fp8x4_to_bf16(r.c[j], sc, nat + 2 * j);
-  }
-};
-
-__global__ __launch_bounds__(GEMM_THREADS, 2) void fp8b32_gemm_kernel(Mxfp4GemmArgs a) {
-  __shared__ GemmShared sh;
-  int item, grp;
-  if (!gemm_unit(a.n_items, a.groups, &item, &grp)) return;
-  const int4 itd = reinterpret_cast<const int4*>(a.items)[item];
-  const int e = itd.x;
-  gemm_load_slots(sh, a.pairs, itd.y, itd.z);
-  GemmItem it;
-  it.x = a.x;
-  it.x_bytes = a.x_bytes;
-  it.gates = a.gates;
-  it.scales = nullptr;
-  it.y = a.y;
-  it.in = a.in;
-  it.out = a.out;
-  it.topk = a.topk;
-  it.grp = grp;
-  it.nrows = itd.z;
-  it.ns = min(8, a.out / 16 - grp * 8);
-  const uint8_t* unit = a.units + (size_t)e * MxUnit<MX_FP8B32>::unit_bytes(a.out, a.in);
-  Fp8b32Producer p(unit, a.out, a.in, grp, it.ns, a.layout);
-  gemm_item(it, sh, p);
-}
-
 }  // namespace
 
 hipError_t launch_mxfp4_decode(const uint8_t* unit, int out, int in, uint16_t* w,
@@ -411,14 +344,6 @@ hipError_t launch_mxfp4_gemv(const Mxfp4GemvArgs& a, hipStream_t s) {
   if (a.fmt == MX_FP8B32)
     return launch_timed(mxfp4_gemv_kernel<MX_FP8B32>, dim3(a.G), dim3(MX_THREADS), s, a);
   return launch_timed(mxfp4_gemv_kernel<MX_FP4>, dim3(a.G), dim3(MX_THREADS), s, a);
-}
-
-hipError_t launch_mxfp4_gemm(const Mxfp4GemmArgs& a, hipStream_t s) {
-  const int blocks = gemm_grid(a.max_items, a.groups);
-  if (blocks == 0) return hipSuccess;
-  if (a.fmt == MX_FP8B32)
-    return launch_timed(fp8b32_gemm_kernel, dim3(blocks), dim3(GEMM_THREADS), s, a);
-  return launch_mxfp4_prefill(a, s);
 }
 
 }  // namespace tq

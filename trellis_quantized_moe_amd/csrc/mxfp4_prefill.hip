@@ -1,20 +1,21 @@
-// Prefill grouped GEMM over MXFP4 experts on the bf16 matrix cores (gfx950;
-// DeepSeek-V4.1-Flash-1017 · exlr8 page, "Stores": the official expert store, E2M1 codes with
-// one E8M0 scale per 32 inputs).
+// Prefill grouped GEMM over the E8M0-scaled stores on the bf16 matrix cores (gfx950;
+// DeepSeek-V4.1-Flash-1017 · exlr8 page, "Stores": MXFP4, the official expert store, E2M1
+// codes with one E8M0 scale per 32 inputs of a channel; fp8b32, the shared expert's store,
+// E4M3 codes with one E8M0 scale per 32 x 32 block).
 //
 // A work item is up to 128 routed rows of one expert times one group of up to 128 output
 // channels over the whole input range, in steps of 64 inputs, on four waves: wave w owns
 // channels 32 w .. 32 w + 31 (strips 2 w, 2 w + 1) for all rows, so no weight is loaded or
 // converted twice and no weight passes through LDS.
 //   - weights: lane (n, q) of a 16-channel strip takes inputs 16 q .. 16 q + 15 of the step
-//     for channel n: 8 contiguous code bytes (one 8-byte load, in the store order and in the
-//     GEMV's read order alike) and the scale of their 32-input block. Eight hardware
-//     conversions (v_cvt_scalef32_pk_bf16_fp4, the scale applied exactly) give the bf16
-//     operands of the step's two 16x16x32 products: inputs 16 q .. 16 q + 7, then
-//     16 q + 8 .. 16 q + 15. The activations take the same inputs in the same order, so
-//     every product sums the same terms as the natural order.
-//   - weight scales come 16 bytes of the channel's scale row (8 steps) per load, every
-//     eighth step, one window ahead;
+//     for channel n: 8 (MXFP4) or 16 (fp8b32) contiguous code bytes, one load in the store
+//     order and in the GEMV's read order alike, and the scale of their 32-input block.
+//     Eight hardware conversions (v_cvt_scalef32_pk_bf16_fp4 / _fp8, the scale applied
+//     exactly) give the bf16 operands of the step's two 16x16x32 products: inputs
+//     16 q .. 16 q + 7, then 16 q + 8 .. 16 q + 15. The activations take the same inputs in
+//     the same order, so every product sums the same terms as the natural order.
+//   - weight scales come 16 bytes of the scale row (the channel's, or its 32-channel
+//     block's: 8 steps) per load, every eighth step, one window ahead;
 //   - activations: the bf16 rows of the item are gathered into a 3-stage LDS ring, two steps
 //     ahead, by loads that write LDS (16-byte chunk c of row r at position c ^ (r % 8));
 //     each wave loads 32 of the 128 rows. Lane (r, q) reads chunks 2 q and 2 q + 1 of row r.
@@ -44,10 +45,39 @@ struct MbShared {
 // strip).
 constexpr int mb_step_loads() { return 4 + MB_NB; }
 
-template <int LAYOUT>
+// A lane's code bytes of one step and strip: 8 (MXFP4) or 16 (fp8b32).
+template <int FMT>
+struct MbCodes;
+template <>
+struct MbCodes<MX_FP4> {
+  u32x2 v;
+  __device__ void load(GemmRsrc r, uint32_t vo, uint32_t so) {
+    v = __builtin_amdgcn_raw_buffer_load_b64(r, vo, so, 0);
+  }
+  // bf16 operands of inputs 16 q .. 16 q + 7 (b0) and 16 q + 8 .. 16 q + 15 (b1)
+  __device__ void convert(float sc, uint32_t b0[4], uint32_t b1[4]) const {
+    fp4x8_to_bf16(v.x, sc, b0);
+    fp4x8_to_bf16(v.y, sc, b1);
+  }
+};
+template <>
+struct MbCodes<MX_FP8B32> {
+  u32x4 v;
+  __device__ void load(GemmRsrc r, uint32_t vo, uint32_t so) {
+    v = __builtin_amdgcn_raw_buffer_load_b128(r, vo, so, 0);
+  }
+  __device__ void convert(float sc, uint32_t b0[4], uint32_t b1[4]) const {
+    fp8x4_to_bf16(v.x, sc, b0);
+    fp8x4_to_bf16(v.y, sc, b0 + 2);
+    fp8x4_to_bf16(v.z, sc, b1);
+    fp8x4_to_bf16(v.w, sc, b1 + 2);
+  }
+};
+
+template <int FMT, int LAYOUT>
 __device__ void mb_item(const Mxfp4GemmArgs& a, MbShared& sh, const uint8_t* unit, int grp,
                         int nrows, int ns) {
-  using U = MxUnit<MX_FP4>;
+  using U = MxUnit<FMT>;
   const int tid = threadIdx.x, lane = tid & 63, q = lane >> 4, n = lane & 15;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int nsteps = a.in / MB_STEP;  // a multiple of 8 (in is a multiple of 512)
@@ -74,31 +104,32 @@ __device__ void mb_item(const Mxfp4GemmArgs& a, MbShared& sh, const uint8_t* uni
   };
 
   // weights: lane (n, q) of strip nb: channel o = 128 grp + 32 w + 16 nb + n (channels past
-  // the group read its last one; their outputs are not stored). Step kk's 8 bytes: blocks
-  // 2 kk and 2 kk + 1 are adjacent in both layouts, and inputs 16 q .. 16 q + 15 are bytes
-  // 8 q .. 8 q + 7 of the pair.
+  // the group read its last one; their outputs are not stored). Step kk's code bytes: blocks
+  // 2 kk and 2 kk + 1 (kCB bytes each) are adjacent in both layouts, and inputs
+  // 16 q .. 16 q + 15 are bytes q kCB / 2 .. (q + 1) kCB / 2 - 1 of the pair.
   const GemmRsrc rb = gemm_rsrc(unit, (uint32_t)U::unit_bytes(a.out, a.in));
   uint32_t bvo[MB_NB], bso[MB_NB];
 #pragma unroll
   for (int nb = 0; nb < MB_NB; ++nb) {
     const int oc = 32 * w + 16 * nb + n;
     const int o = grp * 128 + (oc < 16 * ns ? oc : 16 * ns - 1);
-    bvo[nb] = (LAYOUT ? U::packed_at(a.out, a.in, o, 0) : U::stored_at(a.in, o, 0)) + 8u * q;
-    bso[nb] = U::scale_at(a.out, a.in, o, 0);  // the channel's scale row (16-byte aligned)
+    bvo[nb] = (LAYOUT ? U::packed_at(a.out, a.in, o, 0) : U::stored_at(a.in, o, 0)) +
+              (U::kCB / 2) * (uint32_t)q;
+    bso[nb] = U::scale_at(a.out, a.in, o, 0);  // the scale row (16-byte aligned)
   }
-  // scalar offset of step kk's codes: store order 32 kk; read order, per 128-input step of
-  // the group (ns strips of 64 kCB bytes), 32 bytes for its second half
+  // scalar offset of step kk's codes: store order 2 kCB kk; read order, per 128-input step
+  // of the group (ns strips of 64 kCB bytes), 2 kCB bytes for its second half
   const uint32_t pstep = (uint32_t)ns * 64u * U::kCB;
   auto code_off = [&](int kk) {
-    return LAYOUT ? (uint32_t)(kk >> 1) * pstep + 32u * (uint32_t)(kk & 1) : 32u * (uint32_t)kk;
+    return LAYOUT ? (uint32_t)(kk >> 1) * pstep + 2u * U::kCB * (uint32_t)(kk & 1)
+                  : 2u * U::kCB * (uint32_t)kk;
   };
-  u32x2 bc[2][MB_NB];
+  MbCodes<FMT> bc[2][MB_NB];
   auto load_b = [&](int slot, int kk) {
 #pragma unroll
-    for (int nb = 0; nb < MB_NB; ++nb)
-      bc[slot][nb] = __builtin_amdgcn_raw_buffer_load_b64(rb, bvo[nb], code_off(kk), 0);
+    for (int nb = 0; nb < MB_NB; ++nb) bc[slot][nb].load(rb, bvo[nb], code_off(kk));
   };
-  // scale windows: 16 bytes of the channel's scale row (blocks 16 wi .. 16 wi + 15, steps
+  // scale windows: 16 bytes of the scale row (blocks 16 wi .. 16 wi + 15, steps
   // 8 wi .. 8 wi + 7); step 8 wi + t uses byte 2 t + q / 2. Two windows alternate.
   const int nwin = nsteps / 8;
   u32x4 sw[2][MB_NB];
@@ -145,8 +176,7 @@ __device__ void mb_item(const Mxfp4GemmArgs& a, MbShared& sh, const uint8_t* uni
     for (int nb = 0; nb < MB_NB; ++nb) {
       const int bi = 2 * t + (q >> 1);  // scale byte of this lane's block in the window
       const float sc = e8m0_to_f32((sw[ws][nb][bi >> 2] >> (8 * (bi & 3))) & 0xFFu);
-      fp4x8_to_bf16(bc[d][nb].x, sc, b0[nb]);
-      fp4x8_to_bf16(bc[d][nb].y, sc, b1[nb]);
+      bc[d][nb].convert(sc, b0[nb], b1[nb]);
     }
     load_b(d, nxt);  // the slot just converted, for step kk + 2
     const uint8_t* st = sh.a[kk % MB_STAGES];
@@ -193,6 +223,7 @@ __device__ void mb_item(const Mxfp4GemmArgs& a, MbShared& sh, const uint8_t* uni
   }
 }
 
+template <int FMT>
 __global__ __launch_bounds__(MB_THREADS, 3) void mxfp4_prefill_kernel(Mxfp4GemmArgs a) {
   __shared__ MbShared sh;
   int item, grp;
@@ -206,19 +237,21 @@ __global__ __launch_bounds__(MB_THREADS, 3) void mxfp4_prefill_kernel(Mxfp4GemmA
   }
   __syncthreads();
   const int ns = min(8, a.out / 16 - grp * 8);
-  const uint8_t* unit = a.units + (size_t)e * MxUnit<MX_FP4>::unit_bytes(a.out, a.in);
+  const uint8_t* unit = a.units + (size_t)e * MxUnit<FMT>::unit_bytes(a.out, a.in);
   if (a.layout)
-    mb_item<1>(a, sh, unit, grp, nrows, ns);
+    mb_item<FMT, 1>(a, sh, unit, grp, nrows, ns);
   else
-    mb_item<0>(a, sh, unit, grp, nrows, ns);
+    mb_item<FMT, 0>(a, sh, unit, grp, nrows, ns);
 }
 
 }  // namespace
 
-hipError_t launch_mxfp4_prefill(const Mxfp4GemmArgs& a, hipStream_t s) {
+hipError_t launch_mxfp4_gemm(const Mxfp4GemmArgs& a, hipStream_t s) {
   const int blocks = gemm_grid(a.max_items, a.groups);
   if (blocks == 0) return hipSuccess;
-  return launch_timed(mxfp4_prefill_kernel, dim3(blocks), dim3(MB_THREADS), s, a);
+  if (a.fmt == MX_FP8B32)
+    return launch_timed(mxfp4_prefill_kernel<MX_FP8B32>, dim3(blocks), dim3(MB_THREADS), s, a);
+  return launch_timed(mxfp4_prefill_kernel<MX_FP4>, dim3(blocks), dim3(MB_THREADS), s, a);
 }
 
 }  // namespace tq

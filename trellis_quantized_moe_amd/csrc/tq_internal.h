@@ -215,10 +215,8 @@ struct Mxfp4GemmArgs {
   float* y;
   int E, out, in, topk, groups, max_items;
 };
+// The prefill GEMM on the bf16 matrix cores, both formats (mxfp4_prefill.hip).
 hipError_t launch_mxfp4_gemm(const Mxfp4GemmArgs& a, hipStream_t s);
-// The MXFP4 prefill on the bf16 matrix cores (mxfp4_prefill.hip; launch_mxfp4_gemm calls it
-// for MX_FP4).
-hipError_t launch_mxfp4_prefill(const Mxfp4GemmArgs& a, hipStream_t s);
 
 // MXFP8 activations (FORMAT F18): bf16 [rows][n] -> E4M3 codes [rows][n] and E8M0 block scales
 // [rows][n / 32].
