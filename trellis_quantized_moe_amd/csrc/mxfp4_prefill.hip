@@ -180,18 +180,26 @@ __device__ void mb_item(const Mxfp4GemmArgs& a, MbShared& sh, const uint8_t* uni
     }
     load_b(d, nxt);  // the slot just converted, for step kk + 2
     const uint8_t* st = sh.a[kk % MB_STAGES];
+    // the first half's products of every row block, then the second half's: the two
+    // products of one accumulator are 16 products apart
 #pragma unroll
     for (int mb = 0; mb < 8; ++mb) {
       if (mb < mblocks) {
         const u32x4 a0 = *reinterpret_cast<const u32x4*>(st + 16 * MB_ROW * mb + rd0);
-        const u32x4 a1 = *reinterpret_cast<const u32x4*>(st + 16 * MB_ROW * mb + rd1);
 #pragma unroll
-        for (int nb = 0; nb < MB_NB; ++nb) {
+        for (int nb = 0; nb < MB_NB; ++nb)
           acc[mb][nb] = mfma_bf16(a0, (u32x4){b0[nb][0], b0[nb][1], b0[nb][2], b0[nb][3]},
                                   acc[mb][nb]);
+      }
+    }
+#pragma unroll
+    for (int mb = 0; mb < 8; ++mb) {
+      if (mb < mblocks) {
+        const u32x4 a1 = *reinterpret_cast<const u32x4*>(st + 16 * MB_ROW * mb + rd1);
+#pragma unroll
+        for (int nb = 0; nb < MB_NB; ++nb)
           acc[mb][nb] = mfma_bf16(a1, (u32x4){b1[nb][0], b1[nb][1], b1[nb][2], b1[nb][3]},
                                   acc[mb][nb]);
-        }
       }
     }
   };
