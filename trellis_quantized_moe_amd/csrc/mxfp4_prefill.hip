@@ -17,8 +17,10 @@
 //   - weight scales come 16 bytes of the scale row (the channel's, or its 32-channel
 //     block's: 8 steps) per load, every eighth step, one window ahead;
 //   - activations: the bf16 rows of the item are gathered into a 3-stage LDS ring, two steps
-//     ahead, by loads that write LDS (16-byte chunk c of row r at position c ^ (r % 8));
-//     each wave loads 32 of the 128 rows. Lane (r, q) reads chunks 2 q and 2 q + 1 of row r.
+//     ahead, by loads that write LDS; each wave loads 32 of the 128 rows. Lane (r, q) needs
+//     16-byte chunks 2 q and 2 q + 1 of row r, stored at positions q ^ (r % 8) and
+//     (4 + q) ^ (r % 8) of the row (chunk 2 p at p, 2 p + 1 at 4 + p, then the xor): the 8
+//     lanes the LDS serves together then hit 8 different chunk columns.
 // Three items fit on a compute unit (49 KB of LDS each). The epilogue multiplies by the gate
 // and writes each output once.
 #include "gemm_core.h"
@@ -83,14 +85,16 @@ __device__ void mb_item(const Mxfp4GemmArgs& a, MbShared& sh, const uint8_t* uni
   const int nsteps = a.in / MB_STEP;  // a multiple of 8 (in is a multiple of 512)
 
   // activation chunks: instruction j of wave w fills rows 32 w + 8 j .. + 7 of a stage; lane
-  // l writes position l % 8 of row 32 w + 8 j + l / 8, which holds chunk (l % 8) ^ (row % 8).
-  // Rows past the item load from beyond the buffer's end (x_bytes < 2^31) and read zeros.
+  // l writes position l % 8 of row 32 w + 8 j + l / 8, which holds chunk 2 (x % 4) + x / 4,
+  // x = (l % 8) ^ (row % 8). Rows past the item load from beyond the buffer's end
+  // (x_bytes < 2^31) and read zeros.
   const GemmRsrc ra = gemm_rsrc(a.x, a.x_bytes);
   uint32_t avo[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int r = 32 * w + 8 * j + (lane >> 3);
-    const int c = (lane & 7) ^ (r & 7);
+    const int x = (lane & 7) ^ (r & 7);
+    const int c = 2 * (x & 3) + (x >> 2);
     avo[j] = r < nrows ? 2u * (uint32_t)((sh.slot[r] / a.topk) * a.in) + 16u * c : 0x80000000u;
   }
   // stage st receives the chunks of step kk (past the last step: the last step's again, into
@@ -148,8 +152,8 @@ __device__ void mb_item(const Mxfp4GemmArgs& a, MbShared& sh, const uint8_t* uni
   int mblocks = (nrows + 15) / 16;
   mblocks = mblocks > 8 ? 8 : mblocks;
   // lane (r, q) reads chunks 2 q and 2 q + 1 of row r = 16 mb + n (row % 8 = n % 8)
-  const uint32_t rd0 = MB_ROW * n + 16u * ((2 * q) ^ (n & 7));
-  const uint32_t rd1 = MB_ROW * n + 16u * ((2 * q + 1) ^ (n & 7));
+  const uint32_t rd0 = MB_ROW * n + 16u * (q ^ (n & 7));
+  const uint32_t rd1 = MB_ROW * n + 16u * ((4 + q) ^ (n & 7));
 
   // prologue: the first scale window, steps 0 and 1
   load_s(0, 0);

@@ -14,9 +14,10 @@
 //   - activations: the prepared f16 rows (the same pair layout) are gathered straight
 //     from global memory into LDS by buffer loads that write LDS (no registers), into a
 //     ring of three 16 KB stages, two steps ahead; each wave loads 32 of the 128 rows. A
-//     stage holds 128 rows x 128 bytes in 16-byte chunks, chunk c of row r stored at
-//     position c ^ ((r / 2) % 8) of the row, so the operand reads of one 16-lane group hit
-//     16 different chunk columns.
+//     stage holds 128 rows x 128 bytes in 16-byte chunks; lane group g of the operand reads
+//     needs chunks 2 g and 2 g + 1 of a row, stored at positions g ^ (r % 8) and
+//     (4 + g) ^ (r % 8) of row r (chunk 2 p at p, 2 p + 1 at 4 + p, then the xor), so the 8
+//     lanes the LDS serves together hit 8 different chunk columns.
 //   - codes are loaded two steps ahead into registers (one load per strip and step).
 // Three items fit on a compute unit (50 KB of LDS each, 142 registers per lane), so every
 // item of a prefill chunk is resident at once and each SIMD runs three waves, whose decode
@@ -77,14 +78,16 @@ __device__ __forceinline__ void tg_item(const TrellisGemmArgs& a, TgShared& sh,
 
   // activation loads: instruction j of wave w fills rows TG_AROWS w + 8 j .. + 7 of a stage;
   // lane l writes LDS chunk l of the instruction's 1 KB, i.e. row TG_AROWS w + 8 j + l / 8,
-  // position l % 8, which holds chunk (l % 8) ^ ((row / 2) % 8) of the row's 128 bytes. Rows
-  // past the item load from beyond the buffer's end (x_bytes < 2^31) and read zeros.
+  // position l % 8, which holds chunk 2 (x % 4) + x / 4 of the row's 128 bytes, x =
+  // (l % 8) ^ (row % 8). Rows past the item load from beyond the buffer's end
+  // (x_bytes < 2^31) and read zeros.
   const GemmRsrc ra = gemm_rsrc(a.xp, a.x_bytes);
   uint32_t dvo[TG_AROWS / 8];
 #pragma unroll
   for (int j = 0; j < TG_AROWS / 8; ++j) {
     const int r = TG_AROWS * w + 8 * j + (lane >> 3);
-    const int c = (lane & 7) ^ ((r >> 1) & 7);
+    const int x = (lane & 7) ^ (r & 7);
+    const int c = 2 * (x & 3) + (x >> 2);
     dvo[j] = r < nrows ? 2u * (uint32_t)((sh.slot[r] / a.topk) * a.in) + 16u * c : 0x80000000u;
   }
   auto load_a = [&](int kk) {
@@ -147,8 +150,8 @@ __device__ __forceinline__ void tg_item(const TrellisGemmArgs& a, TgShared& sh,
     for (int nb = 0; nb < TG_NS; ++nb) acc[mb][nb] = (f32x4){0.f, 0.f, 0.f, 0.f};
   const int mblocks = (nrows + 15) >> 4;
   // operand reads of lane (g, n): row 16 mb + n, chunks 2 g and 2 g + 1 of the step
-  const uint32_t rd0 = 128u * n + 16u * ((2 * g) ^ (n >> 1));
-  const uint32_t rd1 = 128u * n + 16u * ((2 * g + 1) ^ (n >> 1));
+  const uint32_t rd0 = 128u * n + 16u * (g ^ (n & 7));
+  const uint32_t rd1 = 128u * n + 16u * ((4 + g) ^ (n & 7));
 
   // B0 / B1: operand registers of the step's first / second product for each strip (pairs
   // 0..3 / 4..7 of the lane's tile column). For K = 2, 3 the halves are decoded apart, so
