@@ -76,7 +76,11 @@ struct MbCodes<MX_FP8B32> {
   }
 };
 
-template <int FMT, int LAYOUT>
+// MBK: the row blocks of 16 the products run over (the item's rows rounded up to an even
+// count of blocks; the rows past the item are zeros in the stages). A constant, so that the
+// products of a step form one straight block in which the operand reads run ahead of the
+// matrix-core work instead of each waiting on its own read.
+template <int FMT, int LAYOUT, int MBK>
 __device__ void mb_item(const Mxfp4GemmArgs& a, MbShared& sh, const uint8_t* unit, int grp,
                         int nrows, int ns) {
   using U = MxUnit<FMT>;
@@ -144,13 +148,11 @@ __device__ void mb_item(const Mxfp4GemmArgs& a, MbShared& sh, const uint8_t* uni
       sw[slot][nb] = __builtin_amdgcn_raw_buffer_load_b128(rb, bso[nb], off, 0);
   };
 
-  f32x4 acc[8][MB_NB];
+  f32x4 acc[MBK][MB_NB];
 #pragma unroll
-  for (int mb = 0; mb < 8; ++mb)
+  for (int mb = 0; mb < MBK; ++mb)
 #pragma unroll
     for (int nb = 0; nb < MB_NB; ++nb) acc[mb][nb] = (f32x4){0.f, 0.f, 0.f, 0.f};
-  int mblocks = (nrows + 15) / 16;
-  mblocks = mblocks > 8 ? 8 : mblocks;
   // lane (r, q) reads chunks 2 q and 2 q + 1 of row r = 16 mb + n (row % 8 = n % 8)
   const uint32_t rd0 = MB_ROW * n + 16u * (q ^ (n & 7));
   const uint32_t rd1 = MB_ROW * n + 16u * ((4 + q) ^ (n & 7));
@@ -187,24 +189,20 @@ __device__ void mb_item(const Mxfp4GemmArgs& a, MbShared& sh, const uint8_t* uni
     // the first half's products of every row block, then the second half's: the two
     // products of one accumulator are 16 products apart
 #pragma unroll
-    for (int mb = 0; mb < 8; ++mb) {
-      if (mb < mblocks) {
-        const u32x4 a0 = *reinterpret_cast<const u32x4*>(st + 16 * MB_ROW * mb + rd0);
+    for (int mb = 0; mb < MBK; ++mb) {
+      const u32x4 a0 = *reinterpret_cast<const u32x4*>(st + 16 * MB_ROW * mb + rd0);
 #pragma unroll
-        for (int nb = 0; nb < MB_NB; ++nb)
-          acc[mb][nb] = mfma_bf16(a0, (u32x4){b0[nb][0], b0[nb][1], b0[nb][2], b0[nb][3]},
-                                  acc[mb][nb]);
-      }
+      for (int nb = 0; nb < MB_NB; ++nb)
+        acc[mb][nb] = mfma_bf16(a0, (u32x4){b0[nb][0], b0[nb][1], b0[nb][2], b0[nb][3]},
+                                acc[mb][nb]);
     }
 #pragma unroll
-    for (int mb = 0; mb < 8; ++mb) {
-      if (mb < mblocks) {
-        const u32x4 a1 = *reinterpret_cast<const u32x4*>(st + 16 * MB_ROW * mb + rd1);
+    for (int mb = 0; mb < MBK; ++mb) {
+      const u32x4 a1 = *reinterpret_cast<const u32x4*>(st + 16 * MB_ROW * mb + rd1);
 #pragma unroll
-        for (int nb = 0; nb < MB_NB; ++nb)
-          acc[mb][nb] = mfma_bf16(a1, (u32x4){b1[nb][0], b1[nb][1], b1[nb][2], b1[nb][3]},
-                                  acc[mb][nb]);
-      }
+      for (int nb = 0; nb < MB_NB; ++nb)
+        acc[mb][nb] = mfma_bf16(a1, (u32x4){b1[nb][0], b1[nb][1], b1[nb][2], b1[nb][3]},
+                                acc[mb][nb]);
     }
   };
   for (int kk = 0; kk < nsteps; kk += 16) {
@@ -224,7 +222,7 @@ __device__ void mb_item(const Mxfp4GemmArgs& a, MbShared& sh, const uint8_t* uni
     if (oc < 16 * ns) {
       const int o = grp * 128 + oc;
 #pragma unroll
-      for (int mb = 0; mb < 8; ++mb) {
+      for (int mb = 0; mb < MBK; ++mb) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int row = 16 * mb + 4 * q + i;
@@ -232,6 +230,17 @@ __device__ void mb_item(const Mxfp4GemmArgs& a, MbShared& sh, const uint8_t* uni
         }
       }
     }
+  }
+}
+
+template <int FMT, int LAYOUT>
+__device__ void mb_rows(const Mxfp4GemmArgs& a, MbShared& sh, const uint8_t* unit, int grp,
+                        int nrows, int ns) {
+  switch ((nrows + 31) >> 5) {
+    case 1: mb_item<FMT, LAYOUT, 2>(a, sh, unit, grp, nrows, ns); break;
+    case 2: mb_item<FMT, LAYOUT, 4>(a, sh, unit, grp, nrows, ns); break;
+    case 3: mb_item<FMT, LAYOUT, 6>(a, sh, unit, grp, nrows, ns); break;
+    default: mb_item<FMT, LAYOUT, 8>(a, sh, unit, grp, nrows, ns); break;
   }
 }
 
@@ -251,9 +260,9 @@ __global__ __launch_bounds__(MB_THREADS, 3) void mxfp4_prefill_kernel(Mxfp4GemmA
   const int ns = min(8, a.out / 16 - grp * 8);
   const uint8_t* unit = a.units + (size_t)e * MxUnit<FMT>::unit_bytes(a.out, a.in);
   if (a.layout)
-    mb_item<FMT, 1>(a, sh, unit, grp, nrows, ns);
+    mb_rows<FMT, 1>(a, sh, unit, grp, nrows, ns);
   else
-    mb_item<FMT, 0>(a, sh, unit, grp, nrows, ns);
+    mb_rows<FMT, 0>(a, sh, unit, grp, nrows, ns);
 }
 
 }  // namespace

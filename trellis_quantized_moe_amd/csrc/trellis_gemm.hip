@@ -148,7 +148,6 @@ __device__ __forceinline__ void tg_item(const TrellisGemmArgs& a, TgShared& sh,
   for (int mb = 0; mb < 8; ++mb)
 #pragma unroll
     for (int nb = 0; nb < TG_NS; ++nb) acc[mb][nb] = (f32x4){0.f, 0.f, 0.f, 0.f};
-  const int mblocks = (nrows + 15) >> 4;
   // operand reads of lane (g, n): row 16 mb + n, chunks 2 g and 2 g + 1 of the step
   const uint32_t rd0 = 128u * n + 16u * (g ^ (n & 7));
   const uint32_t rd1 = 128u * n + 16u * ((4 + g) ^ (n & 7));
@@ -173,17 +172,17 @@ __device__ __forceinline__ void tg_item(const TrellisGemmArgs& a, TgShared& sh,
       prefill_full<K>(c.w[0], c.w[K == 2 ? 0 : 1], row_next(c.w[0]), sel3, B0[nb], B1[nb]);
     }
   };
-  auto products = [&](const uint8_t* st, uint32_t rd, const uint32_t Bh[TG_NS][4], auto full_tag) {
-    constexpr bool FULL = decltype(full_tag)::value;
+  // the products of a step over the first MBK row blocks (a constant: one straight block in
+  // which the operand reads run ahead of the matrix-core work; rows past the item are zeros)
+  auto products = [&](const uint8_t* st, uint32_t rd, const uint32_t Bh[TG_NS][4], auto mbk) {
+    constexpr int MBK = decltype(mbk)::value;
 #pragma unroll
-    for (int mb = 0; mb < 8; ++mb) {
-      if (FULL || mb < mblocks) {
-        const u32x4 av = *reinterpret_cast<const u32x4*>(st + 2048 * mb + rd);
+    for (int mb = 0; mb < MBK; ++mb) {
+      const u32x4 av = *reinterpret_cast<const u32x4*>(st + 2048 * mb + rd);
 #pragma unroll
-        for (int nb = 0; nb < TG_NS; ++nb)
-          acc[mb][nb] = mfma_f16(av, (u32x4){Bh[nb][0], Bh[nb][1], Bh[nb][2], Bh[nb][3]},
-                                 acc[mb][nb]);
-      }
+      for (int nb = 0; nb < TG_NS; ++nb)
+        acc[mb][nb] = mfma_f16(av, (u32x4){Bh[nb][0], Bh[nb][1], Bh[nb][2], Bh[nb][3]},
+                               acc[mb][nb]);
     }
   };
 
@@ -197,7 +196,7 @@ __device__ __forceinline__ void tg_item(const TrellisGemmArgs& a, TgShared& sh,
   else
     dec_half(0, 0, B0);
 
-  auto run = [&](auto full_tag) {
+  auto run = [&](auto mbk) {
     for (int kk = 0; kk < nsteps; kk += 2) {
 #pragma unroll
       for (int d = 0; d < 2; ++d) {
@@ -211,8 +210,8 @@ __device__ __forceinline__ void tg_item(const TrellisGemmArgs& a, TgShared& sh,
         load_a(nxt);
         const uint8_t* st = sh.a[step % TG_STAGES];
         if constexpr (K == 4) {
-          products(st, rd0, B0, full_tag);
-          products(st, rd1, B1, full_tag);
+          products(st, rd0, B0, mbk);
+          products(st, rd1, B1, mbk);
           load_codes(d, nxt);
           dec_full(d ^ 1);  // the next step (past the last: unused)
         } else {
@@ -220,19 +219,22 @@ __device__ __forceinline__ void tg_item(const TrellisGemmArgs& a, TgShared& sh,
           // barrier keeps the next step's first half from being decoded while this step's
           // first-half products still read B0
           dec_half(d, 1, B1);
-          products(st, rd0, B0, full_tag);
+          products(st, rd0, B0, mbk);
           load_codes(d, nxt);
           __builtin_amdgcn_sched_barrier(0);
           dec_half(d ^ 1, 0, B0);  // the next step's first half (past the last: unused)
-          products(st, rd1, B1, full_tag);
+          products(st, rd1, B1, mbk);
         }
       }
     }
   };
-  if (mblocks == 8)
-    run(std::integral_constant<bool, true>());
-  else
-    run(std::integral_constant<bool, false>());
+  // the item's rows rounded up to an even count of row blocks
+  switch ((nrows + 31) >> 5) {
+    case 1: run(std::integral_constant<int, 2>()); break;
+    case 2: run(std::integral_constant<int, 4>()); break;
+    case 3: run(std::integral_constant<int, 6>()); break;
+    default: run(std::integral_constant<int, 8>()); break;
+  }
   // no load may still be writing this workgroup's LDS when it ends
   wait_vmcnt<0>();
 
