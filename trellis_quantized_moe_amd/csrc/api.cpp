@@ -213,6 +213,9 @@ WsLayout ws_layout(int64_t T, int topk, int E, int out, int in, uint32_t flags, 
     off += L.partial_bytes;
   } else {
     L.route_blocks = (int)((N + ROUTE_CHUNK - 1) / ROUTE_CHUNK);
+    // items placed by token range only where rows are shared between experts' items (a
+    // token has several experts), for up to 1024 experts
+    L.split_rows = (topk > 1 && E <= 1024) ? GEMM_SPLIT : 0;
     L.max_items = (int)((N + GEMM_MT - 1) / GEMM_MT) + E;
     const size_t start = off;
     L.counts = off;
@@ -420,6 +423,7 @@ int route_bucket(const int32_t* topk_ids, int64_t T, int32_t topk, int32_t E, in
   r.blocks = L.route_blocks;
   r.item_rows = tq::GEMM_MT;
   r.max_items = 0;
+  r.split_rows = 0;
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t err;
   if (r.N == 0) {
@@ -550,6 +554,7 @@ static int run_route(const tq::WsLayout& L, void* ws, const int32_t* ids, int64_
   r.blocks = L.route_blocks;
   r.item_rows = tq::GEMM_MT;
   r.max_items = L.max_items;
+  r.split_rows = L.split_rows;
   hipError_t err = tq::launch_route(r, s);
   if (err != hipSuccess) return hip_fail(err, "route launch");
   return TQ_OK;

@@ -5,10 +5,23 @@
 //               with one ballot per id bit, counts run in LDS), then the block adds the
 //               earlier waves' counts. The block's counts go to hist.
 //   2. scan:    one workgroup turns hist into per-(block, expert) bases, per-expert counts
-//               and offsets, and the list of (expert, row0, nrows) work items.
+//               and offsets, and the list of (expert, row0, nrows) work items, laid out for
+//               the 8 XCDs (below).
 //   3. scatter: pairs[base[block][e] + rank] = slot; empty (-1) slots get zero outputs and
 //               invalid ids NaN outputs plus a status bit.
 // No step depends on timing, so the order is the same on every run.
+//
+// Work items and the XCDs. The prefill GEMMs give the 8 XCDs (each with its own L2) 8
+// contiguous, equal segments of the item list. Every item gathers its rows' activations, and
+// a token's rows sit in topk experts' items: rows gathered on the same XCD at about the same
+// time come from its L2. The slot order is token-major, so the rank blocks cut it into 8
+// token ranges (block b in range 8 b / blocks), and an expert's slots, in slot order, run
+// through the ranges in turn. With split_rows > 0, the items of an expert with at least
+// split_rows slots go to the segment of the range that holds their middle row (row 64 of the
+// item, or its last row), opening that segment; the other experts' items, in expert order,
+// fill the segments up to an equal share. The items are the same either way (each expert's
+// slots in runs of item_rows); without a split the list is in expert order. Which item
+// computes a slot changes nothing in its result.
 #include "tq_device.h"
 #include "tq_internal.h"
 
@@ -20,6 +33,8 @@ constexpr int RANK_BLOCK = ROUTE_CHUNK;        // slots per rank block
 constexpr int RANK_WAVES = 4;                  // waves per rank block
 constexpr int RANK_ROUNDS = RANK_BLOCK / (64 * RANK_WAVES);  // 64-slot rounds per wave
 constexpr int MAX_E = 4096;
+constexpr int SCAN_PASSES = MAX_E / 1024;  // experts per scan thread
+constexpr int XCDS = 8;
 
 // Wave w of rank block b ranks slots b * RANK_BLOCK + w * (RANK_BLOCK / RANK_WAVES) .. in
 // rounds of 64: the lanes holding the same expert are found with one ballot per id bit, and a
@@ -109,6 +124,50 @@ __device__ int block_scan_1024(int v, int* wave_sums, int* total) {
   return res;
 }
 
+// The same for XCDS ints per thread at once: res[x] is the exclusive prefix of v[x], tot[x]
+// (shared) its total.
+__device__ void block_scan8_1024(const int v[XCDS], int res[XCDS], int (*sums)[XCDS], int* tot) {
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  int incl[XCDS];
+#pragma unroll
+  for (int x = 0; x < XCDS; ++x) incl[x] = v[x];
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+#pragma unroll
+    for (int x = 0; x < XCDS; ++x) {
+      const int t = __shfl_up(incl[x], d, 64);
+      if (lane >= d) incl[x] += t;
+    }
+  }
+  if (lane == 63) {
+#pragma unroll
+    for (int x = 0; x < XCDS; ++x) sums[w][x] = incl[x];
+  }
+  __syncthreads();
+  if (tid < XCDS) {
+    int run = 0;
+    for (int k = 0; k < 16; ++k) {
+      const int t = sums[k][tid];
+      sums[k][tid] = run;
+      run += t;
+    }
+    tot[tid] = run;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int x = 0; x < XCDS; ++x) res[x] = sums[w][x] + incl[x] - v[x];
+  __syncthreads();
+}
+
+// The token range of an expert's slot row r, given the first row of each range (start[0] =
+// 0, non-decreasing).
+__device__ __forceinline__ int item_range(const int start[XCDS], int r) {
+  int x = 0;
+#pragma unroll
+  for (int j = 1; j < XCDS; ++j) x += r >= start[j] ? 1 : 0;
+  return x;
+}
+
 // Thread e reads its column of hist (the count of expert e in each rank block) in batches
 // of SCAN_BATCH independent loads, once for the count and once more for the bases. The loads
 // take one per-thread offset (4 e) and a scalar one per block, so a batch in flight costs
@@ -124,21 +183,40 @@ __device__ __forceinline__ void hist_batch(__amdgpu_buffer_rsrc_t rh, int E, int
                : 0;
 }
 
+// SPLIT: items placed by token range (a.E <= 1024, one expert per thread); else the
+// experts' items in expert order, up to MAX_E experts.
+template <bool SPLIT>
 __global__ __launch_bounds__(1024) void route_scan_kernel(RouteArgs a) {
+  constexpr int PASSES = SPLIT ? 1 : SCAN_PASSES;
   __shared__ int wave_sums[16];
   __shared__ int total;
-  __shared__ int carry[2];
+  __shared__ int sums8[16][XCDS];
+  __shared__ int tot8[XCDS];
+  __shared__ int carry[2 + XCDS];  // slots, other experts' items, split items per range
   const int tid = threadIdx.x;
-  if (tid == 0) {
-    carry[0] = 0;
-    carry[1] = 0;
-  }
+  if (tid < 2 + XCDS) carry[tid] = 0;
   __syncthreads();
   const __amdgpu_buffer_rsrc_t rh = __builtin_amdgcn_make_buffer_rsrc(
       a.hist, (short)0, (int)((size_t)a.blocks * a.E * 4), 0x00020000);
-  // per expert: count, then offsets (exclusive scan) and item bases, 1024 experts a pass
-  for (int e0 = 0; e0 < a.E; e0 += 1024) {
-    const int e = e0 + tid;
+  const int R = a.item_rows;
+  // per expert of this thread (e = 1024 p + tid): slots and offset, whether it is placed by
+  // range, the first row of each range among its slots and the list position of its first
+  // item placed in range x among all items placed in range x, or the position of its first
+  // item among the other experts' items
+  int cnt[PASSES], eoff[PASSES], psm[PASSES];
+  int cx[PASSES][XCDS], pbx[PASSES][XCDS];
+  bool big[PASSES];
+#pragma unroll
+  for (int p = 0; p < PASSES; ++p) {
+    cnt[p] = eoff[p] = psm[p] = 0;
+    big[p] = false;
+#pragma unroll
+    for (int x = 0; x < XCDS; ++x) cx[p][x] = pbx[p][x] = 0;
+  }
+#pragma unroll
+  for (int p = 0; p < PASSES; ++p) {
+    if (p * 1024 >= a.E) break;
+    const int e = p * 1024 + tid;
     const bool mine = e < a.E;
     int c = 0;
     if (mine) {
@@ -146,14 +224,18 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(RouteArgs a) {
         int t[SCAN_BATCH];
         hist_batch(rh, a.E, e, b0, a.blocks, t);
 #pragma unroll
-        for (int j = 0; j < SCAN_BATCH; ++j) c += t[j];
+        for (int j = 0; j < SCAN_BATCH; ++j) {
+          c += t[j];
+          if constexpr (SPLIT) {
+            const int xr = ((b0 + j) * XCDS) / a.blocks;
+#pragma unroll
+            for (int x = 0; x < XCDS; ++x) cx[p][x] += xr == x ? t[j] : 0;
+          }
+        }
       }
     }
-    const int ni = a.items ? (c + a.item_rows - 1) / a.item_rows : 0;
     const int off = block_scan_1024(c, wave_sums, &total) + carry[0];
     const int tc = total;
-    const int ib = block_scan_1024(ni, wave_sums, &total) + carry[1];
-    const int ti = total;
     if (mine) {
       a.counts[e] = c;
       a.offsets[e] = off;
@@ -167,25 +249,103 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(RouteArgs a) {
           run += t[j];
         }
       }
-      if (a.items) {
-        for (int k = 0; k < ni; ++k) {
-          const int r0 = k * a.item_rows;
-          const int rows = min(a.item_rows, c - r0);
-          reinterpret_cast<int4*>(a.items)[ib + k] = make_int4(e, off + r0, rows, 0);
+    }
+    cnt[p] = c;
+    eoff[p] = off;
+    big[p] = SPLIT && mine && c >= a.split_rows;
+    if constexpr (SPLIT) {
+      // cx becomes the first row of each range among the expert's slots
+      int run_r = 0;
+#pragma unroll
+      for (int x = 0; x < XCDS; ++x) {
+        const int t = cx[p][x];
+        cx[p][x] = run_r;
+        run_r += t;
+      }
+      int nb[XCDS], pb[XCDS];
+#pragma unroll
+      for (int x = 0; x < XCDS; ++x) nb[x] = 0;
+      if (big[p]) {
+        for (int r0 = 0; r0 < c; r0 += R) {
+          const int xi = item_range(cx[p], min(r0 + R / 2, c - 1));
+#pragma unroll
+          for (int x = 0; x < XCDS; ++x) nb[x] += xi == x ? 1 : 0;
         }
       }
+      block_scan8_1024(nb, pb, sums8, tot8);
+#pragma unroll
+      for (int x = 0; x < XCDS; ++x) pbx[p][x] = pb[x] + carry[2 + x];
     }
+    const int ns = (a.items && mine && !big[p]) ? (c + R - 1) / R : 0;
+    psm[p] = block_scan_1024(ns, wave_sums, &total) + carry[1];
+    const int ts = total;
     __syncthreads();
     if (tid == 0) {
       carry[0] += tc;
-      carry[1] += ti;
+      carry[1] += ts;
     }
+    if (SPLIT && tid < XCDS) carry[2 + tid] += tot8[tid];
     __syncthreads();
   }
-  if (tid == 0) {
-    a.offsets[a.E] = carry[0];
-    if (a.n_items) *a.n_items = carry[1];
+  if (tid == 0) a.offsets[a.E] = carry[0];
+  if (!a.items) return;
+
+  // segments: x holds the items placed in range x, then its share of the others' items
+  int B[XCDS], S[XCDS], seg[XCDS], ps0[XCDS];
+  const int small = carry[1];
+  int all = small;
+#pragma unroll
+  for (int x = 0; x < XCDS; ++x) {
+    B[x] = carry[2 + x];
+    all += B[x];
   }
+  const int share = (all + XCDS - 1) / XCDS;
+  int rem = small, run = 0, runs = 0;
+#pragma unroll
+  for (int x = 0; x < XCDS; ++x) {
+    S[x] = min(rem, max(0, share - B[x]));
+    rem -= S[x];
+  }
+  S[XCDS - 1] += rem;
+#pragma unroll
+  for (int x = 0; x < XCDS; ++x) {
+    seg[x] = run;
+    ps0[x] = runs;
+    run += B[x] + S[x];
+    runs += S[x];
+  }
+  int4* items = reinterpret_cast<int4*>(a.items);
+#pragma unroll
+  for (int p = 0; p < PASSES; ++p) {
+    const int e = p * 1024 + tid;
+    if (p * 1024 >= a.E || e >= a.E) break;
+    const int c = cnt[p];
+    if (big[p]) {
+      // the ranges of successive items never decrease: k counts the items placed in the
+      // current one
+      int xprev = -1, k = 0;
+      for (int r0 = 0; r0 < c; r0 += R) {
+        const int xi = item_range(cx[p], min(r0 + R / 2, c - 1));
+        k = xi == xprev ? k + 1 : 0;
+        xprev = xi;
+        int base = 0;
+#pragma unroll
+        for (int x = 0; x < XCDS; ++x)
+          if (x == xi) base = seg[x] + pbx[p][x];
+        items[base + k] = make_int4(e, eoff[p] + r0, min(R, c - r0), 0);
+      }
+    } else {
+      for (int k = 0; k * R < c; ++k) {
+        const int g = psm[p] + k;  // its place among the other experts' items
+        int pos = 0;
+#pragma unroll
+        for (int x = 0; x < XCDS; ++x)
+          if (g >= ps0[x] && g < ps0[x] + S[x]) pos = seg[x] + B[x] + (g - ps0[x]);
+        items[pos] = make_int4(e, eoff[p] + k * R, min(R, c - k * R), 0);
+      }
+    }
+  }
+  if (tid == 0) *a.n_items = all;
 }
 
 __global__ __launch_bounds__(256) void route_scatter_kernel(RouteArgs a) {
@@ -242,7 +402,10 @@ hipError_t launch_route(const RouteArgs& a, hipStream_t s) {
                      (int)a.N, a.E, idbits, a.rank, a.hist);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(route_scan_kernel, dim3(1), dim3(1024), 0, s, a);
+  if (a.items && a.split_rows > 0 && a.E <= 1024)
+    hipLaunchKernelGGL(route_scan_kernel<true>, dim3(1), dim3(1024), 0, s, a);
+  else
+    hipLaunchKernelGGL(route_scan_kernel<false>, dim3(1), dim3(1024), 0, s, a);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(route_scatter_kernel, dim3((unsigned)((a.N + 255) / 256)), dim3(256), 0, s,

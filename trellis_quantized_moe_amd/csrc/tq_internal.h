@@ -22,11 +22,13 @@ struct WsLayout {
   size_t info = 0, rec = 0, desc = 0, list = 0, slot_info = 0, prank = 0;
   size_t total = 0;
   int groups = 1, route_blocks = 1, max_items = 0;
+  int split_rows = 0;  // experts with at least this many slots have items placed by token range
   bool gemm = false;
 };
 
 constexpr int ROUTE_CHUNK = 2048;  // ids per route-count block
 constexpr int GEMM_MT = 128;       // token rows per prefill work item
+constexpr int GEMM_SPLIT = 256;    // slots from which an expert's items follow the token ranges
 constexpr int GEMV_MAXK = 16;      // tokens per decode-batch chunk (one MFMA row block)
 
 // ---- measurement hook (tq_time_kernel) -------------------------------------------------
@@ -250,6 +252,7 @@ struct RouteArgs {
   int32_t* pairs;     // [N]
   int32_t* items;     // [max_items][4] or null
   int32_t* n_items;   // [1] or null
+  int split_rows;     // 0: items in expert order
   float* y_special;   // per-slot output rows for empty / invalid slots, or null
   uint32_t* status;
   int blocks, item_rows, max_items;
