@@ -35,6 +35,8 @@ constexpr int RANK_ROUNDS = RANK_BLOCK / (64 * RANK_WAVES);  // 64-slot rounds p
 constexpr int MAX_E = 4096;
 constexpr int SCAN_PASSES = MAX_E / 1024;  // experts per scan thread
 constexpr int XCDS = 8;
+constexpr int XCD_CUS = 32;        // compute units per XCD
+constexpr int ORDER_ROUNDS = 4;    // item lists of up to 4096 are put in snake order
 
 // Wave w of rank block b ranks slots b * RANK_BLOCK + w * (RANK_BLOCK / RANK_WAVES) .. in
 // rounds of 64: the lanes holding the same expert are found with one ballot per id bit, and a
@@ -181,6 +183,84 @@ __device__ __forceinline__ void hist_batch(__amdgpu_buffer_rsrc_t rh, int E, int
     t[j] = b0 + j < blocks
                ? (int)__builtin_amdgcn_raw_buffer_load_b32(rh, 4u * e, 4u * (uint32_t)((b0 + j) * E), 0)
                : 0;
+}
+
+// Snake order within each segment of a list of one-group items. The workgroups of an XCD go
+// to its XCD_CUS compute units in turn, so items j, j + 32 and j + 64 of a segment share a
+// unit. The items of a segment are ranked by their row blocks of 32 (the products' work,
+// heaviest first; ties in list order) and dealt out in rounds of 32 that alternate
+// direction, so that every unit gets a similar amount. Every thread holds up to
+// ORDER_ROUNDS items (positions tid + 1024 m) between reading and writing the list.
+__device__ void snake_order(int4* items, int all, const int seg[XCDS], const int B[XCDS],
+                            const int S[XCDS]) {
+  __shared__ int sums8[16][XCDS];
+  __shared__ int tot8[XCDS];
+  __shared__ int cnt[XCDS][4];     // items per segment and class
+  __shared__ int segp[XCDS][4];    // items of each class before each segment's start
+  __shared__ int carry[4];
+  const int tid = threadIdx.x;
+  if (tid < XCDS * 4) {
+    cnt[tid >> 2][tid & 3] = 0;
+    segp[tid >> 2][tid & 3] = -1;
+  }
+  if (tid < 4) carry[tid] = 0;
+  __threadfence();  // the list, as written, is visible to every thread of the workgroup
+  __syncthreads();
+  int4 it[ORDER_ROUNDS];
+  int cl[ORDER_ROUNDS], sx[ORDER_ROUNDS], pk[ORDER_ROUNDS];
+#pragma unroll
+  for (int m = 0; m < ORDER_ROUNDS; ++m) {
+    const int i = m * 1024 + tid;
+    const bool valid = i < all;
+    it[m] = valid ? items[i] : make_int4(0, 0, 0, 0);
+    // class 0: 4 blocks of 32 rows (the heaviest) .. class 3: 1 block
+    cl[m] = valid ? 4 - min(4, (it[m].z + 31) >> 5) : -1;
+    sx[m] = 0;
+#pragma unroll
+    for (int x = 1; x < XCDS; ++x) sx[m] += i >= seg[x] ? 1 : 0;
+    int v[XCDS], pr[XCDS];
+#pragma unroll
+    for (int q = 0; q < XCDS; ++q) v[q] = q == cl[m] ? 1 : 0;
+    block_scan8_1024(v, pr, sums8, tot8);
+    pk[m] = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      pr[q] += carry[q];
+      if (q == cl[m]) pk[m] = pr[q];
+    }
+    if (valid) atomicAdd(&cnt[sx[m]][cl[m]], 1);
+#pragma unroll
+    for (int x = 0; x < XCDS; ++x) {
+      if (i == seg[x]) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) segp[x][q] = pr[q];
+      }
+    }
+    __syncthreads();
+    if (tid < 4) carry[tid] += tot8[tid];
+    __syncthreads();
+  }
+  // a segment that starts at the end of the list has every item before it
+  if (tid < XCDS * 4 && segp[tid >> 2][tid & 3] < 0) segp[tid >> 2][tid & 3] = carry[tid & 3];
+  __syncthreads();
+#pragma unroll
+  for (int m = 0; m < ORDER_ROUNDS; ++m) {
+    if (m * 1024 + tid >= all) break;
+    int x0 = 0, n = 0, r = 0;
+#pragma unroll
+    for (int x = 0; x < XCDS; ++x) {
+      if (x == sx[m]) {
+        x0 = seg[x];
+        n = B[x] + S[x];
+        r = pk[m] - segp[x][cl[m]];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) r += q < cl[m] ? cnt[x][q] : 0;
+      }
+    }
+    const int round = r / XCD_CUS, j = r % XCD_CUS;
+    const int len = min(XCD_CUS, n - round * XCD_CUS);
+    items[x0 + round * XCD_CUS + ((round & 1) ? len - 1 - j : j)] = it[m];
+  }
 }
 
 // SPLIT: items placed by token range (a.E <= 1024, one expert per thread); else the
@@ -346,6 +426,10 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(RouteArgs a) {
     }
   }
   if (tid == 0) *a.n_items = all;
+  if constexpr (SPLIT) {
+    if ((a.out + 127) / 128 == 1 && all <= 1024 * ORDER_ROUNDS)
+      snake_order(items, all, seg, B, S);
+  }
 }
 
 __global__ __launch_bounds__(256) void route_scatter_kernel(RouteArgs a) {
