@@ -33,10 +33,9 @@ constexpr int RANK_BLOCK = ROUTE_CHUNK;        // slots per rank block
 constexpr int RANK_WAVES = 4;                  // waves per rank block
 constexpr int RANK_ROUNDS = RANK_BLOCK / (64 * RANK_WAVES);  // 64-slot rounds per wave
 constexpr int MAX_E = 4096;
-constexpr int SCAN_PASSES = MAX_E / 1024;  // experts per scan thread
 constexpr int XCDS = 8;
 constexpr int XCD_CUS = 32;        // compute units per XCD
-constexpr int ORDER_ROUNDS = 4;    // item lists of up to 4096 are put in snake order
+constexpr int ORDER_ROUNDS = 2;    // item lists of up to 2048 are put in snake order
 
 // Wave w of rank block b ranks slots b * RANK_BLOCK + w * (RANK_BLOCK / RANK_WAVES) .. in
 // rounds of 64: the lanes holding the same expert are found with one ballot per id bit, and a
@@ -99,26 +98,36 @@ __global__ __launch_bounds__(64 * RANK_WAVES) void route_rank_kernel(
   }
 }
 
+// Inclusive sums within each row of 16 lanes by DPP (row_shr 1, 2, 4, 8; a lane with no
+// source adds 0).
+__device__ __forceinline__ int row_scan_incl(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, false);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, false);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, false);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, false);
+  return v;
+}
+// Inclusive sums over the 64 lanes: the rows', then lane 15 of rows 0 and 2 added to rows 1
+// and 3 (row_bcast 15), then lane 31 to rows 2 and 3 (row_bcast 31).
+__device__ __forceinline__ int wave_scan_incl(int v) {
+  v = row_scan_incl(v);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false);
+  return v;
+}
+
 // Exclusive block scan of one int per thread (1024 threads); returns the prefix and
-// stores the total in *total.
+// stores the total in *total. Wave 0 scans the 16 wave totals.
 __device__ int block_scan_1024(int v, int* wave_sums, int* total) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  int incl = v;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const int t = __shfl_up(incl, d, 64);
-    if (lane >= d) incl += t;
-  }
+  const int incl = wave_scan_incl(v);
   if (lane == 63) wave_sums[w] = incl;
   __syncthreads();
-  if (tid == 0) {
-    int run = 0;
-    for (int k = 0; k < 16; ++k) {
-      const int t = wave_sums[k];
-      wave_sums[k] = run;
-      run += t;
-    }
-    *total = run;
+  if (w == 0) {
+    const int t = lane < 16 ? wave_sums[lane] : 0;
+    const int ti = row_scan_incl(t);
+    if (lane < 16) wave_sums[lane] = ti - t;
+    if (lane == 15) *total = ti;
   }
   __syncthreads();
   const int res = wave_sums[w] + incl - v;
@@ -127,33 +136,27 @@ __device__ int block_scan_1024(int v, int* wave_sums, int* total) {
 }
 
 // The same for XCDS ints per thread at once: res[x] is the exclusive prefix of v[x], tot[x]
-// (shared) its total.
+// (shared) its total. Wave 0 scans the wave totals of four columns per pass, one row of
+// 16 lanes each.
 __device__ void block_scan8_1024(const int v[XCDS], int res[XCDS], int (*sums)[XCDS], int* tot) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   int incl[XCDS];
 #pragma unroll
-  for (int x = 0; x < XCDS; ++x) incl[x] = v[x];
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-#pragma unroll
-    for (int x = 0; x < XCDS; ++x) {
-      const int t = __shfl_up(incl[x], d, 64);
-      if (lane >= d) incl[x] += t;
-    }
-  }
+  for (int x = 0; x < XCDS; ++x) incl[x] = wave_scan_incl(v[x]);
   if (lane == 63) {
 #pragma unroll
     for (int x = 0; x < XCDS; ++x) sums[w][x] = incl[x];
   }
   __syncthreads();
-  if (tid < XCDS) {
-    int run = 0;
-    for (int k = 0; k < 16; ++k) {
-      const int t = sums[k][tid];
-      sums[k][tid] = run;
-      run += t;
+  if (w == 0) {
+#pragma unroll
+    for (int h = 0; h < XCDS / 4; ++h) {
+      const int x = 4 * h + (lane >> 4), k = lane & 15;
+      const int t = sums[k][x];
+      const int ti = row_scan_incl(t);
+      sums[k][x] = ti - t;
+      if (k == 15) tot[x] = ti;
     }
-    tot[tid] = run;
   }
   __syncthreads();
 #pragma unroll
@@ -161,9 +164,15 @@ __device__ void block_scan8_1024(const int v[XCDS], int res[XCDS], int (*sums)[X
   __syncthreads();
 }
 
-// The token range of an expert's slot row r, given the first row of each range (start[0] =
-// 0, non-decreasing).
-__device__ __forceinline__ int item_range(const int start[XCDS], int r) {
+// An expert's items are its slot rows in runs of R; the anchor of item i is row
+// min(R i + R / 2, c - 1). first_items(Y) = the items i < ni - 1 with R i + R / 2 < Y (for
+// those items the anchor is R i + R / 2); the last item is counted on its own.
+__device__ __forceinline__ int first_items(int Y, int R, int ni) {
+  const int n = Y <= R / 2 ? 0 : (Y - R / 2 + R - 1) / R;
+  return min(n, ni - 1);
+}
+// The token range of row r, given the first row of each range (start[0] = 0, ascending).
+__device__ __forceinline__ int row_range(const int start[XCDS], int r) {
   int x = 0;
 #pragma unroll
   for (int j = 1; j < XCDS; ++j) x += r >= start[j] ? 1 : 0;
@@ -198,18 +207,28 @@ __device__ void snake_order(int4* items, int all, const int seg[XCDS], const int
   __shared__ int cnt[XCDS][4];     // items per segment and class
   __shared__ int segp[XCDS][4];    // items of each class before each segment's start
   __shared__ int carry[4];
+  __shared__ int sseg[XCDS], slen[XCDS];
   const int tid = threadIdx.x;
   if (tid < XCDS * 4) {
     cnt[tid >> 2][tid & 3] = 0;
     segp[tid >> 2][tid & 3] = -1;
   }
   if (tid < 4) carry[tid] = 0;
-  __threadfence();  // the list, as written, is visible to every thread of the workgroup
-  __syncthreads();
+  if (tid < XCDS) {
+#pragma unroll
+    for (int x = 0; x < XCDS; ++x) {
+      if (x == tid) {
+        sseg[x] = seg[x];
+        slen[x] = B[x] + S[x];
+      }
+    }
+  }
+  __syncthreads();  // the list, as written, is visible to every thread of the workgroup
   int4 it[ORDER_ROUNDS];
   int cl[ORDER_ROUNDS], sx[ORDER_ROUNDS], pk[ORDER_ROUNDS];
 #pragma unroll
   for (int m = 0; m < ORDER_ROUNDS; ++m) {
+    if (m * 1024 >= all) break;
     const int i = m * 1024 + tid;
     const bool valid = i < all;
     it[m] = valid ? items[i] : make_int4(0, 0, 0, 0);
@@ -246,57 +265,74 @@ __device__ void snake_order(int4* items, int all, const int seg[XCDS], const int
 #pragma unroll
   for (int m = 0; m < ORDER_ROUNDS; ++m) {
     if (m * 1024 + tid >= all) break;
-    int x0 = 0, n = 0, r = 0;
-#pragma unroll
-    for (int x = 0; x < XCDS; ++x) {
-      if (x == sx[m]) {
-        x0 = seg[x];
-        n = B[x] + S[x];
-        r = pk[m] - segp[x][cl[m]];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) r += q < cl[m] ? cnt[x][q] : 0;
-      }
-    }
+    const int x = sx[m];
+    const int x0 = sseg[x], n = slen[x];
+    int r = pk[m] - segp[x][cl[m]];
+    for (int q = 0; q < cl[m]; ++q) r += cnt[x][q];
     const int round = r / XCD_CUS, j = r % XCD_CUS;
     const int len = min(XCD_CUS, n - round * XCD_CUS);
     items[x0 + round * XCD_CUS + ((round & 1) ? len - 1 - j : j)] = it[m];
   }
 }
 
-// SPLIT: items placed by token range (a.E <= 1024, one expert per thread); else the
-// experts' items in expert order, up to MAX_E experts.
-template <bool SPLIT>
+// Per-expert counts and offsets and the bases of every (block, expert) in hist; items (when
+// asked) in expert order. Up to MAX_E experts, 1024 a pass.
+// Thread e writes the bases of its column of hist (off + the slots of the earlier blocks),
+// by buffer stores (those past the last block are dropped). With st, also the first row of
+// each token range x among its slots: the slots of the blocks before the range's first
+// block, the first b with 8 b >= x blocks.
+template <bool ST>
+__device__ __forceinline__ void hist_bases(__amdgpu_buffer_rsrc_t rh, int E, int e, int blocks,
+                                           int off, int (&st)[XCDS]) {
+  int lo[XCDS];
+#pragma unroll
+  for (int x = 0; x < XCDS; ++x) {
+    lo[x] = (x * blocks + XCDS - 1) / XCDS;
+    if constexpr (ST) st[x] = 0;
+  }
+  typedef int i32x32 __attribute__((ext_vector_type(SCAN_BATCH)));
+  int run = off;
+  for (int b0 = 0; b0 < blocks; b0 += SCAN_BATCH) {
+    int t[SCAN_BATCH];
+    hist_batch(rh, E, e, b0, blocks, t);
+    i32x32 pre;  // the base of each block of the batch
+#pragma unroll
+    for (int j = 0; j < SCAN_BATCH; ++j) {
+      pre[j] = run;
+      __builtin_amdgcn_raw_buffer_store_b32(run, rh, 4u * e, 4u * (uint32_t)((b0 + j) * E), 0);
+      run += t[j];
+    }
+    if constexpr (ST) {
+      // a range's first block in this batch: its base (a uniform index into pre)
+#pragma unroll
+      for (int x = 1; x < XCDS; ++x) {
+        const int j = lo[x] - b0;
+        if (j >= 0 && j < SCAN_BATCH) st[x] = pre[j] - off;
+      }
+    }
+  }
+  if constexpr (ST) {
+#pragma unroll
+    for (int x = 1; x < XCDS; ++x)
+      if (lo[x] >= blocks) st[x] = run - off;  // a range with no block starts after them all
+  }
+}
+
 __global__ __launch_bounds__(1024) void route_scan_kernel(RouteArgs a) {
-  constexpr int PASSES = SPLIT ? 1 : SCAN_PASSES;
   __shared__ int wave_sums[16];
   __shared__ int total;
-  __shared__ int sums8[16][XCDS];
-  __shared__ int tot8[XCDS];
-  __shared__ int carry[2 + XCDS];  // slots, other experts' items, split items per range
+  __shared__ int carry[2];
   const int tid = threadIdx.x;
-  if (tid < 2 + XCDS) carry[tid] = 0;
+  if (tid == 0) {
+    carry[0] = 0;
+    carry[1] = 0;
+  }
   __syncthreads();
   const __amdgpu_buffer_rsrc_t rh = __builtin_amdgcn_make_buffer_rsrc(
       a.hist, (short)0, (int)((size_t)a.blocks * a.E * 4), 0x00020000);
   const int R = a.item_rows;
-  // per expert of this thread (e = 1024 p + tid): slots and offset, whether it is placed by
-  // range, the first row of each range among its slots and the list position of its first
-  // item placed in range x among all items placed in range x, or the position of its first
-  // item among the other experts' items
-  int cnt[PASSES], eoff[PASSES], psm[PASSES];
-  int cx[PASSES][XCDS], pbx[PASSES][XCDS];
-  bool big[PASSES];
-#pragma unroll
-  for (int p = 0; p < PASSES; ++p) {
-    cnt[p] = eoff[p] = psm[p] = 0;
-    big[p] = false;
-#pragma unroll
-    for (int x = 0; x < XCDS; ++x) cx[p][x] = pbx[p][x] = 0;
-  }
-#pragma unroll
-  for (int p = 0; p < PASSES; ++p) {
-    if (p * 1024 >= a.E) break;
-    const int e = p * 1024 + tid;
+  for (int e0 = 0; e0 < a.E; e0 += 1024) {
+    const int e = e0 + tid;
     const bool mine = e < a.E;
     int c = 0;
     if (mine) {
@@ -304,79 +340,96 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(RouteArgs a) {
         int t[SCAN_BATCH];
         hist_batch(rh, a.E, e, b0, a.blocks, t);
 #pragma unroll
-        for (int j = 0; j < SCAN_BATCH; ++j) {
-          c += t[j];
-          if constexpr (SPLIT) {
-            const int xr = ((b0 + j) * XCDS) / a.blocks;
-#pragma unroll
-            for (int x = 0; x < XCDS; ++x) cx[p][x] += xr == x ? t[j] : 0;
-          }
-        }
+        for (int j = 0; j < SCAN_BATCH; ++j) c += t[j];
       }
     }
+    const int ni = (a.items && mine) ? (c + R - 1) / R : 0;
     const int off = block_scan_1024(c, wave_sums, &total) + carry[0];
     const int tc = total;
+    const int ib = block_scan_1024(ni, wave_sums, &total) + carry[1];
+    const int ti = total;
     if (mine) {
       a.counts[e] = c;
       a.offsets[e] = off;
-      int run = off;
-      for (int b0 = 0; b0 < a.blocks; b0 += SCAN_BATCH) {
-        int t[SCAN_BATCH];
-        hist_batch(rh, a.E, e, b0, a.blocks, t);
-#pragma unroll
-        for (int j = 0; j < SCAN_BATCH; ++j) {
-          if (b0 + j < a.blocks) a.hist[(size_t)(b0 + j) * a.E + e] = run;
-          run += t[j];
-        }
-      }
+      int unused[XCDS];
+      hist_bases<false>(rh, a.E, e, a.blocks, off, unused);
+      for (int k = 0; k < ni; ++k)
+        reinterpret_cast<int4*>(a.items)[ib + k] =
+            make_int4(e, off + k * R, min(R, c - k * R), 0);
     }
-    cnt[p] = c;
-    eoff[p] = off;
-    big[p] = SPLIT && mine && c >= a.split_rows;
-    if constexpr (SPLIT) {
-      // cx becomes the first row of each range among the expert's slots
-      int run_r = 0;
-#pragma unroll
-      for (int x = 0; x < XCDS; ++x) {
-        const int t = cx[p][x];
-        cx[p][x] = run_r;
-        run_r += t;
-      }
-      int nb[XCDS], pb[XCDS];
-#pragma unroll
-      for (int x = 0; x < XCDS; ++x) nb[x] = 0;
-      if (big[p]) {
-        for (int r0 = 0; r0 < c; r0 += R) {
-          const int xi = item_range(cx[p], min(r0 + R / 2, c - 1));
-#pragma unroll
-          for (int x = 0; x < XCDS; ++x) nb[x] += xi == x ? 1 : 0;
-        }
-      }
-      block_scan8_1024(nb, pb, sums8, tot8);
-#pragma unroll
-      for (int x = 0; x < XCDS; ++x) pbx[p][x] = pb[x] + carry[2 + x];
-    }
-    const int ns = (a.items && mine && !big[p]) ? (c + R - 1) / R : 0;
-    psm[p] = block_scan_1024(ns, wave_sums, &total) + carry[1];
-    const int ts = total;
     __syncthreads();
     if (tid == 0) {
       carry[0] += tc;
-      carry[1] += ts;
+      carry[1] += ti;
     }
-    if (SPLIT && tid < XCDS) carry[2 + tid] += tot8[tid];
     __syncthreads();
   }
-  if (tid == 0) a.offsets[a.E] = carry[0];
-  if (!a.items) return;
+  if (tid == 0) {
+    a.offsets[a.E] = carry[0];
+    if (a.n_items) *a.n_items = carry[1];
+  }
+}
+
+// The same with the items placed by token range (a.items set, a.split_rows > 0, a.E <=
+// 1024: one expert per thread).
+__global__ __launch_bounds__(1024) void route_scan_split_kernel(RouteArgs a) {
+  __shared__ int wave_sums[16];
+  __shared__ int total;
+  __shared__ int sums8[16][XCDS];
+  __shared__ int tot8[XCDS];
+  const int tid = threadIdx.x;
+  const __amdgpu_buffer_rsrc_t rh = __builtin_amdgcn_make_buffer_rsrc(
+      a.hist, (short)0, (int)((size_t)a.blocks * a.E * 4), 0x00020000);
+  const int R = a.item_rows;
+  const int e = tid;
+  const bool mine = e < a.E;
+  int c = 0;
+  if (mine) {
+    for (int b0 = 0; b0 < a.blocks; b0 += SCAN_BATCH) {
+      int t[SCAN_BATCH];
+      hist_batch(rh, a.E, e, b0, a.blocks, t);
+#pragma unroll
+      for (int j = 0; j < SCAN_BATCH; ++j) c += t[j];
+    }
+  }
+  const int off = block_scan_1024(c, wave_sums, &total);
+  const int all_slots = total;
+  // st[x]: the first row of token range x among the expert's slots (the slots of the
+  // blocks before the range's first block)
+  int st[XCDS] = {0, 0, 0, 0, 0, 0, 0, 0};
+  if (mine) {
+    a.counts[e] = c;
+    a.offsets[e] = off;
+    hist_bases<true>(rh, a.E, e, a.blocks, off, st);
+  }
+  const bool big = mine && c >= a.split_rows;
+  // items per range: the counts of first_items between the range starts, and the last item
+  const int ni = (c + R - 1) / R;
+  const int last = (ni - 1) * R;
+  int nb[XCDS], pb[XCDS];
+  int xl = 0;
+  if (big) {
+    xl = row_range(st, min(last + R / 2, c - 1));
+#pragma unroll
+    for (int x = 0; x < XCDS; ++x)
+      nb[x] = first_items(x + 1 < XCDS ? st[x + 1] : c, R, ni) - first_items(st[x], R, ni) +
+              (x == xl ? 1 : 0);
+  } else {
+#pragma unroll
+    for (int x = 0; x < XCDS; ++x) nb[x] = 0;
+  }
+  block_scan8_1024(nb, pb, sums8, tot8);
+  const int ns = (mine && !big) ? ni : 0;
+  const int psm = block_scan_1024(ns, wave_sums, &total);
+  const int small = total;
+  if (tid == 0) a.offsets[a.E] = all_slots;
 
   // segments: x holds the items placed in range x, then its share of the others' items
   int B[XCDS], S[XCDS], seg[XCDS], ps0[XCDS];
-  const int small = carry[1];
   int all = small;
 #pragma unroll
   for (int x = 0; x < XCDS; ++x) {
-    B[x] = carry[2 + x];
+    B[x] = tot8[x];
     all += B[x];
   }
   const int share = (all + XCDS - 1) / XCDS;
@@ -395,41 +448,31 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(RouteArgs a) {
     runs += S[x];
   }
   int4* items = reinterpret_cast<int4*>(a.items);
+  if (big) {
+    // range x takes items first_items(start x) .. first_items(start x + 1) - 1, then the
+    // last item joins the range of its anchor, after them
+    int lpos = 0;
 #pragma unroll
-  for (int p = 0; p < PASSES; ++p) {
-    const int e = p * 1024 + tid;
-    if (p * 1024 >= a.E || e >= a.E) break;
-    const int c = cnt[p];
-    if (big[p]) {
-      // the ranges of successive items never decrease: k counts the items placed in the
-      // current one
-      int xprev = -1, k = 0;
-      for (int r0 = 0; r0 < c; r0 += R) {
-        const int xi = item_range(cx[p], min(r0 + R / 2, c - 1));
-        k = xi == xprev ? k + 1 : 0;
-        xprev = xi;
-        int base = 0;
+    for (int x = 0; x < XCDS; ++x) {
+      const int i0 = first_items(st[x], R, ni);
+      const int i1 = first_items(x + 1 < XCDS ? st[x + 1] : c, R, ni);
+      const int base = seg[x] + pb[x];
+      for (int i = i0; i < i1; ++i) items[base + (i - i0)] = make_int4(e, off + i * R, R, 0);
+      if (x == xl) lpos = base + (i1 - i0);
+    }
+    items[lpos] = make_int4(e, off + last, c - last, 0);
+  } else if (mine) {
+    for (int k = 0; k < ni; ++k) {
+      const int g = psm + k;  // its place among the other experts' items
+      int pos = 0;
 #pragma unroll
-        for (int x = 0; x < XCDS; ++x)
-          if (x == xi) base = seg[x] + pbx[p][x];
-        items[base + k] = make_int4(e, eoff[p] + r0, min(R, c - r0), 0);
-      }
-    } else {
-      for (int k = 0; k * R < c; ++k) {
-        const int g = psm[p] + k;  // its place among the other experts' items
-        int pos = 0;
-#pragma unroll
-        for (int x = 0; x < XCDS; ++x)
-          if (g >= ps0[x] && g < ps0[x] + S[x]) pos = seg[x] + B[x] + (g - ps0[x]);
-        items[pos] = make_int4(e, eoff[p] + k * R, min(R, c - k * R), 0);
-      }
+      for (int x = 0; x < XCDS; ++x)
+        if (g >= ps0[x] && g < ps0[x] + S[x]) pos = seg[x] + B[x] + (g - ps0[x]);
+      items[pos] = make_int4(e, off + k * R, min(R, c - k * R), 0);
     }
   }
   if (tid == 0) *a.n_items = all;
-  if constexpr (SPLIT) {
-    if ((a.out + 127) / 128 == 1 && all <= 1024 * ORDER_ROUNDS)
-      snake_order(items, all, seg, B, S);
-  }
+  if ((a.out + 127) / 128 == 1 && all <= 1024 * ORDER_ROUNDS) snake_order(items, all, seg, B, S);
 }
 
 __global__ __launch_bounds__(256) void route_scatter_kernel(RouteArgs a) {
@@ -487,9 +530,9 @@ hipError_t launch_route(const RouteArgs& a, hipStream_t s) {
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   if (a.items && a.split_rows > 0 && a.E <= 1024)
-    hipLaunchKernelGGL(route_scan_kernel<true>, dim3(1), dim3(1024), 0, s, a);
+    hipLaunchKernelGGL(route_scan_split_kernel, dim3(1), dim3(1024), 0, s, a);
   else
-    hipLaunchKernelGGL(route_scan_kernel<false>, dim3(1), dim3(1024), 0, s, a);
+    hipLaunchKernelGGL(route_scan_kernel, dim3(1), dim3(1024), 0, s, a);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(route_scatter_kernel, dim3((unsigned)((a.N + 255) / 256)), dim3(256), 0, s,
