@@ -819,7 +819,7 @@ def main():
             "unit_bytes": d["bytes"],
             "prefill_tokens": pf["T"], "prefill_TFLOP/s": round(pf["flops"] / pf["sec_per_step"] / 1e12, 3),
             "prefill_ms_per_step": round(pf["sec_per_step"] * 1e3, 5),
-            "prefill_kernel": "fp8b32_gemm_kernel",
+            "prefill_kernel": "mxfp4_prefill_kernel<fp8b32>",
             "prefill_kernel_us": round(pf["kernel_sec"] * 1e6, 3),
             "prefill_frac_bf16_peak": round(pf["flops"] / pf["kernel_sec"] / 1e12 / F16_PEAK_TFLOPS, 4),
         }
