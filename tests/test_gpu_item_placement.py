@@ -4,9 +4,10 @@ and the snake order within segments (one-group layers). Whatever the layout, eve
 slot must be computed once, by its own expert: every slot is compared with the FP64 oracle
 (per-slot and pooled relative L2 <= 1e-3). The shapes: every token on the same two experts
 (all items in one range), fewer rank blocks than token ranges (empty ranges), a block count
-that is neither a multiple of 8 nor of the scan's batch, 1,024 experts (the largest that is
-placed by range) and 1,025 (the plain layout), several output groups (no snake order), and
-the MXFP4 prefill with gates."""
+that is neither a multiple of 8 nor of the scan's batch, more blocks than one batch, more
+items than one round of the snake ordering, 1,024 experts (the largest that is placed by
+range) and 1,025 (the plain layout), several output groups (no snake order), and the MXFP4
+prefill with gates."""
 
 import numpy as np
 import pytest
@@ -49,6 +50,17 @@ def test_fewer_rank_blocks_than_ranges():
 def test_block_count_not_a_multiple_of_8_or_32():
     T, E, topk = 4100, 256, 8  # 32,800 slots: 17 rank blocks
     _trellis(1102, E, T, topk, zipf_routes(rng_for(1102, 2), T, E, topk))
+
+
+def test_more_rank_blocks_than_one_scan_batch():
+    T, E, topk = 10000, 128, 8  # 80,000 slots: 40 rank blocks, range starts in two batches
+    _trellis(1106, E, T, topk, zipf_routes(rng_for(1106, 2), T, E, topk))
+
+
+@pytest.mark.timeout(600)
+def test_item_list_longer_than_one_ordering_round():
+    T, E, topk = 20000, 64, 8  # 160,000 slots: over 1,024 items, two rounds of the ordering
+    _trellis(1107, E, T, topk, zipf_routes(rng_for(1107, 2), T, E, topk))
 
 
 @pytest.mark.parametrize("E", [1024, 1025])
